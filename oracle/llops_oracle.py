@@ -1,0 +1,282 @@
+"""Plain fp64 CPU oracle for the LLoPS linear-attention hot path.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call this module. The product path (the HIP
+library and its Python binding) never does, and this module imports nothing
+from it. Inputs arrive as plain numpy arrays; everything here runs in float64
+with no intermediate rounding, no blocking and no fusion beyond what each
+definition states.
+
+Sources (titles of the pages the method is described on):
+  [LLoPS-notes]  "Learnable Low-Rank Polynomial Sketch for Effective Linear
+                 Attention" -- papernotes.org reading notes (NeurIPS 2026).
+  [LLoPS-arXiv]  the same paper's text (arXiv 2610.14219), signal-papers reader.
+  [SLAY-notes]   "SLAY: Geometry-aware Spherical Linearized Attention with
+                 Yat-kernel" notes -- only its normalised linear-attention form.
+  [LowRank-blog] blog post on low-rank attention, Linformer and Performer --
+                 associativity and the causal cumulative-sum remark.
+
+Readings taken where the pages are silent (each also pinned by a test where
+the mathematics allows; see tests/test_oracle_pins.py):
+  * Theta_{j,r} is d x m and feature i is column i ([LLoPS-notes] key design 2).
+  * Lambda weights are folded into Theta (no separate lambda argument).
+  * Squaring, when asked for, is applied after the sum over r.
+  * Normaliser: out_i = num_i / (phi_Q(q_i) . z_i + delta), delta added once.
+  * Causal mask is inclusive (key j contributes to query i iff j <= i); the
+    decode step adds the new key/value to the state before reading it.
+  * No 1/sqrt(d) scaling inside the method; the kernel is (q^T k)^p.
+parity unpinned: the delta placement and the inclusive diagonal are
+conventions (the pages fix neither); the tests only check that every path
+applies them consistently.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Feature map
+# --------------------------------------------------------------------------
+def featmap(X, theta, square: bool = False) -> np.ndarray:
+    """phi(X) = sum_r prod_j (X Theta_{j,r}), optionally squared element-wise.
+
+    X: [n, d]; theta: [p, t, d, m]. Returns [n, m] float64.
+    [LLoPS-notes] key design 2: psi_p(Q) W_hat = sum_r prod_j Q Theta_{j,r}
+    (p*t low-dimensional products, then a Hadamard product over j and a sum
+    over the t rank components). Squaring: [LLoPS-notes] training strategy
+    (non-negativity) and [LLoPS-arXiv] Sec. 3 non-negativity paragraph.
+    """
+    X = _f64(X)
+    theta = _f64(theta)
+    p, t, d, m = theta.shape
+    assert X.shape[-1] == d
+    F = np.zeros(X.shape[:-1] + (m,))
+    for r in range(t):
+        prod = np.ones(X.shape[:-1] + (m,))
+        for j in range(p):
+            prod = prod * (X @ theta[j, r])
+        F = F + prod
+    if square:
+        F = F * F
+    return F
+
+
+# --------------------------------------------------------------------------
+# Exact polynomial machinery (explicit d^p expansion; tiny d only)
+# --------------------------------------------------------------------------
+def psi(X, p: int) -> np.ndarray:
+    """psi_p(x) = vec(x^{(x)p}) for every row of X: [n, d] -> [n, d^p].
+
+    [LLoPS-arXiv] Sec. 1-3: the exact degree-p monomial feature map; index
+    (a_1, ..., a_p) sits at position a_1 d^{p-1} + ... + a_p (np.kron order).
+    """
+    X = _f64(X)
+    out = []
+    for x in X:
+        v = np.array([1.0])
+        for _ in range(p):
+            v = np.kron(v, x)
+        out.append(v)
+    return np.array(out)
+
+
+def w_hat(theta) -> np.ndarray:
+    """W_hat = sum_r Theta_{1,r} (.)col ... (.)col Theta_{p,r}: [d^p, m].
+
+    Column i of the column-wise Kronecker product is the Kronecker product of
+    the i-th columns, in the same order psi() uses.
+    [LLoPS-notes] key design 2 (equation for W_hat); [LLoPS-arXiv] Eq. 8.
+    """
+    theta = _f64(theta)
+    p, t, d, m = theta.shape
+    W = np.zeros((d ** p, m))
+    for r in range(t):
+        for i in range(m):
+            col = np.array([1.0])
+            for j in range(p):
+                col = np.kron(col, theta[j, r, :, i])
+            W[:, i] += col
+    return W
+
+
+def poly_kernel(Q, K, p: int) -> np.ndarray:
+    """A = (Q K^T)^{*p}, the degree-p polynomial kernel matrix, no scaling.
+
+    [LLoPS-arXiv] kappa(q, k) = (q^T k)^p; [LLoPS-notes] key design 1.
+    """
+    return (_f64(Q) @ _f64(K).T) ** p
+
+
+def eckart_young_floor(Q, K, p: int, m: int) -> float:
+    """sum_{i>m} sigma_i^2 of A = (Q K^T)^{*p}: the least squared Frobenius
+    error any rank-m product phi_Q phi_K^T can reach.
+    [LLoPS-notes] key design 1 (Eckart-Young-Mirsky bound)."""
+    s = np.linalg.svd(poly_kernel(Q, K, p), compute_uv=False)
+    return float(np.sum(s[m:] ** 2))
+
+
+def optimal_linear_sketch(Q, K, p: int, m: int):
+    """Theorem 3.1's construction: W1, W2 in R^{d^p x m} with
+    psi_p(Q) W1 = U_m Sigma_m^{1/2} and psi_p(K) W2 = V_m Sigma_m^{1/2},
+    found by least squares (the proof shows an exact solution exists).
+    [LLoPS-arXiv] Appendix A.1; [LLoPS-notes] key design 1."""
+    A = poly_kernel(Q, K, p)
+    U, s, Vt = np.linalg.svd(A)
+    rs = np.sqrt(s[:m])
+    W1 = np.linalg.lstsq(psi(Q, p), U[:, :m] * rs, rcond=None)[0]
+    W2 = np.linalg.lstsq(psi(K, p), Vt[:m].T * rs, rcond=None)[0]
+    return W1, W2
+
+
+# --------------------------------------------------------------------------
+# Linear attention, one (batch, head) slice
+# --------------------------------------------------------------------------
+def linattn(Q, K, V, theta_q, theta_k, square=False, normalize=False, delta=0.0):
+    """Non-causal: out = phi_Q (phi_K^T V) [/ (phi_Q (phi_K^T 1) + delta)].
+
+    [LLoPS-notes] overall framework: Attn = phi_Q(Q) (phi_K(K)^T V) by
+    associativity; [LowRank-blog] Performer section for the normalised
+    numerator/denominator form; [SLAY-notes] key design 3 for the +delta.
+    """
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    V = _f64(V)
+    num = Pq @ (Pk.T @ V)
+    if not normalize:
+        return num
+    den = Pq @ Pk.sum(axis=0) + delta
+    return num / den[:, None]
+
+
+def causal_quadratic(Q, K, V, theta_q, theta_k, square=False, normalize=False,
+                     delta=0.0):
+    """Causal, materialised: M = tril(phi_Q phi_K^T) (diagonal kept),
+    out = M V [/ (M 1 + delta)]. O(n^2); small n only.
+    [LLoPS-arXiv] Sec. 1 (attention as (phi(Q) phi(K)^T) V); causal masking
+    per the causal-LM use in [LLoPS-notes] training strategy."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    M = np.tril(Pq @ Pk.T)
+    num = M @ _f64(V)
+    if not normalize:
+        return num
+    return num / (M.sum(axis=1) + delta)[:, None]
+
+
+def causal_chunked(Q, K, V, theta_q, theta_k, square=False, normalize=False,
+                   delta=0.0, chunk=64, S0=None, z0=None):
+    """Causal, recurrent over chunks of `chunk` tokens.
+
+    State S (m x dv) and z (m) hold phi_K^T V and phi_K^T 1 of all earlier
+    chunks; within a chunk the masked product is explicit:
+      num_c = tril(Pq_c Pk_c^T) V_c + Pq_c S,  den_c = tril(..) 1 + Pq_c z + delta
+      then S += Pk_c^T V_c, z += Pk_c^T 1.
+    [LowRank-blog] Linformer-vs-Performer table (causal masking by
+    incremental cumulative sums); [LLoPS-arXiv] Sec. 1 (streaming computation
+    with a constant-size state). Returns (out, S_final, z_final).
+    """
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    V = _f64(V)
+    n, m = Pq.shape
+    dv = V.shape[1]
+    S = np.zeros((m, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(m) if z0 is None else _f64(z0).copy()
+    out = np.zeros((n, dv))
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        q, k, v = Pq[c0:c1], Pk[c0:c1], V[c0:c1]
+        A = np.tril(q @ k.T)
+        num = A @ v + q @ S
+        if normalize:
+            den = A.sum(axis=1) + q @ z + delta
+            out[c0:c1] = num / den[:, None]
+        else:
+            out[c0:c1] = num
+        S = S + k.T @ v
+        z = z + k.sum(axis=0)
+    return out, S, z
+
+
+def state_from_prefix(K, V, theta_k, square=False):
+    """S = phi_K^T V and z = phi_K^T 1 over a prefix (the state a causal pass
+    over these tokens leaves behind). [LLoPS-arXiv] Sec. 1 (constant state)."""
+    Pk = featmap(K, theta_k, square)
+    return Pk.T @ _f64(V), Pk.sum(axis=0)
+
+
+def decode(S0, z0, q_steps, k_steps, v_steps, theta_q, theta_k, square=False,
+           normalize=True, delta=0.0):
+    """Single-token recurrent steps for one (batch, head) slice.
+
+    Each step: S += phi_k v^T; z += phi_k; o = phi_q^T S [/ (phi_q^T z + delta)]
+    (state updated before it is read, matching the inclusive causal mask).
+    q_steps, k_steps: [steps, d]; v_steps: [steps, dv].
+    Returns (outs [steps, dv], S, z).
+    [LLoPS-arXiv] Sec. 1 (recurrent memory state); [LowRank-blog] Performer
+    section (sums over keys shared by all queries, updated incrementally).
+    """
+    S = _f64(S0).copy()
+    z = _f64(z0).copy()
+    outs = []
+    for q, k, v in zip(_f64(q_steps), _f64(k_steps), _f64(v_steps)):
+        fq = featmap(q[None], theta_q, square)[0]
+        fk = featmap(k[None], theta_k, square)[0]
+        S = S + np.outer(fk, v)
+        z = z + fk
+        o = fq @ S
+        if normalize:
+            o = o / (fq @ z + delta)
+        outs.append(o)
+    return np.array(outs), S, z
+
+
+# --------------------------------------------------------------------------
+# Batched wrappers over [B, H, n, *] with per-head (or shared) Theta
+# --------------------------------------------------------------------------
+def _theta_for(theta, h):
+    theta = np.asarray(theta)
+    return theta[h] if theta.ndim == 5 else theta
+
+
+def featmap_bh(X, theta, square=False) -> np.ndarray:
+    """featmap over X [B, H, n, d] with theta [H, p, t, d, m] or [p, t, d, m]."""
+    B, H = X.shape[:2]
+    m = np.asarray(theta).shape[-1]
+    out = np.zeros((B, H, X.shape[2], m))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = featmap(X[b, h], _theta_for(theta, h), square)
+    return out
+
+
+def linattn_bh(Q, K, V, theta_q, theta_k, **kw) -> np.ndarray:
+    B, H, n, _ = Q.shape
+    out = np.zeros((B, H, n, V.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = linattn(Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
+                                _theta_for(theta_k, h), **kw)
+    return out
+
+
+def causal_bh(Q, K, V, theta_q, theta_k, chunk=64, S0=None, z0=None, **kw):
+    """Returns (out [B,H,n,dv], S [B,H,m,dv], z [B,H,m])."""
+    B, H, n, _ = Q.shape
+    m = np.asarray(theta_q).shape[-1]
+    dv = V.shape[-1]
+    out = np.zeros((B, H, n, dv))
+    S = np.zeros((B, H, m, dv))
+    z = np.zeros((B, H, m))
+    for b in range(B):
+        for h in range(H):
+            s0 = None if S0 is None else S0[b, h]
+            zz = None if z0 is None else z0[b, h]
+            out[b, h], S[b, h], z[b, h] = causal_chunked(
+                Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
+                _theta_for(theta_k, h), chunk=chunk, S0=s0, z0=zz, **kw)
+    return out, S, z

@@ -1,0 +1,321 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties an oracle function to something other than itself: the
+explicit d^p Kronecker expansion, the exact polynomial kernel, hand-worked
+values, an SVD bound, brute-force loops, or an invariance. CPU only.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import llops_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_theta(rng, p, t, d, m):
+    return rng.standard_normal((p, t, d, m)) / np.sqrt(d)
+
+
+def _selection_theta(d, p):
+    """Theta for the exact kernel: m = d^p columns, column (a_1..a_p) of
+    Theta_j is e_{a_j}, so phi(x)_{a} = prod_j x_{a_j}."""
+    m = d ** p
+    th = np.zeros((p, 1, d, m))
+    for col in range(m):
+        idx = np.unravel_index(col, (d,) * p)
+        for j in range(p):
+            th[j, 0, idx[j], col] = 1.0
+    return th
+
+
+# --------------------------------------------------------------------------
+# P-1: factorised map == explicit psi_p(X) W_hat (column-wise Kronecker)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d,p,t,m", [(2, 2, 1, 3), (2, 2, 2, 3), (3, 1, 2, 5), (3, 2, 3, 5),
+                                     (4, 3, 2, 3), (2, 3, 3, 5), (8, 2, 2, 5), (3, 4, 2, 3)])
+def test_featmap_equals_kronecker_sketch(d, p, t, m):
+    rng = np.random.default_rng(100 + d * 10 + p)
+    X = rng.standard_normal((7, d))
+    th = _rand_theta(rng, p, t, d, m)
+    fast = O.featmap(X, th)
+    slow = O.psi(X, p) @ O.w_hat(th)
+    np.testing.assert_allclose(fast, slow, rtol=1e-12, atol=1e-12 * np.abs(slow).max())
+
+
+def test_featmap_golden_toy():
+    g = _golden("toy_featmap_p2_d2_m3.json")
+    X = np.array(g["X"], float)
+    th = np.array(g["theta_p_t_d_m"], float)
+    np.testing.assert_array_equal(O.featmap(X, th[:, :1]), g["phi_t1"])
+    np.testing.assert_array_equal(O.featmap(X, th[:, :1], square=True), g["phi_t1_squared"])
+    np.testing.assert_array_equal(O.featmap(X, th), g["phi_t2"])
+    np.testing.assert_array_equal(O.featmap(X, th, square=True), g["phi_t2_squared"])
+    # the explicit sketch agrees on the hand-worked values too
+    np.testing.assert_allclose(O.psi(X, 2) @ O.w_hat(th), g["phi_t2"], atol=1e-12)
+
+
+def test_psi_kron_layout():
+    # psi_2(1,2) = (1,2,2,4) in (a,b) -> a*d+b order
+    np.testing.assert_array_equal(O.psi(np.array([[1.0, 2.0]]), 2), [[1, 2, 2, 4]])
+    # <psi_p(x), psi_p(y)> = (x^T y)^p
+    rng = np.random.default_rng(1)
+    x, y = rng.standard_normal((2, 1, 3))
+    for p in (1, 2, 3):
+        np.testing.assert_allclose(O.psi(x, p) @ O.psi(y, p).T, (x @ y.T) ** p, rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P-2: exact polynomial kernel reached with selection Theta
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("d,p", [(2, 2), (3, 2), (4, 2), (2, 3), (3, 3)])
+def test_exact_kernel(d, p):
+    rng = np.random.default_rng(7 * d + p)
+    Q = rng.standard_normal((5, d))
+    K = rng.standard_normal((6, d))
+    th = _selection_theta(d, p)
+    got = O.featmap(Q, th) @ O.featmap(K, th).T
+    np.testing.assert_allclose(got, (Q @ K.T) ** p, rtol=1e-11, atol=1e-12)
+
+
+def test_exact_kernel_squared_closed_form():
+    rng = np.random.default_rng(3)
+    d = 3
+    Q = rng.standard_normal((4, d))
+    K = rng.standard_normal((5, d))
+    th = _selection_theta(d, 2)
+    got = O.featmap(Q, th, square=True) @ O.featmap(K, th, square=True).T
+    np.testing.assert_allclose(got, ((Q * Q) @ (K * K).T) ** 2, rtol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# P-3: special cases named on the pages (Flatten, BASED); P-9: p = 1
+# --------------------------------------------------------------------------
+def test_shared_theta_is_elementwise_power():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((6, 4))
+    T1 = rng.standard_normal((4, 5))
+    for p in (2, 3, 4):
+        th = np.stack([T1[None]] * p)  # [p, 1, d, m], all Theta_j equal
+        np.testing.assert_allclose(O.featmap(X, th), (X @ T1) ** p, rtol=1e-12)
+
+
+def test_based_special_case():
+    """BASED: phi(x) = vec((Wx)(Wx)^T) with W in R^{m' x d}: Theta_1 column
+    (a,b) = W_a, Theta_2 column (a,b) = W_b."""
+    rng = np.random.default_rng(5)
+    d, mp = 4, 3
+    W = rng.standard_normal((mp, d))
+    X = rng.standard_normal((5, d))
+    th = np.zeros((2, 1, d, mp * mp))
+    for a in range(mp):
+        for b in range(mp):
+            th[0, 0, :, a * mp + b] = W[a]
+            th[1, 0, :, a * mp + b] = W[b]
+    want = np.array([np.outer(W @ x, W @ x).ravel() for x in X])
+    np.testing.assert_allclose(O.featmap(X, th), want, rtol=1e-12)
+
+
+def test_degree_one_is_plain_linear_map():
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((5, 4))
+    th = _rand_theta(rng, 1, 3, 4, 6)
+    np.testing.assert_allclose(O.featmap(X, th), X @ th[0].sum(axis=0), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P-4: Eckart-Young floor and Theorem 3.1's tightness
+# --------------------------------------------------------------------------
+def test_eckart_young_floor_bounds_any_sketch():
+    rng = np.random.default_rng(8)
+    d, p, m, n = 3, 2, 4, 12
+    Q = rng.standard_normal((n, d))
+    K = rng.standard_normal((n, d))
+    floor = O.eckart_young_floor(Q, K, p, m)
+    A = O.poly_kernel(Q, K, p)
+    assert floor > 0
+    for trial in range(20):
+        tq = _rand_theta(rng, p, 2, d, m)
+        tk = _rand_theta(rng, p, 2, d, m)
+        err = np.sum((O.featmap(Q, tq) @ O.featmap(K, tk).T - A) ** 2)
+        assert err >= floor * (1 - 1e-12)
+    # m at least the rank of A (<= dim of psi_2 span = 6) -> floor vanishes
+    assert O.eckart_young_floor(Q, K, p, 6) < 1e-18 * np.sum(A ** 2)
+    # m = 0 -> the floor is all of ||A||_F^2
+    np.testing.assert_allclose(O.eckart_young_floor(Q, K, p, 0), np.sum(A ** 2), rtol=1e-12)
+
+
+def test_theorem_3_1_linear_sketch_reaches_floor():
+    rng = np.random.default_rng(9)
+    d, p, m, n = 3, 2, 3, 10
+    Q = rng.standard_normal((n, d))
+    K = rng.standard_normal((n, d))
+    W1, W2 = O.optimal_linear_sketch(Q, K, p, m)
+    A = O.poly_kernel(Q, K, p)
+    err = np.sum(((O.psi(Q, p) @ W1) @ (O.psi(K, p) @ W2).T - A) ** 2)
+    np.testing.assert_allclose(err, O.eckart_young_floor(Q, K, p, m), rtol=1e-8)
+
+
+# --------------------------------------------------------------------------
+# P-5..P-8: attention forms
+# --------------------------------------------------------------------------
+def _brute_attention(Q, K, V, tq, tk, square, normalize, delta, causal):
+    """Per-row loops with the kernel taken from the explicit sketch
+    <psi_p(q) W_q, psi_p(k) W_k> (no featmap, no matrix associativity)."""
+    p = tq.shape[0]
+    fq = O.psi(Q, p) @ O.w_hat(tq)
+    fk = O.psi(K, p) @ O.w_hat(tk)
+    if square:
+        fq, fk = fq * fq, fk * fk
+    n, dv = V.shape
+    out = np.zeros((n, dv))
+    for i in range(n):
+        num = np.zeros(dv)
+        den = 0.0
+        for j in range(n):
+            if causal and j > i:
+                continue
+            w = float(sum(fq[i, a] * fk[j, a] for a in range(fq.shape[1])))
+            num += w * V[j]
+            den += w
+        out[i] = num / (den + delta) if normalize else num
+    return out
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, True), (False, True)])
+def test_noncausal_vs_bruteforce(square, normalize):
+    rng = np.random.default_rng(10)
+    n, d, dv, p, t, m = 9, 3, 2, 2, 2, 4
+    Q, K = rng.standard_normal((2, n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    got = O.linattn(Q, K, V, tq, tk, square=square, normalize=normalize, delta=0.3)
+    want = _brute_attention(Q, K, V, tq, tk, square, normalize, 0.3, causal=False)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, True)])
+@pytest.mark.parametrize("chunk", [1, 4, 7, 16])
+def test_causal_chunked_vs_bruteforce(square, normalize, chunk):
+    rng = np.random.default_rng(11)
+    n, d, dv, p, t, m = 13, 3, 2, 3, 2, 4
+    Q, K = rng.standard_normal((2, n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    got, S, z = O.causal_chunked(Q, K, V, tq, tk, square=square, normalize=normalize,
+                                 delta=0.2, chunk=chunk)
+    want = _brute_attention(Q, K, V, tq, tk, square, normalize, 0.2, causal=True)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    quad = O.causal_quadratic(Q, K, V, tq, tk, square=square, normalize=normalize, delta=0.2)
+    np.testing.assert_allclose(got, quad, rtol=1e-10, atol=1e-12)
+    S_ref, z_ref = O.state_from_prefix(K, V, tk, square=square)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(z, z_ref, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_golden_exact_kernel():
+    g = _golden("exact_kernel_attention_d2.json")
+    q, k, v = (np.array(g[x], float) for x in ("q", "k", "v"))
+    th = _selection_theta(2, 2)
+    dl = g["delta"]
+    out, _, _ = O.causal_chunked(q, k, v, th, th, normalize=True, delta=dl, chunk=2)
+    np.testing.assert_allclose(out, g["causal_normalized"], rtol=1e-14)
+    out, _, _ = O.causal_chunked(q, k, v, th, th, chunk=2)
+    np.testing.assert_allclose(out, g["causal_raw"], rtol=1e-14)
+    np.testing.assert_allclose(O.linattn(q, k, v, th, th, normalize=True, delta=dl),
+                               g["noncausal_normalized"], rtol=1e-14)
+    out, _, _ = O.causal_chunked(q, k, v, th, th, square=True, normalize=True, delta=dl,
+                                 chunk=3)
+    np.testing.assert_allclose(out, g["causal_squared_normalized"], rtol=1e-14)
+    # decode from an empty state walks the same rows
+    outs, _, _ = O.decode(np.zeros((4, 2)), np.zeros(4), q, k, v, th, th,
+                          normalize=True, delta=dl)
+    np.testing.assert_allclose(outs, g["causal_normalized"], rtol=1e-14)
+
+
+def test_state_continuation_and_decode_match_prefill():
+    rng = np.random.default_rng(12)
+    n, d, dv, p, t, m = 20, 4, 3, 2, 2, 5
+    Q, K = rng.standard_normal((2, n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    kw = dict(square=True, normalize=True, delta=1e-3)
+    full, S, z = O.causal_chunked(Q, K, V, tq, tk, chunk=4, **kw)
+    a, S1, z1 = O.causal_chunked(Q[:11], K[:11], V[:11], tq, tk, chunk=3, **kw)
+    b, S2, z2 = O.causal_chunked(Q[11:], K[11:], V[11:], tq, tk, chunk=5, S0=S1, z0=z1, **kw)
+    np.testing.assert_allclose(np.vstack([a, b]), full, rtol=1e-11)
+    np.testing.assert_allclose(S2, S, rtol=1e-11)
+    np.testing.assert_allclose(z2, z, rtol=1e-11)
+    outs, Sd, zd = O.decode(S1, z1, Q[11:], K[11:], V[11:], tq, tk, **kw)
+    np.testing.assert_allclose(outs, full[11:], rtol=1e-11)
+    np.testing.assert_allclose(Sd, S, rtol=1e-11)
+
+
+def test_normaliser_with_unit_values():
+    """V = 1: out_i = den0_i / (den0_i + delta) where den0 is the weight sum."""
+    rng = np.random.default_rng(13)
+    n, d, p, t, m = 10, 3, 2, 2, 4
+    Q, K = rng.standard_normal((2, n, d))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    ones = np.ones((n, 1))
+    raw, _, _ = O.causal_chunked(Q, K, ones, tq, tk, square=True, chunk=4)
+    out, _, _ = O.causal_chunked(Q, K, ones, tq, tk, square=True, normalize=True,
+                                 delta=0.05, chunk=4)
+    np.testing.assert_allclose(out, raw / (raw + 0.05), rtol=1e-12)
+
+
+def test_normalised_output_is_convex_combination():
+    rng = np.random.default_rng(14)
+    n, d, dv, p, t, m = 15, 3, 4, 2, 3, 6
+    Q, K = rng.standard_normal((2, n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    out, _, _ = O.causal_chunked(Q, K, V, tq, tk, square=True, normalize=True, delta=0.0,
+                                 chunk=4)
+    for i in range(n):
+        lo, hi = V[: i + 1].min(axis=0), V[: i + 1].max(axis=0)
+        assert np.all(out[i] >= lo - 1e-12) and np.all(out[i] <= hi + 1e-12)
+    np.testing.assert_allclose(out[0], V[0], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P-10: ordering conventions do not matter
+# --------------------------------------------------------------------------
+def test_symmetries():
+    rng = np.random.default_rng(15)
+    n, d, dv, p, t, m = 8, 3, 2, 3, 3, 5
+    Q, K = rng.standard_normal((2, n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = _rand_theta(rng, p, t, d, m), _rand_theta(rng, p, t, d, m)
+    base = O.featmap(Q, tq, square=True)
+    np.testing.assert_allclose(O.featmap(Q, tq[:, ::-1], square=True), base, rtol=1e-12)
+    np.testing.assert_allclose(O.featmap(Q, tq[[2, 0, 1]], square=True), base, rtol=1e-12)
+    perm = rng.permutation(m)
+    out, _, _ = O.causal_chunked(Q, K, V, tq, tk, square=True, normalize=True, chunk=3)
+    outp, _, _ = O.causal_chunked(Q, K, V, tq[..., perm], tk[..., perm], square=True,
+                                  normalize=True, chunk=3)
+    np.testing.assert_allclose(outp, out, rtol=1e-12)
+
+
+def test_batched_wrappers_use_per_head_theta():
+    rng = np.random.default_rng(16)
+    B, H, n, d, dv, p, t, m = 2, 3, 6, 3, 2, 2, 2, 4
+    Q, K = rng.standard_normal((2, B, H, n, d))
+    V = rng.standard_normal((B, H, n, dv))
+    tq = rng.standard_normal((H, p, t, d, m))
+    tk = rng.standard_normal((H, p, t, d, m))
+    out, S, z = O.causal_bh(Q, K, V, tq, tk, chunk=4, normalize=True, delta=0.1)
+    for b in range(B):
+        for h in range(H):
+            want = O.causal_quadratic(Q[b, h], K[b, h], V[b, h], tq[h], tk[h],
+                                      normalize=True, delta=0.1)
+            np.testing.assert_allclose(out[b, h], want, rtol=1e-11)
+    shared = O.featmap_bh(Q, tq[1])
+    np.testing.assert_allclose(shared[1, 2], O.featmap(Q[1, 2], tq[1]), rtol=1e-14)
