@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""LLoPS hot-path benchmark on one MI355X.
+
+Default: the causal forward at n=65536, p=2, t=4, m=256 (batch 1, 32 heads,
+d=dv=128, bf16 inputs, fp32 accumulation/outputs, squared features,
+normaliser delta=1e-6) -- one step is one full llops_linattn_causal_fwd call
+(feature maps of Q and K, segment states, scan, chunked output pass) over the
+whole batch, inputs resident in HBM. Prints ONE JSON line.
+
+The line also carries:
+  roofline      dominant kernel (the bf16 MFMA feature map) against the bf16
+                dense MFMA peak, its duration timed live with HIP events;
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
+  decode        the single-token decode step (batch 128, 32 heads, 1000
+                consecutive steps from a 4096-token prefix state) against HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="causal_long_n65536")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU budget of the oracle baseline")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (per call, whole batch)
+# ---------------------------------------------------------------------------
+def featmap_flops(w, n_rows):
+    """2 * rows * d * (p*t*m) per projected tensor (the p*t products X Theta)."""
+    return 2.0 * n_rows * w.d * w.p * w.t * w.m
+
+
+def causal_flops(w):
+    """Feature maps of Q and K, state build phi_K^T V and read-out phi_Q S, and
+    the lower triangle (diagonal included) of the intra-chunk products, with
+    the workload's chunk length; normaliser and epilogue terms excluded."""
+    bh = w.batch * w.heads
+    per_bh = (4.0 * w.n * w.d * w.p * w.t * w.m + 4.0 * w.n * w.m * w.dv
+              + w.n * (w.chunk + 1) * (w.m + w.dv))
+    return bh * per_bh
+
+
+def decode_bytes(w):
+    """HBM bytes one decode step must move: fp32 state S and normaliser z read
+    and written, Theta_q/Theta_k read, q/k/v read (bf16), output written."""
+    bh = w.batch * w.heads
+    return (2 * bh * w.m * w.dv * 4 + 2 * bh * w.m * 4 + 2 * w.heads * w.p * w.t * w.d * w.m * 2
+            + bh * (2 * w.d + w.dv) * 2 + bh * w.dv * 4)
+
+
+def decode_state_bytes(w):
+    """Bytes the decode state kernel must move per launch: S and z read and
+    written, phi_q/phi_k (fp32) and v read, output written."""
+    bh = w.batch * w.heads
+    return 2 * bh * w.m * w.dv * 4 + 2 * bh * w.m * 4 + 2 * bh * w.m * 4 + bh * w.dv * 2 \
+        + bh * w.dv * 4
+
+
+# ---------------------------------------------------------------------------
+def to_dev(a, torch, dtype):
+    return torch.from_numpy(a).to("cuda").to(dtype)
+
+
+def bench_causal(w, steps, warmup, torch, lib):
+    from learnable_polynomial_feature_amd.workloads import generate
+    log(f"generating {w.name} inputs")
+    x = generate(w)
+    g = {k: to_dev(v, torch, torch.bfloat16) for k, v in x.items()}
+    del x
+    out = torch.empty((w.batch, w.heads, w.n, w.dv), dtype=torch.float32, device="cuda")
+    shape = lib.make_shape(batch=w.batch, heads=w.heads, n=w.n, d=w.d, dv=w.dv, m=w.m, p=w.p,
+                           t=w.t, square=w.square, normalize=w.normalize, delta=w.delta,
+                           chunk=w.chunk)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_CAUSAL), dtype=torch.uint8,
+                     device="cuda")
+    args = (g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"])
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta, chunk=w.chunk, out=out,
+              workspace=ws)
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        lib.llops_linattn_causal_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    timer = lib.KernelTimer(capacity=16 * steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {steps} steps")
+    torch.cuda.synchronize()
+    with timer:
+        t0.record()
+        for _ in range(steps):
+            lib.llops_linattn_causal_fwd(*args, **kw)
+        t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    return ms, kern
+
+
+def bench_decode(w, steps, torch, lib):
+    """Prefix state from the GPU causal pass (untimed), then `steps` decode steps."""
+    from learnable_polynomial_feature_amd.workloads import decode_prefix, decode_tokens, generate
+    B, H, m, dv = w.batch, w.heads, w.m, w.dv
+    th = generate(w.replace(n=1, batch=1))
+    gq, gk = to_dev(th["theta_q"], torch, torch.bfloat16), to_dev(th["theta_k"], torch,
+                                                                   torch.bfloat16)
+    S = torch.empty((B, H, m, dv), dtype=torch.float32, device="cuda")
+    z = torch.empty((B, H, m), dtype=torch.float32, device="cuda")
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
+    rows = 16
+    log(f"decode: building the {w.prefix}-token prefix state")
+    for b0 in range(0, B, rows):
+        pre = decode_prefix(w, batches=list(range(b0, min(B, b0 + rows))))
+        Kp = to_dev(pre["K_pre"], torch, torch.bfloat16)
+        Vp = to_dev(pre["V_pre"], torch, torch.bfloat16)
+        del pre
+        lib.llops_linattn_causal_fwd(Kp, Kp, Vp, gq, gk, chunk=w.chunk, S_final=S[b0:b0 + rows],
+                                     z_final=z[b0:b0 + rows], **kw)
+        torch.cuda.synchronize()
+        del Kp, Vp
+    log(f"decode: generating {steps} steps of tokens")
+    tok = decode_tokens(w, steps)
+    q = to_dev(tok["q"], torch, torch.bfloat16)
+    k = to_dev(tok["k"], torch, torch.bfloat16)
+    v = to_dev(tok["v"], torch, torch.bfloat16)
+    del tok
+    out = torch.empty((B, H, dv), dtype=torch.float32, device="cuda")
+    shape = lib.make_shape(batch=B, heads=H, n=1, d=w.d, dv=dv, m=m, p=w.p, t=w.t,
+                           square=w.square, normalize=w.normalize, delta=w.delta)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_DECODE), dtype=torch.uint8,
+                     device="cuda")
+    S_init, z_init = S.clone(), z.clone()
+    for s in range(3):  # warmup, then restore the prefix state
+        lib.llops_decode_step(q[s], k[s], v[s], gq, gk, S, z, out=out, workspace=ws, **kw)
+    S.copy_(S_init)
+    z.copy_(z_init)
+    del S_init, z_init
+    torch.cuda.synchronize()
+    timer = lib.KernelTimer(capacity=4 * steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    log(f"decode: timing {steps} steps")
+    with timer:
+        t0.record()
+        for s in range(steps):
+            lib.llops_decode_step(q[s], k[s], v[s], gq, gk, S, z, out=out, workspace=ws, **kw)
+        t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kern = {kk: sum(vv) / len(vv) for kk, vv in timer.durations_ms().items()}
+    return ms, kern
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, as it stands, on whole heads of the same workload."""
+    import numpy as np  # noqa: F401
+    from oracle import llops_oracle as O
+    from learnable_polynomial_feature_amd.workloads import qk_slice, theta_head, v_slice
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    done, elapsed = 0, 0.0
+    while done < w.heads and (elapsed < budget_s * 0.5 or done == 0):
+        h = done
+        q, k, v = qk_slice(w, "q", 0, h), qk_slice(w, "k", 0, h), v_slice(w, 0, h)
+        tq, tk = theta_head(w, "q", h), theta_head(w, "k", h)
+        t = time.perf_counter()
+        O.causal_chunked(q, k, v, tq, tk, square=w.square, normalize=w.normalize, delta=w.delta,
+                         chunk=w.chunk)
+        elapsed += time.perf_counter() - t
+        done += 1
+    per_head = elapsed / done
+    full_step = per_head * w.batch * w.heads
+    return {"value": w.batch * w.n / full_step, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.heads} (batch, head) sequences at full length "
+                      f"({w.n} tokens each), fp64 numpy oracle, {elapsed:.1f} s; full-step time "
+                      f"extrapolated x{w.batch * w.heads}/{done}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from learnable_polynomial_feature_amd import _lib as lib
+    from learnable_polynomial_feature_amd.workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib.library()
+    w = WORKLOADS[args.workload]
+    if w.steps:
+        raise SystemExit("use the default causal workload; decode is reported in the same line")
+
+    ms, kern = bench_causal(w, args.steps, args.warmup, torch, lib)
+    tokens = w.batch * w.n
+    flops = causal_flops(w)
+    feat_ms = kern.get("featmap_bf16")
+    feat_flops = featmap_flops(w, 2 * w.batch * w.heads * w.n)  # Q and K in one launch
+    roofline = None
+    if feat_ms:
+        ach = feat_flops / (feat_ms * 1e-3) / 1e12
+        roofline = {"kernel": "featmap_bf16", "bound": "mfma", "achieved": round(ach, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_ms": round(feat_ms, 4), "flops_per_launch": feat_flops}
+    line = {
+        "metric": "causal LLoPS fwd tokens/sec at n=65536,p=2,t=4,m=256; % MFMA peak; decode GB/s",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
+                   "dv": w.dv, "p": w.p, "t": w.t, "m": w.m, "chunk": w.chunk,
+                   "square": w.square, "normalize": w.normalize, "delta": w.delta,
+                   "parallelism": "single-gpu"},
+        "mfma_frac_step": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": roofline,
+    }
+    if not args.no_decode:
+        wd = WORKLOADS["decode_b128_h32"]
+        dms, dkern = bench_decode(wd, args.decode_steps, torch, lib)
+        gb = decode_bytes(wd) / (dms * 1e-3) / 1e9
+        st_ms = dkern.get("decode_state")
+        st_gb = decode_state_bytes(wd) / (st_ms * 1e-3) / 1e9 if st_ms else None
+        line["decode"] = {
+            "workload": wd.name, "steps": args.decode_steps, "ms_per_step": round(dms, 4),
+            "tokens_per_s": round(wd.batch / (dms * 1e-3), 1),
+            "GBps": round(gb, 1), "hbm_frac": round(gb / PEAK_HBM_GBPS, 4),
+            "kernel_ms": {k: round(v, 4) for k, v in dkern.items()},
+            "roofline": None if st_gb is None else {
+                "kernel": "decode_state", "bound": "hbm", "achieved": round(st_gb, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(st_gb / PEAK_HBM_GBPS, 4),
+                "traffic": None, "bytes_per_launch": decode_state_bytes(wd)},
+        }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * llops.h -- C ABI of the MI355X (gfx950) LLoPS linear-attention library.
+ *
+ * LLoPS ("Learnable Low-Rank Polynomial Sketch for Effective Linear
+ * Attention", arXiv 2610.14219) replaces the exact degree-p monomial map
+ * psi_p(x) = vec(x^{(x)p}) by the CP-factorised sketch
+ *     phi(X) = sum_{r=1..t} prod_{j=1..p} X Theta_{j,r},   Theta_{j,r} in R^{d x m}
+ * (papernotes.org notes, key design 2: psi_p(Q) W_hat = sum_r prod_j Q Theta_{j,r}),
+ * optionally squared element-wise after the r-sum for non-negative weights
+ * (notes, training strategy; paper Sec. 3 non-negativity paragraph), and
+ * uses it in linear attention phi_Q(Q) (phi_K(K)^T V) (notes, overall
+ * framework; paper Sec. 1 associativity).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, frees nothing and keeps no pointer after returning.
+ *  - Tensors are dense row-major:
+ *        X, Q, K       [batch][heads][n][d]
+ *        V             [batch][heads][n][dv]
+ *        phi           [batch][heads][n][m]
+ *        out           [batch][heads][n][dv]
+ *        Theta         [heads][p][t][d][m] if theta_per_head, else [p][t][d][m];
+ *                      Theta[..][j][r][:, i] is column i of Theta_{j+1,r+1}
+ *        S             [batch][heads][m][dv]   (fp32 always)
+ *        z             [batch][heads][m]       (fp32 always)
+ *  - in_dtype applies to X/Q/K/V/Theta; out_dtype to phi/out. Supported:
+ *        in BF16 -> MFMA path (bf16 products, fp32 accumulation);
+ *        in F32  -> fp32 path (fp32 products and accumulation).
+ *        out F32 everywhere; out BF16 for llops_featmap only.
+ *  - Normaliser (normalize = 1): out_i = num_i / (phi_Q(q_i) . z_i + delta),
+ *    delta added once per row after the dot product (the +delta stabiliser of
+ *    the SLAY notes, key design 3; Performer's numerator/denominator form in
+ *    the low-rank-attention blog). normalize = 0 returns num_i.
+ *  - Causal mask is inclusive: key j reaches query i iff j <= i.
+ *  - Calls are asynchronous on `stream` and perform no host synchronisation.
+ *    Validation happens before any launch; on an error nothing is launched and
+ *    nothing is written. Device faults surface at the caller's next sync.
+ *  - n = 0 (or batch*heads = 0) is a successful no-op (state outputs are still
+ *    written as S0/z0, or zeros, by the causal entry point); pointers to
+ *    tensors with no elements may then be null.
+ *  - Thread safety: calls hold no shared mutable state; concurrent calls on
+ *    different streams with disjoint buffers are safe. llops_last_error() is
+ *    per thread.
+ */
+#ifndef LLOPS_H
+#define LLOPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LLOPS_F32 = 0, LLOPS_BF16 = 1 } llops_dtype_t;
+
+typedef enum {
+  LLOPS_OK = 0,
+  LLOPS_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad enum, bad delta */
+  LLOPS_ERR_UNSUPPORTED = 2,  /* valid request with no kernel for its shape */
+  LLOPS_ERR_WORKSPACE = 3,    /* ws_bytes smaller than llops_workspace_bytes() */
+  LLOPS_ERR_HIP = 4           /* a HIP launch or query failed */
+} llops_status_t;
+
+typedef enum {
+  LLOPS_ENTRY_FEATMAP = 0,
+  LLOPS_ENTRY_LINATTN = 1,
+  LLOPS_ENTRY_CAUSAL = 2,
+  LLOPS_ENTRY_DECODE = 3
+} llops_entry_t;
+
+typedef struct llops_shape {
+  int64_t batch, heads, n;  /* n: tokens per sequence (ignored by decode) */
+  int32_t d, dv, m, p, t;   /* head dim, value dim, features, degree, CP rank */
+  int32_t square;           /* 0|1: phi <- phi * phi after the sum over r    */
+  int32_t normalize;        /* 0|1: divide by phi_Q . z + delta              */
+  float delta;              /* >= 0 and finite when normalize = 1            */
+  int32_t chunk;            /* causal block length hint: 0 (default), 16, 32,
+                               64 or 128; changes rounding order, not math   */
+  int32_t theta_per_head;   /* 1: Theta [heads][p][t][d][m]; 0: shared      */
+  int32_t in_dtype;         /* llops_dtype_t                                 */
+  int32_t out_dtype;        /* llops_dtype_t                                 */
+} llops_shape_t;
+
+/* Size limits checked by validation (else LLOPS_ERR_UNSUPPORTED):
+ *   1 <= p <= 8, 1 <= t <= 64, 1 <= d <= 256, 1 <= dv <= 256, 1 <= m <= 1024;
+ *   BF16 in additionally needs d % 16 == 0, m % 16 == 0, dv % 16 == 0 and
+ *   p * d <= 1024; the causal/linattn BF16 path needs m <= 256, dv <= 128.
+ */
+
+/* Bytes of scratch `ws` the entry point needs for this shape (0 if none). */
+size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry);
+
+/*
+ * llops_featmap -- phi = sum_r prod_j X Theta_{j,r}  [squared if shape->square]
+ * (notes, key design 2; paper Sec. 3: p*t projections, Hadamard product over
+ * j, sum over r). X [batch][heads][n][d] (in_dtype), Theta per the layout
+ * above (in_dtype), phi [batch][heads][n][m] (out_dtype). normalize, delta,
+ * dv and chunk are ignored. No workspace.
+ */
+llops_status_t llops_featmap(const llops_shape_t* shape, const void* X,
+                             const void* theta, void* phi, hipStream_t stream);
+
+/*
+ * llops_linattn_fwd -- non-causal linear attention
+ *   out = phi_Q(Q) (phi_K(K)^T V)  [ / (phi_Q(Q) (phi_K(K)^T 1) + delta) ]
+ * (notes, overall framework; paper Sec. 1; blog, Performer section).
+ * Q, K, V, theta_q, theta_k in in_dtype; out fp32 [batch][heads][n][dv].
+ * theta_q may equal theta_k. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_LINATTN).
+ */
+llops_status_t llops_linattn_fwd(const llops_shape_t* shape, const void* Q,
+                                 const void* K, const void* V,
+                                 const void* theta_q, const void* theta_k,
+                                 void* out, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
+ * llops_linattn_causal_fwd -- causal linear attention over a prefix state
+ *   out_i = (phi_Q(q_i) S_i) [ / (phi_Q(q_i) z_i + delta) ],
+ *   S_i = S0 + sum_{j<=i} phi_K(k_j) v_j^T,  z_i = z0 + sum_{j<=i} phi_K(k_j)
+ * (paper Sec. 1: streaming form with a constant-size state; blog: causal
+ * masking by incremental cumulative sums). S0/z0 (fp32, nullable = zeros)
+ * continue an earlier call; S_final/z_final (fp32, nullable) receive the state
+ * after the last token, so prefill(n1) then prefill(n2, S0=S_final) equals
+ * prefill(n1+n2). S0/z0 may alias S_final/z_final.
+ * ws: llops_workspace_bytes(shape, LLOPS_ENTRY_CAUSAL).
+ */
+llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* Q,
+                                        const void* K, const void* V,
+                                        const void* theta_q, const void* theta_k,
+                                        const float* S0, const float* z0,
+                                        void* out, float* S_final, float* z_final,
+                                        void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/*
+ * llops_decode_step -- one new token per (batch, head) on the recurrent state:
+ *   S += phi_K(k) v^T;  z += phi_K(k);  out = phi_Q(q)^T S [ / (phi_Q(q)^T z + delta) ]
+ * (paper Sec. 1: recurrent memory state; the update precedes the read, which
+ * matches the inclusive causal mask). q, k [batch][heads][d], v
+ * [batch][heads][dv] (in_dtype); S [batch][heads][m][dv] and z
+ * [batch][heads][m] fp32, updated in place; out fp32 [batch][heads][dv].
+ * shape->n is ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_DECODE).
+ */
+llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
+                                 const void* k, const void* v,
+                                 const void* theta_q, const void* theta_k,
+                                 float* S, float* z, void* out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Diagnostics: kernel-level timing. While armed on the calling thread, each
+ * kernel launch made by the library on behalf of that thread records
+ * events[2*i] just before and events[2*i+1] just after it on the launch
+ * stream, and stores the kernel's static name in names[i] (names may be
+ * null), for the first `capacity` launches. The caller creates and owns the
+ * 2*capacity events and reads them with hipEventElapsedTime after syncing.
+ * llops_profile_disarm() stops recording and returns the launches recorded.
+ * Arming adds two event records per launch and changes nothing else.
+ */
+llops_status_t llops_profile_arm(hipEvent_t* events, const char** names, int32_t capacity);
+int32_t llops_profile_disarm(void);
+
+/* Static description of a status code. */
+const char* llops_status_str(llops_status_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* llops_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLOPS_H */

@@ -1,0 +1,291 @@
+"""ctypes binding of libllops.so (C ABI in include/llops.h).
+
+Argument marshalling only: tensors are checked for device, dtype and shape,
+made contiguous, and their data pointers are handed to the C entry points
+together with torch's current HIP stream. Every step of the computation runs
+in the library's HIP kernels; if the library is missing the calls raise.
+PyTorch provides device memory and streams and nothing else here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libllops.so")
+
+F32, BF16 = 0, 1
+ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE = 0, 1, 2, 3
+STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
+          3: "LLOPS_ERR_WORKSPACE", 4: "LLOPS_ERR_HIP"}
+EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_linattn_fwd",
+           "llops_linattn_causal_fwd", "llops_decode_step", "llops_status_str",
+           "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
+
+
+class LlopsError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    """Mirror of llops_shape_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("n", ctypes.c_int64),
+        ("d", ctypes.c_int32), ("dv", ctypes.c_int32), ("m", ctypes.c_int32),
+        ("p", ctypes.c_int32), ("t", ctypes.c_int32),
+        ("square", ctypes.c_int32), ("normalize", ctypes.c_int32), ("delta", ctypes.c_float),
+        ("chunk", ctypes.c_int32), ("theta_per_head", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+
+
+def library(path: str | None = None) -> ctypes.CDLL:
+    """Load libllops.so once (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise LlopsError(-1, f"{path} not found; run learnable_polynomial_feature_amd.build")
+    lib = ctypes.CDLL(path)
+    SP = ctypes.POINTER(Shape)
+    lib.llops_workspace_bytes.argtypes = [SP, ctypes.c_int32]
+    lib.llops_workspace_bytes.restype = ctypes.c_size_t
+    lib.llops_featmap.argtypes = [SP, _P, _P, _P, _P]
+    lib.llops_featmap.restype = ctypes.c_int
+    lib.llops_linattn_fwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.llops_linattn_fwd.restype = ctypes.c_int
+    lib.llops_linattn_causal_fwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]
+    lib.llops_linattn_causal_fwd.restype = ctypes.c_int
+    lib.llops_decode_step.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.llops_decode_step.restype = ctypes.c_int
+    lib.llops_status_str.argtypes = [ctypes.c_int]
+    lib.llops_status_str.restype = ctypes.c_char_p
+    lib.llops_last_error.argtypes = []
+    lib.llops_last_error.restype = ctypes.c_char_p
+    lib.llops_profile_arm.argtypes = [_P, _P, ctypes.c_int32]
+    lib.llops_profile_arm.restype = ctypes.c_int
+    lib.llops_profile_disarm.argtypes = []
+    lib.llops_profile_disarm.restype = ctypes.c_int32
+    _LIB = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.contiguous()
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise LlopsError(status, library().llops_last_error().decode())
+
+
+def _theta_dims(theta: torch.Tensor, heads: int):
+    if theta.dim() == 5:
+        if theta.shape[0] != heads:
+            raise ValueError(f"theta has {theta.shape[0]} heads, inputs have {heads}")
+        return (*theta.shape[1:],), 1
+    if theta.dim() == 4:
+        return tuple(theta.shape), 0
+    raise ValueError("theta must be [heads, p, t, d, m] or [p, t, d, m]")
+
+
+def make_shape(*, batch, heads, n, d, dv, m, p, t, square=False, normalize=False, delta=0.0,
+               chunk=0, theta_per_head=1, in_dtype=BF16, out_dtype=F32) -> Shape:
+    return Shape(batch, heads, n, d, dv, m, p, t, int(square), int(normalize),
+                 float(delta), int(chunk), int(theta_per_head), int(in_dtype), int(out_dtype))
+
+
+def llops_workspace_bytes(shape: Shape, entry: int) -> int:
+    return int(library().llops_workspace_bytes(ctypes.byref(shape), int(entry)))
+
+
+def _workspace(shape: Shape, entry: int, device, ws):
+    need = llops_workspace_bytes(shape, entry)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------------------
+def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32):
+    """phi = sum_r prod_j X Theta_{j,r} [squared]; X [B, H, n, d] -> phi [B, H, n, m]."""
+    X = _dev(X, "X")
+    theta = _dev(theta, "theta")
+    if X.dim() != 4:
+        raise ValueError("X must be [batch, heads, n, d]")
+    B, H, n, d = X.shape
+    (p, t, td, m), per_head = _theta_dims(theta, H)
+    if td != d or theta.dtype != X.dtype:
+        raise ValueError("theta's d and dtype must match X")
+    odt = BF16 if out_dtype == torch.bfloat16 else F32
+    if out is None:
+        out = torch.empty((B, H, n, m), dtype=out_dtype, device=X.device)
+    shape = make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=square,
+                       theta_per_head=per_head, in_dtype=_dt(X), out_dtype=odt)
+    lib = library()
+    _check(lib.llops_featmap(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(out), _stream(X)))
+    return out
+
+
+def _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk):
+    if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
+        raise ValueError("Q, K must be [B, H, n, d] and V [B, H, n, dv]")
+    B, H, n, d = Q.shape
+    dq, ph = _theta_dims(theta_q, H)
+    dk, phk = _theta_dims(theta_k, H)
+    if dq != dk or ph != phk:
+        raise ValueError("theta_q and theta_k must have the same shape")
+    p, t, td, m = dq
+    if td != d:
+        raise ValueError("theta's d must match Q")
+    dts = {x.dtype for x in (Q, K, V, theta_q, theta_k)}
+    if len(dts) != 1:
+        raise ValueError("Q, K, V and theta must share one dtype")
+    return make_shape(batch=B, heads=H, n=n, d=d, dv=V.shape[3], m=m, p=p, t=t, square=square,
+                      normalize=normalize, delta=delta, chunk=chunk, theta_per_head=ph,
+                      in_dtype=_dt(Q), out_dtype=F32)
+
+
+def llops_linattn_fwd(Q, K, V, theta_q, theta_k, *, square=False, normalize=False, delta=0.0,
+                      out=None, workspace=None):
+    """Non-causal: out = phi_Q (phi_K^T V) [/ (phi_Q (phi_K^T 1) + delta)] (fp32)."""
+    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
+    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
+    if out is None:
+        out = torch.empty(V.shape, dtype=torch.float32, device=Q.device)
+    ws, wsb = _workspace(shape, ENTRY_LINATTN, Q.device, workspace)
+    _check(library().llops_linattn_fwd(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V),
+                                       _ptr(theta_q), _ptr(theta_k), _ptr(out), _ptr(ws), wsb,
+                                       _stream(Q)))
+    return out
+
+
+def llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k, *, square=False, normalize=False,
+                             delta=0.0, chunk=0, S0=None, z0=None, out=None, S_final=None,
+                             z_final=None, return_state=False, workspace=None):
+    """Causal linear attention with optional initial/final recurrent state.
+
+    Returns out [B, H, n, dv] fp32, or (out, S_final, z_final) when return_state.
+    """
+    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
+    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk)
+    B, H = Q.shape[:2]
+    m, dv = shape.m, shape.dv
+    if S0 is not None:
+        S0 = _dev(S0, "S0")
+        if S0.shape != (B, H, m, dv) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be fp32 [B, H, m, dv]")
+    if z0 is not None:
+        z0 = _dev(z0, "z0")
+        if z0.shape != (B, H, m) or z0.dtype != torch.float32:
+            raise ValueError("z0 must be fp32 [B, H, m]")
+    for name, tt, shp in (("S_final", S_final, (B, H, m, dv)), ("z_final", z_final, (B, H, m))):
+        if tt is not None and (tt.shape != shp or tt.dtype != torch.float32
+                               or not tt.is_contiguous() or tt.device.type != "cuda"):
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape {shp}")
+    if return_state:
+        if S_final is None:
+            S_final = torch.empty((B, H, m, dv), dtype=torch.float32, device=Q.device)
+        if z_final is None:
+            z_final = torch.empty((B, H, m), dtype=torch.float32, device=Q.device)
+    if out is None:
+        out = torch.empty(V.shape, dtype=torch.float32, device=Q.device)
+    ws, wsb = _workspace(shape, ENTRY_CAUSAL, Q.device, workspace)
+    _check(library().llops_linattn_causal_fwd(
+        ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+        _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_final), _ptr(z_final), _ptr(ws), wsb,
+        _stream(Q)))
+    if return_state:
+        return out, S_final, z_final
+    return out
+
+
+def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normalize=True,
+                      delta=0.0, out=None, workspace=None):
+    """One token per (b, h): S, z updated in place; returns out [B, H, dv] fp32."""
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B, H, d] and v [B, H, dv]")
+    if not (S.is_contiguous() and z.is_contiguous()):
+        raise ValueError("S and z are updated in place and must be contiguous")
+    B, H, d = q.shape
+    dq, ph = _theta_dims(theta_q, H)
+    p, t, td, m = dq
+    dv = v.shape[2]
+    if S.shape != (B, H, m, dv) or z.shape != (B, H, m) or S.dtype != torch.float32 \
+            or z.dtype != torch.float32 or S.device.type != "cuda":
+        raise ValueError("S must be fp32 [B, H, m, dv] and z fp32 [B, H, m] on the device")
+    shape = make_shape(batch=B, heads=H, n=1, d=d, dv=dv, m=m, p=p, t=t, square=square,
+                       normalize=normalize, delta=delta, theta_per_head=ph, in_dtype=_dt(q),
+                       out_dtype=F32)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(shape, ENTRY_DECODE, q.device, workspace)
+    _check(library().llops_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(theta_q), _ptr(theta_k), _ptr(S), _ptr(z), _ptr(out),
+                                       _ptr(ws), wsb, _stream(q)))
+    return out
+
+
+class KernelTimer:
+    """Times every kernel the library launches inside a ``with`` block, with
+    HIP events recorded on the launch stream (llops_profile_arm)."""
+
+    def __init__(self, capacity: int = 4096):
+        self.capacity = capacity
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        self._ev = (ctypes.c_void_p * (2 * capacity))(
+            *[e.cuda_event for pair in self.events for e in pair])
+        self._names = (ctypes.c_char_p * capacity)()
+        self.records = []
+
+    def __enter__(self):
+        _check(library().llops_profile_arm(self._ev, self._names, self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        n = library().llops_profile_disarm()
+        self.records = [(self._names[i].decode(), self.events[i]) for i in range(n)]
+        return False
+
+    def durations_ms(self) -> dict:
+        """kernel name -> list of durations (ms); call after synchronising."""
+        out = {}
+        for name, (a, b) in self.records:
+            out.setdefault(name, []).append(a.elapsed_time(b))
+        return out

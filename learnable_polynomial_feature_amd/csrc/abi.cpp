@@ -1,0 +1,411 @@
+// C ABI of libllops: argument validation, workspace layout and kernel dispatch.
+// No allocation, no host synchronisation; every check runs before the first launch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "llops.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+llops_status_t fail(llops_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+llops_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(LLOPS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Sequence segmentation shared by the workspace size query and the launches.
+struct SegPlan {
+  int chunk;
+  int nseg;
+  int64_t seg_len;
+};
+
+SegPlan seg_plan(const llops_shape_t* s, bool causal) {
+  SegPlan p{};
+  const bool bf16 = s->in_dtype == LLOPS_BF16;
+  if (bf16) {
+    // bf16 MFMA blocks are 32 or 64 tokens (a 128-token block with m = 256
+    // does not fit the 160 KiB LDS of a CU); the chunk only orders rounding.
+    p.chunk = (causal && s->chunk > 0 && s->chunk <= 32) ? 32 : 64;
+  } else {
+    p.chunk = s->chunk > 0 ? s->chunk : 64;
+  }
+  const int64_t BH = s->batch * s->heads;
+  const int64_t n = s->n;
+  const int64_t target = bf16 ? 512 : 256;  // workgroups to aim for
+  int64_t nchunks = (n + p.chunk - 1) / p.chunk;
+  if (nchunks < 1) nchunks = 1;
+  int64_t want = BH > 0 ? (target + BH - 1) / BH : 1;
+  if (want < 1) want = 1;
+  int64_t nseg = want < nchunks ? want : nchunks;
+  int64_t chunks_per_seg = (nchunks + nseg - 1) / nseg;
+  p.seg_len = chunks_per_seg * p.chunk;
+  p.nseg = static_cast<int>((nchunks + chunks_per_seg - 1) / chunks_per_seg);
+  return p;
+}
+
+struct WsLayout {
+  size_t phiq, phik, seg, tot, total;
+};
+
+WsLayout ws_layout(const llops_shape_t* s, int entry) {
+  WsLayout w{};
+  const size_t esz = s->in_dtype == LLOPS_BF16 ? 2 : 4;
+  const size_t BH = static_cast<size_t>(s->batch * s->heads);
+  const size_t per = static_cast<size_t>(s->m) * s->dv + s->m;
+  size_t off = 0;
+  if (entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) {
+    const SegPlan sp = seg_plan(s, entry == LLOPS_ENTRY_CAUSAL);
+    const size_t phib = BH * static_cast<size_t>(s->n) * s->m * esz;
+    w.phiq = off;
+    off = round_up(off + phib, 256);
+    w.phik = off;
+    off = round_up(off + phib, 256);
+    w.seg = off;
+    off = round_up(off + BH * sp.nseg * per * sizeof(float), 256);
+    w.tot = off;
+    if (entry == LLOPS_ENTRY_LINATTN) off = round_up(off + BH * per * sizeof(float), 256);
+  } else if (entry == LLOPS_ENTRY_DECODE) {
+    const size_t phib = BH * s->m * sizeof(float);
+    w.phiq = off;
+    off = round_up(off + phib, 256);
+    w.phik = off;
+    off = round_up(off + phib, 256);
+  }
+  w.total = off;
+  return w;
+}
+
+bool is01(int32_t x) { return x == 0 || x == 1; }
+
+llops_status_t validate(const llops_shape_t* s, int entry) {
+  if (!s) return fail(LLOPS_ERR_INVALID_ARG, "shape is null");
+  if (s->batch < 0 || s->heads < 0) return fail(LLOPS_ERR_INVALID_ARG, "batch/heads < 0");
+  if (entry != LLOPS_ENTRY_DECODE && s->n < 0) return fail(LLOPS_ERR_INVALID_ARG, "n < 0");
+  if (s->d < 1 || s->m < 1 || s->p < 1 || s->t < 1)
+    return fail(LLOPS_ERR_INVALID_ARG, "d, m, p, t must be >= 1 (d=%d m=%d p=%d t=%d)", s->d,
+                s->m, s->p, s->t);
+  if (entry != LLOPS_ENTRY_FEATMAP && s->dv < 1)
+    return fail(LLOPS_ERR_INVALID_ARG, "dv must be >= 1");
+  if (!is01(s->in_dtype) || !is01(s->out_dtype))
+    return fail(LLOPS_ERR_INVALID_ARG, "bad dtype enum (in=%d out=%d)", s->in_dtype, s->out_dtype);
+  if (!is01(s->square) || !is01(s->normalize) || !is01(s->theta_per_head))
+    return fail(LLOPS_ERR_INVALID_ARG, "square/normalize/theta_per_head must be 0 or 1");
+  if (entry != LLOPS_ENTRY_FEATMAP && s->normalize && (!isfinite(s->delta) || s->delta < 0.f))
+    return fail(LLOPS_ERR_INVALID_ARG, "delta must be finite and >= 0");
+  if (!(s->chunk == 0 || s->chunk == 16 || s->chunk == 32 || s->chunk == 64 || s->chunk == 128))
+    return fail(LLOPS_ERR_INVALID_ARG, "chunk must be 0, 16, 32, 64 or 128 (got %d)", s->chunk);
+  if (s->p > 8 || s->t > 64 || s->d > 256 || s->m > 1024 ||
+      (entry != LLOPS_ENTRY_FEATMAP && s->dv > 256))
+    return fail(LLOPS_ERR_UNSUPPORTED, "size limits: p<=8, t<=64, d<=256, dv<=256, m<=1024");
+  if (s->heads > 65535) return fail(LLOPS_ERR_UNSUPPORTED, "heads > 65535");
+  if ((entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) && s->batch * s->heads > 65535)
+    return fail(LLOPS_ERR_UNSUPPORTED, "batch * heads > 65535");
+  // the feature map addresses the rows of one workgroup by 32-bit offsets
+  if (entry != LLOPS_ENTRY_DECODE && s->batch > 1 && s->heads * s->n >= (int64_t(1) << 30))
+    return fail(LLOPS_ERR_UNSUPPORTED, "batch > 1 with heads * n >= 2^30");
+  if (entry != LLOPS_ENTRY_FEATMAP && s->out_dtype != LLOPS_F32)
+    return fail(LLOPS_ERR_UNSUPPORTED, "attention outputs are fp32 only");
+  if (s->in_dtype == LLOPS_BF16) {
+    if (s->d % 16 || s->m % 16 || s->p * s->d > 1024)
+      return fail(LLOPS_ERR_UNSUPPORTED, "bf16 needs d %% 16 == 0, m %% 16 == 0, p*d <= 1024");
+    if (entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) {
+      if (s->m % 32 || s->m > 256 || s->dv % 16 || s->dv > 128)
+        return fail(LLOPS_ERR_UNSUPPORTED,
+                    "bf16 attention needs m %% 32 == 0, m <= 256, dv %% 16 == 0, dv <= 128");
+    }
+    if (entry == LLOPS_ENTRY_DECODE && s->dv % 4)
+      return fail(LLOPS_ERR_UNSUPPORTED, "bf16 decode needs dv %% 4 == 0");
+  }
+  return LLOPS_OK;
+}
+
+llops_status_t need(const void* p, const char* name) {
+  if (!p) return fail(LLOPS_ERR_INVALID_ARG, "%s is null", name);
+  if (!aligned16(p)) return fail(LLOPS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return LLOPS_OK;
+}
+
+llops_status_t opt(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(LLOPS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return LLOPS_OK;
+}
+
+#define LLOPS_TRY(expr)                        \
+  do {                                         \
+    const llops_status_t _st = (expr);         \
+    if (_st != LLOPS_OK) return _st;           \
+  } while (0)
+
+#define LLOPS_HIP(expr, what)                  \
+  do {                                         \
+    const hipError_t _e = (expr);              \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+llops::FeatShape feat_shape(const llops_shape_t* s, int64_t n, int out_bf16) {
+  llops::FeatShape f{};
+  f.B = s->batch;
+  f.H = s->heads;
+  f.n = n;
+  f.d = s->d;
+  f.m = s->m;
+  f.p = s->p;
+  f.t = s->t;
+  f.theta_per_head = s->theta_per_head;
+  f.square = s->square;
+  f.out_bf16 = out_bf16;
+  return f;
+}
+
+llops::AttnShape attn_shape(const llops_shape_t* s, bool causal) {
+  const SegPlan sp = seg_plan(s, causal);
+  llops::AttnShape a{};
+  a.BH = s->batch * s->heads;
+  a.n = s->n;
+  a.m = s->m;
+  a.dv = s->dv;
+  a.chunk = sp.chunk;
+  a.nseg = sp.nseg;
+  a.seg_len = sp.seg_len;
+  a.causal = causal ? 1 : 0;
+  a.normalize = s->normalize;
+  a.delta = s->normalize ? s->delta : 0.f;
+  return a;
+}
+
+// Shared body of the non-causal and causal forward passes.
+llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, const void* K,
+                         const void* V, const void* tq, const void* tk, const float* S0,
+                         const float* z0, void* out, float* S_final, float* z_final, void* ws,
+                         size_t ws_bytes, hipStream_t st) {
+  const int entry = causal ? LLOPS_ENTRY_CAUSAL : LLOPS_ENTRY_LINATTN;
+  LLOPS_TRY(validate(s, entry));
+  const int64_t BH = s->batch * s->heads;
+  if (BH == 0) return LLOPS_OK;
+  if (s->n == 0) {  // empty sequences: Q/K/V/out may be null; the state passes through
+    LLOPS_TRY(opt(S0, "S0"));
+    LLOPS_TRY(opt(z0, "z0"));
+    LLOPS_TRY(opt(S_final, "S_final"));
+    LLOPS_TRY(opt(z_final, "z_final"));
+    if (causal && (S_final || z_final))
+      LLOPS_HIP(llops::launch_state_init(BH, s->m, s->dv, S0, z0, S_final, z_final, st),
+                "state_init");
+    return LLOPS_OK;
+  }
+  LLOPS_TRY(need(Q, "Q"));
+  LLOPS_TRY(need(K, "K"));
+  LLOPS_TRY(need(V, "V"));
+  LLOPS_TRY(need(tq, "theta_q"));
+  LLOPS_TRY(need(tk, "theta_k"));
+  LLOPS_TRY(need(out, "out"));
+  LLOPS_TRY(opt(S0, "S0"));
+  LLOPS_TRY(opt(z0, "z0"));
+  LLOPS_TRY(opt(S_final, "S_final"));
+  LLOPS_TRY(opt(z_final, "z_final"));
+  const WsLayout L = ws_layout(s, entry);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (L.total && !ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  if (ws) LLOPS_TRY(opt(ws, "ws"));
+  char* w = static_cast<char*>(ws);
+  const bool bf16 = s->in_dtype == LLOPS_BF16;
+  const llops::AttnShape a = attn_shape(s, causal);
+  const int64_t per = static_cast<int64_t>(s->m) * s->dv + s->m;
+  float* seg = reinterpret_cast<float*>(w + L.seg);
+  llops::FeatJob jobs[2] = {{Q, tq, w + L.phiq}, {K, tk, w + L.phik}};
+  const llops::FeatShape fs = feat_shape(s, s->n, bf16 ? 1 : 0);
+  if (bf16) {
+    LLOPS_HIP(llops::launch_featmap_bf16(fs, jobs, 2, st), "featmap");
+    const uint16_t* pq = reinterpret_cast<const uint16_t*>(w + L.phiq);
+    const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);
+    const uint16_t* vv = static_cast<const uint16_t*>(V);
+    LLOPS_HIP(llops::launch_seg_state_bf16(a, pk, vv, seg, st), "seg_state");
+    if (causal) {
+      LLOPS_HIP(llops::launch_seg_scan(a, seg, S0, z0, S_final, z_final, 1, st), "seg_scan");
+      LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, seg, per, per * a.nseg,
+                                            static_cast<float*>(out), st),
+                "attn_out");
+    } else {
+      float* tot = reinterpret_cast<float*>(w + L.tot);
+      LLOPS_HIP(llops::launch_seg_scan(a, seg, nullptr, nullptr, tot,
+                                       tot + static_cast<int64_t>(s->m) * s->dv, 0, st),
+                "seg_scan");
+      LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, tot, 0, per, static_cast<float*>(out),
+                                            st),
+                "attn_out");
+    }
+  } else {
+    LLOPS_HIP(llops::launch_featmap_f32(fs, jobs, 2, st), "featmap");
+    const float* pq = reinterpret_cast<const float*>(w + L.phiq);
+    const float* pk = reinterpret_cast<const float*>(w + L.phik);
+    const float* vv = static_cast<const float*>(V);
+    LLOPS_HIP(llops::launch_seg_state_f32(a, pk, vv, seg, st), "seg_state");
+    if (causal) {
+      LLOPS_HIP(llops::launch_seg_scan(a, seg, S0, z0, S_final, z_final, 1, st), "seg_scan");
+      LLOPS_HIP(llops::launch_attn_out_f32(a, pq, pk, vv, seg, per, per * a.nseg,
+                                           static_cast<float*>(out), st),
+                "attn_out");
+    } else {
+      float* tot = reinterpret_cast<float*>(w + L.tot);
+      LLOPS_HIP(llops::launch_seg_scan(a, seg, nullptr, nullptr, tot,
+                                       tot + static_cast<int64_t>(s->m) * s->dv, 0, st),
+                "seg_scan");
+      LLOPS_HIP(llops::launch_attn_out_f32(a, pq, pk, vv, tot, 0, per, static_cast<float*>(out),
+                                           st),
+                "attn_out");
+    }
+  }
+  return LLOPS_OK;
+}
+
+}  // namespace
+
+namespace llops {
+namespace {
+struct ProfState {
+  hipEvent_t* events = nullptr;
+  const char** names = nullptr;
+  int32_t cap = 0;
+  int32_t n = 0;
+  bool armed = false;
+};
+thread_local ProfState g_prof;
+}  // namespace
+
+void prof_before(const char* name, hipStream_t st) {
+  if (!g_prof.armed || g_prof.n >= g_prof.cap) return;
+  if (g_prof.names) g_prof.names[g_prof.n] = name;
+  (void)hipEventRecord(g_prof.events[2 * g_prof.n], st);
+}
+
+void prof_after(hipStream_t st) {
+  if (!g_prof.armed || g_prof.n >= g_prof.cap) return;
+  (void)hipEventRecord(g_prof.events[2 * g_prof.n + 1], st);
+  ++g_prof.n;
+}
+}  // namespace llops
+
+extern "C" {
+
+llops_status_t llops_profile_arm(hipEvent_t* events, const char** names, int32_t capacity) {
+  if (!events || capacity < 0) return fail(LLOPS_ERR_INVALID_ARG, "profile: bad events/capacity");
+  llops::g_prof.events = events;
+  llops::g_prof.names = names;
+  llops::g_prof.cap = capacity;
+  llops::g_prof.n = 0;
+  llops::g_prof.armed = true;
+  return LLOPS_OK;
+}
+
+int32_t llops_profile_disarm(void) {
+  const int32_t n = llops::g_prof.n;
+  llops::g_prof = llops::ProfState{};
+  return n;
+}
+
+size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
+  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_DECODE) return 0;
+  if (validate(shape, entry) != LLOPS_OK) return 0;
+  return ws_layout(shape, entry).total;
+}
+
+llops_status_t llops_featmap(const llops_shape_t* s, const void* X, const void* theta, void* phi,
+                             hipStream_t st) {
+  LLOPS_TRY(validate(s, LLOPS_ENTRY_FEATMAP));
+  if (s->batch * s->heads == 0 || s->n == 0) return LLOPS_OK;  // empty: pointers may be null
+  LLOPS_TRY(need(X, "X"));
+  LLOPS_TRY(need(theta, "theta"));
+  LLOPS_TRY(need(phi, "phi"));
+  if (s->in_dtype == LLOPS_F32 && s->out_dtype != LLOPS_F32)
+    return fail(LLOPS_ERR_UNSUPPORTED, "fp32 inputs produce fp32 phi only");
+  llops::FeatJob job{X, theta, phi};
+  const llops::FeatShape fs = feat_shape(s, s->n, s->out_dtype == LLOPS_BF16 ? 1 : 0);
+  if (s->in_dtype == LLOPS_BF16)
+    LLOPS_HIP(llops::launch_featmap_bf16(fs, &job, 1, st), "featmap");
+  else
+    LLOPS_HIP(llops::launch_featmap_f32(fs, &job, 1, st), "featmap");
+  return LLOPS_OK;
+}
+
+llops_status_t llops_linattn_fwd(const llops_shape_t* s, const void* Q, const void* K,
+                                 const void* V, const void* theta_q, const void* theta_k,
+                                 void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+  return attention(s, false, Q, K, V, theta_q, theta_k, nullptr, nullptr, out, nullptr, nullptr,
+                   ws, ws_bytes, st);
+}
+
+llops_status_t llops_linattn_causal_fwd(const llops_shape_t* s, const void* Q, const void* K,
+                                        const void* V, const void* theta_q, const void* theta_k,
+                                        const float* S0, const float* z0, void* out,
+                                        float* S_final, float* z_final, void* ws,
+                                        size_t ws_bytes, hipStream_t st) {
+  return attention(s, true, Q, K, V, theta_q, theta_k, S0, z0, out, S_final, z_final, ws,
+                   ws_bytes, st);
+}
+
+llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const void* k,
+                                 const void* v, const void* theta_q, const void* theta_k, float* S,
+                                 float* z, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+  LLOPS_TRY(validate(s, LLOPS_ENTRY_DECODE));
+  const int64_t BH = s->batch * s->heads;
+  if (BH == 0) return LLOPS_OK;  // empty: pointers may be null
+  LLOPS_TRY(need(q, "q"));
+  LLOPS_TRY(need(k, "k"));
+  LLOPS_TRY(need(v, "v"));
+  LLOPS_TRY(need(theta_q, "theta_q"));
+  LLOPS_TRY(need(theta_k, "theta_k"));
+  LLOPS_TRY(need(S, "S"));
+  LLOPS_TRY(need(z, "z"));
+  LLOPS_TRY(need(out, "out"));
+  const WsLayout L = ws_layout(s, LLOPS_ENTRY_DECODE);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (L.total && !ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  if (ws) LLOPS_TRY(opt(ws, "ws"));
+  char* w = static_cast<char*>(ws);
+  float* fq = reinterpret_cast<float*>(w + L.phiq);
+  float* fk = reinterpret_cast<float*>(w + L.phik);
+  llops::FeatJob jobs[2] = {{q, theta_q, fq}, {k, theta_k, fk}};
+  const llops::FeatShape fs = feat_shape(s, 1, 0);
+  const bool bf16 = s->in_dtype == LLOPS_BF16;
+  if (bf16)
+    LLOPS_HIP(llops::launch_featmap_bf16(fs, jobs, 2, st), "featmap");
+  else
+    LLOPS_HIP(llops::launch_featmap_f32(fs, jobs, 2, st), "featmap");
+  LLOPS_HIP(llops::launch_decode_state(BH, s->m, s->dv, fq, fk, v, bf16 ? 1 : 0, S, z,
+                                       static_cast<float*>(out), s->normalize,
+                                       s->normalize ? s->delta : 0.f, st),
+            "decode_state");
+  return LLOPS_OK;
+}
+
+const char* llops_status_str(llops_status_t status) {
+  switch (status) {
+    case LLOPS_OK: return "LLOPS_OK";
+    case LLOPS_ERR_INVALID_ARG: return "LLOPS_ERR_INVALID_ARG";
+    case LLOPS_ERR_UNSUPPORTED: return "LLOPS_ERR_UNSUPPORTED";
+    case LLOPS_ERR_WORKSPACE: return "LLOPS_ERR_WORKSPACE";
+    case LLOPS_ERR_HIP: return "LLOPS_ERR_HIP";
+    default: return "LLOPS_ERR_UNKNOWN";
+  }
+}
+
+const char* llops_last_error(void) { return g_err; }
+
+}  // extern "C"

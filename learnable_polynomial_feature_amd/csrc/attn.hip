@@ -1,0 +1,605 @@
+// Linear-attention contraction over precomputed LLoPS features.
+//
+//   non-causal: out = phi_Q (phi_K^T V) [/ (phi_Q (phi_K^T 1) + delta)]
+//     (LLoPS notes, overall framework; low-rank-attention blog, Performer
+//      section: associativity and the numerator/denominator form)
+//   causal:     out_i = phi_Q,i S_i [/ (phi_Q,i z_i + delta)], S_i, z_i summed over j <= i
+//     (LLoPS paper Sec. 1: streaming form with constant-size state; blog:
+//      causal masking by incremental cumulative sums)
+//
+// Work decomposition (one GPU): every (batch, head) sequence is cut into
+// `nseg` segments so that batch*heads*nseg workgroups fill the chip.
+//   P1 seg_state: per segment, dS = phi_K^T V and dz = phi_K^T 1 (MFMA; dz via
+//      a constant all-ones B fragment).
+//   scan:         exclusive prefix of (dS, dz) over segments, seeded with
+//                 (S0, z0); the total is the final state.
+//   P2 attn_out:  per segment, walk blocks of C tokens: the masked block
+//      A^T = phi_K phi_Q^T (MFMA) goes to LDS in bf16; the normaliser row sums
+//      read the same rounded A; out = A V + phi_Q S on MFMA with S held in
+//      fp32 accumulator registers (each wave owns dv/4 columns of S and feeds
+//      them straight back as bf16 B fragments, k-permuted to match the
+//      accumulator layout); then S += phi_K^T V, z += colsum(phi_K).
+#include "device.h"
+#include "kernels.h"
+
+namespace llops {
+namespace {
+
+struct AttnArgs {
+  int64_t BH, n;
+  int m, dv, chunk, nseg;
+  int64_t seg_len;
+  int normalize;
+  float delta;
+};
+
+AttnArgs to_args(const AttnShape& s) {
+  AttnArgs a{};
+  a.BH = s.BH;
+  a.n = s.n;
+  a.m = s.m;
+  a.dv = s.dv;
+  a.chunk = s.chunk;
+  a.nseg = s.nseg;
+  a.seg_len = s.seg_len;
+  a.normalize = s.normalize;
+  a.delta = s.delta;
+  return a;
+}
+
+// Load an 8x8 bf16 block (rows r0..r0+7 of a row-major [rows][ld] matrix,
+// columns c0..c0+7), zero-filling rows >= rmax.
+__device__ __forceinline__ void load_block8(const uint16_t* base, int64_t ld, int64_t r0,
+                                            int64_t rmax, int c0, u32x4 out[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + i;
+    out[i] = (r < rmax) ? ld16(base + r * ld + c0) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// ============================================================================
+// P1: per-segment state partials, bf16 features
+// ============================================================================
+template <int MTW, int NT>
+__global__ __launch_bounds__(256) void seg_state_bf16(AttnArgs a, const uint16_t* __restrict__ phik,
+                                                      const uint16_t* __restrict__ v,
+                                                      float* __restrict__ seg) {
+  constexpr int TB = 64;        // tokens per stage (two 32-wide k-steps)
+  constexpr int LROW = TB + 8;  // padded row of the transposed stage
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int m = a.m, dv = NT * 16;
+  uint16_t* KT = smem;             // [m][LROW]   phi_K^T
+  uint16_t* VT = smem + m * LROW;  // [dv][LROW]  V^T
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const uint16_t* K = phik + bh * a.n * m;
+  const uint16_t* Vb = v + bh * a.n * dv;
+  const int MT = m / 16;
+
+  f32x4 acc[MTW][NT + 1];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int c = 0; c <= NT; ++c) acc[i][c] = zero4();
+  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  const int nkb = (TB / 8) * (m / 8), nvb = (TB / 8) * (dv / 8);
+  for (int64_t tb = t0; tb < t1; tb += TB) {
+    __syncthreads();
+    for (int sb = tid; sb < nkb + nvb; sb += 256) {
+      u32x4 blk[8], tr[8];
+      if (sb < nkb) {
+        const int jb = sb / (m / 8), f8 = sb - jb * (m / 8);
+        load_block8(K, m, tb + jb * 8, t1, f8 * 8, blk);
+        transpose8x8(blk, tr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(KT + (f8 * 8 + e) * LROW + jb * 8, tr[e]);
+      } else {
+        const int s2 = sb - nkb;
+        const int jb = s2 / (dv / 8), c8 = s2 - jb * (dv / 8);
+        load_block8(Vb, dv, tb + jb * 8, t1, c8 * 8, blk);
+        transpose8x8(blk, tr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(VT + (c8 * 8 + e) * LROW + jb * 8, tr[e]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MTW; ++i) {
+      const int rt = w + 4 * i;
+      if (rt >= MT) continue;
+#pragma unroll
+      for (int ks = 0; ks < TB / 32; ++ks) {
+        const bf16x8 af = as_bf16x8(ld16(KT + (rt * 16 + c16) * LROW + ks * 32 + g * 8));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const bf16x8 bf = as_bf16x8(ld16(VT + (ct * 16 + c16) * LROW + ks * 32 + g * 8));
+          acc[i][ct] = mfma16x16x32(af, bf, acc[i][ct]);
+        }
+        acc[i][NT] = mfma16x16x32(af, ones, acc[i][NT]);
+      }
+    }
+  }
+  float* out = seg + (bh * a.nseg + gseg) * (static_cast<int64_t>(m) * dv + m);
+#pragma unroll
+  for (int i = 0; i < MTW; ++i) {
+    const int rt = w + 4 * i;
+    if (rt >= MT) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int f = rt * 16 + g * 4 + e;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) out[f * dv + ct * 16 + c16] = acc[i][ct][e];
+      if (c16 == 0) out[m * dv + f] = acc[i][NT][e];
+    }
+  }
+}
+
+// ============================================================================
+// Segment scan (any dtype: state is fp32)
+// ============================================================================
+__global__ __launch_bounds__(256) void seg_scan_kernel(int nseg, int m, int dv,
+                                                       float* __restrict__ seg,
+                                                       const float* S0, const float* z0,
+                                                       float* Sout, int64_t Sout_bh,
+                                                       float* zout, int64_t zout_bh,
+                                                       int exclusive) {
+  const int64_t per = static_cast<int64_t>(m) * dv + m;
+  const int64_t mdv = static_cast<int64_t>(m) * dv;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (e >= per) return;
+  float acc = 0.f;
+  if (e < mdv) {
+    if (S0) acc = S0[bh * mdv + e];
+  } else {
+    if (z0) acc = z0[bh * m + (e - mdv)];
+  }
+  float* p = seg + bh * nseg * per + e;
+  for (int gi = 0; gi < nseg; ++gi, p += per) {
+    const float x = *p;
+    if (exclusive) *p = acc;
+    acc += x;
+  }
+  if (e < mdv) {
+    if (Sout) Sout[bh * Sout_bh + e] = acc;
+  } else {
+    if (zout) zout[bh * zout_bh + (e - mdv)] = acc;
+  }
+}
+
+// ============================================================================
+// P2: output pass, bf16 features
+// ============================================================================
+template <int C, int MTM, int NTW, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_out_bf16(AttnArgs a, const uint16_t* __restrict__ phiq,
+                                                     const uint16_t* __restrict__ phik,
+                                                     const uint16_t* __restrict__ v,
+                                                     const float* __restrict__ state,
+                                                     int64_t st_seg, int64_t st_bh,
+                                                     float* __restrict__ out) {
+  constexpr int CROW = C + 8;
+  constexpr int CT = C / 16;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int m = a.m, dv = a.dv;
+  const int MROW = m + 8;
+  const int MT = m / 16, NT = dv / 16;
+  uint16_t* Qs = smem;                  // [C][MROW]
+  uint16_t* Ks = Qs + C * MROW;         // [C][MROW]
+  uint16_t* KT = Ks + C * MROW;         // [m][CROW]
+  uint16_t* VT = KT + m * CROW;         // [dv][CROW]
+  uint16_t* As = VT + dv * CROW;        // [C][CROW]  A[i][j] (query i, key j)
+  float* zs = reinterpret_cast<float*>(As + C * CROW);  // [m]
+  float* dens = zs + m;                                 // [C]  1 / (den + delta)
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const uint16_t* Qg = phiq + bh * a.n * m;
+  const uint16_t* Kg = phik + bh * a.n * m;
+  const uint16_t* Vg = v + bh * a.n * dv;
+  float* Og = out + bh * a.n * dv;
+  const float* Sin = state + bh * st_bh + gseg * st_seg;
+
+  // S columns owned by this wave: ct = w + 4*i
+  f32x4 S[MTM][NTW];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int ct = w + 4 * i;
+#pragma unroll
+    for (int rt = 0; rt < MTM; ++rt) {
+      f32x4 x = zero4();
+      if (rt < MT && ct < NT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = Sin[(rt * 16 + g * 4 + e) * dv + ct * 16 + c16];
+      }
+      S[rt][i] = x;
+    }
+  }
+  for (int f = tid; f < m; f += 256) zs[f] = Sin[m * dv + f];
+
+  const int nqb = (C / 8) * (m / 8), nvb = (C / 8) * (dv / 8);
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    // ---- stage phi_Q, phi_K (natural and transposed) and V^T
+    // non-causal blocks only need phi_Q (S and z are the totals)
+    const int nstage = CAUSAL ? 2 * nqb + nvb : nqb;
+    for (int sb = tid; sb < nstage; sb += 256) {
+      u32x4 blk[8], tr[8];
+      if (sb < nqb) {
+        const int jb = sb / (m / 8), f8 = sb - jb * (m / 8);
+        load_block8(Qg, m, c0 + jb * 8, t1, f8 * 8, blk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(Qs + (jb * 8 + e) * MROW + f8 * 8, blk[e]);
+      } else if (sb < 2 * nqb) {
+        const int s2 = sb - nqb;
+        const int jb = s2 / (m / 8), f8 = s2 - jb * (m / 8);
+        load_block8(Kg, m, c0 + jb * 8, t1, f8 * 8, blk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(Ks + (jb * 8 + e) * MROW + f8 * 8, blk[e]);
+        transpose8x8(blk, tr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(KT + (f8 * 8 + e) * CROW + jb * 8, tr[e]);
+      } else {
+        const int s2 = sb - 2 * nqb;
+        const int jb = s2 / (dv / 8), c8 = s2 - jb * (dv / 8);
+        load_block8(Vg, dv, c0 + jb * 8, t1, c8 * 8, blk);
+        transpose8x8(blk, tr);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st16(VT + (c8 * 8 + e) * CROW + jb * 8, tr[e]);
+      }
+    }
+    __syncthreads();
+
+    if (CAUSAL) {
+      // ---- masked A^T tiles (key rows j, query columns i), j <= i kept
+      for (int k = w; k < CT * CT; k += 4) {
+        const int jt = k / CT, it = k - jt * CT;
+        f32x4 acc = zero4();
+        if (jt <= it) {
+          const uint16_t* arow = Ks + (jt * 16 + c16) * MROW + g * 8;
+          const uint16_t* brow = Qs + (it * 16 + c16) * MROW + g * 8;
+          for (int kq = 0; kq < m / 32; ++kq)
+            acc = mfma16x16x32(as_bf16x8(ld16(arow + kq * 32)), as_bf16x8(ld16(brow + kq * 32)), acc);
+          if (jt == it) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (g * 4 + e > c16) acc[e] = 0.f;
+          }
+        }
+        const uint32_t lo = pack_bf16x2(acc[0], acc[1]), hi = pack_bf16x2(acc[2], acc[3]);
+        *reinterpret_cast<u32x2*>(As + (it * 16 + c16) * CROW + jt * 16 + g * 4) = u32x2{lo, hi};
+      }
+      __syncthreads();
+    }
+
+    // ---- normaliser: dens[i] = 1 / (sum_j A[i][j] + phi_Q[i] . z + delta)
+    if (a.normalize) {
+      constexpr int TPR = 256 / C;  // threads per row (4 or 8)
+      const int i = tid / TPR, q = tid - i * TPR;
+      float s = 0.f;
+      if (CAUSAL)
+        for (int j = q; j < C; j += TPR) s += bf16_to_f32(As[i * CROW + j]);
+      for (int f = q; f < m; f += TPR) s += bf16_to_f32(Qs[i * MROW + f]) * zs[f];
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o);
+      if (q == 0) dens[i] = 1.f / (s + a.delta);
+      __syncthreads();
+    }
+
+    // ---- out = A V + phi_Q S  (rows of this block, this wave's columns)
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int ct = w + 4 * i;
+      if (ct >= NT) continue;
+      for (int it = 0; it < CT; ++it) {
+        f32x4 acc = zero4();
+        if (CAUSAL) {
+#pragma unroll
+          for (int ks = 0; ks < C / 32; ++ks) {
+            if (ks * 32 > it * 16 + 15) continue;  // keys beyond this query block are masked
+            const bf16x8 af = as_bf16x8(ld16(As + (it * 16 + c16) * CROW + ks * 32 + g * 8));
+            const bf16x8 bf = as_bf16x8(ld16(VT + (ct * 16 + c16) * CROW + ks * 32 + g * 8));
+            acc = mfma16x16x32(af, bf, acc);
+          }
+        }
+        const uint16_t* qrow = Qs + (it * 16 + c16) * MROW + g * 4;
+#pragma unroll
+        for (int kq = 0; kq < MTM / 2; ++kq) {
+          if (2 * kq >= MT) continue;
+          const u32x2 q0 = *reinterpret_cast<const u32x2*>(qrow + kq * 32);
+          const u32x2 q1 = *reinterpret_cast<const u32x2*>(qrow + kq * 32 + 16);
+          const bf16x8 af = as_bf16x8(u32x4{q0[0], q0[1], q1[0], q1[1]});
+          const f32x4 s0 = S[2 * kq][i], s1 = S[2 * kq + 1][i];
+          const bf16x8 bf = as_bf16x8(u32x4{pack_bf16x2(s0[0], s0[1]), pack_bf16x2(s0[2], s0[3]),
+                                            pack_bf16x2(s1[0], s1[1]), pack_bf16x2(s1[2], s1[3])});
+          acc = mfma16x16x32(af, bf, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = it * 16 + g * 4 + e;
+          const int64_t tok = c0 + r;
+          if (tok < t1) {
+            const float val = a.normalize ? acc[e] * dens[r] : acc[e];
+            Og[tok * dv + ct * 16 + c16] = val;
+          }
+        }
+      }
+    }
+
+    if (CAUSAL) {
+      // ---- S += phi_K^T V for this wave's columns
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        const int ct = w + 4 * i;
+        if (ct >= NT) continue;
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks) {
+          const bf16x8 bf = as_bf16x8(ld16(VT + (ct * 16 + c16) * CROW + ks * 32 + g * 8));
+#pragma unroll
+          for (int rt = 0; rt < MTM; ++rt) {
+            if (rt >= MT) continue;
+            const bf16x8 af = as_bf16x8(ld16(KT + (rt * 16 + c16) * CROW + ks * 32 + g * 8));
+            S[rt][i] = mfma16x16x32(af, bf, S[rt][i]);
+          }
+        }
+      }
+      // ---- z += column sums of phi_K (after the normaliser read z)
+      for (int f = tid; f < m; f += 256) {
+        float s = 0.f;
+        for (int j = 0; j < C; ++j) s += bf16_to_f32(Ks[j * MROW + f]);
+        zs[f] += s;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================================
+// fp32 SIMT versions (fp32 inputs: exact-arithmetic reference-grade path)
+// ============================================================================
+__global__ __launch_bounds__(256) void seg_state_f32(AttnArgs a, const float* __restrict__ phik,
+                                                     const float* __restrict__ v,
+                                                     float* __restrict__ seg) {
+  const int m = a.m, dv = a.dv;
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const float* K = phik + bh * a.n * m;
+  const float* V = v + bh * a.n * dv;
+  const int64_t per = static_cast<int64_t>(m) * dv + m;
+  float* out = seg + (bh * a.nseg + gseg) * per;
+  for (int64_t e = threadIdx.x; e < per; e += 256) {
+    float s = 0.f;
+    if (e < static_cast<int64_t>(m) * dv) {
+      const int f = static_cast<int>(e / dv), c = static_cast<int>(e - static_cast<int64_t>(f) * dv);
+      for (int64_t j = t0; j < t1; ++j) s = fmaf(K[j * m + f], V[j * dv + c], s);
+    } else {
+      const int f = static_cast<int>(e - static_cast<int64_t>(m) * dv);
+      for (int64_t j = t0; j < t1; ++j) s += K[j * m + f];
+    }
+    out[e] = s;
+  }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_out_f32(AttnArgs a, const float* __restrict__ phiq,
+                                                    const float* __restrict__ phik,
+                                                    const float* __restrict__ v,
+                                                    float* __restrict__ state, int64_t st_seg,
+                                                    int64_t st_bh, float* __restrict__ out) {
+  extern __shared__ float fsm[];
+  const int C = a.chunk;
+  float* A = fsm;          // [C][C]
+  float* den = A + C * C;  // [C]
+  const int m = a.m, dv = a.dv;
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const float* Q = phiq + bh * a.n * m;
+  const float* K = phik + bh * a.n * m;
+  const float* V = v + bh * a.n * dv;
+  float* O = out + bh * a.n * dv;
+  float* S = state + bh * st_bh + gseg * st_seg;  // [m][dv] then z [m]
+  float* z = S + static_cast<int64_t>(m) * dv;
+  const int tid = threadIdx.x;
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    const int nc = static_cast<int>(min<int64_t>(C, t1 - c0));
+    if (CAUSAL) {
+      for (int e = tid; e < C * C; e += 256) {
+        const int i = e / C, j = e - i * C;
+        float s = 0.f;
+        if (j <= i && i < nc)
+          for (int f = 0; f < m; ++f) s = fmaf(Q[(c0 + i) * m + f], K[(c0 + j) * m + f], s);
+        A[e] = s;
+      }
+      __syncthreads();
+    }
+    if (a.normalize) {
+      for (int i = tid; i < nc; i += 256) {
+        float s = 0.f;
+        if (CAUSAL)
+          for (int j = 0; j <= i; ++j) s += A[i * C + j];
+        for (int f = 0; f < m; ++f) s = fmaf(Q[(c0 + i) * m + f], z[f], s);
+        den[i] = s + a.delta;
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < nc * dv; e += 256) {
+      const int i = e / dv, c = e - i * dv;
+      float s = 0.f;
+      if (CAUSAL)
+        for (int j = 0; j <= i; ++j) s = fmaf(A[i * C + j], V[(c0 + j) * dv + c], s);
+      for (int f = 0; f < m; ++f) s = fmaf(Q[(c0 + i) * m + f], S[f * dv + c], s);
+      O[(c0 + i) * dv + c] = a.normalize ? s / den[i] : s;
+    }
+    if (CAUSAL) {
+      __syncthreads();
+      const int64_t per = static_cast<int64_t>(m) * dv + m;
+      for (int64_t e = tid; e < per; e += 256) {
+        if (e < static_cast<int64_t>(m) * dv) {
+          const int f = static_cast<int>(e / dv), c = static_cast<int>(e - static_cast<int64_t>(f) * dv);
+          float s = S[e];
+          for (int j = 0; j < nc; ++j) s = fmaf(K[(c0 + j) * m + f], V[(c0 + j) * dv + c], s);
+          S[e] = s;
+        } else {
+          const int f = static_cast<int>(e - static_cast<int64_t>(m) * dv);
+          float s = z[f];
+          for (int j = 0; j < nc; ++j) s += K[(c0 + j) * m + f];
+          z[f] = s;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void state_init_kernel(int64_t total_S, int64_t total_z,
+                                                         const float* S0, const float* z0,
+                                                         float* S, float* z) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e < total_S && S) S[e] = S0 ? S0[e] : 0.f;
+  if (e < total_z && z) z[e] = z0 ? z0[e] : 0.f;
+}
+
+template <int C, int MTM, int NTW, bool CAUSAL>
+hipError_t launch_out_t(const AttnArgs& a, dim3 grid, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const float* state, int64_t ss, int64_t sb,
+                        float* out, hipStream_t st) {
+  const size_t lds = (2ull * C * (a.m + 8) + static_cast<size_t>(a.m) * (C + 8) +
+                      static_cast<size_t>(a.dv) * (C + 8) + static_cast<size_t>(C) * (C + 8)) *
+                         sizeof(uint16_t) +
+                     (a.m + C) * sizeof(float);
+  const hipError_t e = allow_lds(attn_out_bf16<C, MTM, NTW, CAUSAL>, lds);
+  if (e != hipSuccess) return e;
+  LLOPS_LAUNCH("attn_out_bf16", st, (attn_out_bf16<C, MTM, NTW, CAUSAL>), grid, dim3(256), lds, st, a, q, k, v,
+                     state, ss, sb, out);
+  return hipGetLastError();
+}
+
+template <int C, bool CAUSAL>
+hipError_t launch_out_c(const AttnArgs& a, dim3 grid, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const float* state, int64_t ss, int64_t sb,
+                        float* out, hipStream_t st) {
+  const bool wide = a.dv > 64;
+  if (a.m <= 64)
+    return wide ? launch_out_t<C, 4, 2, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st)
+                : launch_out_t<C, 4, 1, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st);
+  if (a.m <= 128)
+    return wide ? launch_out_t<C, 8, 2, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st)
+                : launch_out_t<C, 8, 1, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st);
+  return wide ? launch_out_t<C, 16, 2, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st)
+              : launch_out_t<C, 16, 1, CAUSAL>(a, grid, q, k, v, state, ss, sb, out, st);
+}
+
+template <int MTW, int NT>
+hipError_t launch_state_t(const AttnArgs& a, dim3 grid, const uint16_t* k, const uint16_t* v,
+                          float* seg, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(a.m + a.dv) * (64 + 8) * sizeof(uint16_t);
+  LLOPS_LAUNCH("seg_state_bf16", st, (seg_state_bf16<MTW, NT>), grid, dim3(256), lds, st, a, k, v, seg);
+  return hipGetLastError();
+}
+
+template <int MTW>
+hipError_t launch_state_m(const AttnArgs& a, dim3 grid, const uint16_t* k, const uint16_t* v,
+                          float* seg, hipStream_t st) {
+  switch (a.dv / 16) {
+    case 1: return launch_state_t<MTW, 1>(a, grid, k, v, seg, st);
+    case 2: return launch_state_t<MTW, 2>(a, grid, k, v, seg, st);
+    case 3: return launch_state_t<MTW, 3>(a, grid, k, v, seg, st);
+    case 4: return launch_state_t<MTW, 4>(a, grid, k, v, seg, st);
+    case 5: return launch_state_t<MTW, 5>(a, grid, k, v, seg, st);
+    case 6: return launch_state_t<MTW, 6>(a, grid, k, v, seg, st);
+    case 7: return launch_state_t<MTW, 7>(a, grid, k, v, seg, st);
+    case 8: return launch_state_t<MTW, 8>(a, grid, k, v, seg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_seg_state_bf16(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
+                                 float* seg, hipStream_t st) {
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  if (s.m <= 64) return launch_state_m<1>(a, grid, phik, v, seg, st);
+  if (s.m <= 128) return launch_state_m<2>(a, grid, phik, v, seg, st);
+  return launch_state_m<4>(a, grid, phik, v, seg, st);
+}
+
+hipError_t launch_seg_state_f32(const AttnShape& s, const float* phik, const float* v,
+                                float* seg, hipStream_t st) {
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("seg_state_f32", st, seg_state_f32, grid, dim3(256), 0, st, a, phik, v, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_scan(const AttnShape& s, float* seg, const float* S0, const float* z0,
+                           float* Sout, float* zout, int exclusive, hipStream_t st) {
+  // Sout is [BH][m*dv] and zout [BH][m] unless they alias one contiguous
+  // [BH][m*dv + m] buffer (zout == Sout + m*dv), which the non-causal path uses.
+  const int64_t mdv = static_cast<int64_t>(s.m) * s.dv;
+  const int64_t per = mdv + s.m;
+  int64_t Sb = mdv, zb = s.m;
+  if (Sout && zout == Sout + mdv) {
+    Sb = per;
+    zb = per;
+  }
+  dim3 grid(static_cast<unsigned>((per + 255) / 256), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("seg_scan", st, seg_scan_kernel, grid, dim3(256), 0, st, s.nseg, s.m, s.dv, seg, S0, z0,
+                     Sout, Sb, zout, zb, exclusive);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_out_bf16(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
+                                const uint16_t* v, const float* state, int64_t st_seg,
+                                int64_t st_bh, float* out, hipStream_t st) {
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  if (s.causal) {
+    if (s.chunk == 32)
+      return launch_out_c<32, true>(a, grid, phiq, phik, v, state, st_seg, st_bh, out, st);
+    return launch_out_c<64, true>(a, grid, phiq, phik, v, state, st_seg, st_bh, out, st);
+  }
+  return launch_out_c<64, false>(a, grid, phiq, phik, v, state, st_seg, st_bh, out, st);
+}
+
+hipError_t launch_attn_out_f32(const AttnShape& s, const float* phiq, const float* phik,
+                               const float* v, float* state, int64_t st_seg, int64_t st_bh,
+                               float* out, hipStream_t st) {
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  const size_t lds = (static_cast<size_t>(s.chunk) * s.chunk + s.chunk) * sizeof(float);
+  hipError_t e = allow_lds(attn_out_f32<true>, lds);
+  if (e == hipSuccess) e = allow_lds(attn_out_f32<false>, lds);
+  if (e != hipSuccess) return e;
+  if (s.causal)
+    LLOPS_LAUNCH("attn_out_f32", st, attn_out_f32<true>, grid, dim3(256), lds, st, a, phiq, phik, v, state,
+                       st_seg, st_bh, out);
+  else
+    LLOPS_LAUNCH("attn_out_f32", st, attn_out_f32<false>, grid, dim3(256), lds, st, a, phiq, phik, v, state,
+                       st_seg, st_bh, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(int64_t BH, int m, int dv, const float* S0, const float* z0,
+                             float* S, float* z, hipStream_t st) {
+  const int64_t tS = BH * m * dv, tz = BH * m;
+  const int64_t tot = tS > tz ? tS : tz;
+  if (tot == 0) return hipSuccess;
+  LLOPS_LAUNCH("state_init", st, state_init_kernel, dim3(static_cast<unsigned>((tot + 255) / 256)),
+                     dim3(256), 0, st, tS, tz, S0, z0, S, z);
+  return hipGetLastError();
+}
+
+}  // namespace llops

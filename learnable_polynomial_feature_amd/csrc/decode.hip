@@ -1,0 +1,167 @@
+// LLoPS single-token decode step on the recurrent state (LLoPS paper Sec. 1:
+// linear attention as a recurrent memory state updated token by token).
+//   S += phi_K(k) v^T;  z += phi_K(k);  out = phi_Q(q)^T S [/(phi_Q(q)^T z + delta)]
+// The state update precedes the read (inclusive of the new token).
+//
+// One workgroup per (batch, head). The m x dv fp32 state is streamed once:
+// each thread owns 4 adjacent columns (16-byte non-temporal loads/stores) of
+// every (256 / (dv/4))-th row, updates them in registers and accumulates the
+// read-out partial; partials are reduced across row groups in a fixed order.
+// The kernel is bound by HBM bandwidth: 2 * m * dv * 4 bytes of state per
+// (batch, head) against ~3 flops per state element.
+#include "device.h"
+#include "kernels.h"
+
+namespace llops {
+namespace {
+
+template <bool VBF16>
+__device__ __forceinline__ float4 load_v4(const void* v, int64_t idx) {
+  if (VBF16) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(v) + idx);
+    return make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                       __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u));
+  } else {
+    return *reinterpret_cast<const float4*>(static_cast<const float*>(v) + idx);
+  }
+}
+
+template <bool VBF16>
+__device__ __forceinline__ float load_v1(const void* v, int64_t idx) {
+  if (VBF16) return bf16_to_f32(static_cast<const uint16_t*>(v)[idx]);
+  return static_cast<const float*>(v)[idx];
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = x;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Vector path: dv % 4 == 0 and (dv / 4) divides 256.
+template <bool VBF16>
+__global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const float* __restrict__ phiq,
+                                                        const float* __restrict__ phik,
+                                                        const void* __restrict__ v,
+                                                        float* __restrict__ S, float* __restrict__ z,
+                                                        float* __restrict__ out, int normalize,
+                                                        float delta) {
+  __shared__ float4 red4[256];
+  __shared__ float red[4];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int CG = dv >> 2, RG = 256 / CG;
+  const int cg = tid % CG, rg = tid / CG;
+  const float* fq = phiq + bh * m;
+  const float* fk = phik + bh * m;
+  float* Sb = S + bh * static_cast<int64_t>(m) * dv;
+  const float4 vv = load_v4<VBF16>(v, bh * dv + cg * 4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int f = rg; f < m; f += RG) {
+    f32x4* p = reinterpret_cast<f32x4*>(Sb + static_cast<int64_t>(f) * dv + cg * 4);
+    f32x4 s = __builtin_nontemporal_load(p);
+    const float kf = fk[f], qf = fq[f];
+    s[0] = fmaf(kf, vv.x, s[0]);
+    s[1] = fmaf(kf, vv.y, s[1]);
+    s[2] = fmaf(kf, vv.z, s[2]);
+    s[3] = fmaf(kf, vv.w, s[3]);
+    __builtin_nontemporal_store(s, p);
+    acc.x = fmaf(qf, s[0], acc.x);
+    acc.y = fmaf(qf, s[1], acc.y);
+    acc.z = fmaf(qf, s[2], acc.z);
+    acc.w = fmaf(qf, s[3], acc.w);
+  }
+  red4[tid] = acc;
+  // z update and the normaliser dot product
+  float dpart = 0.f;
+  for (int f = tid; f < m; f += 256) {
+    const float zn = z[bh * m + f] + fk[f];
+    z[bh * m + f] = zn;
+    dpart = fmaf(fq[f], zn, dpart);
+  }
+  const float den = normalize ? block_sum(dpart, red) + delta : 1.f;  // has barriers
+  __syncthreads();
+  if (tid < CG) {
+    float4 o = red4[tid];
+    for (int r = 1; r < RG; ++r) {
+      const float4 x = red4[r * CG + tid];
+      o.x += x.x;
+      o.y += x.y;
+      o.z += x.z;
+      o.w += x.w;
+    }
+    const float inv = normalize ? 1.f / den : 1.f;
+    float* ob = out + bh * dv + tid * 4;
+    ob[0] = o.x * inv;
+    ob[1] = o.y * inv;
+    ob[2] = o.z * inv;
+    ob[3] = o.w * inv;
+  }
+}
+
+// Generic path: any dv (one thread per column, rows split over 256/dv groups).
+template <bool VBF16>
+__global__ __launch_bounds__(256) void decode_state_gen(int m, int dv, const float* __restrict__ phiq,
+                                                        const float* __restrict__ phik,
+                                                        const void* __restrict__ v,
+                                                        float* __restrict__ S, float* __restrict__ z,
+                                                        float* __restrict__ out, int normalize,
+                                                        float delta) {
+  __shared__ float red[4];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* fq = phiq + bh * m;
+  const float* fk = phik + bh * m;
+  float* Sb = S + bh * static_cast<int64_t>(m) * dv;
+  float dpart = 0.f;
+  for (int f = tid; f < m; f += 256) {
+    const float zn = z[bh * m + f] + fk[f];
+    z[bh * m + f] = zn;
+    dpart = fmaf(fq[f], zn, dpart);
+  }
+  const float den = normalize ? block_sum(dpart, red) + delta : 1.f;
+  for (int c = tid; c < dv; c += 256) {
+    const float vc = load_v1<VBF16>(v, bh * dv + c);
+    float acc = 0.f;
+    for (int f = 0; f < m; ++f) {
+      const float s = fmaf(fk[f], vc, Sb[static_cast<int64_t>(f) * dv + c]);
+      Sb[static_cast<int64_t>(f) * dv + c] = s;
+      acc = fmaf(fq[f], s, acc);
+    }
+    out[bh * dv + c] = normalize ? acc / den : acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq, const float* phik,
+                               const void* v, int v_bf16, float* S, float* z, float* out,
+                               int normalize, float delta, hipStream_t st) {
+  if (BH <= 0) return hipSuccess;
+  if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(BH));
+  const bool vec = (dv % 4 == 0) && (dv / 4 <= 256) && (256 % (dv / 4) == 0);
+  if (vec) {
+    if (v_bf16)
+      LLOPS_LAUNCH("decode_state", st, decode_state_vec<true>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
+                         z, out, normalize, delta);
+    else
+      LLOPS_LAUNCH("decode_state", st, decode_state_vec<false>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
+                         z, out, normalize, delta);
+  } else {
+    if (v_bf16)
+      LLOPS_LAUNCH("decode_state", st, decode_state_gen<true>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
+                         z, out, normalize, delta);
+    else
+      LLOPS_LAUNCH("decode_state", st, decode_state_gen<false>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
+                         z, out, normalize, delta);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace llops

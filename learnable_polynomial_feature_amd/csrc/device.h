@@ -1,0 +1,71 @@
+// Device helpers shared by the LLoPS kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llops {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- bf16 <-> f32 --------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 pair (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return static_cast<uint16_t>(pack_bf16x2(x, 0.f) & 0xFFFFu);
+}
+
+// ---- 16-byte vector memory ------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- MFMA ------------------------------------------------------------------
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l (g = l / 16, c = l % 16): A holds row c, k = 8g..8g+7; B holds
+// column c, k = 8g..8g+7; D holds column c, rows 4g..4g+3. Any permutation
+// of k applied to both A and B leaves D unchanged.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- 8x8 bf16 transpose in registers --------------------------------------
+// in[r] holds row r (8 bf16 = 4 dwords; dword w = elements 2w, 2w+1).
+// out[c] receives column c (8 bf16: rows 0..7).
+__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = in[2 * q][w], hi = in[2 * q + 1][w];
+      out[2 * w][q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      out[2 * w + 1][q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace llops

@@ -1,0 +1,96 @@
+// Host-side launchers of the LLoPS kernels (internal to libllops.so).
+// Each returns hipSuccess or the launch error; shapes were validated by the
+// C ABI layer before these are called.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace llops {
+
+// Kernels with more than 64 KiB of dynamic LDS must say so before launch
+// (a CU has 160 KiB on gfx950).
+template <typename F>
+inline hipError_t allow_lds(F* kernel, size_t bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+// Kernel-level timing hook behind llops_profile_arm(): while armed on the
+// calling thread, each launch is bracketed by two recorded events.
+void prof_before(const char* name, hipStream_t st);
+void prof_after(hipStream_t st);
+
+#define LLOPS_LAUNCH(name, st, ...)       \
+  do {                                    \
+    ::llops::prof_before(name, st);       \
+    hipLaunchKernelGGL(__VA_ARGS__);      \
+    ::llops::prof_after(st);              \
+  } while (0)
+
+// One feature-map job: X [B][H][n][d] -> phi [B][H][n][m].
+struct FeatJob {
+  const void* X;
+  const void* theta;  // [H][p][t][d][m] or [p][t][d][m]
+  void* phi;
+};
+
+struct FeatShape {
+  int64_t B, H, n;
+  int d, m, p, t;
+  int theta_per_head;
+  int square;
+  int out_bf16;  // phi storage: 1 = bf16, 0 = fp32
+};
+
+// bf16 inputs on MFMA; runs `njobs` (1 or 2) jobs of the same shape in one launch.
+hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njobs,
+                               hipStream_t st);
+// fp32 inputs, fp32 arithmetic, fp32 phi.
+hipError_t launch_featmap_f32(const FeatShape& s, const FeatJob* jobs, int njobs,
+                              hipStream_t st);
+
+// Linear-attention contraction over precomputed features.
+struct AttnShape {
+  int64_t BH, n;
+  int m, dv;
+  int chunk;      // tokens per intra-chunk block
+  int nseg;       // sequence segments per (b, h)
+  int64_t seg_len;  // tokens per segment (multiple of chunk)
+  int causal;
+  int normalize;
+  float delta;
+};
+
+// Per-segment partial state: seg[bh][g][0 : m*dv] = phi_K^T V, [m*dv : +m] = phi_K^T 1.
+hipError_t launch_seg_state_bf16(const AttnShape& a, const uint16_t* phik,
+                                 const uint16_t* v, float* seg, hipStream_t st);
+hipError_t launch_seg_state_f32(const AttnShape& a, const float* phik, const float* v,
+                                float* seg, hipStream_t st);
+// Exclusive scan of seg over g starting from (S0, z0) (null = zeros). Writes the
+// total into (S_tot, z_tot) when non-null. For non-causal (exclusive = 0) the
+// slots are left untouched and only the total is produced.
+hipError_t launch_seg_scan(const AttnShape& a, float* seg, const float* S0,
+                           const float* z0, float* S_tot, float* z_tot, int exclusive,
+                           hipStream_t st);
+// Output pass. Causal: segment g starts from seg[bh][g]. Non-causal: every
+// segment reads the total state `tot` [bh][m*dv + m] (contiguous S then z).
+hipError_t launch_attn_out_bf16(const AttnShape& a, const uint16_t* phiq,
+                                const uint16_t* phik, const uint16_t* v,
+                                const float* state, int64_t state_seg_stride,
+                                int64_t state_bh_stride, float* out, hipStream_t st);
+hipError_t launch_attn_out_f32(const AttnShape& a, const float* phiq, const float* phik,
+                               const float* v, float* state, int64_t state_seg_stride,
+                               int64_t state_bh_stride, float* out, hipStream_t st);
+
+// Decode: per (b, h): S += phik v^T; z += phik; out = phiq^T S [/(phiq^T z + delta)].
+hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq,
+                               const float* phik, const void* v, int v_bf16, float* S,
+                               float* z, float* out, int normalize, float delta,
+                               hipStream_t st);
+
+// Copies (S0, z0) or zeros into (S, z): used when n = 0.
+hipError_t launch_state_init(int64_t BH, int m, int dv, const float* S0, const float* z0,
+                             float* S, float* z, hipStream_t st);
+
+}  // namespace llops
