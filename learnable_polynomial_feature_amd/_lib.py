@@ -269,6 +269,12 @@ class KernelTimer:
         self.capacity = capacity
         self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(capacity)]
+        # torch creates the underlying HIP event on first record; record each
+        # once so every handle passed to the library is a live event
+        for pair in self.events:
+            for e in pair:
+                e.record()
+        torch.cuda.synchronize()
         self._ev = (ctypes.c_void_p * (2 * capacity))(
             *[e.cuda_event for pair in self.events for e in pair])
         self._names = (ctypes.c_char_p * capacity)()
