@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (calibrates rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE against known bytes)")
     return ap.parse_args()
 
 
@@ -205,6 +208,37 @@ def cpu_baseline(w, budget_s):
                       f"extrapolated x{w.batch * w.heads}/{done}"}
 
 
+def copy_probe(torch, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc its
+    FETCH_SIZE / WRITE_SIZE read what `nbytes` of HBM traffic reads as."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} x {nbytes} bytes")
+    del x, y
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "learnable_polynomial_feature_amd", "csrc", rec["source"])
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if sha != rec["source_sha256"]:
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -218,6 +252,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     lib.library()
+    if args.copy_probe:
+        copy_probe(torch)
     w = WORKLOADS[args.workload]
     if w.steps:
         raise SystemExit("use the default causal workload; decode is reported in the same line")
@@ -232,7 +268,8 @@ def main():
         ach = feat_flops / (feat_ms * 1e-3) / 1e12
         roofline = {"kernel": "featmap_bf16", "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": load_traffic("featmap_bf16"),
                     "avg_ms": round(feat_ms, 4), "flops_per_launch": feat_flops}
     line = {
         "metric": "causal LLoPS fwd tokens/sec at n=65536,p=2,t=4,m=256; % MFMA peak; decode GB/s",
@@ -270,7 +307,8 @@ def main():
             "roofline": None if st_gb is None else {
                 "kernel": "decode_state", "bound": "hbm", "achieved": round(st_gb, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(st_gb / PEAK_HBM_GBPS, 4),
-                "traffic": None, "bytes_per_launch": decode_state_bytes(wd)},
+                "traffic": load_traffic("decode_state"),
+                "bytes_per_launch": decode_state_bytes(wd)},
         }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
