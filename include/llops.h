@@ -98,10 +98,14 @@ size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry);
  * (notes, key design 2; paper Sec. 3: p*t projections, Hadamard product over
  * j, sum over r). X [batch][heads][n][d] (in_dtype), Theta per the layout
  * above (in_dtype), phi [batch][heads][n][m] (out_dtype). normalize, delta,
- * dv and chunk are ignored. No workspace.
+ * dv and chunk are ignored. ws: llops_workspace_bytes(shape,
+ * LLOPS_ENTRY_FEATMAP) bytes of device scratch (a repacked copy of Theta for
+ * the bf16 shapes that have an unrolled kernel; 0 bytes otherwise, and ws may
+ * then be null).
  */
 llops_status_t llops_featmap(const llops_shape_t* shape, const void* X,
-                             const void* theta, void* phi, hipStream_t stream);
+                             const void* theta, void* phi, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /*
  * llops_linattn_fwd -- non-causal linear attention

@@ -59,7 +59,7 @@ def library(path: str | None = None) -> ctypes.CDLL:
     SP = ctypes.POINTER(Shape)
     lib.llops_workspace_bytes.argtypes = [SP, ctypes.c_int32]
     lib.llops_workspace_bytes.restype = ctypes.c_size_t
-    lib.llops_featmap.argtypes = [SP, _P, _P, _P, _P]
+    lib.llops_featmap.argtypes = [SP, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_featmap.restype = ctypes.c_int
     lib.llops_linattn_fwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_linattn_fwd.restype = ctypes.c_int
@@ -138,7 +138,7 @@ def _workspace(shape: Shape, entry: int, device, ws):
 
 
 # ---------------------------------------------------------------------------
-def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32):
+def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32, workspace=None):
     """phi = sum_r prod_j X Theta_{j,r} [squared]; X [B, H, n, d] -> phi [B, H, n, m]."""
     X = _dev(X, "X")
     theta = _dev(theta, "theta")
@@ -154,7 +154,9 @@ def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32):
     shape = make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=square,
                        theta_per_head=per_head, in_dtype=_dt(X), out_dtype=odt)
     lib = library()
-    _check(lib.llops_featmap(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(out), _stream(X)))
+    ws, wsb = _workspace(shape, ENTRY_FEATMAP, X.device, workspace)
+    _check(lib.llops_featmap(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(out), _ptr(ws), wsb,
+                             _stream(X)))
     return out
 
 

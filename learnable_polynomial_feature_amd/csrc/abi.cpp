@@ -60,8 +60,17 @@ SegPlan seg_plan(const llops_shape_t* s, bool causal) {
 }
 
 struct WsLayout {
-  size_t phiq, phik, seg, tot, total;
+  size_t phiq, phik, seg, tot, pkq, pkk, total;
 };
+
+llops::FeatShape feat_shape(const llops_shape_t* s, int64_t n, int out_bf16);
+
+// Scratch for the fragment-order copy of one Theta set (bf16 shapes with an
+// unrolled feature-map kernel only).
+size_t pack_bytes(const llops_shape_t* s, int64_t n) {
+  if (s->in_dtype != LLOPS_BF16) return 0;
+  return llops::featmap_pack_bytes(feat_shape(s, n, 1));
+}
 
 WsLayout ws_layout(const llops_shape_t* s, int entry) {
   WsLayout w{};
@@ -69,7 +78,10 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
   const size_t BH = static_cast<size_t>(s->batch * s->heads);
   const size_t per = static_cast<size_t>(s->m) * s->dv + s->m;
   size_t off = 0;
-  if (entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) {
+  if (entry == LLOPS_ENTRY_FEATMAP) {
+    w.pkq = off;
+    off = round_up(off + pack_bytes(s, s->n), 256);
+  } else if (entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) {
     const SegPlan sp = seg_plan(s, entry == LLOPS_ENTRY_CAUSAL);
     const size_t phib = BH * static_cast<size_t>(s->n) * s->m * esz;
     w.phiq = off;
@@ -80,6 +92,11 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
     off = round_up(off + BH * sp.nseg * per * sizeof(float), 256);
     w.tot = off;
     if (entry == LLOPS_ENTRY_LINATTN) off = round_up(off + BH * per * sizeof(float), 256);
+    const size_t pkb = pack_bytes(s, s->n);
+    w.pkq = off;
+    off = round_up(off + pkb, 256);
+    w.pkk = off;
+    off = round_up(off + pkb, 256);
   } else if (entry == LLOPS_ENTRY_DECODE) {
     const size_t phib = BH * s->m * sizeof(float);
     w.phiq = off;
@@ -228,7 +245,7 @@ llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, con
   const llops::AttnShape a = attn_shape(s, causal);
   const int64_t per = static_cast<int64_t>(s->m) * s->dv + s->m;
   float* seg = reinterpret_cast<float*>(w + L.seg);
-  llops::FeatJob jobs[2] = {{Q, tq, w + L.phiq}, {K, tk, w + L.phik}};
+  llops::FeatJob jobs[2] = {{Q, tq, w + L.phiq, w + L.pkq}, {K, tk, w + L.phik, w + L.pkk}};
   const llops::FeatShape fs = feat_shape(s, s->n, bf16 ? 1 : 0);
   if (bf16) {
     LLOPS_HIP(llops::launch_featmap_bf16(fs, jobs, 2, st), "featmap");
@@ -326,7 +343,7 @@ size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
 }
 
 llops_status_t llops_featmap(const llops_shape_t* s, const void* X, const void* theta, void* phi,
-                             hipStream_t st) {
+                             void* ws, size_t ws_bytes, hipStream_t st) {
   LLOPS_TRY(validate(s, LLOPS_ENTRY_FEATMAP));
   if (s->batch * s->heads == 0 || s->n == 0) return LLOPS_OK;  // empty: pointers may be null
   LLOPS_TRY(need(X, "X"));
@@ -334,7 +351,12 @@ llops_status_t llops_featmap(const llops_shape_t* s, const void* X, const void* 
   LLOPS_TRY(need(phi, "phi"));
   if (s->in_dtype == LLOPS_F32 && s->out_dtype != LLOPS_F32)
     return fail(LLOPS_ERR_UNSUPPORTED, "fp32 inputs produce fp32 phi only");
-  llops::FeatJob job{X, theta, phi};
+  const WsLayout L = ws_layout(s, LLOPS_ENTRY_FEATMAP);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (L.total && !ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  if (ws) LLOPS_TRY(opt(ws, "ws"));
+  llops::FeatJob job{X, theta, phi, L.total ? static_cast<char*>(ws) + L.pkq : nullptr};
   const llops::FeatShape fs = feat_shape(s, s->n, s->out_dtype == LLOPS_BF16 ? 1 : 0);
   if (s->in_dtype == LLOPS_BF16)
     LLOPS_HIP(llops::launch_featmap_bf16(fs, &job, 1, st), "featmap");
@@ -381,7 +403,7 @@ llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const vo
   char* w = static_cast<char*>(ws);
   float* fq = reinterpret_cast<float*>(w + L.phiq);
   float* fk = reinterpret_cast<float*>(w + L.phik);
-  llops::FeatJob jobs[2] = {{q, theta_q, fq}, {k, theta_k, fk}};
+  llops::FeatJob jobs[2] = {{q, theta_q, fq, nullptr}, {k, theta_k, fk, nullptr}};
   const llops::FeatShape fs = feat_shape(s, 1, 0);
   const bool bf16 = s->in_dtype == LLOPS_BF16;
   if (bf16)

@@ -51,6 +51,21 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l (h = l / 32, c = l % 32): A holds row c, k = 8h..8h+7; B holds
+// column c, k = 8h..8h+7; D element 4i+e holds row 8i + 4h + e of column c.
+// On gfx950 this shape issues twice the flops per cycle of 16x16x32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
 // ---- 8x8 bf16 transpose in registers --------------------------------------
 // in[r] holds row r (8 bf16 = 4 dwords; dword w = elements 2w, 2w+1).
 // out[c] receives column c (8 bf16: rows 0..7).

@@ -238,6 +238,327 @@ __global__ __launch_bounds__(256) void featmap_f32_kernel(FeatArgsF a) {
   }
 }
 
+// ---- fast bf16 path: (d, p, t) known at compile time, 32x32x16 MFMA ----
+//
+// Theta is first repacked (pack_theta) into fragment order: for head h,
+// 32-feature block fb, rank r, degree index j and 16-deep k-step ks, the
+// 64 lanes' B fragments of v_mfma_f32_32x32x16_bf16 lie next to each other
+// (lane l: features fb*32 + l%32, k = ks*16 + 8*(l/32) .. +7). One stage
+// (fb, r) is then a contiguous P*d*64-byte block that workgroups copy into
+// LDS with plain 16-byte loads, and fragment reads from LDS are lane-linear
+// (bank-conflict free, no padding).
+//
+// A workgroup of 4 waves owns 256 rows of one head; each wave keeps 2 row
+// tiles of 32 rows of X as register-resident A fragments. Stages run one
+// rank at a time through a 2-slot LDS ring, with the global loads of stage
+// s+2 in flight while stage s computes. About 72 KiB of LDS and <= 256 VGPRs
+// let two workgroups share a CU, so one workgroup's barrier and VALU
+// epilogue overlap the other's MFMAs. The epilogue parks phi in a
+// wave-private LDS area and writes whole 128-byte row segments.
+struct FastArgs {
+  FeatJob job[2];
+  int64_t B, H, n;
+  int m;
+  int64_t pk_hstride;  // packed elements between heads (0 = shared)
+  int square;
+  int fg;              // 32-feature blocks per phi flush (1 or 2)
+};
+
+constexpr int kFastRT = 2;                         // 32-row tiles per wave
+constexpr int kFastNW = 4;                         // waves per workgroup
+constexpr int kFastRows = kFastNW * kFastRT * 32;  // rows per workgroup
+
+template <int D, int P, bool OUT_BF16>
+struct FastGeom {
+  static constexpr int KS = D / 16;
+  static constexpr int STAGE = P * KS * 512;       // bf16 elements per stage (P*KS fragments)
+  static constexpr int LPT = P * KS * 64 / (kFastNW * 64);  // 16-byte loads per thread per stage
+  static constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  static constexpr int FGMAX = OUT_BF16 ? 2 : 1;
+  static constexpr int PROW = FGMAX * 32 * ESZ + 16;  // staging row bytes
+  static constexpr int WROWS = kFastRT * 32;
+  static constexpr size_t lds_bytes() {
+    return 2ull * STAGE * 2 + 1ull * kFastNW * WROWS * PROW + 1ull * kFastNW * WROWS * 8;
+  }
+};
+
+// theta [H'][p][t][d][m] -> packed [H'][m/32][t][p][d/16][64 lanes][8]
+__global__ __launch_bounds__(256) void pack_theta_kernel(const uint16_t* __restrict__ th,
+                                                         uint16_t* __restrict__ pk, int64_t total,
+                                                         int P, int T, int D, int m) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int KS = D / 16, FB = m / 32;
+  const int lane = static_cast<int>(idx & 63);
+  int64_t q = idx >> 6;
+  const int ks = static_cast<int>(q % KS);
+  q /= KS;
+  const int j = static_cast<int>(q % P);
+  q /= P;
+  const int r = static_cast<int>(q % T);
+  q /= T;
+  const int fb = static_cast<int>(q % FB);
+  const int64_t h = q / FB;
+  const int k0 = ks * 16 + (lane >> 5) * 8;
+  const uint16_t* src = th + (((h * P + j) * T + r) * D + k0) * m + fb * 32 + (lane & 31);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(m)]) |
+           (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(m)]) << 16);
+  st16(pk + idx * 8, u32x4{w[0], w[1], w[2], w[3]});
+}
+
+template <int D, int P, int T, bool OUT_BF16>
+__global__ __launch_bounds__(kFastNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void featmap_fast(FastArgs a) {
+  using G = FastGeom<D, P, OUT_BF16>;
+  constexpr int RT = kFastRT;
+  constexpr int KS = G::KS;
+  constexpr int LPT = G::LPT;
+  static_assert(D % 32 == 0, "D must be a multiple of 32");
+  static_assert((P * KS * 64) % (kFastNW * 64) == 0, "a stage splits evenly over the threads");
+  extern __shared__ __align__(16) uint16_t smem[];
+
+  const FeatJob job = a.job[blockIdx.z];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, c32 = lane & 31;
+  const int64_t h = blockIdx.y;
+  const int64_t R = a.B * a.n;
+  const int64_t wrow0 = static_cast<int64_t>(blockIdx.x) * kFastRows + wave * G::WROWS;
+
+  uint8_t* pst = reinterpret_cast<uint8_t*>(smem + 2 * G::STAGE) + wave * G::WROWS * G::PROW;
+  int64_t* rowoff = reinterpret_cast<int64_t*>(reinterpret_cast<uint8_t*>(smem + 2 * G::STAGE) +
+                                               kFastNW * G::WROWS * G::PROW) + wave * G::WROWS;
+  // element offset of each of this wave's rows in phi (-1: past the end)
+  for (int i = lane; i < G::WROWS; i += 64) {
+    const int64_t r = wrow0 + i;
+    int64_t off = -1;
+    if (r < R) {
+      const int64_t b = r / a.n;
+      off = ((b * a.H + h) * a.n + (r - b * a.n)) * a.m;
+    }
+    rowoff[i] = off;
+  }
+
+  const uint16_t* pk = static_cast<const uint16_t*>(job.theta_pk) + h * a.pk_hstride;
+  const int FB = a.m / 32;
+  const int nstages = FB * T;  // stage s = (fb, r) = (s / T, s % T)
+  auto load_stage = [&](int s, u32x4 (&v)[LPT]) {
+    const uint16_t* src = pk + static_cast<int64_t>(s) * G::STAGE + tid * 8;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) v[i] = ld16(src + i * (kFastNW * 64 * 8));
+  };
+  auto write_stage = [&](uint16_t* buf, const u32x4 (&v)[LPT]) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) st16(buf + (i * kFastNW * 64 + tid) * 8, v[i]);
+  };
+
+  u32x4 nxt[LPT], nxt2[LPT];
+  load_stage(0, nxt);
+  if (nstages > 1) load_stage(1, nxt2);
+
+  // ---- X fragments: lane holds row rt*32 + c32, k = ks*16 + 8*hh .. +7
+  const uint16_t* X = static_cast<const uint16_t*>(job.X);
+  bf16x8 xf[RT][KS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t r = wrow0 + rt * 32 + c32;
+    const bool ok = r < R;
+    int64_t rho = 0;
+    if (ok) {
+      const int64_t b = r / a.n;
+      rho = (b * a.H + h) * a.n + (r - b * a.n);
+    }
+    const uint16_t* src = X + rho * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      xf[rt][ks] = as_bf16x8(ok ? ld16(src + ks * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u});
+  }
+  write_stage(smem, nxt);
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) nxt[i] = nxt2[i];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  f32x16 sum[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
+  // phi of finished feature blocks waits in the staging area until a.fg
+  // blocks (one 128-byte row segment) or the last block are parked
+  int parked = 0, park_fb0 = 0;
+  bool ready = false;
+
+  auto flush = [&]() {
+    uint8_t* out = static_cast<uint8_t*>(job.phi);
+    constexpr int CPR = G::FGMAX * 2 * G::ESZ;  // 16-byte chunks per full row segment
+    if (parked == G::FGMAX) {
+      // whole segments: fixed trip count, so all LDS reads issue before the stores
+      constexpr int ITER = G::WROWS * CPR / 64;
+      u32x4 v[ITER];
+      int64_t off[ITER];
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int idx = lane + 64 * it;
+        const int row = idx / CPR, ch = idx % CPR;
+        off[it] = rowoff[row];
+        v[it] = ld16(pst + row * G::PROW + ch * 16);
+      }
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int ch = (lane + 64 * it) % CPR;
+        if (off[it] >= 0) st16(out + (off[it] + park_fb0 * 32) * G::ESZ + ch * 16, v[it]);
+      }
+    } else {
+      const int cpr = parked * 2 * G::ESZ;
+      const int total = G::WROWS * cpr;
+      for (int idx = lane; idx < total; idx += 64) {
+        const int row = idx / cpr, ch = idx - (idx / cpr) * cpr;
+        const int64_t o = rowoff[row];
+        if (o >= 0)
+          st16(out + (o + park_fb0 * 32) * G::ESZ + ch * 16, ld16(pst + row * G::PROW + ch * 16));
+      }
+    }
+    parked = 0;
+    ready = false;
+  };
+
+  const uint16_t* fbase = smem + lane * 8;
+  for (int s = 0; s < nstages; ++s) {
+    const int fb = s / T, r = s - (s / T) * T;
+    if (s + 2 < nstages) load_stage(s + 2, nxt2);
+    // fragment (j, ks) of this stage sits at buf + (j*KS + ks)*512 + lane*8;
+    // the stream below always holds the next fragment in flight
+    const uint16_t* buf = fbase + (s & 1) * G::STAGE;
+    bf16x8 fcur = as_bf16x8(ld16(buf));
+    f32x16 prod[RT];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      f32x16 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int nf = j * KS + ks + 1;
+        bf16x8 fnext = fcur;
+        if (nf < P * KS) fnext = as_bf16x8(ld16(buf + nf * 512));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32x32x16(xf[rt][ks], fcur, acc[rt]);
+        fcur = fnext;
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) prod[rt] = (j == 0) ? acc[rt] : prod[rt] * acc[rt];
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sum[rt] += prod[rt];
+    if (r == T - 1) {  // feature block complete: square and park it
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x16 v = sum[rt];
+        if (a.square) v *= v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint8_t* dst = pst + (rt * 32 + 8 * i + 4 * hh + e) * G::PROW +
+                           (parked * 32 + c32) * G::ESZ;
+            if (OUT_BF16)
+              *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(v[4 * i + e]);
+            else
+              *reinterpret_cast<float*>(dst) = v[4 * i + e];
+          }
+        sum[rt] = zero16();
+      }
+      if (parked == 0) park_fb0 = fb;
+      ++parked;
+      ready = parked == a.fg || fb + 1 == FB;
+    }
+    if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, nxt);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) nxt[i] = nxt2[i];
+    // the staging area is private to this wave and LDS accesses of one wave
+    // complete in order, so the parked rows can be read back right away
+    if (ready) flush();
+  }
+}
+
+template <int D, int P, int T, bool OUT_BF16>
+hipError_t launch_fast_t(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
+  using G = FastGeom<D, P, OUT_BF16>;
+  FastArgs a{};
+  a.job[0] = jobs[0];
+  a.job[1] = njobs > 1 ? jobs[1] : jobs[0];
+  a.B = s.B;
+  a.H = s.H;
+  a.n = s.n;
+  a.m = s.m;
+  a.pk_hstride = s.theta_per_head ? static_cast<int64_t>(P) * T * D * s.m : 0;
+  a.square = s.square;
+  const int FB = s.m / 32;
+  a.fg = FB < G::FGMAX ? FB : G::FGMAX;
+  const int64_t tiles = (s.B * s.n + kFastRows - 1) / kFastRows;
+  if (tiles > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
+  // repack Theta of every job into its fragment-order buffer
+  const int64_t th_heads = s.theta_per_head ? s.H : 1;
+  const int64_t total = th_heads * P * T * D * s.m / 8;
+  for (int jb = 0; jb < njobs; ++jb) {
+    if (jb == 1 && jobs[1].theta == jobs[0].theta && jobs[1].theta_pk == jobs[0].theta_pk) break;
+    LLOPS_LAUNCH("pack_theta", st, pack_theta_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
+                 dim3(256), 0, st, static_cast<const uint16_t*>(jobs[jb].theta),
+                 static_cast<uint16_t*>(jobs[jb].theta_pk), total, P, T, D, s.m);
+  }
+  const size_t lds = G::lds_bytes();
+  auto* k = featmap_fast<D, P, T, OUT_BF16>;
+  const hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H), njobs);
+  LLOPS_LAUNCH("featmap_bf16", st, k, grid, dim3(kFastNW * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int P, int T>
+hipError_t launch_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
+  return s.out_bf16 ? launch_fast_t<D, P, T, true>(s, jobs, njobs, st)
+                    : launch_fast_t<D, P, T, false>(s, jobs, njobs, st);
+}
+
+int fast_key(const FeatShape& s) {
+  if (s.B * s.n < 2048 || s.m % 32 != 0) return 0;
+  const int key = s.d * 10000 + s.p * 100 + s.t;
+  switch (key) {
+    case 1280204:
+    case 1280201:
+    case 640204:
+    case 640308: return key;
+    default: return 0;
+  }
+}
+
+bool try_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st, hipError_t* err) {
+  // callers without scratch for the repacked Theta take the generic kernel
+  for (int jb = 0; jb < njobs; ++jb)
+    if (!jobs[jb].theta_pk) return false;
+  switch (fast_key(s)) {
+    case 1280204: *err = launch_fast<128, 2, 4>(s, jobs, njobs, st); return true;
+    case 1280201: *err = launch_fast<128, 2, 1>(s, jobs, njobs, st); return true;
+    case 640204: *err = launch_fast<64, 2, 4>(s, jobs, njobs, st); return true;
+    case 640308: *err = launch_fast<64, 3, 8>(s, jobs, njobs, st); return true;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+size_t featmap_pack_bytes(const FeatShape& s) {
+  if (!fast_key(s)) return 0;
+  const int64_t th_heads = s.theta_per_head ? s.H : 1;
+  return static_cast<size_t>(th_heads) * s.p * s.t * s.d * s.m * sizeof(uint16_t);
+}
+
+namespace {
+
 template <int D>
 hipError_t launch_d(const FeatArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   const hipError_t e = allow_lds(featmap_mfma<D, 4>, lds);
@@ -250,6 +571,8 @@ hipError_t launch_d(const FeatArgs& a, dim3 grid, size_t lds, hipStream_t st) {
 
 hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njobs,
                                hipStream_t st) {
+  hipError_t fast_err = hipSuccess;
+  if (try_fast(s, jobs, njobs, st, &fast_err)) return fast_err;
   FeatArgs a{};
   a.job[0] = jobs[0];
   a.job[1] = njobs > 1 ? jobs[1] : jobs[0];

@@ -33,6 +33,7 @@ struct FeatJob {
   const void* X;
   const void* theta;  // [H][p][t][d][m] or [p][t][d][m]
   void* phi;
+  void* theta_pk;     // featmap_pack_bytes() of scratch for the repacked Theta (or null)
 };
 
 struct FeatShape {
@@ -42,6 +43,10 @@ struct FeatShape {
   int square;
   int out_bf16;  // phi storage: 1 = bf16, 0 = fp32
 };
+
+// Scratch bytes per job for the fragment-order copy of Theta that the
+// unrolled bf16 kernels read (0 when the shape takes the generic kernel).
+size_t featmap_pack_bytes(const FeatShape& s);
 
 // bf16 inputs on MFMA; runs `njobs` (1 or 2) jobs of the same shape in one launch.
 hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njobs,

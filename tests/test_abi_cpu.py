@@ -106,21 +106,41 @@ def test_status_strings(L):
 @fake_ptr
 def test_featmap_validation(L, bad, code):
     s = _shape(**bad)
-    st = L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None)
+    st = L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None)
     assert st == code, _err(L)
 
 
 @fake_ptr
 def test_featmap_null_and_alignment(L):
     s = _shape()
-    assert L.llops_featmap(None, FAKE, FAKE, FAKE, None) == 1
-    assert L.llops_featmap(ctypes.byref(s), None, FAKE, FAKE, None) == 1
+    assert L.llops_featmap(None, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert L.llops_featmap(ctypes.byref(s), None, FAKE, FAKE, None, 0, None) == 1
     assert "X is null" in _err(L)
-    assert L.llops_featmap(ctypes.byref(s), FAKE, MISALIGNED, FAKE, None) == 1
+    assert L.llops_featmap(ctypes.byref(s), FAKE, MISALIGNED, FAKE, None, 0, None) == 1
     assert "aligned" in _err(L)
     # fp32 inputs cannot produce a bf16 phi
     s = _shape(in_dtype=_lib.F32, out_dtype=_lib.BF16)
-    assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None) == 2
+    assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None) == 2
+
+
+@fake_ptr
+def test_featmap_workspace(L):
+    """Shapes with an unrolled bf16 kernel need scratch for the repacked
+    Theta (heads * p * t * d * m bf16); the rest need none."""
+    s = _shape(batch=1, heads=4, n=4096, d=128, m=256, p=2, t=4)
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP)
+    assert need == 4 * 2 * 4 * 128 * 256 * 2
+    assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, need - 1, None) == 3
+    assert "workspace" in _err(L)
+    assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None, need, None) == 1
+    shared = _shape(batch=1, heads=4, n=4096, d=128, m=256, p=2, t=4, theta_per_head=0)
+    assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP) == need // 4
+    for small in (_shape(n=100), _shape(in_dtype=_lib.F32), _shape(n=4096, d=96, m=64)):
+        assert L.llops_workspace_bytes(ctypes.byref(small), _lib.ENTRY_FEATMAP) == 0
+    # the attention entry points hold two repacked copies (Theta_q and Theta_k)
+    a = _shape(batch=1, heads=4, n=4096, d=128, dv=128, m=256, p=2, t=4)
+    big = L.llops_workspace_bytes(ctypes.byref(a), _lib.ENTRY_CAUSAL)
+    assert big >= 2 * need
 
 
 @pytest.mark.parametrize("bad,code", [

@@ -52,6 +52,16 @@ FEAT_CASES = [
     (1, 1, 600, 256, 64, 2, 2, False, False, False),
     (1, 1, 64, 128, 32, 8, 1, False, False, False),
     (2, 1, 257, 96, 80, 3, 5, True, True, True),
+    # >= 2048 rows per head: the unrolled 512-row-tile kernels, with ragged
+    # tiles, batch boundaries inside a tile and partial phi flush groups
+    (2, 2, 1100, 128, 256, 2, 4, True, False, False),
+    (2, 2, 1100, 128, 256, 2, 4, True, False, True),
+    (3, 1, 1000, 128, 64, 2, 1, False, True, True),
+    (1, 2, 2100, 64, 64, 2, 4, True, False, True),
+    (2, 1, 1500, 64, 128, 3, 8, True, False, False),
+    (1, 1, 4096, 128, 80, 2, 4, False, False, False),
+    (1, 1, 4096, 128, 80, 2, 4, True, False, True),
+    (5, 3, 613, 128, 48, 2, 4, True, False, False),
 ]
 
 
@@ -67,6 +77,21 @@ def test_featmap_bf16(lib, case):
     want = O.featmap_bh(x["Q"], x["theta_q"], square=square)
     err = rel_fro(host(phi), want)
     assert err <= (TOL_FEAT_BF16_OUT if out_bf16 else TOL_FEAT_BF16_IN), err
+
+
+@pytest.mark.parametrize("case", [(1, 2, 3000, 128, 256, 2, 4), (2, 1, 1500, 64, 128, 3, 8),
+                                  (1, 1, 300, 64, 64, 2, 4)])
+def test_featmap_bf16_out_is_rounded_f32_out(lib, case):
+    """Storing phi as bf16 rounds the same fp32 value the fp32 output holds
+    (round to nearest even), bit for bit."""
+    B, H, n, d, m, p, t = case
+    w = _w(B, H, n, d, 16, m, p, t)
+    _, g = _inputs(w)
+    announce(f"featmap bf16 vs f32 out {case}")
+    f32 = lib.llops_featmap(g["Q"], g["theta_q"], square=True, out_dtype=torch.float32)
+    b16 = lib.llops_featmap(g["Q"], g["theta_q"], square=True, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(f32.to(torch.bfloat16), b16)
 
 
 @pytest.mark.parametrize("case", [(2, 3, 37, 16, 32, 2, 2, True), (1, 1, 20, 7, 5, 3, 2, False),
@@ -104,6 +129,8 @@ CAUSAL_CASES = [
     (2, 1, 90, 64, 48, 96, 2, 3, True, True, 64),
     (1, 1, 1, 64, 64, 64, 2, 2, True, True, 64),
     (3, 2, 33, 128, 128, 256, 2, 4, True, True, 64),
+    (2, 2, 1500, 128, 128, 256, 2, 4, True, True, 128),
+    (1, 2, 2500, 64, 64, 128, 3, 8, True, True, 64),
 ]
 
 
