@@ -252,21 +252,30 @@ llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, con
     const uint16_t* pq = reinterpret_cast<const uint16_t*>(w + L.phiq);
     const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);
     const uint16_t* vv = static_cast<const uint16_t*>(V);
-    LLOPS_HIP(llops::launch_seg_state_bf16(a, pk, vv, seg, st), "seg_state");
+    const bool mf32 = llops::attn32_supported(a);  // 32x32x16 kernels for this (m, dv)
+    if (mf32)
+      LLOPS_HIP(llops::launch_seg_state32(a, pk, vv, seg, st), "seg_state");
+    else
+      LLOPS_HIP(llops::launch_seg_state_bf16(a, pk, vv, seg, st), "seg_state");
+    const float* state = seg;
+    int64_t st_seg = per, st_bh = per * a.nseg;
     if (causal) {
       LLOPS_HIP(llops::launch_seg_scan(a, seg, S0, z0, S_final, z_final, 1, st), "seg_scan");
-      LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, seg, per, per * a.nseg,
-                                            static_cast<float*>(out), st),
-                "attn_out");
     } else {
       float* tot = reinterpret_cast<float*>(w + L.tot);
       LLOPS_HIP(llops::launch_seg_scan(a, seg, nullptr, nullptr, tot,
                                        tot + static_cast<int64_t>(s->m) * s->dv, 0, st),
                 "seg_scan");
-      LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, tot, 0, per, static_cast<float*>(out),
-                                            st),
-                "attn_out");
+      state = tot;
+      st_seg = 0;
+      st_bh = per;
     }
+    float* o = static_cast<float*>(out);
+    if (mf32)
+      LLOPS_HIP(llops::launch_attn_out32(a, pq, pk, vv, state, st_seg, st_bh, o, st), "attn_out");
+    else
+      LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, state, st_seg, st_bh, o, st),
+                "attn_out");
   } else {
     LLOPS_HIP(llops::launch_featmap_f32(fs, jobs, 2, st), "featmap");
     const float* pq = reinterpret_cast<const float*>(w + L.phiq);

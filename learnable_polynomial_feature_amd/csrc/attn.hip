@@ -71,7 +71,10 @@ __global__ __launch_bounds__(256) void seg_state_bf16(AttnArgs a, const uint16_t
   const int m = a.m, dv = NT * 16;
   uint16_t* KT = smem;             // [m][LROW]   phi_K^T
   uint16_t* VT = smem + m * LROW;  // [dv][LROW]  V^T
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: MFMAs under a condition on it must branch, not
+  // be masked through EXEC (an MFMA runs for the whole wave regardless)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t bh = blockIdx.y;
   const int gseg = blockIdx.x;
@@ -197,7 +200,10 @@ __global__ __launch_bounds__(256) void attn_out_bf16(AttnArgs a, const uint16_t*
   float* zs = reinterpret_cast<float*>(As + C * CROW);  // [m]
   float* dens = zs + m;                                 // [C]  1 / (den + delta)
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: MFMAs under a condition on it must branch, not
+  // be masked through EXEC (an MFMA runs for the whole wave regardless)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t bh = blockIdx.y;
   const int gseg = blockIdx.x;

@@ -1,0 +1,471 @@
+// Segment passes of LLoPS linear attention on 32x32x16 bf16 MFMA.
+//
+//   causal:     out_i = phi_Q,i S_i [/ (phi_Q,i z_i + delta)], S_i = sum_{j<=i} phi_K,j v_j^T
+//     (LLoPS paper Sec. 1: streaming form with a constant-size state; low-rank
+//      attention blog: causal masking by incremental cumulative sums)
+//   non-causal: out = phi_Q S [/ (phi_Q z + delta)] with S, z over all tokens
+//     (LLoPS notes, overall framework; blog, Performer section; SLAY notes,
+//      key design 3 for the +delta)
+//
+// A workgroup has one wave per 32 value columns (dv / 32 waves). Each wave
+// owns its columns of the fp32 state S (m/32 accumulator tiles) and a share of
+// the normaliser state z, kept as accumulator tiles of S against an all-ones
+// value block so that z and phi_Q . z come out of the same MFMAs. A segment is
+// walked in chunks of 32 tokens whose phi_Q / phi_K / V rows are staged in
+// LDS in their natural row-major layout (double buffered; the next chunk is
+// prefetched into registers while the current one computes). Operands that
+// contract over tokens are read with ds_read_b64_tr_b16 (transposing LDS
+// reads), so no transposed copy is ever stored.
+//
+// Fragment conventions for v_mfma_f32_32x32x16_bf16 (lane l, c = l % 32,
+// hh = l / 32): an accumulator element 4i+e holds row 8i + 4hh + e of column
+// c. Taken as an operand, rows 0..15 of a tile (elements 0..7) put k-values
+// {4hh..4hh+3, 8+4hh..8+4hh+3} in lane half hh; every other operand of the
+// same product is read with that same k order ("P16" below).
+#include "device.h"
+#include "kernels.h"
+
+namespace llops {
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 32;  // tokens per chunk
+
+__device__ __forceinline__ uint2 lds_tr64(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(
+          reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// B-style fragment (column = lane % 32, k in P16 order) of the matrix
+// M[k][col] stored row-major in LDS: rows kbase..kbase+15, columns
+// cbase..cbase+31. Within each 16-lane group the transposing read hands lane
+// q column q of 4 consecutive rows supplied by lanes q/4 + 4i.
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int stride, int kbase, int cbase,
+                                          int lane) {
+  const int s = lane & 15, G = lane >> 4;
+  const int row = kbase + 4 * (G >> 1) + (s >> 2);
+  const int col = cbase + (G & 1) * 16 + 4 * (s & 3);
+  const uint2 lo = lds_tr64(base + row * stride + col);
+  const uint2 hi = lds_tr64(base + (row + 8) * stride + col);
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// A-style fragment with k in P16 order from row-major M[row][k] in LDS:
+// row = rbase + lane % 32, k = kbase + {4hh..4hh+3, 8+4hh..8+4hh+3}.
+__device__ __forceinline__ bf16x8 frag_p16(const uint16_t* base, int stride, int rbase, int kbase,
+                                           int lane) {
+  const uint16_t* p = base + (rbase + (lane & 31)) * stride + kbase + 4 * (lane >> 5);
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// Natural-order fragment (k = kbase + 8hh .. +7) of row-major M[row][k].
+__device__ __forceinline__ bf16x8 frag_nat(const uint16_t* base, int stride, int rbase, int kbase,
+                                           int lane) {
+  return as_bf16x8(ld16(base + (rbase + (lane & 31)) * stride + kbase + 8 * (lane >> 5)));
+}
+
+// Accumulator elements [8h, 8h+8) of a fp32 tile as a bf16 operand (P16).
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& t, int h) {
+  return as_bf16x8(u32x4{pack_bf16x2(t[8 * h + 0], t[8 * h + 1]),
+                         pack_bf16x2(t[8 * h + 2], t[8 * h + 3]),
+                         pack_bf16x2(t[8 * h + 4], t[8 * h + 5]),
+                         pack_bf16x2(t[8 * h + 6], t[8 * h + 7])});
+}
+
+struct Seg32Args {
+  int64_t n;
+  int64_t seg_len;   // tokens per segment (multiple of kC)
+  int nseg;
+  int normalize;
+  float delta;
+};
+
+template <int M, int DV>
+struct Seg32Geom {
+  static constexpr int NW = DV / 32;       // waves per workgroup
+  static constexpr int NT = NW * 64;       // threads
+  static constexpr int FT = M / 32;        // feature tiles
+  static constexpr int ZT = FT / NW > 0 ? FT / NW : 1;  // z tiles per wave
+  static constexpr int MP = M + 16;        // LDS row strides (elements): rows shift
+  static constexpr int VP = DV + 16;       //   by 8 banks, conflict-free tr reads
+  static constexpr int BUF = kC * MP * 2 + kC * VP;  // one chunk: phi_Q, phi_K, V
+  static constexpr int QCH = kC * M / 8, VCH = kC * DV / 8;  // 16-byte pieces per chunk
+  static constexpr int LPT_Q = QCH / NT, LPT_V = VCH / NT;
+  static_assert(QCH % NT == 0 && VCH % NT == 0, "chunk splits evenly over the threads");
+  static_assert(FT % NW == 0 || NW % FT == 0, "z tiles split over the waves");
+};
+
+// ============================================================================
+// Pass 1: per-segment (dS, dz) = (phi_K^T V, phi_K^T 1)
+// ============================================================================
+template <int M, int DV>
+__global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
+                                                     const uint16_t* __restrict__ v,
+                                                     float* __restrict__ seg) {
+  using G = Seg32Geom<M, DV>;
+  constexpr int FT = G::FT, MP = G::MP, VP = G::VP, NT = G::NT;
+  constexpr int BUF = kC * MP + kC * VP;  // phi_K and V only
+  constexpr int LK = G::LPT_Q, LV = G::LPT_V;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: MFMAs under a condition on it must branch, not
+  // be masked through EXEC (an MFMA runs for the whole wave regardless)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const uint16_t* Kg = phik + bh * a.n * M;
+  const uint16_t* Vg = v + bh * a.n * DV;
+  const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
+
+  auto load = [&](int c, u32x4 (&rk)[LK], u32x4 (&rv)[LV]) {
+    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
+      rk[i] = (c0 + row < t1) ? ld16(Kg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
+      rv[i] = (c0 + row < t1) ? ld16(Vg + (c0 + row) * DV + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](uint16_t* buf, const u32x4 (&rk)[LK], const u32x4 (&rv)[LV]) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
+      st16(buf + row * MP + col * 8, rk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
+      st16(buf + kC * MP + row * VP + col * 8, rv[i]);
+    }
+  };
+
+  f32x16 S[FT], Z[G::ZT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) S[f] = zero16();
+#pragma unroll
+  for (int z = 0; z < G::ZT; ++z) Z[z] = zero16();
+  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  u32x4 rk[LK], rv[LV];
+  load(0, rk, rv);
+  store(smem, rk, rv);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) load(c + 1, rk, rv);
+    const uint16_t* Ks = smem + (c & 1) * BUF;
+    const uint16_t* Vs = Ks + kC * MP;
+#pragma unroll
+    for (int ks = 0; ks < kC / 16; ++ks) {
+      const bf16x8 vb = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const bf16x8 ka = frag_tr(Ks, MP, ks * 16, f * 32, lane);
+        S[f] = mfma32x32x16(ka, vb, S[f]);
+        if ((f % G::NW) == (w % G::NW) && f / G::NW < G::ZT)
+          Z[f / G::NW] = mfma32x32x16(ka, ones, Z[f / G::NW]);
+      }
+    }
+    if (more) store(smem + ((c + 1) & 1) * BUF, rk, rv);
+    __syncthreads();
+  }
+  float* out = seg + (bh * a.nseg + gseg) * (static_cast<int64_t>(M) * DV + M);
+  const int c32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[(f * 32 + 8 * i + 4 * hh + e) * DV + w * 32 + c32] = S[f][4 * i + e];
+  if (c32 == 0) {
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      if ((f % G::NW) != (w % G::NW) || f / G::NW >= G::ZT) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          out[static_cast<int64_t>(M) * DV + f * 32 + 8 * i + 4 * hh + e] = Z[f / G::NW][4 * i + e];
+    }
+  }
+}
+
+// ============================================================================
+// Pass 2: outputs of one segment, starting from its prefix state
+// ============================================================================
+template <int M, int DV, bool CAUSAL>
+__global__ __launch_bounds__(DV * 2) void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq,
+                                                    const uint16_t* __restrict__ phik,
+                                                    const uint16_t* __restrict__ v,
+                                                    const float* __restrict__ state,
+                                                    int64_t st_seg, int64_t st_bh,
+                                                    float* __restrict__ out) {
+  using G = Seg32Geom<M, DV>;
+  constexpr int FT = G::FT, MP = G::MP, VP = G::VP, NT = G::NT, NW = G::NW, ZT = G::ZT;
+  constexpr int BUF = G::BUF;
+  constexpr int LQ = G::LPT_Q, LV = G::LPT_V;
+  extern __shared__ __align__(16) uint16_t smem[];
+  float* part = reinterpret_cast<float*>(smem + 2 * BUF);  // [NW][kC] z partials
+  float* rsum = part + NW * kC;                            // [kC] masked row sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a scalar: MFMAs under a condition on it must branch, not
+  // be masked through EXEC (an MFMA runs for the whole wave regardless)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, hh = lane >> 5;
+  const int64_t bh = blockIdx.y;
+  const int gseg = blockIdx.x;
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const uint16_t* Qg = phiq + bh * a.n * M;
+  const uint16_t* Kg = phik + bh * a.n * M;
+  const uint16_t* Vg = v + bh * a.n * DV;
+  float* Og = out + bh * a.n * DV;
+  const float* Sin = state + bh * st_bh + gseg * st_seg;
+  const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
+
+  // state: S[f] = rows 32f.. of this wave's 32 columns; Z[z] = z over the
+  // feature tile z*NW + w (all 32 columns hold the same values)
+  f32x16 S[FT], Z[ZT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[f][4 * i + e] = Sin[(f * 32 + 8 * i + 4 * hh + e) * DV + w * 32 + c32];
+#pragma unroll
+  for (int z = 0; z < ZT; ++z) {
+    const int f = z * NW + w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Z[z][4 * i + e] = (f < FT) ? Sin[static_cast<int64_t>(M) * DV + f * 32 + 8 * i + 4 * hh + e] : 0.f;
+  }
+  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  auto load = [&](int c, u32x4 (&rq)[LQ], u32x4 (&rk)[LQ], u32x4 (&rv)[LV]) {
+    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
+      const bool ok = c0 + row < t1;
+      rq[i] = ok ? ld16(Qg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
+      if (CAUSAL) rk[i] = ok ? ld16(Kg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (CAUSAL) {
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
+        rv[i] = (c0 + row < t1) ? ld16(Vg + (c0 + row) * DV + col * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store = [&](uint16_t* buf, const u32x4 (&rq)[LQ], const u32x4 (&rk)[LQ],
+                   const u32x4 (&rv)[LV]) {
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
+      st16(buf + row * MP + col * 8, rq[i]);
+      if (CAUSAL) st16(buf + kC * MP + row * MP + col * 8, rk[i]);
+    }
+    if (CAUSAL) {
+#pragma unroll
+      for (int i = 0; i < LV; ++i) {
+        const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
+        st16(buf + 2 * kC * MP + row * VP + col * 8, rv[i]);
+      }
+    }
+  };
+
+  u32x4 rq[LQ], rk[LQ], rv[LV];
+  load(0, rq, rk, rv);
+  store(smem, rq, rk, rv);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    if (more) load(c + 1, rq, rk, rv);
+    const uint16_t* Qs = smem + (c & 1) * BUF;
+    const uint16_t* Ks = Qs + kC * MP;
+    const uint16_t* Vs = Qs + 2 * kC * MP;
+    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+
+    // ---- masked A^T = phi_K phi_Q^T (keys x queries), every wave
+    f32x16 At = zero16();
+    float rs = 0.f;
+    bf16x8 afr[2];
+    if (CAUSAL) {
+#pragma unroll
+      for (int ks = 0; ks < M / 16; ++ks)
+        At = mfma32x32x16(frag_nat(Ks, MP, 0, ks * 16, lane), frag_nat(Qs, MP, 0, ks * 16, lane), At);
+      // key 8i + 4hh + e reaches query c32 iff it is not later
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (8 * i + 4 * hh + e > c32) At[4 * i + e] = 0.f;
+      afr[0] = acc_frag(At, 0);
+      afr[1] = acc_frag(At, 1);
+      if (a.normalize) {  // row sums of the bf16-rounded weights the A V product uses
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 u = __builtin_bit_cast(u32x4, afr[h]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            rs += __uint_as_float(u[q] << 16) + __uint_as_float(u[q] & 0xFFFF0000u);
+        }
+        rs += __shfl_xor(rs, 32);
+      }
+    }
+
+    // phases are fenced so that fragment reads are not hoisted across them
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- out = phi_Q S (+ A V); den partial = phi_Q z over this wave's z tiles
+    f32x16 O = zero16(), D = zero16();
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 qa = frag_p16(Qs, MP, 0, f * 32 + h * 16, lane);
+        O = mfma32x32x16(qa, acc_frag(S[f], h), O);
+        if (a.normalize && (f % NW) == (w % NW) && f / NW < ZT)
+          D = mfma32x32x16(qa, acc_frag(Z[f / NW], h), D);
+      }
+    }
+    if (CAUSAL) {
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks)
+        O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, w * 32, lane), O);
+    }
+    if (a.normalize) {
+      // column 0 of D holds this wave's part of phi_Q . z for queries 8i+4hh+e
+      if (c32 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[w * kC + 8 * i + 4 * hh + e] = D[4 * i + e];
+      }
+      if (w == 0 && hh == 0) rsum[c32] = rs;
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- S += phi_K^T V; z += phi_K^T 1
+    if (CAUSAL) {
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks) {
+        const bf16x8 vb = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+#pragma unroll
+        for (int f = 0; f < FT; ++f) {
+          const bf16x8 ka = frag_tr(Ks, MP, ks * 16, f * 32, lane);
+          S[f] = mfma32x32x16(ka, vb, S[f]);
+          if ((f % NW) == (w % NW) && f / NW < ZT) Z[f / NW] = mfma32x32x16(ka, ones, Z[f / NW]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (a.normalize) __syncthreads();  // z partials and row sums visible
+
+    // ---- normalise and store this wave's 32 columns
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = 8 * i + 4 * hh + e;
+        const int64_t tok = c0 + q;
+        float val = O[4 * i + e];
+        if (a.normalize) {
+          float den = a.delta + (CAUSAL ? rsum[q] : 0.f);
+#pragma unroll
+          for (int ww = 0; ww < NW; ++ww) den += part[ww * kC + q];
+          val = val / den;
+        }
+        if (tok < t1) Og[tok * DV + w * 32 + c32] = val;
+      }
+    if (more) store(smem + ((c + 1) & 1) * BUF, rq, rk, rv);
+    __syncthreads();
+  }
+}
+
+template <int M, int DV>
+hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, float* seg,
+                          hipStream_t st) {
+  using G = Seg32Geom<M, DV>;
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta};
+  const size_t lds = 2ull * (kC * G::MP + kC * G::VP) * sizeof(uint16_t);
+  auto* kern = seg_state32<M, DV>;
+  const hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("seg_state_bf16", st, kern, grid, dim3(G::NT), lds, st, a, k, v, seg);
+  return hipGetLastError();
+}
+
+template <int M, int DV, bool CAUSAL>
+hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const float* state, int64_t ss, int64_t sb, float* out,
+                        hipStream_t st) {
+  using G = Seg32Geom<M, DV>;
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta};
+  const size_t lds = 2ull * G::BUF * sizeof(uint16_t) + (G::NW + 1) * kC * sizeof(float);
+  auto* kern = attn_out32<M, DV, CAUSAL>;
+  const hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st, a, q, k, v, state, ss, sb, out);
+  return hipGetLastError();
+}
+
+int key32(const AttnShape& s) {
+  if (s.seg_len % kC != 0) return 0;
+  return s.m * 1000 + s.dv;
+}
+
+}  // namespace
+
+bool attn32_supported(const AttnShape& s) {
+  switch (key32(s)) {
+    case 256128:
+    case 128064:
+    case 64064: return true;
+    default: return false;
+  }
+}
+
+hipError_t launch_seg_state32(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
+                              float* seg, hipStream_t st) {
+  switch (key32(s)) {
+    case 256128: return launch_state_t<256, 128>(s, phik, v, seg, st);
+    case 128064: return launch_state_t<128, 64>(s, phik, v, seg, st);
+    case 64064: return launch_state_t<64, 64>(s, phik, v, seg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_out32(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
+                             const uint16_t* v, const float* state, int64_t st_seg,
+                             int64_t st_bh, float* out, hipStream_t st) {
+  switch (key32(s) * 2 + (s.causal ? 1 : 0)) {
+    case 256128 * 2 + 1: return launch_out_t<256, 128, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 256128 * 2: return launch_out_t<256, 128, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 128064 * 2 + 1: return launch_out_t<128, 64, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 128064 * 2: return launch_out_t<128, 64, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 64064 * 2 + 1: return launch_out_t<64, 64, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 64064 * 2: return launch_out_t<64, 64, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace llops

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(NW * 64) void featmap_mfma(FeatArgs a) {
 
   const FeatJob job = a.job[blockIdx.z];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
   const int tile = blockIdx.x / a.fsplit;
   const int fs = blockIdx.x - tile * a.fsplit;
@@ -322,7 +323,8 @@ void featmap_fast(FastArgs a) {
 
   const FeatJob job = a.job[blockIdx.z];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
   const int64_t h = blockIdx.y;
   const int64_t R = a.B * a.n;
@@ -355,9 +357,12 @@ void featmap_fast(FastArgs a) {
     for (int i = 0; i < LPT; ++i) st16(buf + (i * kFastNW * 64 + tid) * 8, v[i]);
   };
 
-  u32x4 nxt[LPT], nxt2[LPT];
-  load_stage(0, nxt);
-  if (nstages > 1) load_stage(1, nxt2);
+  // two register sets for the prefetched stages: stage k lands in set k & 1
+  u32x4 regA[LPT], regB[LPT];
+  // prefetches are unconditional (clamped to the last stage) so the number of
+  // loads in flight is static and waits for one set never drain the other
+  load_stage(0, regA);
+  load_stage(nstages > 1 ? 1 : 0, regB);
 
   // ---- X fragments: lane holds row rt*32 + c32, k = ks*16 + 8*hh .. +7
   const uint16_t* X = static_cast<const uint16_t*>(job.X);
@@ -376,9 +381,7 @@ void featmap_fast(FastArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       xf[rt][ks] = as_bf16x8(ok ? ld16(src + ks * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u});
   }
-  write_stage(smem, nxt);
-#pragma unroll
-  for (int i = 0; i < LPT; ++i) nxt[i] = nxt2[i];
+  write_stage(smem, regA);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -425,13 +428,20 @@ void featmap_fast(FastArgs a) {
   };
 
   const uint16_t* fbase = smem + lane * 8;
-  for (int s = 0; s < nstages; ++s) {
+  // One stage: prefetch stage s+2 into `ld` (the set stage s occupied), run
+  // the MFMAs of stage s from LDS slot s & 1, then move stage s+1 (already in
+  // `wr`) into the other slot. The caller alternates the two sets, so no
+  // register copy waits on loads that are still in flight.
+  auto step = [&](int s, u32x4 (&ld)[LPT], const u32x4 (&wr)[LPT]) {
     const int fb = s / T, r = s - (s / T) * T;
-    if (s + 2 < nstages) load_stage(s + 2, nxt2);
+    load_stage(s + 2 < nstages ? s + 2 : nstages - 1, ld);
     // fragment (j, ks) of this stage sits at buf + (j*KS + ks)*512 + lane*8;
-    // the stream below always holds the next fragment in flight
+    // reads run two fragments ahead of the MFMAs that use them
     const uint16_t* buf = fbase + (s & 1) * G::STAGE;
-    bf16x8 fcur = as_bf16x8(ld16(buf));
+    constexpr int NF = P * KS;
+    bf16x8 fr[NF];
+    fr[0] = as_bf16x8(ld16(buf));
+    if (NF > 1) fr[1] = as_bf16x8(ld16(buf + 512));
     f32x16 prod[RT];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
@@ -440,18 +450,28 @@ void featmap_fast(FastArgs a) {
       for (int rt = 0; rt < RT; ++rt) acc[rt] = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int nf = j * KS + ks + 1;
-        bf16x8 fnext = fcur;
-        if (nf < P * KS) fnext = as_bf16x8(ld16(buf + nf * 512));
+        const int fi = j * KS + ks;
+        if (fi + 2 < NF) fr[fi + 2] = as_bf16x8(ld16(buf + (fi + 2) * 512));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32x32x16(xf[rt][ks], fcur, acc[rt]);
-        fcur = fnext;
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32x32x16(xf[rt][ks], fr[fi], acc[rt]);
       }
+      if (j == 0) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) prod[rt] = (j == 0) ? acc[rt] : prod[rt] * acc[rt];
+        for (int rt = 0; rt < RT; ++rt) prod[rt] = acc[rt];
+      } else if (j + 1 < P) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) prod[rt] *= acc[rt];
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sum[rt][e] = fmaf(prod[rt][e], acc[rt][e], sum[rt][e]);
+      }
     }
+    if (P == 1) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sum[rt] += prod[rt];
+      for (int rt = 0; rt < RT; ++rt) sum[rt] += prod[rt];
+    }
     if (r == T - 1) {  // feature block complete: square and park it
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -474,13 +494,16 @@ void featmap_fast(FastArgs a) {
       ++parked;
       ready = parked == a.fg || fb + 1 == FB;
     }
-    if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, nxt);
+    if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, wr);
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) nxt[i] = nxt2[i];
     // the staging area is private to this wave and LDS accesses of one wave
     // complete in order, so the parked rows can be read back right away
     if (ready) flush();
+  };
+
+  for (int s = 0; s < nstages; s += 2) {
+    step(s, regA, regB);
+    if (s + 1 < nstages) step(s + 1, regB, regA);
   }
 }
 

@@ -88,6 +88,15 @@ hipError_t launch_attn_out_f32(const AttnShape& a, const float* phiq, const floa
                                const float* v, float* state, int64_t state_seg_stride,
                                int64_t state_bh_stride, float* out, hipStream_t st);
 
+// 32x32x16-MFMA segment passes for (m, dv) in {(256, 128), (128, 64), (64, 64)}
+// (same seg / state layouts as the kernels above).
+bool attn32_supported(const AttnShape& a);
+hipError_t launch_seg_state32(const AttnShape& a, const uint16_t* phik, const uint16_t* v,
+                              float* seg, hipStream_t st);
+hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
+                             const uint16_t* v, const float* state, int64_t state_seg_stride,
+                             int64_t state_bh_stride, float* out, hipStream_t st);
+
 // Decode: per (b, h): S += phik v^T; z += phik; out = phiq^T S [/(phiq^T z + delta)].
 hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq,
                                const float* phik, const void* v, int v_bf16, float* S,

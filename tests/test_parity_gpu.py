@@ -192,6 +192,23 @@ def test_noncausal(lib, dtype, normalize):
     assert rel_fro(host(out), want) <= tol
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 333, 64, 64, 128, 3, 2), (1, 3, 200, 64, 64, 64, 2, 2),
+                                   (1, 2, 150, 128, 48, 96, 2, 2)])
+def test_noncausal_bf16_normalised_shapes(lib, shape):
+    """Every (m, dv) kernel variant, including the split of the normaliser
+    state over waves, against the plain non-causal definition."""
+    B, H, n, d, dv, m, p, t = shape
+    w = _w(B, H, n, d, dv, m, p, t, square=True, normalize=True)
+    x, g = _inputs(w)
+    announce(f"noncausal bf16 normalised {shape}")
+    out = lib.llops_linattn_fwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], square=True,
+                                normalize=True, delta=1e-6)
+    torch.cuda.synchronize()
+    want = O.linattn_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], square=True,
+                        normalize=True, delta=1e-6)
+    assert rel_fro(host(out), want) <= TOL_BF16
+
+
 def test_noncausal_bf16_large_head(lib):
     w = _w(1, 2, 700, 128, 128, 256, 2, 4, square=True, normalize=True)
     x, g = _inputs(w)
