@@ -206,24 +206,50 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
 // ============================================================================
 // Pass 2: outputs of one segment, starting from its prefix state
 // ============================================================================
+// 2 * dv/32 waves: wave w owns value-column tile w % (dv/32) and feature half
+// w / (dv/32) of the state (m/64 tiles of 32 features), so every wave keeps
+// m/64 fp32 accumulator tiles of S. The two halves of a column tile each
+// hold a partial phi_Q S; they swap the partial rows the other one finishes
+// through LDS, and each wave normalises and stores 16 of the chunk's 32 rows.
+// Wave dvt < m/64 of each half also keeps one z tile (z against all-ones
+// values, inside its feature half). Chunks are prefetched two ahead into two
+// alternating register sets; the exchange areas alternate by chunk parity, so
+// one barrier per chunk orders everything.
+template <int M, int DV>
+struct Out32Geom {
+  static constexpr int NWD = DV / 32;     // value-column tiles
+  static constexpr int NW = 2 * NWD;      // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int FT = M / 32;
+  static constexpr int FH = FT / 2;       // feature tiles per half
+  static constexpr int MP = M + 16, VP = DV + 16;
+  static constexpr int BUF = kC * MP * 2 + kC * VP;
+  static constexpr int QP = kC * M / 8;   // 16-byte pieces of one phi chunk
+  static constexpr int VPc = kC * DV / 8;
+  // LDS after the two chunk buffers, per parity: xo [NW][8][64] fp32,
+  // part [NW][kC] fp32, rsum [kC] fp32
+  static constexpr int XO = NW * 8 * 64, PART = NW * kC, EXW = XO + PART + kC;
+  static constexpr size_t lds_bytes() { return 2ull * BUF * 2 + 2ull * EXW * 4; }
+  static_assert(FT % 2 == 0, "feature tiles split in two halves");
+  static_assert(QP % NT == 0 && VPc % NT == 0, "chunk pieces split evenly over the threads");
+};
+
 template <int M, int DV, bool CAUSAL>
-__global__ __launch_bounds__(DV * 2) void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq,
-                                                    const uint16_t* __restrict__ phik,
-                                                    const uint16_t* __restrict__ v,
-                                                    const float* __restrict__ state,
-                                                    int64_t st_seg, int64_t st_bh,
-                                                    float* __restrict__ out) {
-  using G = Seg32Geom<M, DV>;
-  constexpr int FT = G::FT, MP = G::MP, VP = G::VP, NT = G::NT, NW = G::NW, ZT = G::ZT;
-  constexpr int BUF = G::BUF;
-  constexpr int LQ = G::LPT_Q, LV = G::LPT_V;
+__global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
+                const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
+                int64_t st_bh, float* __restrict__ out) {
+  using G = Out32Geom<M, DV>;
+  constexpr int FH = G::FH, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD, QP = G::QP;
+  constexpr int NP = CAUSAL ? 2 * QP + G::VPc : QP;  // pieces staged per chunk
+  constexpr int LPT = NP / NT;
   extern __shared__ __align__(16) uint16_t smem[];
-  float* part = reinterpret_cast<float*>(smem + 2 * BUF);  // [NW][kC] z partials
-  float* rsum = part + NW * kC;                            // [kC] masked row sums
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave index as a scalar: MFMAs under a condition on it must branch, not
-  // be masked through EXEC (an MFMA runs for the whole wave regardless)
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: see attn pass 1
+  const int dvt = w % NWD, half = w / NWD;
+  const int f0 = half * FH;                    // first feature tile of this wave
+  const bool has_z = dvt < FH;
+  const int zj = dvt;                          // z tile = feature tile f0 + zj
   const int c32 = lane & 31, hh = lane >> 5;
   const int64_t bh = blockIdx.y;
   const int gseg = blockIdx.x;
@@ -235,91 +261,108 @@ __global__ __launch_bounds__(DV * 2) void attn_out32(Seg32Args a, const uint16_t
   float* Og = out + bh * a.n * DV;
   const float* Sin = state + bh * st_bh + gseg * st_seg;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
+  float* exbase = reinterpret_cast<float*>(smem + 2 * G::BUF);
 
-  // state: S[f] = rows 32f.. of this wave's 32 columns; Z[z] = z over the
-  // feature tile z*NW + w (all 32 columns hold the same values)
-  f32x16 S[FT], Z[ZT];
+  f32x16 S[FH], Z;
 #pragma unroll
-  for (int f = 0; f < FT; ++f)
+  for (int j = 0; j < FH; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S[f][4 * i + e] = Sin[(f * 32 + 8 * i + 4 * hh + e) * DV + w * 32 + c32];
+        S[j][4 * i + e] = Sin[((f0 + j) * 32 + 8 * i + 4 * hh + e) * DV + dvt * 32 + c32];
 #pragma unroll
-  for (int z = 0; z < ZT; ++z) {
-    const int f = z * NW + w;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Z[z][4 * i + e] = (f < FT) ? Sin[static_cast<int64_t>(M) * DV + f * 32 + 8 * i + 4 * hh + e] : 0.f;
-  }
+    for (int e = 0; e < 4; ++e)
+      Z[4 * i + e] = has_z ? Sin[static_cast<int64_t>(M) * DV + (f0 + zj) * 32 + 8 * i + 4 * hh + e] : 0.f;
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  auto load = [&](int c, u32x4 (&rq)[LQ], u32x4 (&rk)[LQ], u32x4 (&rv)[LV]) {
+  // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows; a thread's
+  // pieces t + i*NT never straddle two tensors, so the branch folds away
+  auto load = [&](int c, u32x4 (&r)[LPT]) {
     const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+    int t = tid;  // opaque: per-piece addresses are rebuilt, not kept live
+    asm volatile("" : "+v"(t));
 #pragma unroll
-    for (int i = 0; i < LQ; ++i) {
-      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
-      const bool ok = c0 + row < t1;
-      rq[i] = ok ? ld16(Qg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
-      if (CAUSAL) rk[i] = ok ? ld16(Kg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (CAUSAL) {
-#pragma unroll
-      for (int i = 0; i < LV; ++i) {
-        const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
-        rv[i] = (c0 + row < t1) ? ld16(Vg + (c0 + row) * DV + col * 8) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LPT; ++i) {
+      const int p = t + i * NT;
+      const uint16_t* src;
+      int row;
+      if (i * NT < 2 * QP) {
+        const int pp = (i * NT < QP) ? p : p - QP;
+        row = pp / (M / 8);
+        src = ((i * NT < QP) ? Qg : Kg) + (c0 + row) * M + (pp % (M / 8)) * 8;
+      } else {
+        const int pp = p - 2 * QP;
+        row = pp / (DV / 8);
+        src = Vg + (c0 + row) * DV + (pp % (DV / 8)) * 8;
       }
+      r[i] = (c0 + row < t1) ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store = [&](uint16_t* buf, const u32x4 (&rq)[LQ], const u32x4 (&rk)[LQ],
-                   const u32x4 (&rv)[LV]) {
+  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT]) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
 #pragma unroll
-    for (int i = 0; i < LQ; ++i) {
-      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
-      st16(buf + row * MP + col * 8, rq[i]);
-      if (CAUSAL) st16(buf + kC * MP + row * MP + col * 8, rk[i]);
-    }
-    if (CAUSAL) {
-#pragma unroll
-      for (int i = 0; i < LV; ++i) {
-        const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
-        st16(buf + 2 * kC * MP + row * VP + col * 8, rv[i]);
+    for (int i = 0; i < LPT; ++i) {
+      const int p = t + i * NT;
+      uint16_t* dst;
+      if (i * NT < 2 * QP) {
+        const int pp = (i * NT < QP) ? p : p - QP;
+        dst = buf + ((i * NT < QP) ? 0 : kC * MP) + (pp / (M / 8)) * MP + (pp % (M / 8)) * 8;
+      } else {
+        const int pp = p - 2 * QP;
+        dst = buf + 2 * kC * MP + (pp / (DV / 8)) * VP + (pp % (DV / 8)) * 8;
       }
+      st16(dst, r[i]);
     }
   };
 
-  u32x4 rq[LQ], rk[LQ], rv[LV];
-  load(0, rq, rk, rv);
-  store(smem, rq, rk, rv);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) load(c + 1, rq, rk, rv);
-    const uint16_t* Qs = smem + (c & 1) * BUF;
+  // one chunk: prefetch chunk c+2 into `ld` (whose chunk c is already in
+  // LDS; unconditional, clamped, so wait counts stay static), compute chunk
+  // c, move chunk c+1 from `wr` into the other LDS slot, publish partials,
+  // barrier, finish this wave's rows
+  auto step = [&](int c, u32x4 (&ld)[LPT], const u32x4 (&wr)[LPT]) {
+    load(c + 2 < nch ? c + 2 : nch - 1, ld);
+    // Lane-dependent bases pass through an empty asm so the compiler cannot
+    // hoist every derived LDS address and mask compare out of the chunk loop
+    // (kept live across iterations they exhaust the 256-register budget).
+    int lbase = (c & 1) * G::BUF;
+    asm volatile("" : "+v"(lbase));
+    int lim = c32 - 4 * hh;  // key 8i+4hh+e reaches query c32 iff 8i+e <= lim
+    asm volatile("" : "+v"(lim));
+    const uint16_t* Qs = smem + lbase;
     const uint16_t* Ks = Qs + kC * MP;
     const uint16_t* Vs = Qs + 2 * kC * MP;
+    int exoff = (c & 1) * G::EXW;
+    asm volatile("" : "+v"(exoff));
+    float* ex = exbase + exoff;
+    float* xo = ex;
+    float* part = ex + G::XO;
+    float* rsum = part + G::PART;
     const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
 
-    // ---- masked A^T = phi_K phi_Q^T (keys x queries), every wave
-    f32x16 At = zero16();
-    float rs = 0.f;
+    f32x16 O = zero16(), D = zero16();
     bf16x8 afr[2];
-    if (CAUSAL) {
+    if (CAUSAL && half == 0) {
+      // masked A^T = phi_K phi_Q^T (keys x queries)
+      f32x16 At = zero16();
 #pragma unroll
-      for (int ks = 0; ks < M / 16; ++ks)
+      for (int ks = 0; ks < M / 16; ++ks) {
         At = mfma32x32x16(frag_nat(Ks, MP, 0, ks * 16, lane), frag_nat(Qs, MP, 0, ks * 16, lane), At);
-      // key 8i + 4hh + e reaches query c32 iff it is not later
+        // bound the fragment reads the scheduler may hoist ahead (registers)
+        if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (8 * i + 4 * hh + e > c32) At[4 * i + e] = 0.f;
+          if (8 * i + e > lim) At[4 * i + e] = 0.f;  // key after query
       afr[0] = acc_frag(At, 0);
       afr[1] = acc_frag(At, 1);
-      if (a.normalize) {  // row sums of the bf16-rounded weights the A V product uses
+      if (a.normalize && dvt == 0) {  // row sums of the rounded weights A V uses
+        float rs = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4 u = __builtin_bit_cast(u32x4, afr[h]);
@@ -328,74 +371,84 @@ __global__ __launch_bounds__(DV * 2) void attn_out32(Seg32Args a, const uint16_t
             rs += __uint_as_float(u[q] << 16) + __uint_as_float(u[q] & 0xFFFF0000u);
         }
         rs += __shfl_xor(rs, 32);
+        if (hh == 0) rsum[c32] = rs;
       }
-    }
-
-    // phases are fenced so that fragment reads are not hoisted across them
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- out = phi_Q S (+ A V); den partial = phi_Q z over this wave's z tiles
-    f32x16 O = zero16(), D = zero16();
-#pragma unroll
-    for (int f = 0; f < FT; ++f) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 qa = frag_p16(Qs, MP, 0, f * 32 + h * 16, lane);
-        O = mfma32x32x16(qa, acc_frag(S[f], h), O);
-        if (a.normalize && (f % NW) == (w % NW) && f / NW < ZT)
-          D = mfma32x32x16(qa, acc_frag(Z[f / NW], h), D);
-      }
-    }
-    if (CAUSAL) {
 #pragma unroll
       for (int ks = 0; ks < kC / 16; ++ks)
-        O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, w * 32, lane), O);
+        O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
     }
-    if (a.normalize) {
-      // column 0 of D holds this wave's part of phi_Q . z for queries 8i+4hh+e
-      if (c32 == 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    // partial phi_Q S over this wave's feature half; phi_Q . z over its z tile
+#pragma unroll
+    for (int j = 0; j < FH; ++j) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 qa = frag_p16(Qs, MP, 0, (f0 + j) * 32 + h * 16, lane);
+        O = mfma32x32x16(qa, acc_frag(S[j], h), O);
+        if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // publish: the 16 rows the partner wave finishes, and the z partial
+    {
+      // elements 8..15 are rows 16..31 (a select between constant indices:
+      // a runtime index into the tile would force it through scratch)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xo[(w * 8 + e) * 64 + lane] = half == 0 ? O[8 + e] : O[e];
+      if (a.normalize && has_z && c32 == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) part[w * kC + 8 * i + 4 * hh + e] = D[4 * i + e];
       }
-      if (w == 0 && hh == 0) rsum[c32] = rs;
     }
-
     __builtin_amdgcn_sched_barrier(0);
-    // ---- S += phi_K^T V; z += phi_K^T 1
-    if (CAUSAL) {
+    if (CAUSAL) {  // S += phi_K^T V, z += phi_K^T 1
 #pragma unroll
       for (int ks = 0; ks < kC / 16; ++ks) {
-        const bf16x8 vb = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+        const bf16x8 vb = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
 #pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          const bf16x8 ka = frag_tr(Ks, MP, ks * 16, f * 32, lane);
-          S[f] = mfma32x32x16(ka, vb, S[f]);
-          if ((f % NW) == (w % NW) && f / NW < ZT) Z[f / NW] = mfma32x32x16(ka, ones, Z[f / NW]);
+        for (int j = 0; j < FH; ++j) {
+          const bf16x8 ka = frag_tr(Ks, MP, ks * 16, (f0 + j) * 32, lane);
+          S[j] = mfma32x32x16(ka, vb, S[j]);
+          if (has_z && j == zj) Z = mfma32x32x16(ka, ones, Z);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (a.normalize) __syncthreads();  // z partials and row sums visible
-
-    // ---- normalise and store this wave's 32 columns
+    if (c + 1 < nch) store(smem + ((c + 1) & 1) * G::BUF, wr);
+    __syncthreads();
+    // finish rows 16*half .. +15: own part + partner's part, normalise, store
+    {
+      const int kept = half == 0 ? 0 : 8;
+      const int partner = (1 - half) * NWD + dvt;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int q = 8 * i + 4 * hh + e;
-        const int64_t tok = c0 + q;
-        float val = O[4 * i + e];
+      for (int e = 0; e < 8; ++e) {
+        const int i = (kept + e) >> 2, ee = e & 3;
+        const int q = 8 * i + 4 * hh + ee;
+        float val = (half == 0 ? O[e] : O[8 + e]) + xo[(partner * 8 + e) * 64 + lane];
         if (a.normalize) {
           float den = a.delta + (CAUSAL ? rsum[q] : 0.f);
 #pragma unroll
-          for (int ww = 0; ww < NW; ++ww) den += part[ww * kC + q];
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int d = 0; d < FH && d < NWD; ++d) den += part[(hf * NWD + d) * kC + q];
           val = val / den;
         }
-        if (tok < t1) Og[tok * DV + w * 32 + c32] = val;
+        const int64_t tok = c0 + q;
+        if (tok < t1) Og[tok * DV + dvt * 32 + c32] = val;
       }
-    if (more) store(smem + ((c + 1) & 1) * BUF, rq, rk, rv);
-    __syncthreads();
+    }
+  };
+
+  u32x4 rA[LPT], rB[LPT];
+  load(0, rA);
+  load(nch > 1 ? 1 : 0, rB);
+  store(smem, rA);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    step(c, rA, rB);
+    if (c + 1 < nch) step(c + 1, rB, rA);
   }
 }
 
@@ -417,9 +470,9 @@ template <int M, int DV, bool CAUSAL>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* state, int64_t ss, int64_t sb, float* out,
                         hipStream_t st) {
-  using G = Seg32Geom<M, DV>;
+  using G = Out32Geom<M, DV>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta};
-  const size_t lds = 2ull * G::BUF * sizeof(uint16_t) + (G::NW + 1) * kC * sizeof(float);
+  const size_t lds = G::lds_bytes();
   auto* kern = attn_out32<M, DV, CAUSAL>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
