@@ -222,13 +222,17 @@ struct Out32Geom {
   static constexpr int NT = NW * 64;
   static constexpr int FT = M / 32;
   static constexpr int FH = FT / 2;       // feature tiles per half
-  static constexpr int MP = M + 16, VP = DV + 16;
-  static constexpr int BUF = kC * MP * 2 + kC * VP;
+  // row strides (elements): phi_K and V are read transposed (4 rows x 32 B
+  // per 16 lanes, conflict-free when rows shift by 8 banks); phi_Q only in
+  // row order (b64/b128 over 16 rows, conflict-free when rows shift by 4)
+  static constexpr int QPAD = M + 8, MP = M + 16, VP = DV + 16;
+  static constexpr int BUF = kC * QPAD + kC * MP + kC * VP;
   static constexpr int QP = kC * M / 8;   // 16-byte pieces of one phi chunk
   static constexpr int VPc = kC * DV / 8;
   // LDS after the two chunk buffers, per parity: xo [NW][8][64] fp32,
-  // part [NW][kC] fp32, rsum [kC] fp32
-  static constexpr int XO = NW * 8 * 64, PART = NW * kC, EXW = XO + PART + kC;
+  // part [kC][8] fp32 (z partial of wave w at [q][w]), rsum [kC] fp32
+  static constexpr int XO = NW * 8 * 64, PART = kC * 8, EXW = XO + PART + kC;
+  static_assert(NW <= 8, "z partial slots");
   static constexpr size_t lds_bytes() { return 2ull * BUF * 2 + 2ull * EXW * 4; }
   static_assert(FT % 2 == 0, "feature tiles split in two halves");
   static_assert(QP % NT == 0 && VPc % NT == 0, "chunk pieces split evenly over the threads");
@@ -240,7 +244,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
                 int64_t st_bh, float* __restrict__ out) {
   using G = Out32Geom<M, DV>;
-  constexpr int FH = G::FH, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD, QP = G::QP;
+  constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
+  constexpr int QP = G::QP;
   constexpr int NP = CAUSAL ? 2 * QP + G::VPc : QP;  // pieces staged per chunk
   constexpr int LPT = NP / NT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -308,12 +313,14 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     for (int i = 0; i < LPT; ++i) {
       const int p = t + i * NT;
       uint16_t* dst;
-      if (i * NT < 2 * QP) {
-        const int pp = (i * NT < QP) ? p : p - QP;
-        dst = buf + ((i * NT < QP) ? 0 : kC * MP) + (pp / (M / 8)) * MP + (pp % (M / 8)) * 8;
+      if (i * NT < QP) {
+        dst = buf + (p / (M / 8)) * QPAD + (p % (M / 8)) * 8;
+      } else if (i * NT < 2 * QP) {
+        const int pp = p - QP;
+        dst = buf + kC * QPAD + (pp / (M / 8)) * MP + (pp % (M / 8)) * 8;
       } else {
         const int pp = p - 2 * QP;
-        dst = buf + 2 * kC * MP + (pp / (DV / 8)) * VP + (pp % (DV / 8)) * 8;
+        dst = buf + kC * QPAD + kC * MP + (pp / (DV / 8)) * VP + (pp % (DV / 8)) * 8;
       }
       st16(dst, r[i]);
     }
@@ -333,8 +340,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     int lim = c32 - 4 * hh;  // key 8i+4hh+e reaches query c32 iff 8i+e <= lim
     asm volatile("" : "+v"(lim));
     const uint16_t* Qs = smem + lbase;
-    const uint16_t* Ks = Qs + kC * MP;
-    const uint16_t* Vs = Qs + 2 * kC * MP;
+    const uint16_t* Ks = Qs + kC * QPAD;
+    const uint16_t* Vs = Ks + kC * MP;
     int exoff = (c & 1) * G::EXW;
     asm volatile("" : "+v"(exoff));
     float* ex = exbase + exoff;
@@ -350,7 +357,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       f32x16 At = zero16();
 #pragma unroll
       for (int ks = 0; ks < M / 16; ++ks) {
-        At = mfma32x32x16(frag_nat(Ks, MP, 0, ks * 16, lane), frag_nat(Qs, MP, 0, ks * 16, lane), At);
+        At = mfma32x32x16(frag_nat(Ks, MP, 0, ks * 16, lane), frag_nat(Qs, QPAD, 0, ks * 16, lane), At);
         // bound the fragment reads the scheduler may hoist ahead (registers)
         if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
@@ -383,7 +390,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     for (int j = 0; j < FH; ++j) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 qa = frag_p16(Qs, MP, 0, (f0 + j) * 32 + h * 16, lane);
+        const bf16x8 qa = frag_p16(Qs, QPAD, 0, (f0 + j) * 32 + h * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], h), O);
         if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
       }
@@ -399,7 +406,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part[w * kC + 8 * i + 4 * hh + e] = D[4 * i + e];
+          for (int e = 0; e < 4; ++e) part[(8 * i + 4 * hh + e) * 8 + w] = D[4 * i + e];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -428,11 +435,16 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         const int q = 8 * i + 4 * hh + ee;
         float val = (half == 0 ? O[e] : O[8 + e]) + xo[(partner * 8 + e) * 64 + lane];
         if (a.normalize) {
+          // partials of the z-tile owners (d < m/64 in each half), fixed order
+          const u32x4 lo = ld16(part + q * 8), hi = ld16(part + q * 8 + 4);
+          const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
+                               __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                               __uint_as_float(hi[2]), __uint_as_float(hi[3])};
           float den = a.delta + (CAUSAL ? rsum[q] : 0.f);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int d = 0; d < FH && d < NWD; ++d) den += part[(hf * NWD + d) * kC + q];
+            for (int d = 0; d < FH && d < NWD; ++d) den += pv[hf * NWD + d];
           val = val / den;
         }
         const int64_t tok = c0 + q;
