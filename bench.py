@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 
 
 def parse():
@@ -37,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="causal_long_n65536")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' per-config lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
@@ -123,6 +126,80 @@ def bench_causal(w, steps, warmup, torch, lib):
     ms = t0.elapsed_time(t1) / steps
     kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
     return ms, kern
+
+
+def attention_flops(w):
+    """Algorithmic flops of one call: causal_flops for causal workloads; for
+    the non-causal form the feature maps plus phi_K^T V and phi_Q S."""
+    if w.causal:
+        return causal_flops(w)
+    bh = w.batch * w.heads
+    return bh * (4.0 * w.n * w.d * w.p * w.t * w.m + 4.0 * w.n * w.m * w.dv)
+
+
+def bench_config(w, steps, warmup, torch, lib):
+    """One full-batch call of the workload's entry point, inputs resident in
+    HBM: (ms per call, kernel ms)."""
+    from learnable_polynomial_feature_amd.workloads import generate
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    x = generate(w)
+    g = {k: to_dev(v, torch, dt) for k, v in x.items()}
+    del x
+    args = (g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"])
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
+    out = torch.empty((w.batch, w.heads, w.n, w.dv), dtype=torch.float32, device="cuda")
+    if w.causal:
+        shape = lib.make_shape(batch=w.batch, heads=w.heads, n=w.n, d=w.d, dv=w.dv, m=w.m,
+                               p=w.p, t=w.t, square=w.square, normalize=w.normalize,
+                               delta=w.delta, chunk=w.chunk,
+                               in_dtype=lib.BF16 if w.dtype == "bf16" else lib.F32)
+        ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_CAUSAL), dtype=torch.uint8,
+                         device="cuda")
+
+        def call():
+            lib.llops_linattn_causal_fwd(*args, chunk=w.chunk, out=out, workspace=ws, **kw)
+    else:
+        shape = lib.make_shape(batch=w.batch, heads=w.heads, n=w.n, d=w.d, dv=w.dv, m=w.m,
+                               p=w.p, t=w.t, square=w.square, normalize=w.normalize,
+                               delta=w.delta, in_dtype=lib.BF16 if w.dtype == "bf16" else lib.F32)
+        ws = torch.empty(max(1, lib.llops_workspace_bytes(shape, lib.ENTRY_LINATTN)),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            lib.llops_linattn_fwd(*args, out=out, workspace=ws, **kw)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    timer = lib.KernelTimer(capacity=8 * steps)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    with timer:
+        t0.record()
+        for _ in range(steps):
+            call()
+        t1.record()
+    torch.cuda.synchronize()
+    kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    return t0.elapsed_time(t1) / steps, kern
+
+
+def config_lines(steps, torch, lib):
+    """Per-workload throughput next to the bf16 MFMA (or fp32) peak."""
+    from learnable_polynomial_feature_amd.workloads import WORKLOADS
+    res = {}
+    for name in ("tiny_noncausal_f32", "causal_p2_m64", "causal_p3_m128"):
+        w = WORKLOADS[name]
+        log(f"config {name}")
+        ms, kern = bench_config(w, steps, 3, torch, lib)
+        fl = attention_flops(w)
+        tf = fl / (ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        res[name] = {"ms_per_call": round(ms, 4), "us_per_call": round(ms * 1e3, 2),
+                     "tokens_per_s": round(w.batch * w.n / (ms * 1e-3), 1),
+                     "algorithmic_tflop": round(fl / 1e12, 5), "achieved_tflops": round(tf, 3),
+                     "peak_tflops": peak, "frac": round(tf / peak, 5),
+                     "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+    return res
 
 
 def bench_decode(w, steps, torch, lib):
@@ -310,6 +387,8 @@ def main():
                 "traffic": load_traffic("decode_state"),
                 "bytes_per_launch": decode_state_bytes(wd)},
         }
+    if not args.no_configs:
+        line["configs"] = config_lines(20, torch, lib)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
