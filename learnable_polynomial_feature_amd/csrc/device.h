@@ -42,6 +42,18 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// ---- buffer loads ----------------------------------------------------------
+// A raw buffer resource over [base, base + bytes): loads address it with a
+// 32-bit lane offset plus a scalar offset (no per-lane 64-bit address math)
+// and read zeros past `bytes` (range-checked by the hardware).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---- MFMA ------------------------------------------------------------------
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
 // Lane l (g = l / 16, c = l % 16): A holds row c, k = 8g..8g+7; B holds

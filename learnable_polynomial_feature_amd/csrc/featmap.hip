@@ -347,10 +347,18 @@ void featmap_fast(FastArgs a) {
   const uint16_t* pk = static_cast<const uint16_t*>(job.theta_pk) + h * a.pk_hstride;
   const int FB = a.m / 32;
   const int nstages = FB * T;  // stage s = (fb, r) = (s / T, s % T)
+  // piece i of stage s: buffer load at a loop-invariant 32-bit lane offset
+  // plus a scalar stage offset, so the loads need no per-stage address
+  // registers (reusing load destinations as 64-bit address temporaries made
+  // the compiler drain every outstanding load at the loop head)
+  const uint32_t lane_off = static_cast<uint32_t>(tid) * 16u;
+  const __amdgpu_buffer_rsrc_t pk_rsrc =
+      make_rsrc(pk, static_cast<uint32_t>(nstages) * G::STAGE * 2u);
   auto load_stage = [&](int s, u32x4 (&v)[LPT]) {
-    const uint16_t* src = pk + static_cast<int64_t>(s) * G::STAGE + tid * 8;
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) v[i] = ld16(src + i * (kFastNW * 64 * 8));
+    for (int i = 0; i < LPT; ++i)
+      v[i] = buf_ld16(pk_rsrc, lane_off,
+                      static_cast<uint32_t>(s) * (G::STAGE * 2u) + i * (kFastNW * 64u * 16u));
   };
   auto write_stage = [&](uint16_t* buf, const u32x4 (&v)[LPT]) {
 #pragma unroll
@@ -435,6 +443,7 @@ void featmap_fast(FastArgs a) {
   auto step = [&](int s, u32x4 (&ld)[LPT], const u32x4 (&wr)[LPT]) {
     const int fb = s / T, r = s - (s / T) * T;
     load_stage(s + 2 < nstages ? s + 2 : nstages - 1, ld);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the stage
     // fragment (j, ks) of this stage sits at buf + (j*KS + ks)*512 + lane*8;
     // reads run two fragments ahead of the MFMAs that use them
     const uint16_t* buf = fbase + (s & 1) * G::STAGE;
