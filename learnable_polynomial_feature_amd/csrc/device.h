@@ -54,6 +54,15 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vof
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// ---- cross-half lane exchange ---------------------------------------------
+// v_permlane32_swap: lanes 32..63 of x trade values with lanes 0..31 of y;
+// lanes 0..31 of x and lanes 32..63 of y keep theirs.
+__device__ __forceinline__ void swap_halves(uint32_t& x, uint32_t& y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  x = r[0];
+  y = r[1];
+}
+
 // ---- MFMA ------------------------------------------------------------------
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
 // Lane l (g = l / 16, c = l % 16): A holds row c, k = 8g..8g+7; B holds

@@ -243,44 +243,46 @@ __global__ __launch_bounds__(256) void featmap_f32_kernel(FeatArgsF a) {
 //
 // Theta is first repacked (pack_theta) into fragment order: for head h,
 // 32-feature block fb, rank r, degree index j and 16-deep k-step ks, the
-// 64 lanes' B fragments of v_mfma_f32_32x32x16_bf16 lie next to each other
-// (lane l: features fb*32 + l%32, k = ks*16 + 8*(l/32) .. +7). One stage
+// 64 lanes' fragments of v_mfma_f32_32x32x16_bf16 lie next to each other
+// (lane l: feature fb*32 + l%32, k = ks*16 + 8*(l/32) .. +7). One stage
 // (fb, r) is then a contiguous P*d*64-byte block that workgroups copy into
 // LDS with plain 16-byte loads, and fragment reads from LDS are lane-linear
 // (bank-conflict free, no padding).
 //
+// The MFMAs compute the transposed tile (features x rows): Theta fragments
+// are the A operand and the wave's register-resident X rows the B operand.
+// A lane then holds one row's features 8i + 4*(l/32) + e (i, e < 4); one
+// v_permlane32_swap per register pair gives every lane 16 contiguous bytes
+// of phi, so the epilogue stores straight to global memory.
+//
 // A workgroup of 4 waves owns 256 rows of one head; each wave keeps 2 row
-// tiles of 32 rows of X as register-resident A fragments. Stages run one
-// rank at a time through a 2-slot LDS ring, with the global loads of stage
-// s+2 in flight while stage s computes. About 72 KiB of LDS and <= 256 VGPRs
-// let two workgroups share a CU, so one workgroup's barrier and VALU
-// epilogue overlap the other's MFMAs. The epilogue parks phi in a
-// wave-private LDS area and writes whole 128-byte row segments.
+// tiles of 32 rows of X in registers. Stages run one rank at a time through
+// a 2-slot LDS ring. In the middle of stage s (after the j = 0 MFMAs) each
+// thread moves its share of stage s+1 from registers into the free slot and
+// issues the loads of stage s+2, so a whole stage covers the load latency
+// and one register set suffices. 32 KiB of LDS (d = 128, p = 2) and <= 256
+// VGPRs let two workgroups share a CU, so one workgroup's barrier and VALU
+// epilogue overlap the other's MFMAs.
 struct FastArgs {
   FeatJob job[2];
   int64_t B, H, n;
   int m;
   int64_t pk_hstride;  // packed elements between heads (0 = shared)
   int square;
-  int fg;              // 32-feature blocks per phi flush (1 or 2)
 };
 
 constexpr int kFastRT = 2;                         // 32-row tiles per wave
 constexpr int kFastNW = 4;                         // waves per workgroup
 constexpr int kFastRows = kFastNW * kFastRT * 32;  // rows per workgroup
 
-template <int D, int P, bool OUT_BF16>
+template <int D, int P>
 struct FastGeom {
   static constexpr int KS = D / 16;
-  static constexpr int STAGE = P * KS * 512;       // bf16 elements per stage (P*KS fragments)
-  static constexpr int LPT = P * KS * 64 / (kFastNW * 64);  // 16-byte loads per thread per stage
-  static constexpr int ESZ = OUT_BF16 ? 2 : 4;
-  static constexpr int FGMAX = OUT_BF16 ? 2 : 1;
-  static constexpr int PROW = FGMAX * 32 * ESZ + 16;  // staging row bytes
-  static constexpr int WROWS = kFastRT * 32;
-  static constexpr size_t lds_bytes() {
-    return 2ull * STAGE * 2 + 1ull * kFastNW * WROWS * PROW + 1ull * kFastNW * WROWS * 8;
-  }
+  static constexpr int NF = P * KS;                // fragments per stage
+  static constexpr int STAGE = NF * 512;           // bf16 elements per stage
+  static constexpr int LPT = NF * 64 / (kFastNW * 64);  // 16-byte loads per thread per stage
+  static constexpr int FD = NF < 6 ? NF : 6;       // fragment reads in flight
+  static constexpr size_t lds_bytes() { return 2ull * STAGE * 2; }
 };
 
 // theta [H'][p][t][d][m] -> packed [H'][m/32][t][p][d/16][64 lanes][8]
@@ -313,12 +315,14 @@ __global__ __launch_bounds__(256) void pack_theta_kernel(const uint16_t* __restr
 template <int D, int P, int T, bool OUT_BF16>
 __global__ __launch_bounds__(kFastNW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_fast(FastArgs a) {
-  using G = FastGeom<D, P, OUT_BF16>;
+  using G = FastGeom<D, P>;
   constexpr int RT = kFastRT;
   constexpr int KS = G::KS;
+  constexpr int NF = G::NF;
+  constexpr int FD = G::FD;
   constexpr int LPT = G::LPT;
   static_assert(D % 32 == 0, "D must be a multiple of 32");
-  static_assert((P * KS * 64) % (kFastNW * 64) == 0, "a stage splits evenly over the threads");
+  static_assert((NF * 64) % (kFastNW * 64) == 0, "a stage splits evenly over the threads");
   extern __shared__ __align__(16) uint16_t smem[];
 
   const FeatJob job = a.job[blockIdx.z];
@@ -328,29 +332,14 @@ void featmap_fast(FastArgs a) {
   const int hh = lane >> 5, c32 = lane & 31;
   const int64_t h = blockIdx.y;
   const int64_t R = a.B * a.n;
-  const int64_t wrow0 = static_cast<int64_t>(blockIdx.x) * kFastRows + wave * G::WROWS;
-
-  uint8_t* pst = reinterpret_cast<uint8_t*>(smem + 2 * G::STAGE) + wave * G::WROWS * G::PROW;
-  int64_t* rowoff = reinterpret_cast<int64_t*>(reinterpret_cast<uint8_t*>(smem + 2 * G::STAGE) +
-                                               kFastNW * G::WROWS * G::PROW) + wave * G::WROWS;
-  // element offset of each of this wave's rows in phi (-1: past the end)
-  for (int i = lane; i < G::WROWS; i += 64) {
-    const int64_t r = wrow0 + i;
-    int64_t off = -1;
-    if (r < R) {
-      const int64_t b = r / a.n;
-      off = ((b * a.H + h) * a.n + (r - b * a.n)) * a.m;
-    }
-    rowoff[i] = off;
-  }
+  const int64_t wrow0 = static_cast<int64_t>(blockIdx.x) * kFastRows + wave * (RT * 32);
 
   const uint16_t* pk = static_cast<const uint16_t*>(job.theta_pk) + h * a.pk_hstride;
   const int FB = a.m / 32;
   const int nstages = FB * T;  // stage s = (fb, r) = (s / T, s % T)
   // piece i of stage s: buffer load at a loop-invariant 32-bit lane offset
-  // plus a scalar stage offset, so the loads need no per-stage address
-  // registers (reusing load destinations as 64-bit address temporaries made
-  // the compiler drain every outstanding load at the loop head)
+  // plus a scalar stage offset (no per-stage address registers, so the
+  // compiler never reuses load destinations as address temporaries)
   const uint32_t lane_off = static_cast<uint32_t>(tid) * 16u;
   const __amdgpu_buffer_rsrc_t pk_rsrc =
       make_rsrc(pk, static_cast<uint32_t>(nstages) * G::STAGE * 2u);
@@ -365,16 +354,16 @@ void featmap_fast(FastArgs a) {
     for (int i = 0; i < LPT; ++i) st16(buf + (i * kFastNW * 64 + tid) * 8, v[i]);
   };
 
-  // two register sets for the prefetched stages: stage k lands in set k & 1
-  u32x4 regA[LPT], regB[LPT];
-  // prefetches are unconditional (clamped to the last stage) so the number of
-  // loads in flight is static and waits for one set never drain the other
-  load_stage(0, regA);
-  load_stage(nstages > 1 ? 1 : 0, regB);
+  // stage 0 goes straight to slot 0; stage 1 waits in registers
+  u32x4 reg[LPT];
+  load_stage(0, reg);
+  write_stage(smem, reg);
+  load_stage(nstages > 1 ? 1 : 0, reg);
 
-  // ---- X fragments: lane holds row rt*32 + c32, k = ks*16 + 8*hh .. +7
+  // ---- X fragments (B operand): lane holds row rt*32 + c32, k = ks*16 + 8*hh .. +7
   const uint16_t* X = static_cast<const uint16_t*>(job.X);
   bf16x8 xf[RT][KS];
+  int64_t rowoff[RT];  // element offset of the lane's phi row, -1 past the end
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t r = wrow0 + rt * 32 + c32;
@@ -384,73 +373,75 @@ void featmap_fast(FastArgs a) {
       const int64_t b = r / a.n;
       rho = (b * a.H + h) * a.n + (r - b * a.n);
     }
+    rowoff[rt] = ok ? rho * a.m : -1;
     const uint16_t* src = X + rho * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       xf[rt][ks] = as_bf16x8(ok ? ld16(src + ks * 16 + hh * 8) : u32x4{0u, 0u, 0u, 0u});
   }
-  write_stage(smem, regA);
+  // drain every load here: a wait for the X fragments left to the compiler
+  // lands inside the stage loop and would drain the Theta prefetch each stage
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  f32x16 sum[RT];
+  const uint16_t* fbase = smem + lane * 8;
+  uint8_t* out = static_cast<uint8_t*>(job.phi);
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  constexpr int NQ = OUT_BF16 ? 2 : 4;  // 16-byte pieces per lane per row tile
+  // phi of the last finished feature block, rounded and regrouped so piece q
+  // of tile rt is 16 contiguous bytes at byte q*32 + 16*hh of the lane's row
+  u32x4 cv[RT][NQ];
+  auto finish = [&](const f32x16 (&sum)[RT]) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
-  // phi of finished feature blocks waits in the staging area until a.fg
-  // blocks (one 128-byte row segment) or the last block are parked
-  int parked = 0, park_fb0 = 0;
-  bool ready = false;
-
-  auto flush = [&]() {
-    uint8_t* out = static_cast<uint8_t*>(job.phi);
-    constexpr int CPR = G::FGMAX * 2 * G::ESZ;  // 16-byte chunks per full row segment
-    if (parked == G::FGMAX) {
-      // whole segments: fixed trip count, so all LDS reads issue before the stores
-      constexpr int ITER = G::WROWS * CPR / 64;
-      u32x4 v[ITER];
-      int64_t off[ITER];
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x16 v = sum[rt];
+      if (a.square) v *= v;
+      if (OUT_BF16) {
+        // lane (hh, c32) holds features 8i + 4hh + e of row c32; after the
+        // swaps hh = 0 lanes own features 0..7 and 16..23, hh = 1 lanes
+        // 8..15 and 24..31 (lanes c32 and c32 + 32 share a row)
+        uint32_t w[4][2];
 #pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int idx = lane + 64 * it;
-        const int row = idx / CPR, ch = idx % CPR;
-        off[it] = rowoff[row];
-        v[it] = ld16(pst + row * G::PROW + ch * 16);
-      }
+        for (int i = 0; i < 4; ++i) {
+          w[i][0] = pack_bf16x2(v[4 * i], v[4 * i + 1]);
+          w[i][1] = pack_bf16x2(v[4 * i + 2], v[4 * i + 3]);
+        }
 #pragma unroll
-      for (int it = 0; it < ITER; ++it) {
-        const int ch = (lane + 64 * it) % CPR;
-        if (off[it] >= 0) st16(out + (off[it] + park_fb0 * 32) * G::ESZ + ch * 16, v[it]);
-      }
-    } else {
-      const int cpr = parked * 2 * G::ESZ;
-      const int total = G::WROWS * cpr;
-      for (int idx = lane; idx < total; idx += 64) {
-        const int row = idx / cpr, ch = idx - (idx / cpr) * cpr;
-        const int64_t o = rowoff[row];
-        if (o >= 0)
-          st16(out + (o + park_fb0 * 32) * G::ESZ + ch * 16, ld16(pst + row * G::PROW + ch * 16));
+        for (int e = 0; e < 2; ++e) {
+          swap_halves(w[0][e], w[1][e]);
+          swap_halves(w[2][e], w[3][e]);
+        }
+        cv[rt][0] = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
+        cv[rt][NQ - 1] = u32x4{w[2][0], w[2][1], w[3][0], w[3][1]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i)
+          cv[rt][i] = u32x4{__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                            __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])};
       }
     }
-    parked = 0;
-    ready = false;
+  };
+  auto emit = [&](int fb) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint8_t* dst = out + (rowoff[rt] + fb * 32) * ESZ + hh * 16;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (rowoff[rt] >= 0) st16(dst + q * 32, cv[rt][q]);
+    }
   };
 
-  const uint16_t* fbase = smem + lane * 8;
-  // One stage: prefetch stage s+2 into `ld` (the set stage s occupied), run
-  // the MFMAs of stage s from LDS slot s & 1, then move stage s+1 (already in
-  // `wr`) into the other slot. The caller alternates the two sets, so no
-  // register copy waits on loads that are still in flight.
-  auto step = [&](int s, u32x4 (&ld)[LPT], const u32x4 (&wr)[LPT]) {
-    const int fb = s / T, r = s - (s / T) * T;
-    load_stage(s + 2 < nstages ? s + 2 : nstages - 1, ld);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the stage
-    // fragment (j, ks) of this stage sits at buf + (j*KS + ks)*512 + lane*8;
-    // reads run two fragments ahead of the MFMAs that use them
+  // One stage: MFMAs of stage s from slot s & 1. After the j = 0 block the
+  // registers holding stage s+1 go to the other slot (free since the last
+  // barrier), the previous feature block's phi is stored if store_fb >= 0,
+  // and stage s+2 is requested. The stores go before the loads: waits for
+  // loads count in issue order, so a store issued after a load would be
+  // waited for together with it half a stage later.
+  auto stage = [&](int s, f32x16 (&sum)[RT], int store_fb) {
     const uint16_t* buf = fbase + (s & 1) * G::STAGE;
-    constexpr int NF = P * KS;
     bf16x8 fr[NF];
-    fr[0] = as_bf16x8(ld16(buf));
-    if (NF > 1) fr[1] = as_bf16x8(ld16(buf + 512));
+#pragma unroll
+    for (int i = 0; i < FD; ++i) fr[i] = as_bf16x8(ld16(buf + i * 512));
     f32x16 prod[RT];
 #pragma unroll
     for (int j = 0; j < P; ++j) {
@@ -460,11 +451,24 @@ void featmap_fast(FastArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int fi = j * KS + ks;
-        if (fi + 2 < NF) fr[fi + 2] = as_bf16x8(ld16(buf + (fi + 2) * 512));
+        if (fi + FD < NF) fr[fi + FD] = as_bf16x8(ld16(buf + (fi + FD) * 512));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32x32x16(xf[rt][ks], fr[fi], acc[rt]);
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32x32x16(fr[fi], xf[rt][ks], acc[rt]);
+        // pin the read FD fragments ahead of its MFMAs (the scheduler would
+        // otherwise sink it next to its use and expose the LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (j == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, reg);
+        if (store_fb >= 0) emit(store_fb);
+        load_stage(s + 2 < nstages ? s + 2 : nstages - 1, reg);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (P == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sum[rt] += acc[rt];
+      } else if (j == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) prod[rt] = acc[rt];
       } else if (j + 1 < P) {
@@ -477,48 +481,25 @@ void featmap_fast(FastArgs a) {
           for (int e = 0; e < 16; ++e) sum[rt][e] = fmaf(prod[rt][e], acc[rt][e], sum[rt][e]);
       }
     }
-    if (P == 1) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) sum[rt] += prod[rt];
-    }
-    if (r == T - 1) {  // feature block complete: square and park it
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        f32x16 v = sum[rt];
-        if (a.square) v *= v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint8_t* dst = pst + (rt * 32 + 8 * i + 4 * hh + e) * G::PROW +
-                           (parked * 32 + c32) * G::ESZ;
-            if (OUT_BF16)
-              *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(v[4 * i + e]);
-            else
-              *reinterpret_cast<float*>(dst) = v[4 * i + e];
-          }
-        sum[rt] = zero16();
-      }
-      if (parked == 0) park_fb0 = fb;
-      ++parked;
-      ready = parked == a.fg || fb + 1 == FB;
-    }
-    if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, wr);
     __syncthreads();
-    // the staging area is private to this wave and LDS accesses of one wave
-    // complete in order, so the parked rows can be read back right away
-    if (ready) flush();
   };
 
-  for (int s = 0; s < nstages; s += 2) {
-    step(s, regA, regB);
-    if (s + 1 < nstages) step(s + 1, regB, regA);
+  for (int fb = 0; fb < FB; ++fb) {
+    f32x16 sum[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
+    // stages stay rolled: unrolling lets the scheduler interleave stages
+    // and exceed the register budget
+#pragma unroll 1
+    for (int r = 0; r < T; ++r) stage(fb * T + r, sum, r == 0 ? fb - 1 : -1);
+    finish(sum);
   }
+  emit(FB - 1);
 }
 
 template <int D, int P, int T, bool OUT_BF16>
 hipError_t launch_fast_t(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
-  using G = FastGeom<D, P, OUT_BF16>;
+  using G = FastGeom<D, P>;
   FastArgs a{};
   a.job[0] = jobs[0];
   a.job[1] = njobs > 1 ? jobs[1] : jobs[0];
@@ -528,8 +509,6 @@ hipError_t launch_fast_t(const FeatShape& s, const FeatJob* jobs, int njobs, hip
   a.m = s.m;
   a.pk_hstride = s.theta_per_head ? static_cast<int64_t>(P) * T * D * s.m : 0;
   a.square = s.square;
-  const int FB = s.m / 32;
-  a.fg = FB < G::FGMAX ? FB : G::FGMAX;
   const int64_t tiles = (s.B * s.n + kFastRows - 1) / kFastRows;
   if (tiles > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
   // repack Theta of every job into its fragment-order buffer
