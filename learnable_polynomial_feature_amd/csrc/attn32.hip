@@ -77,6 +77,15 @@ __device__ __forceinline__ bf16x8 acc_frag(const f32x16& t, int h) {
                          pack_bf16x2(t[8 * h + 6], t[8 * h + 7])});
 }
 
+// a if first else b, for two elements of one accumulator tile and a
+// wave-uniform condition. The values pass through an empty asm first: a plain
+// select between elements of one vector is rewritten into an indexed register
+// read (M0-relative moves or a select chain over the whole tile).
+__device__ __forceinline__ float pick(float a, float b, bool first) {
+  asm volatile("" : "+v"(a), "+v"(b));
+  return first ? a : b;
+}
+
 struct Seg32Args {
   int64_t n;
   int64_t seg_len;   // tokens per segment (multiple of kC)
@@ -398,10 +407,9 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     __builtin_amdgcn_sched_barrier(0);
     // publish: the 16 rows the partner wave finishes, and the z partial
     {
-      // elements 8..15 are rows 16..31 (a select between constant indices:
-      // a runtime index into the tile would force it through scratch)
+      // elements 8..15 are rows 16..31
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xo[(w * 8 + e) * 64 + lane] = half == 0 ? O[8 + e] : O[e];
+      for (int e = 0; e < 8; ++e) xo[(w * 8 + e) * 64 + lane] = pick(O[8 + e], O[e], half == 0);
       if (a.normalize && has_z && c32 == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -425,30 +433,54 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < nch) store(smem + ((c + 1) & 1) * G::BUF, wr);
     __syncthreads();
-    // finish rows 16*half .. +15: own part + partner's part, normalise, store
+    // finish rows 16*half .. +15: own part + partner's part, normalise, store.
+    // All LDS reads are issued before any arithmetic and the normalisation
+    // branch covers the whole block, so the eight rows overlap instead of
+    // running as eight dependent read-add-divide-store chains.
     {
       const int kept = half == 0 ? 0 : 8;
       const int partner = (1 - half) * NWD + dvt;
+      float val[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int i = (kept + e) >> 2, ee = e & 3;
-        const int q = 8 * i + 4 * hh + ee;
-        float val = (half == 0 ? O[e] : O[8 + e]) + xo[(partner * 8 + e) * 64 + lane];
-        if (a.normalize) {
-          // partials of the z-tile owners (d < m/64 in each half), fixed order
-          const u32x4 lo = ld16(part + q * 8), hi = ld16(part + q * 8 + 4);
-          const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
-                               __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
-                               __uint_as_float(hi[2]), __uint_as_float(hi[3])};
-          float den = a.delta + (CAUSAL ? rsum[q] : 0.f);
+      for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
+      if (a.normalize) {
+        // partials of the z-tile owners (d < m/64 in each half), fixed order
+        float den[8];
+        u32x4 lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
+          lo[e] = ld16(part + q * 8);
+          hi[e] = ld16(part + q * 8 + 4);
+          den[e] = a.delta + (CAUSAL ? rsum[q] : 0.f);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv[8] = {__uint_as_float(lo[e][0]), __uint_as_float(lo[e][1]),
+                               __uint_as_float(lo[e][2]), __uint_as_float(lo[e][3]),
+                               __uint_as_float(hi[e][0]), __uint_as_float(hi[e][1]),
+                               __uint_as_float(hi[e][2]), __uint_as_float(hi[e][3])};
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-            for (int d = 0; d < FH && d < NWD; ++d) den += pv[hf * NWD + d];
-          val = val / den;
+            for (int d = 0; d < FH && d < NWD; ++d) den[e] += pv[hf * NWD + d];
+          // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
+          val[e] *= __builtin_amdgcn_rcpf(den[e]);
         }
-        const int64_t tok = c0 + q;
-        if (tok < t1) Og[tok * DV + dvt * 32 + c32] = val;
+      }
+      // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
+      float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
+      if (c0 + kC <= t1) {  // whole chunk in range: no per-row checks
+#pragma unroll
+        for (int e = 0; e < 8; ++e) orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV] = val[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * ((kept + e) >> 2) + (e & 3);
+          if (c0 + r + 4 * hh < t1) orow[r * DV] = val[e];
+        }
       }
     }
   };
