@@ -134,18 +134,20 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   const uint16_t* Vg = v + bh * a.n * DV;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
 
+  // Raw buffer views of this segment's rows: reads past the segment end
+  // return zeros (hardware range check), so every load is unconditional, the
+  // number in flight is static and a wait for one chunk never drains the next.
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
   auto load = [&](int c, u32x4 (&rk)[LK], u32x4 (&rv)[LV]) {
-    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+    // piece idx of a chunk is 16 contiguous bytes at byte 16 * idx
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
-      rk[i] = (c0 + row < t1) ? ld16(Kg + (c0 + row) * M + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < LK; ++i)
+      rk[i] = buf_ld16(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
 #pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int idx = tid + i * NT, row = idx / (DV / 8), col = idx % (DV / 8);
-      rv[i] = (c0 + row < t1) ? ld16(Vg + (c0 + row) * DV + col * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < LV; ++i)
+      rv[i] = buf_ld16(rsv, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
   };
   auto store = [&](uint16_t* buf, const u32x4 (&rk)[LK], const u32x4 (&rv)[LV]) {
 #pragma unroll
@@ -167,13 +169,12 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   for (int z = 0; z < G::ZT; ++z) Z[z] = zero16();
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  u32x4 rk[LK], rv[LV];
-  load(0, rk, rv);
-  store(smem, rk, rv);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    if (more) load(c + 1, rk, rv);
+  // one chunk: request chunk c+2 into (lk, lv) (chunk c, its old contents,
+  // is already in LDS; clamped past the end), run chunk c from LDS, move
+  // chunk c+1 from (wk, wv) into the other slot, barrier
+  auto step = [&](int c, u32x4 (&lk)[LK], u32x4 (&lv)[LV], const u32x4 (&wk)[LK],
+                  const u32x4 (&wv)[LV]) {
+    load(c + 2 < nch ? c + 2 : nch - 1, lk, lv);
     const uint16_t* Ks = smem + (c & 1) * BUF;
     const uint16_t* Vs = Ks + kC * MP;
 #pragma unroll
@@ -187,8 +188,18 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
           Z[f / G::NW] = mfma32x32x16(ka, ones, Z[f / G::NW]);
       }
     }
-    if (more) store(smem + ((c + 1) & 1) * BUF, rk, rv);
+    if (c + 1 < nch) store(smem + ((c + 1) & 1) * BUF, wk, wv);
     __syncthreads();
+  };
+
+  u32x4 ak[LK], av[LV], bk[LK], bv[LV];
+  load(0, ak, av);
+  load(nch > 1 ? 1 : 0, bk, bv);
+  store(smem, ak, av);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    step(c, ak, av, bk, bv);
+    if (c + 1 < nch) step(c + 1, bk, bv, ak, av);
   }
   float* out = seg + (bh * a.nseg + gseg) * (static_cast<int64_t>(M) * DV + M);
   const int c32 = lane & 31, hh = lane >> 5;
@@ -292,27 +303,28 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       Z[4 * i + e] = has_z ? Sin[static_cast<int64_t>(M) * DV + (f0 + zj) * 32 + 8 * i + 4 * hh + e] : 0.f;
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows; a thread's
-  // pieces t + i*NT never straddle two tensors, so the branch folds away
+  // Raw buffer views of this segment's rows: reads past the segment end
+  // return zeros (hardware range check), so every load is unconditional and
+  // the waits for one chunk never drain the loads of the next.
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const __amdgpu_buffer_rsrc_t rsq = make_rsrc(Qg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
+  // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
+  // contiguous bytes each; a thread's pieces t + i*NT never straddle two
+  // tensors, so the selection folds away
   auto load = [&](int c, u32x4 (&r)[LPT]) {
-    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
-    int t = tid;  // opaque: per-piece addresses are rebuilt, not kept live
+    int t = tid;  // opaque: per-piece offsets are rebuilt, not kept live
     asm volatile("" : "+v"(t));
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int p = t + i * NT;
-      const uint16_t* src;
-      int row;
-      if (i * NT < 2 * QP) {
-        const int pp = (i * NT < QP) ? p : p - QP;
-        row = pp / (M / 8);
-        src = ((i * NT < QP) ? Qg : Kg) + (c0 + row) * M + (pp % (M / 8)) * 8;
-      } else {
-        const int pp = p - 2 * QP;
-        row = pp / (DV / 8);
-        src = Vg + (c0 + row) * DV + (pp % (DV / 8)) * 8;
-      }
-      r[i] = (c0 + row < t1) ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
+      if (i * NT < QP)
+        r[i] = buf_ld16(rsq, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+      else if (i * NT < 2 * QP)
+        r[i] = buf_ld16(rsk, (p - QP) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+      else
+        r[i] = buf_ld16(rsv, (p - 2 * QP) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
     }
   };
   auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT]) {
@@ -488,6 +500,14 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   u32x4 rA[LPT], rB[LPT];
   load(0, rA);
   load(nch > 1 ? 1 : 0, rB);
+  // The prefix state must be in registers before the chunk loop: a wait for
+  // it left to the compiler lands inside the loop and drains the chunk
+  // prefetch on every chunk (and the scheduler sinks the state loads below a
+  // plain s_waitcnt). An empty asm reading every state register makes the
+  // wait happen here.
+#pragma unroll
+  for (int j = 0; j < FH; ++j) asm volatile("" : "+v"(S[j]));
+  asm volatile("" : "+v"(Z));
   store(smem, rA);
   __syncthreads();
   for (int c = 0; c < nch; c += 2) {
@@ -527,6 +547,8 @@ hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k
 
 int key32(const AttnShape& s) {
   if (s.seg_len % kC != 0) return 0;
+  // buffer views of one segment's rows need byte offsets below 2^31
+  if (s.seg_len * (s.m > s.dv ? s.m : s.dv) * 2 >= (int64_t{1} << 31)) return 0;
   return s.m * 1000 + s.dv;
 }
 
