@@ -375,12 +375,26 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     bf16x8 afr[2];
     if (CAUSAL && half == 0) {
       // masked A^T = phi_K phi_Q^T (keys x queries)
+      // fragment reads run AD k-steps ahead of the MFMA chain (pinned: the
+      // scheduler would otherwise sink each read next to its MFMA and expose
+      // the LDS latency on every step)
+      constexpr int KS = M / 16, AD = KS < 3 ? KS : 3;
       f32x16 At = zero16();
+      bf16x8 fk[AD], fq[AD];
 #pragma unroll
-      for (int ks = 0; ks < M / 16; ++ks) {
-        At = mfma32x32x16(frag_nat(Ks, MP, 0, ks * 16, lane), frag_nat(Qs, QPAD, 0, ks * 16, lane), At);
-        // bound the fragment reads the scheduler may hoist ahead (registers)
-        if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < AD; ++i) {
+        fk[i] = frag_nat(Ks, MP, 0, i * 16, lane);
+        fq[i] = frag_nat(Qs, QPAD, 0, i * 16, lane);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = fk[ks % AD], qb = fq[ks % AD];
+        if (ks + AD < KS) {
+          fk[ks % AD] = frag_nat(Ks, MP, 0, (ks + AD) * 16, lane);
+          fq[ks % AD] = frag_nat(Qs, QPAD, 0, (ks + AD) * 16, lane);
+        }
+        At = mfma32x32x16(ka, qb, At);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -406,14 +420,21 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // partial phi_Q S over this wave's feature half; phi_Q . z over its z tile
+    // partial phi_Q S over this wave's feature half; phi_Q . z over its z
+    // tile. The phi_Q fragment reads run QD products ahead (pinned).
+    {
+      constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
+      bf16x8 qf[QD];
 #pragma unroll
-    for (int j = 0; j < FH; ++j) {
+      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 qa = frag_p16(Qs, QPAD, 0, (f0 + j) * 32 + h * 16, lane);
+      for (int idx = 0; idx < NQ; ++idx) {
+        const int j = idx >> 1, h = idx & 1;
+        const bf16x8 qa = qf[idx % QD];
+        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], h), O);
         if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -430,16 +451,23 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (CAUSAL) {  // S += phi_K^T V, z += phi_K^T 1
+    if (CAUSAL) {  // S += phi_K^T V, z += phi_K^T 1; phi_K reads run KD ahead
+      constexpr int NK = (kC / 16) * FH, KD = NK < 2 ? NK : 2;
+      bf16x8 kf[KD];
 #pragma unroll
-      for (int ks = 0; ks < kC / 16; ++ks) {
-        const bf16x8 vb = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
+      for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FH) * 16, (f0 + i % FH) * 32, lane);
+      bf16x8 vb[kC / 16];
 #pragma unroll
-        for (int j = 0; j < FH; ++j) {
-          const bf16x8 ka = frag_tr(Ks, MP, ks * 16, (f0 + j) * 32, lane);
-          S[j] = mfma32x32x16(ka, vb, S[j]);
-          if (has_z && j == zj) Z = mfma32x32x16(ka, ones, Z);
-        }
+      for (int ks = 0; ks < kC / 16; ++ks) vb[ks] = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
+#pragma unroll
+      for (int idx = 0; idx < NK; ++idx) {
+        const int ks = idx / FH, j = idx % FH;
+        const bf16x8 ka = kf[idx % KD];
+        if (idx + KD < NK)
+          kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FH) * 16, (f0 + (idx + KD) % FH) * 32, lane);
+        S[j] = mfma32x32x16(ka, vb[ks], S[j]);
+        if (has_z && j == zj) Z = mfma32x32x16(ka, ones, Z);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
