@@ -169,38 +169,39 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   for (int z = 0; z < G::ZT; ++z) Z[z] = zero16();
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  // one chunk: request chunk c+2 into (lk, lv) (chunk c, its old contents,
-  // is already in LDS; clamped past the end), run chunk c from LDS, move
-  // chunk c+1 from (wk, wv) into the other slot, barrier
-  auto step = [&](int c, u32x4 (&lk)[LK], u32x4 (&lv)[LV], const u32x4 (&wk)[LK],
-                  const u32x4 (&wv)[LV]) {
-    load(c + 2 < nch ? c + 2 : nch - 1, lk, lv);
+  // one chunk: request chunk c+1 into the registers (clamped past the
+  // end), run chunk c from LDS, move chunk c+1 into the other slot, barrier
+  u32x4 rk[LK], rv[LV];
+  auto step = [&](int c) {
+    load(c + 1 < nch ? c + 1 : nch - 1, rk, rv);
     const uint16_t* Ks = smem + (c & 1) * BUF;
     const uint16_t* Vs = Ks + kC * MP;
+    // phi_K fragment reads run KD products ahead (pinned: the scheduler
+    // would sink each next to its MFMA and expose the LDS latency)
+    constexpr int NK = (kC / 16) * FT, KD = NK < 2 ? NK : 2;
+    bf16x8 vb[kC / 16], kf[KD];
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ++ks) {
-      const bf16x8 vb = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+    for (int ks = 0; ks < kC / 16; ++ks) vb[ks] = frag_tr(Vs, VP, ks * 16, w * 32, lane);
 #pragma unroll
-      for (int f = 0; f < FT; ++f) {
-        const bf16x8 ka = frag_tr(Ks, MP, ks * 16, f * 32, lane);
-        S[f] = mfma32x32x16(ka, vb, S[f]);
-        if ((f % G::NW) == (w % G::NW) && f / G::NW < G::ZT)
-          Z[f / G::NW] = mfma32x32x16(ka, ones, Z[f / G::NW]);
-      }
+    for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FT) * 16, (i % FT) * 32, lane);
+#pragma unroll
+    for (int idx = 0; idx < NK; ++idx) {
+      const int ks = idx / FT, f = idx % FT;
+      const bf16x8 ka = kf[idx % KD];
+      if (idx + KD < NK) kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FT) * 16, ((idx + KD) % FT) * 32, lane);
+      S[f] = mfma32x32x16(ka, vb[ks], S[f]);
+      if ((f % G::NW) == (w % G::NW) && f / G::NW < G::ZT)
+        Z[f / G::NW] = mfma32x32x16(ka, ones, Z[f / G::NW]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (c + 1 < nch) store(smem + ((c + 1) & 1) * BUF, wk, wv);
+    if (c + 1 < nch) store(smem + ((c + 1) & 1) * BUF, rk, rv);
     __syncthreads();
   };
 
-  u32x4 ak[LK], av[LV], bk[LK], bv[LV];
-  load(0, ak, av);
-  load(nch > 1 ? 1 : 0, bk, bv);
-  store(smem, ak, av);
+  load(0, rk, rv);
+  store(smem, rk, rv);
   __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    step(c, ak, av, bk, bv);
-    if (c + 1 < nch) step(c + 1, bk, bv, ak, av);
-  }
+  for (int c = 0; c < nch; ++c) step(c);
   float* out = seg + (bh * a.nseg + gseg) * (static_cast<int64_t>(M) * DV + M);
   const int c32 = lane & 31, hh = lane >> 5;
 #pragma unroll
