@@ -388,10 +388,15 @@ void featmap_fast(FastArgs a) {
   uint8_t* out = static_cast<uint8_t*>(job.phi);
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
   constexpr int NQ = OUT_BF16 ? 2 : 4;  // 16-byte pieces per lane per row tile
-  // phi of the last finished feature block, rounded and regrouped so piece q
-  // of tile rt is 16 contiguous bytes at byte q*32 + 16*hh of the lane's row
-  u32x4 cv[RT][NQ];
-  auto finish = [&](const f32x16 (&sum)[RT]) {
+  // phi of finished feature blocks, rounded and regrouped so piece q of
+  // tile rt is 16 contiguous bytes at byte q*32 + 16*hh of the lane's row.
+  // bf16 rows hold two 32-feature blocks per 128-byte line: the blocks are
+  // stored in pairs (cv0 = even block, cv1 = odd block) so each line is
+  // written whole while it is in L2; stored one at a time, a line's halves
+  // lie four stages apart and some lines reach HBM twice.
+  constexpr int PAIR = OUT_BF16 ? 2 : 1;
+  u32x4 cv0[RT][NQ], cv1[RT][NQ];
+  auto finish = [&](const f32x16 (&sum)[RT], u32x4 (&cv)[RT][NQ]) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       f32x16 v = sum[rt];
@@ -421,7 +426,7 @@ void featmap_fast(FastArgs a) {
       }
     }
   };
-  auto emit = [&](int fb) {
+  auto emit = [&](int fb, const u32x4 (&cv)[RT][NQ]) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       uint8_t* dst = out + (rowoff[rt] + fb * 32) * ESZ + hh * 16;
@@ -433,10 +438,11 @@ void featmap_fast(FastArgs a) {
 
   // One stage: MFMAs of stage s from slot s & 1. After the j = 0 block the
   // registers holding stage s+1 go to the other slot (free since the last
-  // barrier), the previous feature block's phi is stored if store_fb >= 0,
-  // and stage s+2 is requested. The stores go before the loads: waits for
-  // loads count in issue order, so a store issued after a load would be
-  // waited for together with it half a stage later.
+  // barrier), the previous PAIR feature blocks' phi is stored if
+  // store_fb >= 0 (blocks store_fb ..), and stage s+2 is requested. The
+  // stores go before the loads: waits for loads count in issue order, so a
+  // store issued after a load would be waited for together with it half a
+  // stage later.
   auto stage = [&](int s, f32x16 (&sum)[RT], int store_fb) {
     const uint16_t* buf = fbase + (s & 1) * G::STAGE;
     bf16x8 fr[NF];
@@ -461,7 +467,10 @@ void featmap_fast(FastArgs a) {
       if (j == 0) {
         __builtin_amdgcn_sched_barrier(0);
         if (s + 1 < nstages) write_stage(smem + ((s + 1) & 1) * G::STAGE, reg);
-        if (store_fb >= 0) emit(store_fb);
+        if (store_fb >= 0) {
+          emit(store_fb, cv0);
+          if (PAIR == 2) emit(store_fb + 1, cv1);
+        }
         load_stage(s + 2 < nstages ? s + 2 : nstages - 1, reg);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -484,17 +493,30 @@ void featmap_fast(FastArgs a) {
     __syncthreads();
   };
 
-  for (int fb = 0; fb < FB; ++fb) {
-    f32x16 sum[RT];
+  // stages stay rolled: unrolling lets the scheduler interleave stages and
+  // exceed the register budget
+  for (int fb = 0; fb < FB; fb += PAIR) {
+    {
+      f32x16 sum[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
-    // stages stay rolled: unrolling lets the scheduler interleave stages
-    // and exceed the register budget
+      for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
 #pragma unroll 1
-    for (int r = 0; r < T; ++r) stage(fb * T + r, sum, r == 0 ? fb - 1 : -1);
-    finish(sum);
+      for (int r = 0; r < T; ++r) stage(fb * T + r, sum, r == 0 && fb >= PAIR ? fb - PAIR : -1);
+      finish(sum, cv0);
+    }
+    if (PAIR == 2 && fb + 1 < FB) {
+      f32x16 sum[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) sum[rt] = zero16();
+#pragma unroll 1
+      for (int r = 0; r < T; ++r) stage((fb + 1) * T + r, sum, -1);
+      finish(sum, cv1);
+    }
   }
-  emit(FB - 1);
+  // the last block or pair
+  const int last = (FB - 1) / PAIR * PAIR;
+  emit(last, cv0);
+  if (PAIR == 2 && last + 1 < FB) emit(last + 1, cv1);
 }
 
 template <int D, int P, int T, bool OUT_BF16>
