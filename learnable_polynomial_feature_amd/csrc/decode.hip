@@ -9,6 +9,8 @@
 // read-out partial; partials are reduced across row groups in a fixed order.
 // The kernel is bound by HBM bandwidth: 2 * m * dv * 4 bytes of state per
 // (batch, head) against ~3 flops per state element.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -42,7 +44,9 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
   return red[0] + red[1] + red[2] + red[3];
 }
 
-// Vector path: dv % 4 == 0 and (dv / 4) divides 256.
+constexpr int kDecodeMaxM = 1024;  // feature count the vector path stages in LDS
+
+// Vector path: dv % 4 == 0, (dv / 4) divides 256, m <= kDecodeMaxM.
 template <bool VBF16>
 __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const float* __restrict__ phiq,
                                                         const float* __restrict__ phik,
@@ -60,22 +64,57 @@ __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const flo
   const float* fk = phik + bh * m;
   float* Sb = S + bh * static_cast<int64_t>(m) * dv;
   const float4 vv = load_v4<VBF16>(v, bh * dv + cg * 4);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int f = rg; f < m; f += RG) {
-    f32x4* p = reinterpret_cast<f32x4*>(Sb + static_cast<int64_t>(f) * dv + cg * 4);
-    f32x4 s = __builtin_nontemporal_load(p);
-    const float kf = fk[f], qf = fq[f];
-    s[0] = fmaf(kf, vv.x, s[0]);
-    s[1] = fmaf(kf, vv.y, s[1]);
-    s[2] = fmaf(kf, vv.z, s[2]);
-    s[3] = fmaf(kf, vv.w, s[3]);
-    __builtin_nontemporal_store(s, p);
-    acc.x = fmaf(qf, s[0], acc.x);
-    acc.y = fmaf(qf, s[1], acc.y);
-    acc.z = fmaf(qf, s[2], acc.z);
-    acc.w = fmaf(qf, s[3], acc.w);
+  // phi_k and phi_q of this (batch, head) in LDS: the row loop then issues
+  // only the state's vector loads and stores
+  __shared__ float fks[kDecodeMaxM], fqs[kDecodeMaxM];
+  for (int f = tid; f < m; f += 256) {
+    fks[f] = fk[f];
+    fqs[f] = fq[f];
   }
+  __syncthreads();
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto update = [&](f32x4& st, float kf, float qf) {
+    st[0] = fmaf(kf, vv.x, st[0]);
+    st[1] = fmaf(kf, vv.y, st[1]);
+    st[2] = fmaf(kf, vv.z, st[2]);
+    st[3] = fmaf(kf, vv.w, st[3]);
+    acc.x = fmaf(qf, st[0], acc.x);
+    acc.y = fmaf(qf, st[1], acc.y);
+    acc.z = fmaf(qf, st[2], acc.z);
+    acc.w = fmaf(qf, st[3], acc.w);
+  };
+  // Rows go in batches whose loads are all issued before the first store: in
+  // a plain loop the compiler cannot move a row's load above the previous
+  // row's store (it cannot prove they miss each other), so each thread would
+  // keep one 16-byte load in flight. Batches of 32 rows (a thread's whole
+  // share at m = 256, dv = 128) keep 512 bytes per thread in flight; smaller
+  // batches take the rest. At 32 rows the kernel needs 256 VGPRs, one wave
+  // per SIMD: fewer concurrent state streams measured faster than two waves
+  // per SIMD with the same batch.
+  int f = rg;
+  auto batch = [&](auto u_c) {
+    constexpr int U = decltype(u_c)::value;
+    for (; f + (U - 1) * RG < m; f += U * RG) {
+      f32x4* p[U];
+      f32x4 st[U];
+      float kf[U], qf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        p[u] = reinterpret_cast<f32x4*>(Sb + static_cast<int64_t>(f + u * RG) * dv + cg * 4);
+        st[u] = __builtin_nontemporal_load(p[u]);
+        kf[u] = fks[f + u * RG];
+        qf[u] = fqs[f + u * RG];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        update(st[u], kf[u], qf[u]);
+        __builtin_nontemporal_store(st[u], p[u]);
+      }
+    }
+  };
+  batch(std::integral_constant<int, 32>{});
+  batch(std::integral_constant<int, 8>{});
+  batch(std::integral_constant<int, 1>{});
   red4[tid] = acc;
   // z update and the normaliser dot product
   float dpart = 0.f;
@@ -145,7 +184,7 @@ hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq, con
   if (BH <= 0) return hipSuccess;
   if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(BH));
-  const bool vec = (dv % 4 == 0) && (dv / 4 <= 256) && (256 % (dv / 4) == 0);
+  const bool vec = (dv % 4 == 0) && (dv / 4 <= 256) && (256 % (dv / 4) == 0) && m <= kDecodeMaxM;
   if (vec) {
     if (v_bf16)
       LLOPS_LAUNCH("decode_state", st, decode_state_vec<true>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
