@@ -146,7 +146,9 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* 
  * matches the inclusive causal mask). q, k [batch][heads][d], v
  * [batch][heads][dv] (in_dtype); S [batch][heads][m][dv] and z
  * [batch][heads][m] fp32, updated in place; out fp32 [batch][heads][dv].
- * shape->n is ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_DECODE).
+ * shape->n is ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_DECODE)
+ * bytes: phi_q and phi_k in fp32, plus repacked copies of Theta_q and Theta_k
+ * for the bf16 shapes that have an unrolled feature-map kernel.
  */
 llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
                                  const void* k, const void* v,

@@ -103,6 +103,11 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
     off = round_up(off + phib, 256);
     w.phik = off;
     off = round_up(off + phib, 256);
+    const size_t pkb = pack_bytes(s, 1);
+    w.pkq = off;
+    off = round_up(off + pkb, 256);
+    w.pkk = off;
+    off = round_up(off + pkb, 256);
   }
   w.total = off;
   return w;
@@ -412,8 +417,10 @@ llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const vo
   char* w = static_cast<char*>(ws);
   float* fq = reinterpret_cast<float*>(w + L.phiq);
   float* fk = reinterpret_cast<float*>(w + L.phik);
-  llops::FeatJob jobs[2] = {{q, theta_q, fq, nullptr}, {k, theta_k, fk, nullptr}};
   const llops::FeatShape fs = feat_shape(s, 1, 0);
+  const bool packed = pack_bytes(s, 1) > 0;
+  llops::FeatJob jobs[2] = {{q, theta_q, fq, packed ? w + L.pkq : nullptr},
+                            {k, theta_k, fk, packed ? w + L.pkk : nullptr}};
   const bool bf16 = s->in_dtype == LLOPS_BF16;
   if (bf16)
     LLOPS_HIP(llops::launch_featmap_bf16(fs, jobs, 2, st), "featmap");

@@ -269,6 +269,8 @@ struct FastArgs {
   int m;
   int64_t pk_hstride;  // packed elements between heads (0 = shared)
   int square;
+  int fsplit;          // feature-block groups per row tile (grid.x = tiles * fsplit)
+  int fb_per;          // 32-feature blocks per group
 };
 
 constexpr int kFastRT = 2;                         // 32-row tiles per wave
@@ -285,12 +287,18 @@ struct FastGeom {
   static constexpr size_t lds_bytes() { return 2ull * STAGE * 2; }
 };
 
-// theta [H'][p][t][d][m] -> packed [H'][m/32][t][p][d/16][64 lanes][8]
-__global__ __launch_bounds__(256) void pack_theta_kernel(const uint16_t* __restrict__ th,
-                                                         uint16_t* __restrict__ pk, int64_t total,
-                                                         int P, int T, int D, int m) {
+// theta [H'][p][t][d][m] -> packed [H'][m/32][t][p][d/16][64 lanes][8];
+// blockIdx.y picks one of up to two (theta, packed) pairs
+struct PackArgs {
+  const uint16_t* th[2];
+  uint16_t* pk[2];
+};
+__global__ __launch_bounds__(256) void pack_theta_kernel(PackArgs pa, int64_t total, int P, int T,
+                                                         int D, int m) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= total) return;
+  const uint16_t* __restrict__ th = pa.th[blockIdx.y];
+  uint16_t* __restrict__ pk = pa.pk[blockIdx.y];
   const int KS = D / 16, FB = m / 32;
   const int lane = static_cast<int>(idx & 63);
   int64_t q = idx >> 6;
@@ -332,11 +340,17 @@ void featmap_fast(FastArgs a) {
   const int hh = lane >> 5, c32 = lane & 31;
   const int64_t h = blockIdx.y;
   const int64_t R = a.B * a.n;
-  const int64_t wrow0 = static_cast<int64_t>(blockIdx.x) * kFastRows + wave * (RT * 32);
+  // few rows (decode-sized batches): the feature blocks of a row tile are
+  // split over a.fsplit workgroups, fb_per blocks each
+  const int tile = blockIdx.x / a.fsplit;
+  const int fb0 = (blockIdx.x - tile * a.fsplit) * a.fb_per;
+  const int FB = min(a.m / 32, fb0 + a.fb_per) - fb0;  // blocks of this workgroup
+  if (FB <= 0) return;
+  const int64_t wrow0 = static_cast<int64_t>(tile) * kFastRows + wave * (RT * 32);
 
-  const uint16_t* pk = static_cast<const uint16_t*>(job.theta_pk) + h * a.pk_hstride;
-  const int FB = a.m / 32;
-  const int nstages = FB * T;  // stage s = (fb, r) = (s / T, s % T)
+  const uint16_t* pk = static_cast<const uint16_t*>(job.theta_pk) + h * a.pk_hstride +
+                       static_cast<int64_t>(fb0) * T * G::STAGE;
+  const int nstages = FB * T;  // stage s = (fb, r) = (s / T, s % T), fb local
   // piece i of stage s: buffer load at a loop-invariant 32-bit lane offset
   // plus a scalar stage offset (no per-stage address registers, so the
   // compiler never reuses load destinations as address temporaries)
@@ -385,8 +399,8 @@ void featmap_fast(FastArgs a) {
   __syncthreads();
 
   const uint16_t* fbase = smem + lane * 8;
-  uint8_t* out = static_cast<uint8_t*>(job.phi);
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  uint8_t* out = static_cast<uint8_t*>(job.phi) + static_cast<int64_t>(fb0) * 32 * ESZ;
   constexpr int NQ = OUT_BF16 ? 2 : 4;  // 16-byte pieces per lane per row tile
   // phi of finished feature blocks, rounded and regrouped so piece q of
   // tile rt is 16 contiguous bytes at byte q*32 + 16*hh of the lane's row.
@@ -532,21 +546,37 @@ hipError_t launch_fast_t(const FeatShape& s, const FeatJob* jobs, int njobs, hip
   a.pk_hstride = s.theta_per_head ? static_cast<int64_t>(P) * T * D * s.m : 0;
   a.square = s.square;
   const int64_t tiles = (s.B * s.n + kFastRows - 1) / kFastRows;
-  if (tiles > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
+  // under ~1024 workgroups, split the feature blocks to fill the chip
+  const int FB = s.m / 32;
+  int fsplit = 1;
+  const int64_t wgs = tiles * s.H * njobs;
+  if (wgs > 0 && wgs < 1024) {
+    const int64_t want = (1024 + wgs - 1) / wgs;
+    fsplit = static_cast<int>(want < FB ? want : FB);
+  }
+  a.fb_per = (FB + fsplit - 1) / fsplit;
+  a.fsplit = (FB + a.fb_per - 1) / a.fb_per;
+  if (tiles * a.fsplit > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
   // repack Theta of every job into its fragment-order buffer
   const int64_t th_heads = s.theta_per_head ? s.H : 1;
   const int64_t total = th_heads * P * T * D * s.m / 8;
+  // one launch for both jobs (the second is skipped when it repeats the first)
+  PackArgs pa{};
+  int npack = 0;
   for (int jb = 0; jb < njobs; ++jb) {
     if (jb == 1 && jobs[1].theta == jobs[0].theta && jobs[1].theta_pk == jobs[0].theta_pk) break;
-    LLOPS_LAUNCH("pack_theta", st, pack_theta_kernel, dim3(static_cast<unsigned>((total + 255) / 256)),
-                 dim3(256), 0, st, static_cast<const uint16_t*>(jobs[jb].theta),
-                 static_cast<uint16_t*>(jobs[jb].theta_pk), total, P, T, D, s.m);
+    pa.th[npack] = static_cast<const uint16_t*>(jobs[jb].theta);
+    pa.pk[npack] = static_cast<uint16_t*>(jobs[jb].theta_pk);
+    ++npack;
   }
+  LLOPS_LAUNCH("pack_theta", st, pack_theta_kernel,
+               dim3(static_cast<unsigned>((total + 255) / 256), static_cast<unsigned>(npack)), dim3(256), 0,
+               st, pa, total, P, T, D, s.m);
   const size_t lds = G::lds_bytes();
   auto* k = featmap_fast<D, P, T, OUT_BF16>;
   const hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H), njobs);
+  dim3 grid(static_cast<unsigned>(tiles * a.fsplit), static_cast<unsigned>(s.H), njobs);
   LLOPS_LAUNCH("featmap_bf16", st, k, grid, dim3(kFastNW * 64), lds, st, a);
   return hipGetLastError();
 }
@@ -558,7 +588,7 @@ hipError_t launch_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipSt
 }
 
 int fast_key(const FeatShape& s) {
-  if (s.B * s.n < 2048 || s.m % 32 != 0) return 0;
+  if (s.B * s.n < 1 || s.m % 32 != 0) return 0;
   const int key = s.d * 10000 + s.p * 100 + s.t;
   switch (key) {
     case 1280204:

@@ -135,8 +135,11 @@ def test_featmap_workspace(L):
     assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None, need, None) == 1
     shared = _shape(batch=1, heads=4, n=4096, d=128, m=256, p=2, t=4, theta_per_head=0)
     assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP) == need // 4
-    for small in (_shape(n=100), _shape(in_dtype=_lib.F32), _shape(n=4096, d=96, m=64)):
-        assert L.llops_workspace_bytes(ctypes.byref(small), _lib.ENTRY_FEATMAP) == 0
+    # few rows take the same kernel with the feature blocks split over workgroups
+    few = _shape(batch=1, heads=4, n=100, d=128, m=256, p=2, t=4)
+    assert L.llops_workspace_bytes(ctypes.byref(few), _lib.ENTRY_FEATMAP) == need
+    for other in (_shape(in_dtype=_lib.F32), _shape(n=4096, d=96, m=64)):
+        assert L.llops_workspace_bytes(ctypes.byref(other), _lib.ENTRY_FEATMAP) == 0
     # the attention entry points hold two repacked copies (Theta_q and Theta_k)
     a = _shape(batch=1, heads=4, n=4096, d=128, dv=128, m=256, p=2, t=4)
     big = L.llops_workspace_bytes(ctypes.byref(a), _lib.ENTRY_CAUSAL)
@@ -211,7 +214,9 @@ def test_workspace_sizes_follow_layout(L):
     need32 = L.llops_workspace_bytes(ctypes.byref(s32), _lib.ENTRY_LINATTN)
     assert need32 >= 2 * 256 * 32 * 4
     dec = _lib.make_shape(batch=128, heads=32, n=1, d=128, dv=128, m=256, p=2, t=4)
-    assert L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_DECODE) == 2 * 128 * 32 * 256 * 4
+    # phi_q and phi_k in fp32, then the two repacked Theta copies
+    pk = 32 * 2 * 4 * 128 * 256 * 2
+    assert L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_DECODE) == 2 * 128 * 32 * 256 * 4 + 2 * pk
 
 
 @fake_ptr
