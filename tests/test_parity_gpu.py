@@ -52,8 +52,9 @@ FEAT_CASES = [
     (1, 1, 600, 256, 64, 2, 2, False, False, False),
     (1, 1, 64, 128, 32, 8, 1, False, False, False),
     (2, 1, 257, 96, 80, 3, 5, True, True, True),
-    # >= 2048 rows per head: the unrolled 512-row-tile kernels, with ragged
-    # tiles, batch boundaries inside a tile and partial phi flush groups
+    # the unrolled 256-row-tile kernels, with ragged tiles, batch boundaries
+    # inside a tile and an odd number of 32-feature blocks (bf16 phi is
+    # stored in block pairs)
     (2, 2, 1100, 128, 256, 2, 4, True, False, False),
     (2, 2, 1100, 128, 256, 2, 4, True, False, True),
     (3, 1, 1000, 128, 64, 2, 1, False, True, True),
@@ -62,6 +63,11 @@ FEAT_CASES = [
     (1, 1, 4096, 128, 80, 2, 4, False, False, False),
     (1, 1, 4096, 128, 80, 2, 4, True, False, True),
     (5, 3, 613, 128, 48, 2, 4, True, False, False),
+    # few row tiles: feature blocks split over workgroups (one block each,
+    # then two per workgroup with a single block left in the last group)
+    (1, 3, 700, 128, 96, 2, 4, True, False, True),
+    (2, 2, 300, 128, 160, 2, 1, False, False, True),
+    (1, 8, 12800, 128, 160, 2, 1, True, False, True),
 ]
 
 
