@@ -183,6 +183,44 @@ def bench_config(w, steps, warmup, torch, lib):
     return t0.elapsed_time(t1) / steps, kern
 
 
+def featmap_variants(steps, torch, lib):
+    """The feature map alone on the p = 4 / t = 1 and BASED-shaped variants at
+    the long workload's geometry (1 x 32 heads x 65536 rows, d = 128, m = 256,
+    bf16 phi), against the bf16 MFMA peak."""
+    res = {}
+    g = torch.Generator(device="cpu").manual_seed(5)
+    B, H, n, d, m = 1, 32, 65536, 128, 256
+    X = (torch.randn(B, H, n, d, generator=g) * 0.5).to(torch.bfloat16).to("cuda")
+    for name, p, t in (("p4_t1", 4, 1), ("based_p2_t1", 2, 1)):
+        th = (torch.randn(H, p, t, d, m, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda")
+        shape = lib.make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=False,
+                               in_dtype=lib.BF16, out_dtype=lib.BF16)
+        ws = torch.empty(max(1, lib.llops_workspace_bytes(shape, lib.ENTRY_FEATMAP)),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, H, n, m), dtype=torch.bfloat16, device="cuda")
+
+        def call():
+            lib.llops_featmap(X, th, out=out, out_dtype=torch.bfloat16, workspace=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        timer = lib.KernelTimer(capacity=4 * steps)
+        with timer:
+            for _ in range(steps):
+                call()
+        torch.cuda.synchronize()
+        kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+        fl = 2.0 * B * H * n * d * p * t * m
+        ms = kern["featmap_bf16"]
+        tf = fl / (ms * 1e-3) / 1e12
+        res[name] = {"workload": f"featmap {B}x{H}x{n} d={d} m={m} p={p} t={t} bf16 phi",
+                     "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+                     "tflop_per_launch": round(fl / 1e12, 4), "achieved_tflops": round(tf, 1),
+                     "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del th, ws, out
+    return res
+
+
 def config_lines(steps, torch, lib):
     """Per-workload throughput next to the bf16 MFMA (or fp32) peak."""
     from learnable_polynomial_feature_amd.workloads import WORKLOADS
@@ -396,6 +434,8 @@ def main():
         }
     if not args.no_configs:
         line["configs"] = config_lines(20, torch, lib)
+        log("feature-map variants")
+        line["variants"] = featmap_variants(10, torch, lib)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -593,7 +593,10 @@ int fast_key(const FeatShape& s) {
   switch (key) {
     case 1280204:
     case 1280201:
+    case 1280401:
     case 640204:
+    case 640201:
+    case 640401:
     case 640308: return key;
     default: return 0;
   }
@@ -606,6 +609,9 @@ bool try_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st
   switch (fast_key(s)) {
     case 1280204: *err = launch_fast<128, 2, 4>(s, jobs, njobs, st); return true;
     case 1280201: *err = launch_fast<128, 2, 1>(s, jobs, njobs, st); return true;
+    case 1280401: *err = launch_fast<128, 4, 1>(s, jobs, njobs, st); return true;
+    case 640201: *err = launch_fast<64, 2, 1>(s, jobs, njobs, st); return true;
+    case 640401: *err = launch_fast<64, 4, 1>(s, jobs, njobs, st); return true;
     case 640204: *err = launch_fast<64, 2, 4>(s, jobs, njobs, st); return true;
     case 640308: *err = launch_fast<64, 3, 8>(s, jobs, njobs, st); return true;
     default: return false;
