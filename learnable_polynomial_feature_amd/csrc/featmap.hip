@@ -1,7 +1,12 @@
 // LLoPS feature map  phi(X) = sum_r prod_j X Theta_{j,r}  [squared after the r-sum]
 // (papernotes.org LLoPS notes, key design 2; arXiv 2610.14219 Sec. 3).
 //
-// bf16 path: each workgroup owns 256 rows (4 waves x 64) of one head. A wave
+// Three kernels: featmap_fast (bf16, (d, p, t) fixed at compile time, 32x32x16
+// MFMA; described at its definition below) takes the shapes it is
+// instantiated for; featmap_mfma (bf16, any shape the validation allows) and
+// featmap_f32_kernel (fp32 inputs) take the rest.
+//
+// featmap_mfma: each workgroup owns 256 rows (4 waves x 64) of one head. A wave
 // keeps its X rows resident as MFMA A-fragments for the whole kernel and
 // walks the features 16 at a time; for every 16-feature block the Theta
 // columns of all (j, r) pairs are staged, transposed to k-major rows, into a
