@@ -100,8 +100,8 @@ size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry);
  * above (in_dtype), phi [batch][heads][n][m] (out_dtype). normalize, delta,
  * dv and chunk are ignored. ws: llops_workspace_bytes(shape,
  * LLOPS_ENTRY_FEATMAP) bytes of device scratch (a repacked copy of Theta for
- * the bf16 shapes that have an unrolled kernel; 0 bytes otherwise, and ws may
- * then be null).
+ * the bf16 shapes that have an unrolled kernel and more than 1024 rows per
+ * head; 0 bytes otherwise, and ws may then be null).
  */
 llops_status_t llops_featmap(const llops_shape_t* shape, const void* X,
                              const void* theta, void* phi, void* ws, size_t ws_bytes,
@@ -148,7 +148,7 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* 
  * [batch][heads][m] fp32, updated in place; out fp32 [batch][heads][dv].
  * shape->n is ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_DECODE)
  * bytes: phi_q and phi_k in fp32, plus repacked copies of Theta_q and Theta_k
- * for the bf16 shapes that have an unrolled feature-map kernel.
+ * when batch > 1024 on a bf16 shape with an unrolled feature-map kernel.
  */
 llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
                                  const void* k, const void* v,

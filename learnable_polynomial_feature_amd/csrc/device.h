@@ -87,6 +87,69 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// ---- MFMA operand fragments from LDS (v_mfma_f32_32x32x16_bf16) -----------
+// "P16" k-order: a 16-deep k-slice puts k = {4hh..4hh+3, 8+4hh..8+4hh+3} in
+// lane half hh (hh = lane / 32). An accumulator tile's elements [8h, 8h+8)
+// have exactly that order over its rows 16h..16h+15, so accumulators can be
+// reused as operands; every other operand of such a product is read in P16
+// order too.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr64(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(
+          reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// B-style fragment (column = lane % 32, k in P16 order) of the matrix
+// M[k][col] stored row-major in LDS: rows kbase..kbase+15, columns
+// cbase..cbase+31. Within each 16-lane group the transposing read hands lane
+// q column q of 4 consecutive rows supplied by lanes q/4 + 4i.
+__device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int stride, int kbase, int cbase,
+                                          int lane) {
+  const int s = lane & 15, G = lane >> 4;
+  const int row = kbase + 4 * (G >> 1) + (s >> 2);
+  const int col = cbase + (G & 1) * 16 + 4 * (s & 3);
+  const uint2 lo = lds_tr64(base + row * stride + col);
+  const uint2 hi = lds_tr64(base + (row + 8) * stride + col);
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// A-style fragment with k in P16 order from row-major M[row][k] in LDS:
+// row = rbase + lane % 32, k = kbase + {4hh..4hh+3, 8+4hh..8+4hh+3}.
+__device__ __forceinline__ bf16x8 frag_p16(const uint16_t* base, int stride, int rbase, int kbase,
+                                           int lane) {
+  const uint16_t* p = base + (rbase + (lane & 31)) * stride + kbase + 4 * (lane >> 5);
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
+// Natural-order fragment (k = kbase + 8hh .. +7) of row-major M[row][k].
+__device__ __forceinline__ bf16x8 frag_nat(const uint16_t* base, int stride, int rbase, int kbase,
+                                           int lane) {
+  return as_bf16x8(ld16(base + (rbase + (lane & 31)) * stride + kbase + 8 * (lane >> 5)));
+}
+
+// Accumulator elements [8h, 8h+8) of a fp32 tile as a bf16 operand (P16).
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& t, int h) {
+  return as_bf16x8(u32x4{pack_bf16x2(t[8 * h + 0], t[8 * h + 1]),
+                         pack_bf16x2(t[8 * h + 2], t[8 * h + 3]),
+                         pack_bf16x2(t[8 * h + 4], t[8 * h + 5]),
+                         pack_bf16x2(t[8 * h + 6], t[8 * h + 7])});
+}
+
+// a if first else b, for two elements of one accumulator tile and a
+// wave-uniform condition. The values pass through an empty asm first: a plain
+// select between elements of one vector is rewritten into an indexed register
+// read (M0-relative moves or a select chain over the whole tile).
+__device__ __forceinline__ float pick(float a, float b, bool first) {
+  asm volatile("" : "+v"(a), "+v"(b));
+  return first ? a : b;
+}
+
+
 // ---- 8x8 bf16 transpose in registers --------------------------------------
 // in[r] holds row r (8 bf16 = 4 dwords; dword w = elements 2w, 2w+1).
 // out[c] receives column c (8 bf16: rows 0..7).

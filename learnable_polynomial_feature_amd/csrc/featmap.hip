@@ -538,6 +538,152 @@ void featmap_fast(FastArgs a) {
   if (PAIR == 2 && last + 1 < FB) emit(last + 1, cv1);
 }
 
+// ---- few rows per head (decode-sized batches): Theta in its natural layout ----
+//
+// With a few hundred rows per head the projection is bound by reading Theta
+// once. A workgroup owns one 32-feature block of one head and every row: it
+// stages Theta_{j,r}[:, block] for all (j, r) side by side in LDS rows of d
+// (natural layout, 16-byte loads) and 32 rows of X per wave, and reads both
+// operands in P16 k-order (the Theta side with the transposing LDS read), so
+// Theta needs no fragment-order copy and no repacking launch.
+constexpr int kSmallRows = 1024;  // rows per head up to which this path runs
+
+struct SmallArgs {
+  FeatJob job[2];
+  int64_t B, H, n;
+  int m;
+  int64_t th_hstride;  // Theta elements between heads (0 = shared)
+  int square;
+};
+
+template <int D, int P, int T>
+struct SmallGeom {
+  static constexpr int PT = P * T;
+  static constexpr int TW = PT * 32 + 16;  // Theta row stride (elements): rows shift by 8 banks
+  static constexpr size_t lds_bytes() { return 1ull * D * TW * 2; }
+};
+
+template <int D, int P, int T, bool OUT_BF16>
+__global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
+  using G = SmallGeom<D, P, T>;
+  constexpr int PT = G::PT, TW = G::TW, KS = D / 16, NF = P * KS;
+  static_assert(PT % 2 == 0, "Theta rows need an even block count to stay conflict free");
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* Ts = smem;           // [D][TW]: Theta_{j,r}[k][block] at column (j*T + r) * 32
+  const FeatJob job = a.job[blockIdx.z];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, c32 = lane & 31;
+  const int fb = blockIdx.x;
+  const int64_t h = blockIdx.y;
+  const int64_t R = a.B * a.n;
+
+  const uint16_t* th = static_cast<const uint16_t*>(job.theta) + h * a.th_hstride;
+  // all of a thread's Theta loads are issued before its first LDS store
+  constexpr int TL = PT * D * 4 / 256;  // 16-byte pieces per thread
+  static_assert((PT * D * 4) % 256 == 0, "Theta block splits evenly over the threads");
+  {
+    u32x4 tv[TL];
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+      const int idx = tid + 256 * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
+      tv[i] = ld16(th + (static_cast<int64_t>(jr) * D + k) * a.m + fb * 32 + q * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+      const int idx = tid + 256 * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
+      st16(Ts + k * TW + jr * 32 + q * 8, tv[i]);
+    }
+  }
+  __syncthreads();
+
+  const uint16_t* X = static_cast<const uint16_t*>(job.X);
+  uint8_t* out = static_cast<uint8_t*>(job.phi);
+  constexpr int ESZ = OUT_BF16 ? 2 : 4;
+  for (int64_t t0 = static_cast<int64_t>(w) * 32; t0 < R; t0 += 4 * 32) {
+    // X fragments straight from global memory in P16 k-order: lane row
+    // t0 + c32, k = 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3} (zeros past the end)
+    bf16x8 xf[KS];
+    {
+      const int64_t r = t0 + c32 < R ? t0 + c32 : R - 1;
+      const int64_t b = r / a.n;
+      const uint16_t* src = X + ((b * a.H + h) * a.n + (r - b * a.n)) * D + 4 * hh;
+      u32x2 lo[KS], hi[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        lo[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16);
+        hi[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16 + 8);
+      }
+      const bool ok = t0 + c32 < R;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        xf[ks] = as_bf16x8(ok ? u32x4{lo[ks][0], lo[ks][1], hi[ks][0], hi[ks][1]} : u32x4{0u, 0u, 0u, 0u});
+    }
+    f32x16 sum = zero16();
+#pragma unroll 1
+    for (int r = 0; r < T; ++r) {
+      // Theta fragments of rank r, (j, ks) flattened, read two ahead (pinned)
+      bf16x8 fr[3];
+      fr[0] = frag_tr(Ts, TW, 0, r * 32, lane);
+      if (NF > 1) fr[1] = frag_tr(Ts, TW, (1 % KS) * 16, ((1 / KS) * T + r) * 32, lane);
+      f32x16 prod, acc;
+#pragma unroll
+      for (int fi = 0; fi < NF; ++fi) {
+        const int j = fi / KS, ks = fi % KS;
+        if (fi + 2 < NF)
+          fr[(fi + 2) % 3] = frag_tr(Ts, TW, ((fi + 2) % KS) * 16, (((fi + 2) / KS) * T + r) * 32, lane);
+        acc = mfma32x32x16(xf[ks], fr[fi % 3], ks == 0 ? zero16() : acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == KS - 1) prod = j == 0 ? acc : prod * acc;
+      }
+      sum += prod;
+    }
+    if (a.square) sum *= sum;
+    // element 4i+e: row t0 + 8i + 4hh + e, feature fb*32 + c32
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = t0 + 8 * i + 4 * hh + e;
+        if (r < R) {
+          const int64_t b = r / a.n;
+          uint8_t* dst = out + (((b * a.H + h) * a.n + (r - b * a.n)) * a.m + fb * 32 + c32) * ESZ;
+          if (OUT_BF16)
+            *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(sum[4 * i + e]);
+          else
+            *reinterpret_cast<float*>(dst) = sum[4 * i + e];
+        }
+      }
+  }
+}
+
+template <int D, int P, int T, bool OUT_BF16>
+hipError_t launch_small_t(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
+  using G = SmallGeom<D, P, T>;
+  SmallArgs a{};
+  a.job[0] = jobs[0];
+  a.job[1] = njobs > 1 ? jobs[1] : jobs[0];
+  a.B = s.B;
+  a.H = s.H;
+  a.n = s.n;
+  a.m = s.m;
+  a.th_hstride = s.theta_per_head ? static_cast<int64_t>(P) * T * D * s.m : 0;
+  a.square = s.square;
+  if (s.H > 65535) return hipErrorInvalidValue;
+  auto* k = featmap_small<D, P, T, OUT_BF16>;
+  const hipError_t e = allow_lds(k, G::lds_bytes());
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>(s.m / 32), static_cast<unsigned>(s.H), njobs);
+  LLOPS_LAUNCH("featmap_bf16", st, k, grid, dim3(256), G::lds_bytes(), st, a);
+  return hipGetLastError();
+}
+
+template <int D, int P, int T>
+hipError_t launch_small(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
+  return s.out_bf16 ? launch_small_t<D, P, T, true>(s, jobs, njobs, st)
+                    : launch_small_t<D, P, T, false>(s, jobs, njobs, st);
+}
+
 template <int D, int P, int T, bool OUT_BF16>
 hipError_t launch_fast_t(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st) {
   using G = FastGeom<D, P>;
@@ -607,7 +753,21 @@ int fast_key(const FeatShape& s) {
   }
 }
 
+bool small_rows(const FeatShape& s) { return s.B * s.n <= kSmallRows; }
+
 bool try_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st, hipError_t* err) {
+  if (small_rows(s)) {
+    switch (fast_key(s)) {
+      case 1280204: *err = launch_small<128, 2, 4>(s, jobs, njobs, st); return true;
+      case 1280201: *err = launch_small<128, 2, 1>(s, jobs, njobs, st); return true;
+      case 1280401: *err = launch_small<128, 4, 1>(s, jobs, njobs, st); return true;
+      case 640204: *err = launch_small<64, 2, 4>(s, jobs, njobs, st); return true;
+      case 640201: *err = launch_small<64, 2, 1>(s, jobs, njobs, st); return true;
+      case 640401: *err = launch_small<64, 4, 1>(s, jobs, njobs, st); return true;
+      case 640308: *err = launch_small<64, 3, 8>(s, jobs, njobs, st); return true;
+      default: return false;
+    }
+  }
   // callers without scratch for the repacked Theta take the generic kernel
   for (int jb = 0; jb < njobs; ++jb)
     if (!jobs[jb].theta_pk) return false;
@@ -626,7 +786,7 @@ bool try_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st
 }  // namespace
 
 size_t featmap_pack_bytes(const FeatShape& s) {
-  if (!fast_key(s)) return 0;
+  if (!fast_key(s) || small_rows(s)) return 0;
   const int64_t th_heads = s.theta_per_head ? s.H : 1;
   return static_cast<size_t>(th_heads) * s.p * s.t * s.d * s.m * sizeof(uint16_t);
 }

@@ -135,9 +135,12 @@ def test_featmap_workspace(L):
     assert L.llops_featmap(ctypes.byref(s), FAKE, FAKE, FAKE, None, need, None) == 1
     shared = _shape(batch=1, heads=4, n=4096, d=128, m=256, p=2, t=4, theta_per_head=0)
     assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP) == need // 4
-    # few rows take the same kernel with the feature blocks split over workgroups
-    few = _shape(batch=1, heads=4, n=100, d=128, m=256, p=2, t=4)
-    assert L.llops_workspace_bytes(ctypes.byref(few), _lib.ENTRY_FEATMAP) == need
+    # up to 1024 rows per head the unrolled shapes read Theta in place (no
+    # repacked copy); f32 inputs and shapes without an unrolled kernel need none
+    few = _shape(batch=1, heads=4, n=1024, d=128, m=256, p=2, t=4)
+    assert L.llops_workspace_bytes(ctypes.byref(few), _lib.ENTRY_FEATMAP) == 0
+    more = _shape(batch=1, heads=4, n=1025, d=128, m=256, p=2, t=4)
+    assert L.llops_workspace_bytes(ctypes.byref(more), _lib.ENTRY_FEATMAP) == need
     for other in (_shape(in_dtype=_lib.F32), _shape(n=4096, d=96, m=64)):
         assert L.llops_workspace_bytes(ctypes.byref(other), _lib.ENTRY_FEATMAP) == 0
     # the attention entry points hold two repacked copies (Theta_q and Theta_k)
@@ -214,9 +217,8 @@ def test_workspace_sizes_follow_layout(L):
     need32 = L.llops_workspace_bytes(ctypes.byref(s32), _lib.ENTRY_LINATTN)
     assert need32 >= 2 * 256 * 32 * 4
     dec = _lib.make_shape(batch=128, heads=32, n=1, d=128, dv=128, m=256, p=2, t=4)
-    # phi_q and phi_k in fp32, then the two repacked Theta copies
-    pk = 32 * 2 * 4 * 128 * 256 * 2
-    assert L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_DECODE) == 2 * 128 * 32 * 256 * 4 + 2 * pk
+    # phi_q and phi_k in fp32 (128 rows per head: Theta is read in place)
+    assert L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_DECODE) == 2 * 128 * 32 * 256 * 4
 
 
 @fake_ptr
