@@ -65,6 +65,44 @@ def featmap(X, theta, square: bool = False) -> np.ndarray:
     return F
 
 
+def featmap_bwd(X, theta, dphi, square: bool = False):
+    """Gradients of phi = featmap(X, theta, square) for an upstream gradient
+    dphi: returns (dX, dtheta), the derivatives of L = sum(dphi * phi).
+
+    X: [n, d]; theta: [p, t, d, m]; dphi: [n, m]. Float64.
+    Theta is trained end to end ([LLoPS-notes] training strategy;
+    [LLoPS-arXiv] Sec. 3). The chain rule through the definition of featmap:
+    with Y_{j,r} = X Theta_{j,r} and s = sum_r prod_j Y_{j,r},
+      ds = dphi * 2 s (squared) or dphi,
+      dY_{j,r} = ds * prod_{j' != j} Y_{j',r},
+      dX = sum_{j,r} dY_{j,r} Theta_{j,r}^T,  dTheta_{j,r} = X^T dY_{j,r}.
+    """
+    X = _f64(X)
+    theta = _f64(theta)
+    G = _f64(dphi)
+    p, t, d, m = theta.shape
+    Y = [[X @ theta[j, r] for r in range(t)] for j in range(p)]
+    s = np.zeros(X.shape[:-1] + (m,))
+    for r in range(t):
+        prod = np.ones_like(s)
+        for j in range(p):
+            prod = prod * Y[j][r]
+        s = s + prod
+    ds = G * (2.0 * s) if square else G
+    dX = np.zeros_like(X)
+    dtheta = np.zeros_like(theta)
+    for r in range(t):
+        for j in range(p):
+            other = np.ones_like(s)
+            for jj in range(p):
+                if jj != j:
+                    other = other * Y[jj][r]
+            dY = ds * other
+            dX = dX + dY @ theta[j, r].T
+            dtheta[j, r] = X.T @ dY
+    return dX, dtheta
+
+
 # --------------------------------------------------------------------------
 # Exact polynomial machinery (explicit d^p expansion; tiny d only)
 # --------------------------------------------------------------------------
@@ -252,6 +290,24 @@ def featmap_bh(X, theta, square=False) -> np.ndarray:
         for h in range(H):
             out[b, h] = featmap(X[b, h], _theta_for(theta, h), square)
     return out
+
+
+def featmap_bwd_bh(X, theta, dphi, square=False):
+    """featmap_bwd over X [B, H, n, d] and dphi [B, H, n, m]; theta [H, p, t,
+    d, m] or shared [p, t, d, m] (whose gradient then sums over all heads)."""
+    theta = np.asarray(theta)
+    B, H = X.shape[:2]
+    dX = np.zeros(X.shape)
+    dth = np.zeros(theta.shape)
+    for b in range(B):
+        for h in range(H):
+            gx, gt = featmap_bwd(X[b, h], _theta_for(theta, h), dphi[b, h], square)
+            dX[b, h] = gx
+            if theta.ndim == 5:
+                dth[h] += gt
+            else:
+                dth += gt
+    return dX, dth
 
 
 def linattn_bh(Q, K, V, theta_q, theta_k, **kw) -> np.ndarray:

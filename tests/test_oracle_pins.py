@@ -319,3 +319,63 @@ def test_batched_wrappers_use_per_head_theta():
             np.testing.assert_allclose(out[b, h], want, rtol=1e-11)
     shared = O.featmap_bh(Q, tq[1])
     np.testing.assert_allclose(shared[1, 2], O.featmap(Q[1, 2], tq[1]), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# feature-map backward (gradients of L = sum(dphi * phi))
+# ---------------------------------------------------------------------------
+def _loss(X, theta, G, square):
+    return float(np.sum(G * O.featmap(X, theta, square)))
+
+
+@pytest.mark.parametrize("p,t,square", [(2, 2, False), (2, 2, True), (3, 1, True), (1, 3, False)])
+def test_featmap_bwd_matches_central_differences(p, t, square):
+    """Every entry of dX and dTheta against a central difference of the loss
+    in float64 (step 1e-6 on O(1) values: truncation error ~1e-12)."""
+    rng = np.random.default_rng(31)
+    n, d, m = 5, 3, 4
+    X = rng.standard_normal((n, d))
+    theta = rng.standard_normal((p, t, d, m)) * 0.7
+    G = rng.standard_normal((n, m))
+    dX, dth = O.featmap_bwd(X, theta, G, square)
+    eps = 1e-6
+    for idx in np.ndindex(X.shape):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[idx] += eps
+        Xm[idx] -= eps
+        fd = (_loss(Xp, theta, G, square) - _loss(Xm, theta, G, square)) / (2 * eps)
+        assert abs(dX[idx] - fd) <= 1e-6 * max(1.0, abs(fd))
+    for idx in np.ndindex(theta.shape):
+        tp, tm = theta.copy(), theta.copy()
+        tp[idx] += eps
+        tm[idx] -= eps
+        fd = (_loss(X, tp, G, square) - _loss(X, tm, G, square)) / (2 * eps)
+        assert abs(dth[idx] - fd) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_featmap_bwd_degree_one_is_linear_map_gradient():
+    """p = t = 1 makes phi = X Theta: the textbook gradients dX = dphi Theta^T
+    and dTheta = X^T dphi; squared, phi = (X Theta)^2 doubles dphi by X Theta."""
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((7, 4))
+    W = rng.standard_normal((4, 6))
+    G = rng.standard_normal((7, 6))
+    dX, dth = O.featmap_bwd(X, W[None, None], G)
+    assert np.allclose(dX, G @ W.T, rtol=1e-13, atol=1e-13)
+    assert np.allclose(dth[0, 0], X.T @ G, rtol=1e-13, atol=1e-13)
+    dX2, dth2 = O.featmap_bwd(X, W[None, None], G, square=True)
+    G2 = 2.0 * (X @ W) * G
+    assert np.allclose(dX2, G2 @ W.T, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dth2[0, 0], X.T @ G2, rtol=1e-12, atol=1e-12)
+
+
+def test_featmap_bwd_shared_theta_sums_heads():
+    """With one Theta for every head its gradient is the sum of the per-head
+    gradients (the same array appears in every head's map)."""
+    rng = np.random.default_rng(33)
+    X = rng.standard_normal((2, 3, 4, 3))
+    th = rng.standard_normal((2, 2, 3, 4))
+    G = rng.standard_normal((2, 3, 4, 4))
+    _, dth_shared = O.featmap_bwd_bh(X, th, G)
+    _, dth_heads = O.featmap_bwd_bh(X, np.repeat(th[None], 3, axis=0), G)
+    assert np.allclose(dth_shared, dth_heads.sum(axis=0), rtol=1e-13, atol=1e-13)
