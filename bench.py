@@ -221,6 +221,59 @@ def featmap_variants(steps, torch, lib):
     return res
 
 
+def featmap_backward(steps, torch, lib):
+    """The feature map's backward (dX and dTheta from a bf16 dphi) at the long
+    workload's geometry: 1 x 32 heads x 65536 rows, d = 128, m = 256, p = 2,
+    t = 4, squared, per-head Theta. Algorithmic work is three products of
+    2 d m p t flops per row (Y = X Theta, dY Theta^T, X^T dY); the kernels
+    recompute Y (twice in the dX kernel when squared) instead of storing it."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    B, H, n, d, m, p, t = 1, 32, 65536, 128, 256, 2, 4
+    X = (torch.randn(B, H, n, d, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda")
+    th = (torch.randn(H, p, t, d, m, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda")
+    G = torch.randn(B, H, n, m, generator=g).to(torch.bfloat16).to("cuda")
+    shape = lib.make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=True,
+                           in_dtype=lib.BF16, out_dtype=lib.BF16)
+    ws = torch.empty(max(1, lib.llops_workspace_bytes(shape, lib.ENTRY_FEATMAP_BWD)),
+                     dtype=torch.uint8, device="cuda")
+    dX = torch.empty((B, H, n, d), dtype=torch.float32, device="cuda")
+    dth = torch.empty(th.shape, dtype=torch.float32, device="cuda")
+
+    def call():
+        lib.llops_featmap_bwd(X, th, G, square=True, dX=dX, dtheta=dth, workspace=ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    timer = lib.KernelTimer(capacity=4 * steps)
+    with timer:
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    unit = 2.0 * B * H * n * d * m * p * t
+    fl = 3 * unit
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"workload": f"featmap backward {B}x{H}x{n} d={d} m={m} p={p} t={t} squared, "
+                       "bf16 X/Theta/dphi, fp32 dX/dTheta",
+           "ms_per_call": round(ms, 4), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
+           "algorithmic_tflop": round(fl / 1e12, 4), "achieved_tflops": round(tf, 1),
+           "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+           "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+    # per kernel: dX does Y (x2 when squared) and dY Theta^T; dTheta does Y and X^T dY
+    for k, mult in (("featmap_bwd_dx", 2), ("featmap_bwd_dth", 2)):
+        if k in kern:
+            a = mult * unit / (kern[k] * 1e-3) / 1e12
+            res[k] = {"algorithmic_tflop": round(mult * unit / 1e12, 4),
+                      "achieved_tflops": round(a, 1), "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    del X, th, G, ws, dX, dth
+    return res
+
+
 def config_lines(steps, torch, lib):
     """Per-workload throughput next to the bf16 MFMA (or fp32) peak."""
     from learnable_polynomial_feature_amd.workloads import WORKLOADS
@@ -436,6 +489,8 @@ def main():
         line["configs"] = config_lines(20, torch, lib)
         log("feature-map variants")
         line["variants"] = featmap_variants(10, torch, lib)
+        log("feature-map backward")
+        line["featmap_backward"] = featmap_backward(10, torch, lib)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -68,7 +68,8 @@ typedef enum {
   LLOPS_ENTRY_FEATMAP = 0,
   LLOPS_ENTRY_LINATTN = 1,
   LLOPS_ENTRY_CAUSAL = 2,
-  LLOPS_ENTRY_DECODE = 3
+  LLOPS_ENTRY_DECODE = 3,
+  LLOPS_ENTRY_FEATMAP_BWD = 4
 } llops_entry_t;
 
 typedef struct llops_shape {
@@ -106,6 +107,28 @@ size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry);
 llops_status_t llops_featmap(const llops_shape_t* shape, const void* X,
                              const void* theta, void* phi, void* ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/*
+ * llops_featmap_bwd -- gradients of L = sum(dphi * phi) for phi = llops_featmap(X, Theta):
+ *   Y_{j,r} = X Theta_{j,r},  s = sum_r prod_j Y_{j,r},  ds = dphi * 2s (square) or dphi,
+ *   dY_{j,r} = ds * prod_{j' != j} Y_{j',r},
+ *   dX = sum_{j,r} dY_{j,r} Theta_{j,r}^T,  dTheta_{j,r} = X^T dY_{j,r}
+ * (the chain rule through key design 2 of the notes; Theta is learned end to
+ * end, notes' training strategy). X and Theta as for llops_featmap (in_dtype
+ * BF16 only); dphi [batch][heads][n][m] in out_dtype (F32 or BF16); dX fp32
+ * [batch][heads][n][d]; dtheta fp32 in Theta's layout, summed over heads when
+ * Theta is shared. Both outputs are overwritten (n = 0 with heads > 0 writes
+ * a zero dtheta). Kernels exist for p = 2, t in {1, 4}, d in {64, 128},
+ * m % 32 == 0 (else LLOPS_ERR_UNSUPPORTED). Y is recomputed from X on MFMA
+ * and dY rounded to bf16 before its two products; the head and row sums run
+ * in a fixed order, so results are deterministic. ws:
+ * llops_workspace_bytes(shape, LLOPS_ENTRY_FEATMAP_BWD) bytes (partial dTheta
+ * sums per row chunk). normalize, delta, dv and chunk are ignored.
+ */
+llops_status_t llops_featmap_bwd(const llops_shape_t* shape, const void* X,
+                                 const void* theta, const void* dphi, float* dX,
+                                 float* dtheta, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 /*
  * llops_linattn_fwd -- non-causal linear attention

@@ -17,10 +17,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libllops.so")
 
 F32, BF16 = 0, 1
-ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE = 0, 1, 2, 3
+ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD = 0, 1, 2, 3, 4
 STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
           3: "LLOPS_ERR_WORKSPACE", 4: "LLOPS_ERR_HIP"}
-EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_linattn_fwd",
+EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd",
            "llops_linattn_causal_fwd", "llops_decode_step", "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -61,6 +61,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_workspace_bytes.restype = ctypes.c_size_t
     lib.llops_featmap.argtypes = [SP, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_featmap.restype = ctypes.c_int
+    lib.llops_featmap_bwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.llops_featmap_bwd.restype = ctypes.c_int
     lib.llops_linattn_fwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_linattn_fwd.restype = ctypes.c_int
     lib.llops_linattn_causal_fwd.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -158,6 +160,39 @@ def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32, 
     _check(lib.llops_featmap(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(out), _ptr(ws), wsb,
                              _stream(X)))
     return out
+
+
+def llops_featmap_bwd(X, theta, dphi, *, square=False, dX=None, dtheta=None, workspace=None):
+    """Gradients (dX, dtheta) of sum(dphi * phi) for phi = llops_featmap(X, theta, square).
+
+    X [B, H, n, d] and theta bf16; dphi [B, H, n, m] fp32 or bf16; dX fp32 like
+    X, dtheta fp32 like theta (summed over heads when theta is shared).
+    """
+    X = _dev(X, "X")
+    theta = _dev(theta, "theta")
+    dphi = _dev(dphi, "dphi")
+    if X.dim() != 4:
+        raise ValueError("X must be [batch, heads, n, d]")
+    B, H, n, d = X.shape
+    (p, t, td, m), per_head = _theta_dims(theta, H)
+    if td != d or theta.dtype != X.dtype:
+        raise ValueError("theta's d and dtype must match X")
+    if tuple(dphi.shape) != (B, H, n, m):
+        raise ValueError(f"dphi must be [{B}, {H}, {n}, {m}]")
+    if dX is None:
+        dX = torch.empty((B, H, n, d), dtype=torch.float32, device=X.device)
+    if dtheta is None:
+        dtheta = torch.empty(theta.shape, dtype=torch.float32, device=X.device)
+    for name, o, want in (("dX", dX, (B, H, n, d)), ("dtheta", dtheta, tuple(theta.shape))):
+        if o.dtype != torch.float32 or tuple(o.shape) != want or not o.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {want}")
+    shape = make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=square,
+                       theta_per_head=per_head, in_dtype=_dt(X), out_dtype=_dt(dphi))
+    lib = library()
+    ws, wsb = _workspace(shape, ENTRY_FEATMAP_BWD, X.device, workspace)
+    _check(lib.llops_featmap_bwd(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(dphi), _ptr(dX),
+                                 _ptr(dtheta), _ptr(ws), wsb, _stream(X)))
+    return dX, dtheta
 
 
 def _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk):

@@ -81,6 +81,10 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
   if (entry == LLOPS_ENTRY_FEATMAP) {
     w.pkq = off;
     off = round_up(off + pack_bytes(s, s->n), 256);
+  } else if (entry == LLOPS_ENTRY_FEATMAP_BWD) {
+    w.seg = off;
+    if (s->in_dtype == LLOPS_BF16)
+      off = round_up(off + llops::featmap_bwd_ws_bytes(feat_shape(s, s->n, 0)), 256);
   } else if (entry == LLOPS_ENTRY_LINATTN || entry == LLOPS_ENTRY_CAUSAL) {
     const SegPlan sp = seg_plan(s, entry == LLOPS_ENTRY_CAUSAL);
     const size_t phib = BH * static_cast<size_t>(s->n) * s->m * esz;
@@ -117,6 +121,8 @@ bool is01(int32_t x) { return x == 0 || x == 1; }
 
 llops_status_t validate(const llops_shape_t* s, int entry) {
   if (!s) return fail(LLOPS_ERR_INVALID_ARG, "shape is null");
+  // the backward takes the feature map's shape rules
+  if (entry == LLOPS_ENTRY_FEATMAP_BWD) entry = LLOPS_ENTRY_FEATMAP;
   if (s->batch < 0 || s->heads < 0) return fail(LLOPS_ERR_INVALID_ARG, "batch/heads < 0");
   if (entry != LLOPS_ENTRY_DECODE && s->n < 0) return fail(LLOPS_ERR_INVALID_ARG, "n < 0");
   if (s->d < 1 || s->m < 1 || s->p < 1 || s->t < 1)
@@ -351,7 +357,7 @@ int32_t llops_profile_disarm(void) {
 }
 
 size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
-  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_DECODE) return 0;
+  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_FEATMAP_BWD) return 0;
   if (validate(shape, entry) != LLOPS_OK) return 0;
   return ws_layout(shape, entry).total;
 }
@@ -376,6 +382,38 @@ llops_status_t llops_featmap(const llops_shape_t* s, const void* X, const void* 
     LLOPS_HIP(llops::launch_featmap_bf16(fs, &job, 1, st), "featmap");
   else
     LLOPS_HIP(llops::launch_featmap_f32(fs, &job, 1, st), "featmap");
+  return LLOPS_OK;
+}
+
+llops_status_t llops_featmap_bwd(const llops_shape_t* s, const void* X, const void* theta,
+                                 const void* dphi, float* dX, float* dtheta, void* ws,
+                                 size_t ws_bytes, hipStream_t st) {
+  LLOPS_TRY(validate(s, LLOPS_ENTRY_FEATMAP_BWD));
+  if (s->in_dtype != LLOPS_BF16)
+    return fail(LLOPS_ERR_UNSUPPORTED, "featmap backward takes bf16 X and Theta only");
+  const llops::FeatShape fs = feat_shape(s, s->n, 0);
+  if (!llops::featmap_bwd_supported(fs))
+    return fail(LLOPS_ERR_UNSUPPORTED,
+                "featmap backward kernels: p = 2, t in {1, 4}, d in {64, 128}, m %% 32 == 0 "
+                "(got p=%d t=%d d=%d m=%d)", s->p, s->t, s->d, s->m);
+  if (s->heads == 0) return LLOPS_OK;  // nothing to write
+  const bool rows = s->batch > 0 && s->n > 0;
+  LLOPS_TRY(need(theta, "theta"));
+  LLOPS_TRY(need(dtheta, "dtheta"));
+  if (rows) {
+    LLOPS_TRY(need(X, "X"));
+    LLOPS_TRY(need(dphi, "dphi"));
+    LLOPS_TRY(need(dX, "dX"));
+  }
+  const WsLayout L = ws_layout(s, LLOPS_ENTRY_FEATMAP_BWD);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (L.total && !ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  if (ws) LLOPS_TRY(opt(ws, "ws"));
+  LLOPS_HIP(llops::launch_featmap_bwd(fs, X, theta, dphi, s->out_dtype == LLOPS_BF16 ? 1 : 0, dX,
+                                      dtheta, L.total ? static_cast<char*>(ws) + L.seg : nullptr,
+                                      st),
+            "featmap_bwd");
   return LLOPS_OK;
 }
 

@@ -55,6 +55,16 @@ hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njob
 hipError_t launch_featmap_f32(const FeatShape& s, const FeatJob* jobs, int njobs,
                               hipStream_t st);
 
+// Feature-map backward (bf16 X and Theta): dX [B][H][n][d] and dtheta in
+// Theta's layout (fp32; summed over heads for a shared Theta) from dphi
+// [B][H][n][m] (bf16 when dphi_bf16, else fp32). dtheta is overwritten.
+bool featmap_bwd_supported(const FeatShape& s);
+// Scratch bytes for the per-chunk partial dTheta sums.
+size_t featmap_bwd_ws_bytes(const FeatShape& s);
+hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* theta,
+                              const void* dphi, int dphi_bf16, float* dX, float* dtheta,
+                              void* ws, hipStream_t st);
+
 // Linear-attention contraction over precomputed features.
 struct AttnShape {
   int64_t BH, n;

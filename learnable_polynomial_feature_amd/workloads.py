@@ -14,6 +14,7 @@ Distributions (the five workloads the hot path is measured on):
   Q, K  ~ N(0,1)/sqrt(d), or rows L2-normalised then scaled by 2
   V     ~ N(0,1) (the tiny fp32 case: N(0,1)/sqrt(d))
   Theta ~ N(0, 1/d), i.e. standard deviation 1/sqrt(d), one draw per head
+  dphi  ~ N(0,1): the upstream gradient handed to the feature-map backward
 Draws are float32; bf16 workloads round to bf16 with round-to-nearest-even and
 keep the rounded values in float32 arrays (exactly representable), so the GPU
 receives them losslessly and the oracle sees the identical numbers.
@@ -29,6 +30,7 @@ import numpy as np
 # tensor ids for stream derivation
 _T_Q, _T_K, _T_V, _T_THQ, _T_THK = 1, 2, 3, 4, 5
 _T_PRE_K, _T_PRE_V, _T_STEP_Q, _T_STEP_K, _T_STEP_V = 6, 7, 8, 9, 10
+_T_DPHI = 11
 
 
 @dataclasses.dataclass(frozen=True)
@@ -142,6 +144,32 @@ def theta_head(w: Workload, which: str, h: int) -> np.ndarray:
     tid = _T_THQ if which == "q" else _T_THK
     x = _normal(w.seed, tid, (h,), (w.p, w.t, w.d, w.m)) / np.float32(np.sqrt(w.d))
     return _store(w, x)
+
+
+def dphi_slice(w: Workload, b: int, h: int, bf16: bool = False) -> np.ndarray:
+    """One (b, h) slice [n, m] of the feature map's upstream gradient, float32
+    draws (rounded to bf16 values when ``bf16``)."""
+    x = _normal(w.seed, _T_DPHI, (b, h), (w.n, w.m))
+    return round_bf16(x) if bf16 else x
+
+
+def q_and_dphi(w: Workload, heads: list[int] | None = None,
+               batches: list[int] | None = None, bf16_dphi: bool = False) -> dict:
+    """Q [B', H', n, d] (the feature map's input X) and dphi [B', H', n, m]."""
+    heads = list(range(w.heads)) if heads is None else list(heads)
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    B, H = len(batches), len(heads)
+    Q = np.empty((B, H, w.n, w.d), np.float32)
+    G = np.empty((B, H, w.n, w.m), np.float32)
+
+    def fill(bh):
+        bi, hi = bh
+        Q[bi, hi] = qk_slice(w, "q", batches[bi], heads[hi])
+        G[bi, hi] = dphi_slice(w, batches[bi], heads[hi], bf16_dphi)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, [(bi, hi) for bi in range(B) for hi in range(H)]))
+    return {"Q": Q, "dphi": G, "theta_q": np.stack([theta_head(w, "q", h) for h in heads])}
 
 
 def generate(w: Workload, heads: list[int] | None = None,

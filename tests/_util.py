@@ -36,7 +36,12 @@ def announce(msg: str):
 #  bf16 feature map stored as bf16                        -> 5e-3: one rounding to 8
 #      significant bits (unit roundoff 2^-8) on top of the fp32 result
 #  bf16 attention paths (phi, A and S rounded to bf16 as MFMA operands) -> 2e-2
+#  feature-map backward (bf16 X, Theta)                   -> 5e-3: Y and s are exact
+#      products summed in fp32; dY is rounded once to bf16 (unit roundoff 2^-9)
+#      before the two fp32-accumulated products, so each output is a sum of
+#      terms with one independent relative error of at most 2^-9 each
 TOL_F32 = 1e-5
 TOL_FEAT_BF16_IN = 1e-5
 TOL_FEAT_BF16_OUT = 5e-3
 TOL_BF16 = 2e-2
+TOL_BWD_BF16 = 5e-3

@@ -248,3 +248,53 @@ def test_missing_library_raises(tmp_path):
             mod.library(str(tmp_path / "nope.so"))
     finally:
         mod._LIB = saved
+
+
+def _bwd_shape(**kw):
+    base = dict(batch=2, heads=3, n=100, d=64, m=64, p=2, t=4, square=1)
+    base.update(kw)
+    return _shape(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(p=0), 1), (dict(m=0), 1), (dict(in_dtype=7), 1), (dict(square=2), 1), (dict(n=-1), 1),
+    (dict(t=2), 2), (dict(p=3), 2), (dict(p=1), 2), (dict(d=96), 2), (dict(m=48), 2),
+    (dict(in_dtype=_lib.F32), 2), (dict(p=9), 2),
+])
+@fake_ptr
+def test_featmap_bwd_validation(L, bad, code):
+    s = _bwd_shape(**bad)
+    st = L.llops_featmap_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code, _err(L)
+
+
+@fake_ptr
+def test_featmap_bwd_pointers_and_workspace(L):
+    s = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4)
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP_BWD)
+    slot = 4 * 2 * 4 * 256 * 128 * 4  # one fp32 partial dTheta for every head
+    assert need > 0 and need % slot == 0
+    shared = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, theta_per_head=0)
+    assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP_BWD) == need
+    args = [FAKE] * 5
+    assert L.llops_featmap_bwd(ctypes.byref(s), *args, FAKE, need - 1, None) == 3
+    assert "workspace" in _err(L)
+    assert L.llops_featmap_bwd(ctypes.byref(s), *args, None, need, None) == 1
+    for i, name in enumerate(("X", "theta", "dphi", "dX", "dtheta")):
+        a = list(args)
+        a[i] = None
+        assert L.llops_featmap_bwd(ctypes.byref(s), *a, FAKE, need, None) == 1
+        assert f"{name} is null" in _err(L)
+        a[i] = MISALIGNED
+        assert L.llops_featmap_bwd(ctypes.byref(s), *a, FAKE, need, None) == 1
+        assert "aligned" in _err(L)
+    # no rows: X, dphi and dX may be null (dtheta is still written, as zeros)
+    empty = _bwd_shape(batch=1, heads=4, n=0, d=128, m=256, t=4)
+    assert L.llops_workspace_bytes(ctypes.byref(empty), _lib.ENTRY_FEATMAP_BWD) == 0
+    assert L.llops_featmap_bwd(ctypes.byref(empty), None, FAKE, None, None, None, None, 0,
+                               None) == 1
+    assert "dtheta is null" in _err(L)
+    # t = 1 keeps one partial per wave and chunk
+    t1 = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=1)
+    need1 = L.llops_workspace_bytes(ctypes.byref(t1), _lib.ENTRY_FEATMAP_BWD)
+    assert need1 > 0 and need1 % (4 * 4 * 2 * 1 * 256 * 128 * 4) == 0
