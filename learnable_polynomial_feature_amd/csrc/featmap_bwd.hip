@@ -19,14 +19,19 @@
 // operand straight from its accumulator, Theta^T read from the staged rows.
 //
 // dTheta (featmap_bwd_dth): a workgroup owns one feature block, one head and
-// one chunk of rows, and walks the chunk 32 rows at a time with the rows
-// staged in LDS. Y is recomputed in the natural orientation (rows x
-// features), so dY^T is an A operand from registers and X (read transposed
-// from LDS) the B operand. With t = 4 each wave takes one rank and the waves
-// swap their rank's product through LDS to form s; with t = 1 every wave
-// computes the one rank and takes a quarter of the d columns. The workgroup
-// writes its chunk's partial dTheta; featmap_bwd_reduce sums the chunks (and
-// the heads, for a shared Theta) in a fixed order and transposes.
+// one chunk of rows. Each wave keeps the Theta fragments of its rank in
+// registers for the whole chunk and walks the chunk a step of rows at a time
+// with the rows staged in LDS. Y is recomputed in the natural orientation
+// (rows x features), so dY^T is an A operand from registers and X (read
+// transposed from LDS) the B operand. With t = 4 the four waves take one rank
+// each over the same 32 rows and swap their rank's product through LDS to
+// form s; with t = 1 each wave takes its own 32 of a 128-row step. The
+// workgroup writes its chunk's partial dTheta (one per wave for t = 1);
+// featmap_bwd_reduce sums the partials (and the heads, for a shared Theta) in
+// a fixed order and transposes.
+#include <algorithm>
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -38,7 +43,8 @@ struct BwdArgs {
   const uint16_t* theta;  // [H'][p][t][d][m] bf16
   const void* dphi;       // [B][H][n][m], fp32 or bf16
   float* dX;              // [B][H][n][d]
-  float* part;            // dTheta partials [chunk][H][p][t][m][d]
+  float* part;            // dTheta partials [slot][H][p][t][m][d]
+  uint16_t* ds;           // [B][H][n][m] bf16: ds of the squared map when t > 1 (else null)
   int64_t B, H, n;
   int m;
   int64_t th_hstride;     // Theta elements between heads (0 = shared)
@@ -56,8 +62,7 @@ struct BwdGeom {
   static constexpr int XW = D + 16;        // staged X row stride: rows shift by 8 banks
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
-  static constexpr size_t x_lds() { return 1ull * RB * XW * 2; }
-  static constexpr size_t exch_lds() { return T == 4 ? 4ull * 16 * 64 * 4 : 0; }
+  static constexpr size_t x_lds() { return 2ull * RB * XW * 2; }  // double buffered
   static_assert(PT % 2 == 0, "staged Theta rows need an even block count to stay conflict free");
   static_assert((PT * D * 4) % 256 == 0, "a Theta block splits evenly over the threads");
 };
@@ -81,17 +86,51 @@ __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t
   }
 }
 
-// Sequence row of head h for row r of the head's [B*n] rows.
-__device__ __forceinline__ int64_t rho_of(int64_t r, int64_t h, const BwdArgs& a) {
-  const int64_t b = r / a.n;
-  return (b * a.H + h) * a.n + (r - b * a.n);
+// Row t of a head's B*n rows is token i of sequence b, stored at sequence row
+// (b*H + h)*n + i. A cursor holds (b, i) of a wave-uniform row t0, so the
+// rows t0 + o nearby need no division: with n >= span (the largest o + 1)
+// they cross at most one sequence boundary.
+struct RowCursor {
+  int64_t b, i;
+};
+
+__device__ __forceinline__ RowCursor cursor_at(int64_t t, const BwdArgs& a) {
+  const int64_t b = t / a.n;
+  return RowCursor{b, t - b * a.n};
+}
+
+__device__ __forceinline__ RowCursor cursor_advance(RowCursor c, int64_t by, const BwdArgs& a) {
+  c.i += by;
+  while (c.i >= a.n) {  // wave-uniform; one pass when n >= by
+    c.i -= a.n;
+    ++c.b;
+  }
+  return c;
+}
+
+template <bool ONE_WRAP>
+__device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64_t h,
+                                            const BwdArgs& a) {
+  int64_t i = c.i + o, b = c.b;
+  if constexpr (ONE_WRAP) {
+    const bool wrap = i >= a.n;
+    i = wrap ? i - a.n : i;
+    b = wrap ? b + 1 : b;
+  } else {
+    const int64_t q = i / a.n;
+    b += q;
+    i -= q * a.n;
+  }
+  return (b * a.H + h) * a.n + i;
 }
 
 // ---------------------------------------------------------------------------
 // dX
 // ---------------------------------------------------------------------------
 // GB: dphi is bf16 (else fp32).
-template <int D, int P, int T, bool GB>
+// OW: n >= 32, so a wave's 32 rows cross at most one sequence boundary.
+// WDS: also store ds (squared map, t > 1) as bf16 for the dTheta kernel.
+template <int D, int P, int T, bool GB, bool OW, bool WDS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_bwd_dx(BwdArgs a) {
   using G = BwdGeom<D, P, T>;
@@ -109,7 +148,9 @@ void featmap_bwd_dx(BwdArgs a) {
   // k = 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}; zeros past the end
   bf16x8 xf[KS];
   const bool ok = t0 + c32 < R;
-  const int64_t rho = rho_of(ok ? t0 + c32 : R - 1, h, a);
+  const int64_t tb = t0 < R ? t0 : R - 1;  // a wave past the end reads the last row
+  const RowCursor cur = cursor_at(tb, a);
+  const int64_t rho = rho_near<OW>(cur, ok ? c32 : R - 1 - tb, h, a);
   {
     const uint16_t* src = a.X + rho * D + 4 * hh;
     u32x2 lo[KS], hi[KS];
@@ -127,7 +168,7 @@ void featmap_bwd_dx(BwdArgs a) {
 
   // Y_{j,r} of the staged feature block, transposed: element 4i+e is
   // feature 8i + 4hh + e of row t0 + c32
-  auto y_of = [&](int j, int r) {
+  auto y_of = [&](int j, int r) __attribute__((always_inline)) {
     f32x16 acc = zero16();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -181,6 +222,15 @@ void featmap_bwd_dx(BwdArgs a) {
       ds *= 2.f * s;
     }
     if (!ok) ds = zero16();
+    if constexpr (WDS) {
+      if (ok) {
+        uint16_t* dst = a.ds + rho * a.m + fb * 32 + 4 * hh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x2*>(dst + 8 * i) =
+              u32x2{pack_bf16x2(ds[4 * i], ds[4 * i + 1]), pack_bf16x2(ds[4 * i + 2], ds[4 * i + 3])};
+      }
+    }
 #pragma unroll 1
     for (int r = 0; r < T; ++r) {
       f32x16 y[P];
@@ -210,9 +260,9 @@ void featmap_bwd_dx(BwdArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t r = t0 + 8 * i + 4 * hh + e;
-      if (r < R) {
-        float* dst = a.dX + rho_of(r, h, a) * D + c32;
+      const int o = 8 * i + 4 * hh + e;
+      if (t0 + o < R) {
+        float* dst = a.dX + rho_near<OW>(cur, o, h, a) * D + c32;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) dst[dt * 32] = dx[dt][4 * i + e];
       }
@@ -222,7 +272,13 @@ void featmap_bwd_dx(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dTheta partials
 // ---------------------------------------------------------------------------
-template <int D, int P, int T, bool GB>
+// RM, how a step's rows map to sequence rows: 2 = n is a multiple of the
+// step, so a step's rows are consecutive in memory; 1 = n >= the step, so a
+// step crosses at most one sequence boundary; 0 = any n.
+// GB: the gradient read (dphi, or ds from the dX kernel) is bf16.
+// With t = 4 and a squared map the gradient read is ds itself; with t = 1
+// and a squared map each wave forms s from its own (only) rank.
+template <int D, int P, int T, bool GB, int RM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void featmap_bwd_dth(BwdArgs a) {
   using G = BwdGeom<D, P, T>;
@@ -231,10 +287,11 @@ void featmap_bwd_dth(BwdArgs a) {
   constexpr int RB = G::RB;                 // rows per step
   constexpr int XL = RB * (D / 8) / 256;    // 16-byte pieces of a step's X per thread
   static_assert(XL >= 1 && RB * (D / 8) % 256 == 0, "a step's rows split evenly over the threads");
+  // LDS: the staged Theta block at the start; once each wave holds its
+  // rank's Theta fragments in registers, the same bytes hold two steps' rows
+  // of X (one being read, the next being written).
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* Ts = smem;
-  uint16_t* Xs = smem + D * TW;
-  float* exch = reinterpret_cast<float*>(Xs + RB * XW);  // [wave][4][64][4] (t = 4)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
@@ -253,8 +310,18 @@ void featmap_bwd_dth(BwdArgs a) {
   const int64_t r1 = min(R, r0 + a.chunk_rows);
   const int rk = T == 4 ? w : 0;       // the rank this wave recomputes
   const int wr = T == 4 ? 0 : 32 * w;  // this wave's first row within a step
+  const void* gsrc = (T > 1 && a.square) ? static_cast<const void*>(a.ds) : a.dphi;
+  const bool own_s = T == 1 && a.square;
 
   stage_theta<D, PT>(Ts, TW, a.theta + h * a.th_hstride, a.m, fb, tid);
+  __syncthreads();
+  // B operands of Y_{j,rk} = X Theta_{j,rk}: Theta rows 16ks.. (P16), lane
+  // column c32 = feature fb*32 + c32; held for the whole chunk
+  bf16x8 tf[P][KS];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) tf[j][ks] = frag_tr(Ts, TW, ks * 16, (j * T + rk) * 32, lane);
 
   f32x16 acc[P][DT];
 #pragma unroll
@@ -262,77 +329,122 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[j][dt] = zero16();
 
-  // X of one step, row-major; rows past the chunk read its last row
+  // One step's X (row-major) and gradient (element 4i+e: row
+  // wr + 8i + 4hh + e of the step, feature fb*32 + c32), read two steps ahead
+  // for X and one for the gradient; rows past the chunk read as zeros (RM 2)
+  // or as its last row. The gradient stays raw bits until it is used.
   u32x4 xv[XL];
-  auto load_x = [&](int64_t t0) {
+  uint32_t gn[16];
+  auto load_step = [&](const RowCursor& c, int64_t t0) __attribute__((always_inline)) {
+    if constexpr (RM == 2) {
+      constexpr uint32_t ES = GB ? 2 : 4;
+      const int64_t rho0 = (c.b * a.H + h) * a.n + c.i;
+      const uint32_t rows = static_cast<uint32_t>(r1 - t0 < RB ? r1 - t0 : RB);
+      const auto rx = make_rsrc(a.X + rho0 * D, rows * D * 2u);
 #pragma unroll
-    for (int it = 0; it < XL; ++it) {
-      const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
-      const int64_t r = t0 + rr < r1 ? t0 + rr : r1 - 1;
-      xv[it] = ld16(a.X + rho_of(r, h, a) * D + q * 8);
+      for (int it = 0; it < XL; ++it) xv[it] = buf_ld16(rx, (tid + 256u * it) * 16u, 0u);
+      const auto rg = make_rsrc(static_cast<const char*>(gsrc) + rho0 * a.m * ES,
+                                rows * static_cast<uint32_t>(a.m) * ES);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off =
+              ((wr + 8 * i + 4 * hh + e) * static_cast<uint32_t>(a.m) + fb * 32 + c32) * ES;
+          gn[4 * i + e] = GB ? buf_ld2(rg, off) : buf_ld4(rg, off);
+        }
+    } else {
+#pragma unroll
+      for (int it = 0; it < XL; ++it) {
+        const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
+        const int64_t o = t0 + rr < r1 ? rr : r1 - 1 - t0;
+        xv[it] = ld16(a.X + rho_near<RM == 1>(c, o, h, a) * D + q * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t r = wr + 8 * i + 4 * hh + e;
+          const int64_t o = t0 + r < r1 ? r : r1 - 1 - t0;
+          const int64_t idx = rho_near<RM == 1>(c, o, h, a) * a.m + fb * 32 + c32;
+          gn[4 * i + e] = GB ? static_cast<uint32_t>(static_cast<const uint16_t*>(gsrc)[idx])
+                             : __float_as_uint(static_cast<const float*>(gsrc)[idx]);
+        }
     }
   };
-  load_x(r0);
-  for (int64_t t0 = r0; t0 < r1; t0 += RB) {
-    __syncthreads();  // the previous step's X and exchange reads are done
+  auto store_x = [&](uint16_t* Xs, int64_t t0) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < XL; ++it) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
       st16(Xs + rr * XW + q * 8, t0 + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u});
     }
-    __syncthreads();
-    // upstream gradient: element 4i+e is row t0 + wr + 8i + 4hh + e, feature fb*32 + c32
+  };
+  auto widen = [&]() __attribute__((always_inline)) {
     f32x16 g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int k = 0; k < 16; ++k) g[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
+    return g;
+  };
+  // the cursor of the step whose rows are loaded next
+  RowCursor lc = cursor_at(r0, a);
+  int64_t lt = r0;
+  auto load_next = [&]() __attribute__((always_inline)) {
+    if (lt + RB < r1) {
+      lc = cursor_advance(lc, RB, a);
+      lt += RB;
+    }
+    load_step(lc, lt);
+  };
+
+  load_step(lc, lt);  // step 0
+  __syncthreads();    // every wave holds its Theta fragments: Ts may be overwritten
+  store_x(smem, r0);
+  f32x16 g = widen();
+  load_next();        // step 1
+  __syncthreads();
+  int buf = 0;
+  for (int64_t t0 = r0; t0 < r1; t0 += RB) {
+    uint16_t* Xs = smem + buf * (RB * XW);
+    // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..
+    // in P16 order) and B operands of the dTheta product (k = rows
+    // wr + 16hf.., column dt*32 + c32)
+    bf16x8 xa[KS], xb[2][DT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r = t0 + wr + 8 * i + 4 * hh + e;
-        const int64_t idx = rho_of(r < r1 ? r : r1 - 1, h, a) * a.m + fb * 32 + c32;
-        g[4 * i + e] = GB ? bf16_to_f32(static_cast<const uint16_t*>(a.dphi)[idx])
-                          : static_cast<const float*>(a.dphi)[idx];
-      }
-    load_x(t0 + RB < r1 ? t0 + RB : t0);  // next step's rows, in flight during this one
+    for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(Xs, XW, wr, ks * 16, lane);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) xb[hf][dt] = frag_tr(Xs, XW, wr + hf * 16, dt * 32, lane);
+    // the next step's rows go to the other buffer (last read before the
+    // previous barrier); the gradient of the next step is widened and the
+    // step after it requested
+    store_x(smem + (buf ^ 1) * (RB * XW), t0 + RB);
+    const f32x16 g_next = widen();
+    load_next();
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
     // Y_{j,rk} in the natural orientation: element 4i+e is row wr + 8i + 4hh + e
     // of the step, lane column c32 is feature fb*32 + c32
     f32x16 y[P];
 #pragma unroll
-    for (int j = 0; j < P; ++j) {
-      y[j] = zero16();
+    for (int j = 0; j < P; ++j) y[j] = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        y[j] = mfma32x32x16(frag_p16(Xs, XW, wr, ks * 16, lane),
-                            frag_tr(Ts, TW, ks * 16, (j * T + rk) * 32, lane), y[j]);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < P; ++j) y[j] = mfma32x32x16(xa[ks], tf[j][ks], y[j]);
     f32x16 ds = g;
-    if (a.square) {
+    if (own_s) {
       f32x16 s = y[0];
 #pragma unroll
       for (int j = 1; j < P; ++j) s *= y[j];
-      if constexpr (T == 4) {  // s = sum of the four waves' rank products
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          st16(exch + ((w * 4 + q) * 64 + lane) * 4,
-               u32x4{__float_as_uint(s[4 * q]), __float_as_uint(s[4 * q + 1]),
-                     __float_as_uint(s[4 * q + 2]), __float_as_uint(s[4 * q + 3])});
-        __syncthreads();
-        s = zero16();
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 u = ld16(exch + ((v * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * q + e] += __uint_as_float(u[e]);
-          }
-      }
       ds *= 2.f * s;
     }
+    if (t0 + RB > r1) {  // the chunk's last, partial step
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (t0 + wr + 8 * i + 4 * hh + e >= r1) ds[4 * i + e] = 0.f;
+        for (int e = 0; e < 4; ++e)
+          if (t0 + wr + 8 * i + 4 * hh + e >= r1) ds[4 * i + e] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < P; ++j) {
       f32x16 dy = ds;
@@ -345,10 +457,12 @@ void featmap_bwd_dth(BwdArgs a) {
       for (int hf = 0; hf < 2; ++hf) {
         const bf16x8 af = acc_frag(dy, hf);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[j][dt] = mfma32x32x16(af, frag_tr(Xs, XW, wr + hf * 16, dt * 32, lane), acc[j][dt]);
+        for (int dt = 0; dt < DT; ++dt) acc[j][dt] = mfma32x32x16(af, xb[hf][dt], acc[j][dt]);
       }
     }
+    g = g_next;
+    buf ^= 1;
+    __syncthreads();  // the next step's rows are in place; this step's are free
   }
   // partial dTheta^T tile: element 4i+e is feature fb*32 + 8i + 4hh + e, lane
   // column c32 is d = dt*32 + c32; layout [slot][H][p][t][m][d], one slot per
@@ -451,14 +565,26 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
   if (R > 0) {
     const int64_t tiles = (R + 127) / 128;
     if (tiles > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
-    auto* kx = featmap_bwd_dx<D, P, T, GB>;
+    // with t > 1 and a squared map the dX kernel also stores ds (bf16) for
+    // the dTheta kernel, which then reads it in place of dphi
+    const bool wds = T > 1 && s.square;
+    auto* kx = s.n >= 32 ? (wds ? featmap_bwd_dx<D, P, T, GB, true, true>
+                                : featmap_bwd_dx<D, P, T, GB, true, false>)
+                         : (wds ? featmap_bwd_dx<D, P, T, GB, false, true>
+                                : featmap_bwd_dx<D, P, T, GB, false, false>);
     hipError_t e = allow_lds(kx, G::theta_lds());
     if (e != hipSuccess) return e;
     LLOPS_LAUNCH("featmap_bwd_dx", st, kx,
                  dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H)), dim3(256),
                  G::theta_lds(), st, a);
-    const size_t lds = G::theta_lds() + G::x_lds() + G::exch_lds();
-    auto* kt = featmap_bwd_dth<D, P, T, GB>;
+    const size_t lds = std::max(G::theta_lds(), G::x_lds());
+    const int rm = s.n % G::RB == 0 ? 2 : s.n >= G::RB ? 1 : 0;
+    auto* kt = wds ? (rm == 2 ? featmap_bwd_dth<D, P, T, true, 2>
+                      : rm == 1 ? featmap_bwd_dth<D, P, T, true, 1>
+                                : featmap_bwd_dth<D, P, T, true, 0>)
+                   : (rm == 2 ? featmap_bwd_dth<D, P, T, GB, 2>
+                      : rm == 1 ? featmap_bwd_dth<D, P, T, GB, 1>
+                                : featmap_bwd_dth<D, P, T, GB, 0>);
     e = allow_lds(kt, lds);
     if (e != hipSuccess) return e;
     const int64_t wgs = static_cast<int64_t>(s.m / 32) * a.chunks * s.H;
@@ -481,14 +607,23 @@ hipError_t launch_bwd_g(const FeatShape& s, const BwdArgs& a, int dphi_bf16, flo
                    : launch_bwd_t<D, P, T, false>(s, a, dtheta, st);
 }
 
+bool featmap_bwd_supported_impl(const FeatShape& s) { return bwd_key(s) != 0; }
+
+// Scratch: the partial dTheta slots, then (t > 1, squared) ds in bf16.
+size_t bwd_part_bytes(const FeatShape& s) {
+  const BwdPlan p = bwd_plan(s);
+  const size_t b = static_cast<size_t>(p.slots) * s.H * s.p * s.t * s.m * s.d * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace
 
-bool featmap_bwd_supported(const FeatShape& s) { return bwd_key(s) != 0; }
+bool featmap_bwd_supported(const FeatShape& s) { return featmap_bwd_supported_impl(s); }
 
 size_t featmap_bwd_ws_bytes(const FeatShape& s) {
   if (!bwd_key(s)) return 0;
-  const BwdPlan p = bwd_plan(s);
-  return static_cast<size_t>(p.slots) * s.H * s.p * s.t * s.m * s.d * sizeof(float);
+  const size_t ds = s.t > 1 && s.square ? static_cast<size_t>(s.B) * s.H * s.n * s.m * 2 : 0;
+  return bwd_part_bytes(s) + ds;
 }
 
 hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* theta,
@@ -501,6 +636,9 @@ hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* the
   a.dphi = dphi;
   a.dX = dX;
   a.part = static_cast<float*>(ws);
+  a.ds = s.t > 1 && s.square && ws
+             ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + bwd_part_bytes(s))
+             : nullptr;
   a.B = s.B;
   a.H = s.H;
   a.n = s.n;

@@ -273,7 +273,10 @@ def test_featmap_bwd_pointers_and_workspace(L):
     s = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4)
     need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP_BWD)
     slot = 4 * 2 * 4 * 256 * 128 * 4  # one fp32 partial dTheta for every head
-    assert need > 0 and need % slot == 0
+    ds = 1 * 4 * 4096 * 256 * 2       # t > 1 and squared: ds of every row in bf16
+    assert need > ds and (need - ds) % slot == 0
+    plain = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, square=0)
+    assert L.llops_workspace_bytes(ctypes.byref(plain), _lib.ENTRY_FEATMAP_BWD) == need - ds
     shared = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, theta_per_head=0)
     assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP_BWD) == need
     args = [FAKE] * 5
