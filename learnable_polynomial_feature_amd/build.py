@@ -30,9 +30,15 @@ COMMON = [
 ]
 
 
+# Per-source flags. The backward kernels hold MFMA accumulators and operands
+# together in more than 256 registers; with MFMA results in VGPRs the
+# allocator stops shuttling accumulators through AGPR copies every step.
+EXTRA = {"featmap_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[cmd.index("-c"):cmd.index("-c")] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -62,7 +62,10 @@ struct BwdGeom {
   static constexpr int XW = D + 16;        // staged X row stride: rows shift by 8 banks
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
-  static constexpr size_t x_lds() { return 2ull * RB * XW * 2; }  // double buffered
+  static constexpr int XP = D + 8;          // second copy of staged X (t = 4): rows shift by 4 banks
+  static constexpr size_t x_lds() {         // three row buffers
+    return 3ull * RB * (T == 4 ? XW + XP : XW) * 2;
+  }
   static_assert(PT % 2 == 0, "staged Theta rows need an even block count to stay conflict free");
   static_assert((PT * D * 4) % 256 == 0, "a Theta block splits evenly over the threads");
 };
@@ -288,8 +291,8 @@ void featmap_bwd_dth(BwdArgs a) {
   constexpr int XL = RB * (D / 8) / 256;    // 16-byte pieces of a step's X per thread
   static_assert(XL >= 1 && RB * (D / 8) % 256 == 0, "a step's rows split evenly over the threads");
   // LDS: the staged Theta block at the start; once each wave holds its
-  // rank's Theta fragments in registers, the same bytes hold two steps' rows
-  // of X (one being read, the next being written).
+  // rank's Theta fragments in registers, the same bytes hold three steps'
+  // rows of X.
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* Ts = smem;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,22 +332,34 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[j][dt] = zero16();
 
-  // One step's X (row-major) and gradient (element 4i+e: row
-  // wr + 8i + 4hh + e of the step, feature fb*32 + c32), read two steps ahead
-  // for X and one for the gradient; rows past the chunk read as zeros (RM 2)
-  // or as its last row. The gradient stays raw bits until it is used.
+  // A step's X (row-major), requested two steps ahead, and its gradient
+  // (element 4i+e: row wr + 8i + 4hh + e of the step, feature fb*32 + c32),
+  // requested one step ahead and kept as raw bits until the step widens it.
+  // Rows past the chunk read as zeros (RM 2) or as its last row.
   u32x4 xv[XL];
   uint32_t gn[16];
-  auto load_step = [&](const RowCursor& c, int64_t t0) __attribute__((always_inline)) {
-    if constexpr (RM == 2) {
-      constexpr uint32_t ES = GB ? 2 : 4;
-      const int64_t rho0 = (c.b * a.H + h) * a.n + c.i;
-      const uint32_t rows = static_cast<uint32_t>(r1 - t0 < RB ? r1 - t0 : RB);
-      const auto rx = make_rsrc(a.X + rho0 * D, rows * D * 2u);
+  constexpr uint32_t ES = GB ? 2 : 4;
+  auto step_rows = [&](int64_t t) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(r1 - t < RB ? r1 - t : RB);
+  };
+  auto load_x = [&](const RowCursor& c, int64_t t) __attribute__((always_inline)) {
+    if constexpr (RM == 2) {  // the step's rows are consecutive in memory
+      const auto rx = make_rsrc(a.X + ((c.b * a.H + h) * a.n + c.i) * D, step_rows(t) * D * 2u);
 #pragma unroll
       for (int it = 0; it < XL; ++it) xv[it] = buf_ld16(rx, (tid + 256u * it) * 16u, 0u);
-      const auto rg = make_rsrc(static_cast<const char*>(gsrc) + rho0 * a.m * ES,
-                                rows * static_cast<uint32_t>(a.m) * ES);
+    } else {
+#pragma unroll
+      for (int it = 0; it < XL; ++it) {
+        const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
+        const int64_t o = t + rr < r1 ? rr : r1 - 1 - t;
+        xv[it] = ld16(a.X + rho_near<RM == 1>(c, o, h, a) * D + q * 8);
+      }
+    }
+  };
+  auto load_g = [&](const RowCursor& c, int64_t t) __attribute__((always_inline)) {
+    if constexpr (RM == 2) {
+      const auto rg = make_rsrc(static_cast<const char*>(gsrc) + ((c.b * a.H + h) * a.n + c.i) * a.m * ES,
+                                step_rows(t) * static_cast<uint32_t>(a.m) * ES);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -355,72 +370,82 @@ void featmap_bwd_dth(BwdArgs a) {
         }
     } else {
 #pragma unroll
-      for (int it = 0; it < XL; ++it) {
-        const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
-        const int64_t o = t0 + rr < r1 ? rr : r1 - 1 - t0;
-        xv[it] = ld16(a.X + rho_near<RM == 1>(c, o, h, a) * D + q * 8);
-      }
-#pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int64_t r = wr + 8 * i + 4 * hh + e;
-          const int64_t o = t0 + r < r1 ? r : r1 - 1 - t0;
+          const int64_t o = t + r < r1 ? r : r1 - 1 - t;
           const int64_t idx = rho_near<RM == 1>(c, o, h, a) * a.m + fb * 32 + c32;
           gn[4 * i + e] = GB ? static_cast<uint32_t>(static_cast<const uint16_t*>(gsrc)[idx])
                              : __float_as_uint(static_cast<const float*>(gsrc)[idx]);
         }
     }
   };
-  auto store_x = [&](uint16_t* Xs, int64_t t0) __attribute__((always_inline)) {
+  // LDS per row buffer: the rows with stride XW (read transposed, B operands
+  // of the dTheta product) and, for t = 4, again with stride XP (read as A
+  // operands of Y); each stride keeps its own read pattern free of bank
+  // conflicts. With t = 1 one copy serves both.
+  constexpr int XP = T == 4 ? G::XP : XW;
+  constexpr int BUFW = T == 4 ? RB * (XW + XP) : RB * XW;
+  auto xbuf = [&](int k) __attribute__((always_inline)) { return smem + k * BUFW; };
+  auto pbuf = [&](int k) __attribute__((always_inline)) {
+    return T == 4 ? smem + k * BUFW + RB * XW : smem + k * BUFW;
+  };
+  auto store_x = [&](int k, int64_t t) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < XL; ++it) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
-      st16(Xs + rr * XW + q * 8, t0 + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u});
+      const u32x4 v = t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
+      st16(xbuf(k) + rr * XW + q * 8, v);
+      if constexpr (T == 4) st16(pbuf(k) + rr * XP + q * 8, v);
     }
   };
   auto widen = [&]() __attribute__((always_inline)) {
-    f32x16 g;
+    f32x16 v;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) g[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
-    return g;
+    for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
+    return v;
   };
-  // the cursor of the step whose rows are loaded next
-  RowCursor lc = cursor_at(r0, a);
-  int64_t lt = r0;
-  auto load_next = [&]() __attribute__((always_inline)) {
-    if (lt + RB < r1) {
-      lc = cursor_advance(lc, RB, a);
-      lt += RB;
+  // the cursor of the last step whose X was requested (it stays on the
+  // chunk's last step once there)
+  RowCursor cx = cursor_at(r0, a);
+  int64_t tx = r0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (tx + RB < r1) {
+      cx = cursor_advance(cx, RB, a);
+      tx += RB;
     }
-    load_step(lc, lt);
   };
 
-  load_step(lc, lt);  // step 0
-  __syncthreads();    // every wave holds its Theta fragments: Ts may be overwritten
-  store_x(smem, r0);
+  // Three row buffers in rotation: step i reads buffer i%3 (its Y and dTheta
+  // operands) and buffer (i+1)%3 (the next step's Y operands, read while
+  // this step's products run), and fills buffer (i+2)%3, which was last read
+  // before the previous barrier.
+  load_x(cx, tx);  // step 0
+  load_g(cx, tx);
+  __syncthreads();  // every wave holds its Theta fragments: Ts may be overwritten
+  store_x(0, r0);
   f32x16 g = widen();
-  load_next();        // step 1
+  advance();
+  load_x(cx, tx);  // step 1
+  store_x(1, r0 + RB);
+  load_g(cx, tx);
+  advance();
+  load_x(cx, tx);  // step 2
   __syncthreads();
-  int buf = 0;
-  for (int64_t t0 = r0; t0 < r1; t0 += RB) {
-    uint16_t* Xs = smem + buf * (RB * XW);
-    // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..
-    // in P16 order) and B operands of the dTheta product (k = rows
-    // wr + 16hf.., column dt*32 + c32)
-    bf16x8 xa[KS], xb[2][DT];
+  // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..
+  // in P16 order) and B operands of the dTheta product (k = rows wr + 16hf..,
+  // column dt*32 + c32)
+  bf16x8 xa[KS], xb[2][DT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(Xs, XW, wr, ks * 16, lane);
+  for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(pbuf(0), XP, wr, ks * 16, lane);
+  int cur = 0, nxt = 1, fut = 2;
+  for (int64_t t0 = r0; t0 < r1; t0 += RB) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) xb[hf][dt] = frag_tr(Xs, XW, wr + hf * 16, dt * 32, lane);
-    // the next step's rows go to the other buffer (last read before the
-    // previous barrier); the gradient of the next step is widened and the
-    // step after it requested
-    store_x(smem + (buf ^ 1) * (RB * XW), t0 + RB);
-    const f32x16 g_next = widen();
-    load_next();
+      for (int dt = 0; dt < DT; ++dt)
+        xb[hf][dt] = frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
     // Y_{j,rk} in the natural orientation: element 4i+e is row wr + 8i + 4hh + e
     // of the step, lane column c32 is feature fb*32 + c32
@@ -431,6 +456,10 @@ void featmap_bwd_dth(BwdArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int j = 0; j < P; ++j) y[j] = mfma32x32x16(xa[ks], tf[j][ks], y[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next step's Y operands, in flight during this step's products
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(pbuf(nxt), XP, wr, ks * 16, lane);
     f32x16 ds = g;
     if (own_s) {
       f32x16 s = y[0];
@@ -438,12 +467,12 @@ void featmap_bwd_dth(BwdArgs a) {
       for (int j = 1; j < P; ++j) s *= y[j];
       ds *= 2.f * s;
     }
-    if (t0 + RB > r1) {  // the chunk's last, partial step
+    if constexpr (RM != 2) {  // rows past the chunk (RM 2 steps are always whole)
+      const int64_t left = r1 - t0 - wr - 4 * hh;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (t0 + wr + 8 * i + 4 * hh + e >= r1) ds[4 * i + e] = 0.f;
+        for (int e = 0; e < 4; ++e) ds[4 * i + e] = 8 * i + e < left ? ds[4 * i + e] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < P; ++j) {
@@ -460,9 +489,19 @@ void featmap_bwd_dth(BwdArgs a) {
         for (int dt = 0; dt < DT; ++dt) acc[j][dt] = mfma32x32x16(af, xb[hf][dt], acc[j][dt]);
       }
     }
-    g = g_next;
-    buf ^= 1;
-    __syncthreads();  // the next step's rows are in place; this step's are free
+    __builtin_amdgcn_sched_barrier(0);
+    // rows two steps ahead into the free buffer; the next step's gradient is
+    // widened and the one after it requested; rows three steps ahead requested
+    store_x(fut, t0 + 2 * RB);
+    g = widen();
+    load_g(cx, tx);
+    advance();
+    load_x(cx, tx);
+    const int k = cur;
+    cur = nxt;
+    nxt = fut;
+    fut = k;
+    __syncthreads();  // the stored rows are visible; this step's buffer is free
   }
   // partial dTheta^T tile: element 4i+e is feature fb*32 + 8i + 4hh + e, lane
   // column c32 is d = dt*32 + c32; layout [slot][H][p][t][m][d], one slot per
