@@ -12,7 +12,7 @@
 // k-order (device.h), so recomputed tiles feed the next product from
 // registers.
 //
-// dX (featmap_bwd_dx): a workgroup owns 128 rows (32 per wave) of one head and
+// dX (featmap_bwd_dx): a workgroup owns 256 rows (32 per wave) of one head and
 // keeps their dX tile (rows x d) in registers. Per feature block it
 // recomputes s in the transposed orientation (features x rows), forms ds,
 // recomputes each rank's Y, and adds dY_{j,r} Theta_{j,r}^T: dY as the A
@@ -63,6 +63,8 @@ struct BwdGeom {
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
   static constexpr int XP = D + 8;          // second copy of staged X (t = 4): rows shift by 4 banks
+  static constexpr int TW2 = PT * 32 + 8;   // second copy of staged Theta (dX kernel): 4-bank shift
+  static constexpr size_t dx_lds() { return 1ull * D * (TW + TW2) * 2; }
   static constexpr size_t x_lds() {         // three row buffers
     return 3ull * RB * (T == 4 ? XW + XP : XW) * 2;
   }
@@ -70,22 +72,26 @@ struct BwdGeom {
   static_assert((PT * D * 4) % 256 == 0, "a Theta block splits evenly over the threads");
 };
 
-// Theta_{j,r}[k][fb*32 + c] -> Ts[k][(j*T + r)*32 + c]; all loads of a thread
-// are issued before its first LDS store.
-template <int D, int PT>
+// Theta_{j,r}[k][fb*32 + c] -> Ts[k][(j*T + r)*32 + c] (row stride TW) and,
+// when Ts2 is given, again into Ts2 with row stride TW2; NT threads, and all
+// loads of a thread are issued before its first LDS store.
+template <int D, int PT, int NT = 256>
 __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t* th, int m,
-                                            int fb, int tid) {
-  constexpr int TL = PT * D * 4 / 256;
+                                            int fb, int tid, uint16_t* Ts2 = nullptr,
+                                            int TW2 = 0) {
+  static_assert((PT * D * 4) % NT == 0, "a Theta block splits evenly over the threads");
+  constexpr int TL = PT * D * 4 / NT;
   u32x4 tv[TL];
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    const int idx = tid + 256 * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
+    const int idx = tid + NT * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
     tv[i] = ld16(th + (static_cast<int64_t>(jr) * D + k) * m + fb * 32 + q * 8);
   }
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    const int idx = tid + 256 * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
+    const int idx = tid + NT * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
     st16(Ts + k * TW + jr * 32 + q * 8, tv[i]);
+    if (Ts2) st16(Ts2 + k * TW2 + jr * 32 + q * 8, tv[i]);
   }
 }
 
@@ -134,18 +140,22 @@ __device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64
 // OW: n >= 32, so a wave's 32 rows cross at most one sequence boundary.
 // WDS: also store ds (squared map, t > 1) as bf16 for the dTheta kernel.
 template <int D, int P, int T, bool GB, bool OW, bool WDS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_bwd_dx(BwdArgs a) {
   using G = BwdGeom<D, P, T>;
-  constexpr int KS = G::KS, DT = G::DT, TW = G::TW, PT = G::PT;
+  constexpr int KS = G::KS, DT = G::DT, TW = G::TW, TW2 = G::TW2, PT = G::PT;
+  // Theta is staged twice: Ts (stride TW) serves the transposed reads of the
+  // Y recompute, Ts2 (stride TW2) the row reads of the dX product, each free
+  // of bank conflicts.
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* Ts = smem;
+  uint16_t* Ts2 = smem + D * TW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
   const int64_t h = blockIdx.y;
   const int64_t R = a.B * a.n;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 128 + w * 32;  // this wave's rows
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 256 + w * 32;  // this wave's rows
 
   // X fragments (B operand of the transposed recompute): lane row t0 + c32,
   // k = 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}; zeros past the end
@@ -210,7 +220,7 @@ void featmap_bwd_dx(BwdArgs a) {
       }
     }
     __syncthreads();  // every wave is done with the previous block's Theta
-    stage_theta<D, PT>(Ts, TW, th, a.m, fb, tid);
+    stage_theta<D, PT, 512>(Ts, TW, th, a.m, fb, tid, Ts2, TW2);
     __syncthreads();
     f32x16 ds = g;
     if (a.square) {
@@ -252,7 +262,7 @@ void featmap_bwd_dx(BwdArgs a) {
           const bf16x8 af = acc_frag(dy, hf);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-            dx[dt] = mfma32x32x16(af, frag_p16(Ts, TW, dt * 32, (j * T + r) * 32 + hf * 16, lane),
+            dx[dt] = mfma32x32x16(af, frag_p16(Ts2, TW2, dt * 32, (j * T + r) * 32 + hf * 16, lane),
                                   dx[dt]);
         }
       }
@@ -602,7 +612,7 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
   const int hpo = s.theta_per_head ? 1 : static_cast<int>(s.H);
   const int slots = T == 4 ? a.chunks : 4 * a.chunks;
   if (R > 0) {
-    const int64_t tiles = (R + 127) / 128;
+    const int64_t tiles = (R + 255) / 256;
     if (tiles > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
     // with t > 1 and a squared map the dX kernel also stores ds (bf16) for
     // the dTheta kernel, which then reads it in place of dphi
@@ -611,11 +621,11 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
                                 : featmap_bwd_dx<D, P, T, GB, true, false>)
                          : (wds ? featmap_bwd_dx<D, P, T, GB, false, true>
                                 : featmap_bwd_dx<D, P, T, GB, false, false>);
-    hipError_t e = allow_lds(kx, G::theta_lds());
+    hipError_t e = allow_lds(kx, G::dx_lds());
     if (e != hipSuccess) return e;
     LLOPS_LAUNCH("featmap_bwd_dx", st, kx,
-                 dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H)), dim3(256),
-                 G::theta_lds(), st, a);
+                 dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H)), dim3(512),
+                 G::dx_lds(), st, a);
     const size_t lds = std::max(G::theta_lds(), G::x_lds());
     const int rm = s.n % G::RB == 0 ? 2 : s.n >= G::RB ? 1 : 0;
     auto* kt = wds ? (rm == 2 ? featmap_bwd_dth<D, P, T, true, 2>
