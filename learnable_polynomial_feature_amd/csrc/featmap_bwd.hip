@@ -12,7 +12,7 @@
 // k-order (device.h), so recomputed tiles feed the next product from
 // registers.
 //
-// dX (featmap_bwd_dx): a workgroup owns 256 rows (32 per wave) of one head and
+// dX (featmap_bwd_dx): a workgroup owns 128 rows (32 per wave) of one head and
 // keeps their dX tile (rows x d) in registers. Per feature block it
 // recomputes s in the transposed orientation (features x rows), forms ds,
 // recomputes each rank's Y, and adds dY_{j,r} Theta_{j,r}^T: dY as the A
@@ -45,6 +45,7 @@ struct BwdArgs {
   float* dX;              // [B][H][n][d]
   float* part;            // dTheta partials [slot][H][p][t][m][d]
   uint16_t* ds;           // [B][H][n][m] bf16: ds of the squared map when t > 1 (else null)
+  uint16_t* ds_dump;      // 64 bytes written by lanes past the last row
   int64_t B, H, n;
   int m;
   int64_t th_hstride;     // Theta elements between heads (0 = shared)
@@ -63,7 +64,10 @@ struct BwdGeom {
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
   static constexpr int XP = D + 8;          // second copy of staged X (t = 4): rows shift by 4 banks
-  static constexpr int TW2 = PT * 32 + 8;   // second copy of staged Theta (dX kernel): 4-bank shift
+  // Second staged copy of Theta in the dX kernel, read as rows (frag_p16):
+  // consecutive rows shift by 8 bytes (2 banks), so the 16 rows one LDS
+  // cycle serves cover all 32 banks. Rows are then only 8-byte aligned.
+  static constexpr int TW2 = PT * 32 + 4;
   static constexpr size_t dx_lds() { return 1ull * D * (TW + TW2) * 2; }
   static constexpr size_t x_lds() {         // three row buffers
     return 3ull * RB * (T == 4 ? XW + XP : XW) * 2;
@@ -82,16 +86,21 @@ __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t
   static_assert((PT * D * 4) % NT == 0, "a Theta block splits evenly over the threads");
   constexpr int TL = PT * D * 4 / NT;
   u32x4 tv[TL];
+  // piece idx: 16 bytes of staged row k = idx / (4 PT) at column
+  // 8 * (idx % (4 PT)); consecutive lanes fill a row
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    const int idx = tid + NT * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
-    tv[i] = ld16(th + (static_cast<int64_t>(jr) * D + k) * m + fb * 32 + q * 8);
+    const int idx = tid + NT * i, k = idx / (4 * PT), pc = idx % (4 * PT);
+    tv[i] = ld16(th + (static_cast<int64_t>(pc >> 2) * D + k) * m + fb * 32 + (pc & 3) * 8);
   }
 #pragma unroll
   for (int i = 0; i < TL; ++i) {
-    const int idx = tid + NT * i, q = idx & 3, k = (idx >> 2) % D, jr = (idx >> 2) / D;
-    st16(Ts + k * TW + jr * 32 + q * 8, tv[i]);
-    if (Ts2) st16(Ts2 + k * TW2 + jr * 32 + q * 8, tv[i]);
+    const int idx = tid + NT * i, k = idx / (4 * PT), pc = idx % (4 * PT);
+    st16(Ts + k * TW + pc * 8, tv[i]);
+    if (Ts2) {  // rows of the second copy are 8-byte aligned
+      *reinterpret_cast<u32x2*>(Ts2 + k * TW2 + pc * 8) = u32x2{tv[i][0], tv[i][1]};
+      *reinterpret_cast<u32x2*>(Ts2 + k * TW2 + pc * 8 + 4) = u32x2{tv[i][2], tv[i][3]};
+    }
   }
 }
 
@@ -138,15 +147,17 @@ __device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64
 // ---------------------------------------------------------------------------
 // GB: dphi is bf16 (else fp32).
 // OW: n >= 32, so a wave's 32 rows cross at most one sequence boundary.
-// WDS: also store ds (squared map, t > 1) as bf16 for the dTheta kernel.
-template <int D, int P, int T, bool GB, bool OW, bool WDS>
+// SQ: the map is squared; with t > 1 the kernel then also stores ds (bf16)
+// for the dTheta kernel.
+template <int D, int P, int T, bool GB, bool OW, bool SQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_bwd_dx(BwdArgs a) {
   using G = BwdGeom<D, P, T>;
   constexpr int KS = G::KS, DT = G::DT, TW = G::TW, TW2 = G::TW2, PT = G::PT;
-  // Theta is staged twice: Ts (stride TW) serves the transposed reads of the
-  // Y recompute, Ts2 (stride TW2) the row reads of the dX product, each free
-  // of bank conflicts.
+  constexpr bool WDS = SQ && T > 1;
+  // The Theta block is staged twice: Ts (stride TW) for the transposing
+  // reads of the Y recompute, Ts2 (stride TW2) for the row reads of the dX
+  // product; each stride keeps its read pattern free of bank conflicts.
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* Ts = smem;
   uint16_t* Ts2 = smem + D * TW;
@@ -179,93 +190,137 @@ void featmap_bwd_dx(BwdArgs a) {
   }
   const uint16_t* th = a.theta + h * a.th_hstride;
 
-  // Y_{j,r} of the staged feature block, transposed: element 4i+e is
-  // feature 8i + 4hh + e of row t0 + c32
-  auto y_of = [&](int j, int r) __attribute__((always_inline)) {
-    f32x16 acc = zero16();
+  // upstream gradient of this lane's row, features fb*32 + 8i + 4hh + {0..3},
+  // as raw bits until ds is formed
+  u32x4 gr[GB ? 2 : 4];
+  auto load_g = [&](int fb) __attribute__((always_inline)) {
+    const int64_t base = rho * a.m + fb * 32 + 4 * hh;
+    if constexpr (GB) {
+      const uint16_t* src = static_cast<const uint16_t*>(a.dphi) + base;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = mfma32x32x16(frag_tr(Ts, TW, ks * 16, (j * T + r) * 32, lane), xf[ks], acc);
-    return acc;
+      for (int i = 0; i < 2; ++i) {
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(src + 16 * i);
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(src + 16 * i + 8);
+        gr[i] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      }
+    } else {
+      const float* src = static_cast<const float*>(a.dphi) + base;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gr[i] = ld16(src + 8 * i);
+    }
   };
+  auto g_at = [&](int i, int e) __attribute__((always_inline)) {
+    if constexpr (GB) {
+      const uint32_t u = gr[i / 2][2 * (i % 2) + e / 2];
+      return __uint_as_float(e & 1 ? u & 0xffff0000u : u << 16);
+    } else {
+      return __uint_as_float(gr[i][e]);
+    }
+  };
+  // (j, r) of the q-th rank product, r-major
+  auto jr_of = [](int q) { return (q % P) * T + q / P; };
 
   f32x16 dx[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dx[dt] = zero16();
   const int FB = a.m / 32;
   for (int fb = 0; fb < FB; ++fb) {
-    // upstream gradient of this lane's row, features fb*32 + 8i + 4hh + {0..3}
-    f32x16 g;
-    {
-      const int64_t base = rho * a.m + fb * 32 + 4 * hh;
-      if constexpr (GB) {
-        u32x2 gv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          gv[i] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.dphi) + base + 8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            g[4 * i + e] = __uint_as_float(e & 1 ? gv[i][e >> 1] & 0xffff0000u : gv[i][e >> 1] << 16);
-      } else {
-        f32x4 gv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          gv[i] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dphi) + base + 8 * i);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) g[4 * i + e] = gv[i][e];
-      }
-    }
+    load_g(fb);
     __syncthreads();  // every wave is done with the previous block's Theta
     stage_theta<D, PT, 512>(Ts, TW, th, a.m, fb, tid, Ts2, TW2);
     __syncthreads();
-    f32x16 ds = g;
-    if (a.square) {
-      f32x16 s = zero16();
-#pragma unroll 1
-      for (int r = 0; r < T; ++r) {
-        f32x16 prod = y_of(0, r);
+
+    // Pass 1, rank by rank: Y_{j,r} transposed (element 4i+e is feature
+    // 8i + 4hh + e of row t0 + c32), its P chains interleaved over k, kept as
+    // bf16 pairs; s for a squared map. Theta fragments are read two MFMAs
+    // ahead.
+    constexpr int NA = PT * KS;
+    auto read_a = [&](int idx) __attribute__((always_inline)) {
+      // idx = (r*KS + ks)*P + j
+      const int j = idx % P, ks = (idx / P) % KS, r = idx / (P * KS);
+      return frag_tr(Ts, TW, ks * 16, (j * T + r) * 32, lane);
+    };
+    uint32_t yb[PT][8];
+    f32x16 s = zero16();
+    f32x16 yv[P];
+    bf16x8 fr[3];
+    fr[0] = read_a(0);
+    fr[1] = read_a(1);
 #pragma unroll
-        for (int j = 1; j < P; ++j) prod *= y_of(j, r);
+    for (int r = 0; r < T; ++r) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const int idx = (r * KS + ks) * P + j;
+          if (idx + 2 < NA) fr[(idx + 2) % 3] = read_a(idx + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          yv[j] = mfma32x32x16(fr[idx % 3], xf[ks], ks == 0 ? zero16() : yv[j]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      if constexpr (SQ) {
+        f32x16 prod = yv[0];
+#pragma unroll
+        for (int jj = 1; jj < P; ++jj) prod *= yv[jj];
         s += prod;
       }
-      ds *= 2.f * s;
-    }
-    if (!ok) ds = zero16();
-    if constexpr (WDS) {
-      if (ok) {
-        uint16_t* dst = a.ds + rho * a.m + fb * 32 + 4 * hh;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<u32x2*>(dst + 8 * i) =
-              u32x2{pack_bf16x2(ds[4 * i], ds[4 * i + 1]), pack_bf16x2(ds[4 * i + 2], ds[4 * i + 3])};
+      for (int jj = 0; jj < P; ++jj)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          yb[jj * T + r][k] = pack_bf16x2(yv[jj][2 * k], yv[jj][2 * k + 1]);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gv = g_at(i, e);
+        ds[4 * i + e] = ok ? (SQ ? 2.f * s[4 * i + e] * gv : gv) : 0.f;
       }
+    if constexpr (WDS) {
+      uint16_t* dst = ok ? a.ds + rho * a.m + fb * 32 + 4 * hh : a.ds_dump + 16 * hh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x2*>(dst + 8 * i) =
+            u32x2{pack_bf16x2(ds[4 * i], ds[4 * i + 1]), pack_bf16x2(ds[4 * i + 2], ds[4 * i + 3])};
     }
-#pragma unroll 1
-    for (int r = 0; r < T; ++r) {
-      f32x16 y[P];
+    // Pass 2, over (r, j): dY_{j,r} = ds * prod_{j' != j} Y_{j',r} in
+    // registers, then dX[rows][d] += dY[rows][f] Theta^T[f][d]: dY as the A
+    // operand (lane row, k = features in P16 order), Theta^T read as rows of
+    // the staged block, two MFMAs ahead.
+    constexpr int NB = PT * 2 * DT;
+    auto read_b = [&](int idx) __attribute__((always_inline)) {
+      const int q = idx / (2 * DT), hf = (idx / DT) % 2, dt = idx % DT;
+      return frag_p16(Ts2, TW2, dt * 32, jr_of(q) * 32 + hf * 16, lane);
+    };
+    fr[0] = read_b(0);
+    fr[1] = read_b(1);
+    bf16x8 af[2];
 #pragma unroll
-      for (int j = 0; j < P; ++j) y[j] = y_of(j, r);
+    for (int q = 0; q < PT; ++q)
 #pragma unroll
-      for (int j = 0; j < P; ++j) {
+    for (int hd = 0; hd < 2 * DT; ++hd) {
+      const int idx = q * 2 * DT + hd, hf = hd / DT, dt = hd % DT, r = q / P, j = q % P;
+      if (idx + 2 < NB) fr[(idx + 2) % 3] = read_b(idx + 2);
+      if (hf == 0 && dt == 0) {
         f32x16 dy = ds;
 #pragma unroll
-        for (int jj = 0; jj < P; ++jj)
-          if (jj != j) dy *= y[jj];
-        // dX[rows][d] += dY[rows][f] Theta^T[f][d]: dY as the A operand (lane
-        // row, k = features in P16 order), Theta^T from the staged rows of d
+        for (int jj = 0; jj < P; ++jj) {
+          if (jj == j) continue;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const bf16x8 af = acc_frag(dy, hf);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            dx[dt] = mfma32x32x16(af, frag_p16(Ts2, TW2, dt * 32, (j * T + r) * 32 + hf * 16, lane),
-                                  dx[dt]);
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t u = yb[jj * T + r][k];
+            dy[2 * k] *= __uint_as_float(u << 16);
+            dy[2 * k + 1] *= __uint_as_float(u & 0xffff0000u);
+          }
         }
+        af[0] = acc_frag(dy, 0);
+        af[1] = acc_frag(dy, 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      dx[dt] = mfma32x32x16(af[hf], fr[idx % 3], dx[dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // dx[dt] element 4i+e: row t0 + 8i + 4hh + e, column dt*32 + c32
@@ -617,10 +672,10 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
     // with t > 1 and a squared map the dX kernel also stores ds (bf16) for
     // the dTheta kernel, which then reads it in place of dphi
     const bool wds = T > 1 && s.square;
-    auto* kx = s.n >= 32 ? (wds ? featmap_bwd_dx<D, P, T, GB, true, true>
-                                : featmap_bwd_dx<D, P, T, GB, true, false>)
-                         : (wds ? featmap_bwd_dx<D, P, T, GB, false, true>
-                                : featmap_bwd_dx<D, P, T, GB, false, false>);
+    auto* kx = s.n >= 32 ? (s.square ? featmap_bwd_dx<D, P, T, GB, true, true>
+                                     : featmap_bwd_dx<D, P, T, GB, true, false>)
+                         : (s.square ? featmap_bwd_dx<D, P, T, GB, false, true>
+                                     : featmap_bwd_dx<D, P, T, GB, false, false>);
     hipError_t e = allow_lds(kx, G::dx_lds());
     if (e != hipSuccess) return e;
     LLOPS_LAUNCH("featmap_bwd_dx", st, kx,
@@ -671,7 +726,9 @@ bool featmap_bwd_supported(const FeatShape& s) { return featmap_bwd_supported_im
 
 size_t featmap_bwd_ws_bytes(const FeatShape& s) {
   if (!bwd_key(s)) return 0;
-  const size_t ds = s.t > 1 && s.square ? static_cast<size_t>(s.B) * s.H * s.n * s.m * 2 : 0;
+  // ds, then 256 bytes that lanes past the last row write instead
+  const size_t rows = static_cast<size_t>(s.B) * s.H * s.n;
+  const size_t ds = s.t > 1 && s.square && rows > 0 ? rows * s.m * 2 + 256 : 0;
   return bwd_part_bytes(s) + ds;
 }
 
@@ -688,6 +745,7 @@ hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* the
   a.ds = s.t > 1 && s.square && ws
              ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + bwd_part_bytes(s))
              : nullptr;
+  a.ds_dump = a.ds ? a.ds + static_cast<size_t>(s.B) * s.H * s.n * s.m : nullptr;
   a.B = s.B;
   a.H = s.H;
   a.n = s.n;

@@ -273,7 +273,7 @@ def test_featmap_bwd_pointers_and_workspace(L):
     s = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4)
     need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP_BWD)
     slot = 4 * 2 * 4 * 256 * 128 * 4  # one fp32 partial dTheta for every head
-    ds = 1 * 4 * 4096 * 256 * 2       # t > 1 and squared: ds of every row in bf16
+    ds = 1 * 4 * 4096 * 256 * 2 + 256  # t > 1 and squared: ds of every row in bf16, and a 256-byte slot
     assert need > ds and (need - ds) % slot == 0
     plain = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, square=0)
     assert L.llops_workspace_bytes(ctypes.byref(plain), _lib.ENTRY_FEATMAP_BWD) == need - ds
