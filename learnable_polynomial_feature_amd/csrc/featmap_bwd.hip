@@ -63,7 +63,7 @@ struct BwdGeom {
   static constexpr int XW = D + 16;        // staged X row stride: rows shift by 8 banks
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
-  static constexpr int XP = D + 8;          // second copy of staged X (t = 4): rows shift by 4 banks
+  static constexpr int XP = D + 4;          // second copy of staged X (t = 4): rows shift by 2 banks
   // Second staged copy of Theta in the dX kernel, read as rows (frag_p16):
   // consecutive rows shift by 8 bytes (2 banks), so the 16 rows one LDS
   // cycle serves cover all 32 banks. Rows are then only 8-byte aligned.
@@ -462,7 +462,10 @@ void featmap_bwd_dth(BwdArgs a) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
       const u32x4 v = t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
       st16(xbuf(k) + rr * XW + q * 8, v);
-      if constexpr (T == 4) st16(pbuf(k) + rr * XP + q * 8, v);
+      if constexpr (T == 4) {  // rows of the second copy are 8-byte aligned
+        *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8) = u32x2{v[0], v[1]};
+        *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8 + 4) = u32x2{v[2], v[3]};
+      }
     }
   };
   auto widen = [&]() __attribute__((always_inline)) {
