@@ -240,6 +240,45 @@ def causal_chunked(Q, K, V, theta_q, theta_k, square=False, normalize=False,
     return out, S, z
 
 
+def causal_attn_bwd(Pq, Pk, V, G, normalize=False, delta=0.0):
+    """Gradients (dPq, dPk, dV) of L = sum(G * out) for the causal contraction
+    over given features, out = M V [/ (M 1 + delta)] with M = tril(Pq Pk^T).
+
+    The chain rule through the materialised form of causal_quadratic
+    ([LLoPS-arXiv] Sec. 1; the normalised form of [LowRank-blog] Performer
+    section with [SLAY-notes] key design 3's +delta):
+      normalised:  dnum = G / den,  dden = -sum_cols(G * out) / den
+      plain:       dnum = G,        dden = 0
+      dM = tril(dnum V^T + dden 1^T)
+      dPq = dM Pk,  dPk = dM^T Pq,  dV = M^T dnum.
+    """
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    M = np.tril(Pq @ Pk.T)
+    if normalize:
+        den = M.sum(axis=1) + delta
+        out = (M @ V) / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(Pq.shape[0])
+    dM = np.tril(dnum @ V.T + dden[:, None])
+    return dM @ Pk, dM.T @ Pq, M.T @ dnum
+
+
+def causal_bwd(Q, K, V, theta_q, theta_k, G, square=False, normalize=False, delta=0.0):
+    """Gradients (dQ, dK, dV, dTheta_q, dTheta_k) of L = sum(G * out) for
+    out = causal_quadratic(Q, K, V, theta_q, theta_k, ...): causal_attn_bwd
+    for the feature gradients, then featmap_bwd on each side (Theta is trained
+    end to end: [LLoPS-notes] training strategy; [LLoPS-arXiv] Sec. 3)."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    dPq, dPk, dV = causal_attn_bwd(Pq, Pk, V, G, normalize, delta)
+    dQ, dtq = featmap_bwd(Q, theta_q, dPq, square)
+    dK, dtk = featmap_bwd(K, theta_k, dPk, square)
+    return dQ, dK, dV, dtq, dtk
+
+
 def state_from_prefix(K, V, theta_k, square=False):
     """S = phi_K^T V and z = phi_K^T 1 over a prefix (the state a causal pass
     over these tokens leaves behind). [LLoPS-arXiv] Sec. 1 (constant state)."""
@@ -308,6 +347,29 @@ def featmap_bwd_bh(X, theta, dphi, square=False):
             else:
                 dth += gt
     return dX, dth
+
+
+def causal_bwd_bh(Q, K, V, theta_q, theta_k, G, **kw):
+    """causal_bwd over [B, H, n, .] tensors; a shared theta's gradient sums
+    over all heads. Returns (dQ, dK, dV, dTheta_q, dTheta_k)."""
+    theta_q, theta_k = np.asarray(theta_q), np.asarray(theta_k)
+    B, H = Q.shape[:2]
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    dtq, dtk = np.zeros(theta_q.shape), np.zeros(theta_k.shape)
+    for b in range(B):
+        for h in range(H):
+            gq, gk, gv, tq, tk = causal_bwd(Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
+                                            _theta_for(theta_k, h), G[b, h], **kw)
+            dQ[b, h], dK[b, h], dV[b, h] = gq, gk, gv
+            if theta_q.ndim == 5:
+                dtq[h] += tq
+            else:
+                dtq += tq
+            if theta_k.ndim == 5:
+                dtk[h] += tk
+            else:
+                dtk += tk
+    return dQ, dK, dV, dtq, dtk
 
 
 def linattn_bh(Q, K, V, theta_q, theta_k, **kw) -> np.ndarray:

@@ -379,3 +379,71 @@ def test_featmap_bwd_shared_theta_sums_heads():
     _, dth_shared = O.featmap_bwd_bh(X, th, G)
     _, dth_heads = O.featmap_bwd_bh(X, np.repeat(th[None], 3, axis=0), G)
     assert np.allclose(dth_shared, dth_heads.sum(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def _causal_loss(Q, K, V, tq, tk, G, square, normalize, delta):
+    return float(np.sum(G * O.causal_quadratic(Q, K, V, tq, tk, square=square,
+                                               normalize=normalize, delta=delta)))
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, False), (False, True),
+                                              (True, True)])
+def test_causal_bwd_matches_central_differences(square, normalize):
+    """Every entry of dQ, dK, dV, dTheta_q and dTheta_k against a central
+    difference of L = sum(G * out) through the materialised causal form, in
+    float64 (normalised runs use squared or positive features so the
+    denominator stays away from zero)."""
+    rng = np.random.default_rng(41)
+    n, d, dv, m, p, t = 6, 3, 2, 4, 2, 2
+    Q = rng.standard_normal((n, d)) * 0.8
+    K = rng.standard_normal((n, d)) * 0.8
+    V = rng.standard_normal((n, dv))
+    tq = rng.standard_normal((p, t, d, m)) * 0.6
+    tk = rng.standard_normal((p, t, d, m)) * 0.6
+    if normalize and not square:  # keep phi > 0: Theta and inputs of one sign
+        Q, K, tq, tk = np.abs(Q), np.abs(K), np.abs(tq), np.abs(tk)
+    G = rng.standard_normal((n, dv))
+    delta = 0.3 if normalize else 0.0
+    args = [Q, K, V, tq, tk]
+    grads = O.causal_bwd(*args, G, square=square, normalize=normalize, delta=delta)
+    eps = 1e-6
+    for which in range(5):
+        for idx in np.ndindex(args[which].shape):
+            ap = [a.copy() for a in args]
+            am = [a.copy() for a in args]
+            ap[which][idx] += eps
+            am[which][idx] -= eps
+            fd = (_causal_loss(*ap, G, square, normalize, delta)
+                  - _causal_loss(*am, G, square, normalize, delta)) / (2 * eps)
+            got = grads[which][idx]
+            assert abs(got - fd) <= 2e-6 * max(1.0, abs(fd)), (which, idx, got, fd)
+
+
+def test_causal_attn_bwd_first_token_and_last_value():
+    """Closed forms at the ends of the sequence: the first query sees only
+    the first key, so dPq[0] = (G[0].V[0]) Pk[0] without a normaliser; the
+    last value is reached only by the last query, so dV[-1] = (Pq[-1].Pk[-1]) G[-1]."""
+    rng = np.random.default_rng(42)
+    n, m, dv = 7, 5, 3
+    Pq, Pk = rng.standard_normal((n, m)), rng.standard_normal((n, m))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    dPq, dPk, dV = O.causal_attn_bwd(Pq, Pk, V, G)
+    assert np.allclose(dPq[0], (G[0] @ V[0]) * Pk[0], rtol=1e-13, atol=1e-13)
+    assert np.allclose(dV[-1], (Pq[-1] @ Pk[-1]) * G[-1], rtol=1e-13, atol=1e-13)
+    assert np.allclose(dPk[-1], (G[-1] @ V[-1]) * Pq[-1], rtol=1e-13, atol=1e-13)
+
+
+def test_causal_bwd_shared_theta_sums_heads():
+    """causal_bwd_bh with a shared Theta returns the head sum of the per-head
+    gradients of the same Theta copied to every head."""
+    rng = np.random.default_rng(43)
+    B, H, n, d, dv, m = 1, 3, 5, 3, 2, 4
+    Q, K = rng.standard_normal((B, H, n, d)), rng.standard_normal((B, H, n, d))
+    V, G = rng.standard_normal((B, H, n, dv)), rng.standard_normal((B, H, n, dv))
+    tq, tk = rng.standard_normal((2, 1, d, m)), rng.standard_normal((2, 1, d, m))
+    shared = O.causal_bwd_bh(Q, K, V, tq, tk, G, square=True)
+    per = O.causal_bwd_bh(Q, K, V, np.stack([tq] * H), np.stack([tk] * H), G, square=True)
+    for a, b in zip(shared[:3], per[:3]):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+    assert np.allclose(shared[3], per[3].sum(0), rtol=1e-12, atol=1e-12)
+    assert np.allclose(shared[4], per[4].sum(0), rtol=1e-12, atol=1e-12)
