@@ -69,7 +69,8 @@ typedef enum {
   LLOPS_ENTRY_LINATTN = 1,
   LLOPS_ENTRY_CAUSAL = 2,
   LLOPS_ENTRY_DECODE = 3,
-  LLOPS_ENTRY_FEATMAP_BWD = 4
+  LLOPS_ENTRY_FEATMAP_BWD = 4,
+  LLOPS_ENTRY_CAUSAL_BWD = 5
 } llops_entry_t;
 
 typedef struct llops_shape {
@@ -161,6 +162,32 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* 
                                         void* out, float* S_final, float* z_final,
                                         void* ws, size_t ws_bytes,
                                         hipStream_t stream);
+
+/*
+ * llops_linattn_causal_bwd -- gradients of L = sum(dO * out) for
+ * out = llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k) started from a
+ * zero state: dQ, dK [batch][heads][n][d], dV [batch][heads][n][dv] and
+ * dtheta_q, dtheta_k in Theta's layout (summed over heads when shared), all
+ * fp32 and overwritten. dO is fp32 [batch][heads][n][dv] (out_dtype F32).
+ * With M = tril(phi_Q phi_K^T), num = M V and den = M 1 + delta:
+ *   dnum = dO / den, dden = -sum_v(dO * out) / den   (normalize = 0: dnum = dO, dden = 0)
+ *   dM = tril(dnum V^T + dden 1^T), dphi_Q = dM phi_K, dphi_K = dM^T phi_Q, dV = M^T dnum,
+ * then llops_featmap_bwd on each side (paper Sec. 1 attention form; blog,
+ * Performer section, and SLAY notes key design 3 for the normaliser; Theta is
+ * learned end to end, notes' training strategy). The three sums are run as
+ * causal linear attentions over bf16 features (dphi_K and dV over the
+ * reversed sequence), so they carry the forward's bf16 rounding.
+ * in_dtype BF16 only; kernels exist for p = 2, t in {1, 4}, d in {64, 128},
+ * m in {64, 128, 256}, dv % 16 == 0 and dv <= 128 (else LLOPS_ERR_UNSUPPORTED).
+ * theta_q and theta_k may alias; their gradients are still returned apart.
+ * chunk is ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_CAUSAL_BWD).
+ */
+llops_status_t llops_linattn_causal_bwd(const llops_shape_t* shape, const void* Q,
+                                        const void* K, const void* V,
+                                        const void* theta_q, const void* theta_k,
+                                        const float* dO, float* dQ, float* dK, float* dV,
+                                        float* dtheta_q, float* dtheta_k,
+                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * llops_decode_step -- one new token per (batch, head) on the recurrent state:

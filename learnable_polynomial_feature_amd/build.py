@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libllops.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["featmap.hip", "featmap_bwd.hip", "attn.hip", "attn32.hip", "decode.hip", "abi.cpp"]
+SOURCES = ["featmap.hip", "featmap_bwd.hip", "attn.hip", "attn32.hip", "attn_bwd.hip", "decode.hip",
+           "abi.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,143 @@
+// Element-wise and row-copy kernels of the causal linear-attention backward.
+//
+// For out = M V [/ (M 1 + delta)], M = tril(phi_Q phi_K^T), and an upstream
+// gradient G of out, the chain rule (LLoPS paper, Sec. 1 form of the
+// attention; the normalised numerator/denominator form of the Performer
+// section of the low-rank-attention post, with SLAY's +delta) gives
+//   dnum = G / den,  dden = -sum_v(G * out) / den      (plain: dnum = G, dden = 0)
+//   dM = tril(dnum V^T + dden 1^T)
+//   dphi_Q = dM phi_K,  dphi_K = dM^T phi_Q,  dV = M^T dnum.
+// Each of the three is itself a causal (or, in reversed token order, causal)
+// linear attention over features the library already contracts:
+//   dphi_Q_i = sum_{j<=i} (a_i . b_j) phi_K_j   with a = [dnum | dden | 0], b = [V | 1 | 0];
+//   dphi_K and dV are the same sums over i >= j, i.e. causal sums over the
+//   reversed sequence.
+// The host side (abi.cpp) runs them on the forward's segment kernels; the
+// kernels here build a and b, reverse or slice rows, and scatter results.
+#include "device.h"
+#include "kernels.h"
+
+namespace llops {
+namespace {
+
+// dst[bh][i'][doff + c] = src[bh][i][soff + c] for c < width, i' = n-1-i when
+// reversing (else i). Four elements per thread.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void rows_copy(const TI* __restrict__ src, int sw, int soff,
+                                                 TO* __restrict__ dst, int dw, int doff,
+                                                 int width, int64_t n, int64_t rows, int rev) {
+  const int q = width / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * q) return;
+  const int64_t r = idx / q;
+  const int c = static_cast<int>(idx - r * q) * 4;
+  const int64_t bh = r / n, i = r - bh * n;
+  const int64_t ro = rev ? bh * n + (n - 1 - i) : r;
+  const TI* s = src + r * sw + soff + c;
+  TO* d = dst + ro * dw + doff + c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (sizeof(TI) == 2 && sizeof(TO) == 2) {
+      d[e] = s[e];
+    } else {
+      d[e] = static_cast<TO>(s[e]);
+    }
+  }
+}
+
+// Column 0 of a [rows][16] bf16 block is 1, the rest 0: values whose causal
+// sum is the denominator M 1.
+__global__ __launch_bounds__(256) void fill_ones16(uint16_t* __restrict__ dst, int64_t rows) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * 16) return;
+  dst[idx] = (idx % 16) == 0 ? 0x3F80u : 0u;
+}
+
+// One wave per row: from num (fp32 [rows][dv]), the plain causal sums den1
+// (fp32 [rows][16], column 0 = M 1), the upstream gradient G (fp32) and V
+// (bf16), writes a = [dnum | dden | 0] and b = [V | 1 | 0] (bf16 [rows][MA])
+// in forward and reversed row order, and dnum (bf16 [rows][dv]) reversed.
+__global__ __launch_bounds__(64) void make_ab(const float* __restrict__ num,
+                                              const float* __restrict__ den1,
+                                              const float* __restrict__ G,
+                                              const uint16_t* __restrict__ V, int dv, int MA,
+                                              int64_t n, int normalize, float delta,
+                                              uint16_t* __restrict__ a, uint16_t* __restrict__ ra,
+                                              uint16_t* __restrict__ b, uint16_t* __restrict__ rb,
+                                              uint16_t* __restrict__ rdnum) {
+  const int64_t r = blockIdx.x;
+  const int64_t bh = r / n, i = r - bh * n;
+  const int64_t rr = bh * n + (n - 1 - i);
+  const int lane = threadIdx.x;
+  const float den = normalize ? den1[r * 16] + delta : 1.f;
+  const float inv = 1.f / den;
+  // dden = -(G . out) / den with out = num / den
+  float dot = 0.f;
+  for (int c = lane; c < dv; c += 64) dot += G[r * dv + c] * (num[r * dv + c] * inv);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+  const float dden = normalize ? -dot * inv : 0.f;
+  for (int c = lane; c < MA; c += 64) {
+    uint16_t av, bv;
+    if (c < dv) {
+      av = f32_to_bf16(G[r * dv + c] * inv);
+      bv = V[r * dv + c];
+      rdnum[rr * dv + c] = av;
+    } else if (c == dv) {
+      av = f32_to_bf16(dden);
+      bv = 0x3F80u;
+    } else {
+      av = 0u;
+      bv = 0u;
+    }
+    a[r * MA + c] = av;
+    ra[rr * MA + c] = av;
+    b[r * MA + c] = bv;
+    rb[rr * MA + c] = bv;
+  }
+}
+
+unsigned blocks_for(int64_t work, int per) {
+  return static_cast<unsigned>((work + per - 1) / per);
+}
+
+}  // namespace
+
+hipError_t launch_rows_copy_bf16(const uint16_t* src, int sw, int soff, uint16_t* dst, int dw,
+                                 int doff, int width, int64_t n, int64_t rows, int rev,
+                                 hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  LLOPS_LAUNCH("attn_bwd_rows", st, (rows_copy<uint16_t, uint16_t>),
+               dim3(blocks_for(rows * (width / 4), 256)), dim3(256), 0, st, src, sw, soff, dst, dw,
+               doff, width, n, rows, rev);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_copy_f32(const float* src, int sw, int soff, float* dst, int dw, int doff,
+                                int width, int64_t n, int64_t rows, int rev, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  LLOPS_LAUNCH("attn_bwd_rows", st, (rows_copy<float, float>),
+               dim3(blocks_for(rows * (width / 4), 256)), dim3(256), 0, st, src, sw, soff, dst, dw,
+               doff, width, n, rows, rev);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  LLOPS_LAUNCH("attn_bwd_ones", st, fill_ones16, dim3(blocks_for(rows * 16, 256)), dim3(256), 0,
+               st, dst, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
+                          int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
+                          uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
+                          hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>(rows)), dim3(64), 0,
+               st, num, den1, G, V, dv, MA, n, normalize, delta, a, ra, b, rb, rdnum);
+  return hipGetLastError();
+}
+
+}  // namespace llops

@@ -65,6 +65,20 @@ hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* the
                               const void* dphi, int dphi_bf16, float* dX, float* dtheta,
                               void* ws, hipStream_t st);
 
+// Causal-attention backward helpers (attn_bwd.hip). Rows are [rows][width]
+// blocks of per-(b, h) sequences of n rows; rev = 1 writes row i of each
+// sequence to row n-1-i.
+hipError_t launch_rows_copy_bf16(const uint16_t* src, int sw, int soff, uint16_t* dst, int dw,
+                                 int doff, int width, int64_t n, int64_t rows, int rev,
+                                 hipStream_t st);
+hipError_t launch_rows_copy_f32(const float* src, int sw, int soff, float* dst, int dw, int doff,
+                                int width, int64_t n, int64_t rows, int rev, hipStream_t st);
+hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st);
+hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
+                          int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
+                          uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
+                          hipStream_t st);
+
 // Linear-attention contraction over precomputed features.
 struct AttnShape {
   int64_t BH, n;

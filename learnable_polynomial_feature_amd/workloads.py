@@ -15,6 +15,7 @@ Distributions (the five workloads the hot path is measured on):
   V     ~ N(0,1) (the tiny fp32 case: N(0,1)/sqrt(d))
   Theta ~ N(0, 1/d), i.e. standard deviation 1/sqrt(d), one draw per head
   dphi  ~ N(0,1): the upstream gradient handed to the feature-map backward
+  dO    ~ N(0,1): the upstream gradient of the attention output (float32)
 Draws are float32; bf16 workloads round to bf16 with round-to-nearest-even and
 keep the rounded values in float32 arrays (exactly representable), so the GPU
 receives them losslessly and the oracle sees the identical numbers.
@@ -31,6 +32,7 @@ import numpy as np
 _T_Q, _T_K, _T_V, _T_THQ, _T_THK = 1, 2, 3, 4, 5
 _T_PRE_K, _T_PRE_V, _T_STEP_Q, _T_STEP_K, _T_STEP_V = 6, 7, 8, 9, 10
 _T_DPHI = 11
+_T_DOUT = 12
 
 
 @dataclasses.dataclass(frozen=True)
@@ -151,6 +153,23 @@ def dphi_slice(w: Workload, b: int, h: int, bf16: bool = False) -> np.ndarray:
     draws (rounded to bf16 values when ``bf16``)."""
     x = _normal(w.seed, _T_DPHI, (b, h), (w.n, w.m))
     return round_bf16(x) if bf16 else x
+
+
+def dout_slice(w: Workload, b: int, h: int) -> np.ndarray:
+    """One (b, h) slice [n, dv] of the attention output's upstream gradient."""
+    return _normal(w.seed, _T_DOUT, (b, h), (w.n, w.dv))
+
+
+def dout(w: Workload, heads: list[int] | None = None,
+         batches: list[int] | None = None) -> np.ndarray:
+    """dO [B', H', n, dv] float32 for the selected batch rows and heads."""
+    heads = list(range(w.heads)) if heads is None else list(heads)
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    G = np.empty((len(batches), len(heads), w.n, w.dv), np.float32)
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            G[bi, hi] = dout_slice(w, b, h)
+    return G
 
 
 def q_and_dphi(w: Workload, heads: list[int] | None = None,

@@ -266,6 +266,53 @@ def causal_attn_bwd(Pq, Pk, V, G, normalize=False, delta=0.0):
     return dM @ Pk, dM.T @ Pq, M.T @ dnum
 
 
+def causal_attn_bwd_chunked(Pq, Pk, V, G, normalize=False, delta=0.0, chunk=256):
+    """causal_attn_bwd without the n x n matrix, for long sequences: the same
+    sums split at chunk boundaries. Prefix states S = sum Pk^T V, z = sum Pk
+    of earlier chunks give num, den and dPq; suffix states R = sum Pq^T dnum,
+    r = sum Pq^T dden of later chunks give dPk and dV; inside a chunk the
+    masked products are explicit ([LowRank-blog] causal masking by running
+    sums, taken in both directions)."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    n, m = Pq.shape
+    dv = V.shape[1]
+    dnum = np.zeros((n, dv))
+    dden = np.zeros(n)
+    dPq = np.zeros((n, m))
+    S, z = np.zeros((m, dv)), np.zeros(m)
+    for c0 in range(0, n, chunk):
+        c1 = min(n, c0 + chunk)
+        q, k, v, g = Pq[c0:c1], Pk[c0:c1], V[c0:c1], G[c0:c1]
+        A = np.tril(q @ k.T)
+        num = A @ v + q @ S
+        if normalize:
+            den = A.sum(axis=1) + q @ z + delta
+            out = num / den[:, None]
+            dn = g / den[:, None]
+            dd = -(g * out).sum(axis=1) / den
+        else:
+            dn, dd = g, np.zeros(c1 - c0)
+        dnum[c0:c1], dden[c0:c1] = dn, dd
+        P = np.tril(dn @ v.T + dd[:, None])
+        dPq[c0:c1] = dn @ S.T + np.outer(dd, z) + P @ k
+        S = S + k.T @ v
+        z = z + k.sum(axis=0)
+    dPk = np.zeros((n, m))
+    dV = np.zeros((n, dv))
+    Rs, r = np.zeros((m, dv)), np.zeros(m)
+    for c0 in reversed(range(0, n, chunk)):
+        c1 = min(n, c0 + chunk)
+        q, k, v = Pq[c0:c1], Pk[c0:c1], V[c0:c1]
+        dn, dd = dnum[c0:c1], dden[c0:c1]
+        A = np.tril(q @ k.T)
+        P = np.tril(dn @ v.T + dd[:, None])
+        dPk[c0:c1] = v @ Rs.T + r[None, :] + P.T @ q
+        dV[c0:c1] = k @ Rs + A.T @ dn
+        Rs = Rs + q.T @ dn
+        r = r + q.T @ dd
+    return dPq, dPk, dV
+
+
 def causal_bwd(Q, K, V, theta_q, theta_k, G, square=False, normalize=False, delta=0.0):
     """Gradients (dQ, dK, dV, dTheta_q, dTheta_k) of L = sum(G * out) for
     out = causal_quadratic(Q, K, V, theta_q, theta_k, ...): causal_attn_bwd

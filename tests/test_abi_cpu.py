@@ -301,3 +301,41 @@ def test_featmap_bwd_pointers_and_workspace(L):
     t1 = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=1)
     need1 = L.llops_workspace_bytes(ctypes.byref(t1), _lib.ENTRY_FEATMAP_BWD)
     assert need1 > 0 and need1 % (4 * 4 * 2 * 1 * 256 * 128 * 4) == 0
+
+
+def _cbwd_shape(**kw):
+    base = dict(batch=1, heads=2, n=300, d=64, dv=64, m=64, p=2, t=4, square=1, normalize=1)
+    base.update(kw)
+    return _shape(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(p=0), 1), (dict(dv=0), 1), (dict(delta=-1.0), 1), (dict(n=-1), 1),
+    (dict(in_dtype=_lib.F32), 2), (dict(t=2), 2), (dict(p=3), 2), (dict(m=96), 2),
+    (dict(m=192), 2), (dict(d=96), 2), (dict(dv=144), 2), (dict(out_dtype=_lib.BF16), 2),
+])
+@fake_ptr
+def test_causal_bwd_validation(L, bad, code):
+    s = _cbwd_shape(**bad)
+    st = L.llops_linattn_causal_bwd(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None)
+    assert st == code, _err(L)
+    assert L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD) == 0
+
+
+@fake_ptr
+def test_causal_bwd_pointers_and_workspace(L):
+    s = _cbwd_shape(batch=2, heads=3, n=1000, d=128, dv=128, m=256)
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD)
+    R = 2 * 3 * 1000
+    # at least: phi_Q, phi_K (bf16), their fp32 gradients, a, b and reversed copies
+    assert need >= R * 256 * (2 + 2 + 4 + 4) + 4 * R * 192 * 2
+    plain = _cbwd_shape(batch=2, heads=3, n=1000, d=128, dv=128, m=256, normalize=0)
+    assert L.llops_workspace_bytes(ctypes.byref(plain), _lib.ENTRY_CAUSAL_BWD) < need
+    args = [FAKE] * 11
+    assert L.llops_linattn_causal_bwd(ctypes.byref(s), *args, FAKE, need - 1, None) == 3
+    names = ("Q", "K", "V", "theta_q", "theta_k", "dO", "dQ", "dK", "dV", "dtheta_q", "dtheta_k")
+    for i, name in enumerate(names):
+        a = list(args)
+        a[i] = None
+        assert L.llops_linattn_causal_bwd(ctypes.byref(s), *a, FAKE, need, None) == 1
+        assert f"{name} is null" in _err(L)

@@ -447,3 +447,19 @@ def test_causal_bwd_shared_theta_sums_heads():
         assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
     assert np.allclose(shared[3], per[3].sum(0), rtol=1e-12, atol=1e-12)
     assert np.allclose(shared[4], per[4].sum(0), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("normalize,chunk", [(False, 4), (True, 4), (True, 7), (False, 64)])
+def test_causal_attn_bwd_chunked_equals_materialised(normalize, chunk):
+    """The chunked backward (prefix and suffix states) equals the materialised
+    chain rule (itself pinned by central differences above), ragged chunks
+    included."""
+    rng = np.random.default_rng(44)
+    n, m, dv = 23, 6, 5
+    Pq = np.abs(rng.standard_normal((n, m)))
+    Pk = np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    want = O.causal_attn_bwd(Pq, Pk, V, G, normalize=normalize, delta=0.5)
+    got = O.causal_attn_bwd_chunked(Pq, Pk, V, G, normalize=normalize, delta=0.5, chunk=chunk)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
