@@ -87,10 +87,14 @@ size_t feat_attn_seg_bytes(const llops_shape_t* s, int M, int DV) {
          (static_cast<size_t>(M) * DV + M) * sizeof(float);
 }
 
-// a = [dnum | dden | 0] and b = [V | 1 | 0] are MA wide; the phi values are
-// contracted in pieces of W columns.
-int bwd_ma(const llops_shape_t* s) { return (s->dv + 1 + 63) / 64 * 64; }
-int bwd_w(const llops_shape_t* s) { return s->m < 128 ? s->m : 128; }
+// a = [dnum | dden | 0] and b = [V | 1 | 0] are MA wide and the phi values
+// are contracted in pieces of W columns, with (MA, W) one of the shapes the
+// 32x32x16 segment kernels take: (256, 128), (128, 64), (64, 64).
+int bwd_ma(const llops_shape_t* s) { return s->dv + 1 <= 64 ? 64 : s->dv + 1 <= 128 ? 128 : 256; }
+int bwd_w(const llops_shape_t* s) {
+  const int w = bwd_ma(s) == 256 ? 128 : 64;
+  return s->m < w ? s->m : w;
+}
 
 struct BwdWs {
   size_t phq, phk, pkq, pkk, num, den1, ones, a, ra, b, rb, rdnum, rphq, rphk, vp, tmp, dphq, dphk,
@@ -177,8 +181,8 @@ BwdWs bwd_ws(const llops_shape_t* s) {
   w.rphk = take(R * m * 2);
   w.vp = take(R * W * 2);
   w.tmp = take(R * (W > dv ? W : dv) * 4);
-  w.dphq = take(R * m * 4);
-  w.dphk = take(R * m * 4);
+  w.dphq = take(R * m * 2);
+  w.dphk = take(R * m * 2);
   size_t seg = feat_attn_seg_bytes(s, s->m, s->dv);
   const size_t seg2 = feat_attn_seg_bytes(s, static_cast<int>(MA), static_cast<int>(W));
   const size_t seg3 = feat_attn_seg_bytes(s, s->m, 16);
@@ -601,18 +605,18 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, c
             "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
-  float *dphq = f32(L.dphq), *dphk = f32(L.dphk);
+  uint16_t *dphq = u16(L.dphq), *dphk = u16(L.dphk);  // bf16, as the forward stores phi
   // dphi_Q_i = sum_{j<=i} (a_i . b_j) phi_K_j, W columns of phi_K at a time
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     LLOPS_HIP(causal_on_features(s, MA, W, a, b, vp, tmp, seg, st), "attn dphi_q");
-    LLOPS_HIP(llops::launch_rows_copy_f32(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
   }
   // dphi_K_j = sum_{i>=j} (a_i . b_j) phi_Q_i: causal over the reversed sequence
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
     LLOPS_HIP(causal_on_features(s, MA, W, rb, ra, vp, tmp, seg, st), "attn dphi_k");
-    LLOPS_HIP(llops::launch_rows_copy_f32(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
   }
   // dV_j = sum_{i>=j} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
   uint16_t *rphq = u16(L.rphq), *rphk = u16(L.rphk);
@@ -621,9 +625,9 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, c
   LLOPS_HIP(causal_on_features(s, m, dv, rphk, rphq, rdnum, tmp, seg, st), "attn dv");
   LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
   // through the feature maps
-  LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dphq, 0, dQ, dtheta_q, fb, st),
+  LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dphq, 1, dQ, dtheta_q, fb, st),
             "featmap_bwd q");
-  LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dphk, 0, dK, dtheta_k, fb, st),
+  LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dphk, 1, dK, dtheta_k, fb, st),
             "featmap_bwd k");
   return LLOPS_OK;
 }

@@ -21,27 +21,32 @@ namespace llops {
 namespace {
 
 // dst[bh][i'][doff + c] = src[bh][i][soff + c] for c < width, i' = n-1-i when
-// reversing (else i). Four elements per thread.
+// reversing (else i); fp32 -> bf16 rounds to nearest even. Eight elements per
+// thread; widths are multiples of 8, rows * width / 8 < 2^31.
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void rows_copy(const TI* __restrict__ src, int sw, int soff,
                                                  TO* __restrict__ dst, int dw, int doff,
-                                                 int width, int64_t n, int64_t rows, int rev) {
-  const int q = width / 4;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+                                                 int width, int n, int rows, int rev) {
+  const int q = width / 8;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= rows * q) return;
-  const int64_t r = idx / q;
-  const int c = static_cast<int>(idx - r * q) * 4;
-  const int64_t bh = r / n, i = r - bh * n;
-  const int64_t ro = rev ? bh * n + (n - 1 - i) : r;
-  const TI* s = src + r * sw + soff + c;
+  const int r = idx / q;
+  const int c = (idx - r * q) * 8;
+  const int bh = r / n, i = r - bh * n;
+  const int64_t ro = rev ? static_cast<int64_t>(bh) * n + (n - 1 - i) : r;
+  const TI* s = src + static_cast<int64_t>(r) * sw + soff + c;
   TO* d = dst + ro * dw + doff + c;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if constexpr (sizeof(TI) == 2 && sizeof(TO) == 2) {
-      d[e] = s[e];
-    } else {
-      d[e] = static_cast<TO>(s[e]);
-    }
+  if constexpr (sizeof(TI) == 2 && sizeof(TO) == 2) {
+    st16(d, ld16(s));
+  } else if constexpr (sizeof(TI) == 4 && sizeof(TO) == 4) {
+    st16(d, ld16(s));
+    st16(d + 4, ld16(s + 4));
+  } else {  // fp32 -> bf16
+    const u32x4 lo = ld16(s), hi = ld16(s + 4);
+    st16(d, u32x4{pack_bf16x2(__uint_as_float(lo[0]), __uint_as_float(lo[1])),
+                  pack_bf16x2(__uint_as_float(lo[2]), __uint_as_float(lo[3])),
+                  pack_bf16x2(__uint_as_float(hi[0]), __uint_as_float(hi[1])),
+                  pack_bf16x2(__uint_as_float(hi[2]), __uint_as_float(hi[3]))});
   }
 }
 
@@ -53,22 +58,23 @@ __global__ __launch_bounds__(256) void fill_ones16(uint16_t* __restrict__ dst, i
   dst[idx] = (idx % 16) == 0 ? 0x3F80u : 0u;
 }
 
-// One wave per row: from num (fp32 [rows][dv]), the plain causal sums den1
+// One wave per row (four rows per workgroup): from num (fp32 [rows][dv]), the plain causal sums den1
 // (fp32 [rows][16], column 0 = M 1), the upstream gradient G (fp32) and V
 // (bf16), writes a = [dnum | dden | 0] and b = [V | 1 | 0] (bf16 [rows][MA])
 // in forward and reversed row order, and dnum (bf16 [rows][dv]) reversed.
-__global__ __launch_bounds__(64) void make_ab(const float* __restrict__ num,
+__global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               const float* __restrict__ den1,
                                               const float* __restrict__ G,
                                               const uint16_t* __restrict__ V, int dv, int MA,
-                                              int64_t n, int normalize, float delta,
+                                              int64_t n, int64_t rows, int normalize, float delta,
                                               uint16_t* __restrict__ a, uint16_t* __restrict__ ra,
                                               uint16_t* __restrict__ b, uint16_t* __restrict__ rb,
                                               uint16_t* __restrict__ rdnum) {
-  const int64_t r = blockIdx.x;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
   const int64_t bh = r / n, i = r - bh * n;
   const int64_t rr = bh * n + (n - 1 - i);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const float den = normalize ? den1[r * 16] + delta : 1.f;
   const float inv = 1.f / den;
   // dden = -(G . out) / den with out = num / den
@@ -101,25 +107,34 @@ unsigned blocks_for(int64_t work, int per) {
   return static_cast<unsigned>((work + per - 1) / per);
 }
 
+template <typename TI, typename TO>
+hipError_t rows_copy_t(const TI* src, int sw, int soff, TO* dst, int dw, int doff, int width,
+                       int64_t n, int64_t rows, int rev, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if (width % 8 || rows * (width / 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_rows", st, (rows_copy<TI, TO>),
+               dim3(blocks_for(rows * (width / 8), 256)), dim3(256), 0, st, src, sw, soff, dst, dw,
+               doff, width, static_cast<int>(n), static_cast<int>(rows), rev);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_rows_copy_bf16(const uint16_t* src, int sw, int soff, uint16_t* dst, int dw,
                                  int doff, int width, int64_t n, int64_t rows, int rev,
                                  hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  LLOPS_LAUNCH("attn_bwd_rows", st, (rows_copy<uint16_t, uint16_t>),
-               dim3(blocks_for(rows * (width / 4), 256)), dim3(256), 0, st, src, sw, soff, dst, dw,
-               doff, width, n, rows, rev);
-  return hipGetLastError();
+  return rows_copy_t(src, sw, soff, dst, dw, doff, width, n, rows, rev, st);
 }
 
 hipError_t launch_rows_copy_f32(const float* src, int sw, int soff, float* dst, int dw, int doff,
                                 int width, int64_t n, int64_t rows, int rev, hipStream_t st) {
-  if (rows == 0) return hipSuccess;
-  LLOPS_LAUNCH("attn_bwd_rows", st, (rows_copy<float, float>),
-               dim3(blocks_for(rows * (width / 4), 256)), dim3(256), 0, st, src, sw, soff, dst, dw,
-               doff, width, n, rows, rev);
-  return hipGetLastError();
+  return rows_copy_t(src, sw, soff, dst, dw, doff, width, n, rows, rev, st);
+}
+
+hipError_t launch_rows_copy_f32_bf16(const float* src, int sw, int soff, uint16_t* dst, int dw,
+                                     int doff, int width, int64_t n, int64_t rows, int rev,
+                                     hipStream_t st) {
+  return rows_copy_t(src, sw, soff, dst, dw, doff, width, n, rows, rev, st);
 }
 
 hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st) {
@@ -134,9 +149,10 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
                           hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>(rows)), dim3(64), 0,
-               st, num, den1, G, V, dv, MA, n, normalize, delta, a, ra, b, rb, rdnum);
+  if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 3) / 4)),
+               dim3(256), 0, st, num, den1, G, V, dv, MA, n, rows, normalize, delta, a, ra, b, rb,
+               rdnum);
   return hipGetLastError();
 }
 

@@ -73,6 +73,9 @@ hipError_t launch_rows_copy_bf16(const uint16_t* src, int sw, int soff, uint16_t
                                  hipStream_t st);
 hipError_t launch_rows_copy_f32(const float* src, int sw, int soff, float* dst, int dw, int doff,
                                 int width, int64_t n, int64_t rows, int rev, hipStream_t st);
+hipError_t launch_rows_copy_f32_bf16(const float* src, int sw, int soff, uint16_t* dst, int dw,
+                                     int doff, int width, int64_t n, int64_t rows, int rev,
+                                     hipStream_t st);
 hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st);
 hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
