@@ -10,23 +10,27 @@
 // in LDS rows of d, in Theta's natural layout, and recompute Y on 32x32x16
 // MFMA from it: nothing of size n x p*t*m is stored. Operands are read in P16
 // k-order (device.h), so recomputed tiles feed the next product from
-// registers.
+// registers. Row strides of staged blocks are chosen per read pattern: the
+// transposing reads want rows 8 banks apart, the 8-byte row reads 2 banks
+// apart, so a block read both ways is staged twice.
 //
-// dX (featmap_bwd_dx): a workgroup owns 128 rows (32 per wave) of one head and
-// keeps their dX tile (rows x d) in registers. Per feature block it
-// recomputes s in the transposed orientation (features x rows), forms ds,
-// recomputes each rank's Y, and adds dY_{j,r} Theta_{j,r}^T: dY as the A
-// operand straight from its accumulator, Theta^T read from the staged rows.
+// dX (featmap_bwd_dx): a workgroup of 8 waves owns 256 rows (32 per wave) of
+// one head and keeps their dX tile (rows x d) in registers. Per feature block
+// it recomputes every Y_{j,r} once in the transposed orientation (features x
+// rows), forms s and ds, keeps the Y tiles as bf16 pairs, and adds
+// dY_{j,r} Theta_{j,r}^T: dY as the A operand straight from registers,
+// Theta^T read as rows of the second staged copy. With t > 1 and a squared
+// map it also stores ds for the dTheta kernel.
 //
 // dTheta (featmap_bwd_dth): a workgroup owns one feature block, one head and
 // one chunk of rows. Each wave keeps the Theta fragments of its rank in
 // registers for the whole chunk and walks the chunk a step of rows at a time
-// with the rows staged in LDS. Y is recomputed in the natural orientation
+// through three LDS row buffers. Y is recomputed in the natural orientation
 // (rows x features), so dY^T is an A operand from registers and X (read
 // transposed from LDS) the B operand. With t = 4 the four waves take one rank
-// each over the same 32 rows and swap their rank's product through LDS to
-// form s; with t = 1 each wave takes its own 32 of a 128-row step. The
-// workgroup writes its chunk's partial dTheta (one per wave for t = 1);
+// each over the same 32 rows and read ds from the dX kernel; with t = 1 each
+// wave takes its own 32 of a 128-row step and forms s itself. The workgroup
+// writes its chunk's partial dTheta (one per wave for t = 1);
 // featmap_bwd_reduce sums the partials (and the heads, for a shared Theta) in
 // a fixed order and transposes.
 #include <algorithm>
