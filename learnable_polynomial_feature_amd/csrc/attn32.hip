@@ -44,8 +44,8 @@ struct Seg32Geom {
   static constexpr int NT = NW * 64;       // threads
   static constexpr int FT = M / 32;        // feature tiles
   static constexpr int ZT = FT / NW > 0 ? FT / NW : 1;  // z tiles per wave
-  static constexpr int MP = M + 16;        // LDS row strides (elements): rows shift
-  static constexpr int VP = DV + 16;       //   by 8 banks, conflict-free tr reads
+  static constexpr int MP = M + 32;        // LDS row strides (elements): rows 64 bytes
+  static constexpr int VP = DV + 32;       //   apart mod 256, conflict-free tr reads
   static constexpr int BUF = kC * MP * 2 + kC * VP;  // one chunk: phi_Q, phi_K, V
   static constexpr int QCH = kC * M / 8, VCH = kC * DV / 8;  // 16-byte pieces per chunk
   static constexpr int LPT_Q = QCH / NT, LPT_V = VCH / NT;

@@ -559,7 +559,7 @@ struct SmallArgs {
 template <int D, int P, int T>
 struct SmallGeom {
   static constexpr int PT = P * T;
-  static constexpr int TW = PT * 32 + 16;  // Theta row stride (elements): rows shift by 8 banks
+  static constexpr int TW = PT * 32 + 32;  // Theta row stride (elements): rows 64 bytes apart mod 256
   static constexpr size_t lds_bytes() { return 1ull * D * TW * 2; }
 };
 

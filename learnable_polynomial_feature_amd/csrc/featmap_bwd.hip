@@ -63,14 +63,17 @@ struct BwdGeom {
   static constexpr int PT = P * T;
   static constexpr int KS = D / 16;        // 16-deep k-steps over d
   static constexpr int DT = D / 32;        // 32-wide tiles of d
-  static constexpr int TW = PT * 32 + 16;  // staged Theta row stride: rows shift by 8 banks
-  static constexpr int XW = D + 16;        // staged X row stride: rows shift by 8 banks
+  // Row strides of staged blocks (elements). Transposing reads (4 rows x
+  // 32 bytes per 16 lanes) are conflict free when rows sit 64 bytes apart
+  // modulo 256 (measured: a 32-byte shift takes twice the LDS cycles);
+  // 8-byte row reads (frag_p16) when rows sit 8 bytes apart modulo 256.
+  static constexpr int TW = PT * 32 + 32;  // staged Theta, read transposed
+  static constexpr int XW = D + 32;        // staged X, read transposed
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
-  static constexpr int XP = D + 4;          // second copy of staged X (t = 4): rows shift by 2 banks
+  static constexpr int XP = D + 4;          // second copy of staged X (t = 4), read as rows
   // Second staged copy of Theta in the dX kernel, read as rows (frag_p16):
-  // consecutive rows shift by 8 bytes (2 banks), so the 16 rows one LDS
-  // cycle serves cover all 32 banks. Rows are then only 8-byte aligned.
+  // consecutive rows shift by 8 bytes. Rows are then only 8-byte aligned.
   static constexpr int TW2 = PT * 32 + 4;
   static constexpr size_t dx_lds() { return 1ull * D * (TW + TW2) * 2; }
   static constexpr size_t x_lds() {         // three row buffers
