@@ -58,10 +58,12 @@ __global__ __launch_bounds__(256) void fill_ones16(uint16_t* __restrict__ dst, i
   dst[idx] = (idx % 16) == 0 ? 0x3F80u : 0u;
 }
 
-// One wave per row (four rows per workgroup): from num (fp32 [rows][dv]), the plain causal sums den1
-// (fp32 [rows][16], column 0 = M 1), the upstream gradient G (fp32) and V
-// (bf16), writes a = [dnum | dden | 0] and b = [V | 1 | 0] (bf16 [rows][MA])
-// in forward and reversed row order, and dnum (bf16 [rows][dv]) reversed.
+// 32 lanes per row, eight rows per workgroup: from num (fp32 [rows][dv]),
+// the plain causal sums den1 (fp32 [rows][16], column 0 = M 1), the upstream
+// gradient G (fp32) and V (bf16), writes a = [dnum | dden | 0] and
+// b = [V | 1 | 0] (bf16 [rows][MA]) in forward and reversed row order, and
+// dnum (bf16 [rows][dv]) reversed. A lane owns 8 consecutive columns and
+// writes them as one 16-byte store; dv and MA are multiples of 8, MA <= 256.
 __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               const float* __restrict__ den1,
                                               const float* __restrict__ G,
@@ -70,37 +72,47 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               uint16_t* __restrict__ a, uint16_t* __restrict__ ra,
                                               uint16_t* __restrict__ b, uint16_t* __restrict__ rb,
                                               uint16_t* __restrict__ rdnum) {
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int64_t bh = r / n, i = r - bh * n;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  const bool live = r < rows;  // every lane joins the shuffles below
+  const int64_t rc = live ? r : rows - 1;
+  const int64_t bh = rc / n, i = rc - bh * n;
   const int64_t rr = bh * n + (n - 1 - i);
-  const int lane = threadIdx.x & 63;
-  const float den = normalize ? den1[r * 16] + delta : 1.f;
+  const float den = normalize ? den1[rc * 16] + delta : 1.f;
   const float inv = 1.f / den;
-  // dden = -(G . out) / den with out = num / den
+  const int c0 = 8 * l;  // this lane's columns c0 .. c0+7
+  float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float dot = 0.f;
-  for (int c = lane; c < dv; c += 64) dot += G[r * dv + c] * (num[r * dv + c] * inv);
+  if (c0 < dv) {
+    const u32x4 g0 = ld16(G + rc * dv + c0), g1 = ld16(G + rc * dv + c0 + 4);
+    const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-  const float dden = normalize ? -dot * inv : 0.f;
-  for (int c = lane; c < MA; c += 64) {
-    uint16_t av, bv;
-    if (c < dv) {
-      av = f32_to_bf16(G[r * dv + c] * inv);
-      bv = V[r * dv + c];
-      rdnum[rr * dv + c] = av;
-    } else if (c == dv) {
-      av = f32_to_bf16(dden);
-      bv = 0x3F80u;
-    } else {
-      av = 0u;
-      bv = 0u;
+    for (int e = 0; e < 4; ++e) {
+      g[e] = __uint_as_float(g0[e]);
+      g[4 + e] = __uint_as_float(g1[e]);
+      dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
     }
-    a[r * MA + c] = av;
-    ra[rr * MA + c] = av;
-    b[r * MA + c] = bv;
-    rb[rr * MA + c] = bv;
   }
+  // dden = -(G . out) / den with out = num / den (sum over the row's 32 lanes)
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+  const float dden = normalize ? -dot * inv : 0.f;
+  if (!live || c0 >= MA) return;
+  u32x4 av, bv;
+  if (c0 + 8 <= dv) {
+    av = u32x4{pack_bf16x2(g[0] * inv, g[1] * inv), pack_bf16x2(g[2] * inv, g[3] * inv),
+               pack_bf16x2(g[4] * inv, g[5] * inv), pack_bf16x2(g[6] * inv, g[7] * inv)};
+    bv = ld16(V + rc * dv + c0);
+    st16(rdnum + rr * dv + c0, av);
+  } else {  // c0 == dv: the dden and ones column, then zeros
+    const bool first = c0 == dv;
+    av = u32x4{first ? static_cast<uint32_t>(f32_to_bf16(dden)) : 0u, 0u, 0u, 0u};
+    bv = u32x4{first ? 0x3F80u : 0u, 0u, 0u, 0u};
+  }
+  st16(a + rc * MA + c0, av);
+  st16(ra + rr * MA + c0, av);
+  st16(b + rc * MA + c0, bv);
+  st16(rb + rr * MA + c0, bv);
 }
 
 unsigned blocks_for(int64_t work, int per) {
@@ -149,8 +161,9 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
                           hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
-  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 3) / 4)),
+  if ((rows + 7) / 8 > 0x7fffffffLL || dv % 8 || MA % 8 || MA > 256 || MA <= dv)
+    return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 7) / 8)),
                dim3(256), 0, st, num, den1, G, V, dv, MA, n, rows, normalize, delta, a, ra, b, rb,
                rdnum);
   return hipGetLastError();
