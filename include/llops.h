@@ -70,7 +70,8 @@ typedef enum {
   LLOPS_ENTRY_CAUSAL = 2,
   LLOPS_ENTRY_DECODE = 3,
   LLOPS_ENTRY_FEATMAP_BWD = 4,
-  LLOPS_ENTRY_CAUSAL_BWD = 5
+  LLOPS_ENTRY_CAUSAL_BWD = 5,
+  LLOPS_ENTRY_LINATTN_BWD = 6
 } llops_entry_t;
 
 typedef struct llops_shape {
@@ -188,6 +189,20 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* shape, const void* 
                                         const float* dO, float* dQ, float* dK, float* dV,
                                         float* dtheta_q, float* dtheta_k,
                                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * llops_linattn_bwd -- the same gradients for the non-causal
+ * out = llops_linattn_fwd(Q, K, V, theta_q, theta_k): M = phi_Q phi_K^T without
+ * the mask, so each of dphi_Q = dM phi_K, dphi_K = dM^T phi_Q, dV = M^T dnum is
+ * a non-causal linear attention (paper Sec. 1 associativity). Arguments,
+ * layouts, kernels and limits as for llops_linattn_causal_bwd.
+ * ws: llops_workspace_bytes(shape, LLOPS_ENTRY_LINATTN_BWD).
+ */
+llops_status_t llops_linattn_bwd(const llops_shape_t* shape, const void* Q, const void* K,
+                                 const void* V, const void* theta_q, const void* theta_k,
+                                 const float* dO, float* dQ, float* dK, float* dV,
+                                 float* dtheta_q, float* dtheta_k,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * llops_decode_step -- one new token per (batch, head) on the recurrent state:

@@ -6,7 +6,7 @@ Importing the package does not load the library; the first binding call does,
 and it raises if the library is missing.
 """
 _BINDING = ("llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd", "llops_linattn_causal_fwd",
-            "llops_linattn_causal_bwd",
+            "llops_linattn_causal_bwd", "llops_linattn_bwd",
             "llops_decode_step", "llops_workspace_bytes", "LlopsError", "library")
 
 

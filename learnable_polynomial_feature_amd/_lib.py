@@ -17,12 +17,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libllops.so")
 
 F32, BF16 = 0, 1
-ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD, ENTRY_CAUSAL_BWD = \
-    0, 1, 2, 3, 4, 5
+(ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD, ENTRY_CAUSAL_BWD,
+ ENTRY_LINATTN_BWD) = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
           3: "LLOPS_ERR_WORKSPACE", 4: "LLOPS_ERR_HIP"}
 EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd",
-           "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_decode_step",
+           "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
+           "llops_decode_step",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -72,6 +73,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_linattn_causal_fwd.restype = ctypes.c_int
     lib.llops_linattn_causal_bwd.argtypes = [SP] + [_P] * 12 + [ctypes.c_size_t, _P]
     lib.llops_linattn_causal_bwd.restype = ctypes.c_int
+    lib.llops_linattn_bwd.argtypes = [SP] + [_P] * 12 + [ctypes.c_size_t, _P]
+    lib.llops_linattn_bwd.restype = ctypes.c_int
     lib.llops_decode_step.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_decode_step.restype = ctypes.c_int
     lib.llops_status_str.argtypes = [ctypes.c_int]
@@ -279,6 +282,16 @@ def llops_linattn_causal_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, nor
     """Gradients (dQ, dK, dV, dtheta_q, dtheta_k) of sum(dO * out) for
     out = llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k, ...) from a zero
     state. Q, K, V and thetas bf16; dO fp32 [B, H, n, dv]; all results fp32."""
+    return _attn_bwd(True, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, workspace)
+
+
+def llops_linattn_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, normalize=False, delta=0.0,
+                      workspace=None):
+    """The same gradients for the non-causal llops_linattn_fwd."""
+    return _attn_bwd(False, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, workspace)
+
+
+def _attn_bwd(causal, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, workspace):
     Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
     theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
     shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
@@ -289,10 +302,12 @@ def llops_linattn_causal_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, nor
     dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
     dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
     lib = library()
-    ws, wsb = _workspace(shape, ENTRY_CAUSAL_BWD, Q.device, workspace)
-    _check(lib.llops_linattn_causal_bwd(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V),
-                                        _ptr(theta_q), _ptr(theta_k), _ptr(dO), _ptr(dQ), _ptr(dK),
-                                        _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(ws), wsb, _stream(Q)))
+    ws, wsb = _workspace(shape, ENTRY_CAUSAL_BWD if causal else ENTRY_LINATTN_BWD, Q.device,
+                         workspace)
+    fn = lib.llops_linattn_causal_bwd if causal else lib.llops_linattn_bwd
+    _check(fn(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+              _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(ws), wsb,
+              _stream(Q)))
     return dQ, dK, dV, dtq, dtk
 
 

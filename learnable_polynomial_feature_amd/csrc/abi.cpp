@@ -80,9 +80,9 @@ llops_shape_t feat_attn_shape(const llops_shape_t* s, int M, int DV) {
 
 SegPlan seg_plan(const llops_shape_t* s, bool causal);
 
-size_t feat_attn_seg_bytes(const llops_shape_t* s, int M, int DV) {
+size_t feat_attn_seg_bytes(const llops_shape_t* s, int M, int DV, bool causal) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
-  const SegPlan sp = seg_plan(&t, true);
+  const SegPlan sp = seg_plan(&t, causal);
   return static_cast<size_t>(s->batch * s->heads) * sp.nseg *
          (static_cast<size_t>(M) * DV + M) * sizeof(float);
 }
@@ -98,7 +98,7 @@ int bwd_w(const llops_shape_t* s) {
 
 struct BwdWs {
   size_t phq, phk, pkq, pkk, num, den1, ones, a, ra, b, rb, rdnum, rphq, rphk, vp, tmp, dphq, dphk,
-      seg, fb, total;
+      seg, tot, fb, total;
 };
 
 llops::FeatShape feat_shape(const llops_shape_t* s, int64_t n, int out_bf16);
@@ -155,7 +155,9 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
   return w;
 }
 
-BwdWs bwd_ws(const llops_shape_t* s) {
+// The non-causal backward needs no reversed copies; it keeps the segment
+// totals instead.
+BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   BwdWs w{};
   const size_t R = static_cast<size_t>(s->batch * s->heads) * static_cast<size_t>(s->n);
   const size_t m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s);
@@ -173,22 +175,27 @@ BwdWs bwd_ws(const llops_shape_t* s) {
   w.den1 = take(s->normalize ? R * 16 * 4 : 0);
   w.ones = take(s->normalize ? R * 16 * 2 : 0);
   w.a = take(R * MA * 2);
-  w.ra = take(R * MA * 2);
+  w.ra = take(causal ? R * MA * 2 : 0);
   w.b = take(R * MA * 2);
-  w.rb = take(R * MA * 2);
+  w.rb = take(causal ? R * MA * 2 : 0);
   w.rdnum = take(R * dv * 2);
-  w.rphq = take(R * m * 2);
-  w.rphk = take(R * m * 2);
+  w.rphq = take(causal ? R * m * 2 : 0);
+  w.rphk = take(causal ? R * m * 2 : 0);
   w.vp = take(R * W * 2);
   w.tmp = take(R * (W > dv ? W : dv) * 4);
   w.dphq = take(R * m * 2);
   w.dphk = take(R * m * 2);
-  size_t seg = feat_attn_seg_bytes(s, s->m, s->dv);
-  const size_t seg2 = feat_attn_seg_bytes(s, static_cast<int>(MA), static_cast<int>(W));
-  const size_t seg3 = feat_attn_seg_bytes(s, s->m, 16);
+  size_t seg = feat_attn_seg_bytes(s, s->m, s->dv, causal);
+  const size_t seg2 = feat_attn_seg_bytes(s, static_cast<int>(MA), static_cast<int>(W), causal);
+  const size_t seg3 = feat_attn_seg_bytes(s, s->m, 16, causal);
   if (seg2 > seg) seg = seg2;
   if (seg3 > seg) seg = seg3;
   w.seg = take(seg);
+  // per (b, h) totals of the non-causal passes (largest of the shapes above)
+  const size_t BH = static_cast<size_t>(s->batch * s->heads);
+  size_t per = m * dv + m;
+  if (MA * W + MA > per) per = MA * W + MA;
+  w.tot = take(causal ? 0 : BH * per * sizeof(float));
   w.fb = take(llops::featmap_bwd_ws_bytes(feat_shape(s, s->n, 0)));
   w.total = off;
   return w;
@@ -294,34 +301,45 @@ llops::AttnShape attn_shape(const llops_shape_t* s, bool causal) {
   return a;
 }
 
-llops_status_t validate_causal_bwd(const llops_shape_t* s) {
-  LLOPS_TRY(validate(s, LLOPS_ENTRY_CAUSAL));
+llops_status_t validate_attn_bwd(const llops_shape_t* s, bool causal) {
+  LLOPS_TRY(validate(s, causal ? LLOPS_ENTRY_CAUSAL : LLOPS_ENTRY_LINATTN));
   if (s->in_dtype != LLOPS_BF16)
-    return fail(LLOPS_ERR_UNSUPPORTED, "causal backward takes bf16 Q, K, V and Theta only");
+    return fail(LLOPS_ERR_UNSUPPORTED, "attention backward takes bf16 Q, K, V and Theta only");
   if (!llops::featmap_bwd_supported(feat_shape(s, s->n, 0)) ||
       !(s->m == 64 || s->m == 128 || s->m == 256))
     return fail(LLOPS_ERR_UNSUPPORTED,
-                "causal backward kernels: p = 2, t in {1, 4}, d in {64, 128}, m in {64, 128, 256} "
+                "attention backward kernels: p = 2, t in {1, 4}, d in {64, 128}, m in {64, 128, 256} "
                 "(got p=%d t=%d d=%d m=%d)", s->p, s->t, s->d, s->m);
   return LLOPS_OK;
 }
 
-// out_i = sum_{j<=i} (fq_i . fk_j) v_j over bf16 features fq, fk [BH][n][M]
-// and values v [BH][n][DV]; fp32 out. The forward's segment kernels.
-hipError_t causal_on_features(const llops_shape_t* s, int M, int DV, const uint16_t* fq,
-                              const uint16_t* fk, const uint16_t* v, float* out, float* seg,
-                              hipStream_t st) {
+// out_i = sum_{j<=i} (fq_i . fk_j) v_j (causal) or sum over all j (tot holds
+// the per-(b, h) totals then) over bf16 features fq, fk [BH][n][M] and values
+// v [BH][n][DV]; fp32 out. The forward's segment kernels.
+hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
+                            const uint16_t* fq, const uint16_t* fk, const uint16_t* v, float* out,
+                            float* seg, float* tot, hipStream_t st) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
-  const llops::AttnShape a = attn_shape(&t, true);
+  const llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
   const bool mf32 = llops::attn32_supported(a);
   hipError_t e = mf32 ? llops::launch_seg_state32(a, fk, v, seg, st)
                       : llops::launch_seg_state_bf16(a, fk, v, seg, st);
   if (e != hipSuccess) return e;
-  e = llops::launch_seg_scan(a, seg, nullptr, nullptr, nullptr, nullptr, 1, st);
+  const float* state = seg;
+  int64_t st_seg = per, st_bh = per * a.nseg;
+  if (causal) {
+    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, nullptr, nullptr, 1, st);
+  } else {
+    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, tot, tot + static_cast<int64_t>(M) * DV,
+                               0, st);
+    state = tot;
+    st_seg = 0;
+    st_bh = per;
+  }
   if (e != hipSuccess) return e;
-  return mf32 ? llops::launch_attn_out32(a, fq, fk, v, seg, per, per * a.nseg, out, st)
-              : llops::launch_attn_out_bf16(a, fq, fk, v, seg, per, per * a.nseg, out, st);
+  return mf32 ? llops::launch_attn_out32(a, fq, fk, v, state, st_seg, st_bh, out, st)
+              : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
 }
 
 // Shared body of the non-causal and causal forward passes.
@@ -464,10 +482,11 @@ int32_t llops_profile_disarm(void) {
 }
 
 size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
-  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_CAUSAL_BWD) return 0;
-  if (entry == LLOPS_ENTRY_CAUSAL_BWD) {
-    if (validate_causal_bwd(shape) != LLOPS_OK) return 0;
-    return bwd_ws(shape).total;
+  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_LINATTN_BWD) return 0;
+  if (entry == LLOPS_ENTRY_CAUSAL_BWD || entry == LLOPS_ENTRY_LINATTN_BWD) {
+    const bool causal = entry == LLOPS_ENTRY_CAUSAL_BWD;
+    if (validate_attn_bwd(shape, causal) != LLOPS_OK) return 0;
+    return bwd_ws(shape, causal).total;
   }
   if (validate(shape, entry) != LLOPS_OK) return 0;
   return ws_layout(shape, entry).total;
@@ -544,12 +563,12 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* s, const void* Q, c
                    ws_bytes, st);
 }
 
-llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, const void* K,
-                                        const void* V, const void* theta_q, const void* theta_k,
-                                        const float* dO, float* dQ, float* dK, float* dV,
-                                        float* dtheta_q, float* dtheta_k, void* ws,
-                                        size_t ws_bytes, hipStream_t st) {
-  LLOPS_TRY(validate_causal_bwd(s));
+// Shared body of the causal and non-causal attention backward.
+static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const void* Q, const void* K,
+                             const void* V, const void* theta_q, const void* theta_k,
+                             const float* dO, float* dQ, float* dK, float* dV, float* dtheta_q,
+                             float* dtheta_k, void* ws, size_t ws_bytes, hipStream_t st) {
+  LLOPS_TRY(validate_attn_bwd(s, causal));
   const int64_t BH = s->batch * s->heads;
   if (s->heads == 0) return LLOPS_OK;
   LLOPS_TRY(need(theta_q, "theta_q"));
@@ -566,7 +585,7 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, c
     LLOPS_TRY(need(dK, "dK"));
     LLOPS_TRY(need(dV, "dV"));
   }
-  const BwdWs L = bwd_ws(s);
+  const BwdWs L = bwd_ws(s, causal);
   if (ws_bytes < L.total)
     return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
   if (L.total && !ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
@@ -585,51 +604,82 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, c
   const int64_t n = s->n;
   uint16_t *phq = u16(L.phq), *phk = u16(L.phk);
   float* seg = f32(L.seg);
+  float* tot = causal ? nullptr : f32(L.tot);
   // feature maps of Q and K (bf16, as the forward stores them)
   llops::FeatJob jobs[2] = {{Q, theta_q, phq, w + L.pkq}, {K, theta_k, phk, w + L.pkk}};
   LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, n, 1), jobs, 2, st), "featmap");
   // num = M V and, with the normaliser, M 1
   float* num = f32(L.num);
-  LLOPS_HIP(causal_on_features(s, m, dv, phq, phk, static_cast<const uint16_t*>(V), num, seg, st),
+  LLOPS_HIP(attn_on_features(s, causal, m, dv, phq, phk, static_cast<const uint16_t*>(V), num, seg,
+                             tot, st),
             "attn num");
   float* den1 = nullptr;
   if (s->normalize) {
     den1 = f32(L.den1);
     LLOPS_HIP(llops::launch_fill_ones16(u16(L.ones), R, st), "ones");
-    LLOPS_HIP(causal_on_features(s, m, 16, phq, phk, u16(L.ones), den1, seg, st), "attn den");
+    LLOPS_HIP(attn_on_features(s, causal, m, 16, phq, phk, u16(L.ones), den1, seg, tot, st),
+              "attn den");
   }
-  uint16_t *a = u16(L.a), *ra = u16(L.ra), *b = u16(L.b), *rb = u16(L.rb), *rdnum = u16(L.rdnum);
+  // a = [dnum | dden | 0], b = [V | 1 | 0]; causal: also reversed copies
+  // and dnum reversed, non-causal: dnum in order
+  uint16_t *a = u16(L.a), *b = u16(L.b), *dn = u16(L.rdnum);
+  uint16_t *ra = causal ? u16(L.ra) : nullptr, *rb = causal ? u16(L.rb) : nullptr;
   LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
-                                  s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb,
-                                  rdnum, st),
+                                  s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
+                                  causal ? 1 : 0, st),
             "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
   uint16_t *dphq = u16(L.dphq), *dphk = u16(L.dphk);  // bf16, as the forward stores phi
-  // dphi_Q_i = sum_{j<=i} (a_i . b_j) phi_K_j, W columns of phi_K at a time
+  // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j, W columns of phi_K at a time
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
-    LLOPS_HIP(causal_on_features(s, MA, W, a, b, vp, tmp, seg, st), "attn dphi_q");
+    LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, vp, tmp, seg, tot, st), "attn dphi_q");
     LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
   }
-  // dphi_K_j = sum_{i>=j} (a_i . b_j) phi_Q_i: causal over the reversed sequence
+  // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: causal over the reversed sequence
+  const int rv = causal ? 1 : 0;
   for (int p0 = 0; p0 < m; p0 += W) {
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
-    LLOPS_HIP(causal_on_features(s, MA, W, rb, ra, vp, tmp, seg, st), "attn dphi_k");
-    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
+    LLOPS_HIP(attn_on_features(s, causal, MA, W, causal ? rb : b, causal ? ra : a, vp, tmp, seg,
+                               tot, st),
+              "attn dphi_k");
+    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, rv, st), "rows");
   }
-  // dV_j = sum_{i>=j} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
-  uint16_t *rphq = u16(L.rphq), *rphk = u16(L.rphk);
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
-  LLOPS_HIP(causal_on_features(s, m, dv, rphk, rphq, rdnum, tmp, seg, st), "attn dv");
-  LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
+  // dV_j = sum_{i(>=j)} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
+  if (causal) {
+    uint16_t *rphq = u16(L.rphq), *rphk = u16(L.rphk);
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
+    LLOPS_HIP(attn_on_features(s, true, m, dv, rphk, rphq, dn, tmp, seg, nullptr, st), "attn dv");
+    LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
+  } else {
+    LLOPS_HIP(attn_on_features(s, false, m, dv, phk, phq, dn, dV, seg, tot, st), "attn dv");
+  }
   // through the feature maps
   LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dphq, 1, dQ, dtheta_q, fb, st),
             "featmap_bwd q");
   LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dphk, 1, dK, dtheta_k, fb, st),
             "featmap_bwd k");
   return LLOPS_OK;
+}
+
+llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, const void* K,
+                                        const void* V, const void* theta_q, const void* theta_k,
+                                        const float* dO, float* dQ, float* dK, float* dV,
+                                        float* dtheta_q, float* dtheta_k, void* ws,
+                                        size_t ws_bytes, hipStream_t st) {
+  return attn_backward(s, true, Q, K, V, theta_q, theta_k, dO, dQ, dK, dV, dtheta_q, dtheta_k, ws,
+                       ws_bytes, st);
+}
+
+llops_status_t llops_linattn_bwd(const llops_shape_t* s, const void* Q, const void* K,
+                                 const void* V, const void* theta_q, const void* theta_k,
+                                 const float* dO, float* dQ, float* dK, float* dV,
+                                 float* dtheta_q, float* dtheta_k, void* ws, size_t ws_bytes,
+                                 hipStream_t st) {
+  return attn_backward(s, false, Q, K, V, theta_q, theta_k, dO, dQ, dK, dV, dtheta_q, dtheta_k, ws,
+                       ws_bytes, st);
 }
 
 llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const void* k,

@@ -61,9 +61,10 @@ __global__ __launch_bounds__(256) void fill_ones16(uint16_t* __restrict__ dst, i
 // 32 lanes per row, eight rows per workgroup: from num (fp32 [rows][dv]),
 // the plain causal sums den1 (fp32 [rows][16], column 0 = M 1), the upstream
 // gradient G (fp32) and V (bf16), writes a = [dnum | dden | 0] and
-// b = [V | 1 | 0] (bf16 [rows][MA]) in forward and reversed row order, and
-// dnum (bf16 [rows][dv]) reversed. A lane owns 8 consecutive columns and
-// writes them as one 16-byte store; dv and MA are multiples of 8, MA <= 256.
+// b = [V | 1 | 0] (bf16 [rows][MA]), with rev also in reversed row order
+// (ra, rb), and dnum (bf16 [rows][dv]) reversed when rev, else in order. A
+// lane owns 8 consecutive columns and writes them as one 16-byte store; dv
+// and MA are multiples of 8, MA <= 256.
 __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               const float* __restrict__ den1,
                                               const float* __restrict__ G,
@@ -71,13 +72,13 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               int64_t n, int64_t rows, int normalize, float delta,
                                               uint16_t* __restrict__ a, uint16_t* __restrict__ ra,
                                               uint16_t* __restrict__ b, uint16_t* __restrict__ rb,
-                                              uint16_t* __restrict__ rdnum) {
+                                              uint16_t* __restrict__ rdnum, int rev) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int l = threadIdx.x & 31;
   const bool live = r < rows;  // every lane joins the shuffles below
   const int64_t rc = live ? r : rows - 1;
   const int64_t bh = rc / n, i = rc - bh * n;
-  const int64_t rr = bh * n + (n - 1 - i);
+  const int64_t rr = rev ? bh * n + (n - 1 - i) : rc;
   const float den = normalize ? den1[rc * 16] + delta : 1.f;
   const float inv = 1.f / den;
   const int c0 = 8 * l;  // this lane's columns c0 .. c0+7
@@ -110,9 +111,11 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
     bv = u32x4{first ? 0x3F80u : 0u, 0u, 0u, 0u};
   }
   st16(a + rc * MA + c0, av);
-  st16(ra + rr * MA + c0, av);
   st16(b + rc * MA + c0, bv);
-  st16(rb + rr * MA + c0, bv);
+  if (rev) {
+    st16(ra + rr * MA + c0, av);
+    st16(rb + rr * MA + c0, bv);
+  }
 }
 
 unsigned blocks_for(int64_t work, int per) {
@@ -159,13 +162,13 @@ hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st) {
 hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
-                          hipStream_t st) {
+                          int rev, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if ((rows + 7) / 8 > 0x7fffffffLL || dv % 8 || MA % 8 || MA > 256 || MA <= dv)
     return hipErrorInvalidValue;
   LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 7) / 8)),
                dim3(256), 0, st, num, den1, G, V, dv, MA, n, rows, normalize, delta, a, ra, b, rb,
-               rdnum);
+               rdnum, rev);
   return hipGetLastError();
 }
 

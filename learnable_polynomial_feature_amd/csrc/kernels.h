@@ -80,7 +80,7 @@ hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st);
 hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
-                          hipStream_t st);
+                          int rev, hipStream_t st);
 
 // Linear-attention contraction over precomputed features.
 struct AttnShape {

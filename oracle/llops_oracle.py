@@ -240,6 +240,72 @@ def causal_chunked(Q, K, V, theta_q, theta_k, square=False, normalize=False,
     return out, S, z
 
 
+def attn_bwd(Pq, Pk, V, G, normalize=False, delta=0.0, causal=True):
+    """Gradients (dPq, dPk, dV) of L = sum(G * out) for out = M V [/ (M 1 + delta)]
+    over given features, M = Pq Pk^T, lower-triangular (diagonal kept) when
+    causal. The chain rule through the materialised form of causal_quadratic
+    and linattn ([LLoPS-arXiv] Sec. 1; [LowRank-blog] Performer section for
+    the normalised form, [SLAY-notes] key design 3 for the +delta):
+      normalised:  dnum = G / den,  dden = -sum_cols(G * out) / den
+      plain:       dnum = G,        dden = 0
+      dM = dnum V^T + dden 1^T (lower triangle when causal)
+      dPq = dM Pk,  dPk = dM^T Pq,  dV = M^T dnum.
+    """
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    M = Pq @ Pk.T
+    if causal:
+        M = np.tril(M)
+    if normalize:
+        den = M.sum(axis=1) + delta
+        out = (M @ V) / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(Pq.shape[0])
+    dM = dnum @ V.T + dden[:, None]
+    if causal:
+        dM = np.tril(dM)
+    return dM @ Pk, dM.T @ Pq, M.T @ dnum
+
+
+def attn_bwd_factored(Pq, Pk, V, G, normalize=False, delta=0.0):
+    """Non-causal attn_bwd without the n x n matrix: by associativity
+    ([LLoPS-arXiv] Sec. 1) with S = Pk^T V and z = Pk^T 1,
+      num = Pq S,  den = Pq z + delta,
+      dPq = dnum S^T + dden z^T,
+      dPk = V (dnum^T Pq) + 1 (dden^T Pq),
+      dV  = Pk (Pq^T dnum).
+    Exact (up to rounding order) for any n; used where n^2 does not fit."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    S = Pk.T @ V
+    z = Pk.sum(axis=0)
+    if normalize:
+        den = Pq @ z + delta
+        out = (Pq @ S) / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(Pq.shape[0])
+    dPq = dnum @ S.T + np.outer(dden, z)
+    dPk = V @ (dnum.T @ Pq) + np.outer(np.ones(Pk.shape[0]), dden @ Pq)
+    dV = Pk @ (Pq.T @ dnum)
+    return dPq, dPk, dV
+
+
+def linattn_bwd(Q, K, V, theta_q, theta_k, G, square=False, normalize=False, delta=0.0):
+    """Gradients (dQ, dK, dV, dTheta_q, dTheta_k) of L = sum(G * out) for
+    out = linattn(Q, K, V, theta_q, theta_k, ...): attn_bwd without the mask,
+    then featmap_bwd on each side."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    dPq, dPk, dV = attn_bwd(Pq, Pk, V, G, normalize, delta, causal=False)
+    dQ, dtq = featmap_bwd(Q, theta_q, dPq, square)
+    dK, dtk = featmap_bwd(K, theta_k, dPk, square)
+    return dQ, dK, dV, dtq, dtk
+
+
 def causal_attn_bwd(Pq, Pk, V, G, normalize=False, delta=0.0):
     """Gradients (dPq, dPk, dV) of L = sum(G * out) for the causal contraction
     over given features, out = M V [/ (M 1 + delta)] with M = tril(Pq Pk^T).
@@ -396,17 +462,26 @@ def featmap_bwd_bh(X, theta, dphi, square=False):
     return dX, dth
 
 
+def linattn_bwd_bh(Q, K, V, theta_q, theta_k, G, **kw):
+    """linattn_bwd over [B, H, n, .] tensors (shared theta: summed over heads)."""
+    return _bwd_bh(linattn_bwd, Q, K, V, theta_q, theta_k, G, **kw)
+
+
 def causal_bwd_bh(Q, K, V, theta_q, theta_k, G, **kw):
     """causal_bwd over [B, H, n, .] tensors; a shared theta's gradient sums
     over all heads. Returns (dQ, dK, dV, dTheta_q, dTheta_k)."""
+    return _bwd_bh(causal_bwd, Q, K, V, theta_q, theta_k, G, **kw)
+
+
+def _bwd_bh(fn, Q, K, V, theta_q, theta_k, G, **kw):
     theta_q, theta_k = np.asarray(theta_q), np.asarray(theta_k)
     B, H = Q.shape[:2]
     dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
     dtq, dtk = np.zeros(theta_q.shape), np.zeros(theta_k.shape)
     for b in range(B):
         for h in range(H):
-            gq, gk, gv, tq, tk = causal_bwd(Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
-                                            _theta_for(theta_k, h), G[b, h], **kw)
+            gq, gk, gv, tq, tk = fn(Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
+                                    _theta_for(theta_k, h), G[b, h], **kw)
             dQ[b, h], dK[b, h], dV[b, h] = gq, gk, gv
             if theta_q.ndim == 5:
                 dtq[h] += tq

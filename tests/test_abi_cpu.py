@@ -314,28 +314,50 @@ def _cbwd_shape(**kw):
     (dict(in_dtype=_lib.F32), 2), (dict(t=2), 2), (dict(p=3), 2), (dict(m=96), 2),
     (dict(m=192), 2), (dict(d=96), 2), (dict(dv=144), 2), (dict(out_dtype=_lib.BF16), 2),
 ])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @fake_ptr
-def test_causal_bwd_validation(L, bad, code):
+def test_attn_bwd_validation(L, bad, code, causal):
     s = _cbwd_shape(**bad)
-    st = L.llops_linattn_causal_bwd(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None)
+    fn, entry = _attn_bwd_entry(L, causal)
+    st = fn(ctypes.byref(s), *([FAKE] * 11), FAKE, 1 << 40, None)
     assert st == code, _err(L)
-    assert L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD) == 0
+    assert L.llops_workspace_bytes(ctypes.byref(s), entry) == 0
 
 
+def _attn_bwd_entry(L, causal):
+    if causal:
+        return L.llops_linattn_causal_bwd, _lib.ENTRY_CAUSAL_BWD
+    return L.llops_linattn_bwd, _lib.ENTRY_LINATTN_BWD
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @fake_ptr
-def test_causal_bwd_pointers_and_workspace(L):
+def test_attn_bwd_pointers_and_workspace(L, causal):
+    fn, entry = _attn_bwd_entry(L, causal)
     s = _cbwd_shape(batch=2, heads=3, n=1000, d=128, dv=128, m=256)
-    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD)
+    need = L.llops_workspace_bytes(ctypes.byref(s), entry)
     R = 2 * 3 * 1000
-    # at least: phi_Q, phi_K (bf16), their fp32 gradients, a, b and reversed copies
-    assert need >= R * 256 * (2 + 2 + 4 + 4) + 4 * R * 192 * 2
+    # at least: phi_Q, phi_K (bf16), fp32 num and M 1, a and b (the causal
+    # pass also keeps reversed copies of a, b, phi_Q and phi_K)
+    floor = R * 256 * (2 + 2) + R * (128 + 16) * 4 + 2 * R * 192 * 2
+    if causal:
+        floor += 2 * R * 192 * 2 + 2 * R * 256 * 2
+    assert need >= floor
     plain = _cbwd_shape(batch=2, heads=3, n=1000, d=128, dv=128, m=256, normalize=0)
-    assert L.llops_workspace_bytes(ctypes.byref(plain), _lib.ENTRY_CAUSAL_BWD) < need
+    assert L.llops_workspace_bytes(ctypes.byref(plain), entry) < need
     args = [FAKE] * 11
-    assert L.llops_linattn_causal_bwd(ctypes.byref(s), *args, FAKE, need - 1, None) == 3
+    assert fn(ctypes.byref(s), *args, FAKE, need - 1, None) == 3
     names = ("Q", "K", "V", "theta_q", "theta_k", "dO", "dQ", "dK", "dV", "dtheta_q", "dtheta_k")
     for i, name in enumerate(names):
         a = list(args)
         a[i] = None
-        assert L.llops_linattn_causal_bwd(ctypes.byref(s), *a, FAKE, need, None) == 1
+        assert fn(ctypes.byref(s), *a, FAKE, need, None) == 1
         assert f"{name} is null" in _err(L)
+
+
+@fake_ptr
+def test_noncausal_bwd_workspace_below_causal(L):
+    s = _cbwd_shape(batch=2, heads=3, n=1000, d=128, dv=128, m=256)
+    c = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD)
+    nc = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_LINATTN_BWD)
+    assert 0 < nc < c

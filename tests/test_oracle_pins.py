@@ -463,3 +463,56 @@ def test_causal_attn_bwd_chunked_equals_materialised(normalize, chunk):
     got = O.causal_attn_bwd_chunked(Pq, Pk, V, G, normalize=normalize, delta=0.5, chunk=chunk)
     for a, b in zip(got, want):
         assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def _lin_loss(Q, K, V, tq, tk, G, square, normalize, delta):
+    return float(np.sum(G * O.linattn(Q, K, V, tq, tk, square=square, normalize=normalize,
+                                      delta=delta)))
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, True)])
+def test_linattn_bwd_matches_central_differences(square, normalize):
+    """Non-causal: every entry of dQ, dK, dV, dTheta_q, dTheta_k against a
+    central difference of L = sum(G * linattn(...))."""
+    rng = np.random.default_rng(45)
+    n, d, dv, m, p, t = 6, 3, 2, 4, 2, 2
+    args = [rng.standard_normal((n, d)) * 0.8, rng.standard_normal((n, d)) * 0.8,
+            rng.standard_normal((n, dv)), rng.standard_normal((p, t, d, m)) * 0.6,
+            rng.standard_normal((p, t, d, m)) * 0.6]
+    G = rng.standard_normal((n, dv))
+    delta = 0.3 if normalize else 0.0
+    grads = O.linattn_bwd(*args, G, square=square, normalize=normalize, delta=delta)
+    eps = 1e-6
+    for which in range(5):
+        for idx in np.ndindex(args[which].shape):
+            ap = [a.copy() for a in args]
+            am = [a.copy() for a in args]
+            ap[which][idx] += eps
+            am[which][idx] -= eps
+            fd = (_lin_loss(*ap, G, square, normalize, delta)
+                  - _lin_loss(*am, G, square, normalize, delta)) / (2 * eps)
+            assert abs(grads[which][idx] - fd) <= 2e-6 * max(1.0, abs(fd)), (which, idx)
+
+
+def test_attn_bwd_causal_flag_matches_causal_attn_bwd():
+    rng = np.random.default_rng(46)
+    Pq, Pk = np.abs(rng.standard_normal((9, 4))), np.abs(rng.standard_normal((9, 4)))
+    V, G = rng.standard_normal((9, 3)), rng.standard_normal((9, 3))
+    for a, b in zip(O.attn_bwd(Pq, Pk, V, G, True, 0.2, causal=True),
+                    O.causal_attn_bwd(Pq, Pk, V, G, True, 0.2)):
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_attn_bwd_factored_equals_materialised(normalize):
+    """The factored non-causal backward (states S = Pk^T V, z = Pk^T 1) equals
+    the materialised chain rule, which the central-difference test above pins."""
+    rng = np.random.default_rng(45)
+    n, m, dv = 19, 6, 5
+    Pq = np.abs(rng.standard_normal((n, m)))
+    Pk = np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    want = O.attn_bwd(Pq, Pk, V, G, normalize=normalize, delta=0.5, causal=False)
+    got = O.attn_bwd_factored(Pq, Pk, V, G, normalize=normalize, delta=0.5)
+    for a, b in zip(got, want):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
