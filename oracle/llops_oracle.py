@@ -25,6 +25,11 @@ the mathematics allows; see tests/test_oracle_pins.py):
   * Causal mask is inclusive (key j contributes to query i iff j <= i); the
     decode step adds the new key/value to the state before reading it.
   * No 1/sqrt(d) scaling inside the method; the kernel is (q^T k)^p.
+  * Gated state update (named as future work in [LLoPS-notes] conclusion,
+    with Mamba2's semiseparable matrix as the example): one scalar decay
+    a_i = exp(g_i) per token and head multiplies the whole state (S and z)
+    before token i is added, so key j reaches query i >= j with weight
+    exp(g_{j+1} + ... + g_i).
 parity unpinned: the delta placement and the inclusive diagonal are
 conventions (the pages fix neither); the tests only check that every path
 applies them consistently.
@@ -428,6 +433,75 @@ def decode(S0, z0, q_steps, k_steps, v_steps, theta_q, theta_k, square=False,
 # --------------------------------------------------------------------------
 # Batched wrappers over [B, H, n, *] with per-head (or shared) Theta
 # --------------------------------------------------------------------------
+def gated_causal_quadratic(Q, K, V, theta_q, theta_k, log_gate, square=False, normalize=False,
+                           delta=0.0, S0=None, z0=None):
+    """Causal attention with a per-token scalar decay, materialised: with
+    c = cumsum(log_gate),
+      M_ij = exp(c_i - c_j) (phi_Q,i . phi_K,j) for j <= i, else 0,
+      num_i = (M V)_i + exp(c_i) phi_Q,i S0,  den_i = (M 1)_i + exp(c_i) phi_Q,i z0 + delta,
+      out = num [/ den].
+    The semiseparable (decay-masked) form of Mamba2 that [LLoPS-notes]
+    conclusion names for combining the sketch with forgetting gates, on the
+    attention of [LLoPS-arXiv] Sec. 1. O(n^2); small n only."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    V = _f64(V)
+    c = np.cumsum(_f64(log_gate))
+    n = Pq.shape[0]
+    i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+    W = np.where(j <= i, np.exp(np.where(j <= i, c[:, None] - c[None, :], 0.0)), 0.0)
+    M = W * (Pq @ Pk.T)
+    num = M @ V
+    den = M.sum(axis=1)
+    if S0 is not None:
+        num = num + np.exp(c)[:, None] * (Pq @ _f64(S0))
+    if z0 is not None:
+        den = den + np.exp(c) * (Pq @ _f64(z0))
+    if not normalize:
+        return num
+    return num / (den + delta)[:, None]
+
+
+def gated_recurrent(Q, K, V, theta_q, theta_k, log_gate, square=False, normalize=False,
+                    delta=0.0, S0=None, z0=None):
+    """The same gated attention token by token (the recurrent form of
+    [LLoPS-arXiv] Sec. 1 with the decay of [LLoPS-notes] conclusion):
+      S <- exp(g_i) S + phi_K,i v_i^T,  z <- exp(g_i) z + phi_K,i,
+      out_i = phi_Q,i S [/ (phi_Q,i z + delta)].
+    Returns (out [n, dv], S, z)."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    V = _f64(V)
+    g = _f64(log_gate)
+    m, dv = Pq.shape[1], V.shape[1]
+    S = np.zeros((m, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros(m) if z0 is None else _f64(z0).copy()
+    out = np.zeros((Pq.shape[0], dv))
+    for t in range(Pq.shape[0]):
+        a = np.exp(g[t])
+        S = a * S + np.outer(Pk[t], V[t])
+        z = a * z + Pk[t]
+        o = Pq[t] @ S
+        out[t] = o / (Pq[t] @ z + delta) if normalize else o
+    return out, S, z
+
+
+def gated_recurrent_bh(Q, K, V, theta_q, theta_k, log_gate, S0=None, z0=None, **kw):
+    """gated_recurrent over [B, H, n, .] tensors, log_gate [B, H, n].
+    Returns (out [B,H,n,dv], S [B,H,m,dv], z [B,H,m])."""
+    B, H, n, _ = Q.shape
+    m = np.asarray(theta_q).shape[-1]
+    dv = V.shape[-1]
+    out, S, z = np.zeros((B, H, n, dv)), np.zeros((B, H, m, dv)), np.zeros((B, H, m))
+    for b in range(B):
+        for h in range(H):
+            out[b, h], S[b, h], z[b, h] = gated_recurrent(
+                Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h), _theta_for(theta_k, h),
+                log_gate[b, h], S0=None if S0 is None else S0[b, h],
+                z0=None if z0 is None else z0[b, h], **kw)
+    return out, S, z
+
+
 def _theta_for(theta, h):
     theta = np.asarray(theta)
     return theta[h] if theta.ndim == 5 else theta

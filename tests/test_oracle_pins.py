@@ -516,3 +516,74 @@ def test_attn_bwd_factored_equals_materialised(normalize):
     got = O.attn_bwd_factored(Pq, Pk, V, G, normalize=normalize, delta=0.5)
     for a, b in zip(got, want):
         assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# ---- gated (decayed) causal attention --------------------------------------
+
+def _gated_inputs(rng, n=9, d=3, dv=2, m=4, t=2):
+    Q, K = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = rng.standard_normal((2, t, d, m)), rng.standard_normal((2, t, d, m))
+    g = -np.abs(rng.standard_normal(n))
+    return Q, K, V, tq, tk, g
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_gated_zero_gate_is_causal(normalize):
+    """log_gate = 0 (no decay) reduces both gated forms to causal_quadratic."""
+    rng = np.random.default_rng(60)
+    Q, K, V, tq, tk, g = _gated_inputs(rng)
+    z = np.zeros_like(g)
+    want = O.causal_quadratic(Q, K, V, tq, tk, square=True, normalize=normalize, delta=0.25)
+    a = O.gated_causal_quadratic(Q, K, V, tq, tk, z, square=True, normalize=normalize, delta=0.25)
+    b, _, _ = O.gated_recurrent(Q, K, V, tq, tk, z, square=True, normalize=normalize, delta=0.25)
+    assert np.allclose(a, want, rtol=1e-12, atol=1e-12)
+    assert np.allclose(b, want, rtol=1e-12, atol=1e-12)
+
+
+def test_gated_geometric_series():
+    """Scalar features (d = m = p = t = 1, Theta = 1), k = v = 1 and a constant
+    decay gamma: out_i = q_i (1 - gamma^(i+1)) / (1 - gamma), the geometric
+    sum over keys 0..i with weight gamma^(i-j)."""
+    n, gamma = 12, 0.8
+    q = np.linspace(0.5, 2.0, n)[:, None]
+    ones = np.ones((n, 1))
+    th = np.ones((1, 1, 1, 1))
+    g = np.full(n, np.log(gamma))
+    want = q[:, 0] * (1 - gamma ** (np.arange(n) + 1)) / (1 - gamma)
+    a = O.gated_causal_quadratic(q, ones, ones, th, th, g)
+    b, S, z = O.gated_recurrent(q, ones, ones, th, th, g)
+    assert np.allclose(a[:, 0], want, rtol=1e-13)
+    assert np.allclose(b[:, 0], want, rtol=1e-13)
+    assert np.isclose(S[0, 0], (1 - gamma ** n) / (1 - gamma), rtol=1e-13)
+
+
+def test_gated_full_forgetting():
+    """A gate of exp(-800) = 0 forgets everything before the current token:
+    normalised with delta = 0 and a positive (squared) map, out_i = v_i."""
+    rng = np.random.default_rng(61)
+    Q, K, V, tq, tk, _ = _gated_inputs(rng)
+    g = np.full(Q.shape[0], -800.0)
+    a = O.gated_causal_quadratic(Q, K, V, tq, tk, g, square=True, normalize=True)
+    b, _, _ = O.gated_recurrent(Q, K, V, tq, tk, g, square=True, normalize=True)
+    assert np.allclose(a, V, rtol=1e-12, atol=1e-12)
+    assert np.allclose(b, V, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_gated_recurrent_equals_materialised_and_continues(normalize):
+    """The recurrence equals the decay-masked matrix form, and splitting the
+    sequence with the first half's (S, z) as the second half's initial state
+    reproduces the whole."""
+    rng = np.random.default_rng(62)
+    Q, K, V, tq, tk, g = _gated_inputs(rng, n=15)
+    kw = dict(square=True, normalize=normalize, delta=0.5)
+    whole, S, z = O.gated_recurrent(Q, K, V, tq, tk, g, **kw)
+    assert np.allclose(O.gated_causal_quadratic(Q, K, V, tq, tk, g, **kw), whole,
+                       rtol=1e-12, atol=1e-12)
+    k = 6
+    _, S1, z1 = O.gated_recurrent(Q[:k], K[:k], V[:k], tq, tk, g[:k], **kw)
+    second = O.gated_causal_quadratic(Q[k:], K[k:], V[k:], tq, tk, g[k:], S0=S1, z0=z1, **kw)
+    assert np.allclose(second, whole[k:], rtol=1e-12, atol=1e-12)
+    _, S2, z2 = O.gated_recurrent(Q[k:], K[k:], V[k:], tq, tk, g[k:], S0=S1, z0=z1, **kw)
+    assert np.allclose(S2, S, rtol=1e-12, atol=1e-12) and np.allclose(z2, z, rtol=1e-12)
