@@ -71,7 +71,9 @@ typedef enum {
   LLOPS_ENTRY_DECODE = 3,
   LLOPS_ENTRY_FEATMAP_BWD = 4,
   LLOPS_ENTRY_CAUSAL_BWD = 5,
-  LLOPS_ENTRY_LINATTN_BWD = 6
+  LLOPS_ENTRY_LINATTN_BWD = 6,
+  LLOPS_ENTRY_GATED_CAUSAL = 7,
+  LLOPS_ENTRY_GATED_DECODE = 8
 } llops_entry_t;
 
 typedef struct llops_shape {
@@ -165,6 +167,35 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* 
                                         hipStream_t stream);
 
 /*
+ * llops_linattn_gated_causal_fwd -- causal linear attention with a decaying state
+ *   S_i = exp(g_i) S_{i-1} + phi_K(k_i) v_i^T,  z_i = exp(g_i) z_{i-1} + phi_K(k_i),
+ *   S_{-1} = S0, z_{-1} = z0,  out_i = (phi_Q(q_i) S_i) [ / (phi_Q(q_i) z_i + delta) ],
+ * i.e. key j reaches query i >= j with weight exp(g_{j+1} + ... + g_i) (the
+ * decay-masked, semiseparable form). The LLoPS notes name data-driven
+ * forgetting gates (Mamba2's semiseparable matrix) as the way forward in
+ * "limitations and outlook" and say the feature map drops into gated state
+ * rules unchanged ("highlights"); the gate here is one scalar per token and
+ * head, applied to the whole state before the token is added, which with
+ * g = 0 is exactly llops_linattn_causal_fwd.
+ * log_gate: fp32 [batch][heads][n], g_i = log of the decay (device, 4-byte
+ * aligned). Values <= 0 keep every factor in (0, 1]; positive values grow the
+ * state and can overflow. Other arguments as for llops_linattn_causal_fwd;
+ * S_final/z_final include the decay of every token. in_dtype BF16 only, with
+ * (m, dv) in {(256, 128), (128, 64), (64, 64)} (else LLOPS_ERR_UNSUPPORTED).
+ * Decay factors are computed in fp32 from chunk-local sums of g and the
+ * decay-weighted V rounded to bf16 before its product.
+ * ws: llops_workspace_bytes(shape, LLOPS_ENTRY_GATED_CAUSAL).
+ */
+llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* shape, const void* Q,
+                                              const void* K, const void* V,
+                                              const void* theta_q, const void* theta_k,
+                                              const float* log_gate,
+                                              const float* S0, const float* z0,
+                                              void* out, float* S_final, float* z_final,
+                                              void* ws, size_t ws_bytes,
+                                              hipStream_t stream);
+
+/*
  * llops_linattn_causal_bwd -- gradients of L = sum(dO * out) for
  * out = llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k) started from a
  * zero state: dQ, dK [batch][heads][n][d], dV [batch][heads][n][dv] and
@@ -220,6 +251,23 @@ llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
                                  const void* theta_q, const void* theta_k,
                                  float* S, float* z, void* out,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * llops_gated_decode_step -- llops_decode_step on a decaying state:
+ *   S = exp(g) S + phi_K(k) v^T;  z = exp(g) z + phi_K(k);
+ *   out = phi_Q(q)^T S [ / (phi_Q(q)^T z + delta) ]
+ * with one log gate g per (batch, head): log_gate fp32 [batch][heads]
+ * (device, 4-byte aligned). The recurrent step of
+ * llops_linattn_gated_causal_fwd (same source passages); g = 0 is
+ * llops_decode_step. Other arguments, layouts and limits as for
+ * llops_decode_step. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_GATED_DECODE).
+ */
+llops_status_t llops_gated_decode_step(const llops_shape_t* shape, const void* q,
+                                       const void* k, const void* v,
+                                       const void* theta_q, const void* theta_k,
+                                       const float* log_gate,
+                                       float* S, float* z, void* out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Diagnostics: kernel-level timing. While armed on the calling thread, each

@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libllops.so")
 
 F32, BF16 = 0, 1
 (ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD, ENTRY_CAUSAL_BWD,
- ENTRY_LINATTN_BWD) = 0, 1, 2, 3, 4, 5, 6
+ ENTRY_LINATTN_BWD, ENTRY_GATED_CAUSAL, ENTRY_GATED_DECODE) = 0, 1, 2, 3, 4, 5, 6, 7, 8
 STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
           3: "LLOPS_ERR_WORKSPACE", 4: "LLOPS_ERR_HIP"}
 EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd",
            "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
-           "llops_decode_step",
+           "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -77,6 +77,10 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_linattn_bwd.restype = ctypes.c_int
     lib.llops_decode_step.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     lib.llops_decode_step.restype = ctypes.c_int
+    lib.llops_linattn_gated_causal_fwd.argtypes = [SP] + [_P] * 12 + [ctypes.c_size_t, _P]
+    lib.llops_linattn_gated_causal_fwd.restype = ctypes.c_int
+    lib.llops_gated_decode_step.argtypes = [SP] + [_P] * 10 + [ctypes.c_size_t, _P]
+    lib.llops_gated_decode_step.restype = ctypes.c_int
     lib.llops_status_str.argtypes = [ctypes.c_int]
     lib.llops_status_str.restype = ctypes.c_char_p
     lib.llops_last_error.argtypes = []
@@ -243,6 +247,23 @@ def llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k, *, square=False, normali
 
     Returns out [B, H, n, dv] fp32, or (out, S_final, z_final) when return_state.
     """
+    return _causal(None, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk, S0, z0, out,
+                   S_final, z_final, return_state, workspace)
+
+
+def llops_linattn_gated_causal_fwd(Q, K, V, theta_q, theta_k, log_gate, *, square=False,
+                                   normalize=False, delta=0.0, chunk=0, S0=None, z0=None, out=None,
+                                   S_final=None, z_final=None, return_state=False, workspace=None):
+    """Causal linear attention whose state decays by exp(log_gate[b, h, i]) before token i.
+
+    log_gate: fp32 [B, H, n]. Returns as llops_linattn_causal_fwd.
+    """
+    return _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk, S0, z0,
+                   out, S_final, z_final, return_state, workspace)
+
+
+def _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk, S0, z0, out,
+            S_final, z_final, return_state, workspace):
     Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
     theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
     shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk)
@@ -267,11 +288,21 @@ def llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k, *, square=False, normali
             z_final = torch.empty((B, H, m), dtype=torch.float32, device=Q.device)
     if out is None:
         out = torch.empty(V.shape, dtype=torch.float32, device=Q.device)
-    ws, wsb = _workspace(shape, ENTRY_CAUSAL, Q.device, workspace)
-    _check(library().llops_linattn_causal_fwd(
-        ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
-        _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_final), _ptr(z_final), _ptr(ws), wsb,
-        _stream(Q)))
+    if log_gate is None:
+        ws, wsb = _workspace(shape, ENTRY_CAUSAL, Q.device, workspace)
+        _check(library().llops_linattn_causal_fwd(
+            ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+            _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_final), _ptr(z_final), _ptr(ws), wsb,
+            _stream(Q)))
+    else:
+        log_gate = _dev(log_gate, "log_gate")
+        if log_gate.shape != Q.shape[:3] or log_gate.dtype != torch.float32:
+            raise ValueError("log_gate must be fp32 [B, H, n]")
+        ws, wsb = _workspace(shape, ENTRY_GATED_CAUSAL, Q.device, workspace)
+        _check(library().llops_linattn_gated_causal_fwd(
+            ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+            _ptr(log_gate), _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_final), _ptr(z_final),
+            _ptr(ws), wsb, _stream(Q)))
     if return_state:
         return out, S_final, z_final
     return out
@@ -314,6 +345,17 @@ def _attn_bwd(causal, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, w
 def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normalize=True,
                       delta=0.0, out=None, workspace=None):
     """One token per (b, h): S, z updated in place; returns out [B, H, dv] fp32."""
+    return _decode(None, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, workspace)
+
+
+def llops_gated_decode_step(q, k, v, theta_q, theta_k, log_gate, S, z, *, square=False,
+                            normalize=True, delta=0.0, out=None, workspace=None):
+    """llops_decode_step on a state first decayed by exp(log_gate) (fp32 [B, H])."""
+    return _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out,
+                   workspace)
+
+
+def _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, workspace):
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
     theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
@@ -332,10 +374,20 @@ def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normaliz
                        out_dtype=F32)
     if out is None:
         out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
-    ws, wsb = _workspace(shape, ENTRY_DECODE, q.device, workspace)
-    _check(library().llops_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
-                                       _ptr(theta_q), _ptr(theta_k), _ptr(S), _ptr(z), _ptr(out),
-                                       _ptr(ws), wsb, _stream(q)))
+    if log_gate is None:
+        ws, wsb = _workspace(shape, ENTRY_DECODE, q.device, workspace)
+        _check(library().llops_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(theta_q), _ptr(theta_k), _ptr(S), _ptr(z),
+                                           _ptr(out), _ptr(ws), wsb, _stream(q)))
+    else:
+        log_gate = _dev(log_gate, "log_gate")
+        if log_gate.shape != (B, H) or log_gate.dtype != torch.float32:
+            raise ValueError("log_gate must be fp32 [B, H]")
+        ws, wsb = _workspace(shape, ENTRY_GATED_DECODE, q.device, workspace)
+        _check(library().llops_gated_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                                 _ptr(theta_q), _ptr(theta_k), _ptr(log_gate),
+                                                 _ptr(S), _ptr(z), _ptr(out), _ptr(ws), wsb,
+                                                 _stream(q)))
     return out
 
 

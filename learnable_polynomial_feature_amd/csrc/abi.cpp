@@ -60,7 +60,7 @@ SegPlan seg_plan(const llops_shape_t* s, bool causal) {
 }
 
 struct WsLayout {
-  size_t phiq, phik, seg, tot, pkq, pkk, total;
+  size_t phiq, phik, seg, tot, pkq, pkk, gl, gseg, total;
 };
 
 // ---- causal backward: workspace plan ---------------------------------------
@@ -112,6 +112,9 @@ size_t pack_bytes(const llops_shape_t* s, int64_t n) {
 
 WsLayout ws_layout(const llops_shape_t* s, int entry) {
   WsLayout w{};
+  const bool gated = entry == LLOPS_ENTRY_GATED_CAUSAL;
+  if (gated) entry = LLOPS_ENTRY_CAUSAL;
+  if (entry == LLOPS_ENTRY_GATED_DECODE) entry = LLOPS_ENTRY_DECODE;
   const size_t esz = s->in_dtype == LLOPS_BF16 ? 2 : 4;
   const size_t BH = static_cast<size_t>(s->batch * s->heads);
   const size_t per = static_cast<size_t>(s->m) * s->dv + s->m;
@@ -139,6 +142,12 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
     off = round_up(off + pkb, 256);
     w.pkk = off;
     off = round_up(off + pkb, 256);
+    if (gated) {  // chunk-local gate sums [BH][n rounded up to 32], segment gate sums [BH][nseg]
+      w.gl = off;
+      off = round_up(off + BH * static_cast<size_t>((s->n + 31) / 32 * 32) * sizeof(float), 256);
+      w.gseg = off;
+      off = round_up(off + BH * sp.nseg * sizeof(float), 256);
+    }
   } else if (entry == LLOPS_ENTRY_DECODE) {
     const size_t phib = BH * s->m * sizeof(float);
     w.phiq = off;
@@ -205,6 +214,8 @@ bool is01(int32_t x) { return x == 0 || x == 1; }
 
 llops_status_t validate(const llops_shape_t* s, int entry) {
   if (!s) return fail(LLOPS_ERR_INVALID_ARG, "shape is null");
+  if (entry == LLOPS_ENTRY_GATED_CAUSAL) entry = LLOPS_ENTRY_CAUSAL;
+  if (entry == LLOPS_ENTRY_GATED_DECODE) entry = LLOPS_ENTRY_DECODE;
   // the backward takes the feature map's shape rules
   if (entry == LLOPS_ENTRY_FEATMAP_BWD) entry = LLOPS_ENTRY_FEATMAP;
   if (s->batch < 0 || s->heads < 0) return fail(LLOPS_ERR_INVALID_ARG, "batch/heads < 0");
@@ -250,6 +261,13 @@ llops_status_t validate(const llops_shape_t* s, int entry) {
 llops_status_t need(const void* p, const char* name) {
   if (!p) return fail(LLOPS_ERR_INVALID_ARG, "%s is null", name);
   if (!aligned16(p)) return fail(LLOPS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return LLOPS_OK;
+}
+
+llops_status_t need4(const void* p, const char* name) {
+  if (!p) return fail(LLOPS_ERR_INVALID_ARG, "%s is null", name);
+  if (reinterpret_cast<uintptr_t>(p) & 3u)
+    return fail(LLOPS_ERR_INVALID_ARG, "%s is not 4-byte aligned", name);
   return LLOPS_OK;
 }
 
@@ -310,6 +328,19 @@ llops_status_t validate_attn_bwd(const llops_shape_t* s, bool causal) {
     return fail(LLOPS_ERR_UNSUPPORTED,
                 "attention backward kernels: p = 2, t in {1, 4}, d in {64, 128}, m in {64, 128, 256} "
                 "(got p=%d t=%d d=%d m=%d)", s->p, s->t, s->d, s->m);
+  return LLOPS_OK;
+}
+
+// The gated causal form runs on the 32x32x16 segment kernels only.
+llops_status_t validate_gated(const llops_shape_t* s) {
+  LLOPS_TRY(validate(s, LLOPS_ENTRY_GATED_CAUSAL));
+  if (s->in_dtype != LLOPS_BF16)
+    return fail(LLOPS_ERR_UNSUPPORTED, "gated causal attention takes bf16 inputs only");
+  const llops::AttnShape a = attn_shape(s, true);
+  if (s->batch * s->heads > 0 && !llops::attn32_supported(a))
+    return fail(LLOPS_ERR_UNSUPPORTED,
+                "gated causal attention kernels: (m, dv) in {(256, 128), (128, 64), (64, 64)} "
+                "(got m=%d dv=%d)", s->m, s->dv);
   return LLOPS_OK;
 }
 
@@ -482,7 +513,8 @@ int32_t llops_profile_disarm(void) {
 }
 
 size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
-  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_LINATTN_BWD) return 0;
+  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_GATED_DECODE) return 0;
+  if (entry == LLOPS_ENTRY_GATED_CAUSAL && validate_gated(shape) != LLOPS_OK) return 0;
   if (entry == LLOPS_ENTRY_CAUSAL_BWD || entry == LLOPS_ENTRY_LINATTN_BWD) {
     const bool causal = entry == LLOPS_ENTRY_CAUSAL_BWD;
     if (validate_attn_bwd(shape, causal) != LLOPS_OK) return 0;
@@ -561,6 +593,55 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* s, const void* Q, c
                                         size_t ws_bytes, hipStream_t st) {
   return attention(s, true, Q, K, V, theta_q, theta_k, S0, z0, out, S_final, z_final, ws,
                    ws_bytes, st);
+}
+
+llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* s, const void* Q, const void* K,
+                                              const void* V, const void* theta_q,
+                                              const void* theta_k, const float* log_gate,
+                                              const float* S0, const float* z0, void* out,
+                                              float* S_final, float* z_final, void* ws,
+                                              size_t ws_bytes, hipStream_t st) {
+  LLOPS_TRY(validate_gated(s));
+  const int64_t BH = s->batch * s->heads;
+  if (BH == 0) return LLOPS_OK;
+  LLOPS_TRY(opt(S0, "S0"));
+  LLOPS_TRY(opt(z0, "z0"));
+  LLOPS_TRY(opt(S_final, "S_final"));
+  LLOPS_TRY(opt(z_final, "z_final"));
+  if (s->n == 0) {  // no tokens, no decay: the state passes through
+    if (S_final || z_final)
+      LLOPS_HIP(llops::launch_state_init(BH, s->m, s->dv, S0, z0, S_final, z_final, st),
+                "state_init");
+    return LLOPS_OK;
+  }
+  LLOPS_TRY(need(Q, "Q"));
+  LLOPS_TRY(need(K, "K"));
+  LLOPS_TRY(need(V, "V"));
+  LLOPS_TRY(need(theta_q, "theta_q"));
+  LLOPS_TRY(need(theta_k, "theta_k"));
+  LLOPS_TRY(need4(log_gate, "log_gate"));
+  LLOPS_TRY(need(out, "out"));
+  const WsLayout L = ws_layout(s, LLOPS_ENTRY_GATED_CAUSAL);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (!ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  LLOPS_TRY(opt(ws, "ws"));
+  char* w = static_cast<char*>(ws);
+  const llops::AttnShape a = attn_shape(s, true);
+  float* seg = reinterpret_cast<float*>(w + L.seg);
+  float* gl = reinterpret_cast<float*>(w + L.gl);
+  float* gseg = reinterpret_cast<float*>(w + L.gseg);
+  llops::FeatJob jobs[2] = {{Q, theta_q, w + L.phiq, w + L.pkq}, {K, theta_k, w + L.phik, w + L.pkk}};
+  LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, s->n, 1), jobs, 2, st), "featmap");
+  const uint16_t* pq = reinterpret_cast<const uint16_t*>(w + L.phiq);
+  const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);
+  const uint16_t* vv = static_cast<const uint16_t*>(V);
+  LLOPS_HIP(llops::launch_gate_cumsum32(BH, s->n, log_gate, gl, st), "gate_cumsum");
+  LLOPS_HIP(llops::launch_seg_state32_gated(a, pk, vv, gl, gseg, seg, st), "seg_state_gated");
+  LLOPS_HIP(llops::launch_seg_scan_gated(a, seg, gseg, S0, z0, S_final, z_final, st), "seg_scan");
+  LLOPS_HIP(llops::launch_attn_out32_gated(a, pq, pk, vv, gl, seg, static_cast<float*>(out), st),
+            "attn_out_gated");
+  return LLOPS_OK;
 }
 
 // Shared body of the causal and non-causal attention backward.
@@ -682,9 +763,10 @@ llops_status_t llops_linattn_bwd(const llops_shape_t* s, const void* Q, const vo
                        ws_bytes, st);
 }
 
-llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const void* k,
-                                 const void* v, const void* theta_q, const void* theta_k, float* S,
-                                 float* z, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+static llops_status_t decode_impl(const llops_shape_t* s, const void* q, const void* k,
+                                  const void* v, const void* theta_q, const void* theta_k,
+                                  const float* log_gate, float* S, float* z, void* out, void* ws,
+                                  size_t ws_bytes, hipStream_t st) {
   LLOPS_TRY(validate(s, LLOPS_ENTRY_DECODE));
   const int64_t BH = s->batch * s->heads;
   if (BH == 0) return LLOPS_OK;  // empty: pointers may be null
@@ -696,6 +778,7 @@ llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const vo
   LLOPS_TRY(need(S, "S"));
   LLOPS_TRY(need(z, "z"));
   LLOPS_TRY(need(out, "out"));
+  if (log_gate) LLOPS_TRY(need4(log_gate, "log_gate"));
   const WsLayout L = ws_layout(s, LLOPS_ENTRY_DECODE);
   if (ws_bytes < L.total)
     return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
@@ -715,9 +798,23 @@ llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const vo
     LLOPS_HIP(llops::launch_featmap_f32(fs, jobs, 2, st), "featmap");
   LLOPS_HIP(llops::launch_decode_state(BH, s->m, s->dv, fq, fk, v, bf16 ? 1 : 0, S, z,
                                        static_cast<float*>(out), s->normalize,
-                                       s->normalize ? s->delta : 0.f, st),
+                                       s->normalize ? s->delta : 0.f, log_gate, st),
             "decode_state");
   return LLOPS_OK;
+}
+
+llops_status_t llops_decode_step(const llops_shape_t* s, const void* q, const void* k,
+                                 const void* v, const void* theta_q, const void* theta_k, float* S,
+                                 float* z, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+  return decode_impl(s, q, k, v, theta_q, theta_k, nullptr, S, z, out, ws, ws_bytes, st);
+}
+
+llops_status_t llops_gated_decode_step(const llops_shape_t* s, const void* q, const void* k,
+                                       const void* v, const void* theta_q, const void* theta_k,
+                                       const float* log_gate, float* S, float* z, void* out,
+                                       void* ws, size_t ws_bytes, hipStream_t st) {
+  if (s && s->batch * s->heads > 0) LLOPS_TRY(need4(log_gate, "log_gate"));
+  return decode_impl(s, q, k, v, theta_q, theta_k, log_gate, S, z, out, ws, ws_bytes, st);
 }
 
 const char* llops_status_str(llops_status_t status) {

@@ -151,7 +151,8 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int nseg, int m, int dv,
                                                        const float* S0, const float* z0,
                                                        float* Sout, int64_t Sout_bh,
                                                        float* zout, int64_t zout_bh,
-                                                       int exclusive) {
+                                                       int exclusive,
+                                                       const float* __restrict__ gseg) {
   const int64_t per = static_cast<int64_t>(m) * dv + m;
   const int64_t mdv = static_cast<int64_t>(m) * dv;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -164,10 +165,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int nseg, int m, int dv,
     if (z0) acc = z0[bh * m + (e - mdv)];
   }
   float* p = seg + bh * nseg * per + e;
-  for (int gi = 0; gi < nseg; ++gi, p += per) {
-    const float x = *p;
-    if (exclusive) *p = acc;
-    acc += x;
+  if (gseg) {  // gated: the prefix decays through each segment before its own sum is added
+    const float* gs = gseg + bh * nseg;
+    for (int gi = 0; gi < nseg; ++gi, p += per) {
+      const float x = *p;
+      if (exclusive) *p = acc;
+      acc = fmaf(__expf(gs[gi]), acc, x);
+    }
+  } else {
+    for (int gi = 0; gi < nseg; ++gi, p += per) {
+      const float x = *p;
+      if (exclusive) *p = acc;
+      acc += x;
+    }
   }
   if (e < mdv) {
     if (Sout) Sout[bh * Sout_bh + e] = acc;
@@ -563,7 +573,18 @@ hipError_t launch_seg_scan(const AttnShape& s, float* seg, const float* S0, cons
   }
   dim3 grid(static_cast<unsigned>((per + 255) / 256), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH("seg_scan", st, seg_scan_kernel, grid, dim3(256), 0, st, s.nseg, s.m, s.dv, seg, S0, z0,
-                     Sout, Sb, zout, zb, exclusive);
+                     Sout, Sb, zout, zb, exclusive, static_cast<const float*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_scan_gated(const AttnShape& s, float* seg, const float* gseg,
+                                 const float* S0, const float* z0, float* Sout, float* zout,
+                                 hipStream_t st) {
+  const int64_t mdv = static_cast<int64_t>(s.m) * s.dv;
+  const int64_t per = mdv + s.m;
+  dim3 grid(static_cast<unsigned>((per + 255) / 256), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("seg_scan", st, seg_scan_kernel, grid, dim3(256), 0, st, s.nseg, s.m, s.dv, seg, S0,
+               z0, Sout, mdv, zout, static_cast<int64_t>(s.m), 1, gseg);
   return hipGetLastError();
 }
 

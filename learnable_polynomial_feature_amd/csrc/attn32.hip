@@ -17,6 +17,18 @@
 // contract over tokens are read with ds_read_b64_tr_b16 (transposing LDS
 // reads), so no transposed copy is ever stored.
 //
+// Gated variant (causal only): a per-token scalar decay a_i = exp(g_i)
+// scales the whole state before token i is added, S_i = a_i S_{i-1} +
+// phi_K,i v_i^T (the forgetting gates the LLoPS notes name as future work,
+// limitations and outlook, with Mamba2's semiseparable form as the example).
+// With L the inclusive sum of g inside each 32-token chunk (gate_cumsum32
+// below) and T its value at the chunk's last token, a chunk contributes
+//   intra: A_qk = exp(L_q - L_k) phi_Q,q . phi_K,k  (k <= q),
+//   inter: exp(L_q) phi_Q,q S_prev,
+//   carry: S = exp(T) S_prev + phi_K^T diag(exp(T - L_k)) V,
+// and every exponent is <= 0 when g <= 0, so no factor overflows. The
+// per-chunk L values ride in LDS behind the chunk's rows.
+//
 // Fragment conventions for v_mfma_f32_32x32x16_bf16 (lane l, c = l % 32,
 // hh = l / 32): an accumulator element 4i+e holds row 8i + 4hh + e of column
 // c. Taken as an operand, rows 0..15 of a tile (elements 0..7) put k-values
@@ -36,7 +48,52 @@ struct Seg32Args {
   int nseg;
   int normalize;
   float delta;
+  const float* gl;   // gated: chunk-local inclusive sums of log gates [BH][n]
+  float* gseg;       // gated pass 1: per-segment sum of log gates [BH][nseg]
 };
+
+constexpr int kGL = 2 * kC;  // LDS slots (uint16) of one chunk's 32 fp32 gate sums
+
+// Row stride of the gate sums L [BH][n rounded up to 32]: every chunk's 32
+// values start on a 128-byte boundary.
+__host__ __device__ __forceinline__ int64_t gl_ld(int64_t n) { return (n + kC - 1) / kC * kC; }
+
+// Scale the 8 bf16 values of an operand fragment by s[0..7] (fp32 products,
+// rounded back to bf16 to nearest even).
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* s) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = pack_bf16x2(__uint_as_float(u[q] << 16) * s[2 * q],
+                       __uint_as_float(u[q] & 0xFFFF0000u) * s[2 * q + 1]);
+  return as_bf16x8(r);
+}
+
+// Gate sums of the 16 tokens 8i + 4hh + e (i, e < 4) this lane's fragments
+// cover (accumulator rows, P16 operand k-values), element 4i + e.
+__device__ __forceinline__ void gate_rows(const float* gls, int hh, float (&L)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(gls + 8 * i + 4 * hh);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) L[4 * i + e] = x[e];
+  }
+}
+
+// Carry weights w_k = exp(T - L_k) of this lane's 16 tokens, element 4i + e
+// (0 past the chunk's valid rows); elements 8ks..8ks+7 line up with the P16
+// k-values of the ks-th V fragment of the chunk.
+__device__ __forceinline__ void gate_carry(const float* gls, int hh, float T, int valid,
+                                           float (&wv)[16]) {
+  float L[16];
+  gate_rows(gls, hh, L);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int tok = 8 * (k >> 2) + 4 * hh + (k & 3);
+    wv[k] = tok < valid ? __expf(T - L[k]) : 0.f;
+  }
+}
 
 template <int M, int DV>
 struct Seg32Geom {
@@ -56,14 +113,14 @@ struct Seg32Geom {
 // ============================================================================
 // Pass 1: per-segment (dS, dz) = (phi_K^T V, phi_K^T 1)
 // ============================================================================
-template <int M, int DV>
+template <int M, int DV, bool GATED>
 __global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                                                      const uint16_t* __restrict__ v,
                                                      float* __restrict__ seg) {
   using G = Seg32Geom<M, DV>;
   constexpr int FT = G::FT, MP = G::MP, VP = G::VP, NT = G::NT;
-  constexpr int BUF = kC * MP + kC * VP;  // phi_K and V only
+  constexpr int BUF = kC * MP + kC * VP + (GATED ? kGL : 0);  // phi_K, V [, gate sums]
   constexpr int LK = G::LPT_Q, LV = G::LPT_V;
   extern __shared__ __align__(16) uint16_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -84,6 +141,12 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
+  // gated: the chunk's 32 gate sums (128 bytes) come with the chunk, loaded
+  // by the first 8 lanes of wave 0 (every lane of that wave issues the load)
+  const __amdgpu_buffer_rsrc_t rsg =
+      make_rsrc(GATED ? a.gl + bh * gl_ld(a.n) + t0 : nullptr,
+                GATED ? static_cast<uint32_t>(gl_ld(seg_rows)) * 4u : 0u);
+  u32x4 rg = u32x4{0u, 0u, 0u, 0u};
   auto load = [&](int c, u32x4 (&rk)[LK], u32x4 (&rv)[LV]) {
     // piece idx of a chunk is 16 contiguous bytes at byte 16 * idx
 #pragma unroll
@@ -92,8 +155,10 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
 #pragma unroll
     for (int i = 0; i < LV; ++i)
       rv[i] = buf_ld16(rsv, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
+    if (GATED && w == 0) rg = buf_ld16(rsg, (lane & 7) * 16u, static_cast<uint32_t>(c) * (kC * 4u));
   };
   auto store = [&](uint16_t* buf, const u32x4 (&rk)[LK], const u32x4 (&rv)[LV]) {
+    if (GATED && w == 0 && lane < 8) st16(buf + kC * MP + kC * VP + lane * 8, rg);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
@@ -112,6 +177,8 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
 #pragma unroll
   for (int z = 0; z < G::ZT; ++z) Z[z] = zero16();
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  const int hh = lane >> 5;
+  float gsum = 0.f;  // gated: sum of this segment's log gates
 
   // one chunk: request chunk c+1 into the registers (clamped past the
   // end), run chunk c from LDS, move chunk c+1 into the other slot, barrier
@@ -123,9 +190,35 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
     // phi_K fragment reads run KD products ahead (pinned: the scheduler
     // would sink each next to its MFMA and expose the LDS latency)
     constexpr int NK = (kC / 16) * FT, KD = NK < 2 ? NK : 2;
-    bf16x8 vb[kC / 16], kf[KD];
+    bf16x8 vb[kC / 16], kf[KD], zb[kC / 16];
 #pragma unroll
-    for (int ks = 0; ks < kC / 16; ++ks) vb[ks] = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+    for (int ks = 0; ks < kC / 16; ++ks) {
+      vb[ks] = frag_tr(Vs, VP, ks * 16, w * 32, lane);
+      zb[ks] = ones;
+    }
+    if constexpr (GATED) {
+      // S <- exp(T) S + phi_K^T diag(exp(T - L)) V over this chunk
+      const float* gls = reinterpret_cast<const float*>(Vs + kC * VP);
+      const int64_t left = t1 - (t0 + static_cast<int64_t>(c) * kC);
+      const int valid = left < kC ? static_cast<int>(left) : kC;
+      const float T = gls[valid - 1];
+      float wv[16];
+      gate_carry(gls, hh, T, valid, wv);
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks) {
+        vb[ks] = scale_frag(vb[ks], wv + 8 * ks);
+        zb[ks] = as_bf16x8(u32x4{pack_bf16x2(wv[8 * ks + 0], wv[8 * ks + 1]),
+                                 pack_bf16x2(wv[8 * ks + 2], wv[8 * ks + 3]),
+                                 pack_bf16x2(wv[8 * ks + 4], wv[8 * ks + 5]),
+                                 pack_bf16x2(wv[8 * ks + 6], wv[8 * ks + 7])});
+      }
+      const float decay = __expf(T);
+#pragma unroll
+      for (int f = 0; f < FT; ++f) S[f] *= decay;
+#pragma unroll
+      for (int z = 0; z < G::ZT; ++z) Z[z] *= decay;
+      gsum += T;
+    }
 #pragma unroll
     for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FT) * 16, (i % FT) * 32, lane);
 #pragma unroll
@@ -135,7 +228,7 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
       if (idx + KD < NK) kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FT) * 16, ((idx + KD) % FT) * 32, lane);
       S[f] = mfma32x32x16(ka, vb[ks], S[f]);
       if ((f % G::NW) == (w % G::NW) && f / G::NW < G::ZT)
-        Z[f / G::NW] = mfma32x32x16(ka, ones, Z[f / G::NW]);
+        Z[f / G::NW] = mfma32x32x16(ka, zb[ks], Z[f / G::NW]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (c + 1 < nch) store(smem + ((c + 1) & 1) * BUF, rk, rv);
@@ -146,8 +239,9 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   store(smem, rk, rv);
   __syncthreads();
   for (int c = 0; c < nch; ++c) step(c);
+  if (GATED && tid == 0) a.gseg[bh * a.nseg + gseg] = gsum;
   float* out = seg + (bh * a.nseg + gseg) * (static_cast<int64_t>(M) * DV + M);
-  const int c32 = lane & 31, hh = lane >> 5;
+  const int c32 = lane & 31;
 #pragma unroll
   for (int f = 0; f < FT; ++f)
 #pragma unroll
@@ -180,7 +274,7 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
 // values, inside its feature half). Chunks are prefetched two ahead into two
 // alternating register sets; the exchange areas alternate by chunk parity, so
 // one barrier per chunk orders everything.
-template <int M, int DV>
+template <int M, int DV, bool GATED>
 struct Out32Geom {
   static constexpr int NWD = DV / 32;     // value-column tiles
   static constexpr int NW = 2 * NWD;      // waves
@@ -191,7 +285,7 @@ struct Out32Geom {
   // per 16 lanes, conflict-free when rows shift by 8 banks); phi_Q only in
   // row order (b64/b128 over 16 rows, conflict-free when rows shift by 4)
   static constexpr int QPAD = M + 8, MP = M + 16, VP = DV + 16;
-  static constexpr int BUF = kC * QPAD + kC * MP + kC * VP;
+  static constexpr int BUF = kC * QPAD + kC * MP + kC * VP + (GATED ? kGL : 0);  // + gate sums
   static constexpr int QP = kC * M / 8;   // 16-byte pieces of one phi chunk
   static constexpr int VPc = kC * DV / 8;
   // LDS after the two chunk buffers, per parity: xo [NW][8][64] fp32,
@@ -203,14 +297,15 @@ struct Out32Geom {
   static_assert(QP % NT == 0 && VPc % NT == 0, "chunk pieces split evenly over the threads");
 };
 
-template <int M, int DV, bool CAUSAL>
+template <int M, int DV, bool CAUSAL, bool GATED>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
                 int64_t st_bh, float* __restrict__ out) {
-  using G = Out32Geom<M, DV>;
+  using G = Out32Geom<M, DV, GATED>;
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
+  static_assert(CAUSAL || !GATED, "the gated form is causal");
   constexpr int NP = CAUSAL ? 2 * QP + G::VPc : QP;  // pieces staged per chunk
   constexpr int LPT = NP / NT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -258,7 +353,13 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
   // contiguous bytes each; a thread's pieces t + i*NT never straddle two
   // tensors, so the selection folds away
-  auto load = [&](int c, u32x4 (&r)[LPT]) {
+  // gated: the chunk's 32 gate sums (128 bytes), loaded by wave 0 and
+  // stored by its first 8 lanes behind the chunk's V rows
+  const __amdgpu_buffer_rsrc_t rsg =
+      make_rsrc(GATED ? a.gl + bh * gl_ld(a.n) + t0 : nullptr,
+                GATED ? static_cast<uint32_t>(gl_ld(seg_rows)) * 4u : 0u);
+  auto load = [&](int c, u32x4 (&r)[LPT], u32x4& rg) {
+    if (GATED && w == 0) rg = buf_ld16(rsg, (lane & 7) * 16u, static_cast<uint32_t>(c) * (kC * 4u));
     int t = tid;  // opaque: per-piece offsets are rebuilt, not kept live
     asm volatile("" : "+v"(t));
 #pragma unroll
@@ -272,7 +373,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         r[i] = buf_ld16(rsv, (p - 2 * QP) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
     }
   };
-  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT]) {
+  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT], const u32x4& rg) {
+    if (GATED && w == 0 && lane < 8) st16(buf + kC * QPAD + kC * MP + kC * VP + lane * 8, rg);
     int t = tid;
     asm volatile("" : "+v"(t));
 #pragma unroll
@@ -296,8 +398,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // LDS; unconditional, clamped, so wait counts stay static), compute chunk
   // c, move chunk c+1 from `wr` into the other LDS slot, publish partials,
   // barrier, finish this wave's rows
-  auto step = [&](int c, u32x4 (&ld)[LPT], const u32x4 (&wr)[LPT]) {
-    load(c + 2 < nch ? c + 2 : nch - 1, ld);
+  auto step = [&](int c, u32x4 (&ld)[LPT], u32x4& ldg, const u32x4 (&wr)[LPT], const u32x4& wrg) {
+    load(c + 2 < nch ? c + 2 : nch - 1, ld, ldg);
     // Lane-dependent bases pass through an empty asm so the compiler cannot
     // hoist every derived LDS address and mask compare out of the chunk loop
     // (kept live across iterations they exhaust the 256-register budget).
@@ -315,9 +417,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     float* part = ex + G::XO;
     float* rsum = part + G::PART;
     const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+    // gated: the chunk's gate sums L sit behind its V rows
+    auto gate_sums = [&]() { return reinterpret_cast<const float*>(Vs + kC * VP); };
 
     f32x16 O = zero16(), D = zero16();
     bf16x8 afr[2];
+    auto intra = [&]() {
     if (CAUSAL && half == 0) {
       // masked A^T = phi_K phi_Q^T (keys x queries)
       // fragment reads run AD k-steps ahead of the MFMA chain (pinned: the
@@ -341,11 +446,24 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         At = mfma32x32x16(ka, qb, At);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if constexpr (GATED) {
+        // A_qk = exp(L_q - L_k) phi_Q,q . phi_K,k for key k <= query q
+        const float* gls = gate_sums();
+        float Lr[16];
+        gate_rows(gls, hh, Lr);
+        const float Lq = gls[c32];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (8 * i + e > lim) At[4 * i + e] = 0.f;  // key after query
+          for (int e = 0; e < 4; ++e)
+            At[4 * i + e] = 8 * i + e > lim ? 0.f : At[4 * i + e] * __expf(Lq - Lr[4 * i + e]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (8 * i + e > lim) At[4 * i + e] = 0.f;  // key after query
+      }
       afr[0] = acc_frag(At, 0);
       afr[1] = acc_frag(At, 1);
       if (a.normalize && dvt == 0) {  // row sums of the rounded weights A V uses
@@ -364,10 +482,10 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       for (int ks = 0; ks < kC / 16; ++ks)
         O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    };
     // partial phi_Q S over this wave's feature half; phi_Q . z over its z
     // tile. The phi_Q fragment reads run QD products ahead (pinned).
-    {
+    auto inter = [&]() {
       constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
       bf16x8 qf[QD];
 #pragma unroll
@@ -381,6 +499,26 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    if constexpr (GATED) {
+      // the carried state reaches query q with weight exp(L_q): scale the
+      // inter-chunk rows before the intra-chunk product adds its own
+      inter();
+      __builtin_amdgcn_sched_barrier(0);
+      float Lr[16];
+      gate_rows(gate_sums(), hh, Lr);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float sc = __expf(Lr[k]);
+        O[k] *= sc;
+        D[k] *= sc;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      intra();
+    } else {
+      intra();
+      __builtin_amdgcn_sched_barrier(0);
+      inter();
     }
     __builtin_amdgcn_sched_barrier(0);
     // publish: the 16 rows the partner wave finishes, and the z partial
@@ -401,9 +539,32 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       bf16x8 kf[KD];
 #pragma unroll
       for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FH) * 16, (f0 + i % FH) * 32, lane);
-      bf16x8 vb[kC / 16];
+      bf16x8 vb[kC / 16], zb[kC / 16];
 #pragma unroll
-      for (int ks = 0; ks < kC / 16; ++ks) vb[ks] = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
+      for (int ks = 0; ks < kC / 16; ++ks) {
+        vb[ks] = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
+        zb[ks] = ones;
+      }
+      if constexpr (GATED) {
+        // S <- exp(T) S + phi_K^T diag(exp(T - L)) V, z likewise
+        const float* gls = gate_sums();
+        const int valid = t1 - c0 < kC ? static_cast<int>(t1 - c0) : kC;  // rows in range
+        const float T = gls[valid - 1];
+        float wv[16];
+        gate_carry(gls, hh, T, valid, wv);
+#pragma unroll
+        for (int ks = 0; ks < kC / 16; ++ks) {
+          vb[ks] = scale_frag(vb[ks], wv + 8 * ks);
+          zb[ks] = as_bf16x8(u32x4{pack_bf16x2(wv[8 * ks + 0], wv[8 * ks + 1]),
+                                   pack_bf16x2(wv[8 * ks + 2], wv[8 * ks + 3]),
+                                   pack_bf16x2(wv[8 * ks + 4], wv[8 * ks + 5]),
+                                   pack_bf16x2(wv[8 * ks + 6], wv[8 * ks + 7])});
+        }
+        const float decay = __expf(T);
+#pragma unroll
+        for (int j = 0; j < FH; ++j) S[j] *= decay;
+        Z *= decay;
+      }
 #pragma unroll
       for (int idx = 0; idx < NK; ++idx) {
         const int ks = idx / FH, j = idx % FH;
@@ -411,12 +572,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         if (idx + KD < NK)
           kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FH) * 16, (f0 + (idx + KD) % FH) * 32, lane);
         S[j] = mfma32x32x16(ka, vb[ks], S[j]);
-        if (has_z && j == zj) Z = mfma32x32x16(ka, ones, Z);
+        if (has_z && j == zj) Z = mfma32x32x16(ka, zb[ks], Z);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < nch) store(smem + ((c + 1) & 1) * G::BUF, wr);
+    if (c + 1 < nch) store(smem + ((c + 1) & 1) * G::BUF, wr, wrg);
     __syncthreads();
     // finish rows 16*half .. +15: own part + partner's part, normalise, store.
     // All LDS reads are issued before any arithmetic and the normalisation
@@ -470,9 +631,9 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     }
   };
 
-  u32x4 rA[LPT], rB[LPT];
-  load(0, rA);
-  load(nch > 1 ? 1 : 0, rB);
+  u32x4 rA[LPT], rB[LPT], gA = u32x4{0u, 0u, 0u, 0u}, gB = gA;
+  load(0, rA, gA);
+  load(nch > 1 ? 1 : 0, rB, gB);
   // The prefix state must be in registers before the chunk loop: a wait for
   // it left to the compiler lands inside the loop and drains the chunk
   // prefetch on every chunk (and the scheduler sinks the state loads below a
@@ -481,40 +642,64 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < FH; ++j) asm volatile("" : "+v"(S[j]));
   asm volatile("" : "+v"(Z));
-  store(smem, rA);
+  store(smem, rA, gA);
   __syncthreads();
   for (int c = 0; c < nch; c += 2) {
-    step(c, rA, rB);
-    if (c + 1 < nch) step(c + 1, rB, rA);
+    step(c, rA, gA, rB, gB);
+    if (c + 1 < nch) step(c + 1, rB, gB, rA, gA);
   }
 }
 
-template <int M, int DV>
-hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, float* seg,
-                          hipStream_t st) {
+// Chunk-local inclusive sums of the log gates: L[bh][t] = sum of g[bh][t']
+// over t' from the start of t's 32-token chunk (chunks start at multiples of
+// 32) to t, rows gl_ld(n) apart. The padding t in [n, gl_ld(n)) is written
+// too (g taken as 0 there, so it repeats the last sum): the passes read whole
+// 32-token chunks and every value they read is finite. One 32-lane group
+// scans one chunk with lane shuffles.
+__global__ __launch_bounds__(256) void gate_cumsum32(int64_t n, int64_t nch, int64_t total,
+                                                     const float* __restrict__ g,
+                                                     float* __restrict__ L) {
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  const int64_t bh = id / nch, tok = (id % nch) * kC + l;
+  const bool live = id < total;
+  float x = live && tok < n ? g[bh * n + tok] : 0.f;
+#pragma unroll
+  for (int o = 1; o < kC; o <<= 1) {
+    const float y = __shfl_up(x, o, kC);
+    if (l >= o) x += y;
+  }
+  if (live) L[bh * nch * kC + tok] = x;
+}
+
+template <int M, int DV, bool GATED>
+hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, const float* gl,
+                          float* gseg, float* seg, hipStream_t st) {
   using G = Seg32Geom<M, DV>;
-  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta};
-  const size_t lds = 2ull * (kC * G::MP + kC * G::VP) * sizeof(uint16_t);
-  auto* kern = seg_state32<M, DV>;
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, gseg};
+  const size_t lds = 2ull * (kC * G::MP + kC * G::VP + (GATED ? kGL : 0)) * sizeof(uint16_t);
+  auto* kern = seg_state32<M, DV, GATED>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
-  LLOPS_LAUNCH("seg_state_bf16", st, kern, grid, dim3(G::NT), lds, st, a, k, v, seg);
+  LLOPS_LAUNCH(GATED ? "seg_state_gated" : "seg_state_bf16", st, kern, grid, dim3(G::NT), lds, st,
+               a, k, v, seg);
   return hipGetLastError();
 }
 
-template <int M, int DV, bool CAUSAL>
+template <int M, int DV, bool CAUSAL, bool GATED>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
-                        const uint16_t* v, const float* state, int64_t ss, int64_t sb, float* out,
-                        hipStream_t st) {
-  using G = Out32Geom<M, DV>;
-  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta};
+                        const uint16_t* v, const float* gl, const float* state, int64_t ss,
+                        int64_t sb, float* out, hipStream_t st) {
+  using G = Out32Geom<M, DV, GATED>;
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
   const size_t lds = G::lds_bytes();
-  auto* kern = attn_out32<M, DV, CAUSAL>;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
-  LLOPS_LAUNCH("attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st, a, q, k, v, state, ss, sb, out);
+  LLOPS_LAUNCH(GATED ? "attn_out_gated" : "attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st,
+               a, q, k, v, state, ss, sb, out);
   return hipGetLastError();
 }
 
@@ -539,9 +724,9 @@ bool attn32_supported(const AttnShape& s) {
 hipError_t launch_seg_state32(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
                               float* seg, hipStream_t st) {
   switch (key32(s)) {
-    case 256128: return launch_state_t<256, 128>(s, phik, v, seg, st);
-    case 128064: return launch_state_t<128, 64>(s, phik, v, seg, st);
-    case 64064: return launch_state_t<64, 64>(s, phik, v, seg, st);
+    case 256128: return launch_state_t<256, 128, false>(s, phik, v, nullptr, nullptr, seg, st);
+    case 128064: return launch_state_t<128, 64, false>(s, phik, v, nullptr, nullptr, seg, st);
+    case 64064: return launch_state_t<64, 64, false>(s, phik, v, nullptr, nullptr, seg, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -549,13 +734,46 @@ hipError_t launch_seg_state32(const AttnShape& s, const uint16_t* phik, const ui
 hipError_t launch_attn_out32(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
                              const uint16_t* v, const float* state, int64_t st_seg,
                              int64_t st_bh, float* out, hipStream_t st) {
+  const float* g = nullptr;
   switch (key32(s) * 2 + (s.causal ? 1 : 0)) {
-    case 256128 * 2 + 1: return launch_out_t<256, 128, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
-    case 256128 * 2: return launch_out_t<256, 128, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
-    case 128064 * 2 + 1: return launch_out_t<128, 64, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
-    case 128064 * 2: return launch_out_t<128, 64, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
-    case 64064 * 2 + 1: return launch_out_t<64, 64, true>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
-    case 64064 * 2: return launch_out_t<64, 64, false>(s, phiq, phik, v, state, st_seg, st_bh, out, st);
+    case 256128 * 2 + 1: return launch_out_t<256, 128, true, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    case 256128 * 2: return launch_out_t<256, 128, false, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    case 128064 * 2 + 1: return launch_out_t<128, 64, true, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    case 128064 * 2: return launch_out_t<128, 64, false, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    case 64064 * 2 + 1: return launch_out_t<64, 64, true, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    case 64064 * 2: return launch_out_t<64, 64, false, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L, hipStream_t st) {
+  const int64_t nch = (n + kC - 1) / kC, total = BH * nch;
+  if (total == 0) return hipSuccess;
+  if ((total + 7) / 8 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("gate_cumsum32", st, gate_cumsum32, dim3(static_cast<unsigned>((total + 7) / 8)),
+               dim3(256), 0, st, n, nch, total, g, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_state32_gated(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
+                                    const float* gl, float* gseg, float* seg, hipStream_t st) {
+  switch (key32(s)) {
+    case 256128: return launch_state_t<256, 128, true>(s, phik, v, gl, gseg, seg, st);
+    case 128064: return launch_state_t<128, 64, true>(s, phik, v, gl, gseg, seg, st);
+    case 64064: return launch_state_t<64, 64, true>(s, phik, v, gl, gseg, seg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_out32_gated(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
+                                   const uint16_t* v, const float* gl, const float* state,
+                                   float* out, hipStream_t st) {
+  if (!s.causal) return hipErrorInvalidValue;
+  const int64_t per = static_cast<int64_t>(s.m) * s.dv + s.m;
+  switch (key32(s)) {
+    case 256128: return launch_out_t<256, 128, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
+    case 128064: return launch_out_t<128, 64, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
+    case 64064: return launch_out_t<64, 64, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,7 +1,10 @@
 // LLoPS single-token decode step on the recurrent state (LLoPS paper Sec. 1:
 // linear attention as a recurrent memory state updated token by token).
 //   S += phi_K(k) v^T;  z += phi_K(k);  out = phi_Q(q)^T S [/(phi_Q(q)^T z + delta)]
-// The state update precedes the read (inclusive of the new token).
+// The state update precedes the read (inclusive of the new token). The gated
+// form first scales S and z by a = exp(g) for a per-(batch, head) log gate g
+// (the forgetting gates the LLoPS notes name as future work, limitations and
+// outlook).
 //
 // One workgroup per (batch, head). The m x dv fp32 state is streamed once:
 // each thread owns 4 adjacent columns (16-byte non-temporal loads/stores) of
@@ -47,13 +50,13 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
 constexpr int kDecodeMaxM = 1024;  // feature count the vector path stages in LDS
 
 // Vector path: dv % 4 == 0, (dv / 4) divides 256, m <= kDecodeMaxM.
-template <bool VBF16>
+template <bool VBF16, bool GATED>
 __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const float* __restrict__ phiq,
                                                         const float* __restrict__ phik,
                                                         const void* __restrict__ v,
                                                         float* __restrict__ S, float* __restrict__ z,
                                                         float* __restrict__ out, int normalize,
-                                                        float delta) {
+                                                        float delta, const float* __restrict__ lg) {
   __shared__ float4 red4[256];
   __shared__ float red[4];
   const int64_t bh = blockIdx.x;
@@ -64,6 +67,7 @@ __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const flo
   const float* fk = phik + bh * m;
   float* Sb = S + bh * static_cast<int64_t>(m) * dv;
   const float4 vv = load_v4<VBF16>(v, bh * dv + cg * 4);
+  const float ga = GATED ? __expf(lg[bh]) : 1.f;  // state decay of this (batch, head)
   // phi_k and phi_q of this (batch, head) in LDS: the row loop then issues
   // only the state's vector loads and stores
   __shared__ float fks[kDecodeMaxM], fqs[kDecodeMaxM];
@@ -74,6 +78,7 @@ __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const flo
   __syncthreads();
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   auto update = [&](f32x4& st, float kf, float qf) {
+    if (GATED) st *= ga;
     st[0] = fmaf(kf, vv.x, st[0]);
     st[1] = fmaf(kf, vv.y, st[1]);
     st[2] = fmaf(kf, vv.z, st[2]);
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const flo
   // z update and the normaliser dot product
   float dpart = 0.f;
   for (int f = tid; f < m; f += 256) {
-    const float zn = z[bh * m + f] + fk[f];
+    const float zn = (GATED ? ga * z[bh * m + f] : z[bh * m + f]) + fk[f];
     z[bh * m + f] = zn;
     dpart = fmaf(fq[f], zn, dpart);
   }
@@ -144,22 +149,23 @@ __global__ __launch_bounds__(256) void decode_state_vec(int m, int dv, const flo
 }
 
 // Generic path: any dv (one thread per column, rows split over 256/dv groups).
-template <bool VBF16>
+template <bool VBF16, bool GATED>
 __global__ __launch_bounds__(256) void decode_state_gen(int m, int dv, const float* __restrict__ phiq,
                                                         const float* __restrict__ phik,
                                                         const void* __restrict__ v,
                                                         float* __restrict__ S, float* __restrict__ z,
                                                         float* __restrict__ out, int normalize,
-                                                        float delta) {
+                                                        float delta, const float* __restrict__ lg) {
   __shared__ float red[4];
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
   const float* fq = phiq + bh * m;
   const float* fk = phik + bh * m;
   float* Sb = S + bh * static_cast<int64_t>(m) * dv;
+  const float ga = GATED ? __expf(lg[bh]) : 1.f;
   float dpart = 0.f;
   for (int f = tid; f < m; f += 256) {
-    const float zn = z[bh * m + f] + fk[f];
+    const float zn = (GATED ? ga * z[bh * m + f] : z[bh * m + f]) + fk[f];
     z[bh * m + f] = zn;
     dpart = fmaf(fq[f], zn, dpart);
   }
@@ -168,7 +174,8 @@ __global__ __launch_bounds__(256) void decode_state_gen(int m, int dv, const flo
     const float vc = load_v1<VBF16>(v, bh * dv + c);
     float acc = 0.f;
     for (int f = 0; f < m; ++f) {
-      const float s = fmaf(fk[f], vc, Sb[static_cast<int64_t>(f) * dv + c]);
+      const float s0 = Sb[static_cast<int64_t>(f) * dv + c];
+      const float s = fmaf(fk[f], vc, GATED ? ga * s0 : s0);
       Sb[static_cast<int64_t>(f) * dv + c] = s;
       acc = fmaf(fq[f], s, acc);
     }
@@ -176,31 +183,43 @@ __global__ __launch_bounds__(256) void decode_state_gen(int m, int dv, const flo
   }
 }
 
-}  // namespace
 
-hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq, const float* phik,
-                               const void* v, int v_bf16, float* S, float* z, float* out,
-                               int normalize, float delta, hipStream_t st) {
-  if (BH <= 0) return hipSuccess;
-  if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
+template <bool GATED>
+hipError_t launch_decode_t(int64_t BH, int m, int dv, const float* phiq, const float* phik,
+                           const void* v, int v_bf16, float* S, float* z, float* out,
+                           int normalize, float delta, const float* lg, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(BH));
   const bool vec = (dv % 4 == 0) && (dv / 4 <= 256) && (256 % (dv / 4) == 0) && m <= kDecodeMaxM;
   if (vec) {
     if (v_bf16)
-      LLOPS_LAUNCH("decode_state", st, decode_state_vec<true>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
-                         z, out, normalize, delta);
+      LLOPS_LAUNCH("decode_state", st, (decode_state_vec<true, GATED>), grid, dim3(256), 0, st, m, dv,
+                   phiq, phik, v, S, z, out, normalize, delta, lg);
     else
-      LLOPS_LAUNCH("decode_state", st, decode_state_vec<false>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
-                         z, out, normalize, delta);
+      LLOPS_LAUNCH("decode_state", st, (decode_state_vec<false, GATED>), grid, dim3(256), 0, st, m,
+                   dv, phiq, phik, v, S, z, out, normalize, delta, lg);
   } else {
     if (v_bf16)
-      LLOPS_LAUNCH("decode_state", st, decode_state_gen<true>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
-                         z, out, normalize, delta);
+      LLOPS_LAUNCH("decode_state", st, (decode_state_gen<true, GATED>), grid, dim3(256), 0, st, m, dv,
+                   phiq, phik, v, S, z, out, normalize, delta, lg);
     else
-      LLOPS_LAUNCH("decode_state", st, decode_state_gen<false>, grid, dim3(256), 0, st, m, dv, phiq, phik, v, S,
-                         z, out, normalize, delta);
+      LLOPS_LAUNCH("decode_state", st, (decode_state_gen<false, GATED>), grid, dim3(256), 0, st, m,
+                   dv, phiq, phik, v, S, z, out, normalize, delta, lg);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq, const float* phik,
+                               const void* v, int v_bf16, float* S, float* z, float* out,
+                               int normalize, float delta, const float* log_gate, hipStream_t st) {
+  if (BH <= 0) return hipSuccess;
+  if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (log_gate)
+    return launch_decode_t<true>(BH, m, dv, phiq, phik, v, v_bf16, S, z, out, normalize, delta,
+                                 log_gate, st);
+  return launch_decode_t<false>(BH, m, dv, phiq, phik, v, v_bf16, S, z, out, normalize, delta,
+                                nullptr, st);
 }
 
 }  // namespace llops

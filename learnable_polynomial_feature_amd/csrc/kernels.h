@@ -124,11 +124,28 @@ hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uin
                              const uint16_t* v, const float* state, int64_t state_seg_stride,
                              int64_t state_bh_stride, float* out, hipStream_t st);
 
-// Decode: per (b, h): S += phik v^T; z += phik; out = phiq^T S [/(phiq^T z + delta)].
+// Gated causal passes (per-token log gates g [BH][n], decay exp(g)), on the
+// 32x32x16 kernels' shapes. gate_cumsum32 writes L = the inclusive sum of g
+// inside each 32-token chunk; pass 1 writes the per-segment sums of g to
+// gseg [BH][nseg] next to the decayed segment states; launch_seg_scan with
+// gseg carries the prefix through each segment's decay; pass 2 reads seg.
+hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L, hipStream_t st);
+hipError_t launch_seg_state32_gated(const AttnShape& a, const uint16_t* phik, const uint16_t* v,
+                                    const float* gl, float* gseg, float* seg, hipStream_t st);
+hipError_t launch_attn_out32_gated(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
+                                   const uint16_t* v, const float* gl, const float* state,
+                                   float* out, hipStream_t st);
+// Causal scan with per-segment decays: prefix_{g+1} = exp(gseg[g]) prefix_g + seg[g].
+hipError_t launch_seg_scan_gated(const AttnShape& a, float* seg, const float* gseg,
+                                 const float* S0, const float* z0, float* S_tot, float* z_tot,
+                                 hipStream_t st);
+
+// Decode: per (b, h): S = a S + phik v^T; z = a z + phik; out = phiq^T S [/(phiq^T z + delta)]
+// with a = exp(log_gate[b, h]), or a = 1 when log_gate is null.
 hipError_t launch_decode_state(int64_t BH, int m, int dv, const float* phiq,
                                const float* phik, const void* v, int v_bf16, float* S,
                                float* z, float* out, int normalize, float delta,
-                               hipStream_t st);
+                               const float* log_gate, hipStream_t st);
 
 // Copies (S0, z0) or zeros into (S, z): used when n = 0.
 hipError_t launch_state_init(int64_t BH, int m, int dv, const float* S0, const float* z0,

@@ -16,6 +16,9 @@ Distributions (the five workloads the hot path is measured on):
   Theta ~ N(0, 1/d), i.e. standard deviation 1/sqrt(d), one draw per head
   dphi  ~ N(0,1): the upstream gradient handed to the feature-map backward
   dO    ~ N(0,1): the upstream gradient of the attention output (float32)
+  log gate g = log(sigmoid(u)), u ~ N(mu, 1) (float32, never rounded): a
+        per-token state decay exp(g) in (0, 1); mu = 4 puts the median decay
+        near 0.982, a retention-biased forgetting gate
 Draws are float32; bf16 workloads round to bf16 with round-to-nearest-even and
 keep the rounded values in float32 arrays (exactly representable), so the GPU
 receives them losslessly and the oracle sees the identical numbers.
@@ -33,6 +36,7 @@ _T_Q, _T_K, _T_V, _T_THQ, _T_THK = 1, 2, 3, 4, 5
 _T_PRE_K, _T_PRE_V, _T_STEP_Q, _T_STEP_K, _T_STEP_V = 6, 7, 8, 9, 10
 _T_DPHI = 11
 _T_DOUT = 12
+_T_GATE, _T_STEP_GATE = 13, 14
 
 
 @dataclasses.dataclass(frozen=True)
@@ -158,6 +162,36 @@ def dphi_slice(w: Workload, b: int, h: int, bf16: bool = False) -> np.ndarray:
 def dout_slice(w: Workload, b: int, h: int) -> np.ndarray:
     """One (b, h) slice [n, dv] of the attention output's upstream gradient."""
     return _normal(w.seed, _T_DOUT, (b, h), (w.n, w.dv))
+
+
+def _log_sigmoid(u: np.ndarray) -> np.ndarray:
+    # log(1 / (1 + exp(-u))) without overflow for large |u|
+    u64 = u.astype(np.float64)
+    return (np.minimum(u64, 0.0) - np.log1p(np.exp(-np.abs(u64)))).astype(np.float32)
+
+
+def gate_slice(w: Workload, b: int, h: int, n: int | None = None, mu: float = 4.0) -> np.ndarray:
+    """One (b, h) slice [n] of per-token log gates, log(sigmoid(N(mu, 1)))."""
+    n = w.n if n is None else n
+    return _log_sigmoid(_normal(w.seed, _T_GATE, (b, h), (n,)) + np.float32(mu))
+
+
+def log_gates(w: Workload, heads: list[int] | None = None, batches: list[int] | None = None,
+              mu: float = 4.0) -> np.ndarray:
+    """Log gates [B', H', n] float32 for the selected batch rows and heads."""
+    heads = list(range(w.heads)) if heads is None else list(heads)
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    g = np.empty((len(batches), len(heads), w.n), np.float32)
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            g[bi, hi] = gate_slice(w, b, h, mu=mu)
+    return g
+
+
+def decode_step_gates(w: Workload, step: int, mu: float = 4.0) -> np.ndarray:
+    """Step ``step``'s log gates [B, H], log(sigmoid(N(mu, 1)))."""
+    return _log_sigmoid(_normal(w.seed, _T_STEP_GATE, (step,), (w.batch, w.heads))
+                        + np.float32(mu))
 
 
 def dout(w: Workload, heads: list[int] | None = None,

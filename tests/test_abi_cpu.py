@@ -361,3 +361,71 @@ def test_noncausal_bwd_workspace_below_causal(L):
     c = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD)
     nc = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_LINATTN_BWD)
     assert 0 < nc < c
+
+
+# ---- gated causal attention and gated decode -------------------------------
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(in_dtype=_lib.F32), 2), (dict(m=96), 2), (dict(dv=32), 2), (dict(m=256, dv=64), 2),
+    (dict(delta=-1.0), 1), (dict(dv=0), 1), (dict(m=512), 2),
+])
+@fake_ptr
+def test_gated_validation(L, bad, code):
+    """The gated form runs on the (m, dv) in {(256,128), (128,64), (64,64)}
+    bf16 kernels; anything else is refused before any launch."""
+    s = _shape(**bad)
+    ws = L.llops_workspace_bytes(ctypes.byref(_shape()), _lib.ENTRY_GATED_CAUSAL)
+    assert ws > 0
+    assert L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL) == 0
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          None, None, FAKE, None, None, FAKE, ws, None)
+    assert st == code, _err(L)
+
+
+@fake_ptr
+def test_gated_pointers_and_workspace(L):
+    s = _shape()
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL)
+    # the gate is required, 4-byte aligned; a 16-byte-misaligned gate is fine
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                          None, None, FAKE, None, None, FAKE, need, None)
+    assert st == 1 and "log_gate is null" in _err(L)
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          ctypes.c_void_p(0x10002), None, None, FAKE, None, None,
+                                          FAKE, need, None)
+    assert st == 1 and "log_gate" in _err(L)
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          ctypes.c_void_p(0x10004), None, None, FAKE, None, None,
+                                          FAKE, need - 1, None)
+    assert st == 3 and "workspace" in _err(L)
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          MISALIGNED, None, FAKE, None, None, FAKE, need, None)
+    assert st == 1 and "S0" in _err(L)
+
+
+def test_gated_workspace_layout(L):
+    """The gated workspace is the causal one plus the chunk-local gate sums
+    (rows padded to 32 tokens) and one fp32 gate sum per segment."""
+    s = _lib.make_shape(batch=1, heads=32, n=65536, d=128, dv=128, m=256, p=2, t=4, square=1,
+                        normalize=1, delta=1e-6, chunk=128)
+    base = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL)
+    gated = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL)
+    assert base + 32 * 65536 * 4 <= gated <= base + 32 * 65536 * 4 + 32 * 512 * 4 + 512
+    r = _lib.make_shape(batch=2, heads=3, n=33, d=64, dv=64, m=64, p=2, t=2)
+    gr = L.llops_workspace_bytes(ctypes.byref(r), _lib.ENTRY_GATED_CAUSAL)
+    assert gr >= L.llops_workspace_bytes(ctypes.byref(r), _lib.ENTRY_CAUSAL) + 6 * 64 * 4
+    dec = _lib.make_shape(batch=128, heads=32, n=1, d=128, dv=128, m=256, p=2, t=4)
+    assert (L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_GATED_DECODE)
+            == L.llops_workspace_bytes(ctypes.byref(dec), _lib.ENTRY_DECODE))
+
+
+@fake_ptr
+def test_gated_decode_requires_gate(L):
+    s = _shape()
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_DECODE)
+    st = L.llops_gated_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                   FAKE, FAKE, FAKE, need, None)
+    assert st == 1 and "log_gate is null" in _err(L)
+    st = L.llops_gated_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   FAKE, FAKE, FAKE, need - 1, None)
+    assert st == 3, _err(L)

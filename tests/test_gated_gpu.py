@@ -1,0 +1,240 @@
+"""GPU parity of the gated (decaying-state) causal attention and decode step
+against the fp64 oracle's token-by-token recurrence, on seeded inputs that
+span several 32-token chunks, several segments and ragged tails; plus the
+degenerate gates (no decay, full forgetting), state continuation, n = 0 and
+n = 1, and the full 1 x 32 x 65536 shape on sampled heads."""
+import numpy as np
+import pytest
+
+from learnable_polynomial_feature_amd.workloads import (Workload, decode_step_gates, generate,
+                                                         log_gates)
+from oracle import llops_oracle as O
+
+from _util import TOL_BF16, announce, dev, host, rel_fro
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _w(B, H, n, d, dv, m, p, t, qk="gauss", normalize=True, delta=1e-6, seed=0):
+    return Workload("gated", batch=B, heads=H, n=n, d=d, dv=dv, p=p, t=t, m=m, dtype="bf16",
+                    causal=True, square=True, normalize=normalize, delta=delta, chunk=64,
+                    qk_dist=qk, seed=seed)
+
+
+def _inputs(w, heads=None):
+    x = generate(w, heads=heads)
+    return x, {k: dev(v, torch.bfloat16) for k, v in x.items()}
+
+
+def _state0(B, H, m, dv, seed):
+    """A synthetic fp32 initial state: S0 ~ N(0, 0.01^2), z0 = |N(0, 0.01^2)|
+    (z sums non-negative squared features, so it is kept non-negative)."""
+    rng = np.random.default_rng(seed)
+    S0 = (0.01 * rng.standard_normal((B, H, m, dv))).astype(np.float32)
+    z0 = np.abs(0.01 * rng.standard_normal((B, H, m))).astype(np.float32)
+    return S0, z0
+
+
+GATED_CASES = [
+    # B, H, n, d, dv, m, p, t, qk, mu (gate u ~ N(mu, 1)), normalize
+    (2, 3, 300, 64, 64, 64, 2, 4, "gauss", 4.0, True),
+    (1, 2, 777, 128, 128, 256, 2, 4, "gauss", 4.0, True),
+    (2, 2, 1000, 64, 64, 128, 3, 8, "l2x2", 4.0, True),
+    (2, 32, 2048, 64, 64, 64, 2, 1, "gauss", 2.0, True),   # 8 chunks per segment
+    (1, 3, 513, 128, 128, 256, 2, 4, "gauss", 0.0, True),  # strong decay (median 1/2)
+    (2, 2, 450, 64, 64, 64, 2, 4, "gauss", 3.0, False),    # no normaliser
+]
+
+
+@pytest.mark.parametrize("case", GATED_CASES, ids=[str(c) for c in GATED_CASES])
+def test_gated_causal(lib, case):
+    B, H, n, d, dv, m, p, t, qk, mu, normalize = case
+    w = _w(B, H, n, d, dv, m, p, t, qk=qk, normalize=normalize)
+    x, g = _inputs(w)
+    lg = log_gates(w, mu=mu)
+    S0, z0 = _state0(B, H, m, dv, seed=7)
+    kw = dict(square=True, normalize=normalize, delta=1e-6)
+    announce(f"gated causal {case}")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(
+        g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], torch.from_numpy(lg).cuda(),
+        S0=torch.from_numpy(S0).cuda(), z0=torch.from_numpy(z0).cuda(), return_state=True, **kw)
+    torch.cuda.synchronize()
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      S0=S0, z0=z0, **kw)
+    assert rel_fro(host(out), ro) <= TOL_BF16
+    assert rel_fro(host(S), rS) <= TOL_BF16
+    assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+def test_gated_zero_gate_is_causal(lib):
+    """log_gate = 0 is the ungated causal attention: every decay factor is
+    exp(0) = 1 exactly, so only the fp32 order of the two output sums differs."""
+    w = _w(2, 2, 700, 128, 128, 256, 2, 4)
+    x, g = _inputs(w)
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated zero gate")
+    zero = torch.zeros((2, 2, 700), dtype=torch.float32, device="cuda")
+    a, Sa, za = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                   g["theta_k"], zero, return_state=True, **kw)
+    b, Sb, zb = lib.llops_linattn_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                             return_state=True, **kw)
+    torch.cuda.synchronize()
+    assert rel_fro(host(a), host(b)) <= 1e-5
+    assert rel_fro(host(Sa), host(Sb)) <= 1e-6
+    assert rel_fro(host(za), host(zb)) <= 1e-6
+    ro, _, _ = O.causal_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], chunk=64, **kw)
+    assert rel_fro(host(a), ro) <= TOL_BF16
+
+
+def test_gated_full_forgetting(lib):
+    """A decay of exp(-800) = 0 in fp32 forgets everything before the current
+    token: each output row is the current value row scaled by
+    s / (s + delta), s = phi_Q(q_i) . phi_K(k_i)."""
+    w = _w(1, 2, 200, 64, 64, 64, 2, 4, delta=1e-6)
+    x, g = _inputs(w)
+    lg = np.full((1, 2, 200), -800.0, np.float32)
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated full forgetting")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                   g["theta_k"], torch.from_numpy(lg).cuda(),
+                                                   return_state=True, **kw)
+    torch.cuda.synchronize()
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      **kw)
+    assert rel_fro(host(out), ro) <= TOL_BF16
+    assert rel_fro(host(S), rS) <= TOL_BF16
+    assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+def test_gated_state_continuation(lib):
+    """A split at a token that is not a chunk boundary, with the first part's
+    final state as the second part's initial state, reproduces the whole."""
+    w = _w(2, 2, 400, 64, 64, 64, 2, 4)
+    x, g = _inputs(w)
+    lg = log_gates(w, mu=3.0)
+    lgd = torch.from_numpy(lg).cuda()
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated continuation")
+    full, Sf, zf = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                      g["theta_k"], lgd, return_state=True, **kw)
+    n1 = 147
+    a, S1, z1 = lib.llops_linattn_gated_causal_fwd(
+        g["Q"][:, :, :n1], g["K"][:, :, :n1], g["V"][:, :, :n1], g["theta_q"], g["theta_k"],
+        lgd[:, :, :n1], return_state=True, **kw)
+    b, S2, z2 = lib.llops_linattn_gated_causal_fwd(
+        g["Q"][:, :, n1:], g["K"][:, :, n1:], g["V"][:, :, n1:], g["theta_q"], g["theta_k"],
+        lgd[:, :, n1:], S0=S1, z0=z1, return_state=True, **kw)
+    torch.cuda.synchronize()
+    both = np.concatenate([host(a), host(b)], axis=2)
+    assert rel_fro(both, host(full)) <= 1e-2
+    assert rel_fro(host(S2), host(Sf)) <= 1e-2
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      **kw)
+    assert rel_fro(both, ro) <= TOL_BF16
+    assert rel_fro(host(S2), rS) <= TOL_BF16
+    assert rel_fro(host(z2), rz) <= TOL_BF16
+
+
+def test_gated_empty_and_single_token(lib):
+    w = _w(2, 3, 1, 64, 64, 64, 2, 4)
+    x, g = _inputs(w)
+    S0, z0 = _state0(2, 3, 64, 64, seed=9)
+    S0d, z0d = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated n = 0 and n = 1")
+    lg = log_gates(w, mu=1.0)
+    e = g["Q"][:, :, :0]
+    _, Se, ze = lib.llops_linattn_gated_causal_fwd(e, e, g["V"][:, :, :0], g["theta_q"],
+                                                   g["theta_k"], torch.from_numpy(lg).cuda()[:, :, :0],
+                                                   S0=S0d, z0=z0d, return_state=True, **kw)
+    out, S1, z1 = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                     g["theta_k"], torch.from_numpy(lg).cuda(),
+                                                     S0=S0d, z0=z0d, return_state=True, **kw)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Se), S0) and np.array_equal(host(ze), z0)
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      S0=S0, z0=z0, **kw)
+    assert rel_fro(host(out), ro) <= TOL_BF16
+    assert rel_fro(host(S1), rS) <= TOL_BF16
+    assert rel_fro(host(z1), rz) <= TOL_BF16
+
+
+@pytest.mark.parametrize("case", [(4, 3, 64, 64, 64, 2, 4), (8, 4, 128, 128, 256, 2, 4)])
+def test_gated_decode(lib, case):
+    """Decode steps with per-step gates from an oracle-built prefix state
+    against the oracle's recurrence over the same tokens."""
+    B, H, d, dv, m, p, t = case
+    prefix, steps = 40, 6
+    w = _w(B, H, prefix + steps, d, dv, m, p, t)
+    x, g = _inputs(w)
+    S0 = np.zeros((B, H, m, dv))
+    z0 = np.zeros((B, H, m))
+    for b in range(B):
+        for h in range(H):
+            S0[b, h], z0[b, h] = O.state_from_prefix(x["K"][b, h, :prefix], x["V"][b, h, :prefix],
+                                                     x["theta_k"][h], square=True)
+    S0, z0 = S0.astype(np.float32), z0.astype(np.float32)
+    S, z = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    lg = np.stack([decode_step_gates(w, s, mu=2.0) for s in range(steps)], axis=2)  # [B, H, steps]
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce(f"gated decode {case}")
+    outs = []
+    for s in range(steps):
+        i = prefix + s
+        outs.append(lib.llops_gated_decode_step(
+            g["Q"][:, :, i], g["K"][:, :, i], g["V"][:, :, i], g["theta_q"], g["theta_k"],
+            torch.from_numpy(np.ascontiguousarray(lg[:, :, s])).cuda(), S, z, **kw))
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], axis=2)
+    sl = slice(prefix, prefix + steps)
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"][:, :, sl], x["K"][:, :, sl], x["V"][:, :, sl],
+                                      x["theta_q"], x["theta_k"], lg, S0=S0, z0=z0, **kw)
+    assert rel_fro(got, ro) <= TOL_BF16
+    assert rel_fro(host(S), rS) <= TOL_BF16
+    assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+def test_gated_decode_zero_gate_is_decode(lib):
+    """A zero log gate multiplies the state by exp(0) = 1 exactly: bit for bit
+    the ungated step."""
+    w = _w(8, 4, 3, 128, 128, 256, 2, 4)
+    x, g = _inputs(w)
+    rng = np.random.default_rng(3)
+    S0 = rng.standard_normal((8, 4, 256, 128)).astype(np.float32)
+    z0 = np.abs(rng.standard_normal((8, 4, 256))).astype(np.float32)
+    Sa, za = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    Sb, zb = Sa.clone(), za.clone()
+    zero = torch.zeros((8, 4), dtype=torch.float32, device="cuda")
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated decode zero gate")
+    for i in range(3):
+        oa = lib.llops_gated_decode_step(g["Q"][:, :, i], g["K"][:, :, i], g["V"][:, :, i],
+                                         g["theta_q"], g["theta_k"], zero, Sa, za, **kw)
+        ob = lib.llops_decode_step(g["Q"][:, :, i], g["K"][:, :, i], g["V"][:, :, i],
+                                   g["theta_q"], g["theta_k"], Sb, zb, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb) and torch.equal(za, zb)
+
+
+def test_gated_full_size_sampled_heads(lib):
+    """1 x 32 x 65536 (d = 128, m = 256, p = 2, t = 4, squared, normalised),
+    retention-biased gates, in one launch configuration of the full shape:
+    heads 0 and 31 against the oracle's token-by-token recurrence."""
+    w = Workload("gated_long", batch=1, heads=32, n=65536, d=128, dv=128, p=2, t=4, m=256,
+                 dtype="bf16", causal=True, square=True, normalize=True, delta=1e-6, chunk=128)
+    x, g = _inputs(w)
+    lg = log_gates(w, mu=4.0)
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce("gated full size 1x32x65536")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                   g["theta_k"], torch.from_numpy(lg).cuda(),
+                                                   chunk=128, return_state=True, **kw)
+    torch.cuda.synchronize()
+    for h in (0, 31):
+        ro, rS, rz = O.gated_recurrent(x["Q"][0, h], x["K"][0, h], x["V"][0, h],
+                                       x["theta_q"][h], x["theta_k"][h], lg[0, h], **kw)
+        assert rel_fro(host(out[0, h]), ro) <= TOL_BF16, h
+        assert rel_fro(host(S[0, h]), rS) <= TOL_BF16, h
+        assert rel_fro(host(z[0, h]), rz) <= TOL_BF16, h
