@@ -12,7 +12,9 @@ The line also carries:
                 dense MFMA peak, its duration timed live with HIP events;
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload;
   decode        the single-token decode step (batch 128, 32 heads, 1000
-                consecutive steps from a 4096-token prefix state) against HBM.
+                consecutive steps from a 4096-token prefix state) against HBM,
+                and the gated decode step over the same tokens;
+  gated         the gated (decaying-state) causal pass on the same inputs.
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -125,7 +129,47 @@ def bench_causal(w, steps, warmup, torch, lib):
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
     kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
-    return ms, kern
+    return ms, kern, (args, ws)
+
+
+def bench_gated(w, steps, torch, lib, args, ws_causal):
+    """The gated causal pass (per-token state decay exp(g), g = log sigmoid
+    of N(4, 1) draws) on the same device inputs as the causal step."""
+    from learnable_polynomial_feature_amd.workloads import log_gates
+    del ws_causal
+    lg = torch.from_numpy(log_gates(w, mu=4.0)).to("cuda")
+    out = torch.empty((w.batch, w.heads, w.n, w.dv), dtype=torch.float32, device="cuda")
+    shape = lib.make_shape(batch=w.batch, heads=w.heads, n=w.n, d=w.d, dv=w.dv, m=w.m, p=w.p,
+                           t=w.t, square=w.square, normalize=w.normalize, delta=w.delta,
+                           chunk=w.chunk)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_GATED_CAUSAL), dtype=torch.uint8,
+                     device="cuda")
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta, chunk=w.chunk, out=out,
+              workspace=ws)
+    for _ in range(2):
+        lib.llops_linattn_gated_causal_fwd(*args, lg, **kw)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        lib.llops_linattn_gated_causal_fwd(*args, lg, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    timer = lib.KernelTimer(capacity=16 * steps)
+    with timer:
+        for _ in range(steps):
+            lib.llops_linattn_gated_causal_fwd(*args, lg, **kw)
+    torch.cuda.synchronize()
+    kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    fl = causal_flops(w)
+    del lg, out, ws
+    return {"workload": f"gated causal {w.batch}x{w.heads}x{w.n} d={w.d} dv={w.dv} m={w.m} "
+                        f"p={w.p} t={w.t}, squared, normalised, log gates log(sigmoid(N(4,1)))",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(w.batch * w.n / (ms * 1e-3), 1),
+            "mfma_frac_step": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
 
 
 def attention_flops(w):
@@ -395,7 +439,33 @@ def bench_decode(w, steps, torch, lib):
             lib.llops_decode_step(q[s], k[s], v[s], gq, gk, S, z, out=out, workspace=ws, **kw)
     torch.cuda.synchronize()
     kern = {kk: sum(vv) / len(vv) for kk, vv in timer.durations_ms().items()}
-    return ms, kern
+    # the gated step over the same tokens, with per-step log gates
+    from learnable_polynomial_feature_amd.workloads import decode_step_gates
+    gsteps = min(steps, 200)
+    lg = torch.from_numpy(np.stack([decode_step_gates(w, s) for s in range(gsteps)])).to("cuda")
+    for s in range(3):
+        lib.llops_gated_decode_step(q[s], k[s], v[s], gq, gk, lg[s], S, z, out=out, workspace=ws,
+                                    **kw)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(gsteps):
+        lib.llops_gated_decode_step(q[s], k[s], v[s], gq, gk, lg[s], S, z, out=out, workspace=ws,
+                                    **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    gms = t0.elapsed_time(t1) / gsteps
+    timer = lib.KernelTimer(capacity=8 * gsteps)
+    with timer:
+        for s in range(gsteps):
+            lib.llops_gated_decode_step(q[s], k[s], v[s], gq, gk, lg[s], S, z, out=out,
+                                        workspace=ws, **kw)
+    torch.cuda.synchronize()
+    gkern = {kk: sum(vv) / len(vv) for kk, vv in timer.durations_ms().items()}
+    gated = {"steps": gsteps, "ms_per_step": round(gms, 4),
+             "tokens_per_s": round(B / (gms * 1e-3), 1),
+             "GBps": round(decode_bytes(w) / (gms * 1e-3) / 1e9, 1),
+             "kernel_ms": {kk: round(vv, 4) for kk, vv in gkern.items()}}
+    return ms, kern, gated
 
 
 def cpu_baseline(w, budget_s):
@@ -477,7 +547,7 @@ def main():
     if w.steps:
         raise SystemExit("use the default causal workload; decode is reported in the same line")
 
-    ms, kern = bench_causal(w, args.steps, args.warmup, torch, lib)
+    ms, kern, (cargs, cws) = bench_causal(w, args.steps, args.warmup, torch, lib)
     tokens = w.batch * w.n
     flops = causal_flops(w)
     feat_ms = kern.get("featmap_bf16")
@@ -514,7 +584,7 @@ def main():
     }
     if not args.no_decode:
         wd = WORKLOADS["decode_b128_h32"]
-        dms, dkern = bench_decode(wd, args.decode_steps, torch, lib)
+        dms, dkern, dgated = bench_decode(wd, args.decode_steps, torch, lib)
         gb = decode_bytes(wd) / (dms * 1e-3) / 1e9
         st_ms = dkern.get("decode_state")
         st_gb = decode_state_bytes(wd) / (st_ms * 1e-3) / 1e9 if st_ms else None
@@ -528,7 +598,12 @@ def main():
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(st_gb / PEAK_HBM_GBPS, 4),
                 "traffic": load_traffic("decode_state"),
                 "bytes_per_launch": decode_state_bytes(wd)},
+            "gated": dgated,
         }
+    if not args.no_configs:
+        log("gated causal")
+        line["gated"] = bench_gated(w, 10, torch, lib, cargs, cws)
+    del cargs, cws
     if not args.no_configs:
         line["configs"] = config_lines(20, torch, lib)
         log("feature-map variants")

@@ -141,12 +141,12 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
-  // gated: the chunk's 32 gate sums (128 bytes) come with the chunk, loaded
-  // by the first 8 lanes of wave 0 (every lane of that wave issues the load)
+  // gated: the chunk's 32 gate sums (128 bytes) come with the chunk, one per
+  // lane of the first half of wave 0
   const __amdgpu_buffer_rsrc_t rsg =
       make_rsrc(GATED ? a.gl + bh * gl_ld(a.n) + t0 : nullptr,
                 GATED ? static_cast<uint32_t>(gl_ld(seg_rows)) * 4u : 0u);
-  u32x4 rg = u32x4{0u, 0u, 0u, 0u};
+  uint32_t rg = 0u;
   auto load = [&](int c, u32x4 (&rk)[LK], u32x4 (&rv)[LV]) {
     // piece idx of a chunk is 16 contiguous bytes at byte 16 * idx
 #pragma unroll
@@ -155,10 +155,10 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
 #pragma unroll
     for (int i = 0; i < LV; ++i)
       rv[i] = buf_ld16(rsv, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
-    if (GATED && w == 0) rg = buf_ld16(rsg, (lane & 7) * 16u, static_cast<uint32_t>(c) * (kC * 4u));
+    if (GATED && w == 0) rg = buf_ld4(rsg, (lane & 31) * 4u + static_cast<uint32_t>(c) * (kC * 4u));
   };
   auto store = [&](uint16_t* buf, const u32x4 (&rk)[LK], const u32x4 (&rv)[LV]) {
-    if (GATED && w == 0 && lane < 8) st16(buf + kC * MP + kC * VP + lane * 8, rg);
+    if (GATED && w == 0 && lane < kC) reinterpret_cast<uint32_t*>(buf + kC * MP + kC * VP)[lane] = rg;
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int idx = tid + i * NT, row = idx / (M / 8), col = idx % (M / 8);
@@ -353,13 +353,13 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
   // contiguous bytes each; a thread's pieces t + i*NT never straddle two
   // tensors, so the selection folds away
-  // gated: the chunk's 32 gate sums (128 bytes), loaded by wave 0 and
-  // stored by its first 8 lanes behind the chunk's V rows
+  // gated: the chunk's 32 gate sums (128 bytes), one per lane of the first
+  // half of wave 0, stored behind the chunk's V rows
   const __amdgpu_buffer_rsrc_t rsg =
       make_rsrc(GATED ? a.gl + bh * gl_ld(a.n) + t0 : nullptr,
                 GATED ? static_cast<uint32_t>(gl_ld(seg_rows)) * 4u : 0u);
-  auto load = [&](int c, u32x4 (&r)[LPT], u32x4& rg) {
-    if (GATED && w == 0) rg = buf_ld16(rsg, (lane & 7) * 16u, static_cast<uint32_t>(c) * (kC * 4u));
+  auto load = [&](int c, u32x4 (&r)[LPT], uint32_t& rg) {
+    if (GATED && w == 0) rg = buf_ld4(rsg, (lane & 31) * 4u + static_cast<uint32_t>(c) * (kC * 4u));
     int t = tid;  // opaque: per-piece offsets are rebuilt, not kept live
     asm volatile("" : "+v"(t));
 #pragma unroll
@@ -373,8 +373,9 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         r[i] = buf_ld16(rsv, (p - 2 * QP) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
     }
   };
-  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT], const u32x4& rg) {
-    if (GATED && w == 0 && lane < 8) st16(buf + kC * QPAD + kC * MP + kC * VP + lane * 8, rg);
+  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT], const uint32_t& rg) {
+    if (GATED && w == 0 && lane < kC)
+      reinterpret_cast<uint32_t*>(buf + kC * QPAD + kC * MP + kC * VP)[lane] = rg;
     int t = tid;
     asm volatile("" : "+v"(t));
 #pragma unroll
@@ -398,7 +399,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // LDS; unconditional, clamped, so wait counts stay static), compute chunk
   // c, move chunk c+1 from `wr` into the other LDS slot, publish partials,
   // barrier, finish this wave's rows
-  auto step = [&](int c, u32x4 (&ld)[LPT], u32x4& ldg, const u32x4 (&wr)[LPT], const u32x4& wrg) {
+  auto step = [&](int c, u32x4 (&ld)[LPT], uint32_t& ldg, const u32x4 (&wr)[LPT], const uint32_t& wrg) {
     load(c + 2 < nch ? c + 2 : nch - 1, ld, ldg);
     // Lane-dependent bases pass through an empty asm so the compiler cannot
     // hoist every derived LDS address and mask compare out of the chunk loop
@@ -422,7 +423,6 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 
     f32x16 O = zero16(), D = zero16();
     bf16x8 afr[2];
-    auto intra = [&]() {
     if (CAUSAL && half == 0) {
       // masked A^T = phi_K phi_Q^T (keys x queries)
       // fragment reads run AD k-steps ahead of the MFMA chain (pinned: the
@@ -482,10 +482,14 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       for (int ks = 0; ks < kC / 16; ++ks)
         O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
     }
-    };
+    __builtin_amdgcn_sched_barrier(0);
     // partial phi_Q S over this wave's feature half; phi_Q . z over its z
-    // tile. The phi_Q fragment reads run QD products ahead (pinned).
-    auto inter = [&]() {
+    // tile. The phi_Q fragment reads run QD products ahead (pinned). Gated:
+    // the carried state reaches query q with weight exp(L_q), applied to the
+    // query's phi_Q row (the A operand's row is this lane's query c32).
+    {
+      float eq = 1.f;
+      if constexpr (GATED) eq = __expf(gate_sums()[c32]);
       constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
       bf16x8 qf[QD];
 #pragma unroll
@@ -493,32 +497,16 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const int j = idx >> 1, h = idx & 1;
-        const bf16x8 qa = qf[idx % QD];
+        bf16x8 qa = qf[idx % QD];
+        if constexpr (GATED) {
+          const float e8[8] = {eq, eq, eq, eq, eq, eq, eq, eq};
+          qa = scale_frag(qa, e8);
+        }
         if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], h), O);
         if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
         __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    if constexpr (GATED) {
-      // the carried state reaches query q with weight exp(L_q): scale the
-      // inter-chunk rows before the intra-chunk product adds its own
-      inter();
-      __builtin_amdgcn_sched_barrier(0);
-      float Lr[16];
-      gate_rows(gate_sums(), hh, Lr);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float sc = __expf(Lr[k]);
-        O[k] *= sc;
-        D[k] *= sc;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      intra();
-    } else {
-      intra();
-      __builtin_amdgcn_sched_barrier(0);
-      inter();
     }
     __builtin_amdgcn_sched_barrier(0);
     // publish: the 16 rows the partner wave finishes, and the z partial
@@ -631,7 +619,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     }
   };
 
-  u32x4 rA[LPT], rB[LPT], gA = u32x4{0u, 0u, 0u, 0u}, gB = gA;
+  u32x4 rA[LPT], rB[LPT];
+  uint32_t gA = 0u, gB = 0u;
   load(0, rA, gA);
   load(nch > 1 ? 1 : 0, rB, gB);
   // The prefix state must be in registers before the chunk loop: a wait for
