@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads' per-config lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated causal pass")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
@@ -600,7 +601,7 @@ def main():
                 "bytes_per_launch": decode_state_bytes(wd)},
             "gated": dgated,
         }
-    if not args.no_configs:
+    if not args.no_gated:
         log("gated causal")
         line["gated"] = bench_gated(w, 10, torch, lib, cargs, cws)
     del cargs, cws
