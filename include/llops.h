@@ -180,10 +180,12 @@ llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* 
  * log_gate: fp32 [batch][heads][n], g_i = log of the decay (device, 4-byte
  * aligned). Values <= 0 keep every factor in (0, 1]; positive values grow the
  * state and can overflow. Other arguments as for llops_linattn_causal_fwd;
- * S_final/z_final include the decay of every token. in_dtype BF16 only, with
+ * S_final/z_final include the decay of every token. in_dtype F32 runs the
+ * fp32 kernels (any shape within the general limits); in_dtype BF16 needs
  * (m, dv) in {(256, 128), (128, 64), (64, 64)} (else LLOPS_ERR_UNSUPPORTED).
- * Decay factors are computed in fp32 from chunk-local sums of g and the
- * decay-weighted V rounded to bf16 before its product.
+ * Decay factors are computed in fp32 from chunk-local sums of g; on the
+ * bf16 path the decay-weighted phi_Q and V are rounded to bf16 before their
+ * products.
  * ws: llops_workspace_bytes(shape, LLOPS_ENTRY_GATED_CAUSAL).
  */
 llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* shape, const void* Q,

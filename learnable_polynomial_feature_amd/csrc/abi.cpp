@@ -331,11 +331,11 @@ llops_status_t validate_attn_bwd(const llops_shape_t* s, bool causal) {
   return LLOPS_OK;
 }
 
-// The gated causal form runs on the 32x32x16 segment kernels only.
+// The gated causal form: fp32 inputs on the fp32 kernels (any shape), bf16
+// inputs on the 32x32x16 segment kernels only.
 llops_status_t validate_gated(const llops_shape_t* s) {
   LLOPS_TRY(validate(s, LLOPS_ENTRY_GATED_CAUSAL));
-  if (s->in_dtype != LLOPS_BF16)
-    return fail(LLOPS_ERR_UNSUPPORTED, "gated causal attention takes bf16 inputs only");
+  if (s->in_dtype != LLOPS_BF16) return LLOPS_OK;
   const llops::AttnShape a = attn_shape(s, true);
   if (s->batch * s->heads > 0 && !llops::attn32_supported(a))
     return fail(LLOPS_ERR_UNSUPPORTED,
@@ -632,6 +632,19 @@ llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* s, const void
   float* gl = reinterpret_cast<float*>(w + L.gl);
   float* gseg = reinterpret_cast<float*>(w + L.gseg);
   llops::FeatJob jobs[2] = {{Q, theta_q, w + L.phiq, w + L.pkq}, {K, theta_k, w + L.phik, w + L.pkk}};
+  if (s->in_dtype != LLOPS_BF16) {
+    LLOPS_HIP(llops::launch_featmap_f32(feat_shape(s, s->n, 0), jobs, 2, st), "featmap");
+    const float* pq = reinterpret_cast<const float*>(w + L.phiq);
+    const float* pk = reinterpret_cast<const float*>(w + L.phik);
+    const float* vv = static_cast<const float*>(V);
+    LLOPS_HIP(llops::launch_seg_state_f32_gated(a, pk, vv, log_gate, gseg, seg, st),
+              "seg_state_f32_gated");
+    LLOPS_HIP(llops::launch_seg_scan_gated(a, seg, gseg, S0, z0, S_final, z_final, st), "seg_scan");
+    LLOPS_HIP(llops::launch_attn_out_f32_gated(a, pq, pk, vv, log_gate, seg,
+                                               static_cast<float*>(out), st),
+              "attn_out_f32_gated");
+    return LLOPS_OK;
+  }
   LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, s->n, 1), jobs, 2, st), "featmap");
   const uint16_t* pq = reinterpret_cast<const uint16_t*>(w + L.phiq);
   const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);

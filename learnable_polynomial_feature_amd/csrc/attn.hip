@@ -479,6 +479,129 @@ __global__ __launch_bounds__(256) void attn_out_f32(AttnArgs a, const float* __r
   }
 }
 
+// Gated fp32 passes: the state decays by exp(g_j) before token j is added
+// (a per-token scalar forgetting gate: the LLoPS notes, limitations and
+// outlook). Pass 1 runs the recurrence S = exp(g_j) S + phi_K,j v_j^T over
+// its segment and writes the segment's sum of g; the output pass walks
+// chunks with chunk-local inclusive gate sums L (every exponent <= 0 for
+// g <= 0): A_ij = exp(L_i - L_j) phi_Q,i . phi_K,j (j <= i), the carried
+// state weighted by exp(L_i), and S = exp(T) S + sum_j exp(T - L_j) phi_K,j v_j^T.
+__global__ __launch_bounds__(256) void seg_state_f32_gated(AttnArgs a, const float* __restrict__ phik,
+                                                           const float* __restrict__ v,
+                                                           const float* __restrict__ lg,
+                                                           float* __restrict__ gseg,
+                                                           float* __restrict__ seg) {
+  const int m = a.m, dv = a.dv;
+  const int64_t bh = blockIdx.y;
+  const int gs = blockIdx.x;
+  const int64_t t0 = gs * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const float* K = phik + bh * a.n * m;
+  const float* V = v + bh * a.n * dv;
+  const float* G = lg + bh * a.n;
+  const int64_t per = static_cast<int64_t>(m) * dv + m;
+  float* out = seg + (bh * a.nseg + gs) * per;
+  for (int64_t e = threadIdx.x; e < per; e += 256) {
+    float s = 0.f;
+    if (e < static_cast<int64_t>(m) * dv) {
+      const int f = static_cast<int>(e / dv), c = static_cast<int>(e - static_cast<int64_t>(f) * dv);
+      for (int64_t j = t0; j < t1; ++j) s = fmaf(K[j * m + f], V[j * dv + c], expf(G[j]) * s);
+    } else {
+      const int f = static_cast<int>(e - static_cast<int64_t>(m) * dv);
+      for (int64_t j = t0; j < t1; ++j) s = fmaf(expf(G[j]), s, K[j * m + f]);
+    }
+    out[e] = s;
+  }
+  if (threadIdx.x == 0) {
+    float tot = 0.f;
+    for (int64_t j = t0; j < t1; ++j) tot += G[j];
+    gseg[bh * a.nseg + gs] = tot;
+  }
+}
+
+__global__ __launch_bounds__(256) void attn_out_f32_gated(AttnArgs a, const float* __restrict__ phiq,
+                                                          const float* __restrict__ phik,
+                                                          const float* __restrict__ v,
+                                                          const float* __restrict__ lg,
+                                                          float* __restrict__ state,
+                                                          float* __restrict__ out) {
+  extern __shared__ float fsm[];
+  const int C = a.chunk;
+  float* A = fsm;          // [C][C]
+  float* den = A + C * C;  // [C]
+  float* L = den + C;      // [C] chunk-local inclusive gate sums
+  const int m = a.m, dv = a.dv;
+  const int64_t bh = blockIdx.y;
+  const int gs = blockIdx.x;
+  const int64_t t0 = gs * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const float* Q = phiq + bh * a.n * m;
+  const float* K = phik + bh * a.n * m;
+  const float* V = v + bh * a.n * dv;
+  const float* G = lg + bh * a.n;
+  float* O = out + bh * a.n * dv;
+  const int64_t per = static_cast<int64_t>(m) * dv + m;
+  float* S = state + (bh * a.nseg + gs) * per;  // [m][dv] then z [m]
+  float* z = S + static_cast<int64_t>(m) * dv;
+  const int tid = threadIdx.x;
+  for (int64_t c0 = t0; c0 < t1; c0 += C) {
+    const int nc = static_cast<int>(min<int64_t>(C, t1 - c0));
+    if (tid == 0) {
+      float acc = 0.f;
+      for (int i = 0; i < nc; ++i) {
+        acc += G[c0 + i];
+        L[i] = acc;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < C * C; e += 256) {
+      const int i = e / C, j = e - i * C;
+      float s = 0.f;
+      if (j <= i && i < nc) {
+        for (int f = 0; f < m; ++f) s = fmaf(Q[(c0 + i) * m + f], K[(c0 + j) * m + f], s);
+        s *= expf(L[i] - L[j]);
+      }
+      A[e] = s;
+    }
+    __syncthreads();
+    if (a.normalize) {
+      for (int i = tid; i < nc; i += 256) {
+        float s = 0.f, qz = 0.f;
+        for (int j = 0; j <= i; ++j) s += A[i * C + j];
+        for (int f = 0; f < m; ++f) qz = fmaf(Q[(c0 + i) * m + f], z[f], qz);
+        den[i] = fmaf(expf(L[i]), qz, s) + a.delta;
+      }
+      __syncthreads();
+    }
+    for (int e = tid; e < nc * dv; e += 256) {
+      const int i = e / dv, c = e - i * dv;
+      float s = 0.f, qs = 0.f;
+      for (int j = 0; j <= i; ++j) s = fmaf(A[i * C + j], V[(c0 + j) * dv + c], s);
+      for (int f = 0; f < m; ++f) qs = fmaf(Q[(c0 + i) * m + f], S[f * dv + c], qs);
+      s = fmaf(expf(L[i]), qs, s);
+      O[(c0 + i) * dv + c] = a.normalize ? s / den[i] : s;
+    }
+    __syncthreads();
+    const float T = L[nc - 1];
+    const float decay = expf(T);
+    for (int64_t e = tid; e < per; e += 256) {
+      if (e < static_cast<int64_t>(m) * dv) {
+        const int f = static_cast<int>(e / dv), c = static_cast<int>(e - static_cast<int64_t>(f) * dv);
+        float s = decay * S[e];
+        for (int j = 0; j < nc; ++j)
+          s = fmaf(expf(T - L[j]) * K[(c0 + j) * m + f], V[(c0 + j) * dv + c], s);
+        S[e] = s;
+      } else {
+        const int f = static_cast<int>(e - static_cast<int64_t>(m) * dv);
+        float s = decay * z[f];
+        for (int j = 0; j < nc; ++j) s = fmaf(expf(T - L[j]), K[(c0 + j) * m + f], s);
+        z[f] = s;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(256) void state_init_kernel(int64_t total_S, int64_t total_z,
                                                          const float* S0, const float* z0,
                                                          float* S, float* z) {
@@ -616,6 +739,30 @@ hipError_t launch_attn_out_f32(const AttnShape& s, const float* phiq, const floa
   else
     LLOPS_LAUNCH("attn_out_f32", st, attn_out_f32<false>, grid, dim3(256), lds, st, a, phiq, phik, v, state,
                        st_seg, st_bh, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_state_f32_gated(const AttnShape& s, const float* phik, const float* v,
+                                      const float* log_gate, float* gseg, float* seg,
+                                      hipStream_t st) {
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  LLOPS_LAUNCH("seg_state_f32_gated", st, seg_state_f32_gated, grid, dim3(256), 0, st, a, phik, v,
+               log_gate, gseg, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_out_f32_gated(const AttnShape& s, const float* phiq, const float* phik,
+                                     const float* v, const float* log_gate, float* state,
+                                     float* out, hipStream_t st) {
+  if (!s.causal) return hipErrorInvalidValue;
+  const AttnArgs a = to_args(s);
+  dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
+  const size_t lds = (static_cast<size_t>(s.chunk) * s.chunk + 2 * s.chunk) * sizeof(float);
+  const hipError_t e = allow_lds(attn_out_f32_gated, lds);
+  if (e != hipSuccess) return e;
+  LLOPS_LAUNCH("attn_out_f32_gated", st, attn_out_f32_gated, grid, dim3(256), lds, st, a, phiq,
+               phik, v, log_gate, state, out);
   return hipGetLastError();
 }
 

@@ -135,6 +135,13 @@ hipError_t launch_seg_state32_gated(const AttnShape& a, const uint16_t* phik, co
 hipError_t launch_attn_out32_gated(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                                    const uint16_t* v, const float* gl, const float* state,
                                    float* out, hipStream_t st);
+// fp32 gated passes over the raw log gates g [BH][n] (any chunk, m, dv).
+hipError_t launch_seg_state_f32_gated(const AttnShape& a, const float* phik, const float* v,
+                                      const float* log_gate, float* gseg, float* seg,
+                                      hipStream_t st);
+hipError_t launch_attn_out_f32_gated(const AttnShape& a, const float* phiq, const float* phik,
+                                     const float* v, const float* log_gate, float* state,
+                                     float* out, hipStream_t st);
 // Causal scan with per-segment decays: prefix_{g+1} = exp(gseg[g]) prefix_g + seg[g].
 hipError_t launch_seg_scan_gated(const AttnShape& a, float* seg, const float* gseg,
                                  const float* S0, const float* z0, float* S_tot, float* z_tot,

@@ -366,13 +366,13 @@ def test_noncausal_bwd_workspace_below_causal(L):
 # ---- gated causal attention and gated decode -------------------------------
 
 @pytest.mark.parametrize("bad,code", [
-    (dict(in_dtype=_lib.F32), 2), (dict(m=96), 2), (dict(dv=32), 2), (dict(m=256, dv=64), 2),
+    (dict(m=96), 2), (dict(dv=32), 2), (dict(m=256, dv=64), 2),
     (dict(delta=-1.0), 1), (dict(dv=0), 1), (dict(m=512), 2),
 ])
 @fake_ptr
 def test_gated_validation(L, bad, code):
-    """The gated form runs on the (m, dv) in {(256,128), (128,64), (64,64)}
-    bf16 kernels; anything else is refused before any launch."""
+    """bf16 gated attention runs on the (m, dv) in {(256,128), (128,64),
+    (64,64)} kernels; anything else is refused before any launch."""
     s = _shape(**bad)
     ws = L.llops_workspace_bytes(ctypes.byref(_shape()), _lib.ENTRY_GATED_CAUSAL)
     assert ws > 0
@@ -401,6 +401,18 @@ def test_gated_pointers_and_workspace(L):
     st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                           MISALIGNED, None, FAKE, None, None, FAKE, need, None)
     assert st == 1 and "S0" in _err(L)
+
+
+@fake_ptr
+def test_gated_f32_any_shape(L):
+    """fp32 inputs take the fp32 gated kernels for shapes the bf16 kernels
+    refuse; a short workspace still stops the call before any launch."""
+    s = _shape(in_dtype=_lib.F32, m=96, dv=24, d=20)
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL)
+    assert need > 0
+    st = L.llops_linattn_gated_causal_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          None, None, FAKE, None, None, FAKE, need - 1, None)
+    assert st == 3, _err(L)
 
 
 def test_gated_workspace_layout(L):

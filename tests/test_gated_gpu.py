@@ -10,22 +10,24 @@ from learnable_polynomial_feature_amd.workloads import (Workload, decode_step_ga
                                                          log_gates)
 from oracle import llops_oracle as O
 
-from _util import TOL_BF16, announce, dev, host, rel_fro
+from _util import TOL_BF16, TOL_F32, announce, dev, host, rel_fro
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
 
-def _w(B, H, n, d, dv, m, p, t, qk="gauss", normalize=True, delta=1e-6, seed=0):
-    return Workload("gated", batch=B, heads=H, n=n, d=d, dv=dv, p=p, t=t, m=m, dtype="bf16",
-                    causal=True, square=True, normalize=normalize, delta=delta, chunk=64,
+def _w(B, H, n, d, dv, m, p, t, qk="gauss", normalize=True, delta=1e-6, seed=0, dtype="bf16",
+       square=True, chunk=64):
+    return Workload("gated", batch=B, heads=H, n=n, d=d, dv=dv, p=p, t=t, m=m, dtype=dtype,
+                    causal=True, square=square, normalize=normalize, delta=delta, chunk=chunk,
                     qk_dist=qk, seed=seed)
 
 
 def _inputs(w, heads=None):
     x = generate(w, heads=heads)
-    return x, {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    return x, {k: dev(v, tdt) for k, v in x.items()}
 
 
 def _state0(B, H, m, dv, seed):
@@ -66,6 +68,39 @@ def test_gated_causal(lib, case):
     assert rel_fro(host(out), ro) <= TOL_BF16
     assert rel_fro(host(S), rS) <= TOL_BF16
     assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+F32_CASES = [
+    # B, H, n, d, dv, m, p, t, square, normalize, chunk, mu
+    (1, 1, 256, 16, 16, 32, 2, 2, False, False, 0, 2.0),   # the tiny fp32 shape, gated
+    (2, 2, 150, 16, 8, 24, 3, 2, True, True, 16, 1.0),
+    (1, 2, 300, 32, 20, 40, 2, 3, True, True, 128, 0.0),
+    (1, 1, 70, 5, 3, 7, 2, 2, False, True, 32, 4.0),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[str(c) for c in F32_CASES])
+def test_gated_causal_f32(lib, case):
+    """fp32 inputs and arithmetic: the gated pass against the oracle's
+    recurrence at the fp32 tolerance, from a non-zero initial state."""
+    B, H, n, d, dv, m, p, t, square, normalize, chunk, mu = case
+    w = _w(B, H, n, d, dv, m, p, t, dtype="f32", square=square, normalize=normalize,
+           delta=1e-3, chunk=chunk)
+    x, g = _inputs(w)
+    lg = log_gates(w, mu=mu)
+    S0, z0 = _state0(B, H, m, dv, seed=5)
+    kw = dict(square=square, normalize=normalize, delta=1e-3)
+    announce(f"gated causal f32 {case}")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(
+        g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], torch.from_numpy(lg).cuda(),
+        S0=torch.from_numpy(S0).cuda(), z0=torch.from_numpy(z0).cuda(), chunk=chunk,
+        return_state=True, **kw)
+    torch.cuda.synchronize()
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      S0=S0, z0=z0, **kw)
+    assert rel_fro(host(out), ro) <= TOL_F32
+    assert rel_fro(host(S), rS) <= TOL_F32
+    assert rel_fro(host(z), rz) <= TOL_F32
 
 
 def test_gated_zero_gate_is_causal(lib):
