@@ -502,6 +502,117 @@ def gated_recurrent_bh(Q, K, V, theta_q, theta_k, log_gate, S0=None, z0=None, **
     return out, S, z
 
 
+def gated_attn_bwd(Pq, Pk, V, G, log_gate, normalize=False, delta=0.0):
+    """Gradients (dPq, dPk, dV, dg) of L = sum(G * out) for the gated causal
+    contraction from a zero state, out = M V [/ (M 1 + delta)] with
+    M_ij = W_ij (Pq_i . Pk_j), W_ij = exp(c_i - c_j) for j <= i (else 0) and
+    c = cumsum(log_gate): the chain rule through the materialised form of
+    gated_causal_quadratic ([LLoPS-notes] limitations and outlook for the
+    gate; [LLoPS-arXiv] Sec. 1 attention form; [SLAY-notes] key design 3):
+      dnum, dden as in causal_attn_bwd;  dM = tril(dnum V^T + dden 1^T),
+      dPq = (dM * W) Pk,  dPk = (dM * W)^T Pq,  dV = M^T dnum,
+      dc_i = sum_j (dM * M)_ij - sum_k (dM * M)_ki   (c_i enters row i with +,
+             column i with -),  dg_l = sum_{i >= l} dc_i   (c_i = sum_{l <= i} g_l)."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    c = np.cumsum(_f64(log_gate))
+    n = Pq.shape[0]
+    i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+    W = np.where(j <= i, np.exp(np.where(j <= i, c[:, None] - c[None, :], 0.0)), 0.0)
+    M = W * (Pq @ Pk.T)
+    if normalize:
+        den = M.sum(axis=1) + delta
+        out = (M @ V) / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(n)
+    dM = np.tril(dnum @ V.T + dden[:, None])
+    dA = dM * W
+    X = dM * M
+    dc = X.sum(axis=1) - X.sum(axis=0)
+    dg = np.cumsum(dc[::-1])[::-1]
+    return dA @ Pk, dA.T @ Pq, M.T @ dnum, dg
+
+
+def gated_attn_bwd_recurrent(Pq, Pk, V, G, log_gate, normalize=False, delta=0.0):
+    """gated_attn_bwd without the n x n matrix, for long sequences: the same
+    sums as running states. Forward, token by token: S_i = a_i S_{i-1} +
+    Pk_i V_i^T, z_i = a_i z_i-1 + Pk_i (a_i = exp(g_i)) give num, den and
+    dPq_i = S_i dnum_i + dden_i z_i. Backward over the tokens: R_j = Pq_j dnum_j^T
+    + a_{j+1} R_{j+1}, r_j = dden_j Pq_j + a_{j+1} r_{j+1} give dPk_j = R_j V_j + r_j
+    and dV_j = R_j^T Pk_j. The gate gradient uses (dM * M) row sums = Pq_i . dPq_i
+    and column sums = Pk_j . dPk_j, so dc = rowdot(Pq, dPq) - rowdot(Pk, dPk)."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    a = np.exp(_f64(log_gate))
+    n, m = Pq.shape
+    dv = V.shape[1]
+    S, z = np.zeros((m, dv)), np.zeros(m)
+    dnum, dden, dPq = np.zeros((n, dv)), np.zeros(n), np.zeros((n, m))
+    for t in range(n):
+        S = a[t] * S + np.outer(Pk[t], V[t])
+        z = a[t] * z + Pk[t]
+        num = Pq[t] @ S
+        if normalize:
+            den = Pq[t] @ z + delta
+            dnum[t] = G[t] / den
+            dden[t] = -(G[t] @ (num / den)) / den
+        else:
+            dnum[t] = G[t]
+        dPq[t] = S @ dnum[t] + dden[t] * z
+    R, r = np.zeros((m, dv)), np.zeros(m)
+    dPk, dV = np.zeros((n, m)), np.zeros((n, dv))
+    for t in reversed(range(n)):
+        nxt = a[t + 1] if t + 1 < n else 0.0
+        R = nxt * R + np.outer(Pq[t], dnum[t])
+        r = nxt * r + dden[t] * Pq[t]
+        dPk[t] = R @ V[t] + r
+        dV[t] = R.T @ Pk[t]
+    dc = (Pq * dPq).sum(axis=1) - (Pk * dPk).sum(axis=1)
+    dg = np.cumsum(dc[::-1])[::-1]
+    return dPq, dPk, dV, dg
+
+
+def gated_causal_bwd(Q, K, V, theta_q, theta_k, log_gate, G, square=False, normalize=False,
+                     delta=0.0, recurrent=False):
+    """Gradients (dQ, dK, dV, dTheta_q, dTheta_k, dlog_gate) of L = sum(G * out)
+    for out = gated_causal_quadratic(...) from a zero state: the feature
+    gradients (materialised, or the running-state form when recurrent), then
+    featmap_bwd on each side."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    fn = gated_attn_bwd_recurrent if recurrent else gated_attn_bwd
+    dPq, dPk, dV, dg = fn(Pq, Pk, V, G, log_gate, normalize, delta)
+    dQ, dtq = featmap_bwd(Q, theta_q, dPq, square)
+    dK, dtk = featmap_bwd(K, theta_k, dPk, square)
+    return dQ, dK, dV, dtq, dtk, dg
+
+
+def gated_causal_bwd_bh(Q, K, V, theta_q, theta_k, log_gate, G, **kw):
+    """gated_causal_bwd over [B, H, n, .] tensors (log_gate [B, H, n]); a
+    shared theta's gradient sums over the heads."""
+    theta_q, theta_k = np.asarray(theta_q), np.asarray(theta_k)
+    B, H = Q.shape[:2]
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    dtq, dtk = np.zeros(theta_q.shape), np.zeros(theta_k.shape)
+    dg = np.zeros(np.shape(log_gate))
+    for b in range(B):
+        for h in range(H):
+            gq, gk, gv, tq, tk, gg = gated_causal_bwd(
+                Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h), _theta_for(theta_k, h),
+                log_gate[b, h], G[b, h], **kw)
+            dQ[b, h], dK[b, h], dV[b, h], dg[b, h] = gq, gk, gv, gg
+            if theta_q.ndim == 5:
+                dtq[h] += tq
+            else:
+                dtq += tq
+            if theta_k.ndim == 5:
+                dtk[h] += tk
+            else:
+                dtk += tk
+    return dQ, dK, dV, dtq, dtk, dg
+
+
 def _theta_for(theta, h):
     theta = np.asarray(theta)
     return theta[h] if theta.ndim == 5 else theta

@@ -587,3 +587,76 @@ def test_gated_recurrent_equals_materialised_and_continues(normalize):
     assert np.allclose(second, whole[k:], rtol=1e-12, atol=1e-12)
     _, S2, z2 = O.gated_recurrent(Q[k:], K[k:], V[k:], tq, tk, g[k:], S0=S1, z0=z1, **kw)
     assert np.allclose(S2, S, rtol=1e-12, atol=1e-12) and np.allclose(z2, z, rtol=1e-12)
+
+
+# ---- gated attention backward ------------------------------------------------
+
+def _gated_loss(Q, K, V, tq, tk, g, G, **kw):
+    return float((G * O.gated_causal_quadratic(Q, K, V, tq, tk, g, **kw)).sum())
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, False), (True, True)])
+def test_gated_bwd_central_differences(square, normalize):
+    """Every entry of Q, K, V, Theta_q, Theta_k and the log gates against
+    (L(x + h) - L(x - h)) / 2h of L = sum(G * gated_causal_quadratic)."""
+    rng = np.random.default_rng(70 + 2 * square + normalize)
+    n, d, dv, m, p, t = 7, 3, 2, 4, 2, 2
+    Q, K = 0.7 * rng.standard_normal((n, d)), 0.7 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = 0.6 * rng.standard_normal((p, t, d, m)), 0.6 * rng.standard_normal((p, t, d, m))
+    g = -np.abs(0.5 * rng.standard_normal(n))
+    G = rng.standard_normal((n, dv))
+    kw = dict(square=square, normalize=normalize, delta=0.5)
+    got = O.gated_causal_bwd(Q, K, V, tq, tk, g, G, **kw)
+    args = [Q, K, V, tq, tk, g]
+    h = 1e-6
+    for which, grad in zip(range(6), got):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            num[idx] = (_gated_loss(*ap, G, **kw) - _gated_loss(*am, G, **kw)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), which
+
+
+def test_gated_bwd_zero_gate_is_causal_bwd():
+    """With log_gate = 0 the feature and value gradients are the ungated ones."""
+    rng = np.random.default_rng(75)
+    n, m, dv = 11, 5, 3
+    Pq, Pk = np.abs(rng.standard_normal((n, m))), np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    want = O.causal_attn_bwd(Pq, Pk, V, G, normalize=True, delta=0.3)
+    got = O.gated_attn_bwd(Pq, Pk, V, G, np.zeros(n), normalize=True, delta=0.3)
+    for a, b in zip(got[:3], want):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_gated_bwd_recurrent_equals_materialised(normalize):
+    rng = np.random.default_rng(76 + normalize)
+    n, m, dv = 13, 4, 3
+    Pq, Pk = np.abs(rng.standard_normal((n, m))), np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    g = -np.abs(rng.standard_normal(n))
+    a = O.gated_attn_bwd(Pq, Pk, V, G, g, normalize=normalize, delta=0.2)
+    b = O.gated_attn_bwd_recurrent(Pq, Pk, V, G, g, normalize=normalize, delta=0.2)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-11, atol=1e-12)
+
+
+def test_gated_bwd_gate_gradient_closed_form():
+    """Scalar features (Pq = Pk = 1), v = 1, G = 1, no normaliser, constant
+    decay a: out_i = sum_{k=0..i} a^k, so L = sum_i sum_{k<=i} a^k and
+    d/dg_l of the product chain: g_l appears in every weight a^(i-j) with
+    j < l <= i, each contributing a^(i-j), so dg_l = sum_{i>=l} sum_{j<l} a^(i-j)."""
+    n, a = 9, 0.7
+    g = np.full(n, np.log(a))
+    ones = np.ones((n, 1))
+    _, _, _, dg = O.gated_attn_bwd(ones, ones, ones, ones, g)
+    want = np.array([sum(a ** (i - j) for i in range(l, n) for j in range(l))
+                     for l in range(n)])
+    assert np.allclose(dg, want, rtol=1e-13, atol=1e-15)
