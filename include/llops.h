@@ -73,7 +73,8 @@ typedef enum {
   LLOPS_ENTRY_CAUSAL_BWD = 5,
   LLOPS_ENTRY_LINATTN_BWD = 6,
   LLOPS_ENTRY_GATED_CAUSAL = 7,
-  LLOPS_ENTRY_GATED_DECODE = 8
+  LLOPS_ENTRY_GATED_DECODE = 8,
+  LLOPS_ENTRY_GATED_CAUSAL_BWD = 9
 } llops_entry_t;
 
 typedef struct llops_shape {
@@ -253,6 +254,34 @@ llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
                                  const void* theta_q, const void* theta_k,
                                  float* S, float* z, void* out,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * llops_linattn_gated_causal_bwd -- gradients of L = sum(dO * out) for
+ * out = llops_linattn_gated_causal_fwd(Q, K, V, theta_q, theta_k, log_gate)
+ * started from a zero state: dQ, dK, dV, dtheta_q, dtheta_k as for
+ * llops_linattn_causal_bwd, and dlog_gate fp32 [batch][heads][n]. With
+ * W_ij = exp(c_i - c_j) (j <= i), c = cumsum(log_gate), M = W * (phi_Q phi_K^T):
+ *   dM = tril(dnum V^T + dden 1^T),  dphi_Q = (dM * W) phi_K,  dphi_K = (dM * W)^T phi_Q,
+ *   dV = M^T dnum,  dlog_gate_l = sum_{i >= l} (phi_Q,i . dphi_Q,i - phi_K,i . dphi_K,i)
+ * (the chain rule through the decay-masked form; the gate after the LLoPS
+ * notes' limitations and outlook, the attention of the paper's Sec. 1, the
+ * normaliser of the SLAY notes' key design 3). The three sums are gated
+ * causal linear attentions over bf16 features (dphi_K and dV over the
+ * reversed sequence, whose gates are shifted by one token), so they carry
+ * the forward's bf16 rounding; the gate gradient's row dots are taken on the
+ * fp32 pass outputs. in_dtype BF16 only; kernels exist for p = 2, t in
+ * {1, 4}, d in {64, 128} and (m, dv) in {(256, 128), (128, 64), (64, 64)}
+ * (else LLOPS_ERR_UNSUPPORTED). All outputs are overwritten. chunk is
+ * ignored. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_GATED_CAUSAL_BWD).
+ */
+llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* shape, const void* Q,
+                                              const void* K, const void* V,
+                                              const void* theta_q, const void* theta_k,
+                                              const float* log_gate, const float* dO,
+                                              float* dQ, float* dK, float* dV,
+                                              float* dtheta_q, float* dtheta_k,
+                                              float* dlog_gate, void* ws, size_t ws_bytes,
+                                              hipStream_t stream);
 
 /*
  * llops_gated_decode_step -- llops_decode_step on a decaying state:

@@ -8,6 +8,7 @@ and it raises if the library is missing.
 _BINDING = ("llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd", "llops_linattn_causal_fwd",
             "llops_linattn_causal_bwd", "llops_linattn_bwd",
             "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
+            "llops_linattn_gated_causal_bwd",
             "llops_workspace_bytes", "LlopsError", "library")
 
 

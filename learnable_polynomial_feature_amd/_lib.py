@@ -18,12 +18,14 @@ LIB_PATH = os.path.join(_HERE, "libllops.so")
 
 F32, BF16 = 0, 1
 (ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD, ENTRY_CAUSAL_BWD,
- ENTRY_LINATTN_BWD, ENTRY_GATED_CAUSAL, ENTRY_GATED_DECODE) = 0, 1, 2, 3, 4, 5, 6, 7, 8
+ ENTRY_LINATTN_BWD, ENTRY_GATED_CAUSAL, ENTRY_GATED_DECODE,
+ ENTRY_GATED_CAUSAL_BWD) = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
           3: "LLOPS_ERR_WORKSPACE", 4: "LLOPS_ERR_HIP"}
 EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd",
            "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
            "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
+           "llops_linattn_gated_causal_bwd",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -81,6 +83,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_linattn_gated_causal_fwd.restype = ctypes.c_int
     lib.llops_gated_decode_step.argtypes = [SP] + [_P] * 10 + [ctypes.c_size_t, _P]
     lib.llops_gated_decode_step.restype = ctypes.c_int
+    lib.llops_linattn_gated_causal_bwd.argtypes = [SP] + [_P] * 14 + [ctypes.c_size_t, _P]
+    lib.llops_linattn_gated_causal_bwd.restype = ctypes.c_int
     lib.llops_status_str.argtypes = [ctypes.c_int]
     lib.llops_status_str.restype = ctypes.c_char_p
     lib.llops_last_error.argtypes = []
@@ -340,6 +344,32 @@ def _attn_bwd(causal, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, w
               _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(ws), wsb,
               _stream(Q)))
     return dQ, dK, dV, dtq, dtk
+
+
+def llops_linattn_gated_causal_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, *, square=False,
+                                   normalize=False, delta=0.0, workspace=None):
+    """Gradients (dQ, dK, dV, dtheta_q, dtheta_k, dlog_gate) of sum(dO * out) for
+    out = llops_linattn_gated_causal_fwd(Q, K, V, theta_q, theta_k, log_gate, ...)
+    from a zero state. Q, K, V and thetas bf16; log_gate fp32 [B, H, n]; dO fp32
+    [B, H, n, dv]; all results fp32."""
+    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
+    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
+    dO, log_gate = _dev(dO, "dO"), _dev(log_gate, "log_gate")
+    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(V.shape):
+        raise ValueError("dO must be fp32 with V's shape")
+    if log_gate.dtype != torch.float32 or tuple(log_gate.shape) != tuple(Q.shape[:3]):
+        raise ValueError("log_gate must be fp32 [B, H, n]")
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
+    dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
+    dg = torch.empty(log_gate.shape, **f32)
+    ws, wsb = _workspace(shape, ENTRY_GATED_CAUSAL_BWD, Q.device, workspace)
+    _check(library().llops_linattn_gated_causal_bwd(
+        ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+        _ptr(log_gate), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(dg),
+        _ptr(ws), wsb, _stream(Q)))
+    return dQ, dK, dV, dtq, dtk, dg
 
 
 def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normalize=True,

@@ -35,7 +35,8 @@ struct SegPlan {
   int64_t seg_len;
 };
 
-SegPlan seg_plan(const llops_shape_t* s, bool causal) {
+// target: workgroups per pass to aim for (0 = the default for the dtype).
+SegPlan seg_plan(const llops_shape_t* s, bool causal, int64_t target_wg = 0) {
   SegPlan p{};
   const bool bf16 = s->in_dtype == LLOPS_BF16;
   if (bf16) {
@@ -47,7 +48,7 @@ SegPlan seg_plan(const llops_shape_t* s, bool causal) {
   }
   const int64_t BH = s->batch * s->heads;
   const int64_t n = s->n;
-  const int64_t target = bf16 ? 512 : 256;  // workgroups to aim for
+  const int64_t target = target_wg > 0 ? target_wg : bf16 ? 512 : 256;  // workgroups to aim for
   int64_t nchunks = (n + p.chunk - 1) / p.chunk;
   if (nchunks < 1) nchunks = 1;
   int64_t want = BH > 0 ? (target + BH - 1) / BH : 1;
@@ -78,11 +79,15 @@ llops_shape_t feat_attn_shape(const llops_shape_t* s, int M, int DV) {
   return t;
 }
 
-SegPlan seg_plan(const llops_shape_t* s, bool causal);
+// The gated backward splits its passes into 4x the default segments: its gate
+// gradient is exact at segment starts and a running sum of per-token terms
+// in between, whose rounding grows with the segment length.
+constexpr int64_t kGatedBwdWG = 2048;
 
-size_t feat_attn_seg_bytes(const llops_shape_t* s, int M, int DV, bool causal) {
+size_t feat_attn_seg_bytes(const llops_shape_t* s, int M, int DV, bool causal,
+                           int64_t target_wg = 0) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
-  const SegPlan sp = seg_plan(&t, causal);
+  const SegPlan sp = seg_plan(&t, causal, target_wg);
   return static_cast<size_t>(s->batch * s->heads) * sp.nseg *
          (static_cast<size_t>(M) * DV + M) * sizeof(float);
 }
@@ -303,8 +308,8 @@ llops::FeatShape feat_shape(const llops_shape_t* s, int64_t n, int out_bf16) {
   return f;
 }
 
-llops::AttnShape attn_shape(const llops_shape_t* s, bool causal) {
-  const SegPlan sp = seg_plan(s, causal);
+llops::AttnShape attn_shape(const llops_shape_t* s, bool causal, int64_t target_wg = 0) {
+  const SegPlan sp = seg_plan(s, causal, target_wg);
   llops::AttnShape a{};
   a.BH = s->batch * s->heads;
   a.n = s->n;
@@ -371,6 +376,75 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
   if (e != hipSuccess) return e;
   return mf32 ? llops::launch_attn_out32(a, fq, fk, v, state, st_seg, st_bh, out, st)
               : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
+}
+
+// ---- gated causal backward ---------------------------------------------------
+// The denominator pass of the gated backward runs M against all-ones values
+// of a width the 32x32x16 kernels take for m.
+int gated_den_w(const llops_shape_t* s) { return s->m == 256 ? 128 : 64; }
+
+struct GBwdWs {
+  BwdWs b;  // the ungated backward's buffers (its seg and den1/ones are not used)
+  size_t glf, grev, glr, gseg, gones, gden, dc, seg, seg2, dgb, total;
+};
+
+GBwdWs gated_bwd_ws(const llops_shape_t* s) {
+  GBwdWs w{};
+  w.b = bwd_ws(s, true);
+  size_t off = w.b.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, 256);
+    return at;
+  };
+  const size_t BH = static_cast<size_t>(s->batch * s->heads);
+  const size_t R = BH * static_cast<size_t>(s->n);
+  const size_t nld = static_cast<size_t>((s->n + 31) / 32 * 32);
+  const int DVo = gated_den_w(s), MA = bwd_ma(s), W = bwd_w(s);
+  w.glf = take(BH * nld * 4);   // chunk-local sums of the forward gates
+  w.grev = take(R * 4);         // gates of the reversed sequence
+  w.glr = take(BH * nld * 4);   // and their chunk-local sums
+  const llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
+  w.gseg = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);
+  w.gones = take(s->normalize ? R * DVo * 2 : 0);
+  w.gden = take(s->normalize ? R * DVo * 4 : 0);
+  w.dc = take(R * 4);           // d/dc_i = phi_Q,i . dphi_Q,i - phi_K,i . dphi_K,i
+  size_t seg = feat_attn_seg_bytes(s, s->m, s->dv, true, kGatedBwdWG);
+  const size_t seg2 = feat_attn_seg_bytes(s, MA, W, true, kGatedBwdWG);
+  const size_t seg3 = feat_attn_seg_bytes(s, s->m, DVo, true, kGatedBwdWG);
+  if (seg2 > seg) seg = seg2;
+  if (seg3 > seg) seg = seg3;
+  w.seg = take(seg);
+  w.seg2 = take(feat_attn_seg_bytes(s, MA, W, true, kGatedBwdWG));  // suffix states, dphi_Q slices
+  w.dgb = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);  // dg at starts
+  w.total = off;
+  return w;
+}
+
+llops_status_t validate_gated_bwd(const llops_shape_t* s) {
+  LLOPS_TRY(validate_attn_bwd(s, true));
+  if (!((s->m == 256 && s->dv == 128) || (s->m == 128 && s->dv == 64) ||
+        (s->m == 64 && s->dv == 64)))
+    return fail(LLOPS_ERR_UNSUPPORTED,
+                "gated backward kernels: (m, dv) in {(256, 128), (128, 64), (64, 64)} "
+                "(got m=%d dv=%d)", s->m, s->dv);
+  return LLOPS_OK;
+}
+
+// out_i = sum_{j<=i} exp(c_i - c_j) (fq_i . fk_j) v_j over bf16 features from a
+// zero state, gl the chunk-local sums of the pass's gates; the gated segment
+// kernels.
+hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const uint16_t* fq,
+                                  const uint16_t* fk, const uint16_t* v, const float* gl,
+                                  float* out, float* seg, float* gseg, hipStream_t st) {
+  const llops_shape_t t = feat_attn_shape(s, M, DV);
+  const llops::AttnShape a = attn_shape(&t, true, kGatedBwdWG);
+  if (!llops::attn32_supported(a)) return hipErrorInvalidValue;
+  hipError_t e = llops::launch_seg_state32_gated(a, fk, v, gl, gseg, seg, st);
+  if (e == hipSuccess)
+    e = llops::launch_seg_scan_gated(a, seg, gseg, nullptr, nullptr, nullptr, nullptr, st);
+  if (e == hipSuccess) e = llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
+  return e;
 }
 
 // Shared body of the non-causal and causal forward passes.
@@ -513,7 +587,9 @@ int32_t llops_profile_disarm(void) {
 }
 
 size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry) {
-  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_GATED_DECODE) return 0;
+  if (!shape || entry < LLOPS_ENTRY_FEATMAP || entry > LLOPS_ENTRY_GATED_CAUSAL_BWD) return 0;
+  if (entry == LLOPS_ENTRY_GATED_CAUSAL_BWD)
+    return validate_gated_bwd(shape) == LLOPS_OK ? gated_bwd_ws(shape).total : 0;
   if (entry == LLOPS_ENTRY_GATED_CAUSAL && validate_gated(shape) != LLOPS_OK) return 0;
   if (entry == LLOPS_ENTRY_CAUSAL_BWD || entry == LLOPS_ENTRY_LINATTN_BWD) {
     const bool causal = entry == LLOPS_ENTRY_CAUSAL_BWD;
@@ -720,7 +796,7 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   uint16_t *ra = causal ? u16(L.ra) : nullptr, *rb = causal ? u16(L.rb) : nullptr;
   LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
                                   s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
-                                  causal ? 1 : 0, st),
+                                  causal ? 1 : 0, 16, st),
             "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
@@ -774,6 +850,127 @@ llops_status_t llops_linattn_bwd(const llops_shape_t* s, const void* Q, const vo
                                  hipStream_t st) {
   return attn_backward(s, false, Q, K, V, theta_q, theta_k, dO, dQ, dK, dV, dtheta_q, dtheta_k, ws,
                        ws_bytes, st);
+}
+
+llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void* Q, const void* K,
+                                              const void* V, const void* theta_q,
+                                              const void* theta_k, const float* log_gate,
+                                              const float* dO, float* dQ, float* dK, float* dV,
+                                              float* dtheta_q, float* dtheta_k, float* dlog_gate,
+                                              void* ws, size_t ws_bytes, hipStream_t st) {
+  LLOPS_TRY(validate_gated_bwd(s));
+  const int64_t BH = s->batch * s->heads;
+  if (s->heads == 0) return LLOPS_OK;
+  LLOPS_TRY(need(theta_q, "theta_q"));
+  LLOPS_TRY(need(theta_k, "theta_k"));
+  LLOPS_TRY(need(dtheta_q, "dtheta_q"));
+  LLOPS_TRY(need(dtheta_k, "dtheta_k"));
+  const int64_t R = BH * s->n;
+  if (R > 0) {
+    LLOPS_TRY(need(Q, "Q"));
+    LLOPS_TRY(need(K, "K"));
+    LLOPS_TRY(need(V, "V"));
+    LLOPS_TRY(need4(log_gate, "log_gate"));
+    LLOPS_TRY(need(dO, "dO"));
+    LLOPS_TRY(need(dQ, "dQ"));
+    LLOPS_TRY(need(dK, "dK"));
+    LLOPS_TRY(need(dV, "dV"));
+    LLOPS_TRY(need4(dlog_gate, "dlog_gate"));
+  }
+  const GBwdWs L = gated_bwd_ws(s);
+  if (ws_bytes < L.total)
+    return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
+  if (!ws) return fail(LLOPS_ERR_INVALID_ARG, "ws is null");
+  LLOPS_TRY(opt(ws, "ws"));
+  char* w = static_cast<char*>(ws);
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(w + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
+  const llops::FeatShape fs0 = feat_shape(s, s->n, 0);
+  float* fb = L.b.fb ? f32(L.b.fb) : nullptr;
+  if (R == 0) {  // no rows: the Theta gradients are zero
+    LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dO, 0, dQ, dtheta_q, fb, st), "featmap_bwd");
+    LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dO, 0, dK, dtheta_k, fb, st), "featmap_bwd");
+    return LLOPS_OK;
+  }
+  const int m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s), DVo = gated_den_w(s);
+  const int64_t n = s->n;
+  uint16_t *phq = u16(L.b.phq), *phk = u16(L.b.phk);
+  float *seg = f32(L.seg), *gseg = f32(L.gseg);
+  llops::FeatJob jobs[2] = {{Q, theta_q, phq, w + L.b.pkq}, {K, theta_k, phk, w + L.b.pkk}};
+  LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, n, 1), jobs, 2, st), "featmap");
+  // chunk-local gate sums, forward and for the reversed sequence
+  float *glf = f32(L.glf), *grev = f32(L.grev), *glr = f32(L.glr);
+  LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, log_gate, glf, st), "gate_cumsum");
+  LLOPS_HIP(llops::launch_gate_reverse_shift(log_gate, n, R, grev, st), "gate_reverse");
+  LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, grev, glr, st), "gate_cumsum");
+  // num = M V and, normalised, M 1 (all-ones values DVo wide; column 0 read)
+  float* num = f32(L.b.num);
+  const uint16_t* vv = static_cast<const uint16_t*>(V);
+  LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st), "attn num");
+  float* den = nullptr;
+  if (s->normalize) {
+    den = f32(L.gden);
+    LLOPS_HIP(llops::launch_fill_ones_bf16(u16(L.gones), R * DVo, st), "ones");
+    LLOPS_HIP(gated_attn_on_features(s, m, DVo, phq, phk, u16(L.gones), glf, den, seg, gseg, st),
+              "attn den");
+  }
+  uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
+  uint16_t *ra = u16(L.b.ra), *rb = u16(L.b.rb);
+  LLOPS_HIP(llops::launch_make_ab(num, den, dO, vv, dv, MA, n, R, s->normalize,
+                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, 1, DVo, st),
+            "make_ab");
+  uint16_t* vp = u16(L.b.vp);
+  float* tmp = f32(L.b.tmp);
+  float* dc = f32(L.dc);
+  uint16_t *dphq = u16(L.b.dphq), *dphk = u16(L.b.dphk);
+  // dphi_Q_i = sum_{j<=i} exp(c_i - c_j) (a_i . b_j) phi_K_j; dc_i += phi_Q,i . dphi_Q,i.
+  // The gate gradient at each segment start t0 is exact from states:
+  // dg_t0 = <U_t0, P_t0-1> with P the pass's prefix state sum_{j<t0} (decayed to t0-1)
+  // b_j phi_K,j^T and U_t0 = sum_{i>=t0} exp(c_i - c_{t0-1}) a_i phi_Q,i^T, summed
+  // over the W-column slices; between segment starts the suffix sums of dc fill in.
+  const llops_shape_t tMW = feat_attn_shape(s, MA, W);
+  const llops::AttnShape aMW = attn_shape(&tMW, true, kGatedBwdWG);
+  const int64_t perMW = static_cast<int64_t>(MA) * W + MA;
+  float *seg2 = f32(L.seg2), *dgb = f32(L.dgb);
+  for (int p0 = 0; p0 < m; p0 += W) {
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
+    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, vp, glf, tmp, seg, gseg, st), "attn dphi_q");
+    LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phq, m, p0, W, n, R, 0, 1.f, p0 == 0 ? 1 : 0, dc,
+                                       st),
+              "rowdot");
+    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
+    LLOPS_HIP(llops::launch_seg_state32_anchored(aMW, a, vp, glf, gseg, seg2, st), "anchored");
+    LLOPS_HIP(llops::launch_seg_rscan_gated(BH, aMW.nseg, perMW, static_cast<int64_t>(MA) * W,
+                                            seg2, gseg, st),
+              "rscan");
+    LLOPS_HIP(llops::launch_seg_dot(BH, aMW.nseg, perMW, static_cast<int64_t>(MA) * W, seg, seg2,
+                                    p0 == 0 ? 1 : 0, dgb, st),
+              "segdot");
+  }
+  // dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j) phi_Q_i over the reversed
+  // sequence with its shifted gates; dc_j -= phi_K,j . dphi_K,j
+  for (int p0 = 0; p0 < m; p0 += W) {
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
+    LLOPS_HIP(gated_attn_on_features(s, MA, W, rb, ra, vp, glr, tmp, seg, gseg, st),
+              "attn dphi_k");
+    LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 1, -1.f, 0, dc, st), "rowdot");
+    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
+  }
+  // dV_j = sum_{i>=j} M_ij dnum_i over the reversed sequence
+  uint16_t *rphq = u16(L.b.rphq), *rphk = u16(L.b.rphk);
+  LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
+  LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
+  LLOPS_HIP(gated_attn_on_features(s, m, dv, rphk, rphq, dn, glr, tmp, seg, gseg, st), "attn dv");
+  LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
+  // dlog_gate_l = sum_{i>=l} dc_i, anchored at the exact segment-start values
+  LLOPS_HIP(llops::launch_seg_bridge_dg(dc, BH, n, aMW.seg_len, aMW.nseg, dgb, dlog_gate, st),
+            "bridge");
+  LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dphq, 1, dQ, dtheta_q, fb, st),
+            "featmap_bwd q");
+  LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dphk, 1, dK, dtheta_k, fb, st),
+            "featmap_bwd k");
+  return LLOPS_OK;
 }
 
 static llops_status_t decode_impl(const llops_shape_t* s, const void* q, const void* k,

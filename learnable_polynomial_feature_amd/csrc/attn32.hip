@@ -113,7 +113,11 @@ struct Seg32Geom {
 // ============================================================================
 // Pass 1: per-segment (dS, dz) = (phi_K^T V, phi_K^T 1)
 // ============================================================================
-template <int M, int DV, bool GATED>
+// ANCHOR (gated only): the segment's sum anchored at its start instead of
+// carried to its end, sum_k exp(c_k - c_{t0-1}) phi_K,k v_k^T: weights
+// exp(D + L_k) with D the sum of the segment's earlier chunks, no decay of
+// the accumulator (every exponent still <= 0 for g <= 0).
+template <int M, int DV, bool GATED, bool ANCHOR = false>
 __global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                                                      const uint16_t* __restrict__ v,
@@ -203,7 +207,17 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
       const int valid = left < kC ? static_cast<int>(left) : kC;
       const float T = gls[valid - 1];
       float wv[16];
-      gate_carry(gls, hh, T, valid, wv);
+      if constexpr (ANCHOR) {
+        float L[16];
+        gate_rows(gls, hh, L);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int tok = 8 * (k >> 2) + 4 * hh + (k & 3);
+          wv[k] = tok < valid ? __expf(gsum + L[k]) : 0.f;
+        }
+      } else {
+        gate_carry(gls, hh, T, valid, wv);
+      }
 #pragma unroll
       for (int ks = 0; ks < kC / 16; ++ks) {
         vb[ks] = scale_frag(vb[ks], wv + 8 * ks);
@@ -212,11 +226,13 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                                  pack_bf16x2(wv[8 * ks + 4], wv[8 * ks + 5]),
                                  pack_bf16x2(wv[8 * ks + 6], wv[8 * ks + 7])});
       }
-      const float decay = __expf(T);
+      if constexpr (!ANCHOR) {
+        const float decay = __expf(T);
 #pragma unroll
-      for (int f = 0; f < FT; ++f) S[f] *= decay;
+        for (int f = 0; f < FT; ++f) S[f] *= decay;
 #pragma unroll
-      for (int z = 0; z < G::ZT; ++z) Z[z] *= decay;
+        for (int z = 0; z < G::ZT; ++z) Z[z] *= decay;
+      }
       gsum += T;
     }
 #pragma unroll
@@ -661,13 +677,13 @@ __global__ __launch_bounds__(256) void gate_cumsum32(int64_t n, int64_t nch, int
   if (live) L[bh * nch * kC + tok] = x;
 }
 
-template <int M, int DV, bool GATED>
+template <int M, int DV, bool GATED, bool ANCHOR = false>
 hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, const float* gl,
                           float* gseg, float* seg, hipStream_t st) {
   using G = Seg32Geom<M, DV>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, gseg};
   const size_t lds = 2ull * (kC * G::MP + kC * G::VP + (GATED ? kGL : 0)) * sizeof(uint16_t);
-  auto* kern = seg_state32<M, DV, GATED>;
+  auto* kern = seg_state32<M, DV, GATED, ANCHOR>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
@@ -750,6 +766,17 @@ hipError_t launch_seg_state32_gated(const AttnShape& s, const uint16_t* phik, co
     case 256128: return launch_state_t<256, 128, true>(s, phik, v, gl, gseg, seg, st);
     case 128064: return launch_state_t<128, 64, true>(s, phik, v, gl, gseg, seg, st);
     case 64064: return launch_state_t<64, 64, true>(s, phik, v, gl, gseg, seg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_seg_state32_anchored(const AttnShape& s, const uint16_t* phik,
+                                      const uint16_t* v, const float* gl, float* gseg, float* seg,
+                                      hipStream_t st) {
+  switch (key32(s)) {
+    case 256128: return launch_state_t<256, 128, true, true>(s, phik, v, gl, gseg, seg, st);
+    case 128064: return launch_state_t<128, 64, true, true>(s, phik, v, gl, gseg, seg, st);
+    case 64064: return launch_state_t<64, 64, true, true>(s, phik, v, gl, gseg, seg, st);
     default: return hipErrorInvalidValue;
   }
 }

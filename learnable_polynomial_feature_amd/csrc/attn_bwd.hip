@@ -72,14 +72,14 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
                                               int64_t n, int64_t rows, int normalize, float delta,
                                               uint16_t* __restrict__ a, uint16_t* __restrict__ ra,
                                               uint16_t* __restrict__ b, uint16_t* __restrict__ rb,
-                                              uint16_t* __restrict__ rdnum, int rev) {
+                                              uint16_t* __restrict__ rdnum, int rev, int den_ld) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int l = threadIdx.x & 31;
   const bool live = r < rows;  // every lane joins the shuffles below
   const int64_t rc = live ? r : rows - 1;
   const int64_t bh = rc / n, i = rc - bh * n;
   const int64_t rr = rev ? bh * n + (n - 1 - i) : rc;
-  const float den = normalize ? den1[rc * 16] + delta : 1.f;
+  const float den = normalize ? den1[rc * den_ld] + delta : 1.f;
   const float inv = 1.f / den;
   const int c0 = 8 * l;  // this lane's columns c0 .. c0+7
   float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -162,13 +162,246 @@ hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st) {
 hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
-                          int rev, hipStream_t st) {
+                          int rev, int den_ld, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  if ((rows + 7) / 8 > 0x7fffffffLL || dv % 8 || MA % 8 || MA > 256 || MA <= dv)
+  if ((rows + 7) / 8 > 0x7fffffffLL || dv % 8 || MA % 8 || MA > 256 || MA <= dv || den_ld < 1)
     return hipErrorInvalidValue;
   LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 7) / 8)),
                dim3(256), 0, st, num, den1, G, V, dv, MA, n, rows, normalize, delta, a, ra, b, rb,
-               rdnum, rev);
+               rdnum, rev, den_ld);
+  return hipGetLastError();
+}
+
+// ---- gated backward helpers ------------------------------------------------
+
+// Gates of the reversed sequence: out[bh][l] = g[bh][n - l] for l >= 1 and 0
+// at l = 0, so that key i' reaches query j' >= i' of the reversed sequence
+// with the forward pair's weight exp(g_{j+1} + ... + g_i) (i = n-1-i',
+// j = n-1-j'); the state entering token 0 is zero, so out[0] is never used.
+__global__ __launch_bounds__(256) void gate_reverse_shift(const float* __restrict__ g, int64_t n,
+                                                          int64_t rows, float* __restrict__ out) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int64_t bh = r / n, l = r - bh * n;
+  out[r] = l == 0 ? 0.f : g[bh * n + (n - l)];
+}
+
+// count bf16 ones (count a multiple of 8), 16-byte stores
+__global__ __launch_bounds__(256) void fill_ones_bf16(uint16_t* __restrict__ dst, int64_t pieces) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < pieces) st16(dst + i * 8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+}
+
+// acc[rr] (=|+=) sign * sum_{c < width} x[r][c] * phi[rr][poff + c] for every row
+// r of a [rows][xw] fp32 block, rr = r or its reversal inside its sequence of
+// n rows; one 32-lane group per row, width <= 128 and a multiple of 4.
+__global__ __launch_bounds__(256) void rowdot_acc(const float* __restrict__ x, int xw,
+                                                  const uint16_t* __restrict__ phi, int pw,
+                                                  int poff, int width, int64_t n, int64_t rows,
+                                                  int rev, float sign, int init,
+                                                  float* __restrict__ acc) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  const bool live = r < rows;  // every lane joins the shuffles below
+  const int64_t rc = live ? r : rows - 1;
+  const int64_t bh = rc / n, i = rc - bh * n;
+  const int64_t rr = rev ? bh * n + (n - 1 - i) : rc;
+  float dot = 0.f;
+  const int c0 = 4 * l;
+  if (c0 < width) {
+    const u32x4 xv = ld16(x + rc * xw + c0);
+    const u32x2 pv = *reinterpret_cast<const u32x2*>(phi + rr * pw + poff + c0);
+    dot = __uint_as_float(xv[0]) * __uint_as_float(pv[0] << 16) +
+          __uint_as_float(xv[1]) * __uint_as_float(pv[0] & 0xFFFF0000u) +
+          __uint_as_float(xv[2]) * __uint_as_float(pv[1] << 16) +
+          __uint_as_float(xv[3]) * __uint_as_float(pv[1] & 0xFFFF0000u);
+  }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+  if (live && l == 0) acc[rr] = init ? sign * dot : fmaf(sign, dot, acc[rr]);
+}
+
+// y[bh][i] = sum_{i' >= i} x[bh][i'] for each sequence of n values: one
+// workgroup per sequence, each thread a contiguous run, run totals suffix-
+// summed in a fixed order
+__global__ __launch_bounds__(256) void rev_cumsum(const float* __restrict__ x, int64_t n,
+                                                  float* __restrict__ y) {
+  __shared__ float part[256];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 255) / 256;
+  const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
+  const float* xb = x + bh * n;
+  float* yb = y + bh * n;
+  float s = 0.f;
+  for (int64_t i = lo; i < hi; ++i) s += xb[i];
+  part[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int t = 255; t >= 0; --t) {
+      const float v = part[t];
+      part[t] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  float acc = part[tid];
+  for (int64_t i = hi - 1; i >= lo; --i) {
+    acc += xb[i];
+    yb[i] = acc;
+  }
+}
+
+// Suffix states from segment sums anchored at each segment's start:
+// U_g = dU_g + exp(G_g) U_{g+1}, in place over the segments of each (b, h)
+// (G_g the sum of segment g's log gates); only the first mdv entries of a
+// segment slot are scanned.
+__global__ __launch_bounds__(256) void seg_rscan_gated(int nseg, int64_t per, int64_t mdv,
+                                                       float* __restrict__ seg,
+                                                       const float* __restrict__ gseg) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t bh = blockIdx.y;
+  if (e >= mdv) return;
+  float* p = seg + bh * nseg * per + e;
+  const float* gs = gseg + bh * nseg;
+  float acc = 0.f;
+  for (int gi = nseg - 1; gi >= 0; --gi) {
+    acc = fmaf(__expf(gs[gi]), acc, p[gi * per]);
+    p[gi * per] = acc;
+  }
+}
+
+// dgb[bh][g] (=|+=) <P_g, U_g> over the first mdv entries of segment g's slots
+// of two [BH][nseg][per] buffers; a fixed-order workgroup reduction.
+__global__ __launch_bounds__(256) void seg_dot(int nseg, int64_t per, int64_t mdv,
+                                               const float* __restrict__ P,
+                                               const float* __restrict__ U, int init,
+                                               float* __restrict__ dgb) {
+  __shared__ float red[256];
+  const int g = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const float* pp = P + (bh * nseg + g) * per;
+  const float* uu = U + (bh * nseg + g) * per;
+  float s = 0.f;
+  for (int64_t e = threadIdx.x; e < mdv; e += 256) s = fmaf(pp[e], uu[e], s);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float* d = dgb + bh * nseg + g;
+    *d = init ? red[0] : *d + red[0];
+  }
+}
+
+// dg inside segment g of each sequence from the per-token terms dc and the
+// boundary values dgb (dg at each segment's first token; 0 past the end):
+// dg_l = dgb[g+1] + sum_{i=l}^{t1-1} dc_i - e (t1 - l) / (t1 - t0), where e is
+// what that suffix sum misses dgb[g] by at l = t0, so both ends are exact.
+__global__ __launch_bounds__(256) void seg_bridge_dg(const float* __restrict__ dc, int64_t n,
+                                                     int64_t seg_len, int nseg,
+                                                     const float* __restrict__ dgb,
+                                                     float* __restrict__ dg) {
+  __shared__ float later[256];  // sum of the runs after each thread's run
+  __shared__ float total;       // the whole segment's sum
+  const int g = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t t0 = g * seg_len, t1 = min(n, t0 + seg_len);
+  if (t0 >= t1) return;  // whole workgroup: t0, t1 are uniform
+  const int64_t len = t1 - t0;
+  const int64_t per = (len + 255) / 256;
+  const int64_t lo = min(t1, t0 + tid * per), hi = min(t1, lo + per);
+  const float* x = dc + bh * n;
+  float* y = dg + bh * n;
+  float s = 0.f;
+  for (int64_t i = lo; i < hi; ++i) s += x[i];
+  later[tid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int t = 255; t >= 0; --t) {
+      const float v = later[t];
+      later[t] = acc;
+      acc += v;
+    }
+    total = acc;
+  }
+  __syncthreads();
+  const float next = g + 1 < nseg ? dgb[bh * nseg + g + 1] : 0.f;
+  const float miss = next + total - dgb[bh * nseg + g];
+  float acc = later[tid];
+  for (int64_t i = hi - 1; i >= lo; --i) {
+    acc += x[i];
+    y[i] = next + acc - miss * static_cast<float>(t1 - i) / static_cast<float>(len);
+  }
+}
+
+hipError_t launch_seg_rscan_gated(int64_t BH, int nseg, int64_t per, int64_t mdv, float* seg,
+                                  const float* gseg, hipStream_t st) {
+  if (BH == 0 || nseg == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((mdv + 255) / 256), static_cast<unsigned>(BH));
+  LLOPS_LAUNCH("gated_bwd_rscan", st, seg_rscan_gated, grid, dim3(256), 0, st, nseg, per, mdv, seg,
+               gseg);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_dot(int64_t BH, int nseg, int64_t per, int64_t mdv, const float* P,
+                          const float* U, int init, float* dgb, hipStream_t st) {
+  if (BH == 0 || nseg == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(BH));
+  LLOPS_LAUNCH("gated_bwd_segdot", st, seg_dot, grid, dim3(256), 0, st, nseg, per, mdv, P, U, init,
+               dgb);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_bridge_dg(const float* dc, int64_t BH, int64_t n, int64_t seg_len, int nseg,
+                                const float* dgb, float* dg, hipStream_t st) {
+  if (BH == 0 || n == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(BH));
+  LLOPS_LAUNCH("gated_bwd_bridge", st, seg_bridge_dg, grid, dim3(256), 0, st, dc, n, seg_len, nseg,
+               dgb, dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_reverse_shift(const float* g, int64_t n, int64_t rows, float* out,
+                                     hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if ((rows + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("gate_reverse", st, gate_reverse_shift, dim3(static_cast<unsigned>((rows + 255) / 256)),
+               dim3(256), 0, st, g, n, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_ones_bf16(uint16_t* dst, int64_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  const int64_t pieces = count / 8;
+  if (count % 8 || (pieces + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_ones", st, fill_ones_bf16, dim3(static_cast<unsigned>((pieces + 255) / 256)),
+               dim3(256), 0, st, dst, pieces);
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw, int poff,
+                             int width, int64_t n, int64_t rows, int rev, float sign, int init,
+                             float* acc, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if ((rows + 7) / 8 > 0x7fffffffLL || width > 128 || width % 4 || xw % 4 || (pw % 2) ||
+      (poff % 4) || poff + width > pw || width > xw)
+    return hipErrorInvalidValue;
+  LLOPS_LAUNCH("gated_bwd_rowdot", st, rowdot_acc, dim3(static_cast<unsigned>((rows + 7) / 8)),
+               dim3(256), 0, st, x, xw, phi, pw, poff, width, n, rows, rev, sign, init, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_rev_cumsum(const float* x, int64_t BH, int64_t n, float* y, hipStream_t st) {
+  if (BH == 0 || n == 0) return hipSuccess;
+  if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("gated_bwd_revsum", st, rev_cumsum, dim3(static_cast<unsigned>(BH)), dim3(256), 0,
+               st, x, n, y);
   return hipGetLastError();
 }
 

@@ -80,7 +80,26 @@ hipError_t launch_fill_ones16(uint16_t* dst, int64_t rows, hipStream_t st);
 hipError_t launch_make_ab(const float* num, const float* den1, const float* G, const uint16_t* V,
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
-                          int rev, hipStream_t st);
+                          int rev, int den_ld, hipStream_t st);
+// Gated backward helpers: reversed-sequence gates (shifted by one), bf16
+// ones, row dots of an fp32 block against bf16 feature columns accumulated
+// per row (optionally into the reversed row), per-sequence suffix sums.
+hipError_t launch_gate_reverse_shift(const float* g, int64_t n, int64_t rows, float* out,
+                                     hipStream_t st);
+hipError_t launch_fill_ones_bf16(uint16_t* dst, int64_t count, hipStream_t st);
+hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw, int poff,
+                             int width, int64_t n, int64_t rows, int rev, float sign, int init,
+                             float* acc, hipStream_t st);
+hipError_t launch_rev_cumsum(const float* x, int64_t BH, int64_t n, float* y, hipStream_t st);
+// Exact gate gradient at segment starts: segment sums anchored at the start
+// (launch_seg_state32_anchored), their reverse scan into suffix states, the inner products with the forward pass's prefix
+// states, and the bridged per-segment suffix sums of the per-token terms.
+hipError_t launch_seg_rscan_gated(int64_t BH, int nseg, int64_t per, int64_t mdv, float* seg,
+                                  const float* gseg, hipStream_t st);
+hipError_t launch_seg_dot(int64_t BH, int nseg, int64_t per, int64_t mdv, const float* P,
+                          const float* U, int init, float* dgb, hipStream_t st);
+hipError_t launch_seg_bridge_dg(const float* dc, int64_t BH, int64_t n, int64_t seg_len, int nseg,
+                                const float* dgb, float* dg, hipStream_t st);
 
 // Linear-attention contraction over precomputed features.
 struct AttnShape {
@@ -142,6 +161,11 @@ hipError_t launch_seg_state_f32_gated(const AttnShape& a, const float* phik, con
 hipError_t launch_attn_out_f32_gated(const AttnShape& a, const float* phiq, const float* phik,
                                      const float* v, const float* log_gate, float* state,
                                      float* out, hipStream_t st);
+// Segment sums anchored at the segment start, sum_k exp(c_k - c_{t0-1}) phik_k v_k^T
+// (gate gradient of the backward; same seg layout).
+hipError_t launch_seg_state32_anchored(const AttnShape& a, const uint16_t* phik,
+                                      const uint16_t* v, const float* gl, float* gseg, float* seg,
+                                      hipStream_t st);
 // Causal scan with per-segment decays: prefix_{g+1} = exp(gseg[g]) prefix_g + seg[g].
 hipError_t launch_seg_scan_gated(const AttnShape& a, float* seg, const float* gseg,
                                  const float* S0, const float* z0, float* S_tot, float* z_tot,

@@ -199,7 +199,7 @@ def test_workspace_checks(L):
                                     FAKE, None, None, None, need, None)
     assert st == 1
     assert L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP) == 0
-    assert L.llops_workspace_bytes(ctypes.byref(s), 9) == 0
+    assert L.llops_workspace_bytes(ctypes.byref(s), 10) == 0
     assert L.llops_workspace_bytes(ctypes.byref(_shape(p=0)), _lib.ENTRY_CAUSAL) == 0
 
 
@@ -441,3 +441,34 @@ def test_gated_decode_requires_gate(L):
     st = L.llops_gated_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    FAKE, FAKE, FAKE, need - 1, None)
     assert st == 3, _err(L)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(m=96), 2), (dict(p=3), 2), (dict(m=256, dv=64), 2), (dict(m=128, dv=128), 2),
+    (dict(in_dtype=_lib.F32), 2), (dict(delta=-1.0), 1),
+])
+@fake_ptr
+def test_gated_bwd_validation(L, bad, code):
+    s = _shape(**{"t": 4, **bad})
+    ws = L.llops_workspace_bytes(ctypes.byref(_shape(t=4)), _lib.ENTRY_GATED_CAUSAL_BWD)
+    assert ws > 0
+    assert L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL_BWD) == 0
+    st = L.llops_linattn_gated_causal_bwd(ctypes.byref(s), *([FAKE] * 14), ws, None)
+    assert st == code, _err(L)
+
+
+@fake_ptr
+def test_gated_bwd_pointers_and_workspace(L):
+    s = _shape(t=4)
+    need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_GATED_CAUSAL_BWD)
+    assert need > L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_CAUSAL_BWD)
+    args = [FAKE] * 14
+    args[5] = None  # log_gate
+    st = L.llops_linattn_gated_causal_bwd(ctypes.byref(s), *args, need, None)
+    assert st == 1 and "log_gate is null" in _err(L)
+    args = [FAKE] * 14
+    args[12] = None  # dlog_gate (index 13 is ws)
+    st = L.llops_linattn_gated_causal_bwd(ctypes.byref(s), *args, need, None)
+    assert st == 1 and "dlog_gate is null" in _err(L)
+    st = L.llops_linattn_gated_causal_bwd(ctypes.byref(s), *([FAKE] * 14), need - 1, None)
+    assert st == 3 and "workspace" in _err(L)
