@@ -221,38 +221,6 @@ __global__ __launch_bounds__(256) void rowdot_acc(const float* __restrict__ x, i
   if (live && l == 0) acc[rr] = init ? sign * dot : fmaf(sign, dot, acc[rr]);
 }
 
-// y[bh][i] = sum_{i' >= i} x[bh][i'] for each sequence of n values: one
-// workgroup per sequence, each thread a contiguous run, run totals suffix-
-// summed in a fixed order
-__global__ __launch_bounds__(256) void rev_cumsum(const float* __restrict__ x, int64_t n,
-                                                  float* __restrict__ y) {
-  __shared__ float part[256];
-  const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 255) / 256;
-  const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
-  const float* xb = x + bh * n;
-  float* yb = y + bh * n;
-  float s = 0.f;
-  for (int64_t i = lo; i < hi; ++i) s += xb[i];
-  part[tid] = s;
-  __syncthreads();
-  if (tid == 0) {
-    float acc = 0.f;
-    for (int t = 255; t >= 0; --t) {
-      const float v = part[t];
-      part[t] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-  float acc = part[tid];
-  for (int64_t i = hi - 1; i >= lo; --i) {
-    acc += xb[i];
-    yb[i] = acc;
-  }
-}
-
 // Suffix states from segment sums anchored at each segment's start:
 // U_g = dU_g + exp(G_g) U_{g+1}, in place over the segments of each (b, h)
 // (G_g the sum of segment g's log gates); only the first mdv entries of a
@@ -394,14 +362,6 @@ hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw
     return hipErrorInvalidValue;
   LLOPS_LAUNCH("gated_bwd_rowdot", st, rowdot_acc, dim3(static_cast<unsigned>((rows + 7) / 8)),
                dim3(256), 0, st, x, xw, phi, pw, poff, width, n, rows, rev, sign, init, acc);
-  return hipGetLastError();
-}
-
-hipError_t launch_rev_cumsum(const float* x, int64_t BH, int64_t n, float* y, hipStream_t st) {
-  if (BH == 0 || n == 0) return hipSuccess;
-  if (BH > 0x7fffffffLL) return hipErrorInvalidValue;
-  LLOPS_LAUNCH("gated_bwd_revsum", st, rev_cumsum, dim3(static_cast<unsigned>(BH)), dim3(256), 0,
-               st, x, n, y);
   return hipGetLastError();
 }
 

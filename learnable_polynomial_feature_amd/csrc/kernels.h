@@ -83,14 +83,13 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
                           int rev, int den_ld, hipStream_t st);
 // Gated backward helpers: reversed-sequence gates (shifted by one), bf16
 // ones, row dots of an fp32 block against bf16 feature columns accumulated
-// per row (optionally into the reversed row), per-sequence suffix sums.
+// per row (optionally into the reversed row).
 hipError_t launch_gate_reverse_shift(const float* g, int64_t n, int64_t rows, float* out,
                                      hipStream_t st);
 hipError_t launch_fill_ones_bf16(uint16_t* dst, int64_t count, hipStream_t st);
 hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw, int poff,
                              int width, int64_t n, int64_t rows, int rev, float sign, int init,
                              float* acc, hipStream_t st);
-hipError_t launch_rev_cumsum(const float* x, int64_t BH, int64_t n, float* y, hipStream_t st);
 // Exact gate gradient at segment starts: segment sums anchored at the start
 // (launch_seg_state32_anchored), their reverse scan into suffix states, the inner products with the forward pass's prefix
 // states, and the bridged per-segment suffix sums of the per-token terms.
