@@ -273,3 +273,59 @@ def test_gated_full_size_sampled_heads(lib):
         assert rel_fro(host(out[0, h]), ro) <= TOL_BF16, h
         assert rel_fro(host(S[0, h]), rS) <= TOL_BF16, h
         assert rel_fro(host(z[0, h]), rz) <= TOL_BF16, h
+
+
+@pytest.mark.parametrize("name", ["causal_p2_m64", "causal_p3_m128"])
+def test_gated_workload_shapes(lib, name):
+    """The two mid-size causal workloads (4 x 12 x 2048, m = 64; 2 x 16 x 8192,
+    p = 3, t = 8, m = 128, rows unit-L2 x 2) gated, every head against the
+    oracle's recurrence."""
+    from learnable_polynomial_feature_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    x, g = _inputs(w)
+    lg = log_gates(w, mu=4.0)
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
+    announce(f"gated workload {name}")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                   g["theta_k"], torch.from_numpy(lg).cuda(),
+                                                   chunk=w.chunk, return_state=True, **kw)
+    torch.cuda.synchronize()
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      **kw)
+    assert rel_fro(host(out), ro) <= TOL_BF16
+    assert rel_fro(host(S), rS) <= TOL_BF16
+    assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+def test_gated_decode_full_size(lib):
+    """Batch 128 x 32 heads (d = dv = 128, m = 256), the decode benchmark's
+    launch configuration: 20 gated steps from a synthetic positive state;
+    sampled (b, h) slices against the oracle's recurrence over the same
+    tokens and gates."""
+    from learnable_polynomial_feature_amd.workloads import WORKLOADS, decode_tokens
+    w = WORKLOADS["decode_b128_h32"]
+    steps = 20
+    B, H, m, dv = w.batch, w.heads, w.m, w.dv
+    th = generate(w.replace(n=1, batch=1))
+    gq, gk = dev(th["theta_q"], torch.bfloat16), dev(th["theta_k"], torch.bfloat16)
+    rng = np.random.default_rng(21)
+    S0 = (0.05 * rng.standard_normal((B, H, m, dv))).astype(np.float32)
+    z0 = np.abs(0.05 * rng.standard_normal((B, H, m))).astype(np.float32)
+    S, z = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    tok = decode_tokens(w, steps)
+    lg = np.stack([decode_step_gates(w, s) for s in range(steps)])  # [steps, B, H]
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
+    q, k, v = (dev(tok[c], torch.bfloat16) for c in ("q", "k", "v"))
+    lgd = torch.from_numpy(lg).cuda()
+    announce("gated decode full size 128 x 32")
+    outs = [lib.llops_gated_decode_step(q[s], k[s], v[s], gq, gk, lgd[s], S, z, **kw)
+            for s in range(steps)]
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], axis=2)  # [B, H, steps, dv]
+    for b, h in [(0, 0), (5, 17), (127, 31)]:
+        ro, rS, rz = O.gated_recurrent(tok["q"][:, b, h], tok["k"][:, b, h], tok["v"][:, b, h],
+                                       th["theta_q"][h], th["theta_k"][h], lg[:, b, h],
+                                       S0=S0[b, h], z0=z0[b, h], **kw)
+        assert rel_fro(got[b, h], ro) <= TOL_BF16, (b, h)
+        assert rel_fro(host(S[b, h]), rS) <= TOL_BF16, (b, h)
+        assert rel_fro(host(z[b, h]), rz) <= TOL_BF16, (b, h)
