@@ -126,3 +126,24 @@ def test_gated_bwd_full_size_sampled(lib):
         print(f"[gated_bwd full] head {h} {errs}", flush=True)
         for nm, err in errs.items():
             assert err <= TOL_BF16, (h, nm, err)
+
+
+def test_gated_bwd_shared_aliased_theta(lib):
+    """One shared Theta passed as both theta_q and theta_k: the two gradients
+    come back apart, each summed over the heads."""
+    w = _w(2, 3, 200, 64, 64, 64, 4, True, True)
+    x = generate(w)
+    th = x["theta_q"][0]
+    G = dout(w)
+    lg = log_gates(w, mu=2.0)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    gth = dev(th, torch.bfloat16)
+    announce("gated_bwd shared aliased theta")
+    got = lib.llops_linattn_gated_causal_bwd(g["Q"], g["K"], g["V"], gth, gth,
+                                             dev(lg, torch.float32), dev(G, torch.float32),
+                                             square=True, normalize=True, delta=w.delta)
+    torch.cuda.synchronize()
+    want = O.gated_causal_bwd_bh(x["Q"], x["K"], x["V"], th, th, lg, G, square=True,
+                                 normalize=True, delta=w.delta)
+    for nm, a, b in zip(NAMES, got, want):
+        assert rel_fro(host(a), b) <= TOL_BF16, nm

@@ -329,3 +329,31 @@ def test_gated_decode_full_size(lib):
         assert rel_fro(got[b, h], ro) <= TOL_BF16, (b, h)
         assert rel_fro(host(S[b, h]), rS) <= TOL_BF16, (b, h)
         assert rel_fro(host(z[b, h]), rz) <= TOL_BF16, (b, h)
+
+
+@pytest.mark.parametrize("case", [
+    # B, H, n, m, dv, d, shared theta (aliased q/k), chunk hint
+    (2, 2, 333, 64, 64, 64, True, 64),
+    (1, 3, 290, 128, 64, 64, False, 32),
+    (64, 9, 77, 64, 64, 64, False, 0),     # 576 sequences: one segment each
+    (3, 2, 1, 256, 128, 128, True, 0),
+])
+def test_gated_edge_layouts(lib, case):
+    """Shared Theta passed as both theta_q and theta_k, the 32-token chunk
+    hint, many short sequences (one segment per sequence) and n = 1."""
+    B, H, n, m, dv, d, shared, chunk = case
+    w = _w(B, H, n, d, dv, m, 2, 4, chunk=chunk)
+    x, g = _inputs(w)
+    tq, tk = (x["theta_q"][0], x["theta_q"][0]) if shared else (x["theta_q"], x["theta_k"])
+    gq, gk = (g["theta_q"][0], g["theta_q"][0]) if shared else (g["theta_q"], g["theta_k"])
+    lg = log_gates(w, mu=2.0)
+    kw = dict(square=True, normalize=True, delta=1e-6)
+    announce(f"gated edge layout {case}")
+    out, S, z = lib.llops_linattn_gated_causal_fwd(g["Q"], g["K"], g["V"], gq, gk,
+                                                   torch.from_numpy(lg).cuda(), chunk=chunk,
+                                                   return_state=True, **kw)
+    torch.cuda.synchronize()
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], tq, tk, lg, **kw)
+    assert rel_fro(host(out), ro) <= TOL_BF16
+    assert rel_fro(host(S), rS) <= TOL_BF16
+    assert rel_fro(host(z), rz) <= TOL_BF16
