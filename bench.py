@@ -464,10 +464,32 @@ def bench_decode(w, steps, torch, lib):
         lib.llops_decode_step(q[s], k[s], v[s], gq, gk, S, z, out=out, workspace=ws, **kw)
     S.copy_(S_init)
     z.copy_(z_init)
-    del S_init, z_init
+    torch.cuda.synchronize()
+    # the whole loop captured once as a HIP graph (no host launch work per
+    # step), replayed from the prefix state
+    log(f"decode: capturing {steps} steps as one graph")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        for s in range(steps):
+            lib.llops_decode_step(q[s], k[s], v[s], gq, gk, S, z, out=out, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    S.copy_(S_init)
+    z.copy_(z_init)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph_ms = t0.elapsed_time(t1) / steps
+    del graph
+    S.copy_(S_init)
+    z.copy_(z_init)
+    del S_init, z_init
+    torch.cuda.synchronize()
     log(f"decode: timing {steps} steps")
     # a step is a few short kernels: the per-launch events of the kernel timer
     # would sit between them, so the steps are timed without it and the
@@ -507,7 +529,7 @@ def bench_decode(w, steps, torch, lib):
                                         workspace=ws, **kw)
     torch.cuda.synchronize()
     gkern = {kk: sum(vv) / len(vv) for kk, vv in timer.durations_ms().items()}
-    gated = {"steps": gsteps, "ms_per_step": round(gms, 4),
+    gated = {"graph_ms_per_step": graph_ms, "steps": gsteps, "ms_per_step": round(gms, 4),
              "tokens_per_s": round(B / (gms * 1e-3), 1),
              "GBps": round(decode_bytes(w) / (gms * 1e-3) / 1e9, 1),
              "kernel_ms": {kk: round(vv, 4) for kk, vv in gkern.items()}}
@@ -631,6 +653,7 @@ def main():
     if not args.no_decode:
         wd = WORKLOADS["decode_b128_h32"]
         dms, dkern, dgated = bench_decode(wd, args.decode_steps, torch, lib)
+        graph_ms = dgated.pop("graph_ms_per_step")
         gb = decode_bytes(wd) / (dms * 1e-3) / 1e9
         st_ms = dkern.get("decode_state")
         st_gb = decode_state_bytes(wd) / (st_ms * 1e-3) / 1e9 if st_ms else None
@@ -638,6 +661,11 @@ def main():
             "workload": wd.name, "steps": args.decode_steps, "ms_per_step": round(dms, 4),
             "tokens_per_s": round(wd.batch / (dms * 1e-3), 1),
             "GBps": round(gb, 1), "hbm_frac": round(gb / PEAK_HBM_GBPS, 4),
+            "graph": {"ms_per_step": round(graph_ms, 4),
+                      "tokens_per_s": round(wd.batch / (graph_ms * 1e-3), 1),
+                      "GBps": round(decode_bytes(wd) / (graph_ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(decode_bytes(wd) / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                      "note": "the whole loop captured once as a HIP graph and replayed"},
             "kernel_ms": {k: round(v, 4) for k, v in dkern.items()},
             "roofline": None if st_gb is None else {
                 "kernel": "decode_state", "bound": "hbm", "achieved": round(st_gb, 1),
