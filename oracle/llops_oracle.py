@@ -337,6 +337,68 @@ def causal_attn_bwd(Pq, Pk, V, G, normalize=False, delta=0.0):
     return dM @ Pk, dM.T @ Pq, M.T @ dnum
 
 
+def causal_attn_bwd_state(Pq, Pk, V, G, S0, z0, normalize=False, delta=0.0):
+    """causal_attn_bwd for the contraction continued from an initial state
+    (S0 [m, dv], z0 [m]; causal_quadratic's S0/z0): with
+      num = M V + Pq S0,  den = M 1 + Pq z0 + delta,
+    dnum and dden as before, dM = tril(dnum V^T + dden 1^T), and
+      dPq = dM Pk + dnum S0^T + dden z0^T,  dPk = dM^T Pq,  dV = M^T dnum,
+      dS0 = Pq^T dnum,  dz0 = Pq^T dden
+    ([LLoPS-arXiv] Sec. 1 streaming form; [LowRank-blog] Performer section;
+    [SLAY-notes] key design 3). Returns (dPq, dPk, dV, dS0, dz0)."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    S0, z0 = _f64(S0), _f64(z0)
+    M = np.tril(Pq @ Pk.T)
+    num = M @ V + Pq @ S0
+    if normalize:
+        den = M.sum(axis=1) + Pq @ z0 + delta
+        out = num / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(Pq.shape[0])
+    dM = np.tril(dnum @ V.T + dden[:, None])
+    dPq = dM @ Pk + dnum @ S0.T + np.outer(dden, z0)
+    return dPq, dM.T @ Pq, M.T @ dnum, Pq.T @ dnum, Pq.T @ dden
+
+
+def causal_bwd_state(Q, K, V, theta_q, theta_k, G, S0, z0, square=False, normalize=False,
+                     delta=0.0):
+    """causal_bwd from an initial state: (dQ, dK, dV, dTheta_q, dTheta_k, dS0, dz0)."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    dPq, dPk, dV, dS0, dz0 = causal_attn_bwd_state(Pq, Pk, V, G, S0, z0, normalize, delta)
+    dQ, dtq = featmap_bwd(Q, theta_q, dPq, square)
+    dK, dtk = featmap_bwd(K, theta_k, dPk, square)
+    return dQ, dK, dV, dtq, dtk, dS0, dz0
+
+
+def causal_bwd_state_bh(Q, K, V, theta_q, theta_k, G, S0, z0, **kw):
+    """causal_bwd_state over [B, H, n, .] tensors, S0 [B, H, m, dv], z0 [B, H, m];
+    a shared theta's gradient sums over the heads."""
+    theta_q, theta_k = np.asarray(theta_q), np.asarray(theta_k)
+    B, H = Q.shape[:2]
+    dQ, dK, dV = np.zeros(Q.shape), np.zeros(K.shape), np.zeros(V.shape)
+    dtq, dtk = np.zeros(theta_q.shape), np.zeros(theta_k.shape)
+    dS0, dz0 = np.zeros(np.shape(S0)), np.zeros(np.shape(z0))
+    for b in range(B):
+        for h in range(H):
+            r = causal_bwd_state(Q[b, h], K[b, h], V[b, h], _theta_for(theta_q, h),
+                                 _theta_for(theta_k, h), G[b, h], S0[b, h], z0[b, h], **kw)
+            dQ[b, h], dK[b, h], dV[b, h] = r[0], r[1], r[2]
+            dS0[b, h], dz0[b, h] = r[5], r[6]
+            if theta_q.ndim == 5:
+                dtq[h] += r[3]
+            else:
+                dtq += r[3]
+            if theta_k.ndim == 5:
+                dtk[h] += r[4]
+            else:
+                dtk += r[4]
+    return dQ, dK, dV, dtq, dtk, dS0, dz0
+
+
 def causal_attn_bwd_chunked(Pq, Pk, V, G, normalize=False, delta=0.0, chunk=256):
     """causal_attn_bwd without the n x n matrix, for long sequences: the same
     sums split at chunk boundaries. Prefix states S = sum Pk^T V, z = sum Pk

@@ -660,3 +660,76 @@ def test_gated_bwd_gate_gradient_closed_form():
     want = np.array([sum(a ** (i - j) for i in range(l, n) for j in range(l))
                      for l in range(n)])
     assert np.allclose(dg, want, rtol=1e-13, atol=1e-15)
+
+
+# ---- causal backward from an initial state -----------------------------------
+
+def _state_loss(Q, K, V, tq, tk, S0, z0, G, **kw):
+    # the chunked recurrent form (an independent formulation of the forward)
+    out = O.causal_chunked(Q, K, V, tq, tk, chunk=4, S0=S0, z0=z0, **kw)[0]
+    return float((G * out).sum())
+
+
+@pytest.mark.parametrize("square,normalize", [(False, False), (True, True)])
+def test_causal_bwd_state_central_differences(square, normalize):
+    """Every entry of Q, K, V, Theta_q, Theta_k, S0 and z0 against central
+    differences of sum(G * causal_quadratic(..., S0, z0))."""
+    rng = np.random.default_rng(80 + normalize)
+    n, d, dv, m, p, t = 6, 3, 2, 4, 2, 2
+    Q, K = 0.7 * rng.standard_normal((n, d)), 0.7 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = 0.6 * rng.standard_normal((p, t, d, m)), 0.6 * rng.standard_normal((p, t, d, m))
+    S0 = 0.3 * rng.standard_normal((m, dv))
+    z0 = np.abs(0.3 * rng.standard_normal(m))
+    G = rng.standard_normal((n, dv))
+    kw = dict(square=square, normalize=normalize, delta=0.5)
+    got = O.causal_bwd_state(Q, K, V, tq, tk, G, S0, z0, **kw)
+    args = [Q, K, V, tq, tk, S0, z0]
+    order = [0, 1, 2, 3, 4, 5, 6]
+    h = 1e-6
+    for which, grad in zip(order, got):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            num[idx] = (_state_loss(*ap, G, **kw) - _state_loss(*am, G, **kw)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), which
+
+
+def test_causal_bwd_zero_state_is_causal_bwd():
+    rng = np.random.default_rng(83)
+    n, m, dv = 9, 4, 3
+    Pq, Pk = np.abs(rng.standard_normal((n, m))), np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    want = O.causal_attn_bwd(Pq, Pk, V, G, normalize=True, delta=0.3)
+    got = O.causal_attn_bwd_state(Pq, Pk, V, G, np.zeros((m, dv)), np.zeros(m), normalize=True,
+                                  delta=0.3)
+    for a, b in zip(got[:3], want):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_causal_bwd_state_is_prefix_gradient():
+    """The initial state is what a prefix leaves behind: with S0, z0 built from
+    a prefix of k tokens, dS0 and dz0 chained back through the prefix's
+    S = Pk_pre^T V_pre, z = Pk_pre^T 1 give the prefix keys' and values'
+    gradient contributions of the whole sequence's backward (rows k.. of G)."""
+    rng = np.random.default_rng(84)
+    n, k, m, dv = 10, 4, 3, 2
+    Pq, Pk = np.abs(rng.standard_normal((n, m))), np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    G[:k] = 0.0  # only the continuation's outputs carry loss
+    full = O.causal_attn_bwd(Pq, Pk, V, G, normalize=True, delta=0.2)
+    S0, z0 = Pk[:k].T @ V[:k], Pk[:k].sum(axis=0)
+    part = O.causal_attn_bwd_state(Pq[k:], Pk[k:], V[k:], G[k:], S0, z0, normalize=True,
+                                   delta=0.2)
+    # continuation rows match
+    assert np.allclose(part[0], full[0][k:], rtol=1e-11, atol=1e-12)
+    assert np.allclose(part[1], full[1][k:], rtol=1e-11, atol=1e-12)
+    assert np.allclose(part[2], full[2][k:], rtol=1e-11, atol=1e-12)
+    # prefix rows through the state: dPk_pre = V_pre dS0^T + dz0, dV_pre = Pk_pre dS0
+    assert np.allclose(V[:k] @ part[3].T + part[4][None, :], full[1][:k], rtol=1e-11, atol=1e-12)
+    assert np.allclose(Pk[:k] @ part[3], full[2][:k], rtol=1e-11, atol=1e-12)
