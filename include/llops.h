@@ -225,6 +225,28 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* shape, const void* 
                                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * llops_linattn_causal_bwd_state -- llops_linattn_causal_bwd for the forward
+ * continued from an initial state, out = llops_linattn_causal_fwd(..., S0, z0):
+ *   num = M V + phi_Q S0,  den = M 1 + phi_Q z0 + delta,
+ *   dphi_Q = dM phi_K + dnum S0^T + dden z0^T,  dS0 = phi_Q^T dnum,  dz0 = phi_Q^T dden
+ * (the streaming form of the paper's Sec. 1: a chunk's initial state is the
+ * running sums of the chunks before it, so dS0, dz0 carry the gradient back
+ * to them). S0 [batch][heads][m][dv] and z0 [batch][heads][m] fp32 inputs
+ * (nullable = zeros); dS0, dz0 fp32 outputs of those shapes (nullable = not
+ * wanted), overwritten. The other arguments, limits and the workspace
+ * (LLOPS_ENTRY_CAUSAL_BWD) are those of llops_linattn_causal_bwd, which is
+ * this call with all four null.
+ */
+llops_status_t llops_linattn_causal_bwd_state(const llops_shape_t* shape, const void* Q,
+                                              const void* K, const void* V,
+                                              const void* theta_q, const void* theta_k,
+                                              const float* S0, const float* z0,
+                                              const float* dO, float* dQ, float* dK, float* dV,
+                                              float* dtheta_q, float* dtheta_k,
+                                              float* dS0, float* dz0,
+                                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * llops_linattn_bwd -- the same gradients for the non-causal
  * out = llops_linattn_fwd(Q, K, V, theta_q, theta_k): M = phi_Q phi_K^T without
  * the mask, so each of dphi_Q = dM phi_K, dphi_K = dM^T phi_Q, dV = M^T dnum is

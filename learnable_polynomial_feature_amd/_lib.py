@@ -25,7 +25,7 @@ STATUS = {0: "LLOPS_OK", 1: "LLOPS_ERR_INVALID_ARG", 2: "LLOPS_ERR_UNSUPPORTED",
 EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd",
            "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
            "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
-           "llops_linattn_gated_causal_bwd",
+           "llops_linattn_gated_causal_bwd", "llops_linattn_causal_bwd_state",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -75,6 +75,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_linattn_causal_fwd.restype = ctypes.c_int
     lib.llops_linattn_causal_bwd.argtypes = [SP] + [_P] * 12 + [ctypes.c_size_t, _P]
     lib.llops_linattn_causal_bwd.restype = ctypes.c_int
+    lib.llops_linattn_causal_bwd_state.argtypes = [SP] + [_P] * 16 + [ctypes.c_size_t, _P]
+    lib.llops_linattn_causal_bwd_state.restype = ctypes.c_int
     lib.llops_linattn_bwd.argtypes = [SP] + [_P] * 12 + [ctypes.c_size_t, _P]
     lib.llops_linattn_bwd.restype = ctypes.c_int
     lib.llops_decode_step.argtypes = [SP, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -318,6 +320,39 @@ def llops_linattn_causal_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, nor
     out = llops_linattn_causal_fwd(Q, K, V, theta_q, theta_k, ...) from a zero
     state. Q, K, V and thetas bf16; dO fp32 [B, H, n, dv]; all results fp32."""
     return _attn_bwd(True, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, workspace)
+
+
+def llops_linattn_causal_bwd_state(Q, K, V, theta_q, theta_k, dO, *, S0=None, z0=None,
+                                   square=False, normalize=False, delta=0.0, workspace=None):
+    """Gradients (dQ, dK, dV, dtheta_q, dtheta_k, dS0, dz0) of sum(dO * out) for
+    out = llops_linattn_causal_fwd(..., S0=S0, z0=z0); S0 fp32 [B, H, m, dv] and
+    z0 fp32 [B, H, m] (None = zeros)."""
+    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
+    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
+    dO = _dev(dO, "dO")
+    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(V.shape):
+        raise ValueError("dO must be fp32 with V's shape")
+    B, H = Q.shape[:2]
+    m, dv = shape.m, shape.dv
+    if S0 is not None:
+        S0 = _dev(S0, "S0")
+        if tuple(S0.shape) != (B, H, m, dv) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be fp32 [B, H, m, dv]")
+    if z0 is not None:
+        z0 = _dev(z0, "z0")
+        if tuple(z0.shape) != (B, H, m) or z0.dtype != torch.float32:
+            raise ValueError("z0 must be fp32 [B, H, m]")
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
+    dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
+    dS0, dz0 = torch.empty((B, H, m, dv), **f32), torch.empty((B, H, m), **f32)
+    ws, wsb = _workspace(shape, ENTRY_CAUSAL_BWD, Q.device, workspace)
+    _check(library().llops_linattn_causal_bwd_state(
+        ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k), _ptr(S0),
+        _ptr(z0), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(dS0),
+        _ptr(dz0), _ptr(ws), wsb, _stream(Q)))
+    return dQ, dK, dV, dtq, dtk, dS0, dz0
 
 
 def llops_linattn_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, normalize=False, delta=0.0,

@@ -103,7 +103,7 @@ int bwd_w(const llops_shape_t* s) {
 
 struct BwdWs {
   size_t phq, phk, pkq, pkk, num, den1, ones, a, ra, b, rb, rdnum, rphq, rphk, vp, tmp, dphq, dphk,
-      seg, tot, fb, total;
+      seg, tot, fb, stot, p0, zb16, total;
 };
 
 llops::FeatShape feat_shape(const llops_shape_t* s, int64_t n, int out_bf16);
@@ -211,6 +211,11 @@ BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   if (MA * W + MA > per) per = MA * W + MA;
   w.tot = take(causal ? 0 : BH * per * sizeof(float));
   w.fb = take(llops::featmap_bwd_ws_bytes(feat_shape(s, s->n, 0)));
+  // causal, from an initial state: totals for dS0 / dz0, the initial state of
+  // a dphi_Q slice pass, and z0 broadcast for the M 1 pass
+  w.stot = take(causal ? BH * (m * dv + m) * sizeof(float) : 0);
+  w.p0 = take(causal ? BH * MA * W * sizeof(float) : 0);
+  w.zb16 = take(causal ? BH * m * 16 * sizeof(float) : 0);
   w.total = off;
   return w;
 }
@@ -354,7 +359,8 @@ llops_status_t validate_gated(const llops_shape_t* s) {
 // v [BH][n][DV]; fp32 out. The forward's segment kernels.
 hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
                             const uint16_t* fq, const uint16_t* fk, const uint16_t* v, float* out,
-                            float* seg, float* tot, hipStream_t st) {
+                            float* seg, float* tot, hipStream_t st,
+                            const float* S0init = nullptr) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   const llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
@@ -364,8 +370,8 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
   if (e != hipSuccess) return e;
   const float* state = seg;
   int64_t st_seg = per, st_bh = per * a.nseg;
-  if (causal) {
-    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, nullptr, nullptr, 1, st);
+  if (causal) {  // S0init: [BH][M*DV] initial state (null = zeros)
+    e = llops::launch_seg_scan(a, seg, S0init, nullptr, nullptr, nullptr, 1, st);
   } else {
     e = llops::launch_seg_scan(a, seg, nullptr, nullptr, tot, tot + static_cast<int64_t>(M) * DV,
                                0, st);
@@ -444,6 +450,18 @@ hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const u
   if (e == hipSuccess)
     e = llops::launch_seg_scan_gated(a, seg, gseg, nullptr, nullptr, nullptr, nullptr, st);
   if (e == hipSuccess) e = llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
+  return e;
+}
+
+// Totals over all rows of fk^T v (and fk^T 1) per (b, h) into Stot [BH][M*DV]
+// and ztot (null, or Stot + M*DV for one contiguous [BH][M*DV + M] block).
+hipError_t state_total(const llops_shape_t* s, int M, int DV, const uint16_t* fk,
+                       const uint16_t* v, float* seg, float* Stot, float* ztot, hipStream_t st) {
+  const llops_shape_t t = feat_attn_shape(s, M, DV);
+  const llops::AttnShape a = attn_shape(&t, true);
+  hipError_t e = llops::attn32_supported(a) ? llops::launch_seg_state32(a, fk, v, seg, st)
+                                            : llops::launch_seg_state_bf16(a, fk, v, seg, st);
+  if (e == hipSuccess) e = llops::launch_seg_scan(a, seg, nullptr, nullptr, Stot, ztot, 0, st);
   return e;
 }
 
@@ -734,10 +752,14 @@ llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* s, const void
 }
 
 // Shared body of the causal and non-causal attention backward.
+// S0, z0 (causal only, nullable): the forward continued from an initial
+// state; dS0, dz0 (nullable): its gradients.
 static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const void* Q, const void* K,
                              const void* V, const void* theta_q, const void* theta_k,
                              const float* dO, float* dQ, float* dK, float* dV, float* dtheta_q,
-                             float* dtheta_k, void* ws, size_t ws_bytes, hipStream_t st) {
+                             float* dtheta_k, void* ws, size_t ws_bytes, hipStream_t st,
+                             const float* S0 = nullptr, const float* z0 = nullptr,
+                             float* dS0 = nullptr, float* dz0 = nullptr) {
   LLOPS_TRY(validate_attn_bwd(s, causal));
   const int64_t BH = s->batch * s->heads;
   if (s->heads == 0) return LLOPS_OK;
@@ -755,6 +777,10 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     LLOPS_TRY(need(dK, "dK"));
     LLOPS_TRY(need(dV, "dV"));
   }
+  LLOPS_TRY(opt(S0, "S0"));
+  LLOPS_TRY(opt(z0, "z0"));
+  LLOPS_TRY(opt(dS0, "dS0"));
+  LLOPS_TRY(opt(dz0, "dz0"));
   const BwdWs L = bwd_ws(s, causal);
   if (ws_bytes < L.total)
     return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
@@ -765,9 +791,12 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
   const llops::FeatShape fs0 = feat_shape(s, s->n, 0);
   float* fb = L.fb ? f32(L.fb) : nullptr;
-  if (R == 0) {  // no rows: the Theta gradients are zero
+  if (R == 0) {  // no rows: the Theta (and initial-state) gradients are zero
     LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dO, 0, dQ, dtheta_q, fb, st), "featmap_bwd");
     LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dO, 0, dK, dtheta_k, fb, st), "featmap_bwd");
+    if (dS0 || dz0)
+      LLOPS_HIP(llops::launch_state_init(BH, s->m, s->dv, nullptr, nullptr, dS0, dz0, st),
+                "state_init");
     return LLOPS_OK;
   }
   const int m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s);
@@ -781,13 +810,18 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // num = M V and, with the normaliser, M 1
   float* num = f32(L.num);
   LLOPS_HIP(attn_on_features(s, causal, m, dv, phq, phk, static_cast<const uint16_t*>(V), num, seg,
-                             tot, st),
+                             tot, st, S0),
             "attn num");
   float* den1 = nullptr;
   if (s->normalize) {
     den1 = f32(L.den1);
     LLOPS_HIP(llops::launch_fill_ones16(u16(L.ones), R, st), "ones");
-    LLOPS_HIP(attn_on_features(s, causal, m, 16, phq, phk, u16(L.ones), den1, seg, tot, st),
+    const float* zinit = nullptr;  // z0 in every column of the all-ones pass
+    if (z0) {
+      LLOPS_HIP(llops::launch_state_bcast16(z0, BH, m, f32(L.zb16), st), "state");
+      zinit = f32(L.zb16);
+    }
+    LLOPS_HIP(attn_on_features(s, causal, m, 16, phq, phk, u16(L.ones), den1, seg, tot, st, zinit),
               "attn den");
   }
   // a = [dnum | dden | 0], b = [V | 1 | 0]; causal: also reversed copies
@@ -801,10 +835,33 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
   uint16_t *dphq = u16(L.dphq), *dphk = u16(L.dphk);  // bf16, as the forward stores phi
-  // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j, W columns of phi_K at a time
+  uint16_t *rphq = causal ? u16(L.rphq) : nullptr, *rphk = causal ? u16(L.rphk) : nullptr;
+  if (causal) {
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
+  }
+  // initial-state gradients: dS0 = sum_i phi_Q,i dnum_i^T (reversed rows of
+  // both, paired), dz0 = sum_i dden_i phi_Q,i (dden is column dv of a)
+  if (causal && dS0)
+    LLOPS_HIP(state_total(s, m, dv, rphq, dn, seg, dS0, nullptr, st), "dS0");
+  if (causal && dz0) {
+    float* stot = f32(L.stot);
+    LLOPS_HIP(llops::launch_rows_copy_bf16(a, MA, dv, vp, 16, 0, 16, n, R, 0, st), "rows");
+    LLOPS_HIP(state_total(s, m, 16, phq, vp, seg, stot, stot + static_cast<int64_t>(m) * 16, st),
+              "dz0");
+    LLOPS_HIP(llops::launch_col_extract(stot, BH, m, static_cast<int64_t>(m) * 16 + m, 16, dz0, st),
+              "dz0");
+  }
+  // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j (+ dnum_i . S0 + dden_i z0 from an
+  // initial state), W columns of phi_K at a time
+  const bool init = causal && (S0 || z0);
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
-    LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, vp, tmp, seg, tot, st), "attn dphi_q");
+    if (init)
+      LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
+    LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, vp, tmp, seg, tot, st,
+                               init ? f32(L.p0) : nullptr),
+              "attn dphi_q");
     LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
   }
   // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: causal over the reversed sequence
@@ -818,9 +875,6 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   }
   // dV_j = sum_{i(>=j)} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
   if (causal) {
-    uint16_t *rphq = u16(L.rphq), *rphk = u16(L.rphk);
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
     LLOPS_HIP(attn_on_features(s, true, m, dv, rphk, rphq, dn, tmp, seg, nullptr, st), "attn dv");
     LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
   } else {
@@ -841,6 +895,17 @@ llops_status_t llops_linattn_causal_bwd(const llops_shape_t* s, const void* Q, c
                                         size_t ws_bytes, hipStream_t st) {
   return attn_backward(s, true, Q, K, V, theta_q, theta_k, dO, dQ, dK, dV, dtheta_q, dtheta_k, ws,
                        ws_bytes, st);
+}
+
+llops_status_t llops_linattn_causal_bwd_state(const llops_shape_t* s, const void* Q, const void* K,
+                                              const void* V, const void* theta_q,
+                                              const void* theta_k, const float* S0,
+                                              const float* z0, const float* dO, float* dQ,
+                                              float* dK, float* dV, float* dtheta_q,
+                                              float* dtheta_k, float* dS0, float* dz0, void* ws,
+                                              size_t ws_bytes, hipStream_t st) {
+  return attn_backward(s, true, Q, K, V, theta_q, theta_k, dO, dQ, dK, dV, dtheta_q, dtheta_k, ws,
+                       ws_bytes, st, S0, z0, dS0, dz0);
 }
 
 llops_status_t llops_linattn_bwd(const llops_shape_t* s, const void* Q, const void* K,

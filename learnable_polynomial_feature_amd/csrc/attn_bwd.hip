@@ -335,6 +335,76 @@ hipError_t launch_seg_bridge_dg(const float* dc, int64_t BH, int64_t n, int64_t 
   return hipGetLastError();
 }
 
+// ---- backward from an initial state ------------------------------------------
+
+// out[bh][f][c] = z0[bh][f] for c < 16: the initial state of the M 1 pass
+// (all-ones values 16 wide) that adds phi_Q . z0 to every column.
+__global__ __launch_bounds__(256) void state_bcast16(const float* __restrict__ z0, int64_t total,
+                                                     float* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // over BH * m * 16
+  if (e < total) out[e] = z0[e >> 4];
+}
+
+// Initial state of a dphi_Q slice pass (keys b = [V | 1 | 0], MA wide; values
+// phi_K columns p0 .. p0+W-1): P[bh][alpha][c] = S0[bh][p0+c][alpha] for
+// alpha < dv, z0[bh][p0+c] for alpha = dv, 0 beyond (either source may be
+// null = zeros), so the pass adds dnum_i . S0[p0+c, :] + dden_i z0[p0+c].
+__global__ __launch_bounds__(256) void build_p0(const float* __restrict__ S0,
+                                                const float* __restrict__ z0, int64_t BH, int m,
+                                                int dv, int MA, int W, int p0,
+                                                float* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per = static_cast<int64_t>(MA) * W;
+  if (e >= BH * per) return;
+  const int64_t bh = e / per;
+  const int r = static_cast<int>(e - bh * per);
+  const int alpha = r / W, c = r - alpha * W;
+  float v = 0.f;
+  if (alpha < dv)
+    v = S0 ? S0[(bh * m + p0 + c) * dv + alpha] : 0.f;
+  else if (alpha == dv)
+    v = z0 ? z0[bh * m + p0 + c] : 0.f;
+  out[e] = v;
+}
+
+// out[bh][f] = tot[bh * per + f * ld]: one column of per-(b, h) totals.
+__global__ __launch_bounds__(256) void col_extract(const float* __restrict__ tot, int64_t BH, int m,
+                                                   int64_t per, int ld, float* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= BH * m) return;
+  const int64_t bh = e / m;
+  out[e] = tot[bh * per + (e - bh * m) * ld];
+}
+
+hipError_t launch_state_bcast16(const float* z0, int64_t BH, int m, float* out, hipStream_t st) {
+  const int64_t total = BH * m * 16;
+  if (total == 0) return hipSuccess;
+  if ((total + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_state", st, state_bcast16, dim3(static_cast<unsigned>((total + 255) / 256)),
+               dim3(256), 0, st, z0, total, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_p0(const float* S0, const float* z0, int64_t BH, int m, int dv, int MA,
+                           int W, int p0, float* out, hipStream_t st) {
+  const int64_t total = BH * MA * W;
+  if (total == 0) return hipSuccess;
+  if ((total + 255) / 256 > 0x7fffffffLL || p0 + W > m || dv >= MA) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_state", st, build_p0, dim3(static_cast<unsigned>((total + 255) / 256)),
+               dim3(256), 0, st, S0, z0, BH, m, dv, MA, W, p0, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_col_extract(const float* tot, int64_t BH, int m, int64_t per, int ld, float* out,
+                              hipStream_t st) {
+  const int64_t total = BH * m;
+  if (total == 0) return hipSuccess;
+  if ((total + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_state", st, col_extract, dim3(static_cast<unsigned>((total + 255) / 256)),
+               dim3(256), 0, st, tot, BH, m, per, ld, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_reverse_shift(const float* g, int64_t n, int64_t rows, float* out,
                                      hipStream_t st) {
   if (rows == 0) return hipSuccess;

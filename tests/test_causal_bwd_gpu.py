@@ -101,3 +101,63 @@ def test_causal_bwd_full_size_sampled(lib):
                            ("dtheta_q", dtq[h], rtq), ("dtheta_k", dtk[h], rtk)):
             err = rel_fro(host(a), b)
             assert err <= TOL_BF16, (h, name, err)
+
+
+STATE_CASES = [
+    # B, H, n, d, dv, m, t, square, normalize
+    (1, 2, 300, 64, 64, 64, 4, True, True),
+    (2, 1, 257, 128, 128, 256, 4, True, True),
+    (1, 2, 500, 128, 64, 128, 1, False, False),
+    (2, 2, 100, 64, 32, 64, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", STATE_CASES, ids=[str(c) for c in STATE_CASES])
+def test_causal_bwd_from_initial_state(lib, case):
+    """llops_linattn_causal_bwd_state: the forward continued from (S0, z0), all
+    seven gradients against the fp64 chain rule."""
+    B, H, n, d, dv, m, t, square, normalize = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize)
+    x = generate(w)
+    G = dout(w)
+    rng = np.random.default_rng(31)
+    S0 = (0.01 * rng.standard_normal((B, H, m, dv))).astype(np.float32)
+    z0 = np.abs(0.01 * rng.standard_normal((B, H, m))).astype(np.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce(f"causal_bwd_state {case}")
+    got = lib.llops_linattn_causal_bwd_state(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                             dev(G, torch.float32), S0=dev(S0, torch.float32),
+                                             z0=dev(z0, torch.float32), square=square,
+                                             normalize=normalize, delta=w.delta)
+    torch.cuda.synchronize()
+    want = O.causal_bwd_state_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], G, S0, z0,
+                                 square=square, normalize=normalize, delta=w.delta)
+    names = ("dQ", "dK", "dV", "dtheta_q", "dtheta_k", "dS0", "dz0")
+    for name, a, b in zip(names, got, want):
+        err = rel_fro(host(a), b)
+        assert err <= TOL_BF16, (name, err)
+
+
+def test_causal_bwd_state_without_state_is_causal_bwd(lib):
+    """No initial state: the same numbers as llops_linattn_causal_bwd bit for
+    bit, plus dS0, dz0 of a zero state against the oracle."""
+    w = _w(1, 2, 400, 128, 128, 256, 4, True, True)
+    x = generate(w)
+    G = dout(w)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce("causal_bwd_state without state")
+    a = lib.llops_linattn_causal_bwd_state(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                           dev(G, torch.float32), square=True, normalize=True,
+                                           delta=w.delta)
+    b = lib.llops_linattn_causal_bwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                     dev(G, torch.float32), square=True, normalize=True,
+                                     delta=w.delta)
+    torch.cuda.synchronize()
+    for x1, x2 in zip(a[:5], b):
+        assert torch.equal(x1, x2)
+    m, dv = 256, 128
+    want = O.causal_bwd_state_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], G,
+                                 np.zeros((1, 2, m, dv)), np.zeros((1, 2, m)), square=True,
+                                 normalize=True, delta=w.delta)
+    assert rel_fro(host(a[5]), want[5]) <= TOL_BF16
+    assert rel_fro(host(a[6]), want[6]) <= TOL_BF16
