@@ -635,6 +635,57 @@ def gated_attn_bwd_recurrent(Pq, Pk, V, G, log_gate, normalize=False, delta=0.0)
     return dPq, dPk, dV, dg
 
 
+def gated_attn_bwd_state(Pq, Pk, V, G, log_gate, S0, z0, normalize=False, delta=0.0):
+    """gated_attn_bwd for the contraction continued from an initial state
+    (gated_causal_quadratic's S0/z0, which reach query i with weight exp(c_i)):
+      num = M V + exp(c) * (Pq S0),  den = M 1 + exp(c) * (Pq z0) + delta,
+      dPq_i = ((dM * W) Pk)_i + exp(c_i) (S0 dnum_i + dden_i z0),
+      dS0 = sum_i exp(c_i) Pq_i dnum_i^T,  dz0 = sum_i exp(c_i) dden_i Pq_i,
+    and the gate term: the state's contribution to row i, X_i0 =
+    exp(c_i) (dnum_i . S0^T Pq_i + dden_i Pq_i . z0), joins row i's sum in dc_i.
+    Returns (dPq, dPk, dV, dg, dS0, dz0)."""
+    Pq, Pk, V, G = _f64(Pq), _f64(Pk), _f64(V), _f64(G)
+    S0, z0 = _f64(S0), _f64(z0)
+    c = np.cumsum(_f64(log_gate))
+    e = np.exp(c)
+    n = Pq.shape[0]
+    i, j = np.arange(n)[:, None], np.arange(n)[None, :]
+    W = np.where(j <= i, np.exp(np.where(j <= i, c[:, None] - c[None, :], 0.0)), 0.0)
+    M = W * (Pq @ Pk.T)
+    num = M @ V + e[:, None] * (Pq @ S0)
+    if normalize:
+        den = M.sum(axis=1) + e * (Pq @ z0) + delta
+        out = num / den[:, None]
+        dnum = G / den[:, None]
+        dden = -(G * out).sum(axis=1) / den
+    else:
+        dnum = G
+        dden = np.zeros(n)
+    dM = np.tril(dnum @ V.T + dden[:, None])
+    dA = dM * W
+    X = dM * M
+    x0 = e * ((dnum * (Pq @ S0)).sum(axis=1) + dden * (Pq @ z0))
+    dc = X.sum(axis=1) - X.sum(axis=0) + x0
+    dg = np.cumsum(dc[::-1])[::-1]
+    dPq = dA @ Pk + e[:, None] * (dnum @ S0.T + np.outer(dden, z0))
+    dS0 = (e[:, None] * Pq).T @ dnum
+    dz0 = (e[:, None] * Pq).T @ dden
+    return dPq, dA.T @ Pq, M.T @ dnum, dg, dS0, dz0
+
+
+def gated_causal_bwd_state(Q, K, V, theta_q, theta_k, log_gate, G, S0, z0, square=False,
+                           normalize=False, delta=0.0):
+    """gated_causal_bwd from an initial state:
+    (dQ, dK, dV, dTheta_q, dTheta_k, dlog_gate, dS0, dz0)."""
+    Pq = featmap(Q, theta_q, square)
+    Pk = featmap(K, theta_k, square)
+    dPq, dPk, dV, dg, dS0, dz0 = gated_attn_bwd_state(Pq, Pk, V, G, log_gate, S0, z0, normalize,
+                                                      delta)
+    dQ, dtq = featmap_bwd(Q, theta_q, dPq, square)
+    dK, dtk = featmap_bwd(K, theta_k, dPk, square)
+    return dQ, dK, dV, dtq, dtk, dg, dS0, dz0
+
+
 def gated_causal_bwd(Q, K, V, theta_q, theta_k, log_gate, G, square=False, normalize=False,
                      delta=0.0, recurrent=False):
     """Gradients (dQ, dK, dV, dTheta_q, dTheta_k, dlog_gate) of L = sum(G * out)

@@ -733,3 +733,54 @@ def test_causal_bwd_state_is_prefix_gradient():
     # prefix rows through the state: dPk_pre = V_pre dS0^T + dz0, dV_pre = Pk_pre dS0
     assert np.allclose(V[:k] @ part[3].T + part[4][None, :], full[1][:k], rtol=1e-11, atol=1e-12)
     assert np.allclose(Pk[:k] @ part[3], full[2][:k], rtol=1e-11, atol=1e-12)
+
+
+# ---- gated backward from an initial state -------------------------------------
+
+def _gated_state_loss(Q, K, V, tq, tk, g, S0, z0, G, **kw):
+    out, _, _ = O.gated_recurrent(Q, K, V, tq, tk, g, S0=S0, z0=z0, **kw)
+    return float((G * out).sum())
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+def test_gated_bwd_state_central_differences(normalize):
+    """Every entry of Q, K, V, Theta, the log gates, S0 and z0 against central
+    differences of sum(G * gated_recurrent(..., S0, z0)) (the token-by-token
+    form, independent of the materialised backward)."""
+    rng = np.random.default_rng(90 + normalize)
+    n, d, dv, m, p, t = 6, 3, 2, 4, 2, 2
+    Q, K = 0.7 * rng.standard_normal((n, d)), 0.7 * rng.standard_normal((n, d))
+    V = rng.standard_normal((n, dv))
+    tq, tk = 0.6 * rng.standard_normal((p, t, d, m)), 0.6 * rng.standard_normal((p, t, d, m))
+    g = -np.abs(0.5 * rng.standard_normal(n))
+    S0 = 0.3 * rng.standard_normal((m, dv))
+    z0 = np.abs(0.3 * rng.standard_normal(m))
+    G = rng.standard_normal((n, dv))
+    kw = dict(square=True, normalize=normalize, delta=0.5)
+    got = O.gated_causal_bwd_state(Q, K, V, tq, tk, g, G, S0, z0, **kw)
+    args = [Q, K, V, tq, tk, g, S0, z0]
+    h = 1e-6
+    for which, grad in enumerate(got):
+        x = args[which]
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            ap, am = list(args), list(args)
+            ap[which], am[which] = xp, xm
+            num[idx] = (_gated_state_loss(*ap, G, **kw) - _gated_state_loss(*am, G, **kw)) / (2 * h)
+        assert np.allclose(grad, num, rtol=1e-6, atol=1e-7), which
+
+
+def test_gated_bwd_zero_state_is_gated_bwd():
+    rng = np.random.default_rng(93)
+    n, m, dv = 9, 4, 3
+    Pq, Pk = np.abs(rng.standard_normal((n, m))), np.abs(rng.standard_normal((n, m)))
+    V, G = rng.standard_normal((n, dv)), rng.standard_normal((n, dv))
+    g = -np.abs(rng.standard_normal(n))
+    want = O.gated_attn_bwd(Pq, Pk, V, G, g, normalize=True, delta=0.3)
+    got = O.gated_attn_bwd_state(Pq, Pk, V, G, g, np.zeros((m, dv)), np.zeros(m), normalize=True,
+                                 delta=0.3)
+    for a, b in zip(got[:4], want):
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
