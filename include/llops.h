@@ -306,6 +306,30 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* shape, const 
                                               hipStream_t stream);
 
 /*
+ * llops_linattn_gated_causal_bwd_state -- llops_linattn_gated_causal_bwd for the
+ * forward continued from an initial state, out =
+ * llops_linattn_gated_causal_fwd(..., log_gate, S0, z0), where the state reaches
+ * query i with weight exp(c_i):
+ *   dphi_Q_i += exp(c_i) (S0 dnum_i + dden_i z0),
+ *   dS0 = sum_i exp(c_i) phi_Q,i dnum_i^T,  dz0 = sum_i exp(c_i) dden_i phi_Q,i,
+ * and the gate gradient includes the state's term (same passages). S0, z0 fp32
+ * inputs (nullable = zeros); dS0, dz0 fp32 outputs (nullable = not wanted),
+ * overwritten. Other arguments, limits and the workspace
+ * (LLOPS_ENTRY_GATED_CAUSAL_BWD) as for llops_linattn_gated_causal_bwd, which
+ * is this call with all four null.
+ */
+llops_status_t llops_linattn_gated_causal_bwd_state(const llops_shape_t* shape, const void* Q,
+                                                    const void* K, const void* V,
+                                                    const void* theta_q, const void* theta_k,
+                                                    const float* log_gate, const float* S0,
+                                                    const float* z0, const float* dO,
+                                                    float* dQ, float* dK, float* dV,
+                                                    float* dtheta_q, float* dtheta_k,
+                                                    float* dlog_gate, float* dS0, float* dz0,
+                                                    void* ws, size_t ws_bytes,
+                                                    hipStream_t stream);
+
+/*
  * llops_gated_decode_step -- llops_decode_step on a decaying state:
  *   S = exp(g) S + phi_K(k) v^T;  z = exp(g) z + phi_K(k);
  *   out = phi_Q(q)^T S [ / (phi_Q(q)^T z + delta) ]

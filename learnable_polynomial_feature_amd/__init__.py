@@ -10,6 +10,7 @@ _BINDING = ("llops_featmap", "llops_featmap_bwd", "llops_linattn_fwd", "llops_li
             "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
             "llops_linattn_gated_causal_bwd",
             "llops_linattn_causal_bwd_state",
+            "llops_linattn_gated_causal_bwd_state",
             "llops_workspace_bytes", "LlopsError", "library")
 
 

@@ -26,6 +26,7 @@ EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops
            "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
            "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
            "llops_linattn_gated_causal_bwd", "llops_linattn_causal_bwd_state",
+           "llops_linattn_gated_causal_bwd_state",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -87,6 +88,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_gated_decode_step.restype = ctypes.c_int
     lib.llops_linattn_gated_causal_bwd.argtypes = [SP] + [_P] * 14 + [ctypes.c_size_t, _P]
     lib.llops_linattn_gated_causal_bwd.restype = ctypes.c_int
+    lib.llops_linattn_gated_causal_bwd_state.argtypes = [SP] + [_P] * 18 + [ctypes.c_size_t, _P]
+    lib.llops_linattn_gated_causal_bwd_state.restype = ctypes.c_int
     lib.llops_status_str.argtypes = [ctypes.c_int]
     lib.llops_status_str.restype = ctypes.c_char_p
     lib.llops_last_error.argtypes = []
@@ -387,6 +390,21 @@ def llops_linattn_gated_causal_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, *, s
     out = llops_linattn_gated_causal_fwd(Q, K, V, theta_q, theta_k, log_gate, ...)
     from a zero state. Q, K, V and thetas bf16; log_gate fp32 [B, H, n]; dO fp32
     [B, H, n, dv]; all results fp32."""
+    return _gated_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, None, None, False, square,
+                      normalize, delta, workspace)
+
+
+def llops_linattn_gated_causal_bwd_state(Q, K, V, theta_q, theta_k, log_gate, dO, *, S0=None,
+                                         z0=None, square=False, normalize=False, delta=0.0,
+                                         workspace=None):
+    """The gated backward for the forward continued from (S0, z0) (None = zeros):
+    (dQ, dK, dV, dtheta_q, dtheta_k, dlog_gate, dS0, dz0)."""
+    return _gated_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, S0, z0, True, square, normalize,
+                      delta, workspace)
+
+
+def _gated_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, S0, z0, state, square, normalize, delta,
+               workspace):
     Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
     theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
     shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
@@ -400,11 +418,28 @@ def llops_linattn_gated_causal_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, *, s
     dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
     dg = torch.empty(log_gate.shape, **f32)
     ws, wsb = _workspace(shape, ENTRY_GATED_CAUSAL_BWD, Q.device, workspace)
-    _check(library().llops_linattn_gated_causal_bwd(
+    if not state:
+        _check(library().llops_linattn_gated_causal_bwd(
+            ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
+            _ptr(log_gate), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(dg),
+            _ptr(ws), wsb, _stream(Q)))
+        return dQ, dK, dV, dtq, dtk, dg
+    B, H = Q.shape[:2]
+    m, dv = shape.m, shape.dv
+    if S0 is not None:
+        S0 = _dev(S0, "S0")
+        if tuple(S0.shape) != (B, H, m, dv) or S0.dtype != torch.float32:
+            raise ValueError("S0 must be fp32 [B, H, m, dv]")
+    if z0 is not None:
+        z0 = _dev(z0, "z0")
+        if tuple(z0.shape) != (B, H, m) or z0.dtype != torch.float32:
+            raise ValueError("z0 must be fp32 [B, H, m]")
+    dS0, dz0 = torch.empty((B, H, m, dv), **f32), torch.empty((B, H, m), **f32)
+    _check(library().llops_linattn_gated_causal_bwd_state(
         ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
-        _ptr(log_gate), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(dg),
-        _ptr(ws), wsb, _stream(Q)))
-    return dQ, dK, dV, dtq, dtk, dg
+        _ptr(log_gate), _ptr(S0), _ptr(z0), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq),
+        _ptr(dtk), _ptr(dg), _ptr(dS0), _ptr(dz0), _ptr(ws), wsb, _stream(Q)))
+    return dQ, dK, dV, dtq, dtk, dg, dS0, dz0
 
 
 def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normalize=True,

@@ -391,7 +391,7 @@ int gated_den_w(const llops_shape_t* s) { return s->m == 256 ? 128 : 64; }
 
 struct GBwdWs {
   BwdWs b;  // the ungated backward's buffers (its seg and den1/ones are not used)
-  size_t glf, grev, glr, gseg, gones, gden, dc, seg, seg2, dgb, total;
+  size_t glf, grev, glr, gseg, gones, gden, dc, seg, seg2, dgb, p0, zbw, total;
 };
 
 GBwdWs gated_bwd_ws(const llops_shape_t* s) {
@@ -423,6 +423,8 @@ GBwdWs gated_bwd_ws(const llops_shape_t* s) {
   w.seg = take(seg);
   w.seg2 = take(feat_attn_seg_bytes(s, MA, W, true, kGatedBwdWG));  // suffix states, dphi_Q slices
   w.dgb = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);  // dg at starts
+  w.p0 = take(BH * static_cast<size_t>(MA) * W * 4);  // initial state of a dphi_Q slice pass
+  w.zbw = take(s->normalize ? BH * static_cast<size_t>(s->m) * DVo * 4 : 0);  // z0 broadcast
   w.total = off;
   return w;
 }
@@ -442,13 +444,14 @@ llops_status_t validate_gated_bwd(const llops_shape_t* s) {
 // kernels.
 hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const uint16_t* fq,
                                   const uint16_t* fk, const uint16_t* v, const float* gl,
-                                  float* out, float* seg, float* gseg, hipStream_t st) {
+                                  float* out, float* seg, float* gseg, hipStream_t st,
+                                  const float* S0init = nullptr) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   const llops::AttnShape a = attn_shape(&t, true, kGatedBwdWG);
   if (!llops::attn32_supported(a)) return hipErrorInvalidValue;
   hipError_t e = llops::launch_seg_state32_gated(a, fk, v, gl, gseg, seg, st);
   if (e == hipSuccess)
-    e = llops::launch_seg_scan_gated(a, seg, gseg, nullptr, nullptr, nullptr, nullptr, st);
+    e = llops::launch_seg_scan_gated(a, seg, gseg, S0init, nullptr, nullptr, nullptr, st);
   if (e == hipSuccess) e = llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
   return e;
 }
@@ -818,7 +821,7 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     LLOPS_HIP(llops::launch_fill_ones16(u16(L.ones), R, st), "ones");
     const float* zinit = nullptr;  // z0 in every column of the all-ones pass
     if (z0) {
-      LLOPS_HIP(llops::launch_state_bcast16(z0, BH, m, f32(L.zb16), st), "state");
+      LLOPS_HIP(llops::launch_state_bcast(z0, BH, m, 16, f32(L.zb16), st), "state");
       zinit = f32(L.zb16);
     }
     LLOPS_HIP(attn_on_features(s, causal, m, 16, phq, phk, u16(L.ones), den1, seg, tot, st, zinit),
@@ -917,12 +920,13 @@ llops_status_t llops_linattn_bwd(const llops_shape_t* s, const void* Q, const vo
                        ws_bytes, st);
 }
 
-llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void* Q, const void* K,
-                                              const void* V, const void* theta_q,
-                                              const void* theta_k, const float* log_gate,
-                                              const float* dO, float* dQ, float* dK, float* dV,
-                                              float* dtheta_q, float* dtheta_k, float* dlog_gate,
-                                              void* ws, size_t ws_bytes, hipStream_t st) {
+static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, const void* K,
+                                     const void* V, const void* theta_q, const void* theta_k,
+                                     const float* log_gate, const float* S0, const float* z0,
+                                     const float* dO, float* dQ, float* dK, float* dV,
+                                     float* dtheta_q, float* dtheta_k, float* dlog_gate,
+                                     float* dS0, float* dz0, void* ws, size_t ws_bytes,
+                                     hipStream_t st) {
   LLOPS_TRY(validate_gated_bwd(s));
   const int64_t BH = s->batch * s->heads;
   if (s->heads == 0) return LLOPS_OK;
@@ -942,6 +946,10 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
     LLOPS_TRY(need(dV, "dV"));
     LLOPS_TRY(need4(dlog_gate, "dlog_gate"));
   }
+  LLOPS_TRY(opt(S0, "S0"));
+  LLOPS_TRY(opt(z0, "z0"));
+  LLOPS_TRY(opt(dS0, "dS0"));
+  LLOPS_TRY(opt(dz0, "dz0"));
   const GBwdWs L = gated_bwd_ws(s);
   if (ws_bytes < L.total)
     return fail(LLOPS_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, L.total);
@@ -952,9 +960,12 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
   auto f32 = [&](size_t off) { return reinterpret_cast<float*>(w + off); };
   const llops::FeatShape fs0 = feat_shape(s, s->n, 0);
   float* fb = L.b.fb ? f32(L.b.fb) : nullptr;
-  if (R == 0) {  // no rows: the Theta gradients are zero
+  if (R == 0) {  // no rows: the Theta (and initial-state) gradients are zero
     LLOPS_HIP(llops::launch_featmap_bwd(fs0, Q, theta_q, dO, 0, dQ, dtheta_q, fb, st), "featmap_bwd");
     LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dO, 0, dK, dtheta_k, fb, st), "featmap_bwd");
+    if (dS0 || dz0)
+      LLOPS_HIP(llops::launch_state_init(BH, s->m, s->dv, nullptr, nullptr, dS0, dz0, st),
+                "state_init");
     return LLOPS_OK;
   }
   const int m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s), DVo = gated_den_w(s);
@@ -971,12 +982,19 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
   // num = M V and, normalised, M 1 (all-ones values DVo wide; column 0 read)
   float* num = f32(L.b.num);
   const uint16_t* vv = static_cast<const uint16_t*>(V);
-  LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st), "attn num");
+  LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st, S0),
+            "attn num");
   float* den = nullptr;
   if (s->normalize) {
     den = f32(L.gden);
     LLOPS_HIP(llops::launch_fill_ones_bf16(u16(L.gones), R * DVo, st), "ones");
-    LLOPS_HIP(gated_attn_on_features(s, m, DVo, phq, phk, u16(L.gones), glf, den, seg, gseg, st),
+    const float* zinit = nullptr;  // z0 in every column of the all-ones pass
+    if (z0) {
+      LLOPS_HIP(llops::launch_state_bcast(z0, BH, m, DVo, f32(L.zbw), st), "state");
+      zinit = f32(L.zbw);
+    }
+    LLOPS_HIP(gated_attn_on_features(s, m, DVo, phq, phk, u16(L.gones), glf, den, seg, gseg, st,
+                                     zinit),
               "attn den");
   }
   uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
@@ -997,9 +1015,14 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
   const llops::AttnShape aMW = attn_shape(&tMW, true, kGatedBwdWG);
   const int64_t perMW = static_cast<int64_t>(MA) * W + MA;
   float *seg2 = f32(L.seg2), *dgb = f32(L.dgb);
+  const bool init = S0 || z0;
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
-    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, vp, glf, tmp, seg, gseg, st), "attn dphi_q");
+    if (init)
+      LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
+    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, vp, glf, tmp, seg, gseg, st,
+                                     init ? f32(L.p0) : nullptr),
+              "attn dphi_q");
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phq, m, p0, W, n, R, 0, 1.f, p0 == 0 ? 1 : 0, dc,
                                        st),
               "rowdot");
@@ -1012,6 +1035,9 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
     LLOPS_HIP(llops::launch_seg_dot(BH, aMW.nseg, perMW, static_cast<int64_t>(MA) * W, seg, seg2,
                                     p0 == 0 ? 1 : 0, dgb, st),
               "segdot");
+    // segment 0's suffix state is sum_i exp(c_i) a_i phi_Q,i^T: [dS0^T; dz0^T] for this slice
+    LLOPS_HIP(llops::launch_state_grad_slice(seg2, aMW.nseg, perMW, BH, m, dv, W, p0, dS0, dz0, st),
+              "state grad");
   }
   // dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j) phi_Q_i over the reversed
   // sequence with its shifted gates; dc_j -= phi_K,j . dphi_K,j
@@ -1036,6 +1062,25 @@ llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void
   LLOPS_HIP(llops::launch_featmap_bwd(fs0, K, theta_k, dphk, 1, dK, dtheta_k, fb, st),
             "featmap_bwd k");
   return LLOPS_OK;
+}
+
+llops_status_t llops_linattn_gated_causal_bwd(const llops_shape_t* s, const void* Q, const void* K,
+                                              const void* V, const void* theta_q,
+                                              const void* theta_k, const float* log_gate,
+                                              const float* dO, float* dQ, float* dK, float* dV,
+                                              float* dtheta_q, float* dtheta_k, float* dlog_gate,
+                                              void* ws, size_t ws_bytes, hipStream_t st) {
+  return gated_bwd_body(s, Q, K, V, theta_q, theta_k, log_gate, nullptr, nullptr, dO, dQ, dK, dV,
+                        dtheta_q, dtheta_k, dlog_gate, nullptr, nullptr, ws, ws_bytes, st);
+}
+
+llops_status_t llops_linattn_gated_causal_bwd_state(
+    const llops_shape_t* s, const void* Q, const void* K, const void* V, const void* theta_q,
+    const void* theta_k, const float* log_gate, const float* S0, const float* z0, const float* dO,
+    float* dQ, float* dK, float* dV, float* dtheta_q, float* dtheta_k, float* dlog_gate,
+    float* dS0, float* dz0, void* ws, size_t ws_bytes, hipStream_t st) {
+  return gated_bwd_body(s, Q, K, V, theta_q, theta_k, log_gate, S0, z0, dO, dQ, dK, dV, dtheta_q,
+                        dtheta_k, dlog_gate, dS0, dz0, ws, ws_bytes, st);
 }
 
 static llops_status_t decode_impl(const llops_shape_t* s, const void* q, const void* k,

@@ -337,12 +337,34 @@ hipError_t launch_seg_bridge_dg(const float* dc, int64_t BH, int64_t n, int64_t 
 
 // ---- backward from an initial state ------------------------------------------
 
-// out[bh][f][c] = z0[bh][f] for c < 16: the initial state of the M 1 pass
-// (all-ones values 16 wide) that adds phi_Q . z0 to every column.
-__global__ __launch_bounds__(256) void state_bcast16(const float* __restrict__ z0, int64_t total,
-                                                     float* __restrict__ out) {
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // over BH * m * 16
-  if (e < total) out[e] = z0[e >> 4];
+// out[bh][f][c] = z0[bh][f] for c < width: the initial state of the M 1 pass
+// (all-ones values `width` wide) that adds phi_Q . z0 to every column.
+__global__ __launch_bounds__(256) void state_bcast(const float* __restrict__ z0, int64_t total,
+                                                   int width, float* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;  // over BH * m * width
+  if (e < total) out[e] = z0[e / width];
+}
+
+// dS0[bh][p0+c][alpha] = U[bh][0][alpha][c] (alpha < dv) and dz0[bh][p0+c] =
+// U[bh][0][dv][c]: the suffix state of segment 0 of a dphi_Q slice's
+// start-anchored pass (keys a = [dnum | dden | 0], values phi_Q columns
+// p0 .. p0+W-1) is sum_i exp(c_i) a_i phi_Q,i^T, the initial state's gradient.
+__global__ __launch_bounds__(256) void state_grad_slice(const float* __restrict__ U, int nseg,
+                                                        int64_t per, int64_t BH, int m, int dv,
+                                                        int W, int p0, float* __restrict__ dS0,
+                                                        float* __restrict__ dz0) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t cnt = static_cast<int64_t>(dv + 1) * W;
+  if (e >= BH * cnt) return;
+  const int64_t bh = e / cnt;
+  const int r = static_cast<int>(e - bh * cnt);
+  const int alpha = r / W, c = r - alpha * W;
+  const float v = U[bh * nseg * per + static_cast<int64_t>(alpha) * W + c];
+  if (alpha < dv) {
+    if (dS0) dS0[(bh * m + p0 + c) * dv + alpha] = v;
+  } else if (dz0) {
+    dz0[bh * m + p0 + c] = v;
+  }
 }
 
 // Initial state of a dphi_Q slice pass (keys b = [V | 1 | 0], MA wide; values
@@ -376,12 +398,24 @@ __global__ __launch_bounds__(256) void col_extract(const float* __restrict__ tot
   out[e] = tot[bh * per + (e - bh * m) * ld];
 }
 
-hipError_t launch_state_bcast16(const float* z0, int64_t BH, int m, float* out, hipStream_t st) {
-  const int64_t total = BH * m * 16;
+hipError_t launch_state_bcast(const float* z0, int64_t BH, int m, int width, float* out,
+                              hipStream_t st) {
+  const int64_t total = BH * m * width;
   if (total == 0) return hipSuccess;
-  if ((total + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
-  LLOPS_LAUNCH("attn_bwd_state", st, state_bcast16, dim3(static_cast<unsigned>((total + 255) / 256)),
-               dim3(256), 0, st, z0, total, out);
+  if ((total + 255) / 256 > 0x7fffffffLL || width < 1) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_state", st, state_bcast, dim3(static_cast<unsigned>((total + 255) / 256)),
+               dim3(256), 0, st, z0, total, width, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_grad_slice(const float* U, int nseg, int64_t per, int64_t BH, int m, int dv,
+                                   int W, int p0, float* dS0, float* dz0, hipStream_t st) {
+  const int64_t total = BH * (dv + 1) * W;
+  if (total == 0 || (!dS0 && !dz0)) return hipSuccess;
+  if ((total + 255) / 256 > 0x7fffffffLL || p0 + W > m) return hipErrorInvalidValue;
+  LLOPS_LAUNCH("gated_bwd_state", st, state_grad_slice,
+               dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, U, nseg, per,
+               BH, m, dv, W, p0, dS0, dz0);
   return hipGetLastError();
 }
 

@@ -82,9 +82,14 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
                           int rev, int den_ld, hipStream_t st);
 // Backward from an initial state (S0 [BH][m][dv], z0 [BH][m]): z0 broadcast
-// over 16 columns, the transposed [S0^T; z0^T] slice that starts a dphi_Q
+// over `width` columns, the transposed [S0^T; z0^T] slice that starts a dphi_Q
 // pass, and one column of per-(b, h) totals.
-hipError_t launch_state_bcast16(const float* z0, int64_t BH, int m, float* out, hipStream_t st);
+hipError_t launch_state_bcast(const float* z0, int64_t BH, int m, int width, float* out,
+                              hipStream_t st);
+// dS0, dz0 columns p0 .. p0+W-1 from segment 0 of a dphi_Q slice's start-anchored
+// suffix states U [BH][nseg][per] (gated backward; either output may be null).
+hipError_t launch_state_grad_slice(const float* U, int nseg, int64_t per, int64_t BH, int m, int dv,
+                                   int W, int p0, float* dS0, float* dz0, hipStream_t st);
 hipError_t launch_build_p0(const float* S0, const float* z0, int64_t BH, int m, int dv, int MA,
                            int W, int p0, float* out, hipStream_t st);
 hipError_t launch_col_extract(const float* tot, int64_t BH, int m, int64_t per, int ld, float* out,

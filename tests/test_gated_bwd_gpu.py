@@ -147,3 +147,69 @@ def test_gated_bwd_shared_aliased_theta(lib):
                                  normalize=True, delta=w.delta)
     for nm, a, b in zip(NAMES, got, want):
         assert rel_fro(host(a), b) <= TOL_BF16, nm
+
+
+@pytest.mark.parametrize("case", [
+    # B, H, n, d, dv, m, t, square, normalize, mu
+    (1, 2, 300, 64, 64, 64, 4, True, True, 3.0),
+    (2, 1, 257, 128, 128, 256, 4, True, True, 4.0),
+    (1, 2, 500, 128, 64, 128, 1, False, False, 2.0),
+    (1, 2, 400, 64, 64, 64, 4, True, True, 0.0),
+])
+def test_gated_bwd_from_initial_state(lib, case):
+    """llops_linattn_gated_causal_bwd_state: the gated forward continued from
+    (S0, z0); all eight gradients against the fp64 chain rule."""
+    B, H, n, d, dv, m, t, square, normalize, mu = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize)
+    x = generate(w)
+    G = dout(w)
+    lg = log_gates(w, mu=mu)
+    rng = np.random.default_rng(41)
+    S0 = (0.01 * rng.standard_normal((B, H, m, dv))).astype(np.float32)
+    z0 = np.abs(0.01 * rng.standard_normal((B, H, m))).astype(np.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce(f"gated_bwd_state {case}")
+    got = lib.llops_linattn_gated_causal_bwd_state(
+        g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], dev(lg, torch.float32),
+        dev(G, torch.float32), S0=dev(S0, torch.float32), z0=dev(z0, torch.float32),
+        square=square, normalize=normalize, delta=w.delta)
+    torch.cuda.synchronize()
+    names = NAMES + ("dS0", "dz0")
+    dtq, dtk = np.zeros(x["theta_q"].shape), np.zeros(x["theta_k"].shape)
+    for b in range(B):
+        for h in range(H):
+            want = O.gated_causal_bwd_state(x["Q"][b, h], x["K"][b, h], x["V"][b, h],
+                                            x["theta_q"][h], x["theta_k"][h], lg[b, h], G[b, h],
+                                            S0[b, h], z0[b, h], square=square,
+                                            normalize=normalize, delta=w.delta)
+            dtq[h] += want[3]
+            dtk[h] += want[4]
+            sel = (got[0][b, h], got[1][b, h], got[2][b, h], None, None, got[5][b, h],
+                   got[6][b, h], got[7][b, h])
+            for nm, a, r in zip(names, sel, want):
+                if a is None:
+                    continue
+                err = rel_fro(host(a), r)
+                assert err <= TOL_BF16, (b, h, nm, err)
+    assert rel_fro(host(got[3]), dtq) <= TOL_BF16
+    assert rel_fro(host(got[4]), dtk) <= TOL_BF16
+
+
+def test_gated_bwd_state_without_state_is_gated_bwd(lib):
+    """No initial state: the same numbers as llops_linattn_gated_causal_bwd bit for bit."""
+    w = _w(1, 2, 300, 64, 64, 64, 4, True, True)
+    x = generate(w)
+    G = dout(w)
+    lg = log_gates(w, mu=3.0)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce("gated_bwd_state without state")
+    a = lib.llops_linattn_gated_causal_bwd_state(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                 g["theta_k"], dev(lg, torch.float32),
+                                                 dev(G, torch.float32), square=True,
+                                                 normalize=True, delta=w.delta)
+    b = lib.llops_linattn_gated_causal_bwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                           dev(lg, torch.float32), dev(G, torch.float32),
+                                           square=True, normalize=True, delta=w.delta)
+    torch.cuda.synchronize()
+    for x1, x2 in zip(a[:6], b):
+        assert torch.equal(x1, x2)
