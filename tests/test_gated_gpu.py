@@ -357,3 +357,30 @@ def test_gated_edge_layouts(lib, case):
     assert rel_fro(host(out), ro) <= TOL_BF16
     assert rel_fro(host(S), rS) <= TOL_BF16
     assert rel_fro(host(z), rz) <= TOL_BF16
+
+
+def test_gated_decode_f32(lib):
+    """fp32 q, k, v and Theta (the fp32 feature map and the fp32-value decode
+    kernel with the gate): 6 steps against the oracle's recurrence at the fp32
+    tolerance."""
+    B, H, d, dv, m, steps = 3, 2, 16, 16, 32, 6
+    w = _w(B, H, steps, d, dv, m, 2, 2, dtype="f32", square=False, normalize=True, delta=1e-3)
+    x, g = _inputs(w)
+    rng = np.random.default_rng(12)
+    S0 = (0.1 * rng.standard_normal((B, H, m, dv))).astype(np.float32)
+    z0 = np.abs(0.1 * rng.standard_normal((B, H, m))).astype(np.float32) + 0.5
+    S, z = torch.from_numpy(S0).cuda(), torch.from_numpy(z0).cuda()
+    lg = np.stack([decode_step_gates(w, s, mu=1.0) for s in range(steps)], axis=2)  # [B, H, steps]
+    kw = dict(square=False, normalize=True, delta=1e-3)
+    announce("gated decode f32")
+    outs = [lib.llops_gated_decode_step(g["Q"][:, :, s], g["K"][:, :, s], g["V"][:, :, s],
+                                        g["theta_q"], g["theta_k"],
+                                        torch.from_numpy(np.ascontiguousarray(lg[:, :, s])).cuda(),
+                                        S, z, **kw) for s in range(steps)]
+    torch.cuda.synchronize()
+    got = np.stack([host(o) for o in outs], axis=2)
+    ro, rS, rz = O.gated_recurrent_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], lg,
+                                      S0=S0, z0=z0, **kw)
+    assert rel_fro(got, ro) <= TOL_F32
+    assert rel_fro(host(S), rS) <= TOL_F32
+    assert rel_fro(host(z), rz) <= TOL_F32
