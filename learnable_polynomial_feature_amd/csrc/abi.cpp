@@ -171,6 +171,8 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
 
 // The non-causal backward needs no reversed copies; it keeps the segment
 // totals instead.
+bool num_den_one_pass(const llops_shape_t* s, bool causal);
+
 BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   BwdWs w{};
   const size_t R = static_cast<size_t>(s->batch * s->heads) * static_cast<size_t>(s->n);
@@ -185,9 +187,12 @@ BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   w.phk = take(R * m * 2);
   w.pkq = take(pack_bytes(s, s->n));
   w.pkk = take(pack_bytes(s, s->n));
+  // den1: M 1 per row; on the 32x32x16 shapes the num pass writes it, else a
+  // pass over all-ones values 16 wide ([R][16], column 0 read)
+  const bool one = num_den_one_pass(s, causal);
   w.num = take(R * dv * 4);
-  w.den1 = take(s->normalize ? R * 16 * 4 : 0);
-  w.ones = take(s->normalize ? R * 16 * 2 : 0);
+  w.den1 = take(s->normalize ? R * (one ? 1 : 16) * 4 : 0);
+  w.ones = take(s->normalize && !one ? R * 16 * 2 : 0);
   w.a = take(R * MA * 2);
   w.ra = take(causal ? R * MA * 2 : 0);
   w.b = take(R * MA * 2);
@@ -201,7 +206,7 @@ BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   w.dphk = take(R * m * 2);
   size_t seg = feat_attn_seg_bytes(s, s->m, s->dv, causal);
   const size_t seg2 = feat_attn_seg_bytes(s, static_cast<int>(MA), static_cast<int>(W), causal);
-  const size_t seg3 = feat_attn_seg_bytes(s, s->m, 16, causal);
+  const size_t seg3 = one ? 0 : feat_attn_seg_bytes(s, s->m, 16, causal);
   if (seg2 > seg) seg = seg2;
   if (seg3 > seg) seg = seg3;
   w.seg = take(seg);
@@ -212,10 +217,10 @@ BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   w.tot = take(causal ? 0 : BH * per * sizeof(float));
   w.fb = take(llops::featmap_bwd_ws_bytes(feat_shape(s, s->n, 0)));
   // causal, from an initial state: totals for dS0 / dz0, the initial state of
-  // a dphi_Q slice pass, and z0 broadcast for the M 1 pass
+  // a dphi_Q slice pass, and z0 broadcast for a separate M 1 pass
   w.stot = take(causal ? BH * (m * dv + m) * sizeof(float) : 0);
   w.p0 = take(causal ? BH * MA * W * sizeof(float) : 0);
-  w.zb16 = take(causal ? BH * m * 16 * sizeof(float) : 0);
+  w.zb16 = take(causal && !one ? BH * m * 16 * sizeof(float) : 0);
   w.total = off;
   return w;
 }
@@ -384,14 +389,44 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
               : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
 }
 
+// num = M V and den = M 1 in one pass on the 32x32x16 shapes: the output pass
+// forms each row's denominator phi_Q,i . z_i for the normalised form anyway,
+// so it stores it beside the unnormalised row. (S0init, z0init): the initial
+// state (causal; null = zeros).
+bool num_den_one_pass(const llops_shape_t* s, bool causal) {
+  const llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
+  return llops::attn32_supported(attn_shape(&t, causal));
+}
+
+hipError_t attn_num_den(const llops_shape_t* s, bool causal, const uint16_t* fq,
+                        const uint16_t* fk, const uint16_t* v, float* num, float* den, float* seg,
+                        float* tot, hipStream_t st, const float* S0init, const float* z0init) {
+  llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
+  t.normalize = 1;  // delta stays 0: den is phi_Q . z
+  const llops::AttnShape a = attn_shape(&t, causal);
+  if (!llops::attn32_supported(a)) return hipErrorInvalidValue;
+  const int64_t MD = static_cast<int64_t>(s->m) * s->dv, per = MD + s->m;
+  hipError_t e = llops::launch_seg_state32(a, fk, v, seg, st);
+  if (e != hipSuccess) return e;
+  const float* state = seg;
+  int64_t st_seg = per, st_bh = per * a.nseg;
+  if (causal) {
+    e = llops::launch_seg_scan(a, seg, S0init, z0init, nullptr, nullptr, 1, st);
+  } else {
+    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, tot, tot + MD, 0, st);
+    state = tot;
+    st_seg = 0;
+    st_bh = per;
+  }
+  if (e != hipSuccess) return e;
+  return llops::launch_attn_out32_den(a, fq, fk, v, state, st_seg, st_bh, num, den, st);
+}
+
 // ---- gated causal backward ---------------------------------------------------
-// The denominator pass of the gated backward runs M against all-ones values
-// of a width the 32x32x16 kernels take for m.
-int gated_den_w(const llops_shape_t* s) { return s->m == 256 ? 128 : 64; }
 
 struct GBwdWs {
   BwdWs b;  // the ungated backward's buffers (its seg and den1/ones are not used)
-  size_t glf, grev, glr, gseg, gones, gden, dc, seg, seg2, dgb, p0, zbw, total;
+  size_t glf, grev, glr, gseg, gden, dc, seg, seg2, dgb, p0, total;
 };
 
 GBwdWs gated_bwd_ws(const llops_shape_t* s) {
@@ -406,25 +441,21 @@ GBwdWs gated_bwd_ws(const llops_shape_t* s) {
   const size_t BH = static_cast<size_t>(s->batch * s->heads);
   const size_t R = BH * static_cast<size_t>(s->n);
   const size_t nld = static_cast<size_t>((s->n + 31) / 32 * 32);
-  const int DVo = gated_den_w(s), MA = bwd_ma(s), W = bwd_w(s);
+  const int MA = bwd_ma(s), W = bwd_w(s);
   w.glf = take(BH * nld * 4);   // chunk-local sums of the forward gates
   w.grev = take(R * 4);         // gates of the reversed sequence
   w.glr = take(BH * nld * 4);   // and their chunk-local sums
   const llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
   w.gseg = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);
-  w.gones = take(s->normalize ? R * DVo * 2 : 0);
-  w.gden = take(s->normalize ? R * DVo * 4 : 0);
+  w.gden = take(s->normalize ? R * 4 : 0);  // M 1 per row, from the num pass
   w.dc = take(R * 4);           // d/dc_i = phi_Q,i . dphi_Q,i - phi_K,i . dphi_K,i
   size_t seg = feat_attn_seg_bytes(s, s->m, s->dv, true, kGatedBwdWG);
   const size_t seg2 = feat_attn_seg_bytes(s, MA, W, true, kGatedBwdWG);
-  const size_t seg3 = feat_attn_seg_bytes(s, s->m, DVo, true, kGatedBwdWG);
   if (seg2 > seg) seg = seg2;
-  if (seg3 > seg) seg = seg3;
   w.seg = take(seg);
   w.seg2 = take(feat_attn_seg_bytes(s, MA, W, true, kGatedBwdWG));  // suffix states, dphi_Q slices
   w.dgb = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);  // dg at starts
   w.p0 = take(BH * static_cast<size_t>(MA) * W * 4);  // initial state of a dphi_Q slice pass
-  w.zbw = take(s->normalize ? BH * static_cast<size_t>(s->m) * DVo * 4 : 0);  // z0 broadcast
   w.total = off;
   return w;
 }
@@ -453,6 +484,22 @@ hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const u
   if (e == hipSuccess)
     e = llops::launch_seg_scan_gated(a, seg, gseg, S0init, nullptr, nullptr, nullptr, st);
   if (e == hipSuccess) e = llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
+  return e;
+}
+
+// Gated num = M V and den = M 1 per row in one pass (see attn_num_den).
+hipError_t gated_attn_num_den(const llops_shape_t* s, const uint16_t* fq, const uint16_t* fk,
+                              const uint16_t* v, const float* gl, float* num, float* den,
+                              float* seg, float* gseg, hipStream_t st, const float* S0init,
+                              const float* z0init) {
+  llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
+  t.normalize = 1;  // delta stays 0: den is phi_Q . z
+  const llops::AttnShape a = attn_shape(&t, true, kGatedBwdWG);
+  if (!llops::attn32_supported(a)) return hipErrorInvalidValue;
+  hipError_t e = llops::launch_seg_state32_gated(a, fk, v, gl, gseg, seg, st);
+  if (e == hipSuccess)
+    e = llops::launch_seg_scan_gated(a, seg, gseg, S0init, z0init, nullptr, nullptr, st);
+  if (e == hipSuccess) e = llops::launch_attn_out32_gated_den(a, fq, fk, v, gl, seg, num, den, st);
   return e;
 }
 
@@ -810,13 +857,23 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // feature maps of Q and K (bf16, as the forward stores them)
   llops::FeatJob jobs[2] = {{Q, theta_q, phq, w + L.pkq}, {K, theta_k, phk, w + L.pkk}};
   LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, n, 1), jobs, 2, st), "featmap");
-  // num = M V and, with the normaliser, M 1
+  // num = M V and, with the normaliser, M 1: one pass on the 32x32x16
+  // shapes, else a second pass over all-ones values
   float* num = f32(L.num);
-  LLOPS_HIP(attn_on_features(s, causal, m, dv, phq, phk, static_cast<const uint16_t*>(V), num, seg,
-                             tot, st, S0),
-            "attn num");
   float* den1 = nullptr;
-  if (s->normalize) {
+  int den_ld = 16;
+  if (s->normalize && num_den_one_pass(s, causal)) {
+    den1 = f32(L.den1);
+    den_ld = 1;
+    LLOPS_HIP(attn_num_den(s, causal, phq, phk, static_cast<const uint16_t*>(V), num, den1, seg,
+                           tot, st, S0, z0),
+              "attn num den");
+  } else {
+    LLOPS_HIP(attn_on_features(s, causal, m, dv, phq, phk, static_cast<const uint16_t*>(V), num,
+                               seg, tot, st, S0),
+              "attn num");
+  }
+  if (s->normalize && den_ld == 16) {
     den1 = f32(L.den1);
     LLOPS_HIP(llops::launch_fill_ones16(u16(L.ones), R, st), "ones");
     const float* zinit = nullptr;  // z0 in every column of the all-ones pass
@@ -833,7 +890,7 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   uint16_t *ra = causal ? u16(L.ra) : nullptr, *rb = causal ? u16(L.rb) : nullptr;
   LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
                                   s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
-                                  causal ? 1 : 0, 16, st),
+                                  causal ? 1 : 0, den_ld, st),
             "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
@@ -968,7 +1025,7 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
                 "state_init");
     return LLOPS_OK;
   }
-  const int m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s), DVo = gated_den_w(s);
+  const int m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s);
   const int64_t n = s->n;
   uint16_t *phq = u16(L.b.phq), *phk = u16(L.b.phk);
   float *seg = f32(L.seg), *gseg = f32(L.gseg);
@@ -979,28 +1036,22 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, log_gate, glf, st), "gate_cumsum");
   LLOPS_HIP(llops::launch_gate_reverse_shift(log_gate, n, R, grev, st), "gate_reverse");
   LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, grev, glr, st), "gate_cumsum");
-  // num = M V and, normalised, M 1 (all-ones values DVo wide; column 0 read)
+  // num = M V and, normalised, M 1 per row from the same pass
   float* num = f32(L.b.num);
   const uint16_t* vv = static_cast<const uint16_t*>(V);
-  LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st, S0),
-            "attn num");
   float* den = nullptr;
   if (s->normalize) {
     den = f32(L.gden);
-    LLOPS_HIP(llops::launch_fill_ones_bf16(u16(L.gones), R * DVo, st), "ones");
-    const float* zinit = nullptr;  // z0 in every column of the all-ones pass
-    if (z0) {
-      LLOPS_HIP(llops::launch_state_bcast(z0, BH, m, DVo, f32(L.zbw), st), "state");
-      zinit = f32(L.zbw);
-    }
-    LLOPS_HIP(gated_attn_on_features(s, m, DVo, phq, phk, u16(L.gones), glf, den, seg, gseg, st,
-                                     zinit),
-              "attn den");
+    LLOPS_HIP(gated_attn_num_den(s, phq, phk, vv, glf, num, den, seg, gseg, st, S0, z0),
+              "attn num den");
+  } else {
+    LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st, S0),
+              "attn num");
   }
   uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
   uint16_t *ra = u16(L.b.ra), *rb = u16(L.b.rb);
   LLOPS_HIP(llops::launch_make_ab(num, den, dO, vv, dv, MA, n, R, s->normalize,
-                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, 1, DVo, st),
+                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, 1, 1, st),
             "make_ab");
   uint16_t* vp = u16(L.b.vp);
   float* tmp = f32(L.b.tmp);

@@ -313,11 +313,14 @@ struct Out32Geom {
   static_assert(QP % NT == 0 && VPc % NT == 0, "chunk pieces split evenly over the threads");
 };
 
-template <int M, int DV, bool CAUSAL, bool GATED>
+// DENOUT: the row's denominator (without delta) goes to den_out [BH][n] and the
+// output row stays unnormalised (a.normalize set, so both are formed as in
+// the normalised pass); the backward takes num and den from one pass.
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
-                int64_t st_bh, float* __restrict__ out) {
+                int64_t st_bh, float* __restrict__ out, float* __restrict__ den_out) {
   using G = Out32Geom<M, DV, GATED>;
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
@@ -617,7 +620,17 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
             for (int d = 0; d < FH && d < NWD; ++d) den[e] += pv[hf * NWD + d];
           // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
-          val[e] *= __builtin_amdgcn_rcpf(den[e]);
+          if constexpr (!DENOUT) val[e] *= __builtin_amdgcn_rcpf(den[e]);
+        }
+        if constexpr (DENOUT) {  // one lane per 32-lane group: its 8 rows
+          if (dvt == 0 && c32 == 0) {
+            float* drow = den_out + bh * a.n + c0 + 4 * hh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int r = 8 * ((kept + e) >> 2) + (e & 3);
+              if (c0 + r + 4 * hh < t1) drow[r] = den[e];
+            }
+          }
         }
       }
       // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
@@ -692,19 +705,19 @@ hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t*
   return hipGetLastError();
 }
 
-template <int M, int DV, bool CAUSAL, bool GATED>
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* gl, const float* state, int64_t ss,
-                        int64_t sb, float* out, hipStream_t st) {
+                        int64_t sb, float* out, hipStream_t st, float* den = nullptr) {
   using G = Out32Geom<M, DV, GATED>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
   const size_t lds = G::lds_bytes();
-  auto* kern = attn_out32<M, DV, CAUSAL, GATED>;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH(GATED ? "attn_out_gated" : "attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st,
-               a, q, k, v, state, ss, sb, out);
+               a, q, k, v, state, ss, sb, out, den);
   return hipGetLastError();
 }
 
@@ -751,6 +764,22 @@ hipError_t launch_attn_out32(const AttnShape& s, const uint16_t* phiq, const uin
   }
 }
 
+hipError_t launch_attn_out32_den(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
+                                 const uint16_t* v, const float* state, int64_t st_seg,
+                                 int64_t st_bh, float* out, float* den, hipStream_t st) {
+  if (!s.normalize || !den) return hipErrorInvalidValue;
+  const float* g = nullptr;
+  switch (key32(s) * 2 + (s.causal ? 1 : 0)) {
+    case 256128 * 2 + 1: return launch_out_t<256, 128, true, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    case 256128 * 2: return launch_out_t<256, 128, false, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    case 128064 * 2 + 1: return launch_out_t<128, 64, true, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    case 128064 * 2: return launch_out_t<128, 64, false, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    case 64064 * 2 + 1: return launch_out_t<64, 64, true, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    case 64064 * 2: return launch_out_t<64, 64, false, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L, hipStream_t st) {
   const int64_t nch = (n + kC - 1) / kC, total = BH * nch;
   if (total == 0) return hipSuccess;
@@ -790,6 +819,20 @@ hipError_t launch_attn_out32_gated(const AttnShape& s, const uint16_t* phiq, con
     case 256128: return launch_out_t<256, 128, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
     case 128064: return launch_out_t<128, 64, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
     case 64064: return launch_out_t<64, 64, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_out32_gated_den(const AttnShape& s, const uint16_t* phiq,
+                                       const uint16_t* phik, const uint16_t* v, const float* gl,
+                                       const float* state, float* out, float* den,
+                                       hipStream_t st) {
+  if (!s.causal || !s.normalize || !den) return hipErrorInvalidValue;
+  const int64_t per = static_cast<int64_t>(s.m) * s.dv + s.m;
+  switch (key32(s)) {
+    case 256128: return launch_out_t<256, 128, true, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st, den);
+    case 128064: return launch_out_t<128, 64, true, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st, den);
+    case 64064: return launch_out_t<64, 64, true, true, true>(s, phiq, phik, v, gl, state, per, per * s.nseg, out, st, den);
     default: return hipErrorInvalidValue;
   }
 }

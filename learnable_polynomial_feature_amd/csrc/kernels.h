@@ -154,6 +154,11 @@ hipError_t launch_seg_state32(const AttnShape& a, const uint16_t* phik, const ui
 hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                              const uint16_t* v, const float* state, int64_t state_seg_stride,
                              int64_t state_bh_stride, float* out, hipStream_t st);
+// The same pass with a.normalize set, writing the unnormalised rows to out
+// and each row's denominator phi_Q,i . z_i (no delta) to den [BH][n].
+hipError_t launch_attn_out32_den(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
+                                 const uint16_t* v, const float* state, int64_t state_seg_stride,
+                                 int64_t state_bh_stride, float* out, float* den, hipStream_t st);
 
 // Gated causal passes (per-token log gates g [BH][n], decay exp(g)), on the
 // 32x32x16 kernels' shapes. gate_cumsum32 writes L = the inclusive sum of g
@@ -166,6 +171,10 @@ hipError_t launch_seg_state32_gated(const AttnShape& a, const uint16_t* phik, co
 hipError_t launch_attn_out32_gated(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                                    const uint16_t* v, const float* gl, const float* state,
                                    float* out, hipStream_t st);
+hipError_t launch_attn_out32_gated_den(const AttnShape& a, const uint16_t* phiq,
+                                       const uint16_t* phik, const uint16_t* v, const float* gl,
+                                       const float* state, float* out, float* den,
+                                       hipStream_t st);
 // fp32 gated passes over the raw log gates g [BH][n] (any chunk, m, dv).
 hipError_t launch_seg_state_f32_gated(const AttnShape& a, const float* phik, const float* v,
                                       const float* log_gate, float* gseg, float* seg,
