@@ -362,14 +362,23 @@ llops_status_t validate_gated(const llops_shape_t* s) {
 // out_i = sum_{j<=i} (fq_i . fk_j) v_j (causal) or sum over all j (tot holds
 // the per-(b, h) totals then) over bf16 features fq, fk [BH][n][M] and values
 // v [BH][n][DV]; fp32 out. The forward's segment kernels.
+// outb (bf16, rows ldo apart) and rev (rows written in reversed order): the
+// 32x32x16 kernels only (on32).
+bool on32(const llops_shape_t* s, bool causal, int M, int DV) {
+  const llops_shape_t t = feat_attn_shape(s, M, DV);
+  return llops::attn32_supported(attn_shape(&t, causal));
+}
+
 hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
                             const uint16_t* fq, const uint16_t* fk, const uint16_t* v, float* out,
                             float* seg, float* tot, hipStream_t st,
-                            const float* S0init = nullptr) {
+                            const float* S0init = nullptr, uint16_t* outb = nullptr, int ldo = 0,
+                            int rev = 0) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   const llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
   const bool mf32 = llops::attn32_supported(a);
+  if ((outb || rev) && !mf32) return hipErrorInvalidValue;
   hipError_t e = mf32 ? llops::launch_seg_state32(a, fk, v, seg, st)
                       : llops::launch_seg_state_bf16(a, fk, v, seg, st);
   if (e != hipSuccess) return e;
@@ -385,6 +394,8 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
     st_bh = per;
   }
   if (e != hipSuccess) return e;
+  if (outb || rev)
+    return llops::launch_attn_out32_to(a, fq, fk, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
   return mf32 ? llops::launch_attn_out32(a, fq, fk, v, state, st_seg, st_bh, out, st)
               : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
 }
@@ -914,27 +925,37 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   }
   // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j (+ dnum_i . S0 + dden_i z0 from an
   // initial state), W columns of phi_K at a time
+  // On the 32x32x16 kernels the passes write dphi (bf16, a column slice) and
+  // dV (reversed) in place; otherwise through tmp and a row copy.
+  const bool inplace = on32(s, causal, MA, W);
   const bool init = causal && (S0 || z0);
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     if (init)
       LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
     LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, vp, tmp, seg, tot, st,
-                               init ? f32(L.p0) : nullptr),
+                               init ? f32(L.p0) : nullptr, inplace ? dphq + p0 : nullptr, m),
               "attn dphi_q");
-    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
+    if (!inplace)
+      LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
   }
   // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: causal over the reversed sequence
   const int rv = causal ? 1 : 0;
   for (int p0 = 0; p0 < m; p0 += W) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
     LLOPS_HIP(attn_on_features(s, causal, MA, W, causal ? rb : b, causal ? ra : a, vp, tmp, seg,
-                               tot, st),
+                               tot, st, nullptr, inplace ? dphk + p0 : nullptr, m,
+                               inplace ? rv : 0),
               "attn dphi_k");
-    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, rv, st), "rows");
+    if (!inplace)
+      LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, rv, st), "rows");
   }
   // dV_j = sum_{i(>=j)} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
-  if (causal) {
+  if (causal && on32(s, true, m, dv)) {
+    LLOPS_HIP(attn_on_features(s, true, m, dv, rphk, rphq, dn, dV, seg, nullptr, st, nullptr,
+                               nullptr, 0, 1),
+              "attn dv");
+  } else if (causal) {
     LLOPS_HIP(attn_on_features(s, true, m, dv, rphk, rphq, dn, tmp, seg, nullptr, st), "attn dv");
     LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
   } else {

@@ -316,11 +316,16 @@ struct Out32Geom {
 // DENOUT: the row's denominator (without delta) goes to den_out [BH][n] and the
 // output row stays unnormalised (a.normalize set, so both are formed as in
 // the normalised pass); the backward takes num and den from one pass.
-template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false>
+// OM, the output rows' destination: 0 out [BH][n][DV]; bit 0 set, row t of
+// the pass goes to row n - 1 - t (a pass over the reversed sequence writes
+// in the original order); bit 1 set, bf16 (RNE) into outb, rows ldo elements
+// apart (a column slice of a wider row).
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
-                int64_t st_bh, float* __restrict__ out, float* __restrict__ den_out) {
+                int64_t st_bh, float* __restrict__ out, float* __restrict__ den_out,
+                uint16_t* __restrict__ outb, int ldo) {
   using G = Out32Geom<M, DV, GATED>;
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
@@ -635,7 +640,19 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       }
       // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
       float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
-      if (c0 + kC <= t1) {  // whole chunk in range: no per-row checks
+      if constexpr (OM != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t t = c0 + 8 * ((kept + e) >> 2) + (e & 3) + 4 * hh;
+          if (t < t1) {
+            const int64_t tt = bh * a.n + ((OM & 1) ? a.n - 1 - t : t);
+            if constexpr ((OM & 2) != 0)
+              outb[tt * ldo + dvt * 32 + c32] = f32_to_bf16(val[e]);
+            else
+              out[tt * DV + dvt * 32 + c32] = val[e];
+          }
+        }
+      } else if (c0 + kC <= t1) {  // whole chunk in range: no per-row checks
 #pragma unroll
         for (int e = 0; e < 8; ++e) orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV] = val[e];
       } else {
@@ -705,19 +722,20 @@ hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t*
   return hipGetLastError();
 }
 
-template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false>
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* gl, const float* state, int64_t ss,
-                        int64_t sb, float* out, hipStream_t st, float* den = nullptr) {
+                        int64_t sb, float* out, hipStream_t st, float* den = nullptr,
+                        uint16_t* outb = nullptr, int ldo = 0) {
   using G = Out32Geom<M, DV, GATED>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
   const size_t lds = G::lds_bytes();
-  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT>;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH(GATED ? "attn_out_gated" : "attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st,
-               a, q, k, v, state, ss, sb, out, den);
+               a, q, k, v, state, ss, sb, out, den, outb, ldo);
   return hipGetLastError();
 }
 
@@ -776,6 +794,37 @@ hipError_t launch_attn_out32_den(const AttnShape& s, const uint16_t* phiq, const
     case 128064 * 2: return launch_out_t<128, 64, false, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
     case 64064 * 2 + 1: return launch_out_t<64, 64, true, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
     case 64064 * 2: return launch_out_t<64, 64, false, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st, den);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int M, int DV>
+hipError_t launch_out_om(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                         const uint16_t* v, const float* state, int64_t ss, int64_t sb,
+                         float* out, uint16_t* outb, int ldo, int rev, hipStream_t st) {
+  const int om = (outb ? 2 : 0) | (rev ? 1 : 0);
+  const float* g = nullptr;
+  if (!s.causal) {
+    if (om != 2) return hipErrorInvalidValue;
+    return launch_out_t<M, DV, false, false, false, 2>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo);
+  }
+  switch (om) {
+    case 1: return launch_out_t<M, DV, true, false, false, 1>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo);
+    case 2: return launch_out_t<M, DV, true, false, false, 2>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo);
+    case 3: return launch_out_t<M, DV, true, false, false, 3>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_out32_to(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
+                                const uint16_t* v, const float* state, int64_t st_seg,
+                                int64_t st_bh, float* out, uint16_t* outb, int ldo, int rev,
+                                hipStream_t st) {
+  if (outb ? ldo < s.dv : !out) return hipErrorInvalidValue;
+  switch (key32(s)) {
+    case 256128: return launch_out_om<256, 128>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
+    case 128064: return launch_out_om<128, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
+    case 64064: return launch_out_om<64, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
     default: return hipErrorInvalidValue;
   }
 }

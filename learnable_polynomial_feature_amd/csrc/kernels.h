@@ -154,6 +154,13 @@ hipError_t launch_seg_state32(const AttnShape& a, const uint16_t* phik, const ui
 hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                              const uint16_t* v, const float* state, int64_t state_seg_stride,
                              int64_t state_bh_stride, float* out, hipStream_t st);
+// The same pass writing its rows elsewhere: to outb (bf16, RNE; rows ldo
+// elements apart, e.g. a column slice of a wider row) when outb is set, else
+// to out; rev = 1 (causal only): row t of the pass goes to row n - 1 - t.
+hipError_t launch_attn_out32_to(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
+                                const uint16_t* v, const float* state, int64_t state_seg_stride,
+                                int64_t state_bh_stride, float* out, uint16_t* outb, int ldo,
+                                int rev, hipStream_t st);
 // The same pass with a.normalize set, writing the unnormalised rows to out
 // and each row's denominator phi_Q,i . z_i (no delta) to den [BH][n].
 hipError_t launch_attn_out32_den(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
