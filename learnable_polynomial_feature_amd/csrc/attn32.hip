@@ -627,29 +627,45 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
           // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
           if constexpr (!DENOUT) val[e] *= __builtin_amdgcn_rcpf(den[e]);
         }
-        if constexpr (DENOUT) {  // one lane per 32-lane group: its 8 rows
-          if (dvt == 0 && c32 == 0) {
-            float* drow = den_out + bh * a.n + c0 + 4 * hh;
+      }
+      if constexpr (DENOUT) {
+        // row q = lane of the first 32 lanes of wave 0: the same sum, in the
+        // same order, from the exchange area (read only after the barrier)
+        if (w == 0 && lane < kC && c0 + lane < t1) {
+          float dq = a.delta + (CAUSAL ? rsum[lane] : 0.f);
+          const u32x4 lo = ld16(part + lane * 8), hi = ld16(part + lane * 8 + 4);
+          const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
+                               __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                               __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                               __uint_as_float(hi[2]), __uint_as_float(hi[3])};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int r = 8 * ((kept + e) >> 2) + (e & 3);
-              if (c0 + r + 4 * hh < t1) drow[r] = den[e];
-            }
-          }
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
+          den_out[bh * a.n + c0 + lane] = dq;
         }
       }
       // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
       float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
       if constexpr (OM != 0) {
+        // destination row of this lane's first row c0 + 4hh, then rows r
+        // further on (or back, reversed): wave-uniform offsets
+        const int64_t tb = c0 + 4 * hh;
+        const int64_t d0 = bh * a.n + ((OM & 1) ? a.n - 1 - tb : tb);
+        constexpr int sgn = (OM & 1) ? -1 : 1;
+        if constexpr ((OM & 2) != 0) {
+          uint16_t* ob = outb + d0 * ldo + dvt * 32 + c32;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t t = c0 + 8 * ((kept + e) >> 2) + (e & 3) + 4 * hh;
-          if (t < t1) {
-            const int64_t tt = bh * a.n + ((OM & 1) ? a.n - 1 - t : t);
-            if constexpr ((OM & 2) != 0)
-              outb[tt * ldo + dvt * 32 + c32] = f32_to_bf16(val[e]);
-            else
-              out[tt * DV + dvt * 32 + c32] = val[e];
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * ((kept + e) >> 2) + (e & 3);
+            if (tb + r < t1) ob[sgn * r * ldo] = f32_to_bf16(val[e]);
+          }
+        } else {
+          float* ob = out + d0 * DV + dvt * 32 + c32;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * ((kept + e) >> 2) + (e & 3);
+            if (tb + r < t1) ob[sgn * r * DV] = val[e];
           }
         }
       } else if (c0 + kC <= t1) {  // whole chunk in range: no per-row checks
