@@ -373,14 +373,15 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
                             const uint16_t* fq, const uint16_t* fk, const uint16_t* v, float* out,
                             float* seg, float* tot, hipStream_t st,
                             const float* S0init = nullptr, uint16_t* outb = nullptr, int ldo = 0,
-                            int rev = 0) {
+                            int rev = 0, int vld = 0) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   const llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
   const bool mf32 = llops::attn32_supported(a);
-  if ((outb || rev) && !mf32) return hipErrorInvalidValue;
-  hipError_t e = mf32 ? llops::launch_seg_state32(a, fk, v, seg, st)
-                      : llops::launch_seg_state_bf16(a, fk, v, seg, st);
+  if ((outb || rev || vld) && !mf32) return hipErrorInvalidValue;
+  hipError_t e = vld    ? llops::launch_seg_state32_v(a, fk, v, vld, seg, st)
+                 : mf32 ? llops::launch_seg_state32(a, fk, v, seg, st)
+                        : llops::launch_seg_state_bf16(a, fk, v, seg, st);
   if (e != hipSuccess) return e;
   const float* state = seg;
   int64_t st_seg = per, st_bh = per * a.nseg;
@@ -395,7 +396,8 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
   }
   if (e != hipSuccess) return e;
   if (outb || rev)
-    return llops::launch_attn_out32_to(a, fq, fk, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
+    return llops::launch_attn_out32_to(a, fq, fk, v, state, st_seg, st_bh, out, outb, ldo, rev, st,
+                                       vld);
   return mf32 ? llops::launch_attn_out32(a, fq, fk, v, state, st_seg, st_bh, out, st)
               : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
 }
@@ -927,14 +929,19 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // initial state), W columns of phi_K at a time
   // On the 32x32x16 kernels the passes write dphi (bf16, a column slice) and
   // dV (reversed) in place; otherwise through tmp and a row copy.
+  // They also read their phi slice in place (rows m apart; the reversed
+  // sequence's from the reversed copy of phi_Q) instead of from a sliced copy.
   const bool inplace = on32(s, causal, MA, W);
+  const bool sliced = inplace && n * m * 2 < (int64_t{1} << 31);
   const bool init = causal && (S0 || z0);
   for (int p0 = 0; p0 < m; p0 += W) {
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
+    if (!sliced)
+      LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     if (init)
       LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
-    LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, vp, tmp, seg, tot, st,
-                               init ? f32(L.p0) : nullptr, inplace ? dphq + p0 : nullptr, m),
+    LLOPS_HIP(attn_on_features(s, causal, MA, W, a, b, sliced ? phk + p0 : vp, tmp, seg, tot, st,
+                               init ? f32(L.p0) : nullptr, inplace ? dphq + p0 : nullptr, m, 0,
+                               sliced ? m : 0),
               "attn dphi_q");
     if (!inplace)
       LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
@@ -942,10 +949,12 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: causal over the reversed sequence
   const int rv = causal ? 1 : 0;
   for (int p0 = 0; p0 < m; p0 += W) {
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
-    LLOPS_HIP(attn_on_features(s, causal, MA, W, causal ? rb : b, causal ? ra : a, vp, tmp, seg,
+    if (!sliced)
+      LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
+    const uint16_t* qv = sliced ? (causal ? rphq : phq) + p0 : vp;
+    LLOPS_HIP(attn_on_features(s, causal, MA, W, causal ? rb : b, causal ? ra : a, qv, tmp, seg,
                                tot, st, nullptr, inplace ? dphk + p0 : nullptr, m,
-                               inplace ? rv : 0),
+                               inplace ? rv : 0, sliced ? m : 0),
               "attn dphi_k");
     if (!inplace)
       LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, rv, st), "rows");

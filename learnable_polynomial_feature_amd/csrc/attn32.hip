@@ -117,11 +117,13 @@ struct Seg32Geom {
 // carried to its end, sum_k exp(c_k - c_{t0-1}) phi_K,k v_k^T: weights
 // exp(D + L_k) with D the sum of the segment's earlier chunks, no decay of
 // the accumulator (every exponent still <= 0 for g <= 0).
-template <int M, int DV, bool GATED, bool ANCHOR = false>
+// VSTR: the value rows are vld elements apart (a column slice of a wider
+// row; v points at the slice's first column).
+template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false>
 __global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                                                      const uint16_t* __restrict__ v,
-                                                     float* __restrict__ seg) {
+                                                     float* __restrict__ seg, int vld) {
   using G = Seg32Geom<M, DV>;
   constexpr int FT = G::FT, MP = G::MP, VP = G::VP, NT = G::NT;
   constexpr int BUF = kC * MP + kC * VP + (GATED ? kGL : 0);  // phi_K, V [, gate sums]
@@ -136,7 +138,8 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   const int64_t t0 = gseg * a.seg_len;
   const int64_t t1 = min(a.n, t0 + a.seg_len);
   const uint16_t* Kg = phik + bh * a.n * M;
-  const uint16_t* Vg = v + bh * a.n * DV;
+  const int VL = VSTR ? vld : DV;
+  const uint16_t* Vg = v + bh * a.n * VL;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
 
   // Raw buffer views of this segment's rows: reads past the segment end
@@ -144,7 +147,9 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   // number in flight is static and a wait for one chunk never drains the next.
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
-  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
+  // strided: the view ends at the slice's last element
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(
+      Vg + t0 * VL, VSTR ? (seg_rows ? ((seg_rows - 1u) * VL + DV) * 2u : 0u) : seg_rows * DV * 2u);
   // gated: the chunk's 32 gate sums (128 bytes) come with the chunk, one per
   // lane of the first half of wave 0
   const __amdgpu_buffer_rsrc_t rsg =
@@ -158,7 +163,11 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
       rk[i] = buf_ld16(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
 #pragma unroll
     for (int i = 0; i < LV; ++i)
-      rv[i] = buf_ld16(rsv, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
+      rv[i] = buf_ld16(rsv,
+                       VSTR ? static_cast<uint32_t>((tid + i * NT) / (DV / 8)) * (VL * 2u) +
+                                  static_cast<uint32_t>((tid + i * NT) % (DV / 8)) * 16u
+                            : (tid + i * NT) * 16u,
+                       static_cast<uint32_t>(c) * (kC * VL * 2u));
     if (GATED && w == 0) rg = buf_ld4(rsg, (lane & 31) * 4u + static_cast<uint32_t>(c) * (kC * 4u));
   };
   auto store = [&](uint16_t* buf, const u32x4 (&rk)[LK], const u32x4 (&rv)[LV]) {
@@ -320,12 +329,13 @@ struct Out32Geom {
 // the pass goes to row n - 1 - t (a pass over the reversed sequence writes
 // in the original order); bit 1 set, bf16 (RNE) into outb, rows ldo elements
 // apart (a column slice of a wider row).
-template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0>
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
+          bool VSTR = false>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
                 int64_t st_bh, float* __restrict__ out, float* __restrict__ den_out,
-                uint16_t* __restrict__ outb, int ldo) {
+                uint16_t* __restrict__ outb, int ldo, int vld) {
   using G = Out32Geom<M, DV, GATED>;
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
@@ -346,7 +356,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   const int64_t t1 = min(a.n, t0 + a.seg_len);
   const uint16_t* Qg = phiq + bh * a.n * M;
   const uint16_t* Kg = phik + bh * a.n * M;
-  const uint16_t* Vg = v + bh * a.n * DV;
+  const int VL = VSTR ? vld : DV;  // value row stride (VSTR: a column slice)
+  const uint16_t* Vg = v + bh * a.n * VL;
   float* Og = out + bh * a.n * DV;
   const float* Sin = state + bh * st_bh + gseg * st_seg;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
@@ -373,7 +384,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
   const __amdgpu_buffer_rsrc_t rsq = make_rsrc(Qg + t0 * M, seg_rows * M * 2u);
   const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
-  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(
+      Vg + t0 * VL, VSTR ? (seg_rows ? ((seg_rows - 1u) * VL + DV) * 2u : 0u) : seg_rows * DV * 2u);
   // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
   // contiguous bytes each; a thread's pieces t + i*NT never straddle two
   // tensors, so the selection folds away
@@ -394,7 +406,11 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       else if (i * NT < 2 * QP)
         r[i] = buf_ld16(rsk, (p - QP) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
       else
-        r[i] = buf_ld16(rsv, (p - 2 * QP) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
+        r[i] = buf_ld16(rsv,
+                        VSTR ? static_cast<uint32_t>((p - 2 * QP) / (DV / 8)) * (VL * 2u) +
+                                   static_cast<uint32_t>((p - 2 * QP) % (DV / 8)) * 16u
+                             : (p - 2 * QP) * 16u,
+                        static_cast<uint32_t>(c) * (kC * VL * 2u));
     }
   };
   auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT], const uint32_t& rg) {
@@ -723,35 +739,36 @@ __global__ __launch_bounds__(256) void gate_cumsum32(int64_t n, int64_t nch, int
   if (live) L[bh * nch * kC + tok] = x;
 }
 
-template <int M, int DV, bool GATED, bool ANCHOR = false>
+template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false>
 hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, const float* gl,
-                          float* gseg, float* seg, hipStream_t st) {
+                          float* gseg, float* seg, hipStream_t st, int vld = 0) {
   using G = Seg32Geom<M, DV>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, gseg};
   const size_t lds = 2ull * (kC * G::MP + kC * G::VP + (GATED ? kGL : 0)) * sizeof(uint16_t);
-  auto* kern = seg_state32<M, DV, GATED, ANCHOR>;
+  auto* kern = seg_state32<M, DV, GATED, ANCHOR, VSTR>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH(GATED ? "seg_state_gated" : "seg_state_bf16", st, kern, grid, dim3(G::NT), lds, st,
-               a, k, v, seg);
+               a, k, v, seg, vld);
   return hipGetLastError();
 }
 
-template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0>
+template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
+          bool VSTR = false>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* gl, const float* state, int64_t ss,
                         int64_t sb, float* out, hipStream_t st, float* den = nullptr,
-                        uint16_t* outb = nullptr, int ldo = 0) {
+                        uint16_t* outb = nullptr, int ldo = 0, int vld = 0) {
   using G = Out32Geom<M, DV, GATED>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
   const size_t lds = G::lds_bytes();
-  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM>;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM, VSTR>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH(GATED ? "attn_out_gated" : "attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st,
-               a, q, k, v, state, ss, sb, out, den, outb, ldo);
+               a, q, k, v, state, ss, sb, out, den, outb, ldo, vld);
   return hipGetLastError();
 }
 
@@ -817,9 +834,19 @@ hipError_t launch_attn_out32_den(const AttnShape& s, const uint16_t* phiq, const
 template <int M, int DV>
 hipError_t launch_out_om(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                          const uint16_t* v, const float* state, int64_t ss, int64_t sb,
-                         float* out, uint16_t* outb, int ldo, int rev, hipStream_t st) {
+                         float* out, uint16_t* outb, int ldo, int rev, hipStream_t st,
+                         int vld) {
   const int om = (outb ? 2 : 0) | (rev ? 1 : 0);
   const float* g = nullptr;
+  if (vld) {  // value rows vld apart: the backward's bf16 passes only
+    if (om == 2 && !s.causal)
+      return launch_out_t<M, DV, false, false, false, 2, true>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo, vld);
+    if (om == 2)
+      return launch_out_t<M, DV, true, false, false, 2, true>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo, vld);
+    if (om == 3 && s.causal)
+      return launch_out_t<M, DV, true, false, false, 3, true>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo, vld);
+    return hipErrorInvalidValue;
+  }
   if (!s.causal) {
     if (om != 2) return hipErrorInvalidValue;
     return launch_out_t<M, DV, false, false, false, 2>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo);
@@ -835,12 +862,24 @@ hipError_t launch_out_om(const AttnShape& s, const uint16_t* q, const uint16_t* 
 hipError_t launch_attn_out32_to(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
                                 const uint16_t* v, const float* state, int64_t st_seg,
                                 int64_t st_bh, float* out, uint16_t* outb, int ldo, int rev,
-                                hipStream_t st) {
+                                hipStream_t st, int vld) {
   if (outb ? ldo < s.dv : !out) return hipErrorInvalidValue;
+  if (vld && (vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31))) return hipErrorInvalidValue;
   switch (key32(s)) {
-    case 256128: return launch_out_om<256, 128>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
-    case 128064: return launch_out_om<128, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
-    case 64064: return launch_out_om<64, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st);
+    case 256128: return launch_out_om<256, 128>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
+    case 128064: return launch_out_om<128, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
+    case 64064: return launch_out_om<64, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_seg_state32_v(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
+                                int vld, float* seg, hipStream_t st) {
+  if (vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  switch (key32(s)) {
+    case 256128: return launch_state_t<256, 128, false, false, true>(s, phik, v, nullptr, nullptr, seg, st, vld);
+    case 128064: return launch_state_t<128, 64, false, false, true>(s, phik, v, nullptr, nullptr, seg, st, vld);
+    case 64064: return launch_state_t<64, 64, false, false, true>(s, phik, v, nullptr, nullptr, seg, st, vld);
     default: return hipErrorInvalidValue;
   }
 }

@@ -160,7 +160,11 @@ hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uin
 hipError_t launch_attn_out32_to(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                                 const uint16_t* v, const float* state, int64_t state_seg_stride,
                                 int64_t state_bh_stride, float* out, uint16_t* outb, int ldo,
-                                int rev, hipStream_t st);
+                                int rev, hipStream_t st, int vld = 0);
+// vld != 0 (the backward's bf16 passes): value rows vld elements apart, v at
+// the slice's first column; launch_seg_state32_v is the matching state pass.
+hipError_t launch_seg_state32_v(const AttnShape& a, const uint16_t* phik, const uint16_t* v,
+                                int vld, float* seg, hipStream_t st);
 // The same pass with a.normalize set, writing the unnormalised rows to out
 // and each row's denominator phi_Q,i . z_i (no delta) to den [BH][n].
 hipError_t launch_attn_out32_den(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
