@@ -489,14 +489,17 @@ llops_status_t validate_gated_bwd(const llops_shape_t* s) {
 hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const uint16_t* fq,
                                   const uint16_t* fk, const uint16_t* v, const float* gl,
                                   float* out, float* seg, float* gseg, hipStream_t st,
-                                  const float* S0init = nullptr) {
+                                  const float* S0init = nullptr, int vld = 0, int rev = 0) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   const llops::AttnShape a = attn_shape(&t, true, kGatedBwdWG);
   if (!llops::attn32_supported(a)) return hipErrorInvalidValue;
-  hipError_t e = llops::launch_seg_state32_gated(a, fk, v, gl, gseg, seg, st);
+  hipError_t e = vld ? llops::launch_seg_state32_gated_v(a, fk, v, vld, gl, gseg, seg, false, st)
+                     : llops::launch_seg_state32_gated(a, fk, v, gl, gseg, seg, st);
   if (e == hipSuccess)
     e = llops::launch_seg_scan_gated(a, seg, gseg, S0init, nullptr, nullptr, nullptr, st);
-  if (e == hipSuccess) e = llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
+  if (e == hipSuccess)
+    e = (vld || rev) ? llops::launch_attn_out32_gated_to(a, fq, fk, v, gl, seg, out, rev, vld, st)
+                     : llops::launch_attn_out32_gated(a, fq, fk, v, gl, seg, out, st);
   return e;
 }
 
@@ -1097,19 +1100,32 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   const int64_t perMW = static_cast<int64_t>(MA) * W + MA;
   float *seg2 = f32(L.seg2), *dgb = f32(L.dgb);
   const bool init = S0 || z0;
+  // The passes read their phi slice in place (rows m apart; the reversed
+  // sequence's from the reversed copy of phi_Q) unless phi is too long for a
+  // 32-bit view, and dV is written in the original row order directly.
+  const bool sliced = n * m * 2 < (int64_t{1} << 31);
+  uint16_t *rphq = u16(L.b.rphq), *rphk = u16(L.b.rphk);
+  LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
+  LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
   for (int p0 = 0; p0 < m; p0 += W) {
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
+    if (!sliced)
+      LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     if (init)
       LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
-    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, vp, glf, tmp, seg, gseg, st,
-                                     init ? f32(L.p0) : nullptr),
+    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, sliced ? phk + p0 : vp, glf, tmp, seg, gseg,
+                                     st, init ? f32(L.p0) : nullptr, sliced ? m : 0),
               "attn dphi_q");
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phq, m, p0, W, n, R, 0, 1.f, p0 == 0 ? 1 : 0, dc,
                                        st),
               "rowdot");
     LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
-    LLOPS_HIP(llops::launch_seg_state32_anchored(aMW, a, vp, glf, gseg, seg2, st), "anchored");
+    if (sliced) {
+      LLOPS_HIP(llops::launch_seg_state32_gated_v(aMW, a, phq + p0, m, glf, gseg, seg2, true, st),
+                "anchored");
+    } else {
+      LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
+      LLOPS_HIP(llops::launch_seg_state32_anchored(aMW, a, vp, glf, gseg, seg2, st), "anchored");
+    }
     LLOPS_HIP(llops::launch_seg_rscan_gated(BH, aMW.nseg, perMW, static_cast<int64_t>(MA) * W,
                                             seg2, gseg, st),
               "rscan");
@@ -1123,18 +1139,18 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   // dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j) phi_Q_i over the reversed
   // sequence with its shifted gates; dc_j -= phi_K,j . dphi_K,j
   for (int p0 = 0; p0 < m; p0 += W) {
-    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
-    LLOPS_HIP(gated_attn_on_features(s, MA, W, rb, ra, vp, glr, tmp, seg, gseg, st),
+    if (!sliced)
+      LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
+    LLOPS_HIP(gated_attn_on_features(s, MA, W, rb, ra, sliced ? rphq + p0 : vp, glr, tmp, seg,
+                                     gseg, st, nullptr, sliced ? m : 0),
               "attn dphi_k");
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 1, -1.f, 0, dc, st), "rowdot");
     LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
   }
-  // dV_j = sum_{i>=j} M_ij dnum_i over the reversed sequence
-  uint16_t *rphq = u16(L.b.rphq), *rphk = u16(L.b.rphk);
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
-  LLOPS_HIP(gated_attn_on_features(s, m, dv, rphk, rphq, dn, glr, tmp, seg, gseg, st), "attn dv");
-  LLOPS_HIP(llops::launch_rows_copy_f32(tmp, dv, 0, dV, dv, 0, dv, n, R, 1, st), "rows");
+  // dV_j = sum_{i>=j} M_ij dnum_i over the reversed sequence, rows written back
+  // in the original order
+  LLOPS_HIP(gated_attn_on_features(s, m, dv, rphk, rphq, dn, glr, dV, seg, gseg, st, nullptr, 0, 1),
+            "attn dv");
   // dlog_gate_l = sum_{i>=l} dc_i, anchored at the exact segment-start values
   LLOPS_HIP(llops::launch_seg_bridge_dg(dc, BH, n, aMW.seg_len, aMW.nseg, dgb, dlog_gate, st),
             "bridge");

@@ -927,6 +927,47 @@ hipError_t launch_attn_out32_gated(const AttnShape& s, const uint16_t* phiq, con
   }
 }
 
+hipError_t launch_seg_state32_gated_v(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
+                                      int vld, const float* gl, float* gseg, float* seg,
+                                      bool anchored, hipStream_t st) {
+  if (vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  switch (key32(s) * 2 + (anchored ? 1 : 0)) {
+    case 256128 * 2: return launch_state_t<256, 128, true, false, true>(s, phik, v, gl, gseg, seg, st, vld);
+    case 256128 * 2 + 1: return launch_state_t<256, 128, true, true, true>(s, phik, v, gl, gseg, seg, st, vld);
+    case 128064 * 2: return launch_state_t<128, 64, true, false, true>(s, phik, v, gl, gseg, seg, st, vld);
+    case 128064 * 2 + 1: return launch_state_t<128, 64, true, true, true>(s, phik, v, gl, gseg, seg, st, vld);
+    case 64064 * 2: return launch_state_t<64, 64, true, false, true>(s, phik, v, gl, gseg, seg, st, vld);
+    case 64064 * 2 + 1: return launch_state_t<64, 64, true, true, true>(s, phik, v, gl, gseg, seg, st, vld);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int M, int DV>
+hipError_t launch_out_gated_to(const AttnShape& s, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, const float* gl, const float* state,
+                               float* out, int rev, int vld, hipStream_t st) {
+  const int64_t per = static_cast<int64_t>(M) * DV + M;
+  if (vld && !rev)
+    return launch_out_t<M, DV, true, true, false, 0, true>(s, q, k, v, gl, state, per, per * s.nseg, out, st, nullptr, nullptr, 0, vld);
+  if (rev && !vld)
+    return launch_out_t<M, DV, true, true, false, 1>(s, q, k, v, gl, state, per, per * s.nseg, out, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_out32_gated_to(const AttnShape& s, const uint16_t* phiq,
+                                      const uint16_t* phik, const uint16_t* v, const float* gl,
+                                      const float* state, float* out, int rev, int vld,
+                                      hipStream_t st) {
+  if (!s.causal) return hipErrorInvalidValue;
+  if (vld && (vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31))) return hipErrorInvalidValue;
+  switch (key32(s)) {
+    case 256128: return launch_out_gated_to<256, 128>(s, phiq, phik, v, gl, state, out, rev, vld, st);
+    case 128064: return launch_out_gated_to<128, 64>(s, phiq, phik, v, gl, state, out, rev, vld, st);
+    case 64064: return launch_out_gated_to<64, 64>(s, phiq, phik, v, gl, state, out, rev, vld, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_attn_out32_gated_den(const AttnShape& s, const uint16_t* phiq,
                                        const uint16_t* phik, const uint16_t* v, const float* gl,
                                        const float* state, float* out, float* den,

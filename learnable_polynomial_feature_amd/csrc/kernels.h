@@ -182,6 +182,15 @@ hipError_t launch_seg_state32_gated(const AttnShape& a, const uint16_t* phik, co
 hipError_t launch_attn_out32_gated(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                                    const uint16_t* v, const float* gl, const float* state,
                                    float* out, hipStream_t st);
+// Gated backward passes: value rows vld apart (vld != 0; anchored: the
+// start-anchored state pass), or (output) rows written in reversed order.
+hipError_t launch_seg_state32_gated_v(const AttnShape& a, const uint16_t* phik, const uint16_t* v,
+                                      int vld, const float* gl, float* gseg, float* seg,
+                                      bool anchored, hipStream_t st);
+hipError_t launch_attn_out32_gated_to(const AttnShape& a, const uint16_t* phiq,
+                                      const uint16_t* phik, const uint16_t* v, const float* gl,
+                                      const float* state, float* out, int rev, int vld,
+                                      hipStream_t st);
 hipError_t launch_attn_out32_gated_den(const AttnShape& a, const uint16_t* phiq,
                                        const uint16_t* phik, const uint16_t* v, const float* gl,
                                        const float* state, float* out, float* den,
