@@ -1115,10 +1115,10 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
     LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, sliced ? phk + p0 : vp, glf, tmp, seg, gseg,
                                      st, init ? f32(L.p0) : nullptr, sliced ? m : 0),
               "attn dphi_q");
+    // dc_i += phi_Q,i . dphi_Q,i, and the slice of dphi_Q stored as bf16
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phq, m, p0, W, n, R, 0, 1.f, p0 == 0 ? 1 : 0, dc,
-                                       st),
+                                       st, dphq),
               "rowdot");
-    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
     if (sliced) {
       LLOPS_HIP(llops::launch_seg_state32_gated_v(aMW, a, phq + p0, m, glf, gseg, seg2, true, st),
                 "anchored");
@@ -1144,8 +1144,8 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
     LLOPS_HIP(gated_attn_on_features(s, MA, W, rb, ra, sliced ? rphq + p0 : vp, glr, tmp, seg,
                                      gseg, st, nullptr, sliced ? m : 0),
               "attn dphi_k");
-    LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 1, -1.f, 0, dc, st), "rowdot");
-    LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 1, -1.f, 0, dc, st, dphk),
+              "rowdot");
   }
   // dV_j = sum_{i>=j} M_ij dnum_i over the reversed sequence, rows written back
   // in the original order

@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256) void rowdot_acc(const float* __restrict__ x, i
                                                   const uint16_t* __restrict__ phi, int pw,
                                                   int poff, int width, int64_t n, int64_t rows,
                                                   int rev, float sign, int init,
-                                                  float* __restrict__ acc) {
+                                                  float* __restrict__ acc,
+                                                  uint16_t* __restrict__ out) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int l = threadIdx.x & 31;
   const bool live = r < rows;  // every lane joins the shuffles below
@@ -215,6 +216,12 @@ __global__ __launch_bounds__(256) void rowdot_acc(const float* __restrict__ x, i
           __uint_as_float(xv[1]) * __uint_as_float(pv[0] & 0xFFFF0000u) +
           __uint_as_float(xv[2]) * __uint_as_float(pv[1] << 16) +
           __uint_as_float(xv[3]) * __uint_as_float(pv[1] & 0xFFFF0000u);
+    // out: the x row rounded to bf16 (RNE) at phi's place, where the
+    // gradient dphi is kept
+    if (out && live)
+      *reinterpret_cast<u32x2*>(out + rr * pw + poff + c0) =
+          u32x2{pack_bf16x2(__uint_as_float(xv[0]), __uint_as_float(xv[1])),
+                pack_bf16x2(__uint_as_float(xv[2]), __uint_as_float(xv[3]))};
   }
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
@@ -459,13 +466,13 @@ hipError_t launch_fill_ones_bf16(uint16_t* dst, int64_t count, hipStream_t st) {
 
 hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw, int poff,
                              int width, int64_t n, int64_t rows, int rev, float sign, int init,
-                             float* acc, hipStream_t st) {
+                             float* acc, hipStream_t st, uint16_t* out) {
   if (rows == 0) return hipSuccess;
   if ((rows + 7) / 8 > 0x7fffffffLL || width > 128 || width % 4 || xw % 4 || (pw % 2) ||
       (poff % 4) || poff + width > pw || width > xw)
     return hipErrorInvalidValue;
   LLOPS_LAUNCH("gated_bwd_rowdot", st, rowdot_acc, dim3(static_cast<unsigned>((rows + 7) / 8)),
-               dim3(256), 0, st, x, xw, phi, pw, poff, width, n, rows, rev, sign, init, acc);
+               dim3(256), 0, st, x, xw, phi, pw, poff, width, n, rows, rev, sign, init, acc, out);
   return hipGetLastError();
 }
 

@@ -102,7 +102,8 @@ hipError_t launch_gate_reverse_shift(const float* g, int64_t n, int64_t rows, fl
 hipError_t launch_fill_ones_bf16(uint16_t* dst, int64_t count, hipStream_t st);
 hipError_t launch_rowdot_acc(const float* x, int xw, const uint16_t* phi, int pw, int poff,
                              int width, int64_t n, int64_t rows, int rev, float sign, int init,
-                             float* acc, hipStream_t st);
+                             float* acc, hipStream_t st, uint16_t* out = nullptr);
+// (out: also stores the x rows as bf16, RNE, at phi's rows and columns)
 // Exact gate gradient at segment starts: segment sums anchored at the start
 // (launch_seg_state32_anchored), their reverse scan into suffix states, the inner products with the forward pass's prefix
 // states, and the bridged per-segment suffix sums of the per-token terms.
