@@ -670,11 +670,20 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         const int64_t d0 = bh * a.n + ((OM & 1) ? a.n - 1 - tb : tb);
         constexpr int sgn = (OM & 1) ? -1 : 1;
         if constexpr ((OM & 2) != 0) {
-          uint16_t* ob = outb + d0 * ldo + dvt * 32 + c32;
+          // lanes c32 and c32 ^ 1 hold the same rows of adjacent columns: a
+          // DPP swap gives the even lane rows e, the odd lane rows e + 1 as
+          // bf16 pairs (half the stores)
+          uint32_t* ob = reinterpret_cast<uint32_t*>(outb + d0 * ldo + dvt * 32 + (c32 & ~1));
+          const bool odd = (c32 & 1) != 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * ((kept + e) >> 2) + (e & 3);
-            if (tb + r < t1) ob[sgn * r * ldo] = f32_to_bf16(val[e]);
+          for (int e = 0; e < 8; e += 2) {
+            const float send = odd ? val[e] : val[e + 1];
+            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(
+                __float_as_int(send), 0xB1, 0xF, 0xF, false));  // quad_perm [1, 0, 3, 2]
+            const int ee = odd ? e + 1 : e;
+            const int r = 8 * ((kept + ee) >> 2) + (ee & 3);
+            if (tb + r < t1)
+              ob[sgn * r * (ldo / 2)] = odd ? pack_bf16x2(recv, val[e + 1]) : pack_bf16x2(val[e], recv);
           }
         } else {
           float* ob = out + d0 * DV + dvt * 32 + c32;
