@@ -363,6 +363,50 @@ def causal_backward(steps, torch, lib):
     return res
 
 
+def linattn_backward(steps, torch, lib):
+    """The non-causal attention's full backward (llops_linattn_bwd: feature
+    maps, the attention chain rule as non-causal passes, the feature-map
+    backward of both sides) at the long workload's geometry: 1 x 32 x 65536, d = dv =
+    128, m = 256, p = 2, t = 4, squared, normalised. Synthetic bf16 inputs and
+    an fp32 N(0,1) upstream gradient."""
+    g = torch.Generator(device="cpu").manual_seed(13)
+    B, H, n, d, dv, m, p, t = 1, 32, 65536, 128, 128, 256, 2, 4
+    mk = lambda *shape, scale=1.0: (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16).to("cuda")
+    Q, K = mk(B, H, n, d, scale=d ** -0.5), mk(B, H, n, d, scale=d ** -0.5)
+    V = mk(B, H, n, dv)
+    tq, tk = mk(H, p, t, d, m, scale=d ** -0.5), mk(H, p, t, d, m, scale=d ** -0.5)
+    dO = torch.randn(B, H, n, dv, generator=g).to("cuda")
+    shape = lib.make_shape(batch=B, heads=H, n=n, d=d, dv=dv, m=m, p=p, t=t, square=True,
+                           normalize=True, delta=1e-6)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_LINATTN_BWD), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        return lib.llops_linattn_bwd(Q, K, V, tq, tk, dO, square=True, normalize=True,
+                                     delta=1e-6, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    timer = lib.KernelTimer(capacity=64 * steps)
+    with timer:
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    kern = {k: sum(v) / steps for k, v in timer.durations_ms().items()}  # ms per call
+    res = {"workload": f"non-causal attention backward {B}x{H}x{n} d={d} dv={dv} m={m} p={p} t={t} "
+                       "squared, normalised; bf16 in, fp32 dO and gradients",
+           "ms_per_call": round(ms, 3), "tokens_per_s": round(B * n / (ms * 1e-3), 1),
+           "workspace_GiB": round(ws.numel() / 2 ** 30, 2),
+           "kernel_ms_per_call": {k: round(v, 3) for k, v in sorted(kern.items(), key=lambda kv: -kv[1])}}
+    del Q, K, V, tq, tk, dO, ws
+    return res
+
+
 def gated_backward(steps, torch, lib):
     """The gated causal attention's full backward (llops_linattn_gated_causal_bwd,
     with the log-gate gradient) at the long workload's geometry: 1 x 32 x 65536,
@@ -688,6 +732,8 @@ def main():
         line["causal_backward"] = causal_backward(3, torch, lib)
         log("gated causal attention backward")
         line["gated_backward"] = gated_backward(3, torch, lib)
+        log("non-causal attention backward")
+        line["linattn_backward"] = linattn_backward(3, torch, lib)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
