@@ -407,6 +407,51 @@ def linattn_backward(steps, torch, lib):
     return res
 
 
+def state_backward(steps, torch, lib):
+    """Both causal backwards continued from an initial state
+    (llops_linattn_causal_bwd_state, llops_linattn_gated_causal_bwd_state,
+    which also return dS0 and dz0) at the long workload's geometry: 1 x 32 x
+    65536, d = dv = 128, m = 256, p = 2, t = 4, squared, normalised; S0 ~
+    0.01 N(0,1), z0 = |0.01 N(0,1)|; gated: log gates log(sigmoid(N(4, 1)))."""
+    g = torch.Generator(device="cpu").manual_seed(14)
+    B, H, n, d, dv, m, p, t = 1, 32, 65536, 128, 128, 256, 2, 4
+    mk = lambda *shape, scale=1.0: (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16).to("cuda")
+    Q, K = mk(B, H, n, d, scale=d ** -0.5), mk(B, H, n, d, scale=d ** -0.5)
+    V = mk(B, H, n, dv)
+    tq, tk = mk(H, p, t, d, m, scale=d ** -0.5), mk(H, p, t, d, m, scale=d ** -0.5)
+    dO = torch.randn(B, H, n, dv, generator=g).to("cuda")
+    S0 = (0.01 * torch.randn(B, H, m, dv, generator=g)).to("cuda")
+    z0 = (0.01 * torch.randn(B, H, m, generator=g)).abs().to("cuda")
+    lg = torch.nn.functional.logsigmoid(torch.randn(B, H, n, generator=g) + 4.0).to("cuda")
+    shape = lib.make_shape(batch=B, heads=H, n=n, d=d, dv=dv, m=m, p=p, t=t, square=True,
+                           normalize=True, delta=1e-6)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_GATED_CAUSAL_BWD), dtype=torch.uint8,
+                     device="cuda")
+    calls = {
+        "causal": lambda: lib.llops_linattn_causal_bwd_state(
+            Q, K, V, tq, tk, dO, S0=S0, z0=z0, square=True, normalize=True, delta=1e-6,
+            workspace=ws),
+        "gated": lambda: lib.llops_linattn_gated_causal_bwd_state(
+            Q, K, V, tq, tk, lg, dO, S0=S0, z0=z0, square=True, normalize=True, delta=1e-6,
+            workspace=ws),
+    }
+    res = {"workload": f"causal and gated causal attention backward from an initial state {B}x{H}x{n} "
+                       f"d={d} dv={dv} m={m} p={p} t={t} squared, normalised; bf16 in, fp32 dO, "
+                       "S0, z0 and gradients (incl. dS0, dz0)"}
+    for name, call in calls.items():
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        res[name] = {"ms_per_call": round(ms, 3), "tokens_per_s": round(B * n / (ms * 1e-3), 1)}
+    del Q, K, V, tq, tk, dO, S0, z0, lg, ws
+    return res
+
+
 def gated_backward(steps, torch, lib):
     """The gated causal attention's full backward (llops_linattn_gated_causal_bwd,
     with the log-gate gradient) at the long workload's geometry: 1 x 32 x 65536,
@@ -734,6 +779,8 @@ def main():
         line["gated_backward"] = gated_backward(3, torch, lib)
         log("non-causal attention backward")
         line["linattn_backward"] = linattn_backward(3, torch, lib)
+        log("attention backward from an initial state")
+        line["state_backward"] = state_backward(3, torch, lib)
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
