@@ -67,13 +67,32 @@ def featmap_flops(w, n_rows):
     return 2.0 * n_rows * w.d * w.p * w.t * w.m
 
 
+# (m, dv) shapes of the 32x32x16 segment kernels, which walk 32-token chunks
+# whatever chunk length is asked for (the chunk only orders the rounding)
+_SEG32 = {(256, 128), (128, 64), (64, 64)}
+
+
+def kernel_chunk(w):
+    """Tokens per intra-chunk block the causal kernels actually run: 32 on
+    the 32x32x16 segment kernels; the generic bf16 kernels take 32 when a
+    chunk of at most 32 is asked for, else 64; the fp32 kernels take the
+    requested chunk (64 by default)."""
+    if w.dtype == "bf16":
+        if (w.m, w.dv) in _SEG32:
+            return 32
+        return 32 if 0 < w.chunk <= 32 else 64
+    return w.chunk if w.chunk > 0 else 64
+
+
 def causal_flops(w):
     """Feature maps of Q and K, state build phi_K^T V and read-out phi_Q S, and
-    the lower triangle (diagonal included) of the intra-chunk products, with
-    the workload's chunk length; normaliser and epilogue terms excluded."""
+    the lower triangle (diagonal included) of the intra-chunk products at the
+    chunk length the kernels run (kernel_chunk); normaliser and epilogue terms
+    excluded."""
     bh = w.batch * w.heads
+    C = kernel_chunk(w)
     per_bh = (4.0 * w.n * w.d * w.p * w.t * w.m + 4.0 * w.n * w.m * w.dv
-              + w.n * (w.chunk + 1) * (w.m + w.dv))
+              + w.n * (C + 1) * (w.m + w.dv))
     return bh * per_bh
 
 
@@ -542,6 +561,12 @@ def bench_decode(w, steps, torch, lib):
     q = to_dev(tok["q"], torch, torch.bfloat16)
     k = to_dev(tok["k"], torch, torch.bfloat16)
     v = to_dev(tok["v"], torch, torch.bfloat16)
+    # the tokens of a few slices spread over the batch rows and heads, for
+    # the oracle's CPU baseline
+    sample = [(b, h, tok["q"][:, b, h].copy(), tok["k"][:, b, h].copy(), tok["v"][:, b, h].copy())
+              for b, h in ((0, 0), (45, 2), (90, 11), (127, 15), (18, 5), (63, 17), (108, 1),
+                           (36, 13), (81, 26), (9, 31), (117, 30), (54, 29))
+              if b < B and h < H]
     del tok
     out = torch.empty((B, H, dv), dtype=torch.float32, device="cuda")
     shape = lib.make_shape(batch=B, heads=H, n=1, d=w.d, dv=dv, m=m, p=w.p, t=w.t,
@@ -622,36 +647,87 @@ def bench_decode(w, steps, torch, lib):
              "tokens_per_s": round(B / (gms * 1e-3), 1),
              "GBps": round(decode_bytes(w) / (gms * 1e-3) / 1e9, 1),
              "kernel_ms": {kk: round(vv, 4) for kk, vv in gkern.items()}}
-    return ms, kern, gated
+    return ms, kern, gated, sample
 
 
-def cpu_baseline(w, budget_s):
-    """The fp64 oracle, as it stands, on whole heads of the same workload."""
-    import numpy as np  # noqa: F401
-    from oracle import llops_oracle as O
-    from learnable_polynomial_feature_amd.workloads import qk_slice, theta_head, v_slice
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, budget_s, min_s=0.5):
+    """The fp64 oracle, as it stands, on whole (batch, head) sequences of the
+    workload: causal_chunked at the workload's chunk, or linattn for the
+    non-causal one. Slices run in order until about budget_s of oracle time
+    (at least one; all of them, repeated to at least min_s, when they fit),
+    and the full call's time is extrapolated from the slices done. Input
+    generation is not timed."""
+    from oracle import llops_oracle as O
+    from learnable_polynomial_feature_amd.workloads import generate
+    slices = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
     done, elapsed = 0, 0.0
-    while done < w.heads and (elapsed < budget_s * 0.5 or done == 0):
-        h = done
-        q, k, v = qk_slice(w, "q", 0, h), qk_slice(w, "k", 0, h), v_slice(w, 0, h)
-        tq, tk = theta_head(w, "q", h), theta_head(w, "k", h)
+    cache = {}
+    while (done < len(slices) and (elapsed < budget_s or done == 0)) or \
+            (done % len(slices) == 0 and elapsed < min_s):
+        b, h = slices[done % len(slices)]
+        if (b, h) not in cache:
+            x = generate(w, heads=[h], batches=[b])
+            args = (x["Q"][0, 0], x["K"][0, 0], x["V"][0, 0], x["theta_q"][0], x["theta_k"][0])
+            if len(slices) <= 64:  # small workloads: keep the inputs for repeated passes
+                cache[(b, h)] = args
+        else:
+            args = cache[(b, h)]
         t = time.perf_counter()
-        O.causal_chunked(q, k, v, tq, tk, square=w.square, normalize=w.normalize, delta=w.delta,
-                         chunk=w.chunk)
+        if w.causal:
+            O.causal_chunked(*args, chunk=w.chunk, **kw)
+        else:
+            O.linattn(*args, **kw)
         elapsed += time.perf_counter() - t
         done += 1
-    per_head = elapsed / done
-    full_step = per_head * w.batch * w.heads
-    return {"value": w.batch * w.n / full_step, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {w.batch * w.heads} (batch, head) sequences at full length "
-                      f"({w.n} tokens each), fp64 numpy oracle, {elapsed:.1f} s; full-step time "
-                      f"extrapolated x{w.batch * w.heads}/{done}"}
+    full_call = elapsed / done * len(slices)
+    if done >= len(slices):
+        what = (f"all {len(slices)} (batch, head) sequences, {done // len(slices)} pass(es), "
+                f"{elapsed:.2f} s")
+    else:
+        what = (f"{done} of {len(slices)} (batch, head) sequences at full length ({w.n} tokens "
+                f"each), {elapsed:.1f} s; full call extrapolated x{len(slices)}/{done}")
+    return {"value": round(w.batch * w.n / full_call, 1), "unit": "tokens/s",
+            "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{w.name}: {what}; fp64 numpy oracle"}
+
+
+def cpu_baseline_decode(w, sample, budget_s):
+    """The fp64 oracle's decode (every step of the run, token by token) on
+    (batch, head) slices of the decode workload, from the oracle's own
+    prefix state (built untimed), until about budget_s; the full step's time
+    is extrapolated to all batch x heads slices. sample: [(b, h, q, k, v)]
+    with the slice's per-step tokens [steps, d|dv] as the GPU ran them."""
+    from oracle import llops_oracle as O
+    from learnable_polynomial_feature_amd.workloads import decode_prefix, theta_head
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta)
+    done, elapsed, steps = 0, 0.0, 0
+    for b, h, q, k, v in sample:
+        if done and elapsed >= budget_s:
+            break
+        pre = decode_prefix(w, heads=[h], batches=[b])
+        tq, tk = theta_head(w, "q", h), theta_head(w, "k", h)
+        S0, z0 = O.state_from_prefix(pre["K_pre"][0, 0], pre["V_pre"][0, 0], tk,
+                                     square=w.square)
+        t = time.perf_counter()
+        O.decode(S0, z0, q, k, v, tq, tk, **kw)
+        elapsed += time.perf_counter() - t
+        done += 1
+        steps = len(q)
+    per_step = elapsed / done / steps * w.batch * w.heads  # one step of every slice
+    return {"value": round(w.batch / per_step, 1), "unit": "tokens/s",
+            "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{w.name}: {done} of {w.batch * w.heads} (batch, head) slices x {steps} "
+                      f"steps, {elapsed:.1f} s; full step extrapolated "
+                      f"x{w.batch * w.heads}/{done}; fp64 numpy oracle"}
 
 
 def copy_probe(torch, nbytes=1 << 30, reps=3):
@@ -736,12 +812,18 @@ def main():
                    "parallelism": "single-gpu"},
         "mfma_frac_step": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_tflop_per_step": round(flops / 1e12, 4),
+        # the whole step (every kernel of one call) against the same peak; the
+        # intra-chunk triangle is counted at the 32-token chunk the kernels run
+        "step_roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "flops_per_step": flops, "intra_chunk_tokens": kernel_chunk(w)},
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
         "roofline": roofline,
     }
     if not args.no_decode:
         wd = WORKLOADS["decode_b128_h32"]
-        dms, dkern, dgated = bench_decode(wd, args.decode_steps, torch, lib)
+        dms, dkern, dgated, dsample = bench_decode(wd, args.decode_steps, torch, lib)
         graph_ms = dgated.pop("graph_ms_per_step")
         gb = decode_bytes(wd) / (dms * 1e-3) / 1e9
         st_ms = dkern.get("decode_state")
@@ -782,8 +864,16 @@ def main():
         log("attention backward from an initial state")
         line["state_backward"] = state_backward(3, torch, lib)
     if not args.no_cpu_baseline:
+        # the oracle timed on this host beside every workload's GPU figure
         log("cpu baseline (fp64 oracle)")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds * 0.5)
+        if "configs" in line:
+            for name in line["configs"]:
+                line["configs"][name]["cpu_baseline"] = cpu_baseline(WORKLOADS[name],
+                                                                     args.cpu_seconds / 8)
+        if "decode" in line:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(
+                WORKLOADS["decode_b128_h32"], dsample, args.cpu_seconds / 3)
     print(json.dumps(line), flush=True)
 
 

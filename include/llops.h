@@ -108,6 +108,14 @@ size_t llops_workspace_bytes(const llops_shape_t* shape, int32_t entry);
  * LLOPS_ENTRY_FEATMAP) bytes of device scratch (a repacked copy of Theta for
  * the bf16 shapes that have an unrolled kernel and more than 1024 rows per
  * head; 0 bytes otherwise, and ws may then be null).
+ * Why a workspace here, where the plain definition needs only X, Theta and
+ * phi: the 256-row-tile kernels stream Theta through LDS one (32-feature
+ * block, rank) stage at a time, and a stage is one contiguous p*d*64-byte
+ * block only in a fragment-order copy of Theta, written by a separate launch
+ * (15 us for both Theta sets at 1 x 32 heads x 65536 rows, d = 128, m = 256,
+ * p = 2, t = 4: 0.7% of the feature map). The library allocates nothing, so
+ * that copy lives in caller memory. Up to 1024 rows per head the few-row
+ * kernels read Theta in place and need no workspace.
  */
 llops_status_t llops_featmap(const llops_shape_t* shape, const void* X,
                              const void* theta, void* phi, void* ws, size_t ws_bytes,

@@ -115,12 +115,65 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+# Argument checks run in two passes. The first looks only at metadata
+# (types, shapes, dtypes, contiguity of buffers written in place, agreement
+# between tensors); the second (_on_device) then requires every tensor on one
+# GPU. Nothing reaches the library before both pass, so a mismatched buffer
+# can never become an out-of-bounds access on the device.
+def _t(t, name: str) -> torch.Tensor:
+    """An input tensor (made contiguous; inputs may be copied)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
     return t.contiguous()
+
+
+def _opt_t(t, name: str):
+    return None if t is None else _t(t, name)
+
+
+def _want(t, name: str, shape, dtype=None):
+    """An input's shape (and dtype) as the call requires."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _out(t, name: str, shape, dtype) -> torch.Tensor:
+    """A caller-supplied buffer the library writes in place: it must already
+    have the shape and dtype and be contiguous (a copy cannot stand in)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    _want(t, name, shape, dtype)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} is written in place and must be contiguous")
+    return t
+
+
+def _ws_arg(ws):
+    """A caller-supplied workspace: any dtype, contiguous (its byte size is
+    checked by the library against llops_workspace_bytes)."""
+    if ws is None:
+        return None
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws
+
+
+def _on_device(**tensors):
+    """Every tensor handed to the library lives on one and the same GPU."""
+    first = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if first is None:
+            first = t.device
+        elif t.device != first:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {first}")
 
 
 def _stream(t: torch.Tensor):
@@ -140,6 +193,19 @@ def _theta_dims(theta: torch.Tensor, heads: int):
     if theta.dim() == 4:
         return tuple(theta.shape), 0
     raise ValueError("theta must be [heads, p, t, d, m] or [p, t, d, m]")
+
+
+def _two_thetas(theta_q, theta_k, heads: int, d: int):
+    """(p, t, m, theta_per_head) of a Theta_q / Theta_k pair of one shape and
+    head layout whose d matches the inputs'."""
+    dq, ph = _theta_dims(theta_q, heads)
+    dk, phk = _theta_dims(theta_k, heads)
+    if dq != dk or ph != phk:
+        raise ValueError("theta_q and theta_k must have the same shape")
+    p, t, td, m = dq
+    if td != d:
+        raise ValueError(f"theta's d ({td}) must match the inputs' d ({d})")
+    return p, t, m, ph
 
 
 def make_shape(*, batch, heads, n, d, dv, m, p, t, square=False, normalize=False, delta=0.0,
@@ -162,19 +228,25 @@ def _workspace(shape: Shape, entry: int, device, ws):
 # ---------------------------------------------------------------------------
 def llops_featmap(X, theta, *, square=False, out=None, out_dtype=torch.float32, workspace=None):
     """phi = sum_r prod_j X Theta_{j,r} [squared]; X [B, H, n, d] -> phi [B, H, n, m]."""
-    X = _dev(X, "X")
-    theta = _dev(theta, "theta")
+    X, theta = _t(X, "X"), _t(theta, "theta")
     if X.dim() != 4:
         raise ValueError("X must be [batch, heads, n, d]")
     B, H, n, d = X.shape
     (p, t, td, m), per_head = _theta_dims(theta, H)
     if td != d or theta.dtype != X.dtype:
         raise ValueError("theta's d and dtype must match X")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    idt = _dt(X)
+    if out is not None:
+        _out(out, "out", (B, H, n, m), out_dtype)
+    workspace = _ws_arg(workspace)
+    _on_device(X=X, theta=theta, out=out, workspace=workspace)
     odt = BF16 if out_dtype == torch.bfloat16 else F32
     if out is None:
         out = torch.empty((B, H, n, m), dtype=out_dtype, device=X.device)
     shape = make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=square,
-                       theta_per_head=per_head, in_dtype=_dt(X), out_dtype=odt)
+                       theta_per_head=per_head, in_dtype=idt, out_dtype=odt)
     lib = library()
     ws, wsb = _workspace(shape, ENTRY_FEATMAP, X.device, workspace)
     _check(lib.llops_featmap(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(out), _ptr(ws), wsb,
@@ -188,26 +260,27 @@ def llops_featmap_bwd(X, theta, dphi, *, square=False, dX=None, dtheta=None, wor
     X [B, H, n, d] and theta bf16; dphi [B, H, n, m] fp32 or bf16; dX fp32 like
     X, dtheta fp32 like theta (summed over heads when theta is shared).
     """
-    X = _dev(X, "X")
-    theta = _dev(theta, "theta")
-    dphi = _dev(dphi, "dphi")
+    X, theta, dphi = _t(X, "X"), _t(theta, "theta"), _t(dphi, "dphi")
     if X.dim() != 4:
         raise ValueError("X must be [batch, heads, n, d]")
     B, H, n, d = X.shape
     (p, t, td, m), per_head = _theta_dims(theta, H)
     if td != d or theta.dtype != X.dtype:
         raise ValueError("theta's d and dtype must match X")
-    if tuple(dphi.shape) != (B, H, n, m):
-        raise ValueError(f"dphi must be [{B}, {H}, {n}, {m}]")
+    _want(dphi, "dphi", (B, H, n, m))
+    idt, gdt = _dt(X), _dt(dphi)
+    if dX is not None:
+        _out(dX, "dX", (B, H, n, d), torch.float32)
+    if dtheta is not None:
+        _out(dtheta, "dtheta", tuple(theta.shape), torch.float32)
+    workspace = _ws_arg(workspace)
+    _on_device(X=X, theta=theta, dphi=dphi, dX=dX, dtheta=dtheta, workspace=workspace)
     if dX is None:
         dX = torch.empty((B, H, n, d), dtype=torch.float32, device=X.device)
     if dtheta is None:
         dtheta = torch.empty(theta.shape, dtype=torch.float32, device=X.device)
-    for name, o, want in (("dX", dX, (B, H, n, d)), ("dtheta", dtheta, tuple(theta.shape))):
-        if o.dtype != torch.float32 or tuple(o.shape) != want or not o.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {want}")
     shape = make_shape(batch=B, heads=H, n=n, d=d, dv=1, m=m, p=p, t=t, square=square,
-                       theta_per_head=per_head, in_dtype=_dt(X), out_dtype=_dt(dphi))
+                       theta_per_head=per_head, in_dtype=idt, out_dtype=gdt)
     lib = library()
     ws, wsb = _workspace(shape, ENTRY_FEATMAP_BWD, X.device, workspace)
     _check(lib.llops_featmap_bwd(ctypes.byref(shape), _ptr(X), _ptr(theta), _ptr(dphi), _ptr(dX),
@@ -219,13 +292,7 @@ def _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk):
     if Q.dim() != 4 or K.shape != Q.shape or V.dim() != 4 or V.shape[:3] != Q.shape[:3]:
         raise ValueError("Q, K must be [B, H, n, d] and V [B, H, n, dv]")
     B, H, n, d = Q.shape
-    dq, ph = _theta_dims(theta_q, H)
-    dk, phk = _theta_dims(theta_k, H)
-    if dq != dk or ph != phk:
-        raise ValueError("theta_q and theta_k must have the same shape")
-    p, t, td, m = dq
-    if td != d:
-        raise ValueError("theta's d must match Q")
+    p, t, m, ph = _two_thetas(theta_q, theta_k, H, d)
     dts = {x.dtype for x in (Q, K, V, theta_q, theta_k)}
     if len(dts) != 1:
         raise ValueError("Q, K, V and theta must share one dtype")
@@ -234,12 +301,28 @@ def _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk):
                       in_dtype=_dt(Q), out_dtype=F32)
 
 
+def _attn_inputs(Q, K, V, theta_q, theta_k):
+    return (_t(Q, "Q"), _t(K, "K"), _t(V, "V"), _t(theta_q, "theta_q"), _t(theta_k, "theta_k"))
+
+
+def _state_inputs(S0, z0, B, H, m, dv):
+    S0, z0 = _opt_t(S0, "S0"), _opt_t(z0, "z0")
+    if S0 is not None:
+        _want(S0, "S0", (B, H, m, dv), torch.float32)
+    if z0 is not None:
+        _want(z0, "z0", (B, H, m), torch.float32)
+    return S0, z0
+
+
 def llops_linattn_fwd(Q, K, V, theta_q, theta_k, *, square=False, normalize=False, delta=0.0,
                       out=None, workspace=None):
     """Non-causal: out = phi_Q (phi_K^T V) [/ (phi_Q (phi_K^T 1) + delta)] (fp32)."""
-    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    Q, K, V, theta_q, theta_k = _attn_inputs(Q, K, V, theta_q, theta_k)
     shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
+    if out is not None:
+        _out(out, "out", tuple(V.shape), torch.float32)
+    workspace = _ws_arg(workspace)
+    _on_device(Q=Q, K=K, V=V, theta_q=theta_q, theta_k=theta_k, out=out, workspace=workspace)
     if out is None:
         out = torch.empty(V.shape, dtype=torch.float32, device=Q.device)
     ws, wsb = _workspace(shape, ENTRY_LINATTN, Q.device, workspace)
@@ -267,29 +350,31 @@ def llops_linattn_gated_causal_fwd(Q, K, V, theta_q, theta_k, log_gate, *, squar
 
     log_gate: fp32 [B, H, n]. Returns as llops_linattn_causal_fwd.
     """
+    if log_gate is None:
+        raise ValueError("log_gate is required")
     return _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk, S0, z0,
                    out, S_final, z_final, return_state, workspace)
 
 
 def _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk, S0, z0, out,
             S_final, z_final, return_state, workspace):
-    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+    Q, K, V, theta_q, theta_k = _attn_inputs(Q, K, V, theta_q, theta_k)
     shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, chunk)
     B, H = Q.shape[:2]
     m, dv = shape.m, shape.dv
-    if S0 is not None:
-        S0 = _dev(S0, "S0")
-        if S0.shape != (B, H, m, dv) or S0.dtype != torch.float32:
-            raise ValueError("S0 must be fp32 [B, H, m, dv]")
-    if z0 is not None:
-        z0 = _dev(z0, "z0")
-        if z0.shape != (B, H, m) or z0.dtype != torch.float32:
-            raise ValueError("z0 must be fp32 [B, H, m]")
-    for name, tt, shp in (("S_final", S_final, (B, H, m, dv)), ("z_final", z_final, (B, H, m))):
-        if tt is not None and (tt.shape != shp or tt.dtype != torch.float32
-                               or not tt.is_contiguous() or tt.device.type != "cuda"):
-            raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape {shp}")
+    S0, z0 = _state_inputs(S0, z0, B, H, m, dv)
+    if S_final is not None:
+        _out(S_final, "S_final", (B, H, m, dv), torch.float32)
+    if z_final is not None:
+        _out(z_final, "z_final", (B, H, m), torch.float32)
+    if out is not None:
+        _out(out, "out", tuple(V.shape), torch.float32)
+    if log_gate is not None:
+        log_gate = _t(log_gate, "log_gate")
+        _want(log_gate, "log_gate", tuple(Q.shape[:3]), torch.float32)
+    workspace = _ws_arg(workspace)
+    _on_device(Q=Q, K=K, V=V, theta_q=theta_q, theta_k=theta_k, S0=S0, z0=z0, S_final=S_final,
+               z_final=z_final, out=out, log_gate=log_gate, workspace=workspace)
     if return_state:
         if S_final is None:
             S_final = torch.empty((B, H, m, dv), dtype=torch.float32, device=Q.device)
@@ -304,9 +389,6 @@ def _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk
             _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_final), _ptr(z_final), _ptr(ws), wsb,
             _stream(Q)))
     else:
-        log_gate = _dev(log_gate, "log_gate")
-        if log_gate.shape != Q.shape[:3] or log_gate.dtype != torch.float32:
-            raise ValueError("log_gate must be fp32 [B, H, n]")
         ws, wsb = _workspace(shape, ENTRY_GATED_CAUSAL, Q.device, workspace)
         _check(library().llops_linattn_gated_causal_fwd(
             ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
@@ -315,6 +397,20 @@ def _causal(log_gate, Q, K, V, theta_q, theta_k, square, normalize, delta, chunk
     if return_state:
         return out, S_final, z_final
     return out
+
+
+def _grad_inputs(Q, K, V, theta_q, theta_k, dO, square, normalize, delta):
+    Q, K, V, theta_q, theta_k = _attn_inputs(Q, K, V, theta_q, theta_k)
+    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
+    dO = _t(dO, "dO")
+    _want(dO, "dO", tuple(V.shape), torch.float32)
+    return Q, K, V, theta_q, theta_k, dO, shape
+
+
+def _grads(Q, K, V, theta_q, theta_k):
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    return (torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32),
+            torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32))
 
 
 def llops_linattn_causal_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, normalize=False,
@@ -330,25 +426,16 @@ def llops_linattn_causal_bwd_state(Q, K, V, theta_q, theta_k, dO, *, S0=None, z0
     """Gradients (dQ, dK, dV, dtheta_q, dtheta_k, dS0, dz0) of sum(dO * out) for
     out = llops_linattn_causal_fwd(..., S0=S0, z0=z0); S0 fp32 [B, H, m, dv] and
     z0 fp32 [B, H, m] (None = zeros)."""
-    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
-    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
-    dO = _dev(dO, "dO")
-    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(V.shape):
-        raise ValueError("dO must be fp32 with V's shape")
+    Q, K, V, theta_q, theta_k, dO, shape = _grad_inputs(Q, K, V, theta_q, theta_k, dO, square,
+                                                        normalize, delta)
     B, H = Q.shape[:2]
     m, dv = shape.m, shape.dv
-    if S0 is not None:
-        S0 = _dev(S0, "S0")
-        if tuple(S0.shape) != (B, H, m, dv) or S0.dtype != torch.float32:
-            raise ValueError("S0 must be fp32 [B, H, m, dv]")
-    if z0 is not None:
-        z0 = _dev(z0, "z0")
-        if tuple(z0.shape) != (B, H, m) or z0.dtype != torch.float32:
-            raise ValueError("z0 must be fp32 [B, H, m]")
+    S0, z0 = _state_inputs(S0, z0, B, H, m, dv)
+    workspace = _ws_arg(workspace)
+    _on_device(Q=Q, K=K, V=V, theta_q=theta_q, theta_k=theta_k, dO=dO, S0=S0, z0=z0,
+               workspace=workspace)
+    dQ, dK, dV, dtq, dtk = _grads(Q, K, V, theta_q, theta_k)
     f32 = dict(dtype=torch.float32, device=Q.device)
-    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
-    dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
     dS0, dz0 = torch.empty((B, H, m, dv), **f32), torch.empty((B, H, m), **f32)
     ws, wsb = _workspace(shape, ENTRY_CAUSAL_BWD, Q.device, workspace)
     _check(library().llops_linattn_causal_bwd_state(
@@ -365,15 +452,11 @@ def llops_linattn_bwd(Q, K, V, theta_q, theta_k, dO, *, square=False, normalize=
 
 
 def _attn_bwd(causal, Q, K, V, theta_q, theta_k, dO, square, normalize, delta, workspace):
-    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
-    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
-    dO = _dev(dO, "dO")
-    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(V.shape):
-        raise ValueError("dO must be fp32 with V's shape")
-    f32 = dict(dtype=torch.float32, device=Q.device)
-    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
-    dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
+    Q, K, V, theta_q, theta_k, dO, shape = _grad_inputs(Q, K, V, theta_q, theta_k, dO, square,
+                                                        normalize, delta)
+    workspace = _ws_arg(workspace)
+    _on_device(Q=Q, K=K, V=V, theta_q=theta_q, theta_k=theta_k, dO=dO, workspace=workspace)
+    dQ, dK, dV, dtq, dtk = _grads(Q, K, V, theta_q, theta_k)
     lib = library()
     ws, wsb = _workspace(shape, ENTRY_CAUSAL_BWD if causal else ENTRY_LINATTN_BWD, Q.device,
                          workspace)
@@ -405,17 +488,18 @@ def llops_linattn_gated_causal_bwd_state(Q, K, V, theta_q, theta_k, log_gate, dO
 
 def _gated_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, S0, z0, state, square, normalize, delta,
                workspace):
-    Q, K, V = _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
-    shape = _attn_shape(Q, K, V, theta_q, theta_k, square, normalize, delta, 0)
-    dO, log_gate = _dev(dO, "dO"), _dev(log_gate, "log_gate")
-    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(V.shape):
-        raise ValueError("dO must be fp32 with V's shape")
-    if log_gate.dtype != torch.float32 or tuple(log_gate.shape) != tuple(Q.shape[:3]):
-        raise ValueError("log_gate must be fp32 [B, H, n]")
+    Q, K, V, theta_q, theta_k, dO, shape = _grad_inputs(Q, K, V, theta_q, theta_k, dO, square,
+                                                        normalize, delta)
+    log_gate = _t(log_gate, "log_gate")
+    _want(log_gate, "log_gate", tuple(Q.shape[:3]), torch.float32)
+    B, H = Q.shape[:2]
+    m, dv = shape.m, shape.dv
+    S0, z0 = _state_inputs(S0, z0, B, H, m, dv)
+    workspace = _ws_arg(workspace)
+    _on_device(Q=Q, K=K, V=V, theta_q=theta_q, theta_k=theta_k, dO=dO, log_gate=log_gate, S0=S0,
+               z0=z0, workspace=workspace)
+    dQ, dK, dV, dtq, dtk = _grads(Q, K, V, theta_q, theta_k)
     f32 = dict(dtype=torch.float32, device=Q.device)
-    dQ, dK, dV = torch.empty(Q.shape, **f32), torch.empty(K.shape, **f32), torch.empty(V.shape, **f32)
-    dtq, dtk = torch.empty(theta_q.shape, **f32), torch.empty(theta_k.shape, **f32)
     dg = torch.empty(log_gate.shape, **f32)
     ws, wsb = _workspace(shape, ENTRY_GATED_CAUSAL_BWD, Q.device, workspace)
     if not state:
@@ -424,16 +508,6 @@ def _gated_bwd(Q, K, V, theta_q, theta_k, log_gate, dO, S0, z0, state, square, n
             _ptr(log_gate), _ptr(dO), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dtq), _ptr(dtk), _ptr(dg),
             _ptr(ws), wsb, _stream(Q)))
         return dQ, dK, dV, dtq, dtk, dg
-    B, H = Q.shape[:2]
-    m, dv = shape.m, shape.dv
-    if S0 is not None:
-        S0 = _dev(S0, "S0")
-        if tuple(S0.shape) != (B, H, m, dv) or S0.dtype != torch.float32:
-            raise ValueError("S0 must be fp32 [B, H, m, dv]")
-    if z0 is not None:
-        z0 = _dev(z0, "z0")
-        if tuple(z0.shape) != (B, H, m) or z0.dtype != torch.float32:
-            raise ValueError("z0 must be fp32 [B, H, m]")
     dS0, dz0 = torch.empty((B, H, m, dv), **f32), torch.empty((B, H, m), **f32)
     _check(library().llops_linattn_gated_causal_bwd_state(
         ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(theta_q), _ptr(theta_k),
@@ -451,27 +525,44 @@ def llops_decode_step(q, k, v, theta_q, theta_k, S, z, *, square=False, normaliz
 def llops_gated_decode_step(q, k, v, theta_q, theta_k, log_gate, S, z, *, square=False,
                             normalize=True, delta=0.0, out=None, workspace=None):
     """llops_decode_step on a state first decayed by exp(log_gate) (fp32 [B, H])."""
+    if log_gate is None:
+        raise ValueError("log_gate is required")
     return _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out,
                    workspace)
 
 
-def _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, workspace):
-    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
-    theta_q, theta_k = _dev(theta_q, "theta_q"), _dev(theta_k, "theta_k")
+def _decode_args(q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, log_gate):
+    """Checked decode arguments and their llops_shape_t (metadata only)."""
+    q, k, v = _t(q, "q"), _t(k, "k"), _t(v, "v")
+    theta_q, theta_k = _t(theta_q, "theta_q"), _t(theta_k, "theta_k")
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B, H, d] and v [B, H, dv]")
-    if not (S.is_contiguous() and z.is_contiguous()):
-        raise ValueError("S and z are updated in place and must be contiguous")
     B, H, d = q.shape
-    dq, ph = _theta_dims(theta_q, H)
-    p, t, td, m = dq
     dv = v.shape[2]
-    if S.shape != (B, H, m, dv) or z.shape != (B, H, m) or S.dtype != torch.float32 \
-            or z.dtype != torch.float32 or S.device.type != "cuda":
-        raise ValueError("S must be fp32 [B, H, m, dv] and z fp32 [B, H, m] on the device")
+    p, t, m, ph = _two_thetas(theta_q, theta_k, H, d)
+    if len({x.dtype for x in (q, k, v, theta_q, theta_k)}) != 1:
+        raise ValueError("q, k, v and theta must share one dtype")
+    idt = _dt(q)
+    _out(S, "S", (B, H, m, dv), torch.float32)
+    _out(z, "z", (B, H, m), torch.float32)
+    if out is not None:
+        _out(out, "out", (B, H, dv), torch.float32)
+    if log_gate is not None:
+        log_gate = _t(log_gate, "log_gate")
+        _want(log_gate, "log_gate", (B, H), torch.float32)
     shape = make_shape(batch=B, heads=H, n=1, d=d, dv=dv, m=m, p=p, t=t, square=square,
-                       normalize=normalize, delta=delta, theta_per_head=ph, in_dtype=_dt(q),
+                       normalize=normalize, delta=delta, theta_per_head=ph, in_dtype=idt,
                        out_dtype=F32)
+    return q, k, v, theta_q, theta_k, log_gate, shape
+
+
+def _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, workspace):
+    q, k, v, theta_q, theta_k, log_gate, shape = _decode_args(
+        q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, log_gate)
+    workspace = _ws_arg(workspace)
+    _on_device(q=q, k=k, v=v, theta_q=theta_q, theta_k=theta_k, S=S, z=z, out=out,
+               log_gate=log_gate, workspace=workspace)
+    B, H, dv = shape.batch, shape.heads, shape.dv
     if out is None:
         out = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     if log_gate is None:
@@ -480,9 +571,6 @@ def _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta,
                                            _ptr(theta_q), _ptr(theta_k), _ptr(S), _ptr(z),
                                            _ptr(out), _ptr(ws), wsb, _stream(q)))
     else:
-        log_gate = _dev(log_gate, "log_gate")
-        if log_gate.shape != (B, H) or log_gate.dtype != torch.float32:
-            raise ValueError("log_gate must be fp32 [B, H]")
         ws, wsb = _workspace(shape, ENTRY_GATED_DECODE, q.device, workspace)
         _check(library().llops_gated_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                                  _ptr(theta_q), _ptr(theta_k), _ptr(log_gate),

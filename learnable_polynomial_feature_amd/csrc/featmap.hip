@@ -842,14 +842,24 @@ hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njob
   if (tiles * a.fsplit > 0x7fffffffLL || s.H > 65535) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(tiles * a.fsplit), static_cast<unsigned>(s.H), njobs);
   const size_t lds = 2ull * s.p * tr * 16 * ldsrow * sizeof(uint16_t);
+  // every d the validation admits for bf16 (a multiple of 16 up to 256); the
+  // kernel zeroes both operands past d when d is not a multiple of 32
   switch (s.d) {
     case 16: return launch_d<16>(a, grid, lds, st);
     case 32: return launch_d<32>(a, grid, lds, st);
     case 48: return launch_d<48>(a, grid, lds, st);
     case 64: return launch_d<64>(a, grid, lds, st);
+    case 80: return launch_d<80>(a, grid, lds, st);
     case 96: return launch_d<96>(a, grid, lds, st);
+    case 112: return launch_d<112>(a, grid, lds, st);
     case 128: return launch_d<128>(a, grid, lds, st);
+    case 144: return launch_d<144>(a, grid, lds, st);
+    case 160: return launch_d<160>(a, grid, lds, st);
+    case 176: return launch_d<176>(a, grid, lds, st);
     case 192: return launch_d<192>(a, grid, lds, st);
+    case 208: return launch_d<208>(a, grid, lds, st);
+    case 224: return launch_d<224>(a, grid, lds, st);
+    case 240: return launch_d<240>(a, grid, lds, st);
     case 256: return launch_d<256>(a, grid, lds, st);
     default: return hipErrorInvalidValue;
   }

@@ -13,6 +13,19 @@ def rel_fro(got, want) -> float:
     return float(num / den) if den > 0 else float(num)
 
 
+def row_rel_max(got, want) -> float:
+    """Largest row-wise relative error max_i ||got_i - want_i|| / ||want_i||
+    over the rows (last axis) of the tensors, in float64."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    g = g.reshape(-1, g.shape[-1])
+    w = w.reshape(-1, w.shape[-1])
+    den = np.linalg.norm(w, axis=1)
+    num = np.linalg.norm(g - w, axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float((num / den).max()) if len(den) else 0.0
+
+
 def dev(x, dtype):
     """numpy float32 (storage-exact) -> device tensor of `dtype`."""
     import torch
@@ -40,6 +53,16 @@ def announce(msg: str):
 #      products summed in fp32; dY is rounded once to bf16 (unit roundoff 2^-9)
 #      before the two fp32-accumulated products, so each output is a sum of
 #      terms with one independent relative error of at most 2^-9 each
+#
+# Row-wise bound on the bf16 attention paths (largest relative error of one
+# output row, row_rel_max): 1e-2. Rounding phi, A and S to bf16 as MFMA
+# operands moves a normalised output row by at most about 3e-3 at the long
+# workload (a CPU simulation of those roundings over 8192 rows of three
+# heads), while the normaliser's delta changes the first rows by far more:
+# dropping it or doubling it moves the worst row by 3.9% to 7.5% (pinned on
+# the CPU by test_delta_rows_cpu.py). A whole-tensor norm averages that change
+# away; this bound does not.
+TOL_ROW_BF16 = 1e-2
 TOL_F32 = 1e-5
 TOL_FEAT_BF16_IN = 1e-5
 TOL_FEAT_BF16_OUT = 5e-3

@@ -55,7 +55,7 @@ def test_header_functions_are_exported(L):
         assert hasattr(L, n)
 
 
-def test_shape_struct_layout_matches_header():
+def test_shape_struct_layout_matches_header(tmp_path):
     """Compile a tiny C program against include/llops.h and compare
     sizeof/offsetof with the ctypes mirror."""
     fields = [f for f, _ in _lib.Shape._fields_]
@@ -63,9 +63,8 @@ def test_shape_struct_layout_matches_header():
             'printf("%zu\\n", sizeof(llops_shape_t));']
     prog += [f'printf("%zu\\n", offsetof(llops_shape_t, {f}));' for f in fields]
     prog += ["return 0;}"]
-    tmp = os.path.join(ROOT, "_work") if os.path.isdir(os.path.join(ROOT, "_work")) else "/tmp"
-    c = os.path.join(tmp, "llops_layout_check.c")
-    exe = os.path.join(tmp, "llops_layout_check")
+    c = str(tmp_path / "llops_layout_check.c")
+    exe = str(tmp_path / "llops_layout_check")
     with open(c, "w") as f:
         f.write("\n".join(prog))
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),

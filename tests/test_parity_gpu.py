@@ -8,8 +8,8 @@ import pytest
 from learnable_polynomial_feature_amd.workloads import Workload, generate
 from oracle import llops_oracle as O
 
-from _util import (TOL_BF16, TOL_F32, TOL_FEAT_BF16_IN, TOL_FEAT_BF16_OUT, announce, dev, host,
-                    rel_fro)
+from _util import (TOL_BF16, TOL_F32, TOL_FEAT_BF16_IN, TOL_FEAT_BF16_OUT, TOL_ROW_BF16,
+                    announce, dev, host, rel_fro, row_rel_max)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,19 @@ FEAT_CASES = [
     (1, 3, 700, 128, 96, 2, 4, True, False, True),
     (2, 2, 300, 128, 160, 2, 1, False, False, True),
     (1, 8, 12800, 128, 160, 2, 1, True, False, True),
+    # p = 4 on the unrolled kernels with four distinct Theta_j (each j, r is
+    # its own seeded draw): the 256-row-tile kernels (> 1024 rows per head)
+    # and the few-row kernels that read Theta in place (<= 1024 rows)
+    (1, 2, 2100, 128, 256, 4, 1, True, False, True),
+    (1, 2, 2100, 128, 256, 4, 1, False, True, False),
+    (2, 2, 1100, 64, 128, 4, 1, False, False, False),
+    (128, 4, 1, 128, 256, 4, 1, True, False, False),
+    (300, 2, 1, 64, 64, 4, 1, True, False, True),
+    # head dims that are multiples of 16 but not of 32 (generic kernel,
+    # operands zeroed past d)
+    (2, 2, 300, 80, 64, 2, 2, True, False, False),
+    (1, 1, 200, 112, 48, 3, 1, False, False, True),
+    (1, 1, 150, 240, 32, 2, 2, True, True, False),
 ]
 
 
@@ -137,6 +150,7 @@ CAUSAL_CASES = [
     (3, 2, 33, 128, 128, 256, 2, 4, True, True, 64),
     (2, 2, 1500, 128, 128, 256, 2, 4, True, True, 128),
     (1, 2, 2500, 64, 64, 128, 3, 8, True, True, 64),
+    (1, 2, 300, 80, 64, 64, 2, 2, True, True, 64),
 ]
 
 
@@ -153,6 +167,8 @@ def test_causal_bf16(lib, case):
     ro, rS, rz = O.causal_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], chunk=64,
                              square=square, normalize=normalize, delta=1e-6)
     assert rel_fro(host(out), ro) <= TOL_BF16
+    if normalize:  # delta decides the first rows: bound every row
+        assert row_rel_max(host(out), ro) <= TOL_ROW_BF16, row_rel_max(host(out), ro)
     assert rel_fro(host(S), rS) <= TOL_BF16
     assert rel_fro(host(z), rz) <= TOL_BF16
 
