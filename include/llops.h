@@ -355,6 +355,30 @@ llops_status_t llops_gated_decode_step(const llops_shape_t* shape, const void* q
                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * llops_decode_step_noalloc -- llops_decode_step with no workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It computes
+ * exactly what llops_decode_step computes, with the same kernels. Its scratch
+ * (phi_q, phi_k, and repacked Theta copies when batch > 1024 on a bf16
+ * shape with an unrolled feature-map kernel) lives in a static device array
+ * of 16 MiB inside the library, one per GPU, held until the process ends; a
+ * shape whose scratch (llops_workspace_bytes(shape, LLOPS_ENTRY_DECODE))
+ * exceeds 16 MiB returns LLOPS_ERR_UNSUPPORTED before any launch (batch *
+ * heads * m <= 2^21 fits, e.g. 4096 sequences x heads at m = 256). The call
+ * allocates nothing and needs nothing zeroed: every scratch byte it reads was
+ * written earlier in the same call. The first call on a device looks the
+ * array's address up (hipGetSymbolAddress, with the stream's device
+ * current); later calls reuse it. All calls on one GPU share that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or host
+ * threads without ordering) race on it and must be serialised by the
+ * caller. Other arguments, layouts and errors as for llops_decode_step.
+ */
+llops_status_t llops_decode_step_noalloc(const llops_shape_t* shape, const void* q,
+                                         const void* k, const void* v,
+                                         const void* theta_q, const void* theta_k,
+                                         float* S, float* z, void* out, hipStream_t stream);
+
+/*
  * Diagnostics: kernel-level timing. While armed on the calling thread, each
  * kernel launch made by the library on behalf of that thread records
  * events[2*i] just before and events[2*i+1] just after it on the launch

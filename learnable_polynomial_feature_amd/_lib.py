@@ -26,7 +26,7 @@ EXPORTS = ("llops_workspace_bytes", "llops_featmap", "llops_featmap_bwd", "llops
            "llops_linattn_causal_fwd", "llops_linattn_causal_bwd", "llops_linattn_bwd",
            "llops_decode_step", "llops_linattn_gated_causal_fwd", "llops_gated_decode_step",
            "llops_linattn_gated_causal_bwd", "llops_linattn_causal_bwd_state",
-           "llops_linattn_gated_causal_bwd_state",
+           "llops_linattn_gated_causal_bwd_state", "llops_decode_step_noalloc",
            "llops_status_str",
            "llops_last_error", "llops_profile_arm", "llops_profile_disarm")
 
@@ -90,6 +90,8 @@ def library(path: str | None = None) -> ctypes.CDLL:
     lib.llops_linattn_gated_causal_bwd.restype = ctypes.c_int
     lib.llops_linattn_gated_causal_bwd_state.argtypes = [SP] + [_P] * 18 + [ctypes.c_size_t, _P]
     lib.llops_linattn_gated_causal_bwd_state.restype = ctypes.c_int
+    lib.llops_decode_step_noalloc.argtypes = [SP] + [_P] * 8 + [_P]
+    lib.llops_decode_step_noalloc.restype = ctypes.c_int
     lib.llops_status_str.argtypes = [ctypes.c_int]
     lib.llops_status_str.restype = ctypes.c_char_p
     lib.llops_last_error.argtypes = []
@@ -529,6 +531,23 @@ def llops_gated_decode_step(q, k, v, theta_q, theta_k, log_gate, S, z, *, square
         raise ValueError("log_gate is required")
     return _decode(log_gate, q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out,
                    workspace)
+
+
+def llops_decode_step_noalloc(q, k, v, theta_q, theta_k, S, z, *, square=False, normalize=True,
+                              delta=0.0, out=None):
+    """llops_decode_step with its scratch in the library's static per-GPU
+    buffer (no workspace allocated). Calls overlapping in time on one GPU race
+    on that buffer; S, z updated in place; returns out [B, H, dv] fp32."""
+    q, k, v, theta_q, theta_k, _, shape = _decode_args(
+        q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, None)
+    _on_device(q=q, k=k, v=v, theta_q=theta_q, theta_k=theta_k, S=S, z=z, out=out)
+    if out is None:
+        out = torch.empty((shape.batch, shape.heads, shape.dv), dtype=torch.float32,
+                          device=q.device)
+    _check(library().llops_decode_step_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(theta_q), _ptr(theta_k), _ptr(S), _ptr(z),
+                                               _ptr(out), _stream(q)))
+    return out
 
 
 def _decode_args(q, k, v, theta_q, theta_k, S, z, square, normalize, delta, out, log_gate):

@@ -1,9 +1,12 @@
 // C ABI of libllops: argument validation, workspace layout and kernel dispatch.
 // No allocation, no host synchronisation; every check runs before the first launch.
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "kernels.h"
 #include "llops.h"
@@ -1232,6 +1235,67 @@ llops_status_t llops_gated_decode_step(const llops_shape_t* s, const void* q, co
                                        void* ws, size_t ws_bytes, hipStream_t st) {
   if (s && s->batch * s->heads > 0) LLOPS_TRY(need4(log_gate, "log_gate"));
   return decode_impl(s, q, k, v, theta_q, theta_k, log_gate, S, z, out, ws, ws_bytes, st);
+}
+
+}  // extern "C"
+
+// ---- decode without a caller workspace --------------------------------------
+// The scratch of llops_decode_step_noalloc (phi_q and phi_k, plus repacked
+// Theta copies for batches above 1024 rows per head) lives in this static
+// device array. Each GPU the library runs on holds its own copy for the life
+// of the process; host code never uses the array's name as an address, only
+// the per-device pointer that hipGetSymbolAddress returns for it.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's address on the device `stream` runs on, looked up once per
+// device with that device current (then restored).
+llops_status_t noalloc_scratch(hipStream_t st, void** out) {
+  int cur = 0;
+  LLOPS_HIP(hipGetDevice(&cur), "hipGetDevice");
+  int dev = cur;
+  if (st) LLOPS_HIP(hipStreamGetDevice(st, &dev), "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(LLOPS_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur) LLOPS_HIP(hipSetDevice(dev), "hipSetDevice");
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) LLOPS_HIP(hipSetDevice(cur), "hipSetDevice");
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(LLOPS_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LLOPS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+llops_status_t llops_decode_step_noalloc(const llops_shape_t* s, const void* q, const void* k,
+                                         const void* v, const void* theta_q, const void* theta_k,
+                                         float* S, float* z, void* out, hipStream_t st) {
+  LLOPS_TRY(validate(s, LLOPS_ENTRY_DECODE));
+  const size_t need = ws_layout(s, LLOPS_ENTRY_DECODE).total;
+  if (need > kNoAllocScratchBytes)
+    return fail(LLOPS_ERR_UNSUPPORTED,
+                "decode without a workspace: this shape needs %zu bytes of scratch, the static "
+                "buffer holds %zu", need, kNoAllocScratchBytes);
+  if (s->batch * s->heads == 0) return LLOPS_OK;
+  void* ws = nullptr;
+  LLOPS_TRY(noalloc_scratch(st, &ws));
+  return decode_impl(s, q, k, v, theta_q, theta_k, nullptr, S, z, out, ws, kNoAllocScratchBytes,
+                     st);
 }
 
 const char* llops_status_str(llops_status_t status) {

@@ -471,3 +471,17 @@ def test_gated_bwd_pointers_and_workspace(L):
     assert st == 1 and "dlog_gate is null" in _err(L)
     st = L.llops_linattn_gated_causal_bwd(ctypes.byref(s), *([FAKE] * 14), need - 1, None)
     assert st == 3 and "workspace" in _err(L)
+
+
+@fake_ptr
+def test_decode_noalloc_size_limit(L):
+    """The allocation-free decode refuses a shape whose scratch exceeds its
+    16 MiB static buffer, before touching any device (status UNSUPPORTED)."""
+    big = _shape(batch=4096, heads=8, n=1, d=128, dv=128, m=256, p=2, t=4)
+    st = L.llops_decode_step_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None)
+    assert st == 2 and "static" in _err(L), _err(L)
+    # invalid shapes fail validation first
+    st = L.llops_decode_step_noalloc(ctypes.byref(_shape(p=0)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, None)
+    assert st == 1
