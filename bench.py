@@ -62,11 +62,6 @@ def log(msg):
 # ---------------------------------------------------------------------------
 # algorithmic work (per call, whole batch)
 # ---------------------------------------------------------------------------
-def featmap_flops(w, n_rows):
-    """2 * rows * d * (p*t*m) per projected tensor (the p*t products X Theta)."""
-    return 2.0 * n_rows * w.d * w.p * w.t * w.m
-
-
 # (m, dv) shapes of the 32x32x16 segment kernels, which walk 32-token chunks
 # whatever chunk length is asked for (the chunk only orders the rounding)
 _SEG32 = {(256, 128), (128, 64), (64, 64)}
@@ -94,6 +89,24 @@ def causal_flops(w):
     per_bh = (4.0 * w.n * w.d * w.p * w.t * w.m + 4.0 * w.n * w.m * w.dv
               + w.n * (C + 1) * (w.m + w.dv))
     return bh * per_bh
+
+
+def step_kernel_flops(w, kern):
+    """Algorithmic flops per launch of each kernel of one causal step (whole
+    batch): the feature map projects Q and K (two-kernel path) or K only
+    (when the fused output pass, attn_out_fq, projects Q); the state pass
+    builds phi_K^T V; an output pass reads out phi_Q S plus the intra-chunk
+    triangle at the chunk it runs (its S update repeats the state pass's
+    product and is not credited again)."""
+    bh = w.batch * w.heads
+    proj = 2.0 * w.n * w.d * w.p * w.t * w.m
+    readout = 2.0 * w.n * w.m * w.dv + w.n * (kernel_chunk(w) + 1) * (w.m + w.dv)
+    fused = "attn_out_fq" in kern
+    table = {"featmap_bf16": bh * proj * (1 if fused else 2),
+             "seg_state_bf16": bh * 2.0 * w.n * w.m * w.dv,
+             "attn_out_bf16": bh * readout,
+             "attn_out_fq": bh * (proj + readout)}
+    return {k: v for k, v in table.items() if k in kern}
 
 
 def decode_bytes(w):
@@ -150,6 +163,52 @@ def bench_causal(w, steps, warmup, torch, lib):
     ms = t0.elapsed_time(t1) / steps
     kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
     return ms, kern, (args, ws)
+
+
+def bench_other_path(w, steps, torch, lib, args, ws, fused):
+    """The same causal step on the other execution path: fused = True runs
+    the output pass that projects phi_Q itself (LLOPS_FUSED_Q=1, phi_Q never
+    in HBM); fused = False the two-kernel path (phi_Q and phi_K through HBM,
+    then the segment passes)."""
+    out = torch.empty((w.batch, w.heads, w.n, w.dv), dtype=torch.float32, device="cuda")
+    kw = dict(square=w.square, normalize=w.normalize, delta=w.delta, chunk=w.chunk, out=out,
+              workspace=ws)
+    prev = os.environ.get("LLOPS_FUSED_Q")
+    os.environ["LLOPS_FUSED_Q"] = "1" if fused else "0"
+    try:
+        for _ in range(2):
+            lib.llops_linattn_causal_fwd(*args, **kw)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            lib.llops_linattn_causal_fwd(*args, **kw)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        timer = lib.KernelTimer(capacity=16 * steps)
+        with timer:
+            for _ in range(steps):
+                lib.llops_linattn_causal_fwd(*args, **kw)
+        torch.cuda.synchronize()
+    finally:
+        if prev is None:
+            del os.environ["LLOPS_FUSED_Q"]
+        else:
+            os.environ["LLOPS_FUSED_Q"] = prev
+    kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
+    del out
+    kfl = step_kernel_flops(w, kern)
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch * w.n / (ms * 1e-3), 1),
+            "mfma_frac_step": round(causal_flops(w) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+            "kernel_mfma": {k: {"tflop_per_launch": round(f / 1e12, 4),
+                                "frac": round(f / (kern[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                            for k, f in kfl.items()},
+            "note": ("phi_Q projected inside the output pass, never in HBM (LLOPS_FUSED_Q=1)"
+                     if fused else "phi_Q and phi_K written to HBM by the feature map, read "
+                                   "back by the segment passes")}
 
 
 def bench_gated(w, steps, torch, lib, args, ws_causal):
@@ -783,16 +842,22 @@ def main():
     ms, kern, (cargs, cws) = bench_causal(w, args.steps, args.warmup, torch, lib)
     tokens = w.batch * w.n
     flops = causal_flops(w)
-    feat_ms = kern.get("featmap_bf16")
-    feat_flops = featmap_flops(w, 2 * w.batch * w.heads * w.n)  # Q and K in one launch
+    # the dominant kernel (longest average launch) against the bf16 MFMA
+    # peak, its duration from the HIP events recorded around each launch on
+    # the launch stream; every kernel of the step beside it
+    kfl = step_kernel_flops(w, kern)
+    per_kernel = {k: {"avg_ms": round(kern[k], 4), "tflop_per_launch": round(f / 1e12, 4),
+                      "frac": round(f / (kern[k] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                  for k, f in kfl.items()}
     roofline = None
-    if feat_ms:
-        ach = feat_flops / (feat_ms * 1e-3) / 1e12
-        roofline = {"kernel": "featmap_bf16", "bound": "mfma", "achieved": round(ach, 2),
+    if kfl:
+        dom = max(kfl, key=lambda k: kern[k])
+        ach = kfl[dom] / (kern[dom] * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic("featmap_bf16"),
-                    "avg_ms": round(feat_ms, 4), "flops_per_launch": feat_flops}
+                    "traffic": load_traffic(dom),
+                    "avg_ms": round(kern[dom], 4), "flops_per_launch": kfl[dom]}
     line = {
         "metric": "causal LLoPS fwd tokens/sec at n=65536,p=2,t=4,m=256; % MFMA peak; decode GB/s",
         "value": round(tokens / (ms * 1e-3), 1),
@@ -819,6 +884,7 @@ def main():
                           "frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                           "flops_per_step": flops, "intra_chunk_tokens": kernel_chunk(w)},
         "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+        "kernel_mfma": per_kernel,
         "roofline": roofline,
     }
     if not args.no_decode:
@@ -845,6 +911,12 @@ def main():
                 "bytes_per_launch": decode_state_bytes(wd)},
             "gated": dgated,
         }
+    if "attn_out_fq" in kern:
+        log("two-kernel causal path")
+        line["two_kernel_path"] = bench_other_path(w, 10, torch, lib, cargs, cws, False)
+    else:
+        log("fused causal path")
+        line["fused_path"] = bench_other_path(w, 10, torch, lib, cargs, cws, True)
     if not args.no_gated:
         log("gated causal")
         line["gated"] = bench_gated(w, 10, torch, lib, cargs, cws)

@@ -166,6 +166,15 @@ llops_status_t llops_linattn_fwd(const llops_shape_t* shape, const void* Q,
  * after the last token, so prefill(n1) then prefill(n2, S0=S_final) equals
  * prefill(n1+n2). S0/z0 may alias S_final/z_final.
  * ws: llops_workspace_bytes(shape, LLOPS_ENTRY_CAUSAL).
+ * Two execution paths compute bit for bit the same result on bf16 inputs:
+ * by default the feature maps of Q and K go through the workspace (HBM) and
+ * the segment passes read them back; with the environment variable
+ * LLOPS_FUSED_Q=1 (read at each call), shapes (m, dv, d, p, t) in
+ * {(256, 128, 128, 2, 4), (128, 64, 64, 3, 8)} with more than 1024 rows per
+ * head project phi_Q inside the output pass instead, so phi_Q never reaches
+ * HBM (the fused feature map -> causal pass; the notes' key design 2 and the
+ * paper's runtime paragraph attribute the method's cost to these
+ * projections and element-wise products).
  */
 llops_status_t llops_linattn_causal_fwd(const llops_shape_t* shape, const void* Q,
                                         const void* K, const void* V,

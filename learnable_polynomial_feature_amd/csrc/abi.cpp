@@ -2,6 +2,7 @@
 // No allocation, no host synchronisation; every check runs before the first launch.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -534,6 +535,19 @@ hipError_t state_total(const llops_shape_t* s, int M, int DV, const uint16_t* fk
   return e;
 }
 
+// With LLOPS_FUSED_Q=1 in the environment the causal bf16 forward projects
+// phi_Q inside its output pass (phi_Q never reaches HBM), where a fused kernel
+// exists for the shape and Theta_Q has a fragment-order copy (more than 1024
+// rows per head). Both paths compute the same values bit for bit; the
+// two-kernel path (feature maps of Q and K, then the segment passes) is the
+// default because it measures faster on MI355X (the fused pass re-streams
+// Theta_Q from L2 every 64 rows instead of every 256).
+bool fused_q(const llops_shape_t* s, const llops::AttnShape& a) {
+  const char* env = getenv("LLOPS_FUSED_Q");
+  if (!env || env[0] != '1') return false;
+  return pack_bytes(s, s->n) > 0 && llops::attn32_fq_supported(a, s->d, s->p, s->t);
+}
+
 // Shared body of the non-causal and causal forward passes.
 llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, const void* K,
                          const void* V, const void* tq, const void* tk, const float* S0,
@@ -575,7 +589,22 @@ llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, con
   float* seg = reinterpret_cast<float*>(w + L.seg);
   llops::FeatJob jobs[2] = {{Q, tq, w + L.phiq, w + L.pkq}, {K, tk, w + L.phik, w + L.pkk}};
   const llops::FeatShape fs = feat_shape(s, s->n, bf16 ? 1 : 0);
-  if (bf16) {
+  if (bf16 && causal && fused_q(s, a)) {
+    // phi_Q is projected inside the output pass: only phi_K goes through HBM
+    LLOPS_HIP(llops::launch_featmap_bf16(fs, &jobs[1], 1, st), "featmap");
+    LLOPS_HIP(llops::launch_pack_theta(fs, tq, w + L.pkq, st), "pack_theta");
+    const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);
+    const uint16_t* vv = static_cast<const uint16_t*>(V);
+    LLOPS_HIP(llops::launch_seg_state32(a, pk, vv, seg, st), "seg_state");
+    LLOPS_HIP(llops::launch_seg_scan(a, seg, S0, z0, S_final, z_final, 1, st), "seg_scan");
+    const int64_t pk_hstride =
+        s->theta_per_head ? static_cast<int64_t>(s->p) * s->t * s->d * s->m : 0;
+    LLOPS_HIP(llops::launch_attn_out32_fq(a, s->d, s->p, s->t, static_cast<const uint16_t*>(Q),
+                                          reinterpret_cast<const uint16_t*>(w + L.pkq),
+                                          pk_hstride, s->heads, s->square, pk, vv, seg, per,
+                                          per * a.nseg, static_cast<float*>(out), st),
+              "attn_out_fq");
+  } else if (bf16) {
     LLOPS_HIP(llops::launch_featmap_bf16(fs, jobs, 2, st), "featmap");
     const uint16_t* pq = reinterpret_cast<const uint16_t*>(w + L.phiq);
     const uint16_t* pk = reinterpret_cast<const uint16_t*>(w + L.phik);

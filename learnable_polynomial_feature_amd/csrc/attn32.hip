@@ -726,6 +726,462 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   }
 }
 
+// ============================================================================
+// Fused pass 2: phi_Q projected inside the causal output pass
+// ============================================================================
+// phi_Q = featmap(Q) never reaches HBM (the pages' cost model is p*t small
+// projections plus element-wise products, notes key design 2; here those
+// projections run in the same kernel as the causal read-out). A workgroup
+// walks its segment in blocks of 64 rows:
+//   projection: wave w computes the 32-feature block w of the block's rows,
+//     Y_{j,r} = X_Q Theta_{j,r} on MFMA with the X rows staged in LDS and the
+//     Theta fragments streamed from the fragment-order copy (the layout the
+//     feature-map kernel reads) straight into registers, then the Hadamard
+//     product over j, the sum over r and the square in registers, rounded to
+//     bf16 into an LDS block buffer. The products and the epilogue run in the
+//     feature-map kernel's order, so phi_Q is bit for bit the one that kernel
+//     stores;
+//   read-out: the block's two 32-token chunks run exactly as attn_out32's
+//     (same waves, same exchange, same arithmetic), phi_Q read from the block
+//     buffer, phi_K and V streamed per chunk.
+// The workgroup needs m = 2 dv (one feature block per wave).
+template <int M, int DV, int D, int P, int T>
+struct Fq32Geom {
+  static constexpr int NWD = DV / 32;      // value-column tiles
+  static constexpr int NW = 2 * NWD;       // waves
+  static constexpr int NT = NW * 64;
+  static constexpr int FT = M / 32;
+  static constexpr int FH = FT / 2;
+  static constexpr int RB = 2 * kC;        // rows per projected block
+  static constexpr int KS = D / 16;        // 16-deep k-steps of the projection
+  static constexpr int QPAD = M + 8, MP = M + 16, VP = DV + 16;
+  static constexpr int XP = D + 8;         // X rows 16 bytes apart mod 256: b128 reads conflict-free
+  static constexpr int QB = RB * QPAD;     // phi_Q block buffer (elements)
+  static constexpr int XB = RB * XP;       // X_Q block buffer
+  static constexpr int BUF = kC * MP + kC * VP;  // one chunk: phi_K, V
+  static constexpr int KPc = kC * M / 8, VPc = kC * DV / 8;  // 16-byte pieces per chunk
+  static constexpr int LPT = (KPc + VPc) / NT;
+  static constexpr int LX = RB * D / 8 / NT;  // 16-byte X pieces per thread per block
+  static constexpr int XO = NW * 8 * 64, PART = kC * 8, EXW = XO + PART + kC;
+  static constexpr int NFR = T * P * KS;   // Theta fragments of one feature block
+  static constexpr int TPD = 4;            // Theta fragments in flight per wave
+  static constexpr bool STREAM_NT = true;  // phi_K, V and X loads marked non-temporal
+  static constexpr size_t lds_bytes() { return 2ull * (QB + XB + 2 * BUF) + 2ull * EXW * 4; }
+  static_assert(FT == NW, "one 32-feature block per wave in the projection");
+  static_assert(D % 32 == 0 && FT % 2 == 0, "shape");
+  static_assert(KPc % NT == 0 && VPc % NT == 0 && (RB * D / 8) % NT == 0, "even split");
+  static_assert(NW <= 8, "z partial slots");
+};
+
+template <int M, int DV, int D, int P, int T>
+__global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_out32_fq(Seg32Args a, const uint16_t* __restrict__ xq,
+                   const uint16_t* __restrict__ thpk, int64_t pk_hstride, int64_t H, int square,
+                   const uint16_t* __restrict__ phik, const uint16_t* __restrict__ v,
+                   const float* __restrict__ state, int64_t st_seg, int64_t st_bh,
+                   float* __restrict__ out) {
+  using G = Fq32Geom<M, DV, D, P, T>;
+  constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, XP = G::XP, NT = G::NT;
+  constexpr int NWD = G::NWD, KS = G::KS, LPT = G::LPT, LX = G::LX, KPc = G::KPc;
+  constexpr int NFR = G::NFR, TPD = G::TPD < G::NFR ? G::TPD : G::NFR;
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: see attn pass 1
+  const int dvt = w % NWD, half = w / NWD;
+  const int f0 = half * FH;
+  const bool has_z = dvt < FH;
+  const int zj = dvt;
+  const int c32 = lane & 31, hh = lane >> 5;
+  // XCD-aware work order: workgroups are dispatched to the 8 XCDs round
+  // robin (id % 8), so workgroup id takes sequence bh = xcd * BH/8 + k / nseg
+  // with k = id / 8: the workgroups on one XCD walk the segments of BH/8
+  // sequences and their heads' Theta_Q stays in that XCD's L2 instead of
+  // every XCD streaming every head's
+  const int64_t BH = static_cast<int64_t>(gridDim.x) / a.nseg;
+  const int64_t id = blockIdx.x;
+  int64_t bh;
+  int gseg;
+  if (BH % 8 == 0) {
+    const int64_t k = id / 8;
+    bh = (id % 8) * (BH / 8) + k / a.nseg;
+    gseg = static_cast<int>(k % a.nseg);
+  } else {
+    bh = id / a.nseg;
+    gseg = static_cast<int>(id % a.nseg);
+  }
+  const int64_t t0 = gseg * a.seg_len;
+  const int64_t t1 = min(a.n, t0 + a.seg_len);
+  const uint16_t* Xg = xq + bh * a.n * D;
+  const uint16_t* Kg = phik + bh * a.n * M;
+  const uint16_t* Vg = v + bh * a.n * DV;
+  float* Og = out + bh * a.n * DV;
+  const float* Sin = state + bh * st_bh + gseg * st_seg;
+  const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
+  uint16_t* Qb = smem;                 // [RB][QPAD] phi_Q of the current block
+  uint16_t* Xs = Qb + G::QB;           // [RB][XP]   X_Q rows of the block to project
+  uint16_t* cbuf = Xs + G::XB;         // 2 x [phi_K | V] chunk buffers
+  float* exbase = reinterpret_cast<float*>(cbuf + 2 * G::BUF);
+
+  f32x16 S[FH], Z;
+#pragma unroll
+  for (int j = 0; j < FH; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[j][4 * i + e] = Sin[((f0 + j) * 32 + 8 * i + 4 * hh + e) * DV + dvt * 32 + c32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Z[4 * i + e] = has_z ? Sin[static_cast<int64_t>(M) * DV + (f0 + zj) * 32 + 8 * i + 4 * hh + e] : 0.f;
+  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  // Raw buffer views of this segment's rows (zeros past the segment end) and
+  // of this wave's feature block of the fragment-order Theta_Q: fragment
+  // (r, j, ks) is 1 KiB at byte ((r * P + j) * KS + ks) * 1024, lane l's 16
+  // bytes at 16 l.
+  const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
+  const __amdgpu_buffer_rsrc_t rsx = make_rsrc(Xg + t0 * D, seg_rows * D * 2u);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsv = make_rsrc(Vg + t0 * DV, seg_rows * DV * 2u);
+  const int64_t h = bh % H;
+  const __amdgpu_buffer_rsrc_t rst =
+      make_rsrc(thpk + h * pk_hstride + static_cast<int64_t>(w) * NFR * 512, NFR * 1024u);
+
+  auto load = [&](int c, u32x4 (&r)[LPT]) {
+    int t = tid;  // opaque: per-piece offsets are rebuilt, not kept live
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int p = t + i * NT;
+      if (i * NT < KPc)
+        r[i] = G::STREAM_NT ? buf_ld16_nt(rsk, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u))
+                     : buf_ld16(rsk, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+      else
+        r[i] = G::STREAM_NT ? buf_ld16_nt(rsv, (p - KPc) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u))
+                     : buf_ld16(rsv, (p - KPc) * 16u, static_cast<uint32_t>(c) * (kC * DV * 2u));
+    }
+  };
+  auto store = [&](uint16_t* buf, const u32x4 (&r)[LPT]) {
+    int t = tid;
+    asm volatile("" : "+v"(t));
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int p = t + i * NT;
+      uint16_t* dst;
+      if (i * NT < KPc) {
+        dst = buf + (p / (M / 8)) * MP + (p % (M / 8)) * 8;
+      } else {
+        const int pp = p - KPc;
+        dst = buf + kC * MP + (pp / (DV / 8)) * VP + (pp % (DV / 8)) * 8;
+      }
+      st16(dst, r[i]);
+    }
+  };
+  // X_Q rows of block blk (64 rows from the segment's row 64 blk)
+  auto load_x = [&](int blk, u32x4 (&r)[LX]) {
+#pragma unroll
+    for (int i = 0; i < LX; ++i)
+      r[i] = G::STREAM_NT ? buf_ld16_nt(rsx, (tid + i * NT) * 16u, static_cast<uint32_t>(blk) * (G::RB * D * 2u))
+                   : buf_ld16(rsx, (tid + i * NT) * 16u, static_cast<uint32_t>(blk) * (G::RB * D * 2u));
+  };
+  auto store_x = [&](const u32x4 (&r)[LX]) {
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+      const int p = tid + i * NT;
+      st16(Xs + (p / (D / 8)) * XP + (p % (D / 8)) * 8, r[i]);
+    }
+  };
+
+  // Projection of the block in Xs into Qb: feature block w, both 32-row
+  // tiles. Loop order r, ks, j: each X fragment pair is read once per (r, ks)
+  // and feeds P Theta fragments; Theta fragments stream TPD ahead.
+  auto project = [&]() {
+    auto toff = [](int f) {  // byte offset of the f-th fragment in loop order
+      const int r = f / (KS * P), ks = (f / P) % KS, j = f % P;
+      return static_cast<uint32_t>(((r * P + j) * KS + ks) * 1024);
+    };
+    // lane-dependent bases pass through an empty asm: hoisted out of the block
+    // loop, every derived address of the unrolled projection stays live
+    uint32_t tl = lane * 16u;
+    asm volatile("" : "+v"(tl));
+    int xl = c32 * XP + 8 * hh;
+    asm volatile("" : "+v"(xl));
+    const uint16_t* xb = Xs + xl;
+    bf16x8 tf[TPD];
+#pragma unroll
+    for (int f = 0; f < TPD; ++f) tf[f] = as_bf16x8(buf_ld16(rst, tl, toff(f)));
+    f32x16 sum[2] = {zero16(), zero16()};
+#pragma unroll
+    for (int r = 0; r < T; ++r) {
+      f32x16 acc[P][2];
+#pragma unroll
+      for (int j = 0; j < P; ++j) acc[j][0] = acc[j][1] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        // X rows 0..31 and 32..63 of the block, k = 16 ks + 8 hh .. +7
+        const bf16x8 x0 = as_bf16x8(ld16(xb + ks * 16));
+        const bf16x8 x1 = as_bf16x8(ld16(xb + 32 * XP + ks * 16));
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const int f = (r * KS + ks) * P + j;
+          const bf16x8 ta = tf[f % TPD];
+          if (f + TPD < NFR) tf[f % TPD] = as_bf16x8(buf_ld16(rst, tl, toff(f + TPD)));
+          acc[j][0] = mfma32x32x16(ta, x0, acc[j][0]);
+          acc[j][1] = mfma32x32x16(ta, x1, acc[j][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // Hadamard product over j, sum over r (the feature-map kernel's order)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        if constexpr (P == 1) {
+          sum[rt] += acc[0][rt];
+        } else {
+          f32x16 prod = acc[0][rt];
+#pragma unroll
+          for (int j = 1; j + 1 < P; ++j) prod *= acc[j][rt];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) sum[rt][e] = fmaf(prod[e], acc[P - 1][rt][e], sum[rt][e]);
+        }
+      }
+      // the rank's epilogue happens here: left alone, the compiler sinks every
+      // rank's products below the last rank's MFMAs and keeps all T ranks'
+      // accumulators live at once
+      asm volatile("" : "+v"(sum[0]), "+v"(sum[1]));
+    }
+    // square, round to bf16, regroup so each lane holds 16 contiguous bytes of
+    // its row (lanes c32 and c32 + 32 share row c32), store into the block buffer
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      f32x16 x = sum[rt];
+      if (square) x *= x;
+      uint32_t wv[4][2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[i][0] = pack_bf16x2(x[4 * i], x[4 * i + 1]);
+        wv[i][1] = pack_bf16x2(x[4 * i + 2], x[4 * i + 3]);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        swap_halves(wv[0][e], wv[1][e]);
+        swap_halves(wv[2][e], wv[3][e]);
+      }
+      int ql = (rt * 32 + c32) * QPAD + w * 32 + 8 * hh;
+      asm volatile("" : "+v"(ql));
+      uint16_t* dst = Qb + ql;
+      st16(dst, u32x4{wv[0][0], wv[0][1], wv[1][0], wv[1][1]});
+      st16(dst + 16, u32x4{wv[2][0], wv[2][1], wv[3][0], wv[3][1]});
+    }
+  };
+
+  // one chunk, as attn_out32's causal ungated step, except that chunk c+1
+  // is requested at the start of chunk c (one ahead, into rc) and staged at
+  // its end: no chunk load is in flight during a projection, which leaves
+  // the projection its registers
+  auto step = [&](int c, int qrow, u32x4 (&rc)[LPT], f32x16& O) {
+    if (c + 1 < nch) load(c + 1, rc);
+    int lbase = (c & 1) * G::BUF;
+    asm volatile("" : "+v"(lbase));
+    int lim = c32 - 4 * hh;  // key 8i+4hh+e reaches query c32 iff 8i+e <= lim
+    asm volatile("" : "+v"(lim));
+    int qbase = qrow * QPAD;
+    asm volatile("" : "+v"(qbase));
+    const uint16_t* Qs = Qb + qbase;
+    const uint16_t* Ks = cbuf + lbase;
+    const uint16_t* Vs = Ks + kC * MP;
+    int exoff = (c & 1) * G::EXW;
+    asm volatile("" : "+v"(exoff));
+    float* ex = exbase + exoff;
+    float* xo = ex;
+    float* part = ex + G::XO;
+    float* rsum = part + G::PART;
+
+    O = zero16();
+    f32x16 D2 = zero16();
+    if (half == 0) {
+      // masked A^T = phi_K phi_Q^T (keys x queries); reads AD k-steps ahead
+      constexpr int KSA = M / 16, AD = KSA < 3 ? KSA : 3;
+      f32x16 At = zero16();
+      bf16x8 fk[AD], fq[AD];
+#pragma unroll
+      for (int i = 0; i < AD; ++i) {
+        fk[i] = frag_nat(Ks, MP, 0, i * 16, lane);
+        fq[i] = frag_nat(Qs, QPAD, 0, i * 16, lane);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSA; ++ks) {
+        const bf16x8 ka = fk[ks % AD], qb = fq[ks % AD];
+        if (ks + AD < KSA) {
+          fk[ks % AD] = frag_nat(Ks, MP, 0, (ks + AD) * 16, lane);
+          fq[ks % AD] = frag_nat(Qs, QPAD, 0, (ks + AD) * 16, lane);
+        }
+        At = mfma32x32x16(ka, qb, At);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (8 * i + e > lim) At[4 * i + e] = 0.f;  // key after query
+      bf16x8 afr[2];
+      afr[0] = acc_frag(At, 0);
+      afr[1] = acc_frag(At, 1);
+      if (a.normalize && dvt == 0) {  // row sums of the rounded weights A V uses
+        float rs = 0.f;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 u = __builtin_bit_cast(u32x4, afr[hf]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            rs += __uint_as_float(u[q] << 16) + __uint_as_float(u[q] & 0xFFFF0000u);
+        }
+        rs += __shfl_xor(rs, 32);
+        if (hh == 0) rsum[c32] = rs;
+      }
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks)
+        O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {  // partial phi_Q S over this wave's feature half; phi_Q . z over its z tile
+      constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
+      bf16x8 qf[QD];
+#pragma unroll
+      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
+#pragma unroll
+      for (int idx = 0; idx < NQ; ++idx) {
+        const int j = idx >> 1, hf = idx & 1;
+        const bf16x8 qa = qf[idx % QD];
+        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
+        O = mfma32x32x16(qa, acc_frag(S[j], hf), O);
+        if (a.normalize && has_z && j == zj) D2 = mfma32x32x16(qa, acc_frag(Z, hf), D2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {  // publish: the 16 rows the partner wave finishes, and the z partial
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xo[(w * 8 + e) * 64 + lane] = pick(O[8 + e], O[e], half == 0);
+      if (a.normalize && has_z && c32 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[(8 * i + 4 * hh + e) * 8 + w] = D2[4 * i + e];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {  // S += phi_K^T V, z += phi_K^T 1; phi_K reads run KD ahead
+      constexpr int NK = (kC / 16) * FH, KD = NK < 2 ? NK : 2;
+      bf16x8 kf[KD];
+#pragma unroll
+      for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FH) * 16, (f0 + i % FH) * 32, lane);
+      bf16x8 vb[kC / 16];
+#pragma unroll
+      for (int ks = 0; ks < kC / 16; ++ks) vb[ks] = frag_tr(Vs, VP, ks * 16, dvt * 32, lane);
+#pragma unroll
+      for (int idx = 0; idx < NK; ++idx) {
+        const int ks = idx / FH, j = idx % FH;
+        const bf16x8 ka = kf[idx % KD];
+        if (idx + KD < NK)
+          kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FH) * 16, (f0 + (idx + KD) % FH) * 32, lane);
+        S[j] = mfma32x32x16(ka, vb[ks], S[j]);
+        if (has_z && j == zj) Z = mfma32x32x16(ka, ones, Z);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < nch) store(cbuf + ((c + 1) & 1) * G::BUF, rc);
+  };
+  // finish rows 16 half .. +15 of chunk c (after the chunk's barrier)
+  auto finish = [&](int c, const f32x16& O) {
+    int exoff = (c & 1) * G::EXW;
+    asm volatile("" : "+v"(exoff));
+    const float* ex = exbase + exoff;
+    const float* xo = ex;
+    const float* part = ex + G::XO;
+    const float* rsum = part + G::PART;
+    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+    const int kept = half == 0 ? 0 : 8;
+    const int partner = (1 - half) * NWD + dvt;
+    float val[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
+    if (a.normalize) {
+      float den[8];
+      u32x4 lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
+        lo[e] = ld16(part + q * 8);
+        hi[e] = ld16(part + q * 8 + 4);
+        den[e] = a.delta + rsum[q];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv[8] = {__uint_as_float(lo[e][0]), __uint_as_float(lo[e][1]),
+                             __uint_as_float(lo[e][2]), __uint_as_float(lo[e][3]),
+                             __uint_as_float(hi[e][0]), __uint_as_float(hi[e][1]),
+                             __uint_as_float(hi[e][2]), __uint_as_float(hi[e][3])};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int d = 0; d < FH && d < NWD; ++d) den[e] += pv[hf * NWD + d];
+        val[e] *= __builtin_amdgcn_rcpf(den[e]);
+      }
+    }
+    float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
+    if (c0 + kC <= t1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV] = val[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * ((kept + e) >> 2) + (e & 3);
+        if (c0 + r + 4 * hh < t1) orow[r * DV] = val[e];
+      }
+    }
+  };
+
+  u32x4 rc[LPT], rx[LX];
+  load(0, rc);
+  load_x(0, rx);
+#pragma unroll
+  for (int j = 0; j < FH; ++j) asm volatile("" : "+v"(S[j]));
+  asm volatile("" : "+v"(Z));
+  store(cbuf, rc);
+  store_x(rx);
+  __syncthreads();
+  // Block blk: project its 64 rows (Xs -> Qb), barrier, then its two chunks.
+  // The next block's X rows are loaded during the first chunk and stored
+  // before that chunk's barrier (Xs is free once the projection's barrier
+  // has passed); Qb is rewritten only after the second chunk's barrier, when
+  // no wave reads it any more.
+  const int nblk = (nch + 1) / 2;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int c = 2 * blk;
+    project();
+    __syncthreads();
+    if (blk + 1 < nblk) load_x(blk + 1, rx);
+    {
+      f32x16 O;
+      step(c, 0, rc, O);
+      if (blk + 1 < nblk) store_x(rx);
+      __syncthreads();
+      finish(c, O);
+    }
+    if (c + 1 < nch) {
+      f32x16 O;
+      step(c + 1, kC, rc, O);
+      __syncthreads();
+      finish(c + 1, O);
+    }
+  }
+}
+
 // Chunk-local inclusive sums of the log gates: L[bh][t] = sum of g[bh][t']
 // over t' from the start of t's 32-token chunk (chunks start at multiples of
 // 32) to t, rows gl_ld(n) apart. The padding t in [n, gl_ld(n)) is written
@@ -778,6 +1234,24 @@ hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH(GATED ? "attn_out_gated" : "attn_out_bf16", st, kern, grid, dim3(G::NT), lds, st,
                a, q, k, v, state, ss, sb, out, den, outb, ldo, vld);
+  return hipGetLastError();
+}
+
+template <int M, int DV, int D, int P, int T>
+hipError_t launch_fq_t(const AttnShape& s, const uint16_t* xq, const uint16_t* thpk,
+                       int64_t pk_hstride, int64_t H, int square, const uint16_t* k,
+                       const uint16_t* v, const float* state, int64_t ss, int64_t sb, float* out,
+                       hipStream_t st) {
+  using G = Fq32Geom<M, DV, D, P, T>;
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, nullptr, nullptr};
+  const size_t lds = G::lds_bytes();
+  auto* kern = attn_out32_fq<M, DV, D, P, T>;
+  const hipError_t e = allow_lds(kern, lds);
+  if (e != hipSuccess) return e;
+  if (s.BH * s.nseg > 0x7fffffffLL) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(s.BH * s.nseg));  // one workgroup per (segment, sequence)
+  LLOPS_LAUNCH("attn_out_fq", st, kern, grid, dim3(G::NT), lds, st, a, xq, thpk, pk_hstride, H,
+               square, k, v, state, ss, sb, out);
   return hipGetLastError();
 }
 
@@ -878,6 +1352,33 @@ hipError_t launch_attn_out32_to(const AttnShape& s, const uint16_t* phiq, const 
     case 256128: return launch_out_om<256, 128>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
     case 128064: return launch_out_om<128, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
     case 64064: return launch_out_om<64, 64>(s, phiq, phik, v, state, st_seg, st_bh, out, outb, ldo, rev, st, vld);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// (d, p, t) of the fused output pass per (m, dv): m = 2 dv, one 32-feature
+// block per wave
+int fq_key(const AttnShape& s, int d, int p, int t) {
+  if (!s.causal) return 0;
+  const int k = key32(s);
+  if (k == 256128 && d == 128 && p == 2 && t == 4) return 1;
+  if (k == 128064 && d == 64 && p == 3 && t == 8) return 2;
+  return 0;
+}
+
+bool attn32_fq_supported(const AttnShape& s, int d, int p, int t) {
+  // X rows of a segment are addressed through a 32-bit buffer view
+  return fq_key(s, d, p, t) != 0 && s.seg_len * d * 2 < (int64_t{1} << 31);
+}
+
+hipError_t launch_attn_out32_fq(const AttnShape& s, int d, int p, int t, const uint16_t* xq,
+                                const uint16_t* thpk, int64_t pk_hstride, int64_t H, int square,
+                                const uint16_t* phik, const uint16_t* v, const float* state,
+                                int64_t st_seg, int64_t st_bh, float* out, hipStream_t st) {
+  if (!attn32_fq_supported(s, d, p, t) || H < 1) return hipErrorInvalidValue;
+  switch (fq_key(s, d, p, t)) {
+    case 1: return launch_fq_t<256, 128, 128, 2, 4>(s, xq, thpk, pk_hstride, H, square, phik, v, state, st_seg, st_bh, out, st);
+    case 2: return launch_fq_t<128, 64, 64, 3, 8>(s, xq, thpk, pk_hstride, H, square, phik, v, state, st_seg, st_bh, out, st);
     default: return hipErrorInvalidValue;
   }
 }

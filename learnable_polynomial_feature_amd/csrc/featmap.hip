@@ -785,6 +785,19 @@ bool try_fast(const FeatShape& s, const FeatJob* jobs, int njobs, hipStream_t st
 
 }  // namespace
 
+hipError_t launch_pack_theta(const FeatShape& s, const void* theta, void* pk, hipStream_t st) {
+  if (!fast_key(s) || small_rows(s) || !theta || !pk) return hipErrorInvalidValue;
+  const int64_t th_heads = s.theta_per_head ? s.H : 1;
+  const int64_t total = th_heads * s.p * s.t * s.d * s.m / 8;
+  PackArgs pa{};
+  pa.th[0] = static_cast<const uint16_t*>(theta);
+  pa.pk[0] = static_cast<uint16_t*>(pk);
+  LLOPS_LAUNCH("pack_theta", st, pack_theta_kernel,
+               dim3(static_cast<unsigned>((total + 255) / 256), 1u), dim3(256), 0, st, pa, total,
+               s.p, s.t, s.d, s.m);
+  return hipGetLastError();
+}
+
 size_t featmap_pack_bytes(const FeatShape& s) {
   if (!fast_key(s) || small_rows(s)) return 0;
   const int64_t th_heads = s.theta_per_head ? s.H : 1;

@@ -48,6 +48,10 @@ struct FeatShape {
 // unrolled bf16 kernels read (0 when the shape takes the generic kernel).
 size_t featmap_pack_bytes(const FeatShape& s);
 
+// Fragment-order copy of one Theta set (the layout the 256-row-tile kernels
+// read) into pk (featmap_pack_bytes() bytes); hipErrorInvalidValue when the
+// shape has no unrolled kernel or takes the few-row path.
+hipError_t launch_pack_theta(const FeatShape& s, const void* theta, void* pk, hipStream_t st);
 // bf16 inputs on MFMA; runs `njobs` (1 or 2) jobs of the same shape in one launch.
 hipError_t launch_featmap_bf16(const FeatShape& s, const FeatJob* jobs, int njobs,
                                hipStream_t st);
@@ -155,6 +159,16 @@ hipError_t launch_seg_state32(const AttnShape& a, const uint16_t* phik, const ui
 hipError_t launch_attn_out32(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,
                              const uint16_t* v, const float* state, int64_t state_seg_stride,
                              int64_t state_bh_stride, float* out, hipStream_t st);
+// The causal output pass with phi_Q projected inside it (phi_Q never leaves
+// the chip): X_Q [BH][n][d] bf16 and Theta_Q in fragment order (pack_theta's
+// layout, heads pk_hstride elements apart, 0 = shared) replace phi_Q. Shapes:
+// (m, dv, d, p, t) in {(256, 128, 128, 2, 4), (128, 64, 64, 3, 8)}.
+bool attn32_fq_supported(const AttnShape& a, int d, int p, int t);
+hipError_t launch_attn_out32_fq(const AttnShape& a, int d, int p, int t, const uint16_t* xq,
+                                const uint16_t* thpk, int64_t pk_hstride, int64_t H, int square,
+                                const uint16_t* phik, const uint16_t* v, const float* state,
+                                int64_t state_seg_stride, int64_t state_bh_stride, float* out,
+                                hipStream_t st);
 // The same pass writing its rows elsewhere: to outb (bf16, RNE; rows ldo
 // elements apart, e.g. a column slice of a wider row) when outb is set, else
 // to out; rev = 1 (causal only): row t of the pass goes to row n - 1 - t.
