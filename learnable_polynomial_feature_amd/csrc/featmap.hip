@@ -570,12 +570,28 @@ __global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
   static_assert(PT % 2 == 0, "Theta rows need an even block count to stay conflict free");
   extern __shared__ __align__(16) uint16_t smem[];
   uint16_t* Ts = smem;           // [D][TW]: Theta_{j,r}[k][block] at column (j*T + r) * 32
-  const FeatJob job = a.job[blockIdx.z];
+  // XCD-aware work order: the workgroups of one (head, job) pair -- one per
+  // 32-feature block -- go to one XCD (workgroups reach the 8 XCDs round
+  // robin, id % 8), so the 128-byte Theta rows the neighbouring blocks each
+  // read half of, and the pair's X rows, are fetched once into that XCD's L2
+  const int FB = a.m / 32;
+  const int64_t pairs = static_cast<int64_t>(gridDim.x) / FB;
+  const int64_t id = blockIdx.x;
+  int64_t pair;
+  int fb;
+  if (pairs % 8 == 0) {
+    const int64_t k = id / 8;
+    pair = (id % 8) * (pairs / 8) + k / FB;
+    fb = static_cast<int>(k % FB);
+  } else {
+    pair = id / FB;
+    fb = static_cast<int>(id % FB);
+  }
+  const FeatJob job = a.job[pair / a.H];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
-  const int fb = blockIdx.x;
-  const int64_t h = blockIdx.y;
+  const int64_t h = pair % a.H;
   const int64_t R = a.B * a.n;
 
   const uint16_t* th = static_cast<const uint16_t*>(job.theta) + h * a.th_hstride;
@@ -673,7 +689,8 @@ hipError_t launch_small_t(const FeatShape& s, const FeatJob* jobs, int njobs, hi
   auto* k = featmap_small<D, P, T, OUT_BF16>;
   const hipError_t e = allow_lds(k, G::lds_bytes());
   if (e != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>(s.m / 32), static_cast<unsigned>(s.H), njobs);
+  // one workgroup per (32-feature block, head, job), ordered in the kernel
+  dim3 grid(static_cast<unsigned>(static_cast<int64_t>(s.m / 32) * s.H * njobs));
   LLOPS_LAUNCH("featmap_bf16", st, k, grid, dim3(256), G::lds_bytes(), st, a);
   return hipGetLastError();
 }
