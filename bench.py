@@ -293,17 +293,39 @@ def bench_config(w, steps, warmup, torch, lib):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    timer = lib.KernelTimer(capacity=8 * steps)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    # calls back to back (host launch work included), then the kernels timed
+    # one by one in a second pass (their events would sit between them)
+    t0.record()
+    for _ in range(steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    eager_ms = t0.elapsed_time(t1) / steps
+    timer = lib.KernelTimer(capacity=8 * steps)
     with timer:
-        t0.record()
         for _ in range(steps):
             call()
-        t1.record()
     torch.cuda.synchronize()
     kern = {k: sum(v) / len(v) for k, v in timer.durations_ms().items()}
-    return t0.elapsed_time(t1) / steps, kern
+    # one call captured as a HIP graph and replayed: no host work per call
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        call()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph_ms = t0.elapsed_time(t1) / steps
+    del graph
+    return eager_ms, kern, graph_ms
 
 
 def featmap_variants(steps, torch, lib):
@@ -582,7 +604,7 @@ def config_lines(steps, torch, lib):
     for name in ("tiny_noncausal_f32", "causal_p2_m64", "causal_p3_m128"):
         w = WORKLOADS[name]
         log(f"config {name}")
-        ms, kern = bench_config(w, steps, 3, torch, lib)
+        ms, kern, gms = bench_config(w, steps, 3, torch, lib)
         fl = attention_flops(w)
         tf = fl / (ms * 1e-3) / 1e12
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -590,7 +612,12 @@ def config_lines(steps, torch, lib):
                      "tokens_per_s": round(w.batch * w.n / (ms * 1e-3), 1),
                      "algorithmic_tflop": round(fl / 1e12, 5), "achieved_tflops": round(tf, 3),
                      "peak_tflops": peak, "frac": round(tf / peak, 5),
-                     "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
+                     "kernel_ms": {k: round(v, 4) for k, v in kern.items()},
+                     "kernel_sum_us": round(sum(kern.values()) * 1e3, 2),
+                     "graph": {"us_per_call": round(gms * 1e3, 2),
+                               "tokens_per_s": round(w.batch * w.n / (gms * 1e-3), 1),
+                               "frac": round(fl / (gms * 1e-3) / 1e12 / peak, 5),
+                               "note": "one call captured as a HIP graph and replayed"}}
     return res
 
 
@@ -789,6 +816,29 @@ def cpu_baseline_decode(w, sample, budget_s):
                       f"x{w.batch * w.heads}/{done}; fp64 numpy oracle"}
 
 
+def mfma_calibration(torch, size=8192, reps=10):
+    """What a plain dense bf16 matrix product (torch.matmul, hipBLASLt)
+    reaches on this board under its power cap: context for the MFMA rooflines
+    (the nominal 2.5 PFLOP/s assumes 2.4 GHz)."""
+    a = torch.randn(size, size, device="cuda").to(torch.bfloat16)
+    b = torch.randn(size, size, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        a @ b
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    tf = 2.0 * size ** 3 / (ms * 1e-3) / 1e12
+    del a, b
+    return {"op": f"torch.matmul bf16 {size}x{size}x{size}", "ms": round(ms, 4),
+            "achieved": round(tf, 1), "unit": "TFLOP/s", "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=3):
     """A plain device-to-device copy of known size: under rocprofv3 --pmc its
     FETCH_SIZE / WRITE_SIZE read what `nbytes` of HBM traffic reads as."""
@@ -935,6 +985,9 @@ def main():
         line["linattn_backward"] = linattn_backward(3, torch, lib)
         log("attention backward from an initial state")
         line["state_backward"] = state_backward(3, torch, lib)
+    if not args.no_configs:
+        log("dense bf16 matmul calibration")
+        line["mfma_calibration"] = mfma_calibration(torch)
     if not args.no_cpu_baseline:
         # the oracle timed on this host beside every workload's GPU figure
         log("cpu baseline (fp64 oracle)")

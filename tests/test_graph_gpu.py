@@ -62,3 +62,52 @@ def test_decode_graph_replays_equal_eager(lib, gated):
         assert torch.equal(outs, want[0]), rep
         assert torch.equal(S, want[1]) and torch.equal(z, want[2]), rep
         _ = (S * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_causal_graph_replays_equal_eager(lib, fused, monkeypatch):
+    """A whole causal forward call (feature maps, segment passes, scan, output
+    pass) captured once and replayed three times, with eager work between the
+    replays, equals the eager call bit for bit; on the two-kernel path and on
+    the fused output pass."""
+    if fused:
+        monkeypatch.setenv("LLOPS_FUSED_Q", "1")
+    else:
+        monkeypatch.delenv("LLOPS_FUSED_Q", raising=False)
+    w = Workload("graph_causal", batch=1, heads=4, n=3000, d=128, dv=128, p=2, t=4, m=256,
+                 dtype="bf16", causal=True, square=True, normalize=True, delta=1e-6, chunk=64)
+    x = generate(w)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    kw = dict(square=True, normalize=True, delta=1e-6, chunk=64)
+    shape = lib.make_shape(batch=1, heads=4, n=3000, d=128, dv=128, m=256, p=2, t=4, square=1,
+                           normalize=1, delta=1e-6, chunk=64)
+    ws = torch.empty(lib.llops_workspace_bytes(shape, lib.ENTRY_CAUSAL), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((1, 4, 3000, 128), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((1, 4, 256, 128), dtype=torch.float32, device="cuda")
+    zf = torch.empty((1, 4, 256), dtype=torch.float32, device="cuda")
+    args = (g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"])
+
+    def call():
+        lib.llops_linattn_causal_fwd(*args, out=out, S_final=Sf, z_final=zf, workspace=ws, **kw)
+
+    announce(f"causal graph vs eager, fused={fused}")
+    call()
+    torch.cuda.synchronize()
+    want = (out.clone(), Sf.clone(), zf.clone())
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=cap):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        Sf.zero_()
+        zf.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want[0]), rep
+        assert torch.equal(Sf, want[1]) and torch.equal(zf, want[2]), rep
+        _ = (out * 2).sum().item()  # eager work between replays
