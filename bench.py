@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU budget of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--power", action="store_true",
+                    help="also sample the board's power (amdgpu hwmon sysfs) while the causal "
+                         "step loops on each path and at idle: watts and joules per step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes)")
@@ -816,6 +819,66 @@ def cpu_baseline_decode(w, sample, budget_s):
                       f"x{w.batch * w.heads}/{done}; fp64 numpy oracle"}
 
 
+def _power_node(torch):
+    """The amdgpu hwmon power reading (microwatts) of cuda:0's PCI device, or
+    None when sysfs does not expose it."""
+    import glob
+    props = torch.cuda.get_device_properties(0)
+    bus = getattr(props, "pci_bus_id", None)
+    dev = getattr(props, "pci_device_id", None)
+    dom = getattr(props, "pci_domain_id", 0) or 0
+    cands = []
+    if bus is not None and dev is not None:
+        base = f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0/hwmon/hwmon*/"
+        cands += sorted(glob.glob(base + "power1_average")) + sorted(glob.glob(base + "power1_input"))
+    if not cands:  # a single amdgpu card in sysfs is this one
+        nodes = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_average")) or \
+            sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        if len(nodes) == 1:
+            cands = nodes
+    for f in cands:
+        try:
+            int(open(f).read())
+            return f
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def power_account(node, fn, steps_per_call, secs, torch):
+    """Average board power (W) while fn() runs back to back for about secs,
+    sampled every 5 ms from another thread; joules per step = W x s/step."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append(int(open(node).read()) * 1e-6)
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.005)
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    calls = 0
+    while time.perf_counter() - t0 < secs:
+        fn()
+        calls += 1
+        if calls % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    steps = calls * steps_per_call
+    watts = sum(samples[len(samples) // 5:]) / max(1, len(samples) - len(samples) // 5)
+    return {"watts": round(watts, 1), "ms_per_step": round(wall / steps * 1e3, 4),
+            "joules_per_step": round(watts * wall / steps, 4), "samples": len(samples)}
+
+
 def mfma_calibration(torch, size=8192, reps=10):
     """What a plain dense bf16 matrix product (torch.matmul, hipBLASLt)
     reaches on this board under its power cap: context for the MFMA rooflines
@@ -961,6 +1024,36 @@ def main():
                 "bytes_per_launch": decode_state_bytes(wd)},
             "gated": dgated,
         }
+    if args.power:
+        node = _power_node(torch)
+        if node is None:
+            line["power"] = {"note": "no amdgpu hwmon power node for this device"}
+        else:
+            log(f"power: {node}")
+            out_p = torch.empty((w.batch, w.heads, w.n, w.dv), dtype=torch.float32, device="cuda")
+            kwp = dict(square=w.square, normalize=w.normalize, delta=w.delta, chunk=w.chunk,
+                       out=out_p, workspace=cws)
+            idle = []
+            for _ in range(100):
+                idle.append(int(open(node).read()) * 1e-6)
+                time.sleep(0.005)
+            acct = {"node": node, "idle_watts": round(sum(idle) / len(idle), 1)}
+            try:
+                acct["cap_watts"] = int(open(os.path.join(os.path.dirname(node),
+                                                          "power1_cap")).read()) * 1e-6
+            except (OSError, ValueError):
+                pass
+            prev = os.environ.get("LLOPS_FUSED_Q")
+            for label, flag in (("two_kernel", "0"), ("fused", "1"), ("two_kernel_again", "0")):
+                os.environ["LLOPS_FUSED_Q"] = flag
+                acct[label] = power_account(
+                    node, lambda: lib.llops_linattn_causal_fwd(*cargs, **kwp), 1, 8.0, torch)
+            if prev is None:
+                del os.environ["LLOPS_FUSED_Q"]
+            else:
+                os.environ["LLOPS_FUSED_Q"] = prev
+            line["power"] = acct
+            del out_p
     if "attn_out_fq" in kern:
         log("two-kernel causal path")
         line["two_kernel_path"] = bench_other_path(w, 10, torch, lib, cargs, cws, False)
