@@ -619,29 +619,26 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
 #pragma unroll
       for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
-      if (a.normalize) {
-        // partials of the z-tile owners (d < m/64 in each half), fixed order
-        float den[8];
-        u32x4 lo[8], hi[8];
+      if (a.normalize && !DENOUT) {
+        // row c32's denominator in every lane of each 32-lane half (delta,
+        // the row sum of the rounded A, then the z-tile owners' partials in
+        // wave order), then each lane takes its own eight rows' from the lanes
+        // that hold them (a lane permute, no LDS traffic)
+        float dq = a.delta + (CAUSAL ? rsum[c32] : 0.f);
+        const u32x4 lo = ld16(part + c32 * 8), hi = ld16(part + c32 * 8 + 4);
+        const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
+                             __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                             __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                             __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
-          lo[e] = ld16(part + q * 8);
-          hi[e] = ld16(part + q * 8 + 4);
-          den[e] = a.delta + (CAUSAL ? rsum[q] : 0.f);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv[8] = {__uint_as_float(lo[e][0]), __uint_as_float(lo[e][1]),
-                               __uint_as_float(lo[e][2]), __uint_as_float(lo[e][3]),
-                               __uint_as_float(hi[e][0]), __uint_as_float(hi[e][1]),
-                               __uint_as_float(hi[e][2]), __uint_as_float(hi[e][3])};
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int d = 0; d < FH && d < NWD; ++d) den[e] += pv[hf * NWD + d];
           // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
-          if constexpr (!DENOUT) val[e] *= __builtin_amdgcn_rcpf(den[e]);
+          val[e] *= __builtin_amdgcn_rcpf(__shfl(dq, q));
         }
       }
       if constexpr (DENOUT) {
@@ -1110,27 +1107,21 @@ void attn_out32_fq(Seg32Args a, const uint16_t* __restrict__ xq,
     for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
 #pragma unroll
     for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
-    if (a.normalize) {
-      float den[8];
-      u32x4 lo[8], hi[8];
+    if (a.normalize) {  // as attn_out32's finish: row c32's denominator, then a lane permute
+      float dq = a.delta + rsum[c32];
+      const u32x4 lo = ld16(part + c32 * 8), hi = ld16(part + c32 * 8 + 4);
+      const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
+                           __uint_as_float(lo[2]), __uint_as_float(lo[3]),
+                           __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                           __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
-        lo[e] = ld16(part + q * 8);
-        hi[e] = ld16(part + q * 8 + 4);
-        den[e] = a.delta + rsum[q];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv[8] = {__uint_as_float(lo[e][0]), __uint_as_float(lo[e][1]),
-                             __uint_as_float(lo[e][2]), __uint_as_float(lo[e][3]),
-                             __uint_as_float(hi[e][0]), __uint_as_float(hi[e][1]),
-                             __uint_as_float(hi[e][2]), __uint_as_float(hi[e][3])};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int d = 0; d < FH && d < NWD; ++d) den[e] += pv[hf * NWD + d];
-        val[e] *= __builtin_amdgcn_rcpf(den[e]);
+        val[e] *= __builtin_amdgcn_rcpf(__shfl(dq, q));
       }
     }
     float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
