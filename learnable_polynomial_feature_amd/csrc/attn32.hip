@@ -70,6 +70,52 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* s) {
   return as_bf16x8(r);
 }
 
+// ---- finish of an output-pass chunk ----------------------------------------
+// A finishing wave keeps 16 of the chunk's 32 rows: element e (0..7) of lane
+// half hh is chunk row 8 * ((kept + e) / 4) + 4 * hh + e % 4, kept = 0 or 8.
+__device__ __forceinline__ int kept_row(int kept, int e, int hh) {
+  return 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
+}
+// The row whose denominator a lane forms: lane i of every 16-lane row takes
+// the row of element i % 8 of its half, so that a broadcast from lane e of
+// each 16-lane row (DPP row_newbcast, no LDS traffic) hands every lane the
+// denominator of its element e.
+__device__ __forceinline__ int den_row(int kept, int lane) {
+  return kept_row(kept, lane & 7, lane >> 5);
+}
+template <int E>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + E, 0xF, 0xF, false));
+}
+// val[e] *= the inverse denominator of element e's row (inv: den_row's)
+__device__ __forceinline__ void scale_rows(float (&val)[8], float inv) {
+  val[0] *= row_bcast<0>(inv);
+  val[1] *= row_bcast<1>(inv);
+  val[2] *= row_bcast<2>(inv);
+  val[3] *= row_bcast<3>(inv);
+  val[4] *= row_bcast<4>(inv);
+  val[5] *= row_bcast<5>(inv);
+  val[6] *= row_bcast<6>(inv);
+  val[7] *= row_bcast<7>(inv);
+}
+// Denominator of a chunk row: delta, then the row sum of the rounded masked
+// weights (rs), then the z-tile owners' partials (lo, hi: the row's 8 wave
+// slots; wave w = half * NWD + value tile) in wave order, first feature half
+// then second, NZ z tiles per half.
+template <int NWD, int NZ>
+__device__ __forceinline__ float den_sum(float delta, float rs, u32x4 lo, u32x4 hi) {
+  const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]), __uint_as_float(lo[2]),
+                       __uint_as_float(lo[3]), __uint_as_float(hi[0]), __uint_as_float(hi[1]),
+                       __uint_as_float(hi[2]), __uint_as_float(hi[3])};
+  float dq = delta + rs;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int d = 0; d < NZ; ++d) dq += pv[hf * NWD + d];
+  return dq;
+}
+
 // Gate sums of the 16 tokens 8i + 4hh + e (i, e < 4) this lane's fragments
 // cover (accumulator rows, P16 operand k-values), element 4i + e.
 __device__ __forceinline__ void gate_rows(const float* gls, int hh, float (&L)[16]) {
@@ -614,48 +660,27 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     {
       const int kept = half == 0 ? 0 : 8;
       const int partner = (1 - half) * NWD + dvt;
+      // one batch of LDS reads: the partner's partial rows, and for the
+      // denominator of row den_row its masked-weight row sum and z partials
+      // (read whether or not they are used: the batch costs one round trip)
       float val[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
+      const int rq = den_row(kept, lane);
+      const float rs = CAUSAL ? rsum[rq] : 0.f;
+      const u32x4 lo = ld16(part + rq * 8), hi = ld16(part + rq * 8 + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
       if (a.normalize && !DENOUT) {
-        // row c32's denominator in every lane of each 32-lane half (delta,
-        // the row sum of the rounded A, then the z-tile owners' partials in
-        // wave order), then each lane takes its own eight rows' from the lanes
-        // that hold them (a lane permute, no LDS traffic)
-        float dq = a.delta + (CAUSAL ? rsum[c32] : 0.f);
-        const u32x4 lo = ld16(part + c32 * 8), hi = ld16(part + c32 * 8 + 4);
-        const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
-                             __uint_as_float(lo[2]), __uint_as_float(lo[3]),
-                             __uint_as_float(hi[0]), __uint_as_float(hi[1]),
-                             __uint_as_float(hi[2]), __uint_as_float(hi[3])};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
-          // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
-          val[e] *= __builtin_amdgcn_rcpf(__shfl(dq, q));
-        }
+        // v_rcp_f32 (1 ulp) and a product: far inside the bf16 operands' error
+        scale_rows(val, __builtin_amdgcn_rcpf(den_sum<NWD, (FH < NWD ? FH : NWD)>(a.delta, rs, lo, hi)));
       }
       if constexpr (DENOUT) {
         // row q = lane of the first 32 lanes of wave 0: the same sum, in the
         // same order, from the exchange area (read only after the barrier)
         if (w == 0 && lane < kC && c0 + lane < t1) {
-          float dq = a.delta + (CAUSAL ? rsum[lane] : 0.f);
-          const u32x4 lo = ld16(part + lane * 8), hi = ld16(part + lane * 8 + 4);
-          const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
-                               __uint_as_float(lo[2]), __uint_as_float(lo[3]),
-                               __uint_as_float(hi[0]), __uint_as_float(hi[1]),
-                               __uint_as_float(hi[2]), __uint_as_float(hi[3])};
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
-          den_out[bh * a.n + c0 + lane] = dq;
+          den_out[bh * a.n + c0 + lane] = den_sum<NWD, (FH < NWD ? FH : NWD)>(
+              a.delta, CAUSAL ? rsum[lane] : 0.f, ld16(part + lane * 8), ld16(part + lane * 8 + 4));
         }
       }
       // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
@@ -1102,28 +1127,16 @@ void attn_out32_fq(Seg32Args a, const uint16_t* __restrict__ xq,
     const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
     const int kept = half == 0 ? 0 : 8;
     const int partner = (1 - half) * NWD + dvt;
-    float val[8];
+    float val[8];  // as attn_out32's finish: one batch of LDS reads
 #pragma unroll
     for (int e = 0; e < 8; ++e) val[e] = xo[(partner * 8 + e) * 64 + lane];
+    const int rq = den_row(kept, lane);
+    const float rs = rsum[rq];
+    const u32x4 lo = ld16(part + rq * 8), hi = ld16(part + rq * 8 + 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
-    if (a.normalize) {  // as attn_out32's finish: row c32's denominator, then a lane permute
-      float dq = a.delta + rsum[c32];
-      const u32x4 lo = ld16(part + c32 * 8), hi = ld16(part + c32 * 8 + 4);
-      const float pv[8] = {__uint_as_float(lo[0]), __uint_as_float(lo[1]),
-                           __uint_as_float(lo[2]), __uint_as_float(lo[3]),
-                           __uint_as_float(hi[0]), __uint_as_float(hi[1]),
-                           __uint_as_float(hi[2]), __uint_as_float(hi[3])};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int d = 0; d < FH && d < NWD; ++d) dq += pv[hf * NWD + d];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = 8 * ((kept + e) >> 2) + 4 * hh + (e & 3);
-        val[e] *= __builtin_amdgcn_rcpf(__shfl(dq, q));
-      }
-    }
+    if (a.normalize)
+      scale_rows(val, __builtin_amdgcn_rcpf(den_sum<NWD, (FH < NWD ? FH : NWD)>(a.delta, rs, lo, hi)));
     float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
     if (c0 + kC <= t1) {
 #pragma unroll
