@@ -58,6 +58,18 @@ constexpr int kGL = 2 * kC;  // LDS slots (uint16) of one chunk's 32 fp32 gate s
 // values start on a 128-byte boundary.
 __host__ __device__ __forceinline__ int64_t gl_ld(int64_t n) { return (n + kC - 1) / kC * kC; }
 
+// Smallest LDS row stride (bf16 elements) of at least `cols` whose byte
+// offset mod 256 (the 64 banks) is 2 * res or its mirror 256 - 2 * res (a
+// read touches the mirrored set of banks, so conflicts are the same). Which
+// residue a read pattern wants was measured per pattern: 16-byte row reads
+// 16 or 48 bytes; transposing reads 64 bytes; a block read both ways 48
+// bytes (1x and 2x).
+constexpr int lds_stride_at(int cols, int res) { return cols + ((res - cols) % 128 + 128) % 128; }
+constexpr int lds_stride(int cols, int res) {
+  return lds_stride_at(cols, res) < lds_stride_at(cols, 128 - res) ? lds_stride_at(cols, res)
+                                                                   : lds_stride_at(cols, 128 - res);
+}
+
 // Scale the 8 bf16 values of an operand fragment by s[0..7] (fp32 products,
 // rounded back to bf16 to nearest even).
 __device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float* s) {
@@ -352,10 +364,11 @@ struct Out32Geom {
   static constexpr int NT = NW * 64;
   static constexpr int FT = M / 32;
   static constexpr int FH = FT / 2;       // feature tiles per half
-  // row strides (elements): phi_K and V are read transposed (4 rows x 32 B
-  // per 16 lanes, conflict-free when rows shift by 8 banks); phi_Q only in
-  // row order (b64/b128 over 16 rows, conflict-free when rows shift by 4)
-  static constexpr int QPAD = M + 8, MP = M + 16, VP = DV + 16;
+  // row strides (elements): phi_Q is read in row order only (16-byte reads
+  // 1x, 8-byte 2x at 16 bytes mod 256); phi_K both in row order (A^T) and
+  // transposed (the state update): 1x and 2x at 48 bytes; V only transposed:
+  // 1x at 64 bytes
+  static constexpr int QPAD = M + 8, MP = lds_stride(M, 24), VP = lds_stride(DV, 32);
   static constexpr int BUF = kC * QPAD + kC * MP + kC * VP + (GATED ? kGL : 0);  // + gate sums
   static constexpr int QP = kC * M / 8;   // 16-byte pieces of one phi chunk
   static constexpr int VPc = kC * DV / 8;
@@ -364,6 +377,7 @@ struct Out32Geom {
   static constexpr int XO = NW * 8 * 64, PART = kC * 8, EXW = XO + PART + kC;
   static_assert(NW <= 8, "z partial slots");
   static constexpr size_t lds_bytes() { return 2ull * BUF * 2 + 2ull * EXW * 4; }
+  static_assert(lds_bytes() <= 160 * 1024, "LDS per workgroup");
   static_assert(FT % 2 == 0, "feature tiles split in two halves");
   static_assert(QP % NT == 0 && VPc % NT == 0, "chunk pieces split evenly over the threads");
 };
@@ -776,7 +790,7 @@ struct Fq32Geom {
   static constexpr int FH = FT / 2;
   static constexpr int RB = 2 * kC;        // rows per projected block
   static constexpr int KS = D / 16;        // 16-deep k-steps of the projection
-  static constexpr int QPAD = M + 8, MP = M + 16, VP = DV + 16;
+  static constexpr int QPAD = M + 8, MP = lds_stride(M, 24), VP = lds_stride(DV, 32);
   static constexpr int XP = D + 8;         // X rows 16 bytes apart mod 256: b128 reads conflict-free
   static constexpr int QB = RB * QPAD;     // phi_Q block buffer (elements)
   static constexpr int XB = RB * XP;       // X_Q block buffer
@@ -789,6 +803,7 @@ struct Fq32Geom {
   static constexpr int TPD = 4;            // Theta fragments in flight per wave
   static constexpr bool STREAM_NT = true;  // phi_K, V and X loads marked non-temporal
   static constexpr size_t lds_bytes() { return 2ull * (QB + XB + 2 * BUF) + 2ull * EXW * 4; }
+  static_assert(lds_bytes() <= 160 * 1024, "LDS per workgroup");
   static_assert(FT == NW, "one 32-feature block per wave in the projection");
   static_assert(D % 32 == 0 && FT % 2 == 0, "shape");
   static_assert(KPc % NT == 0 && VPc % NT == 0 && (RB * D / 8) % NT == 0, "even split");
