@@ -128,6 +128,19 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* base, int stride, int 
   return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
+// The same read with k in natural order (k = kbase + 8 * (lane / 32) + 0..7):
+// the 4-row groups start 8 rows apart per lane half instead of 4, so this
+// operand pairs with rows of the other operand read as 16 contiguous bytes.
+__device__ __forceinline__ bf16x8 frag_tr_nat(const uint16_t* base, int stride, int kbase,
+                                              int cbase, int lane) {
+  const int s = lane & 15, G = lane >> 4;
+  const int row = kbase + 8 * (G >> 1) + (s >> 2);
+  const int col = cbase + (G & 1) * 16 + 4 * (s & 3);
+  const uint2 lo = lds_tr64(base + row * stride + col);
+  const uint2 hi = lds_tr64(base + (row + 4) * stride + col);
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
 // A-style fragment with k in P16 order from row-major M[row][k] in LDS:
 // row = rbase + lane % 32, k = kbase + {4hh..4hh+3, 8+4hh..8+4hh+3}.
 __device__ __forceinline__ bf16x8 frag_p16(const uint16_t* base, int stride, int rbase, int kbase,

@@ -544,7 +544,7 @@ void featmap_fast(FastArgs a) {
 // once. A workgroup owns one 32-feature block of one head and every row: it
 // stages Theta_{j,r}[:, block] for all (j, r) side by side in LDS rows of d
 // (natural layout, 16-byte loads) and 32 rows of X per wave, and reads both
-// operands in P16 k-order (the Theta side with the transposing LDS read), so
+// operands in natural k-order (the Theta side with the transposing LDS read), so
 // Theta needs no fragment-order copy and no repacking launch.
 constexpr int kSmallRows = 1024;  // rows per head up to which this path runs
 
@@ -563,6 +563,14 @@ struct SmallGeom {
   static constexpr size_t lds_bytes() { return 1ull * D * TW * 2; }
 };
 
+// Row r of a head's flattened (batch, position) rows -> its row of the
+// [B][H][n] tensor, for r < 2^32 (a 32-bit division: the 64-bit one expands
+// to a long instruction sequence per call).
+__device__ __forceinline__ int64_t head_row(uint32_t r, uint32_t n, int64_t H, int64_t h) {
+  const uint32_t b = r / n;
+  return (static_cast<int64_t>(b) * H + h) * n + (r - b * n);
+}
+
 template <int D, int P, int T, bool OUT_BF16>
 __global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
   using G = SmallGeom<D, P, T>;
@@ -574,27 +582,49 @@ __global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
   // 32-feature block -- go to one XCD (workgroups reach the 8 XCDs round
   // robin, id % 8), so the 128-byte Theta rows the neighbouring blocks each
   // read half of, and the pair's X rows, are fetched once into that XCD's L2
-  const int FB = a.m / 32;
-  const int64_t pairs = static_cast<int64_t>(gridDim.x) / FB;
-  const int64_t id = blockIdx.x;
-  int64_t pair;
-  int fb;
+  // (32-bit index arithmetic: the grid has m/32 * H * jobs < 2^31 workgroups)
+  const uint32_t FB = static_cast<uint32_t>(a.m / 32);
+  const uint32_t pairs = gridDim.x / FB;
+  const uint32_t id = blockIdx.x;
+  uint32_t pair, fb;
   if (pairs % 8 == 0) {
-    const int64_t k = id / 8;
+    const uint32_t k = id / 8;
     pair = (id % 8) * (pairs / 8) + k / FB;
-    fb = static_cast<int>(k % FB);
+    fb = k % FB;
   } else {
     pair = id / FB;
-    fb = static_cast<int>(id % FB);
+    fb = id % FB;
   }
-  const FeatJob job = a.job[pair / a.H];
+  const uint32_t H32 = static_cast<uint32_t>(a.H);
+  const FeatJob job = a.job[pair / H32];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
-  const int64_t h = pair % a.H;
+  const int64_t h = pair % H32;
   const int64_t R = a.B * a.n;
 
   const uint16_t* th = static_cast<const uint16_t*>(job.theta) + h * a.th_hstride;
+  const uint16_t* X = static_cast<const uint16_t*>(job.X);
+  const uint32_t nr = static_cast<uint32_t>(a.n);  // R <= kSmallRows: rows fit 32 bits
+  // X fragments of 32 rows, straight from global memory in natural k-order:
+  // lane row t0 + c32, k = 16ks + 8hh + 0..7, one 16-byte load per k-step
+  // (rows clamped to R - 1 >= 0; zeroed past the end when taken). These
+  // loads are requests-bound (every instruction touches 32 rows), so the
+  // wave's first tile is issued ahead of Theta's loads and overlaps them.
+  auto issue_x = [&](int64_t t0, u32x4 (&xr)[KS]) {
+    const int64_t r = t0 + c32 < R ? t0 + c32 : R - 1;
+    const uint16_t* src = X + head_row(static_cast<uint32_t>(r), nr, a.H, h) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xr[ks] = ld16(src + ks * 16);
+  };
+  auto take_x = [&](int64_t t0, const u32x4 (&xr)[KS], bf16x8 (&xf)[KS]) {
+    const bool ok = t0 + c32 < R;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xf[ks] = as_bf16x8(ok ? xr[ks] : u32x4{0u, 0u, 0u, 0u});
+  };
+  const int64_t tw = static_cast<int64_t>(w) * 32;  // the wave's first row tile
+  u32x4 xr[KS];
+  issue_x(tw, xr);
   // all of a thread's Theta loads are issued before its first LDS store
   constexpr int TL = PT * D * 4 / 256;  // 16-byte pieces per thread
   static_assert((PT * D * 4) % 256 == 0, "Theta block splits evenly over the threads");
@@ -613,41 +643,26 @@ __global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
   }
   __syncthreads();
 
-  const uint16_t* X = static_cast<const uint16_t*>(job.X);
   uint8_t* out = static_cast<uint8_t*>(job.phi);
   constexpr int ESZ = OUT_BF16 ? 2 : 4;
-  for (int64_t t0 = static_cast<int64_t>(w) * 32; t0 < R; t0 += 4 * 32) {
-    // X fragments straight from global memory in P16 k-order: lane row
-    // t0 + c32, k = 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3} (zeros past the end)
+  for (int64_t t0 = tw; t0 < R; t0 += 4 * 32) {
+    if (t0 != tw) issue_x(t0, xr);
     bf16x8 xf[KS];
-    {
-      const int64_t r = t0 + c32 < R ? t0 + c32 : R - 1;
-      const int64_t b = r / a.n;
-      const uint16_t* src = X + ((b * a.H + h) * a.n + (r - b * a.n)) * D + 4 * hh;
-      u32x2 lo[KS], hi[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        lo[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16);
-        hi[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16 + 8);
-      }
-      const bool ok = t0 + c32 < R;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        xf[ks] = as_bf16x8(ok ? u32x4{lo[ks][0], lo[ks][1], hi[ks][0], hi[ks][1]} : u32x4{0u, 0u, 0u, 0u});
-    }
+    take_x(t0, xr, xf);
     f32x16 sum = zero16();
 #pragma unroll 1
     for (int r = 0; r < T; ++r) {
-      // Theta fragments of rank r, (j, ks) flattened, read two ahead (pinned)
+      // Theta fragments of rank r (natural k-order, as X's), (j, ks)
+      // flattened, read two ahead (pinned)
       bf16x8 fr[3];
-      fr[0] = frag_tr(Ts, TW, 0, r * 32, lane);
-      if (NF > 1) fr[1] = frag_tr(Ts, TW, (1 % KS) * 16, ((1 / KS) * T + r) * 32, lane);
+      fr[0] = frag_tr_nat(Ts, TW, 0, r * 32, lane);
+      if (NF > 1) fr[1] = frag_tr_nat(Ts, TW, (1 % KS) * 16, ((1 / KS) * T + r) * 32, lane);
       f32x16 prod, acc;
 #pragma unroll
       for (int fi = 0; fi < NF; ++fi) {
         const int j = fi / KS, ks = fi % KS;
         if (fi + 2 < NF)
-          fr[(fi + 2) % 3] = frag_tr(Ts, TW, ((fi + 2) % KS) * 16, (((fi + 2) / KS) * T + r) * 32, lane);
+          fr[(fi + 2) % 3] = frag_tr_nat(Ts, TW, ((fi + 2) % KS) * 16, (((fi + 2) / KS) * T + r) * 32, lane);
         acc = mfma32x32x16(xf[ks], fr[fi % 3], ks == 0 ? zero16() : acc);
         __builtin_amdgcn_sched_barrier(0);
         if (ks == KS - 1) prod = j == 0 ? acc : prod * acc;
@@ -662,8 +677,7 @@ __global__ __launch_bounds__(256) void featmap_small(SmallArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int64_t r = t0 + 8 * i + 4 * hh + e;
         if (r < R) {
-          const int64_t b = r / a.n;
-          uint8_t* dst = out + (((b * a.H + h) * a.n + (r - b * a.n)) * a.m + fb * 32 + c32) * ESZ;
+          uint8_t* dst = out + (head_row(static_cast<uint32_t>(r), nr, a.H, h) * a.m + fb * 32 + c32) * ESZ;
           if (OUT_BF16)
             *reinterpret_cast<uint16_t*>(dst) = f32_to_bf16(sum[4 * i + e]);
           else
@@ -686,6 +700,7 @@ hipError_t launch_small_t(const FeatShape& s, const FeatJob* jobs, int njobs, hi
   a.th_hstride = s.theta_per_head ? static_cast<int64_t>(P) * T * D * s.m : 0;
   a.square = s.square;
   if (s.H > 65535) return hipErrorInvalidValue;
+  if (s.B * s.n == 0) return hipSuccess;  // no rows (the kernel reads row R - 1 of a head)
   auto* k = featmap_small<D, P, T, OUT_BF16>;
   const hipError_t e = allow_lds(k, G::lds_bytes());
   if (e != hipSuccess) return e;
