@@ -227,8 +227,8 @@ llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* shape, const 
  * then llops_featmap_bwd on each side (paper Sec. 1 attention form; blog,
  * Performer section, and SLAY notes key design 3 for the normaliser; Theta is
  * learned end to end, notes' training strategy). The three sums are run as
- * causal linear attentions over bf16 features (dphi_K and dV over the
- * reversed sequence), so they carry the forward's bf16 rounding.
+ * causal linear attentions over bf16 features (dphi_K and dV as suffix sums,
+ * anti-causal passes), so they carry the forward's bf16 rounding.
  * in_dtype BF16 only; kernels exist for p = 2, t in {1, 4}, d in {64, 128},
  * m in {64, 128, 256}, dv % 16 == 0 and dv <= 128 (else LLOPS_ERR_UNSUPPORTED).
  * theta_q and theta_k may alias; their gradients are still returned apart.

@@ -177,10 +177,22 @@ WsLayout ws_layout(const llops_shape_t* s, int entry) {
 // totals instead.
 bool num_den_one_pass(const llops_shape_t* s, bool causal);
 
-BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
+bool on32(const llops_shape_t* s, bool causal, int M, int DV);
+
+// The causal backward's suffix sums (dphi_K and dV: key i >= query j) run as
+// anti-causal output passes on the 32x32x16 kernels when their in-place forms
+// apply (phi read in place, rows written in place); otherwise, and in the
+// gated backward, as causal passes over reversed copies of their operands.
+bool bwd_anti(const llops_shape_t* s) {
+  return on32(s, true, bwd_ma(s), bwd_w(s)) && on32(s, true, s->m, s->dv) &&
+         s->n * s->m * 2 < (int64_t{1} << 31);
+}
+
+BwdWs bwd_ws(const llops_shape_t* s, bool causal, bool gated = false) {
   BwdWs w{};
   const size_t R = static_cast<size_t>(s->batch * s->heads) * static_cast<size_t>(s->n);
   const size_t m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s);
+  const bool rev = causal && (gated || !bwd_anti(s));  // reversed copies needed
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -198,12 +210,12 @@ BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   w.den1 = take(s->normalize ? R * (one ? 1 : 16) * 4 : 0);
   w.ones = take(s->normalize && !one ? R * 16 * 2 : 0);
   w.a = take(R * MA * 2);
-  w.ra = take(causal ? R * MA * 2 : 0);
+  w.ra = take(rev ? R * MA * 2 : 0);
   w.b = take(R * MA * 2);
-  w.rb = take(causal ? R * MA * 2 : 0);
+  w.rb = take(rev ? R * MA * 2 : 0);
   w.rdnum = take(R * dv * 2);
-  w.rphq = take(causal ? R * m * 2 : 0);
-  w.rphk = take(causal ? R * m * 2 : 0);
+  w.rphq = take(rev ? R * m * 2 : 0);
+  w.rphk = take(rev ? R * m * 2 : 0);
   w.vp = take(R * W * 2);
   w.tmp = take(R * (W > dv ? W : dv) * 4);
   w.dphq = take(R * m * 2);
@@ -377,12 +389,16 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
                             const uint16_t* fq, const uint16_t* fk, const uint16_t* v, float* out,
                             float* seg, float* tot, hipStream_t st,
                             const float* S0init = nullptr, uint16_t* outb = nullptr, int ldo = 0,
-                            int rev = 0, int vld = 0) {
+                            int rev = 0, int vld = 0, bool anti = false) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
-  const llops::AttnShape a = attn_shape(&t, causal);
+  llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
   const bool mf32 = llops::attn32_supported(a);
   if ((outb || rev || vld) && !mf32) return hipErrorInvalidValue;
+  if (anti) {  // suffix sums: the scan from the last segment, chunks from the last
+    if (!causal || !mf32 || rev || S0init) return hipErrorInvalidValue;
+    a.anti = 1;
+  }
   hipError_t e = vld    ? llops::launch_seg_state32_v(a, fk, v, vld, seg, st)
                  : mf32 ? llops::launch_seg_state32(a, fk, v, seg, st)
                         : llops::launch_seg_state_bf16(a, fk, v, seg, st);
@@ -448,7 +464,7 @@ struct GBwdWs {
 
 GBwdWs gated_bwd_ws(const llops_shape_t* s) {
   GBwdWs w{};
-  w.b = bwd_ws(s, true);
+  w.b = bwd_ws(s, true, true);
   size_t off = w.b.total;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -932,26 +948,28 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     LLOPS_HIP(attn_on_features(s, causal, m, 16, phq, phk, u16(L.ones), den1, seg, tot, st, zinit),
               "attn den");
   }
-  // a = [dnum | dden | 0], b = [V | 1 | 0]; causal: also reversed copies
-  // and dnum reversed, non-causal: dnum in order
+  // a = [dnum | dden | 0], b = [V | 1 | 0]; with reversed copies (causal,
+  // off the anti-causal path) also ra, rb and dnum reversed, else dnum in order
+  const bool anti = causal && bwd_anti(s);
+  const bool rev = causal && !anti;
   uint16_t *a = u16(L.a), *b = u16(L.b), *dn = u16(L.rdnum);
-  uint16_t *ra = causal ? u16(L.ra) : nullptr, *rb = causal ? u16(L.rb) : nullptr;
+  uint16_t *ra = rev ? u16(L.ra) : nullptr, *rb = rev ? u16(L.rb) : nullptr;
   LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
                                   s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
-                                  causal ? 1 : 0, den_ld, st),
+                                  rev ? 1 : 0, den_ld, st),
             "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
   uint16_t *dphq = u16(L.dphq), *dphk = u16(L.dphk);  // bf16, as the forward stores phi
-  uint16_t *rphq = causal ? u16(L.rphq) : nullptr, *rphk = causal ? u16(L.rphk) : nullptr;
-  if (causal) {
+  uint16_t *rphq = rev ? u16(L.rphq) : nullptr, *rphk = rev ? u16(L.rphk) : nullptr;
+  if (rev) {
     LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
     LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
   }
-  // initial-state gradients: dS0 = sum_i phi_Q,i dnum_i^T (reversed rows of
-  // both, paired), dz0 = sum_i dden_i phi_Q,i (dden is column dv of a)
+  // initial-state gradients: dS0 = sum_i phi_Q,i dnum_i^T (rows of both in
+  // one order, reversed or not), dz0 = sum_i dden_i phi_Q,i (dden is column dv of a)
   if (causal && dS0)
-    LLOPS_HIP(state_total(s, m, dv, rphq, dn, seg, dS0, nullptr, st), "dS0");
+    LLOPS_HIP(state_total(s, m, dv, rev ? rphq : phq, dn, seg, dS0, nullptr, st), "dS0");
   if (causal && dz0) {
     float* stot = f32(L.stot);
     LLOPS_HIP(llops::launch_rows_copy_bf16(a, MA, dv, vp, 16, 0, 16, n, R, 0, st), "rows");
@@ -981,9 +999,14 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     if (!inplace)
       LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphq, m, p0, W, n, R, 0, st), "rows");
   }
-  // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: causal over the reversed sequence
-  const int rv = causal ? 1 : 0;
-  for (int p0 = 0; p0 < m; p0 += W) {
+  // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: anti-causal, or causal over
+  // the reversed sequence
+  const int rv = rev ? 1 : 0;
+  for (int p0 = 0; anti && p0 < m; p0 += W)
+    LLOPS_HIP(attn_on_features(s, true, MA, W, b, a, phq + p0, tmp, seg, tot, st, nullptr,
+                               dphk + p0, m, 0, m, true),
+              "attn dphi_k");
+  for (int p0 = 0; !anti && p0 < m; p0 += W) {
     if (!sliced)
       LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
     const uint16_t* qv = sliced ? (causal ? rphq : phq) + p0 : vp;
@@ -994,8 +1017,13 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     if (!inplace)
       LLOPS_HIP(llops::launch_rows_copy_f32_bf16(tmp, W, 0, dphk, m, p0, W, n, R, rv, st), "rows");
   }
-  // dV_j = sum_{i(>=j)} (phi_Q_i . phi_K_j) dnum_i: causal over the reversed sequence
-  if (causal && on32(s, true, m, dv)) {
+  // dV_j = sum_{i(>=j)} (phi_Q_i . phi_K_j) dnum_i: anti-causal, or causal over
+  // the reversed sequence
+  if (anti) {
+    LLOPS_HIP(attn_on_features(s, true, m, dv, phk, phq, dn, dV, seg, nullptr, st, nullptr,
+                               nullptr, 0, 0, 0, true),
+              "attn dv");
+  } else if (causal && on32(s, true, m, dv)) {
     LLOPS_HIP(attn_on_features(s, true, m, dv, rphk, rphq, dn, dV, seg, nullptr, st, nullptr,
                                nullptr, 0, 1),
               "attn dv");

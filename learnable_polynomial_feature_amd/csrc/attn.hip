@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int nseg, int m, int dv,
                                                        float* Sout, int64_t Sout_bh,
                                                        float* zout, int64_t zout_bh,
                                                        int exclusive,
-                                                       const float* __restrict__ gseg) {
+                                                       const float* __restrict__ gseg,
+                                                       int reverse) {
   const int64_t per = static_cast<int64_t>(m) * dv + m;
   const int64_t mdv = static_cast<int64_t>(m) * dv;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -164,16 +165,18 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(int nseg, int m, int dv,
   } else {
     if (z0) acc = z0[bh * m + (e - mdv)];
   }
-  float* p = seg + bh * nseg * per + e;
+  // reverse: from the last segment back to the first (suffix sums)
+  const int64_t step = reverse ? -per : per;
+  float* p = seg + bh * nseg * per + e + (reverse ? (nseg - 1) * per : 0);
   if (gseg) {  // gated: the prefix decays through each segment before its own sum is added
     const float* gs = gseg + bh * nseg;
-    for (int gi = 0; gi < nseg; ++gi, p += per) {
+    for (int gi = 0; gi < nseg; ++gi, p += step) {
       const float x = *p;
       if (exclusive) *p = acc;
       acc = fmaf(__expf(gs[gi]), acc, x);
     }
   } else {
-    for (int gi = 0; gi < nseg; ++gi, p += per) {
+    for (int gi = 0; gi < nseg; ++gi, p += step) {
       const float x = *p;
       if (exclusive) *p = acc;
       acc += x;
@@ -696,24 +699,27 @@ hipError_t launch_seg_scan(const AttnShape& s, float* seg, const float* S0, cons
   }
   dim3 grid(static_cast<unsigned>((per + 255) / 256), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH("seg_scan", st, seg_scan_kernel, grid, dim3(256), 0, st, s.nseg, s.m, s.dv, seg, S0, z0,
-                     Sout, Sb, zout, zb, exclusive, static_cast<const float*>(nullptr));
+                     Sout, Sb, zout, zb, exclusive, static_cast<const float*>(nullptr),
+                     s.anti ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_seg_scan_gated(const AttnShape& s, float* seg, const float* gseg,
                                  const float* S0, const float* z0, float* Sout, float* zout,
                                  hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;  // gated suffix scans run on reversed sequences
   const int64_t mdv = static_cast<int64_t>(s.m) * s.dv;
   const int64_t per = mdv + s.m;
   dim3 grid(static_cast<unsigned>((per + 255) / 256), static_cast<unsigned>(s.BH));
   LLOPS_LAUNCH("seg_scan", st, seg_scan_kernel, grid, dim3(256), 0, st, s.nseg, s.m, s.dv, seg, S0,
-               z0, Sout, mdv, zout, static_cast<int64_t>(s.m), 1, gseg);
+               z0, Sout, mdv, zout, static_cast<int64_t>(s.m), 1, gseg, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_out_bf16(const AttnShape& s, const uint16_t* phiq, const uint16_t* phik,
                                 const uint16_t* v, const float* state, int64_t st_seg,
                                 int64_t st_bh, float* out, hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;  // the anti-causal form runs on attn_out32 only
   const AttnArgs a = to_args(s);
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   if (s.causal) {
@@ -727,6 +733,7 @@ hipError_t launch_attn_out_bf16(const AttnShape& s, const uint16_t* phiq, const 
 hipError_t launch_attn_out_f32(const AttnShape& s, const float* phiq, const float* phik,
                                const float* v, float* state, int64_t st_seg, int64_t st_bh,
                                float* out, hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;
   const AttnArgs a = to_args(s);
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
   const size_t lds = (static_cast<size_t>(s.chunk) * s.chunk + s.chunk) * sizeof(float);
@@ -755,6 +762,7 @@ hipError_t launch_seg_state_f32_gated(const AttnShape& s, const float* phik, con
 hipError_t launch_attn_out_f32_gated(const AttnShape& s, const float* phiq, const float* phik,
                                      const float* v, const float* log_gate, float* state,
                                      float* out, hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;
   if (!s.causal) return hipErrorInvalidValue;
   const AttnArgs a = to_args(s);
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));

@@ -385,12 +385,17 @@ struct Out32Geom {
 // DENOUT: the row's denominator (without delta) goes to den_out [BH][n] and the
 // output row stays unnormalised (a.normalize set, so both are formed as in
 // the normalised pass); the backward takes num and den from one pass.
+// ANTI (with CAUSAL): the anti-causal form, row i over keys j >= i. The
+// segment's chunks run from the last to the first, the state entering a
+// segment is the sum over the segments after it, and the intra-chunk mask
+// keeps keys at or after the query. Every chunk keeps its natural row order,
+// so the backward's suffix sums need no reversed copies of their operands.
 // OM, the output rows' destination: 0 out [BH][n][DV]; bit 0 set, row t of
 // the pass goes to row n - 1 - t (a pass over the reversed sequence writes
 // in the original order); bit 1 set, bf16 (RNE) into outb, rows ldo elements
 // apart (a column slice of a wider row).
 template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
-          bool VSTR = false>
+          bool VSTR = false, bool ANTI = false>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
@@ -400,6 +405,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
   static_assert(CAUSAL || !GATED, "the gated form is causal");
+  static_assert(!ANTI || (CAUSAL && !GATED && !DENOUT && (OM & 1) == 0),
+                "the anti-causal form: ungated, no denominator output, rows in place");
   constexpr int NP = CAUSAL ? 2 * QP + G::VPc : QP;  // pieces staged per chunk
   constexpr int LPT = NP / NT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -422,6 +429,13 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   const float* Sin = state + bh * st_bh + gseg * st_seg;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
   float* exbase = reinterpret_cast<float*>(smem + 2 * G::BUF);
+  // chunk processed k-th (clamped to the segment; 0 for an empty one): the
+  // k-th in order, or the k-th from the end (ANTI)
+  auto chunk_at = [&](int k) {
+    const int kk = k < nch - 1 ? k : nch - 1;
+    const int ch = ANTI ? nch - 1 - kk : kk;
+    return ch > 0 ? ch : 0;
+  };
 
   f32x16 S[FH], Z;
 #pragma unroll
@@ -500,13 +514,13 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // c, move chunk c+1 from `wr` into the other LDS slot, publish partials,
   // barrier, finish this wave's rows
   auto step = [&](int c, u32x4 (&ld)[LPT], uint32_t& ldg, const u32x4 (&wr)[LPT], const uint32_t& wrg) {
-    load(c + 2 < nch ? c + 2 : nch - 1, ld, ldg);
+    load(chunk_at(c + 2), ld, ldg);
     // Lane-dependent bases pass through an empty asm so the compiler cannot
     // hoist every derived LDS address and mask compare out of the chunk loop
     // (kept live across iterations they exhaust the 256-register budget).
     int lbase = (c & 1) * G::BUF;
     asm volatile("" : "+v"(lbase));
-    int lim = c32 - 4 * hh;  // key 8i+4hh+e reaches query c32 iff 8i+e <= lim
+    int lim = c32 - 4 * hh;  // key 8i+4hh+e reaches query c32 iff 8i+e <= lim (ANTI: >=)
     asm volatile("" : "+v"(lim));
     const uint16_t* Qs = smem + lbase;
     const uint16_t* Ks = Qs + kC * QPAD;
@@ -517,7 +531,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     float* xo = ex;
     float* part = ex + G::XO;
     float* rsum = part + G::PART;
-    const int64_t c0 = t0 + static_cast<int64_t>(c) * kC;
+    const int64_t c0 = t0 + static_cast<int64_t>(chunk_at(c)) * kC;
     // gated: the chunk's gate sums L sit behind its V rows
     auto gate_sums = [&]() { return reinterpret_cast<const float*>(Vs + kC * VP); };
 
@@ -561,8 +575,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (8 * i + e > lim) At[4 * i + e] = 0.f;  // key after query
+          for (int e = 0; e < 4; ++e)  // zero keys after the query (ANTI: before it)
+            if (ANTI ? 8 * i + e < lim : 8 * i + e > lim) At[4 * i + e] = 0.f;
       }
       afr[0] = acc_frag(At, 0);
       afr[1] = acc_frag(At, 1);
@@ -744,8 +758,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 
   u32x4 rA[LPT], rB[LPT];
   uint32_t gA = 0u, gB = 0u;
-  load(0, rA, gA);
-  load(nch > 1 ? 1 : 0, rB, gB);
+  load(chunk_at(0), rA, gA);
+  load(chunk_at(1), rB, gB);
   // The prefix state must be in registers before the chunk loop: a wait for
   // it left to the compiler lands inside the loop and drains the chunk
   // prefetch on every chunk (and the scheduler sinks the state loads below a
@@ -1239,7 +1253,7 @@ hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t*
 }
 
 template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
-          bool VSTR = false>
+          bool VSTR = false, bool ANTI = false>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* gl, const float* state, int64_t ss,
                         int64_t sb, float* out, hipStream_t st, float* den = nullptr,
@@ -1247,7 +1261,8 @@ hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k
   using G = Out32Geom<M, DV, GATED>;
   Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
   const size_t lds = G::lds_bytes();
-  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM, VSTR>;
+  if ((s.anti != 0) != ANTI) return hipErrorInvalidValue;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM, VSTR, ANTI>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
@@ -1306,6 +1321,15 @@ hipError_t launch_attn_out32(const AttnShape& s, const uint16_t* phiq, const uin
                              const uint16_t* v, const float* state, int64_t st_seg,
                              int64_t st_bh, float* out, hipStream_t st) {
   const float* g = nullptr;
+  if (s.anti) {  // anti-causal, fp32 rows (the backward's dV pass)
+    if (!s.causal) return hipErrorInvalidValue;
+    switch (key32(s)) {
+      case 256128: return launch_out_t<256, 128, true, false, false, 0, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+      case 128064: return launch_out_t<128, 64, true, false, false, 0, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+      case 64064: return launch_out_t<64, 64, true, false, false, 0, false, true>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (key32(s) * 2 + (s.causal ? 1 : 0)) {
     case 256128 * 2 + 1: return launch_out_t<256, 128, true, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
     case 256128 * 2: return launch_out_t<256, 128, false, false>(s, phiq, phik, v, g, state, st_seg, st_bh, out, st);
@@ -1340,6 +1364,10 @@ hipError_t launch_out_om(const AttnShape& s, const uint16_t* q, const uint16_t* 
                          int vld) {
   const int om = (outb ? 2 : 0) | (rev ? 1 : 0);
   const float* g = nullptr;
+  if (s.anti) {  // the backward's suffix passes: bf16 rows in place from a value slice
+    if (!s.causal || om != 2 || !vld) return hipErrorInvalidValue;
+    return launch_out_t<M, DV, true, false, false, 2, true, true>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo, vld);
+  }
   if (vld) {  // value rows vld apart: the backward's bf16 passes only
     if (om == 2 && !s.causal)
       return launch_out_t<M, DV, false, false, false, 2, true>(s, q, k, v, g, state, ss, sb, out, st, nullptr, outb, ldo, vld);
@@ -1394,7 +1422,7 @@ hipError_t launch_attn_out32_fq(const AttnShape& s, int d, int p, int t, const u
                                 const uint16_t* thpk, int64_t pk_hstride, int64_t H, int square,
                                 const uint16_t* phik, const uint16_t* v, const float* state,
                                 int64_t st_seg, int64_t st_bh, float* out, hipStream_t st) {
-  if (!attn32_fq_supported(s, d, p, t) || H < 1) return hipErrorInvalidValue;
+  if (!attn32_fq_supported(s, d, p, t) || H < 1 || s.anti) return hipErrorInvalidValue;
   switch (fq_key(s, d, p, t)) {
     case 1: return launch_fq_t<256, 128, 128, 2, 4>(s, xq, thpk, pk_hstride, H, square, phik, v, state, st_seg, st_bh, out, st);
     case 2: return launch_fq_t<128, 64, 64, 3, 8>(s, xq, thpk, pk_hstride, H, square, phik, v, state, st_seg, st_bh, out, st);
@@ -1424,6 +1452,7 @@ hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L,
 
 hipError_t launch_seg_state32_gated(const AttnShape& s, const uint16_t* phik, const uint16_t* v,
                                     const float* gl, float* gseg, float* seg, hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;  // decayed sums depend on the direction
   switch (key32(s)) {
     case 256128: return launch_state_t<256, 128, true>(s, phik, v, gl, gseg, seg, st);
     case 128064: return launch_state_t<128, 64, true>(s, phik, v, gl, gseg, seg, st);
@@ -1435,6 +1464,7 @@ hipError_t launch_seg_state32_gated(const AttnShape& s, const uint16_t* phik, co
 hipError_t launch_seg_state32_anchored(const AttnShape& s, const uint16_t* phik,
                                       const uint16_t* v, const float* gl, float* gseg, float* seg,
                                       hipStream_t st) {
+  if (s.anti) return hipErrorInvalidValue;
   switch (key32(s)) {
     case 256128: return launch_state_t<256, 128, true, true>(s, phik, v, gl, gseg, seg, st);
     case 128064: return launch_state_t<128, 64, true, true>(s, phik, v, gl, gseg, seg, st);

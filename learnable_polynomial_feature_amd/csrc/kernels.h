@@ -128,6 +128,10 @@ struct AttnShape {
   int causal;
   int normalize;
   float delta;
+  // anti-causal (with causal set): row i reads keys j >= i, i.e. suffix sums.
+  // The segment states are then scanned from the last segment back, and the
+  // output pass walks each segment's chunks from the last to the first.
+  int anti = 0;
 };
 
 // Per-segment partial state: seg[bh][g][0 : m*dv] = phi_K^T V, [m*dv : +m] = phi_K^T 1.
@@ -137,7 +141,8 @@ hipError_t launch_seg_state_f32(const AttnShape& a, const float* phik, const flo
                                 float* seg, hipStream_t st);
 // Exclusive scan of seg over g starting from (S0, z0) (null = zeros). Writes the
 // total into (S_tot, z_tot) when non-null. For non-causal (exclusive = 0) the
-// slots are left untouched and only the total is produced.
+// slots are left untouched and only the total is produced. a.anti: the scan
+// runs from the last segment to the first (exclusive suffix sums).
 hipError_t launch_seg_scan(const AttnShape& a, float* seg, const float* S0,
                            const float* z0, float* S_tot, float* z_tot, int exclusive,
                            hipStream_t st);
