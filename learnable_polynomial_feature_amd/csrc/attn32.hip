@@ -111,6 +111,25 @@ __device__ __forceinline__ void scale_rows(float (&val)[8], float inv) {
   val[6] *= row_bcast<6>(inv);
   val[7] *= row_bcast<7>(inv);
 }
+// t[k] *= the value lane k of this lane's 16-lane row holds (k = 0..15)
+__device__ __forceinline__ void scale_rows16(f32x16& t, float f) {
+  t[0] *= row_bcast<0>(f);
+  t[1] *= row_bcast<1>(f);
+  t[2] *= row_bcast<2>(f);
+  t[3] *= row_bcast<3>(f);
+  t[4] *= row_bcast<4>(f);
+  t[5] *= row_bcast<5>(f);
+  t[6] *= row_bcast<6>(f);
+  t[7] *= row_bcast<7>(f);
+  t[8] *= row_bcast<8>(f);
+  t[9] *= row_bcast<9>(f);
+  t[10] *= row_bcast<10>(f);
+  t[11] *= row_bcast<11>(f);
+  t[12] *= row_bcast<12>(f);
+  t[13] *= row_bcast<13>(f);
+  t[14] *= row_bcast<14>(f);
+  t[15] *= row_bcast<15>(f);
+}
 // Denominator of a chunk row: delta, then the row sum of the rounded masked
 // weights (rs), then the z-tile owners' partials (lo, hi: the row's 8 wave
 // slots; wave w = half * NWD + value tile) in wave order, first feature half
@@ -537,6 +556,24 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 
     f32x16 O = zero16(), D = zero16();
     bf16x8 afr[2];
+    // partial phi_Q S over this wave's feature half; phi_Q . z over its z
+    // tile. The phi_Q fragment reads run QD products ahead (pinned).
+    auto inter = [&]() {
+      constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
+      bf16x8 qf[QD];
+#pragma unroll
+      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
+#pragma unroll
+      for (int idx = 0; idx < NQ; ++idx) {
+        const int j = idx >> 1, h = idx & 1;
+        const bf16x8 qa = qf[idx % QD];
+        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
+        O = mfma32x32x16(qa, acc_frag(S[j], h), O);
+        if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    __builtin_amdgcn_sched_barrier(0);
     if (CAUSAL && half == 0) {
       // masked A^T = phi_K phi_Q^T (keys x queries)
       // fragment reads run AD k-steps ahead of the MFMA chain (pinned: the
@@ -592,35 +629,33 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         rs += __shfl_xor(rs, 32);
         if (hh == 0) rsum[c32] = rs;
       }
+      if constexpr (!GATED) {
 #pragma unroll
-      for (int ks = 0; ks < kC / 16; ++ks)
-        O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
+        for (int ks = 0; ks < kC / 16; ++ks)
+          O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // partial phi_Q S over this wave's feature half; phi_Q . z over its z
-    // tile. The phi_Q fragment reads run QD products ahead (pinned). Gated:
-    // the carried state reaches query q with weight exp(L_q), applied to the
-    // query's phi_Q row (the A operand's row is this lane's query c32).
-    {
-      float eq = 1.f;
-      if constexpr (GATED) eq = __expf(gate_sums()[c32]);
-      constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
-      bf16x8 qf[QD];
+    if constexpr (GATED) {
+      // The carried state reaches query q with weight exp(L_q): a row scale
+      // of phi_Q S and phi_Q . z, applied to the accumulators before A V
+      // joins them. Element k of a tile is row 8(k/4) + 4hh + k%4; lane i
+      // of each 16-lane row takes exp(L) of element i's row, and a DPP row
+      // broadcast from lane k hands it to every lane (folded into the
+      // multiply).
+      inter();
+      const int i16 = lane & 15;
+      const float ef = __expf(gate_sums()[8 * (i16 >> 2) + 4 * hh + (i16 & 3)]);
+      scale_rows16(O, ef);
+      scale_rows16(D, ef);
+      __builtin_amdgcn_sched_barrier(0);
+      if (half == 0) {
 #pragma unroll
-      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
-#pragma unroll
-      for (int idx = 0; idx < NQ; ++idx) {
-        const int j = idx >> 1, h = idx & 1;
-        bf16x8 qa = qf[idx % QD];
-        if constexpr (GATED) {
-          const float e8[8] = {eq, eq, eq, eq, eq, eq, eq, eq};
-          qa = scale_frag(qa, e8);
-        }
-        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
-        O = mfma32x32x16(qa, acc_frag(S[j], h), O);
-        if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ks = 0; ks < kC / 16; ++ks)
+          O = mfma32x32x16(afr[ks], frag_tr(Vs, VP, ks * 16, dvt * 32, lane), O);
       }
+    } else {
+      inter();
     }
     __builtin_amdgcn_sched_barrier(0);
     // publish: the 16 rows the partner wave finishes, and the z partial
