@@ -158,18 +158,37 @@ __device__ __forceinline__ void gate_rows(const float* gls, int hh, float (&L)[1
   }
 }
 
+// f(token) for the 16 tokens of this lane's elements (element k: token
+// 8(k/4) + 4hh + k%4): each lane evaluates f once, at element (lane % 16)'s
+// token, and a DPP row broadcast from lane k hands out element k's value.
+template <class F>
+__device__ __forceinline__ void per_row16(int lane, int hh, F f, float (&out)[16]) {
+  const int i16 = lane & 15;
+  const float v = f(8 * (i16 >> 2) + 4 * hh + (i16 & 3));
+  out[0] = row_bcast<0>(v);
+  out[1] = row_bcast<1>(v);
+  out[2] = row_bcast<2>(v);
+  out[3] = row_bcast<3>(v);
+  out[4] = row_bcast<4>(v);
+  out[5] = row_bcast<5>(v);
+  out[6] = row_bcast<6>(v);
+  out[7] = row_bcast<7>(v);
+  out[8] = row_bcast<8>(v);
+  out[9] = row_bcast<9>(v);
+  out[10] = row_bcast<10>(v);
+  out[11] = row_bcast<11>(v);
+  out[12] = row_bcast<12>(v);
+  out[13] = row_bcast<13>(v);
+  out[14] = row_bcast<14>(v);
+  out[15] = row_bcast<15>(v);
+}
+
 // Carry weights w_k = exp(T - L_k) of this lane's 16 tokens, element 4i + e
 // (0 past the chunk's valid rows); elements 8ks..8ks+7 line up with the P16
-// k-values of the ks-th V fragment of the chunk.
-__device__ __forceinline__ void gate_carry(const float* gls, int hh, float T, int valid,
+// k-values of the ks-th V fragment of the chunk. One exp per lane.
+__device__ __forceinline__ void gate_carry(const float* gls, int lane, int hh, float T, int valid,
                                            float (&wv)[16]) {
-  float L[16];
-  gate_rows(gls, hh, L);
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int tok = 8 * (k >> 2) + 4 * hh + (k & 3);
-    wv[k] = tok < valid ? __expf(T - L[k]) : 0.f;
-  }
+  per_row16(lane, hh, [&](int tok) { return tok < valid ? __expf(T - gls[tok]) : 0.f; }, wv);
 }
 
 template <int M, int DV>
@@ -294,15 +313,10 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
       const float T = gls[valid - 1];
       float wv[16];
       if constexpr (ANCHOR) {
-        float L[16];
-        gate_rows(gls, hh, L);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int tok = 8 * (k >> 2) + 4 * hh + (k & 3);
-          wv[k] = tok < valid ? __expf(gsum + L[k]) : 0.f;
-        }
+        per_row16(lane, hh, [&](int tok) { return tok < valid ? __expf(gsum + gls[tok]) : 0.f; },
+                  wv);
       } else {
-        gate_carry(gls, hh, T, valid, wv);
+        gate_carry(gls, lane, hh, T, valid, wv);
       }
 #pragma unroll
       for (int ks = 0; ks < kC / 16; ++ks) {
@@ -688,7 +702,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         const int valid = t1 - c0 < kC ? static_cast<int>(t1 - c0) : kC;  // rows in range
         const float T = gls[valid - 1];
         float wv[16];
-        gate_carry(gls, hh, T, valid, wv);
+        gate_carry(gls, lane, hh, T, valid, wv);
 #pragma unroll
         for (int ks = 0; ks < kC / 16; ++ks) {
           vb[ks] = scale_frag(vb[ks], wv + 8 * ks);
