@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libllops.so")
+# LLOPS_LIBRARY: another build of the same library (e.g. the host-sanitized
+# one, `python -m learnable_polynomial_feature_amd.build --host-sanitize`)
+LIB_PATH = os.environ.get("LLOPS_LIBRARY") or os.path.join(_HERE, "libllops.so")
 
 F32, BF16 = 0, 1
 (ENTRY_FEATMAP, ENTRY_LINATTN, ENTRY_CAUSAL, ENTRY_DECODE, ENTRY_FEATMAP_BWD, ENTRY_CAUSAL_BWD,

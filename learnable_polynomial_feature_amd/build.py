@@ -1,9 +1,18 @@
 """Build libllops.so (all HIP kernels + the C ABI) for gfx950, in-tree.
 
     python -m learnable_polynomial_feature_amd.build
+    python -m learnable_polynomial_feature_amd.build --host-sanitize
 
 Every source is compiled by hipcc with packed-fp32 instruction selection
 disabled, then linked into learnable_polynomial_feature_amd/libllops.so.
+--host-sanitize builds libllops_hostsan.so instead: the same library with
+AddressSanitizer and UndefinedBehaviorSanitizer on its host code only (every
+-fsanitize behind -Xarch_host; the device code is unchanged). Load it with
+LLOPS_LIBRARY set to its path and the ASan runtime preloaded, e.g.
+
+    LD_PRELOAD=$(hipcc -print-file-name=libclang_rt.asan-x86_64.so) \
+    ASAN_OPTIONS=detect_leaks=0 LLOPS_LIBRARY=<pkg>/libllops_hostsan.so \
+    python -m pytest tests -m "not gpu" -k "abi or binding"
 """
 from __future__ import annotations
 
@@ -37,9 +46,14 @@ COMMON = [
 EXTRA = {"featmap_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# host code only: each -fsanitize applies to the host pass alone
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src: str, build_dir: str = BUILD, extra: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[cmd.index("-c"):cmd.index("-c")] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,18 +66,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 4, host_sanitize: bool = False) -> str:
+    build_dir = BUILD + ("_hostsan" if host_sanitize else "")
+    lib = os.path.join(PKG, "libllops_hostsan.so") if host_sanitize else LIB
+    extra = tuple(HOST_SAN) if host_sanitize else ()
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, build_dir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-shared-libsan", *objs,
+           "-o", tmp] if host_sanitize else [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                                              *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(host_sanitize="--host-sanitize" in sys.argv[1:]))
