@@ -179,20 +179,20 @@ bool num_den_one_pass(const llops_shape_t* s, bool causal);
 
 bool on32(const llops_shape_t* s, bool causal, int M, int DV);
 
-// The causal backward's suffix sums (dphi_K and dV: key i >= query j) run as
+// The causal backwards' suffix sums (dphi_K and dV: key i >= query j) run as
 // anti-causal output passes on the 32x32x16 kernels when their in-place forms
-// apply (phi read in place, rows written in place); otherwise, and in the
-// gated backward, as causal passes over reversed copies of their operands.
+// apply (phi read in place, rows written in place); otherwise as causal
+// passes over reversed copies of their operands (and, gated, reversed gates).
 bool bwd_anti(const llops_shape_t* s) {
   return on32(s, true, bwd_ma(s), bwd_w(s)) && on32(s, true, s->m, s->dv) &&
          s->n * s->m * 2 < (int64_t{1} << 31);
 }
 
-BwdWs bwd_ws(const llops_shape_t* s, bool causal, bool gated = false) {
+BwdWs bwd_ws(const llops_shape_t* s, bool causal) {
   BwdWs w{};
   const size_t R = static_cast<size_t>(s->batch * s->heads) * static_cast<size_t>(s->n);
   const size_t m = s->m, dv = s->dv, MA = bwd_ma(s), W = bwd_w(s);
-  const bool rev = causal && (gated || !bwd_anti(s));  // reversed copies needed
+  const bool rev = causal && !bwd_anti(s);  // reversed copies needed
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -464,7 +464,8 @@ struct GBwdWs {
 
 GBwdWs gated_bwd_ws(const llops_shape_t* s) {
   GBwdWs w{};
-  w.b = bwd_ws(s, true, true);
+  w.b = bwd_ws(s, true);
+  const bool rev = !bwd_anti(s);  // reversed gates for the reversed passes
   size_t off = w.b.total;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -476,8 +477,8 @@ GBwdWs gated_bwd_ws(const llops_shape_t* s) {
   const size_t nld = static_cast<size_t>((s->n + 31) / 32 * 32);
   const int MA = bwd_ma(s), W = bwd_w(s);
   w.glf = take(BH * nld * 4);   // chunk-local sums of the forward gates
-  w.grev = take(R * 4);         // gates of the reversed sequence
-  w.glr = take(BH * nld * 4);   // and their chunk-local sums
+  w.grev = take(rev ? R * 4 : 0);        // gates of the reversed sequence
+  w.glr = take(rev ? BH * nld * 4 : 0);  // and their chunk-local sums
   const llops_shape_t t = feat_attn_shape(s, s->m, s->dv);
   w.gseg = take(BH * static_cast<size_t>(seg_plan(&t, true, kGatedBwdWG).nseg) * 4);
   w.gden = take(s->normalize ? R * 4 : 0);  // M 1 per row, from the num pass
@@ -1124,11 +1125,15 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   float *seg = f32(L.seg), *gseg = f32(L.gseg);
   llops::FeatJob jobs[2] = {{Q, theta_q, phq, w + L.b.pkq}, {K, theta_k, phk, w + L.b.pkk}};
   LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, n, 1), jobs, 2, st), "featmap");
-  // chunk-local gate sums, forward and for the reversed sequence
-  float *glf = f32(L.glf), *grev = f32(L.grev), *glr = f32(L.glr);
+  // chunk-local gate sums, forward and (off the anti-causal path) for the
+  // reversed sequence
+  const bool anti = bwd_anti(s);
+  float *glf = f32(L.glf), *grev = anti ? nullptr : f32(L.grev), *glr = anti ? nullptr : f32(L.glr);
   LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, log_gate, glf, st), "gate_cumsum");
-  LLOPS_HIP(llops::launch_gate_reverse_shift(log_gate, n, R, grev, st), "gate_reverse");
-  LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, grev, glr, st), "gate_cumsum");
+  if (!anti) {
+    LLOPS_HIP(llops::launch_gate_reverse_shift(log_gate, n, R, grev, st), "gate_reverse");
+    LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, grev, glr, st), "gate_cumsum");
+  }
   // num = M V and, normalised, M 1 per row from the same pass
   float* num = f32(L.b.num);
   const uint16_t* vv = static_cast<const uint16_t*>(V);
@@ -1142,9 +1147,10 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
               "attn num");
   }
   uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
-  uint16_t *ra = u16(L.b.ra), *rb = u16(L.b.rb);
+  uint16_t *ra = anti ? nullptr : u16(L.b.ra), *rb = anti ? nullptr : u16(L.b.rb);
   LLOPS_HIP(llops::launch_make_ab(num, den, dO, vv, dv, MA, n, R, s->normalize,
-                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, 1, 1, st),
+                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, anti ? 0 : 1, 1,
+                                  st),
             "make_ab");
   uint16_t* vp = u16(L.b.vp);
   float* tmp = f32(L.b.tmp);
@@ -1164,9 +1170,11 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   // sequence's from the reversed copy of phi_Q) unless phi is too long for a
   // 32-bit view, and dV is written in the original row order directly.
   const bool sliced = n * m * 2 < (int64_t{1} << 31);
-  uint16_t *rphq = u16(L.b.rphq), *rphk = u16(L.b.rphk);
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
-  LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
+  uint16_t *rphq = anti ? nullptr : u16(L.b.rphq), *rphk = anti ? nullptr : u16(L.b.rphk);
+  if (!anti) {
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, 0, rphq, m, 0, m, n, R, 1, st), "rows");
+    LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, 0, rphk, m, 0, m, n, R, 1, st), "rows");
+  }
   for (int p0 = 0; p0 < m; p0 += W) {
     if (!sliced)
       LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
@@ -1195,10 +1203,21 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
     // segment 0's suffix state is sum_i exp(c_i) a_i phi_Q,i^T: [dS0^T; dz0^T] for this slice
     LLOPS_HIP(llops::launch_state_grad_slice(seg2, aMW.nseg, perMW, BH, m, dv, W, p0, dS0, dz0, st),
               "state grad");
+    if (anti) {
+      // dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j) phi_Q_i for this slice: the
+      // anti-causal pass starts each segment from the start-anchored suffix state
+      // of the next one, which seg2 now holds; dc_j -= phi_K,j . dphi_K,j
+      llops::AttnShape ga = aMW;
+      ga.anti = 1;
+      LLOPS_HIP(llops::launch_attn_out32_gated_to(ga, b, a, phq + p0, glf, seg2, tmp, 0, m, st),
+                "attn dphi_k");
+      LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 0, -1.f, 0, dc, st, dphk),
+                "rowdot");
+    }
   }
-  // dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j) phi_Q_i over the reversed
-  // sequence with its shifted gates; dc_j -= phi_K,j . dphi_K,j
-  for (int p0 = 0; p0 < m; p0 += W) {
+  // off the anti-causal path: dphi_K_j = sum_{i>=j} exp(c_i - c_j) (a_i . b_j)
+  // phi_Q_i over the reversed sequence with its shifted gates; dc_j -= phi_K,j . dphi_K,j
+  for (int p0 = 0; !anti && p0 < m; p0 += W) {
     if (!sliced)
       LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, 1, st), "rows");
     LLOPS_HIP(gated_attn_on_features(s, MA, W, rb, ra, sliced ? rphq + p0 : vp, glr, tmp, seg,
@@ -1207,10 +1226,25 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 1, -1.f, 0, dc, st, dphk),
               "rowdot");
   }
-  // dV_j = sum_{i>=j} M_ij dnum_i over the reversed sequence, rows written back
-  // in the original order
-  LLOPS_HIP(gated_attn_on_features(s, m, dv, rphk, rphq, dn, glr, dV, seg, gseg, st, nullptr, 0, 1),
-            "attn dv");
+  // dV_j = sum_{i>=j} M_ij dnum_i: anti-causal from start-anchored suffix
+  // states (state pass, reverse scan), or over the reversed sequence with
+  // rows written back in the original order
+  if (anti) {
+    const llops_shape_t tmd = feat_attn_shape(s, m, dv);
+    llops::AttnShape amd = attn_shape(&tmd, true, kGatedBwdWG);
+    const int64_t permd = static_cast<int64_t>(m) * dv + m;
+    LLOPS_HIP(llops::launch_seg_state32_anchored(amd, phq, dn, glf, gseg, seg, st), "anchored");
+    LLOPS_HIP(llops::launch_seg_rscan_gated(BH, amd.nseg, permd, static_cast<int64_t>(m) * dv, seg,
+                                            gseg, st),
+              "rscan");
+    amd.anti = 1;
+    LLOPS_HIP(llops::launch_attn_out32_gated_to(amd, phk, phq, dn, glf, seg, dV, 0, 0, st),
+              "attn dv");
+  } else {
+    LLOPS_HIP(gated_attn_on_features(s, m, dv, rphk, rphq, dn, glr, dV, seg, gseg, st, nullptr, 0,
+                                     1),
+              "attn dv");
+  }
   // dlog_gate_l = sum_{i>=l} dc_i, anchored at the exact segment-start values
   LLOPS_HIP(llops::launch_seg_bridge_dg(dc, BH, n, aMW.seg_len, aMW.nseg, dgb, dlog_gate, st),
             "bridge");

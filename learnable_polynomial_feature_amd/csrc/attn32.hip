@@ -423,6 +423,14 @@ struct Out32Geom {
 // segment is the sum over the segments after it, and the intra-chunk mask
 // keeps keys at or after the query. Every chunk keeps its natural row order,
 // so the backward's suffix sums need no reversed copies of their operands.
+// With GATED, key j reaches query i <= j with weight exp(c_j - c_i) (c the
+// cumulative log gates): within a chunk exp(L_j - L_i); against the carried
+// state the query row is scaled by exp(T - L_i), keys are carried with
+// exp(L_j) and the state decays by exp(T) per chunk (L the chunk-local
+// inclusive sums, T the chunk's last); every exponent is <= 0. The states
+// are then the start-anchored inclusive suffix sums of the segments (slot g:
+// the sum from segment g's start on), so segment g starts from slot g + 1
+// and the last segment from zero.
 // OM, the output rows' destination: 0 out [BH][n][DV]; bit 0 set, row t of
 // the pass goes to row n - 1 - t (a pass over the reversed sequence writes
 // in the original order); bit 1 set, bf16 (RNE) into outb, rows ldo elements
@@ -438,8 +446,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   constexpr int FH = G::FH, QPAD = G::QPAD, MP = G::MP, VP = G::VP, NT = G::NT, NWD = G::NWD;
   constexpr int QP = G::QP;
   static_assert(CAUSAL || !GATED, "the gated form is causal");
-  static_assert(!ANTI || (CAUSAL && !GATED && !DENOUT && (OM & 1) == 0),
-                "the anti-causal form: ungated, no denominator output, rows in place");
+  static_assert(!ANTI || (CAUSAL && !DENOUT && (OM & 1) == 0),
+                "the anti-causal form: no denominator output, rows in place");
   constexpr int NP = CAUSAL ? 2 * QP + G::VPc : QP;  // pieces staged per chunk
   constexpr int LPT = NP / NT;
   extern __shared__ __align__(16) uint16_t smem[];
@@ -459,7 +467,10 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   const int VL = VSTR ? vld : DV;  // value row stride (VSTR: a column slice)
   const uint16_t* Vg = v + bh * a.n * VL;
   float* Og = out + bh * a.n * DV;
-  const float* Sin = state + bh * st_bh + gseg * st_seg;
+  // gated anti-causal: slot g + 1 (start-anchored suffix sums), none for the last
+  constexpr bool SHIFT = ANTI && GATED;
+  const bool zero_in = SHIFT && gseg + 1 >= a.nseg;
+  const float* Sin = state + bh * st_bh + (gseg + (SHIFT ? 1 : 0)) * st_seg;
   const int nch = static_cast<int>((t1 - t0 + kC - 1) / kC);
   float* exbase = reinterpret_cast<float*>(smem + 2 * G::BUF);
   // chunk processed k-th (clamped to the segment; 0 for an empty one): the
@@ -477,12 +488,14 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S[j][4 * i + e] = Sin[((f0 + j) * 32 + 8 * i + 4 * hh + e) * DV + dvt * 32 + c32];
+        S[j][4 * i + e] = zero_in ? 0.f : Sin[((f0 + j) * 32 + 8 * i + 4 * hh + e) * DV + dvt * 32 + c32];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      Z[4 * i + e] = has_z ? Sin[static_cast<int64_t>(M) * DV + (f0 + zj) * 32 + 8 * i + 4 * hh + e] : 0.f;
+      Z[4 * i + e] = has_z && !zero_in
+                         ? Sin[static_cast<int64_t>(M) * DV + (f0 + zj) * 32 + 8 * i + 4 * hh + e]
+                         : 0.f;
   const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   // Raw buffer views of this segment's rows: reads past the segment end
@@ -613,6 +626,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       }
       if constexpr (GATED) {
         // A_qk = exp(L_q - L_k) phi_Q,q . phi_K,k for key k <= query q
+        // (ANTI: exp(L_k - L_q) for key k >= query q)
         const float* gls = gate_sums();
         float Lr[16];
         gate_rows(gls, hh, Lr);
@@ -620,8 +634,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            At[4 * i + e] = 8 * i + e > lim ? 0.f : At[4 * i + e] * __expf(Lq - Lr[4 * i + e]);
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (ANTI)
+              At[4 * i + e] = 8 * i + e < lim ? 0.f : At[4 * i + e] * __expf(Lr[4 * i + e] - Lq);
+            else
+              At[4 * i + e] = 8 * i + e > lim ? 0.f : At[4 * i + e] * __expf(Lq - Lr[4 * i + e]);
+          }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -659,7 +677,15 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       // multiply).
       inter();
       const int i16 = lane & 15;
-      const float ef = __expf(gate_sums()[8 * (i16 >> 2) + 4 * hh + (i16 & 3)]);
+      const float* gls = gate_sums();
+      const float Lrow = gls[8 * (i16 >> 2) + 4 * hh + (i16 & 3)];
+      float ef;
+      if constexpr (ANTI) {  // exp(T - L_q): the chunk's last valid sum T
+        const int valid = t1 - c0 < kC ? static_cast<int>(t1 - c0) : kC;
+        ef = __expf(gls[valid - 1] - Lrow);
+      } else {
+        ef = __expf(Lrow);
+      }
       scale_rows16(O, ef);
       scale_rows16(D, ef);
       __builtin_amdgcn_sched_barrier(0);
@@ -698,11 +724,15 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       }
       if constexpr (GATED) {
         // S <- exp(T) S + phi_K^T diag(exp(T - L)) V, z likewise
+        // (ANTI: keys carried with exp(L))
         const float* gls = gate_sums();
         const int valid = t1 - c0 < kC ? static_cast<int>(t1 - c0) : kC;  // rows in range
         const float T = gls[valid - 1];
         float wv[16];
-        gate_carry(gls, lane, hh, T, valid, wv);
+        if constexpr (ANTI)
+          per_row16(lane, hh, [&](int tok) { return tok < valid ? __expf(gls[tok]) : 0.f; }, wv);
+        else
+          gate_carry(gls, lane, hh, T, valid, wv);
 #pragma unroll
         for (int ks = 0; ks < kC / 16; ++ks) {
           vb[ks] = scale_frag(vb[ks], wv + 8 * ks);
@@ -1555,6 +1585,12 @@ hipError_t launch_out_gated_to(const AttnShape& s, const uint16_t* q, const uint
                                const uint16_t* v, const float* gl, const float* state,
                                float* out, int rev, int vld, hipStream_t st) {
   const int64_t per = static_cast<int64_t>(M) * DV + M;
+  if (s.anti) {  // suffix sums over start-anchored segment states (slot g + 1)
+    if (rev) return hipErrorInvalidValue;
+    if (vld)
+      return launch_out_t<M, DV, true, true, false, 0, true, true>(s, q, k, v, gl, state, per, per * s.nseg, out, st, nullptr, nullptr, 0, vld);
+    return launch_out_t<M, DV, true, true, false, 0, false, true>(s, q, k, v, gl, state, per, per * s.nseg, out, st);
+  }
   if (vld && !rev)
     return launch_out_t<M, DV, true, true, false, 0, true>(s, q, k, v, gl, state, per, per * s.nseg, out, st, nullptr, nullptr, 0, vld);
   if (rev && !vld)
