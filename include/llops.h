@@ -305,9 +305,8 @@ llops_status_t llops_decode_step(const llops_shape_t* shape, const void* q,
  * (the chain rule through the decay-masked form; the gate after the LLoPS
  * notes' limitations and outlook, the attention of the paper's Sec. 1, the
  * normaliser of the SLAY notes' key design 3). The three sums are gated
- * causal linear attentions over bf16 features (dphi_K and dV over the
- * reversed sequence, whose gates are shifted by one token), so they carry
- * the forward's bf16 rounding; the gate gradient's row dots are taken on the
+ * causal linear attentions over bf16 features (dphi_K and dV as suffix sums,
+ * gated anti-causal passes), so they carry the forward's bf16 rounding; the gate gradient's row dots are taken on the
  * fp32 pass outputs. in_dtype BF16 only; kernels exist for p = 2, t in
  * {1, 4}, d in {64, 128} and (m, dv) in {(256, 128), (128, 64), (64, 64)}
  * (else LLOPS_ERR_UNSUPPORTED). All outputs are overwritten. chunk is
