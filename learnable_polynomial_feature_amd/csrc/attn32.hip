@@ -253,13 +253,15 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                 GATED ? static_cast<uint32_t>(gl_ld(seg_rows)) * 4u : 0u);
   uint32_t rg = 0u;
   auto load = [&](int c, u32x4 (&rk)[LK], u32x4 (&rv)[LV]) {
-    // piece idx of a chunk is 16 contiguous bytes at byte 16 * idx
+    // piece idx of a chunk is 16 contiguous bytes at byte 16 * idx; the rows
+    // are streamed once, so the loads are non-temporal (0.316 -> 0.291 ms at
+    // 1 x 32 x 65536)
 #pragma unroll
     for (int i = 0; i < LK; ++i)
-      rk[i] = buf_ld16(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+      rk[i] = buf_ld16_nt(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
 #pragma unroll
     for (int i = 0; i < LV; ++i)
-      rv[i] = buf_ld16(rsv,
+      rv[i] = buf_ld16_nt(rsv,
                        VSTR ? static_cast<uint32_t>((tid + i * NT) / (DV / 8)) * (VL * 2u) +
                                   static_cast<uint32_t>((tid + i * NT) % (DV / 8)) * 16u
                             : (tid + i * NT) * 16u,
@@ -508,7 +510,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       Vg + t0 * VL, VSTR ? (seg_rows ? ((seg_rows - 1u) * VL + DV) * 2u : 0u) : seg_rows * DV * 2u);
   // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
   // contiguous bytes each; a thread's pieces t + i*NT never straddle two
-  // tensors, so the selection folds away
+  // tensors, so the selection folds away. Streamed once: non-temporal loads.
   // gated: the chunk's 32 gate sums (128 bytes), one per lane of the first
   // half of wave 0, stored behind the chunk's V rows
   const __amdgpu_buffer_rsrc_t rsg =
@@ -522,11 +524,11 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
     for (int i = 0; i < LPT; ++i) {
       const int p = t + i * NT;
       if (i * NT < QP)
-        r[i] = buf_ld16(rsq, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+        r[i] = buf_ld16_nt(rsq, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
       else if (i * NT < 2 * QP)
-        r[i] = buf_ld16(rsk, (p - QP) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+        r[i] = buf_ld16_nt(rsk, (p - QP) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
       else
-        r[i] = buf_ld16(rsv,
+        r[i] = buf_ld16_nt(rsv,
                         VSTR ? static_cast<uint32_t>((p - 2 * QP) / (DV / 8)) * (VL * 2u) +
                                    static_cast<uint32_t>((p - 2 * QP) % (DV / 8)) * 16u
                              : (p - 2 * QP) * 16u,
