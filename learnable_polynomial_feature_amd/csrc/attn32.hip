@@ -792,7 +792,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
               a.delta, CAUSAL ? rsum[lane] : 0.f, ld16(part + lane * 8), ld16(part + lane * 8 + 4));
         }
       }
-      // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk
+      // element e is row 8 * ((kept + e) / 4) + 4 * hh + e % 4 of the chunk; the
+      // rows are written once and not read back here: non-temporal stores
       float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
       if constexpr (OM != 0) {
         // destination row of this lane's first row c0 + 4hh, then rows r
@@ -826,12 +827,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
         }
       } else if (c0 + kC <= t1) {  // whole chunk in range: no per-row checks
 #pragma unroll
-        for (int e = 0; e < 8; ++e) orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV] = val[e];
+        for (int e = 0; e < 8; ++e) __builtin_nontemporal_store(val[e], &orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV]);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * ((kept + e) >> 2) + (e & 3);
-          if (c0 + r + 4 * hh < t1) orow[r * DV] = val[e];
+          if (c0 + r + 4 * hh < t1) __builtin_nontemporal_store(val[e], &orow[r * DV]);
         }
       }
     }
@@ -1247,15 +1248,16 @@ void attn_out32_fq(Seg32Args a, const uint16_t* __restrict__ xq,
     for (int e = 0; e < 8; ++e) val[e] += pick(O[e], O[8 + e], half == 0);
     if (a.normalize)
       scale_rows(val, __builtin_amdgcn_rcpf(den_sum<NWD, (FH < NWD ? FH : NWD)>(a.delta, rs, lo, hi)));
+    // rows written once: non-temporal stores, as in attn_out32
     float* orow = Og + (c0 + 4 * hh) * DV + dvt * 32 + c32;
     if (c0 + kC <= t1) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV] = val[e];
+      for (int e = 0; e < 8; ++e) __builtin_nontemporal_store(val[e], &orow[(8 * ((kept + e) >> 2) + (e & 3)) * DV]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ((kept + e) >> 2) + (e & 3);
-        if (c0 + r + 4 * hh < t1) orow[r * DV] = val[e];
+        if (c0 + r + 4 * hh < t1) __builtin_nontemporal_store(val[e], &orow[r * DV]);
       }
     }
   };
