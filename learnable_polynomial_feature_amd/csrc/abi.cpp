@@ -982,9 +982,10 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j (+ dnum_i . S0 + dden_i z0 from an
   // initial state), W columns of phi_K at a time
   // On the 32x32x16 kernels the passes write dphi (bf16, a column slice) and
-  // dV (reversed) in place; otherwise through tmp and a row copy.
-  // They also read their phi slice in place (rows m apart; the reversed
-  // sequence's from the reversed copy of phi_Q) instead of from a sliced copy.
+  // dV in place (in the original row order when they run over the reversed
+  // sequence); otherwise through tmp and a row copy. They also read their phi
+  // slice in place (rows m apart; on the reversed path the reversed sequence's
+  // from the reversed copy of phi_Q) instead of from a sliced copy.
   const bool inplace = on32(s, causal, MA, W);
   const bool sliced = inplace && n * m * 2 < (int64_t{1} << 31);
   const bool init = causal && (S0 || z0);
@@ -1166,9 +1167,9 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   const int64_t perMW = static_cast<int64_t>(MA) * W + MA;
   float *seg2 = f32(L.seg2), *dgb = f32(L.dgb);
   const bool init = S0 || z0;
-  // The passes read their phi slice in place (rows m apart; the reversed
-  // sequence's from the reversed copy of phi_Q) unless phi is too long for a
-  // 32-bit view, and dV is written in the original row order directly.
+  // The passes read their phi slice in place (rows m apart; on the reversed
+  // path the reversed sequence's from the reversed copy of phi_Q) unless phi
+  // is too long for a 32-bit view, and dV is written in the original row order.
   const bool sliced = n * m * 2 < (int64_t{1} << 31);
   uint16_t *rphq = anti ? nullptr : u16(L.b.rphq), *rphk = anti ? nullptr : u16(L.b.rphk);
   if (!anti) {
