@@ -228,7 +228,11 @@ llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* shape, const 
  * Performer section, and SLAY notes key design 3 for the normaliser; Theta is
  * learned end to end, notes' training strategy). The three sums are run as
  * causal linear attentions over bf16 features (dphi_K and dV as suffix sums,
- * anti-causal passes), so they carry the forward's bf16 rounding.
+ * anti-causal passes), so they carry the forward's bf16 rounding. Where phi
+ * is too long for a 32-bit view, or with LLOPS_BWD_REVERSED=1 in the
+ * environment (read at each call and by the workspace query), the suffix sums
+ * run as causal passes over reversed copies instead (a larger workspace; the
+ * same gradients up to summation order).
  * in_dtype BF16 only; kernels exist for p = 2, t in {1, 4}, d in {64, 128},
  * m in {64, 128, 256}, dv % 16 == 0 and dv <= 128 (else LLOPS_ERR_UNSUPPORTED).
  * theta_q and theta_k may alias; their gradients are still returned apart.

@@ -183,7 +183,11 @@ bool on32(const llops_shape_t* s, bool causal, int M, int DV);
 // anti-causal output passes on the 32x32x16 kernels when their in-place forms
 // apply (phi read in place, rows written in place); otherwise as causal
 // passes over reversed copies of their operands (and, gated, reversed gates).
+// LLOPS_BWD_REVERSED=1 in the environment (read at each call, by the workspace
+// query too) selects the reversed form wherever the anti-causal one applies.
 bool bwd_anti(const llops_shape_t* s) {
+  const char* env = getenv("LLOPS_BWD_REVERSED");
+  if (env && env[0] == '1') return false;
   return on32(s, true, bwd_ma(s), bwd_w(s)) && on32(s, true, s->m, s->dv) &&
          s->n * s->m * 2 < (int64_t{1} << 31);
 }

@@ -63,6 +63,15 @@ def test_causal_bwd(lib, case):
         assert err <= TOL_BF16, (name, err)
 
 
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=[str(CASES[0]), str(CASES[1])])
+def test_causal_bwd_reversed_form(lib, case, monkeypatch):
+    """The reversed-copy form of the suffix sums, selected with
+    LLOPS_BWD_REVERSED=1 on shapes that otherwise take the anti-causal passes,
+    against the oracle."""
+    monkeypatch.setenv("LLOPS_BWD_REVERSED", "1")
+    test_causal_bwd(lib, case)
+
 def test_causal_bwd_no_rows(lib):
     w = _w(1, 2, 0, 64, 64, 64, 4, True, True)
     th = dev(generate(w.replace(n=1))["theta_q"], torch.bfloat16)

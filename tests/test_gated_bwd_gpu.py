@@ -62,6 +62,14 @@ def test_gated_bwd(lib, case):
         assert err <= TOL_BF16, (nm, err)
 
 
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=[str(CASES[0]), str(CASES[1])])
+def test_gated_bwd_reversed_form(lib, case, monkeypatch):
+    """The reversed-copy form of the suffix sums (the fallback for phi too long
+    for a 32-bit view), selected with LLOPS_BWD_REVERSED=1, against the oracle."""
+    monkeypatch.setenv("LLOPS_BWD_REVERSED", "1")
+    test_gated_bwd(lib, case)
+
 def test_gated_bwd_zero_gate_matches_ungated(lib):
     """log_gate = 0: the same gradients as llops_linattn_causal_bwd (different
     kernels and rounding order), and the gate gradient against the oracle."""
