@@ -7,10 +7,11 @@
 //     (LLoPS notes, overall framework; blog, Performer section; SLAY notes,
 //      key design 3 for the +delta)
 //
-// A workgroup has one wave per 32 value columns (dv / 32 waves). Each wave
-// owns its columns of the fp32 state S (m/32 accumulator tiles) and a share of
-// the normaliser state z, kept as accumulator tiles of S against an all-ones
-// value block so that z and phi_Q . z come out of the same MFMAs. A segment is
+// The state pass has one wave per 32 value columns (dv / 32 waves), the
+// output pass two (one per feature half). Each wave owns its columns of the
+// fp32 state S (accumulator tiles) and a share of the normaliser state z,
+// kept as accumulator tiles of S against an all-ones value block so that z
+// and phi_Q . z come out of the same MFMAs. A segment is
 // walked in chunks of 32 tokens whose phi_Q / phi_K / V rows are staged in
 // LDS in their natural row-major layout (double buffered; the next chunk is
 // prefetched into registers while the current one computes). Operands that
@@ -28,6 +29,12 @@
 //   carry: S = exp(T) S_prev + phi_K^T diag(exp(T - L_k)) V,
 // and every exponent is <= 0 when g <= 0, so no factor overflows. The
 // per-chunk L values ride in LDS behind the chunk's rows.
+//
+// Anti-causal form (the backwards' suffix sums, key j >= query i): the output
+// pass walks a segment's chunks from the last to the first with the mirrored
+// intra-chunk mask, and each segment starts from the sum over the segments
+// after it; gated, query rows take exp(T - L_i), keys exp(L_j), the state
+// still decays by exp(T), and again no exponent is positive.
 //
 // Fragment conventions for v_mfma_f32_32x32x16_bf16 (lane l, c = l % 32,
 // hh = l / 32): an accumulator element 4i+e holds row 8i + 4hh + e of column
