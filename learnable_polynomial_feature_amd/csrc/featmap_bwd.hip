@@ -6,21 +6,22 @@
 //   dY_{j,r} = ds * prod_{j' != j} Y_{j',r}
 //   dX = sum_{j,r} dY_{j,r} Theta_{j,r}^T,   dTheta_{j,r} = X^T dY_{j,r}
 //
-// Both kernels stage one 32-feature block of every Theta_{j,r} side by side
-// in LDS rows of d, in Theta's natural layout, and recompute Y on 32x32x16
-// MFMA from it: nothing of size n x p*t*m is stored. Operands are read in P16
-// k-order (device.h), so recomputed tiles feed the next product from
-// registers. Row strides of staged blocks are chosen per read pattern: the
-// transposing reads want rows 8 banks apart, the 8-byte row reads 2 banks
-// apart, so a block read both ways is staged twice.
+// Both kernels recompute Y on 32x32x16 MFMA from one 32-feature block of
+// every Theta_{j,r} at a time: nothing of size n x p*t*m is stored.
 //
 // dX (featmap_bwd_dx): a workgroup of 8 waves owns 256 rows (32 per wave) of
 // one head and keeps their dX tile (rows x d) in registers. Per feature block
 // it recomputes every Y_{j,r} once in the transposed orientation (features x
-// rows), forms s and ds, keeps the Y tiles as bf16 pairs, and adds
-// dY_{j,r} Theta_{j,r}^T: dY as the A operand straight from registers,
-// Theta^T read as rows of the second staged copy. With t > 1 and a squared
-// map it also stores ds for the dTheta kernel.
+// rows; pass 1), forms s and ds, keeps the Y tiles as bf16 pairs, and adds
+// dY_{j,r} Theta_{j,r}^T (pass 2): dY as the A operand straight from
+// registers. The two passes read Theta as different operands (Theta^T with
+// k = d, then Theta^T with k = features), so a small kernel first copies Theta
+// into both fragment orders (pack_bwd_theta). Each pass then reads one
+// 1 KiB fragment per MFMA with lane-linear 16-byte LDS reads, and every block
+// lands in LDS by direct buffer-to-LDS copies issued one pass ahead: the
+// pass-2 block during pass 1, the next pass-1 block during pass 2, so neither
+// wait sits between the barriers. With t > 1 and a squared map the kernel
+// also stores ds for the dTheta kernel.
 //
 // dTheta (featmap_bwd_dth): a workgroup owns one feature block, one head and
 // one chunk of rows. Each wave keeps the Theta fragments of its rank in
@@ -50,6 +51,9 @@ struct BwdArgs {
   float* part;            // dTheta partials [slot][H][p][t][m][d]
   uint16_t* ds;           // [B][H][n][m] bf16: ds of the squared map when t > 1 (else null)
   uint16_t* ds_dump;      // 64 bytes written by lanes past the last row
+  const uint16_t* pk1;    // Theta^T fragments, k = d (pack_bwd_theta), [H'][m/32][t][p][d/16][64][8]
+  const uint16_t* pk2;    // Theta^T fragments, k = features, [H'][m/32][t*p][2][d/32][64][8]
+  int64_t pk_hstride;     // packed elements between heads (0 = shared)
   int64_t B, H, n;
   int m;
   int64_t th_hstride;     // Theta elements between heads (0 = shared)
@@ -63,19 +67,22 @@ struct BwdGeom {
   static constexpr int PT = P * T;
   static constexpr int KS = D / 16;        // 16-deep k-steps over d
   static constexpr int DT = D / 32;        // 32-wide tiles of d
-  // Row strides of staged blocks (elements). Transposing reads (4 rows x
-  // 32 bytes per 16 lanes) are conflict free when rows sit 64 bytes apart
-  // modulo 256 (measured: a 32-byte shift takes twice the LDS cycles);
-  // 8-byte row reads (frag_p16) when rows sit 8 bytes apart modulo 256.
+  // Row strides of the dTheta kernel's staged blocks (elements). Transposing
+  // reads (4 rows x 32 bytes per 16 lanes) are conflict free when rows sit
+  // 64 bytes apart modulo 256 (measured: a 32-byte shift takes twice the LDS
+  // cycles); 8-byte row reads (frag_p16) when rows sit 8 bytes apart modulo
+  // 256.
   static constexpr int TW = PT * 32 + 32;  // staged Theta, read transposed
   static constexpr int XW = D + 32;        // staged X, read transposed
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
   static constexpr int XP = D + 4;          // second copy of staged X (t = 4), read as rows
-  // Second staged copy of Theta in the dX kernel, read as rows (frag_p16):
-  // consecutive rows shift by 8 bytes. Rows are then only 8-byte aligned.
-  static constexpr int TW2 = PT * 32 + 4;
-  static constexpr size_t dx_lds() { return 1ull * D * (TW + TW2) * 2; }
+  // One feature block of packed Theta in either fragment order: PT * KS
+  // fragments of 64 lanes x 8 elements (1 KiB); the dX kernel holds one block
+  // of each order in LDS.
+  static constexpr int NFR = PT * KS;
+  static constexpr int BLK = NFR * 512;
+  static constexpr size_t dx_lds() { return 2ull * BLK * 2; }
   static constexpr size_t x_lds() {         // three row buffers
     return 3ull * RB * (T == 4 ? XW + XP : XW) * 2;
   }
@@ -83,13 +90,11 @@ struct BwdGeom {
   static_assert((PT * D * 4) % 256 == 0, "a Theta block splits evenly over the threads");
 };
 
-// Theta_{j,r}[k][fb*32 + c] -> Ts[k][(j*T + r)*32 + c] (row stride TW) and,
-// when Ts2 is given, again into Ts2 with row stride TW2; NT threads, and all
-// loads of a thread are issued before its first LDS store.
+// Theta_{j,r}[k][fb*32 + c] -> Ts[k][(j*T + r)*32 + c] (row stride TW); NT
+// threads, and all loads of a thread are issued before its first LDS store.
 template <int D, int PT, int NT = 256>
 __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t* th, int m,
-                                            int fb, int tid, uint16_t* Ts2 = nullptr,
-                                            int TW2 = 0) {
+                                            int fb, int tid) {
   static_assert((PT * D * 4) % NT == 0, "a Theta block splits evenly over the threads");
   constexpr int TL = PT * D * 4 / NT;
   u32x4 tv[TL];
@@ -104,10 +109,6 @@ __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t
   for (int i = 0; i < TL; ++i) {
     const int idx = tid + NT * i, k = idx / (4 * PT), pc = idx % (4 * PT);
     st16(Ts + k * TW + pc * 8, tv[i]);
-    if (Ts2) {  // rows of the second copy are 8-byte aligned
-      *reinterpret_cast<u32x2*>(Ts2 + k * TW2 + pc * 8) = u32x2{tv[i][0], tv[i][1]};
-      *reinterpret_cast<u32x2*>(Ts2 + k * TW2 + pc * 8 + 4) = u32x2{tv[i][2], tv[i][3]};
-    }
   }
 }
 
@@ -152,6 +153,59 @@ __device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64
 // ---------------------------------------------------------------------------
 // dX
 // ---------------------------------------------------------------------------
+// Theta in the dX kernel's two fragment orders. Fragment b of feature block
+// fb (P*T*KS per block; 64 lanes x 8 bf16 = 1 KiB) is, in
+//   pk1, b = (r*P + j)*KS + ks: the A operand of Y^T = Theta^T X^T; lane l
+//     holds Theta_{j,r}[16ks + 8(l/32) + e][32fb + l%32], e < 8 (k = d in
+//     natural order);
+//   pk2, b = (q*2 + hf)*DT + dt with q = r*P + j: the B operand of
+//     dY Theta^T; lane l holds Theta_{j,r}[32dt + l%32][32fb + 16hf + k_e],
+//     k_e in P16 order ({4hh..4hh+3, 8+4hh..8+4hh+3}, hh = l/32), the order
+//     of the dY accumulators that meet it.
+// Both orders have P*T*d*m elements per head; one thread writes 16 bytes of
+// each.
+__global__ __launch_bounds__(256) void pack_bwd_theta(const uint16_t* __restrict__ th,
+                                                      uint16_t* __restrict__ pk1,
+                                                      uint16_t* __restrict__ pk2, int64_t total,
+                                                      int P, int T, int D, int m) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int KS = D / 16, DT = D / 32, NFR = P * T * KS, FB = m / 32;
+  const int lane = static_cast<int>(idx & 63), hh = lane >> 5, c = lane & 31;
+  const int64_t f = idx >> 6;  // fragment index over heads and blocks
+  const int b = static_cast<int>(f % NFR);
+  const int fb = static_cast<int>((f / NFR) % FB);
+  const int64_t h = f / (static_cast<int64_t>(NFR) * FB);
+  const uint16_t* base = th + h * P * T * static_cast<int64_t>(D) * m;
+  {
+    const int ks = b % KS, j = (b / KS) % P, r = b / (KS * P);
+    const uint16_t* src =
+        base + ((static_cast<int64_t>(j) * T + r) * D + ks * 16 + 8 * hh) * m + fb * 32 + c;
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(m)]) |
+             (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(m)]) << 16);
+    st16(pk1 + idx * 8, u32x4{v[0], v[1], v[2], v[3]});
+  }
+  {
+    const int dt = b % DT, hf = (b / DT) % 2, q = b / (2 * DT), r = q / P, j = q % P;
+    const uint16_t* src = base + ((static_cast<int64_t>(j) * T + r) * D + dt * 32 + c) * m +
+                          fb * 32 + 16 * hf + 4 * hh;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
+    st16(pk2 + idx * 8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+}
+
+// LDS address of a shared-memory pointer, for the direct buffer-to-LDS copy
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_addr(uint16_t* p) {
+  return reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Every buffer-to-LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // GB: dphi is bf16 (else fp32).
 // OW: n >= 32, so a wave's 32 rows cross at most one sequence boundary.
 // SQ: the map is squared; with t > 1 the kernel then also stores ds (bf16)
@@ -160,14 +214,13 @@ template <int D, int P, int T, bool GB, bool OW, bool SQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_bwd_dx(BwdArgs a) {
   using G = BwdGeom<D, P, T>;
-  constexpr int KS = G::KS, DT = G::DT, TW = G::TW, TW2 = G::TW2, PT = G::PT;
+  constexpr int KS = G::KS, DT = G::DT, PT = G::PT, NFR = G::NFR, BLK = G::BLK;
   constexpr bool WDS = SQ && T > 1;
-  // The Theta block is staged twice: Ts (stride TW) for the transposing
-  // reads of the Y recompute, Ts2 (stride TW2) for the row reads of the dX
-  // product; each stride keeps its read pattern free of bank conflicts.
+  static_assert(NFR % 8 == 0, "a block's fragments split evenly over the 8 waves");
+  // L1 holds the pass-1 block (pk1 order), L2 the pass-2 block (pk2 order).
   extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* Ts = smem;
-  uint16_t* Ts2 = smem + D * TW;
+  uint16_t* L1 = smem;
+  uint16_t* L2 = smem + BLK;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
@@ -176,26 +229,35 @@ void featmap_bwd_dx(BwdArgs a) {
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 256 + w * 32;  // this wave's rows
 
   // X fragments (B operand of the transposed recompute): lane row t0 + c32,
-  // k = 16ks + {4hh..4hh+3, 8+4hh..8+4hh+3}; zeros past the end
+  // k = 16ks + 8hh .. +7; zeros past the end
   bf16x8 xf[KS];
   const bool ok = t0 + c32 < R;
   const int64_t tb = t0 < R ? t0 : R - 1;  // a wave past the end reads the last row
   const RowCursor cur = cursor_at(tb, a);
   const int64_t rho = rho_near<OW>(cur, ok ? c32 : R - 1 - tb, h, a);
   {
-    const uint16_t* src = a.X + rho * D + 4 * hh;
-    u32x2 lo[KS], hi[KS];
+    const uint16_t* src = a.X + rho * D + 8 * hh;
+    u32x4 v[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      lo[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16);
-      hi[ks] = *reinterpret_cast<const u32x2*>(src + ks * 16 + 8);
-    }
+    for (int ks = 0; ks < KS; ++ks) v[ks] = ld16(src + ks * 16);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      xf[ks] = as_bf16x8(ok ? u32x4{lo[ks][0], lo[ks][1], hi[ks][0], hi[ks][1]}
-                            : u32x4{0u, 0u, 0u, 0u});
+    for (int ks = 0; ks < KS; ++ks) xf[ks] = as_bf16x8(ok ? v[ks] : u32x4{0u, 0u, 0u, 0u});
   }
-  const uint16_t* th = a.theta + h * a.th_hstride;
+
+  // This head's packed Theta, block fb at byte fb * NFR KiB of either order;
+  // wave w copies fragments w, w + 8, ... of a block, 16 bytes per lane.
+  const uint32_t hbytes = static_cast<uint32_t>(a.m / 32) * (NFR * 1024u);
+  const __amdgpu_buffer_rsrc_t r1 = make_rsrc(a.pk1 + h * a.pk_hstride, hbytes);
+  const __amdgpu_buffer_rsrc_t r2 = make_rsrc(a.pk2 + h * a.pk_hstride, hbytes);
+  auto copy_block = [&](__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int fb)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NFR / 8; ++i) {
+      const int f = w + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_addr(dst + f * 512), 16, lane * 16u,
+                                               static_cast<uint32_t>(fb * NFR + f) * 1024u, 0, 0);
+    }
+  };
 
   // upstream gradient of this lane's row, features fb*32 + 8i + 4hh + {0..3},
   // as raw bits until ds is formed
@@ -224,18 +286,22 @@ void featmap_bwd_dx(BwdArgs a) {
       return __uint_as_float(gr[i][e]);
     }
   };
-  // (j, r) of the q-th rank product, r-major
-  auto jr_of = [](int q) { return (q % P) * T + q / P; };
+  auto frag_at = [&](const uint16_t* blk, int f) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(blk + f * 512 + lane * 8));
+  };
 
   f32x16 dx[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dx[dt] = zero16();
   const int FB = a.m / 32;
+  copy_block(r1, L1, 0);
+  wait_copies();
+  __syncthreads();
   for (int fb = 0; fb < FB; ++fb) {
     load_g(fb);
-    __syncthreads();  // every wave is done with the previous block's Theta
-    stage_theta<D, PT, 512>(Ts, TW, th, a.m, fb, tid, Ts2, TW2);
-    __syncthreads();
+    // this block's pass-2 fragments land while pass 1 runs (L2 was last
+    // read before the previous barrier)
+    copy_block(r2, L2, fb);
 
     // Pass 1, rank by rank: Y_{j,r} transposed (element 4i+e is feature
     // 8i + 4hh + e of row t0 + c32), its P chains interleaved over k, kept as
@@ -245,7 +311,7 @@ void featmap_bwd_dx(BwdArgs a) {
     auto read_a = [&](int idx) __attribute__((always_inline)) {
       // idx = (r*KS + ks)*P + j
       const int j = idx % P, ks = (idx / P) % KS, r = idx / (P * KS);
-      return frag_tr(Ts, TW, ks * 16, (j * T + r) * 32, lane);
+      return frag_at(L1, (r * P + j) * KS + ks);
     };
     uint32_t yb[PT][8];
     f32x16 s = zero16();
@@ -285,6 +351,11 @@ void featmap_bwd_dx(BwdArgs a) {
         const float gv = g_at(i, e);
         ds[4 * i + e] = ok ? (SQ ? 2.f * s[4 * i + e] * gv : gv) : 0.f;
       }
+    wait_copies();
+    __syncthreads();  // the pass-2 block has landed; every wave is done with L1
+    // the next block's pass-1 fragments land while pass 2 runs (the last
+    // block copies itself again: a branch here costs the allocator registers)
+    copy_block(r1, L1, fb + 1 < FB ? fb + 1 : fb);
     if constexpr (WDS) {
       uint16_t* dst = ok ? a.ds + rho * a.m + fb * 32 + 4 * hh : a.ds_dump + 16 * hh;
 #pragma unroll
@@ -294,22 +365,18 @@ void featmap_bwd_dx(BwdArgs a) {
     }
     // Pass 2, over (r, j): dY_{j,r} = ds * prod_{j' != j} Y_{j',r} in
     // registers, then dX[rows][d] += dY[rows][f] Theta^T[f][d]: dY as the A
-    // operand (lane row, k = features in P16 order), Theta^T read as rows of
-    // the staged block, two MFMAs ahead.
+    // operand (lane row, k = features in P16 order), Theta^T fragments from
+    // L2 in the same order as the MFMAs, two ahead.
     constexpr int NB = PT * 2 * DT;
-    auto read_b = [&](int idx) __attribute__((always_inline)) {
-      const int q = idx / (2 * DT), hf = (idx / DT) % 2, dt = idx % DT;
-      return frag_p16(Ts2, TW2, dt * 32, jr_of(q) * 32 + hf * 16, lane);
-    };
-    fr[0] = read_b(0);
-    fr[1] = read_b(1);
+    fr[0] = frag_at(L2, 0);
+    fr[1] = frag_at(L2, 1);
     bf16x8 af[2];
 #pragma unroll
     for (int q = 0; q < PT; ++q)
 #pragma unroll
     for (int hd = 0; hd < 2 * DT; ++hd) {
       const int idx = q * 2 * DT + hd, hf = hd / DT, dt = hd % DT, r = q / P, j = q % P;
-      if (idx + 2 < NB) fr[(idx + 2) % 3] = read_b(idx + 2);
+      if (idx + 2 < NB) fr[(idx + 2) % 3] = frag_at(L2, idx + 2);
       if (hf == 0 && dt == 0) {
         f32x16 dy = ds;
 #pragma unroll
@@ -329,6 +396,8 @@ void featmap_bwd_dx(BwdArgs a) {
       dx[dt] = mfma32x32x16(af[hf], fr[idx % 3], dx[dt]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    wait_copies();
+    __syncthreads();  // the next pass-1 block has landed; every wave is done with L2
   }
   // dx[dt] element 4i+e: row t0 + 8i + 4hh + e, column dt*32 + c32
 #pragma unroll
@@ -682,6 +751,15 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
     // with t > 1 and a squared map the dX kernel also stores ds (bf16) for
     // the dTheta kernel, which then reads it in place of dphi
     const bool wds = T > 1 && s.square;
+    const int64_t pk_total = hout * P * T * D * s.m / 8;  // 16-byte pieces of either order
+    // the dX kernel addresses one head's packed Theta through a 32-bit range
+    if ((pk_total + 255) / 256 > 0x7fffffffLL || pk_total * 16 / hout > 0xffffffffLL || !a.pk1 ||
+        !a.pk2)
+      return hipErrorInvalidValue;
+    LLOPS_LAUNCH("pack_bwd_theta", st, pack_bwd_theta,
+                 dim3(static_cast<unsigned>((pk_total + 255) / 256)), dim3(256), 0, st, a.theta,
+                 const_cast<uint16_t*>(a.pk1), const_cast<uint16_t*>(a.pk2), pk_total, P, T, D,
+                 s.m);
     auto* kx = s.n >= 32 ? (s.square ? featmap_bwd_dx<D, P, T, GB, true, true>
                                      : featmap_bwd_dx<D, P, T, GB, true, false>)
                          : (s.square ? featmap_bwd_dx<D, P, T, GB, false, true>
@@ -723,10 +801,27 @@ hipError_t launch_bwd_g(const FeatShape& s, const BwdArgs& a, int dphi_bf16, flo
 
 bool featmap_bwd_supported_impl(const FeatShape& s) { return bwd_key(s) != 0; }
 
-// Scratch: the partial dTheta slots, then (t > 1, squared) ds in bf16.
+// Scratch: the partial dTheta slots, then (t > 1, squared) ds in bf16, then
+// Theta in the dX kernel's two fragment orders.
 size_t bwd_part_bytes(const FeatShape& s) {
   const BwdPlan p = bwd_plan(s);
   const size_t b = static_cast<size_t>(p.slots) * s.H * s.p * s.t * s.m * s.d * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+// ds in bf16 (t > 1, squared), then 256 bytes that lanes past the last row
+// write instead
+size_t bwd_ds_bytes(const FeatShape& s) {
+  const size_t rows = static_cast<size_t>(s.B) * s.H * s.n;
+  const size_t b = s.t > 1 && s.square && rows > 0 ? rows * s.m * 2 + 256 : 0;
+  return (b + 255) / 256 * 256;
+}
+
+// Theta in one of the dX kernel's two fragment orders (rows > 0 only)
+size_t bwd_pack_bytes(const FeatShape& s) {
+  if (static_cast<size_t>(s.B) * s.H * s.n == 0) return 0;
+  const size_t th_heads = s.theta_per_head ? s.H : 1;
+  const size_t b = th_heads * s.p * s.t * s.d * s.m * sizeof(uint16_t);
   return (b + 255) / 256 * 256;
 }
 
@@ -736,10 +831,7 @@ bool featmap_bwd_supported(const FeatShape& s) { return featmap_bwd_supported_im
 
 size_t featmap_bwd_ws_bytes(const FeatShape& s) {
   if (!bwd_key(s)) return 0;
-  // ds, then 256 bytes that lanes past the last row write instead
-  const size_t rows = static_cast<size_t>(s.B) * s.H * s.n;
-  const size_t ds = s.t > 1 && s.square && rows > 0 ? rows * s.m * 2 + 256 : 0;
-  return bwd_part_bytes(s) + ds;
+  return bwd_part_bytes(s) + bwd_ds_bytes(s) + 2 * bwd_pack_bytes(s);
 }
 
 hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* theta,
@@ -756,6 +848,12 @@ hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* the
              ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + bwd_part_bytes(s))
              : nullptr;
   a.ds_dump = a.ds ? a.ds + static_cast<size_t>(s.B) * s.H * s.n * s.m : nullptr;
+  if (ws && bwd_pack_bytes(s)) {
+    char* pk = static_cast<char*>(ws) + bwd_part_bytes(s) + bwd_ds_bytes(s);
+    a.pk1 = reinterpret_cast<const uint16_t*>(pk);
+    a.pk2 = reinterpret_cast<const uint16_t*>(pk + bwd_pack_bytes(s));
+  }
+  a.pk_hstride = s.theta_per_head ? static_cast<int64_t>(s.p) * s.t * s.d * s.m : 0;
   a.B = s.B;
   a.H = s.H;
   a.n = s.n;
