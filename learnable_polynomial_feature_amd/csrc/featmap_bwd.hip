@@ -83,8 +83,8 @@ struct BwdGeom {
   static constexpr int NFR = PT * KS;
   static constexpr int BLK = NFR * 512;
   static constexpr size_t dx_lds() { return 2ull * BLK * 2; }
-  static constexpr size_t x_lds() {         // three row buffers
-    return 3ull * RB * (T == 4 ? XW + XP : XW) * 2;
+  static constexpr size_t x_lds() {         // three row buffers, each with a gradient tile
+    return 3ull * RB * ((T == 4 ? XW + XP : XW) + 32) * 2;
   }
   static_assert(PT % 2 == 0, "staged Theta rows need an even block count to stay conflict free");
   static_assert((PT * D * 4) % 256 == 0, "a Theta block splits evenly over the threads");
@@ -456,6 +456,12 @@ void featmap_bwd_dth(BwdArgs a) {
   const int wr = T == 4 ? 0 : 32 * w;  // this wave's first row within a step
   const void* gsrc = (T > 1 && a.square) ? static_cast<const void*>(a.ds) : a.dphi;
   const bool own_s = T == 1 && a.square;
+  // GT: a bf16 gradient whose step rows are consecutive travels with the X
+  // rows: each step's RB x 32 tile is requested once per workgroup (8 bytes
+  // per thread and 32 rows), staged in LDS, and each wave reads its 16 values
+  // with two transposing reads instead of 16 two-byte loads of its own.
+  constexpr bool GT = GB && RM == 2;
+  constexpr int GL = GT ? RB / 32 : 1;  // 8-byte gradient pieces per thread and step
 
   stage_theta<D, PT>(Ts, TW, a.theta + h * a.th_hstride, a.m, fb, tid);
   __syncthreads();
@@ -478,16 +484,27 @@ void featmap_bwd_dth(BwdArgs a) {
   // requested one step ahead and kept as raw bits until the step widens it.
   // Rows past the chunk read as zeros (RM 2) or as its last row.
   u32x4 xv[XL];
-  uint32_t gn[16];
+  u32x2 gv[GL];  // GT: this thread's pieces of a step's gradient tile
+  uint32_t gn[GT ? 1 : 16];
   constexpr uint32_t ES = GB ? 2 : 4;
   auto step_rows = [&](int64_t t) __attribute__((always_inline)) {
     return static_cast<uint32_t>(r1 - t < RB ? r1 - t : RB);
   };
   auto load_x = [&](const RowCursor& c, int64_t t) __attribute__((always_inline)) {
     if constexpr (RM == 2) {  // the step's rows are consecutive in memory
-      const auto rx = make_rsrc(a.X + ((c.b * a.H + h) * a.n + c.i) * D, step_rows(t) * D * 2u);
+      const int64_t row0 = (c.b * a.H + h) * a.n + c.i;
+      const auto rx = make_rsrc(a.X + row0 * D, step_rows(t) * D * 2u);
 #pragma unroll
       for (int it = 0; it < XL; ++it) xv[it] = buf_ld16(rx, (tid + 256u * it) * 16u, 0u);
+      if constexpr (GT) {  // piece idx: row idx / 8, features fb*32 + 4 (idx % 8) .. + 3
+        const auto rg = make_rsrc(static_cast<const uint16_t*>(gsrc) + row0 * a.m,
+                                  step_rows(t) * static_cast<uint32_t>(a.m) * 2u);
+#pragma unroll
+        for (int it = 0; it < GL; ++it) {
+          const uint32_t idx = tid + 256u * it;
+          gv[it] = buf_ld8(rg, ((idx >> 3) * static_cast<uint32_t>(a.m) + fb * 32 + (idx & 7) * 4) * 2u);
+        }
+      }
     } else {
 #pragma unroll
       for (int it = 0; it < XL; ++it) {
@@ -498,7 +515,10 @@ void featmap_bwd_dth(BwdArgs a) {
     }
   };
   auto load_g = [&](const RowCursor& c, int64_t t) __attribute__((always_inline)) {
-    if constexpr (RM == 2) {
+    if constexpr (GT) {
+      (void)c;
+      (void)t;
+    } else if constexpr (RM == 2) {
       const auto rg = make_rsrc(static_cast<const char*>(gsrc) + ((c.b * a.H + h) * a.n + c.i) * a.m * ES,
                                 step_rows(t) * static_cast<uint32_t>(a.m) * ES);
 #pragma unroll
@@ -527,11 +547,15 @@ void featmap_bwd_dth(BwdArgs a) {
   // operands of Y); each stride keeps its own read pattern free of bank
   // conflicts. With t = 1 one copy serves both.
   constexpr int XP = T == 4 ? G::XP : XW;
-  constexpr int BUFW = T == 4 ? RB * (XW + XP) : RB * XW;
+  constexpr int XBW = T == 4 ? RB * (XW + XP) : RB * XW;  // X rows of one buffer
+  constexpr int BUFW = XBW + RB * 32;                      // then the gradient tile (GT)
   auto xbuf = [&](int k) __attribute__((always_inline)) { return smem + k * BUFW; };
   auto pbuf = [&](int k) __attribute__((always_inline)) {
     return T == 4 ? smem + k * BUFW + RB * XW : smem + k * BUFW;
   };
+  // gradient tile: RB rows of 32 features, rows 64 bytes apart (conflict free
+  // for the transposing reads)
+  auto gbuf = [&](int k) __attribute__((always_inline)) { return smem + k * BUFW + XBW; };
   auto store_x = [&](int k, int64_t t) __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < XL; ++it) {
@@ -543,11 +567,34 @@ void featmap_bwd_dth(BwdArgs a) {
         *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8 + 4) = u32x2{v[2], v[3]};
       }
     }
+    if constexpr (GT) {
+#pragma unroll
+      for (int it = 0; it < GL; ++it) {
+        const int idx = tid + 256 * it, rr = idx >> 3;
+        *reinterpret_cast<u32x2*>(gbuf(k) + rr * 32 + (idx & 7) * 4) =
+            t + rr < r1 ? gv[it] : u32x2{0u, 0u};
+      }
+    }
   };
   auto widen = [&]() __attribute__((always_inline)) {
     f32x16 v;
+    if constexpr (!GT) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
+      for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
+    }
+    return v;
+  };
+  // a step's gradient from its staged tile (two transposing reads, rows in
+  // P16 order): element 4i+e is row wr + 8i + 4hh + e, column fb*32 + c32
+  auto tile_g = [&](const u32x4& lo, const u32x4& hi) __attribute__((always_inline)) {
+    f32x16 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(lo[q] << 16);
+      v[2 * q + 1] = __uint_as_float(lo[q] & 0xffff0000u);
+      v[8 + 2 * q] = __uint_as_float(hi[q] << 16);
+      v[8 + 2 * q + 1] = __uint_as_float(hi[q] & 0xffff0000u);
+    }
     return v;
   };
   // the cursor of the last step whose X was requested (it stays on the
@@ -590,6 +637,11 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         xb[hf][dt] = frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
+    u32x4 gtl, gth;
+    if constexpr (GT) {
+      gtl = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr, 0, lane));
+      gth = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr + 16, 0, lane));
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
     // Y_{j,rk} in the natural orientation: element 4i+e is row wr + 8i + 4hh + e
     // of the step, lane column c32 is feature fb*32 + c32
@@ -604,7 +656,11 @@ void featmap_bwd_dth(BwdArgs a) {
     // the next step's Y operands, in flight during this step's products
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(pbuf(nxt), XP, wr, ks * 16, lane);
-    f32x16 ds = g;
+    f32x16 ds;
+    if constexpr (GT)
+      ds = tile_g(gtl, gth);
+    else
+      ds = g;
     if (own_s) {
       f32x16 s = y[0];
 #pragma unroll

@@ -41,6 +41,10 @@ BWD_CASES = [
     (3, 2, 1, 128, 64, 4, True, True, False),
     (1, 4, 2048, 64, 128, 1, False, False, False),
     (2, 2, 1500, 128, 64, 4, True, True, True),
+    # whole 32-row (t = 4) and 128-row (t = 1) steps with a bf16 gradient: the
+    # dTheta kernel stages the gradient tile of each step in shared memory
+    (1, 2, 4096, 128, 256, 4, True, False, False),
+    (2, 2, 1024, 64, 128, 1, True, False, True),
 ]
 
 
