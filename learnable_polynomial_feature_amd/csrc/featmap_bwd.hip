@@ -14,14 +14,13 @@
 // it recomputes every Y_{j,r} once in the transposed orientation (features x
 // rows; pass 1), forms s and ds, keeps the Y tiles as bf16 pairs, and adds
 // dY_{j,r} Theta_{j,r}^T (pass 2): dY as the A operand straight from
-// registers. The two passes read Theta as different operands (Theta^T with
-// k = d, then Theta^T with k = features), so a small kernel first copies Theta
-// into both fragment orders (pack_bwd_theta). Each pass then reads one
-// 1 KiB fragment per MFMA with lane-linear 16-byte LDS reads, and every block
-// lands in LDS by direct buffer-to-LDS copies issued one pass ahead: the
-// pass-2 block during pass 1, the next pass-1 block during pass 2, so neither
-// wait sits between the barriers. With t > 1 and a squared map the kernel
-// also stores ds for the dTheta kernel.
+// registers. A small kernel first copies Theta into fragment order
+// (pack_bwd_theta); pass 1 reads each 1 KiB fragment with lane-linear
+// 16-byte LDS reads, pass 2 reads the same block transposed, and blocks are
+// double-buffered in LDS, each landing by direct buffer-to-LDS copies while
+// the previous one is used. With t > 1 and a squared map the kernel also
+// stores ds for the dTheta kernel, in its own register order (32 contiguous
+// bytes per lane).
 //
 // dTheta (featmap_bwd_dth): a workgroup owns one feature block, one head and
 // one chunk of rows. Each wave keeps the Theta fragments of its rank in
@@ -30,7 +29,10 @@
 // (rows x features), so dY^T is an A operand from registers and X (read
 // transposed from LDS) the B operand. With t = 4 the four waves take one rank
 // each over the same 32 rows and read ds from the dX kernel; with t = 1 each
-// wave takes its own 32 of a 128-row step and forms s itself. The workgroup
+// wave takes its own 32 of a 128-row step and forms s itself. A bf16
+// gradient of whole steps travels with the X rows: each step's tile is
+// staged once per workgroup and read back transposed by every wave. The
+// workgroup
 // writes its chunk's partial dTheta (one per wave for t = 1);
 // featmap_bwd_reduce sums the partials (and the heads, for a shared Theta) in
 // a fixed order and transposes.
@@ -49,10 +51,11 @@ struct BwdArgs {
   const void* dphi;       // [B][H][n][m], fp32 or bf16
   float* dX;              // [B][H][n][d]
   float* part;            // dTheta partials [slot][H][p][t][m][d]
-  uint16_t* ds;           // [B][H][n][m] bf16: ds of the squared map when t > 1 (else null)
-  uint16_t* ds_dump;      // 64 bytes written by lanes past the last row
-  const uint16_t* pk1;    // Theta^T fragments, k = d (pack_bwd_theta), [H'][m/32][t][p][d/16][64][8]
-  const uint16_t* pk2;    // Theta^T fragments, k = features, [H'][m/32][t*p][2][d/32][64][8]
+  // ds of the squared map when t > 1 (else null), bf16 in the dX kernel's
+  // register order: [H][ds_tph 32-row tiles][m/32][64 lanes][16]
+  uint16_t* ds;
+  int64_t ds_tph;         // ds tiles per head: 8 per 256-row workgroup of the dX kernel
+  const uint16_t* pk;     // Theta^T fragments (pack_bwd_theta), [H'][m/32][t][p][d/16][64][8]
   int64_t pk_hstride;     // packed elements between heads (0 = shared)
   int64_t B, H, n;
   int m;
@@ -77,12 +80,10 @@ struct BwdGeom {
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
   static constexpr int XP = D + 4;          // second copy of staged X (t = 4), read as rows
-  // One feature block of packed Theta in either fragment order: PT * KS
-  // fragments of 64 lanes x 8 elements (1 KiB); the dX kernel holds one block
-  // of each order in LDS.
+  // One feature block of packed Theta: PT * KS fragments of 64 lanes x 8
+  // elements (1 KiB); the dX kernel double-buffers it in LDS.
   static constexpr int NFR = PT * KS;
   static constexpr int BLK = NFR * 512;
-  static constexpr size_t dx_lds() { return 2ull * BLK * 2; }
   static constexpr size_t x_lds() {         // three row buffers, each with a gradient tile
     return 3ull * RB * ((T == 4 ? XW + XP : XW) + 32) * 2;
   }
@@ -153,54 +154,57 @@ __device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64
 // ---------------------------------------------------------------------------
 // dX
 // ---------------------------------------------------------------------------
-// Theta in the dX kernel's two fragment orders. Fragment b of feature block
-// fb (P*T*KS per block; 64 lanes x 8 bf16 = 1 KiB) is, in
-//   pk1, b = (r*P + j)*KS + ks: the A operand of Y^T = Theta^T X^T; lane l
-//     holds Theta_{j,r}[16ks + 8(l/32) + e][32fb + l%32], e < 8 (k = d in
-//     natural order);
-//   pk2, b = (q*2 + hf)*DT + dt with q = r*P + j: the B operand of
-//     dY Theta^T; lane l holds Theta_{j,r}[32dt + l%32][32fb + 16hf + k_e],
-//     k_e in P16 order ({4hh..4hh+3, 8+4hh..8+4hh+3}, hh = l/32), the order
-//     of the dY accumulators that meet it.
-// Both orders have P*T*d*m elements per head; one thread writes 16 bytes of
-// each.
+// Theta^T in fragment order for the dX kernel. Fragment b = (r*P + j)*KS + ks
+// of feature block fb is the A operand of Y^T = Theta^T X^T: lane l holds
+// Theta_{j,r}[16ks + 8(l/32) + e][32fb + l%32], e < 8 (k = d in natural
+// order), as one 16-byte chunk. Chunks sit at swizzled places within the
+// fragment (packed_chunk) so that both reads of the dX kernel are free of LDS
+// bank conflicts: its pass 1 reads each lane's chunk whole, its pass 2 reads
+// 8-byte halves of chunks transposed (see featmap_bwd_dx). One thread packs
+// one chunk.
+__host__ __device__ constexpr int packed_chunk(int l) {
+  // l = 32h + c: chunk 32h + (c & 16) + ((c + 8h) & 15). Any 16 consecutive
+  // lanes still take 16 different chunks mod 16 (pass 1), and the 16 (h, c)
+  // pairs of one transposed read, c in 8 consecutive features of a 16-block,
+  // land in 16 different ones (pass 2).
+  return 32 * (l >> 5) + (l & 16) + (((l & 31) + 8 * (l >> 5)) & 15);
+}
+
 __global__ __launch_bounds__(256) void pack_bwd_theta(const uint16_t* __restrict__ th,
-                                                      uint16_t* __restrict__ pk1,
-                                                      uint16_t* __restrict__ pk2, int64_t total,
+                                                      uint16_t* __restrict__ pk, int64_t total,
                                                       int P, int T, int D, int m) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= total) return;
-  const int KS = D / 16, DT = D / 32, NFR = P * T * KS, FB = m / 32;
+  const int KS = D / 16, NFR = P * T * KS, FB = m / 32;
   const int lane = static_cast<int>(idx & 63), hh = lane >> 5, c = lane & 31;
   const int64_t f = idx >> 6;  // fragment index over heads and blocks
   const int b = static_cast<int>(f % NFR);
   const int fb = static_cast<int>((f / NFR) % FB);
   const int64_t h = f / (static_cast<int64_t>(NFR) * FB);
-  const uint16_t* base = th + h * P * T * static_cast<int64_t>(D) * m;
-  {
-    const int ks = b % KS, j = (b / KS) % P, r = b / (KS * P);
-    const uint16_t* src =
-        base + ((static_cast<int64_t>(j) * T + r) * D + ks * 16 + 8 * hh) * m + fb * 32 + c;
-    uint32_t v[4];
+  const int ks = b % KS, j = (b / KS) % P, r = b / (KS * P);
+  const uint16_t* src = th + h * P * T * static_cast<int64_t>(D) * m +
+                        ((static_cast<int64_t>(j) * T + r) * D + ks * 16 + 8 * hh) * m + fb * 32 + c;
+  uint32_t v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(m)]) |
-             (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(m)]) << 16);
-    st16(pk1 + idx * 8, u32x4{v[0], v[1], v[2], v[3]});
-  }
-  {
-    const int dt = b % DT, hf = (b / DT) % 2, q = b / (2 * DT), r = q / P, j = q % P;
-    const uint16_t* src = base + ((static_cast<int64_t>(j) * T + r) * D + dt * 32 + c) * m +
-                          fb * 32 + 16 * hf + 4 * hh;
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-    st16(pk2 + idx * 8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-  }
+  for (int i = 0; i < 4; ++i)
+    v[i] = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(m)]) |
+           (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(m)]) << 16);
+  st16(pk + (f * 64 + packed_chunk(lane)) * 8, u32x4{v[0], v[1], v[2], v[3]});
 }
 
 // LDS address of a shared-memory pointer, for the direct buffer-to-LDS copy
 __device__ __forceinline__ __attribute__((address_space(3))) void* lds_addr(uint16_t* p) {
   return reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(p));
+}
+
+// ds_read_b64_tr_b16 through an address-space cast, which keeps the pointer's
+// shared array visible to the compiler (a cast through an integer hides it,
+// and a read of unknown origin waits for every buffer-to-LDS copy in flight)
+__device__ __forceinline__ uint2 tr64(const uint16_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
 }
 
 // Every buffer-to-LDS copy this wave issued has landed.
@@ -210,6 +214,14 @@ __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)
 // OW: n >= 32, so a wave's 32 rows cross at most one sequence boundary.
 // SQ: the map is squared; with t > 1 the kernel then also stores ds (bf16)
 // for the dTheta kernel.
+//
+// Per feature block the workgroup reads one packed Theta block from LDS in
+// two ways: pass 1 takes fragment (r, j, ks) as the A operand of Y^T; pass 2
+// needs Theta_{j,r} as the B operand of dY Theta^T (column d, k = features
+// in P16 order), which is the same data transposed: two ds_read_b64_tr_b16
+// per operand, each lane supplying 4 consecutive d of one feature (8 bytes of
+// a chunk). Blocks are double-buffered: block fb+1 is copied into the other
+// buffer while block fb is used, and one barrier per block separates them.
 template <int D, int P, int T, bool GB, bool OW, bool SQ>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void featmap_bwd_dx(BwdArgs a) {
@@ -217,10 +229,12 @@ void featmap_bwd_dx(BwdArgs a) {
   constexpr int KS = G::KS, DT = G::DT, PT = G::PT, NFR = G::NFR, BLK = G::BLK;
   constexpr bool WDS = SQ && T > 1;
   static_assert(NFR % 8 == 0, "a block's fragments split evenly over the 8 waves");
-  // L1 holds the pass-1 block (pk1 order), L2 the pass-2 block (pk2 order).
-  extern __shared__ __align__(16) uint16_t smem[];
-  uint16_t* L1 = smem;
-  uint16_t* L2 = smem + BLK;
+  // The two block buffers are distinct shared arrays, and the feature-block
+  // loop below is unrolled by two so that every read names its buffer: the
+  // compiler can then tell that a read of one never waits for the copy into
+  // the other.
+  __shared__ __align__(16) uint16_t LA[BLK];
+  __shared__ __align__(16) uint16_t LB[BLK];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, c32 = lane & 31;
@@ -244,20 +258,31 @@ void featmap_bwd_dx(BwdArgs a) {
     for (int ks = 0; ks < KS; ++ks) xf[ks] = as_bf16x8(ok ? v[ks] : u32x4{0u, 0u, 0u, 0u});
   }
 
-  // This head's packed Theta, block fb at byte fb * NFR KiB of either order;
-  // wave w copies fragments w, w + 8, ... of a block, 16 bytes per lane.
-  const uint32_t hbytes = static_cast<uint32_t>(a.m / 32) * (NFR * 1024u);
-  const __amdgpu_buffer_rsrc_t r1 = make_rsrc(a.pk1 + h * a.pk_hstride, hbytes);
-  const __amdgpu_buffer_rsrc_t r2 = make_rsrc(a.pk2 + h * a.pk_hstride, hbytes);
-  auto copy_block = [&](__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int fb)
-      __attribute__((always_inline)) {
+  // This head's packed Theta, block fb at byte fb * NFR KiB; wave w copies
+  // fragments w, w + 8, ... of a block, 16 bytes per lane.
+  const __amdgpu_buffer_rsrc_t rpk =
+      make_rsrc(a.pk + h * a.pk_hstride, static_cast<uint32_t>(a.m / 32) * (NFR * 1024u));
+  auto copy_block = [&](uint16_t* dst, int fb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NFR / 8; ++i) {
       const int f = w + 8 * i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_addr(dst + f * 512), 16, lane * 16u,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, lds_addr(dst + f * 512), 16, lane * 16u,
                                                static_cast<uint32_t>(fb * NFR + f) * 1024u, 0, 0);
     }
   };
+  // pass 1: this lane's chunk of a fragment
+  const int a_off = packed_chunk(lane) * 8;
+  // pass 2: in the 16-lane group g4 = lane/16 of a transposing read, lane s
+  // supplies d = 32dt + 16(g4 & 1) + 4(s & 3) .. +3 (fragment ks = 2dt + (g4 & 1),
+  // lane half (s & 3) / 2, chunk half (s & 1)) of feature row
+  // 16hf + 4(g4 / 2) + s / 4, and 8 rows further for the second read
+  const int g4 = lane >> 4, s4 = lane & 15;
+  auto b_off = [&](int c) {
+    return (g4 & 1) * 512 + packed_chunk(32 * ((s4 & 3) >> 1) + c) * 8 + (s4 & 1) * 4;
+  };
+  const int crow = 4 * (g4 >> 1) + (s4 >> 2);
+  const int b_lo0 = b_off(crow), b_hi0 = b_off(crow + 8);
+  const int b_lo1 = b_off(16 + crow), b_hi1 = b_off(24 + crow);
 
   // upstream gradient of this lane's row, features fb*32 + 8i + 4hh + {0..3},
   // as raw bits until ds is formed
@@ -286,22 +311,39 @@ void featmap_bwd_dx(BwdArgs a) {
       return __uint_as_float(gr[i][e]);
     }
   };
-  auto frag_at = [&](const uint16_t* blk, int f) __attribute__((always_inline)) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(blk + f * 512 + lane * 8));
-  };
 
   f32x16 dx[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dx[dt] = zero16();
   const int FB = a.m / 32;
-  copy_block(r1, L1, 0);
-  wait_copies();
-  __syncthreads();
-  for (int fb = 0; fb < FB; ++fb) {
+  // ds of the previous block, stored at the top of the next iteration, ahead
+  // of the copies: memory operations count down in issue order, so a wait
+  // for a store (before its registers are reused) placed after the copies
+  // would also wait for them. Block 0's tile first takes zeros, overwritten
+  // in order by the same lanes.
+  u32x4 dsp[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+  auto store_ds = [&](int fb) __attribute__((always_inline)) {
+    if constexpr (WDS) {  // this wave's 32 x 32 tile, 32 contiguous bytes per lane
+      uint16_t* dst = a.ds + ((h * a.ds_tph + t0 / 32) * FB + fb) * 1024 + lane * 16;
+      st16(dst, dsp[0]);
+      st16(dst + 8, dsp[1]);
+    }
+  };
+  // one feature block: blk holds it, nxt takes the next one
+  auto block = [&](const uint16_t* blk, uint16_t* nxt, int fb) __attribute__((always_inline)) {
+    // lane offsets made opaque per block, so the fragment addresses of the
+    // two buffers are formed here (base + immediate) instead of being
+    // hoisted out of the loop into registers of their own
+    int ao = a_off, bl0 = b_lo0, bh0 = b_hi0, bl1 = b_lo1, bh1 = b_hi1;
+    asm volatile("" : "+v"(ao), "+v"(bl0), "+v"(bh0), "+v"(bl1), "+v"(bh1));
+    store_ds(fb > 0 ? fb - 1 : 0);
+    // the gradient next, so that waiting for it leaves the copies below in
+    // flight
     load_g(fb);
-    // this block's pass-2 fragments land while pass 1 runs (L2 was last
-    // read before the previous barrier)
-    copy_block(r2, L2, fb);
+    // the next block lands in the other buffer, last read before the
+    // previous barrier (the last block copies itself again: a branch here
+    // costs the allocator registers)
+    copy_block(nxt, fb + 1 < FB ? fb + 1 : fb);
 
     // Pass 1, rank by rank: Y_{j,r} transposed (element 4i+e is feature
     // 8i + 4hh + e of row t0 + c32), its P chains interleaved over k, kept as
@@ -311,7 +353,7 @@ void featmap_bwd_dx(BwdArgs a) {
     auto read_a = [&](int idx) __attribute__((always_inline)) {
       // idx = (r*KS + ks)*P + j
       const int j = idx % P, ks = (idx / P) % KS, r = idx / (P * KS);
-      return frag_at(L1, (r * P + j) * KS + ks);
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(blk + ((r * P + j) * KS + ks) * 512 + ao));
     };
     uint32_t yb[PT][8];
     f32x16 s = zero16();
@@ -351,32 +393,35 @@ void featmap_bwd_dx(BwdArgs a) {
         const float gv = g_at(i, e);
         ds[4 * i + e] = ok ? (SQ ? 2.f * s[4 * i + e] * gv : gv) : 0.f;
       }
-    wait_copies();
-    __syncthreads();  // the pass-2 block has landed; every wave is done with L1
-    // the next block's pass-1 fragments land while pass 2 runs (the last
-    // block copies itself again: a branch here costs the allocator registers)
-    copy_block(r1, L1, fb + 1 < FB ? fb + 1 : fb);
     if constexpr (WDS) {
-      uint16_t* dst = ok ? a.ds + rho * a.m + fb * 32 + 4 * hh : a.ds_dump + 16 * hh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x2*>(dst + 8 * i) =
-            u32x2{pack_bf16x2(ds[4 * i], ds[4 * i + 1]), pack_bf16x2(ds[4 * i + 2], ds[4 * i + 3])};
+      for (int q = 0; q < 2; ++q)
+        dsp[q] = u32x4{pack_bf16x2(ds[8 * q + 0], ds[8 * q + 1]),
+                       pack_bf16x2(ds[8 * q + 2], ds[8 * q + 3]),
+                       pack_bf16x2(ds[8 * q + 4], ds[8 * q + 5]),
+                       pack_bf16x2(ds[8 * q + 6], ds[8 * q + 7])};
     }
     // Pass 2, over (r, j): dY_{j,r} = ds * prod_{j' != j} Y_{j',r} in
     // registers, then dX[rows][d] += dY[rows][f] Theta^T[f][d]: dY as the A
-    // operand (lane row, k = features in P16 order), Theta^T fragments from
-    // L2 in the same order as the MFMAs, two ahead.
+    // operand (lane row, k = features in P16 order), Theta^T by transposing
+    // reads of the block, two MFMAs ahead.
     constexpr int NB = PT * 2 * DT;
-    fr[0] = frag_at(L2, 0);
-    fr[1] = frag_at(L2, 1);
+    auto read_b = [&](int idx) __attribute__((always_inline)) {
+      const int q = idx / (2 * DT), hf = (idx / DT) % 2, dt = idx % DT;
+      const uint16_t* base = blk + (q * KS + 2 * dt) * 512;
+      const uint2 lo = tr64(base + (hf ? bl1 : bl0));
+      const uint2 hi = tr64(base + (hf ? bh1 : bh0));
+      return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+    };
+    fr[0] = read_b(0);
+    fr[1] = read_b(1);
     bf16x8 af[2];
 #pragma unroll
     for (int q = 0; q < PT; ++q)
 #pragma unroll
     for (int hd = 0; hd < 2 * DT; ++hd) {
       const int idx = q * 2 * DT + hd, hf = hd / DT, dt = hd % DT, r = q / P, j = q % P;
-      if (idx + 2 < NB) fr[(idx + 2) % 3] = frag_at(L2, idx + 2);
+      if (idx + 2 < NB) fr[(idx + 2) % 3] = read_b(idx + 2);
       if (hf == 0 && dt == 0) {
         f32x16 dy = ds;
 #pragma unroll
@@ -397,8 +442,18 @@ void featmap_bwd_dx(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_copies();
-    __syncthreads();  // the next pass-1 block has landed; every wave is done with L2
+    __syncthreads();  // the next block has landed; every wave is done with this one
+  };
+  copy_block(LA, 0);
+  wait_copies();
+  __syncthreads();
+  for (int fb = 0;; fb += 2) {
+    block(LA, LB, fb);
+    if (fb + 1 >= FB) break;
+    block(LB, LA, fb + 1);
+    if (fb + 2 >= FB) break;
   }
+  store_ds(FB - 1);
   // dx[dt] element 4i+e: row t0 + 8i + 4hh + e, column dt*32 + c32
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -422,9 +477,10 @@ void featmap_bwd_dx(BwdArgs a) {
 // GB: the gradient read (dphi, or ds from the dX kernel) is bf16.
 // With t = 4 and a squared map the gradient read is ds itself; with t = 1
 // and a squared map each wave forms s from its own (only) rank.
-template <int D, int P, int T, bool GB, int RM>
+template <int D, int P, int T, bool GB, int RM, bool DS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void featmap_bwd_dth(BwdArgs a) {
+  static_assert(!DS || GB, "ds is bf16");
   using G = BwdGeom<D, P, T>;
   constexpr int KS = G::KS, DT = G::DT, TW = G::TW, XW = G::XW, PT = G::PT;
   static_assert(T == 1 || T == 4, "one rank per wave (t = 4) or one rank for all (t = 1)");
@@ -454,14 +510,24 @@ void featmap_bwd_dth(BwdArgs a) {
   const int64_t r1 = min(R, r0 + a.chunk_rows);
   const int rk = T == 4 ? w : 0;       // the rank this wave recomputes
   const int wr = T == 4 ? 0 : 32 * w;  // this wave's first row within a step
-  const void* gsrc = (T > 1 && a.square) ? static_cast<const void*>(a.ds) : a.dphi;
+  const void* gsrc = DS ? static_cast<const void*>(a.ds) : a.dphi;
   const bool own_s = T == 1 && a.square;
+  // element of ds for head-local row t, feature fb*32 + f (the dX kernel's
+  // tile order: lane 32 (f/4 % 2) + t % 32, element 4 (f/8) + f % 4)
+  auto ds_at = [&](int64_t t, int f) __attribute__((always_inline)) {
+    return ((h * a.ds_tph + (t >> 5)) * FB + fb) * 1024 +
+           (32 * ((f >> 2) & 1) + (t & 31)) * 16 + 4 * (f >> 3) + (f & 3);
+  };
   // GT: a bf16 gradient whose step rows are consecutive travels with the X
   // rows: each step's RB x 32 tile is requested once per workgroup (8 bytes
   // per thread and 32 rows), staged in LDS, and each wave reads its 16 values
   // with two transposing reads instead of 16 two-byte loads of its own.
   constexpr bool GT = GB && RM == 2;
   constexpr int GL = GT ? RB / 32 : 1;  // 8-byte gradient pieces per thread and step
+  // ds tile pieces (GT, DS): wave w moves rows 8w .. 8w + 7 whole (the 8
+  // pieces of a row are elements 4i .. 4i+3, i < 4, of dX lanes row and
+  // 32 + row), so its 64 shared-memory stores fill 512 contiguous bytes
+  const int ds_row = 8 * w + ((lane >> 2) & 7);
 
   stage_theta<D, PT>(Ts, TW, a.theta + h * a.th_hstride, a.m, fb, tid);
   __syncthreads();
@@ -496,7 +562,11 @@ void featmap_bwd_dth(BwdArgs a) {
       const auto rx = make_rsrc(a.X + row0 * D, step_rows(t) * D * 2u);
 #pragma unroll
       for (int it = 0; it < XL; ++it) xv[it] = buf_ld16(rx, (tid + 256u * it) * 16u, 0u);
-      if constexpr (GT) {  // piece idx: row idx / 8, features fb*32 + 4 (idx % 8) .. + 3
+      if constexpr (GT && DS) {  // the step is one 2 KiB tile of ds
+        static_assert(GL == 1, "ds exists for t = 4 only: one piece per thread");
+        const auto rg = make_rsrc(a.ds + ds_at(t, 0), 2048u);
+        gv[0] = buf_ld8(rg, ((32 * hh + ds_row) * 16 + 4 * (lane & 3)) * 2u);
+      } else if constexpr (GT) {  // piece idx: row idx / 8, features fb*32 + 4 (idx % 8) .. + 3
         const auto rg = make_rsrc(static_cast<const uint16_t*>(gsrc) + row0 * a.m,
                                   step_rows(t) * static_cast<uint32_t>(a.m) * 2u);
 #pragma unroll
@@ -536,7 +606,8 @@ void featmap_bwd_dth(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int64_t r = wr + 8 * i + 4 * hh + e;
           const int64_t o = t + r < r1 ? r : r1 - 1 - t;
-          const int64_t idx = rho_near<RM == 1>(c, o, h, a) * a.m + fb * 32 + c32;
+          const int64_t idx =
+              DS ? ds_at(t + o, c32) : rho_near<RM == 1>(c, o, h, a) * a.m + fb * 32 + c32;
           gn[4 * i + e] = GB ? static_cast<uint32_t>(static_cast<const uint16_t*>(gsrc)[idx])
                              : __float_as_uint(static_cast<const float*>(gsrc)[idx]);
         }
@@ -567,7 +638,10 @@ void featmap_bwd_dth(BwdArgs a) {
         *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8 + 4) = u32x2{v[2], v[3]};
       }
     }
-    if constexpr (GT) {
+    if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 8 (lane % 4) + 4 hh ..
+      *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 8 * (lane & 3) + 4 * hh) =
+          t + ds_row < r1 ? gv[0] : u32x2{0u, 0u};
+    } else if constexpr (GT) {
 #pragma unroll
       for (int it = 0; it < GL; ++it) {
         const int idx = tid + 256 * it, rr = idx >> 3;
@@ -577,7 +651,7 @@ void featmap_bwd_dth(BwdArgs a) {
     }
   };
   auto widen = [&]() __attribute__((always_inline)) {
-    f32x16 v;
+    f32x16 v = zero16();
     if constexpr (!GT) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) v[k] = __uint_as_float(GB ? gn[k] << 16 : gn[k]);
@@ -807,33 +881,31 @@ hipError_t launch_bwd_t(const FeatShape& s, const BwdArgs& a, float* dtheta, hip
     // with t > 1 and a squared map the dX kernel also stores ds (bf16) for
     // the dTheta kernel, which then reads it in place of dphi
     const bool wds = T > 1 && s.square;
-    const int64_t pk_total = hout * P * T * D * s.m / 8;  // 16-byte pieces of either order
+    const int64_t pk_total = hout * P * T * D * s.m / 8;  // 16-byte chunks of packed Theta
     // the dX kernel addresses one head's packed Theta through a 32-bit range
-    if ((pk_total + 255) / 256 > 0x7fffffffLL || pk_total * 16 / hout > 0xffffffffLL || !a.pk1 ||
-        !a.pk2)
+    if ((pk_total + 255) / 256 > 0x7fffffffLL || pk_total * 16 / hout > 0xffffffffLL || !a.pk)
       return hipErrorInvalidValue;
     LLOPS_LAUNCH("pack_bwd_theta", st, pack_bwd_theta,
                  dim3(static_cast<unsigned>((pk_total + 255) / 256)), dim3(256), 0, st, a.theta,
-                 const_cast<uint16_t*>(a.pk1), const_cast<uint16_t*>(a.pk2), pk_total, P, T, D,
-                 s.m);
+                 const_cast<uint16_t*>(a.pk), pk_total, P, T, D, s.m);
     auto* kx = s.n >= 32 ? (s.square ? featmap_bwd_dx<D, P, T, GB, true, true>
                                      : featmap_bwd_dx<D, P, T, GB, true, false>)
                          : (s.square ? featmap_bwd_dx<D, P, T, GB, false, true>
                                      : featmap_bwd_dx<D, P, T, GB, false, false>);
-    hipError_t e = allow_lds(kx, G::dx_lds());
-    if (e != hipSuccess) return e;
+    // the dX kernel's LDS (two packed blocks) is static
     LLOPS_LAUNCH("featmap_bwd_dx", st, kx,
-                 dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H)), dim3(512),
-                 G::dx_lds(), st, a);
+                 dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(s.H)), dim3(512), 0,
+                 st, a);
     const size_t lds = std::max(G::theta_lds(), G::x_lds());
     const int rm = s.n % G::RB == 0 ? 2 : s.n >= G::RB ? 1 : 0;
-    auto* kt = wds ? (rm == 2 ? featmap_bwd_dth<D, P, T, true, 2>
-                      : rm == 1 ? featmap_bwd_dth<D, P, T, true, 1>
-                                : featmap_bwd_dth<D, P, T, true, 0>)
-                   : (rm == 2 ? featmap_bwd_dth<D, P, T, GB, 2>
-                      : rm == 1 ? featmap_bwd_dth<D, P, T, GB, 1>
-                                : featmap_bwd_dth<D, P, T, GB, 0>);
-    e = allow_lds(kt, lds);
+    constexpr bool DS = T > 1;  // the kernel reads ds (wds), which exists for t > 1 only
+    auto* kt = wds ? (rm == 2 ? featmap_bwd_dth<D, P, T, true, 2, DS>
+                      : rm == 1 ? featmap_bwd_dth<D, P, T, true, 1, DS>
+                                : featmap_bwd_dth<D, P, T, true, 0, DS>)
+                   : (rm == 2 ? featmap_bwd_dth<D, P, T, GB, 2, false>
+                      : rm == 1 ? featmap_bwd_dth<D, P, T, GB, 1, false>
+                                : featmap_bwd_dth<D, P, T, GB, 0, false>);
+    const hipError_t e = allow_lds(kt, lds);
     if (e != hipSuccess) return e;
     const int64_t wgs = static_cast<int64_t>(s.m / 32) * a.chunks * s.H;
     if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -858,22 +930,23 @@ hipError_t launch_bwd_g(const FeatShape& s, const BwdArgs& a, int dphi_bf16, flo
 bool featmap_bwd_supported_impl(const FeatShape& s) { return bwd_key(s) != 0; }
 
 // Scratch: the partial dTheta slots, then (t > 1, squared) ds in bf16, then
-// Theta in the dX kernel's two fragment orders.
+// Theta in the dX kernel's fragment order.
 size_t bwd_part_bytes(const FeatShape& s) {
   const BwdPlan p = bwd_plan(s);
   const size_t b = static_cast<size_t>(p.slots) * s.H * s.p * s.t * s.m * s.d * sizeof(float);
   return (b + 255) / 256 * 256;
 }
 
-// ds in bf16 (t > 1, squared), then 256 bytes that lanes past the last row
-// write instead
+// ds tiles per head: one per 32 rows of every 256-row dX workgroup
+int64_t bwd_ds_tph(const FeatShape& s) { return (s.B * s.n + 255) / 256 * 8; }
+
+// ds in bf16 (t > 1, squared), in 32-row tiles of 32 x m
 size_t bwd_ds_bytes(const FeatShape& s) {
-  const size_t rows = static_cast<size_t>(s.B) * s.H * s.n;
-  const size_t b = s.t > 1 && s.square && rows > 0 ? rows * s.m * 2 + 256 : 0;
-  return (b + 255) / 256 * 256;
+  if (!(s.t > 1 && s.square) || s.B * s.n == 0) return 0;
+  return static_cast<size_t>(s.H) * bwd_ds_tph(s) * 32 * s.m * sizeof(uint16_t);
 }
 
-// Theta in one of the dX kernel's two fragment orders (rows > 0 only)
+// Theta in the dX kernel's fragment order (rows > 0 only)
 size_t bwd_pack_bytes(const FeatShape& s) {
   if (static_cast<size_t>(s.B) * s.H * s.n == 0) return 0;
   const size_t th_heads = s.theta_per_head ? s.H : 1;
@@ -887,7 +960,7 @@ bool featmap_bwd_supported(const FeatShape& s) { return featmap_bwd_supported_im
 
 size_t featmap_bwd_ws_bytes(const FeatShape& s) {
   if (!bwd_key(s)) return 0;
-  return bwd_part_bytes(s) + bwd_ds_bytes(s) + 2 * bwd_pack_bytes(s);
+  return bwd_part_bytes(s) + bwd_ds_bytes(s) + bwd_pack_bytes(s);
 }
 
 hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* theta,
@@ -903,12 +976,10 @@ hipError_t launch_featmap_bwd(const FeatShape& s, const void* X, const void* the
   a.ds = s.t > 1 && s.square && ws
              ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + bwd_part_bytes(s))
              : nullptr;
-  a.ds_dump = a.ds ? a.ds + static_cast<size_t>(s.B) * s.H * s.n * s.m : nullptr;
-  if (ws && bwd_pack_bytes(s)) {
-    char* pk = static_cast<char*>(ws) + bwd_part_bytes(s) + bwd_ds_bytes(s);
-    a.pk1 = reinterpret_cast<const uint16_t*>(pk);
-    a.pk2 = reinterpret_cast<const uint16_t*>(pk + bwd_pack_bytes(s));
-  }
+  a.ds_tph = bwd_ds_tph(s);
+  if (ws && bwd_pack_bytes(s))
+    a.pk = reinterpret_cast<const uint16_t*>(static_cast<char*>(ws) + bwd_part_bytes(s) +
+                                             bwd_ds_bytes(s));
   a.pk_hstride = s.theta_per_head ? static_cast<int64_t>(s.p) * s.t * s.d * s.m : 0;
   a.B = s.B;
   a.H = s.H;

@@ -272,14 +272,17 @@ def test_featmap_bwd_pointers_and_workspace(L):
     s = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4)
     need = L.llops_workspace_bytes(ctypes.byref(s), _lib.ENTRY_FEATMAP_BWD)
     slot = 4 * 2 * 4 * 256 * 128 * 4  # one fp32 partial dTheta for every head
-    ds = 1 * 4 * 4096 * 256 * 2 + 256  # t > 1 and squared: ds of every row in bf16, and a 256-byte slot
-    pack = 2 * 4 * 128 * 256 * 2  # one head's Theta in bf16, kept in two fragment orders
-    assert need > ds and (need - ds - 2 * 4 * pack) % slot == 0
+    ds = 1 * 4 * 4096 * 256 * 2  # t > 1 and squared: ds of every row in bf16 (whole 256-row tiles)
+    pack = 2 * 4 * 128 * 256 * 2  # one head's Theta in bf16, in fragment order
+    assert need > ds and (need - ds - 4 * pack) % slot == 0
     plain = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, square=0)
     assert L.llops_workspace_bytes(ctypes.byref(plain), _lib.ENTRY_FEATMAP_BWD) == need - ds
     shared = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=4, theta_per_head=0)
-    assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP_BWD) == \
-        need - 2 * 3 * pack
+    assert L.llops_workspace_bytes(ctypes.byref(shared), _lib.ENTRY_FEATMAP_BWD) == need - 3 * pack
+    ragged = _bwd_shape(batch=1, heads=4, n=4000, d=128, m=256, t=4)  # ds rounds up to 4096 rows
+    assert L.llops_workspace_bytes(ctypes.byref(ragged), _lib.ENTRY_FEATMAP_BWD) - ds == \
+        L.llops_workspace_bytes(ctypes.byref(_bwd_shape(batch=1, heads=4, n=4000, d=128, m=256,
+                                                        t=4, square=0)), _lib.ENTRY_FEATMAP_BWD)
     args = [FAKE] * 5
     assert L.llops_featmap_bwd(ctypes.byref(s), *args, FAKE, need - 1, None) == 3
     assert "workspace" in _err(L)
@@ -302,7 +305,7 @@ def test_featmap_bwd_pointers_and_workspace(L):
     t1 = _bwd_shape(batch=1, heads=4, n=4096, d=128, m=256, t=1)
     need1 = L.llops_workspace_bytes(ctypes.byref(t1), _lib.ENTRY_FEATMAP_BWD)
     pack1 = 2 * 1 * 128 * 256 * 2
-    assert need1 > 0 and (need1 - 2 * 4 * pack1) % (4 * 4 * 2 * 1 * 256 * 128 * 4) == 0
+    assert need1 > 0 and (need1 - 4 * pack1) % (4 * 4 * 2 * 1 * 256 * 128 * 4) == 0
 
 
 def _cbwd_shape(**kw):
