@@ -149,6 +149,9 @@ llops_status_t llops_featmap_bwd(const llops_shape_t* shape, const void* X,
  * (notes, overall framework; paper Sec. 1; blog, Performer section).
  * Q, K, V, theta_q, theta_k in in_dtype; out fp32 [batch][heads][n][dv].
  * theta_q may equal theta_k. ws: llops_workspace_bytes(shape, LLOPS_ENTRY_LINATTN).
+ * fp32 inputs with (d, m, p, t) = (16, 32, 2, 2), n <= 1024 and dv in
+ * {4, 8, ..., 20} run as one launch (one workgroup per sequence); other
+ * shapes run the feature map and the segment passes through the workspace.
  */
 llops_status_t llops_linattn_fwd(const llops_shape_t* shape, const void* Q,
                                  const void* K, const void* V,

@@ -654,6 +654,17 @@ llops_status_t attention(const llops_shape_t* s, bool causal, const void* Q, con
     else
       LLOPS_HIP(llops::launch_attn_out_bf16(a, pq, pk, vv, state, st_seg, st_bh, o, st),
                 "attn_out");
+  } else if (!causal && llops::linattn_small_f32_ok(BH, s->n, s->d, s->dv, s->m, s->p, s->t)) {
+    // small fp32 sequences: the whole non-causal pass in one launch
+    const int64_t th_hstride =
+        s->theta_per_head ? static_cast<int64_t>(s->p) * s->t * s->d * s->m : 0;
+    LLOPS_HIP(llops::launch_linattn_small_f32(
+                  s->batch, s->heads, s->n, s->d, s->dv, s->m, s->p, s->t,
+                  static_cast<const float*>(Q), static_cast<const float*>(K),
+                  static_cast<const float*>(V), static_cast<const float*>(tq),
+                  static_cast<const float*>(tk), th_hstride, s->square, s->normalize, s->delta,
+                  static_cast<float*>(out), st),
+              "linattn_small_f32");
   } else {
     LLOPS_HIP(llops::launch_featmap_f32(fs, jobs, 2, st), "featmap");
     const float* pq = reinterpret_cast<const float*>(w + L.phiq);

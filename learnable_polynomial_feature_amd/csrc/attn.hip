@@ -409,6 +409,290 @@ __global__ __launch_bounds__(256) void seg_state_f32(AttnArgs a, const float* __
   }
 }
 
+// Small non-causal fp32 problems in one launch: one workgroup of 512 threads
+// per (b, h) sequence computes phi_K tile by tile, accumulates the state
+// [S | z], then phi_Q tile by tile and the read-out (paper Sec. 1: S =
+// phi_K^T V, z = phi_K^T 1, out = phi_Q S / (phi_Q z + delta)). Four launches
+// (feature map, segment states, scan, output) cost more than the whole
+// problem at these sizes. (d, m, p, t) are compile-time so every loop
+// unrolls and LDS reads pipeline. Work goes in 4-wide groups (float4 through
+// LDS): (row, 4 features) for phi, (feature, column group, row quarter) for
+// the state, (row, column group) for the output; the value tile carries an
+// extra [1 0 0 0] column group, so z and phi_Q z come out as one more group.
+// The state is summed per tile (its row quarters first), then into the
+// running sum: short chains keep the fp32 rounding near that of the
+// segment passes.
+constexpr int kSmallTR = 256;  // rows per tile
+constexpr int kSmallNT = 512;  // threads per workgroup
+
+struct SmallArgs {
+  const float* Q;
+  const float* K;
+  const float* V;
+  const float* tq;  // [H'][p][t][d][m]
+  const float* tk;
+  float* out;
+  int64_t H, n;
+  int dv;
+  int64_t th_hstride;  // elements between heads' Theta (0 = shared)
+  int square, normalize;
+  float delta;
+};
+
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st_f4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void fma4(float a, const float4& b, float4& c) {
+  c.x = fmaf(a, b.x, c.x);
+  c.y = fmaf(a, b.y, c.y);
+  c.z = fmaf(a, b.z, c.z);
+  c.w = fmaf(a, b.w, c.w);
+}
+
+template <int D, int M, int P, int T>
+struct SmallGeom {
+  static constexpr int PTDM = P * T * D * M;
+  // LDS floats for value width dv: Theta_K, Theta_Q, [S | z] (M x W), X and
+  // the value tile, phi, per-quarter state partials, denominators
+  static constexpr int64_t floats(int dv) {
+    return 2LL * PTDM + M * (dv + 4) + kSmallTR * (D + (dv + 4) + M + 1) + 4LL * M * (dv + 4);
+  }
+};
+
+template <int D, int M, int P, int T>
+__global__ __launch_bounds__(kSmallNT) void linattn_small_f32(SmallArgs a) {
+  using G = SmallGeom<D, M, P, T>;
+  constexpr int PTDM = G::PTDM, D4 = D / 4, M4 = M / 4, TR = kSmallTR, NT = kSmallNT;
+  static_assert(D % 4 == 0 && M % 4 == 0, "4-wide groups");
+  extern __shared__ __align__(16) float sm[];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t h = bh % a.H;
+  const int dv = a.dv, W = dv + 4, W4 = W / 4, V4 = dv / 4;
+  float* thk = sm;
+  float* thq = thk + PTDM;
+  float* Sa = thq + PTDM;             // M x W
+  float* X = Sa + M * W;              // TR x D
+  float* Va = X + TR * D;             // TR x W
+  float* ph = Va + TR * W;            // TR x M
+  float* den = ph + TR * M;           // TR
+  float* part = den + TR;             // 4 x M x W
+  const float* gk = a.tk + h * a.th_hstride;
+  const float* gq = a.tq + h * a.th_hstride;
+  for (int i = tid; i < PTDM / 4; i += NT) {
+    st_f4(thk + 4 * i, ld_f4(gk + 4 * i));
+    st_f4(thq + 4 * i, ld_f4(gq + 4 * i));
+  }
+  const int64_t n = a.n;
+  const float* Kb = a.K + bh * n * D;
+  const float* Qb = a.Q + bh * n * D;
+  const float* Vb = a.V + bh * n * dv;
+  float* Ob = a.out + bh * n * dv;
+  const int nt = static_cast<int>((n + TR - 1) / TR);
+  auto rows_of = [&](int tile) {
+    return static_cast<int>(min(static_cast<int64_t>(TR), n - static_cast<int64_t>(tile) * TR));
+  };
+  // A tile's rows travel through registers one tile ahead: this thread's
+  // pieces tid + NT q of X (TR*D4 <= 2 NT) and of the value tile (K tiles;
+  // TR*W4 <= 3 NT).
+  static_assert(TR * D4 <= 2 * NT, "two X pieces per thread");
+  float4 xp[2], vp[3];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) xp[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) vp[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](const float* src, int tile, bool values) {
+    const int64_t r0 = static_cast<int64_t>(tile) * TR;
+    const int rows = rows_of(tile);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = tid + NT * q;
+      if (i < TR * D4) {
+        const int row = i / D4, k4 = i - row * D4;
+        xp[q] = row < rows ? ld_f4(src + (r0 + row) * D + 4 * k4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    if (values) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const int i = tid + NT * q;
+        if (i < TR * W4) {
+          const int row = i / W4, c4 = i - row * W4;
+          vp[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (row < rows)
+            vp[q] = c4 < V4 ? ld_f4(Vb + (r0 + row) * dv + 4 * c4) : make_float4(1.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  };
+  auto place = [&](bool values) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (tid + NT * q < TR * D4) st_f4(X + 4 * (tid + NT * q), xp[q]);
+    if (values) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (tid + NT * q < TR * W4) st_f4(Va + 4 * (tid + NT * q), vp[q]);
+    }
+  };
+  // phi of the tile's rows with Theta th: thread = (4 rows, features
+  // 4q .. 4q+3), so each Theta read from LDS serves four rows
+  constexpr int PR = 2;  // rows per thread
+  static_assert(TR % PR == 0, "whole row groups");
+  auto phi_tile = [&](const float* th, int rows) {
+    for (int gi = tid; gi < (TR / PR) * M4; gi += NT) {
+      const int rb = gi / M4, f = (gi - rb * M4) * 4, row0 = rb * PR;
+      float xr[PR][D];  // this thread's rows, held for all (j, r)
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+#pragma unroll
+        for (int k4 = 0; k4 < D4; ++k4) {
+          const float4 x = ld_f4(X + (row0 + i) * D + 4 * k4);
+          xr[i][4 * k4] = x.x;
+          xr[i][4 * k4 + 1] = x.y;
+          xr[i][4 * k4 + 2] = x.z;
+          xr[i][4 * k4 + 3] = x.w;
+        }
+      float4 acc[PR];
+#pragma unroll
+      for (int i = 0; i < PR; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 1
+      for (int r = 0; r < T; ++r) {
+        float4 prod[PR];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+          const float* tb = th + (j * T + r) * D * M + f;
+          float4 y[PR];
+#pragma unroll
+          for (int i = 0; i < PR; ++i) y[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int k = 0; k < D; ++k) {
+            const float4 w = ld_f4(tb + k * M);
+#pragma unroll
+            for (int i = 0; i < PR; ++i) fma4(xr[i][k], w, y[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < PR; ++i) {
+            if (j == 0) {
+              prod[i] = y[i];
+            } else {
+              prod[i].x *= y[i].x;
+              prod[i].y *= y[i].y;
+              prod[i].z *= y[i].z;
+              prod[i].w *= y[i].w;
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < PR; ++i) {
+          acc[i].x += prod[i].x;
+          acc[i].y += prod[i].y;
+          acc[i].z += prod[i].z;
+          acc[i].w += prod[i].w;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PR; ++i) {
+        float4 v = acc[i];
+        if (a.square) {
+          v.x *= v.x;
+          v.y *= v.y;
+          v.z *= v.z;
+          v.w *= v.w;
+        }
+        if (row0 + i >= rows) v = make_float4(0.f, 0.f, 0.f, 0.f);
+        st_f4(ph + (row0 + i) * M + f, v);
+      }
+    }
+  };
+  __syncthreads();
+  // state: thread = (group (feature, column group), row quarter); the
+  // quarters' sums are added in a fixed order into the running sum
+  const int SG = M * W4;
+  static_assert(TR % 4 == 0, "row quarters");
+  float4 sacc = make_float4(0.f, 0.f, 0.f, 0.f);  // threads tid < SG own group tid
+  fetch(Kb, 0, true);
+  for (int tile = 0; tile < nt; ++tile) {
+    const int rows = rows_of(tile);
+    place(true);
+    __syncthreads();
+    // the next tile (or the first query tile) is in flight while this one runs
+    if (tile + 1 < nt)
+      fetch(Kb, tile + 1, true);
+    else
+      fetch(Qb, 0, false);
+    phi_tile(thk, rows);
+    __syncthreads();
+    for (int u = tid; u < 4 * SG; u += NT) {
+      const int qr = u / SG, g = u - qr * SG, f = g / W4, c4 = g - f * W4;
+      float4 ps = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+      for (int row = qr * (TR / 4); row < (qr + 1) * (TR / 4); ++row)
+        fma4(ph[row * M + f], ld_f4(Va + row * W + 4 * c4), ps);
+      st_f4(part + 4 * u, ps);
+    }
+    __syncthreads();
+    if (tid < SG) {
+      float4 t = ld_f4(part + 4 * tid);
+#pragma unroll
+      for (int qr = 1; qr < 4; ++qr) {
+        const float4 v = ld_f4(part + 4 * (qr * SG + tid));
+        t.x += v.x;
+        t.y += v.y;
+        t.z += v.z;
+        t.w += v.w;
+      }
+      sacc.x += t.x;
+      sacc.y += t.y;
+      sacc.z += t.z;
+      sacc.w += t.w;
+    }
+  }
+  if (tid < SG) st_f4(Sa + (tid / W4) * W + 4 * (tid % W4), sacc);
+  __syncthreads();
+  // read-out: thread = (row, column group); the last column group is phi_Q z
+  for (int tile = 0; tile < nt; ++tile) {
+    const int64_t r0 = static_cast<int64_t>(tile) * TR;
+    const int rows = rows_of(tile);
+    place(false);
+    __syncthreads();
+    if (tile + 1 < nt) fetch(Qb, tile + 1, false);
+    phi_tile(thq, rows);
+    __syncthreads();
+    float4 o[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int g = tid + NT * q;
+      if (g < TR * W4) {
+        const int row = g / W4, c4 = g - row * W4;
+#pragma unroll 8
+        for (int f = 0; f < M; ++f) fma4(ph[row * M + f], ld_f4(Sa + f * W + 4 * c4), o[q]);
+        if (c4 == V4) den[row] = o[q].x + a.delta;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int g = tid + NT * q;
+      if (g < TR * W4) {
+        const int row = g / W4, c4 = g - row * W4;
+        if (row < rows && c4 < V4) {
+          float4 v = o[q];
+          if (a.normalize) {
+            const float dd = den[row];
+            v.x /= dd;
+            v.y /= dd;
+            v.z /= dd;
+            v.w /= dd;
+          }
+          st_f4(Ob + (r0 + row) * dv + 4 * c4, v);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_out_f32(AttnArgs a, const float* __restrict__ phiq,
                                                     const float* __restrict__ phik,
@@ -746,6 +1030,45 @@ hipError_t launch_attn_out_f32(const AttnShape& s, const float* phiq, const floa
   else
     LLOPS_LAUNCH("attn_out_f32", st, attn_out_f32<false>, grid, dim3(256), lds, st, a, phiq, phik, v, state,
                        st_seg, st_bh, out);
+  return hipGetLastError();
+}
+
+// (d, m, p, t) of the small-sequence kernel's instantiations
+int small_key(int d, int m, int p, int t) {
+  const int key = d * 1000000 + m * 1000 + p * 10 + t;
+  switch (key) {
+    case 16032022: return key;  // d = 16, m = 32, p = 2, t = 2
+    default: return 0;
+  }
+}
+
+bool linattn_small_f32_ok(int64_t BH, int64_t n, int d, int dv, int m, int p, int t) {
+  if (BH <= 0 || BH > 0x7fffffffLL || n <= 0 || n > 1024 || dv % 4 || dv <= 0) return false;
+  if (!small_key(d, m, p, t)) return false;
+  const int W4 = dv / 4 + 1;
+  if (m * W4 > kSmallNT || kSmallTR * W4 > 3 * kSmallNT) return false;
+  return SmallGeom<16, 32, 2, 2>::floats(dv) * 4 <= 160 * 1024;
+}
+
+hipError_t launch_linattn_small_f32(int64_t B, int64_t H, int64_t n, int d, int dv, int m, int p,
+                                    int t, const float* Q, const float* K, const float* V,
+                                    const float* tq, const float* tk, int64_t th_hstride,
+                                    int square, int normalize, float delta, float* out,
+                                    hipStream_t st) {
+  if (!linattn_small_f32_ok(B * H, n, d, dv, m, p, t)) return hipErrorInvalidValue;
+  SmallArgs a{Q, K, V, tq, tk, out, H, n, dv, th_hstride, square, normalize, delta};
+  switch (small_key(d, m, p, t)) {
+    case 16032022: {
+      const size_t lds = static_cast<size_t>(SmallGeom<16, 32, 2, 2>::floats(dv) * 4);
+      const hipError_t e = allow_lds(linattn_small_f32<16, 32, 2, 2>, lds);
+      if (e != hipSuccess) return e;
+      LLOPS_LAUNCH("linattn_small_f32", st, (linattn_small_f32<16, 32, 2, 2>),
+                   dim3(static_cast<unsigned>(B * H)), dim3(kSmallNT),
+                   lds, st, a);
+      break;
+    }
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

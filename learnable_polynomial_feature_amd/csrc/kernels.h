@@ -216,6 +216,15 @@ hipError_t launch_attn_out32_gated_den(const AttnShape& a, const uint16_t* phiq,
                                        const float* state, float* out, float* den,
                                        hipStream_t st);
 // fp32 gated passes over the raw log gates g [BH][n] (any chunk, m, dv).
+// Non-causal fp32 attention of small sequences in one launch (one workgroup
+// per (b, h)): Q, K [B][H][n][d], V and out [B][H][n][dv], Theta [H'][p][t][d][m]
+// (th_hstride elements apart, 0 = shared). ok() says whether the shape takes it.
+bool linattn_small_f32_ok(int64_t BH, int64_t n, int d, int dv, int m, int p, int t);
+hipError_t launch_linattn_small_f32(int64_t B, int64_t H, int64_t n, int d, int dv, int m, int p,
+                                    int t, const float* Q, const float* K, const float* V,
+                                    const float* tq, const float* tk, int64_t th_hstride,
+                                    int square, int normalize, float delta, float* out,
+                                    hipStream_t st);
 hipError_t launch_seg_state_f32_gated(const AttnShape& a, const float* phik, const float* v,
                                       const float* log_gate, float* gseg, float* seg,
                                       hipStream_t st);

@@ -214,6 +214,41 @@ def test_noncausal(lib, dtype, normalize):
     assert rel_fro(host(out), want) <= tol
 
 
+# fp32 non-causal shapes. The first five take the one-launch kernel for small
+# sequences (d = 16, m = 32, p = 2, t = 2, n <= 1024, dv a multiple of 4), with
+# a ragged last 256-row tile, one row, dv = 4 and 8, and a shared Theta; the
+# rest take the segment passes (n above 1024; other (d, m, p, t)).
+# Normalised cases with an unsquared map stay short: there phi_Q z can come
+# near zero, and a longer sum leaves fp32 short of the 1e-5 bound on both paths
+F32_NONCAUSAL = [
+    # B, H, n, d, dv, m, p, t, square, normalize, shared
+    (1, 1, 1, 16, 16, 32, 2, 2, False, True, False),
+    (2, 3, 33, 16, 8, 32, 2, 2, True, True, False),
+    (1, 2, 64, 16, 16, 32, 2, 2, False, True, True),
+    (2, 2, 130, 16, 4, 32, 2, 2, True, False, False),
+    (3, 1, 700, 16, 16, 32, 2, 2, True, True, False),
+    (1, 2, 1500, 16, 16, 32, 2, 2, True, True, False),
+    (2, 3, 100, 16, 12, 32, 3, 1, True, False, False),
+    (1, 2, 64, 8, 16, 16, 2, 2, False, True, True),
+    (1, 1, 200, 10, 6, 24, 2, 2, True, True, False),
+]
+
+
+@pytest.mark.parametrize("case", F32_NONCAUSAL, ids=[str(c) for c in F32_NONCAUSAL])
+def test_noncausal_f32_shapes(lib, case):
+    B, H, n, d, dv, m, p, t, square, normalize, shared = case
+    w = _w(B, H, n, d, dv, m, p, t, dtype="f32", square=square, normalize=normalize, delta=1e-3)
+    x, g = _inputs(w, shared=shared)
+    announce(f"noncausal f32 {case}")
+    out = lib.llops_linattn_fwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"],
+                                square=square, normalize=normalize, delta=1e-3)
+    torch.cuda.synchronize()
+    want = O.linattn_bh(x["Q"], x["K"], x["V"], x["theta_q"], x["theta_k"], square=square,
+                        normalize=normalize, delta=1e-3)
+    assert rel_fro(host(out), want) <= TOL_F32
+    assert row_rel_max(host(out), want) <= 10 * TOL_F32
+
+
 @pytest.mark.parametrize("shape", [(2, 2, 333, 64, 64, 128, 3, 2), (1, 3, 200, 64, 64, 64, 2, 2),
                                    (1, 2, 150, 128, 48, 96, 2, 2)])
 def test_noncausal_bf16_normalised_shapes(lib, shape):
