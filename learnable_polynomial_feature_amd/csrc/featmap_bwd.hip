@@ -73,13 +73,13 @@ struct BwdGeom {
   // Row strides of the dTheta kernel's staged blocks (elements). Transposing
   // reads (4 rows x 32 bytes per 16 lanes) are conflict free when rows sit
   // 64 bytes apart modulo 256 (measured: a 32-byte shift takes twice the LDS
-  // cycles); 8-byte row reads (frag_p16) when rows sit 8 bytes apart modulo
-  // 256.
+  // cycles); 16-byte row reads (frag_nat, 16 lanes a cycle) when rows sit 16
+  // bytes apart modulo 256.
   static constexpr int TW = PT * 32 + 32;  // staged Theta, read transposed
   static constexpr int XW = D + 32;        // staged X, read transposed
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
-  static constexpr int XP = D + 4;          // second copy of staged X (t = 4), read as rows
+  static constexpr int XP = D + 8;          // second copy of staged X (t = 4), read as rows
   // One feature block of packed Theta: PT * KS fragments of 64 lanes x 8
   // elements (1 KiB); the dX kernel double-buffers it in LDS.
   static constexpr int NFR = PT * KS;
@@ -159,15 +159,18 @@ __device__ __forceinline__ int64_t rho_near(const RowCursor& c, int64_t o, int64
 // Theta_{j,r}[16ks + 8(l/32) + e][32fb + l%32], e < 8 (k = d in natural
 // order), as one 16-byte chunk. Chunks sit at swizzled places within the
 // fragment (packed_chunk) so that both reads of the dX kernel are free of LDS
-// bank conflicts: its pass 1 reads each lane's chunk whole, its pass 2 reads
-// 8-byte halves of chunks transposed (see featmap_bwd_dx). One thread packs
-// one chunk.
-__host__ __device__ constexpr int packed_chunk(int l) {
-  // l = 32h + c: chunk 32h + (c & 16) + ((c + 8h) & 15). Any 16 consecutive
-  // lanes still take 16 different chunks mod 16 (pass 1), and the 16 (h, c)
-  // pairs of one transposed read, c in 8 consecutive features of a 16-block,
-  // land in 16 different ones (pass 2).
-  return 32 * (l >> 5) + (l & 16) + (((l & 31) + 8 * (l >> 5)) & 15);
+// bank conflicts (64 banks of 4 bytes): its pass 1 reads each lane's chunk
+// whole, its pass 2 reads 8-byte halves of chunks transposed (see
+// featmap_bwd_dx). One thread packs one chunk.
+__host__ __device__ constexpr int packed_chunk(int l, int odd) {
+  // l = 32h + c: chunk 32h + (c & 16) + ((c + 8h) & 15), with bit 2 flipped
+  // in fragments of odd ks. Any 16 consecutive lanes still take 16 different
+  // chunks mod 16 (a 16-byte read serves 16 lanes a cycle, pass 1). The 16
+  // (h, c) pairs of one transposed read, c in 4 consecutive features, take 8
+  // chunks whole, and the other 16 lanes of the same cycle read the same
+  // features of fragment ks + 1: the flip moves those to the other 8 chunks
+  // mod 16 (pass 2).
+  return (32 * (l >> 5) + (l & 16) + (((l & 31) + 8 * (l >> 5)) & 15)) ^ (odd ? 4 : 0);
 }
 
 __global__ __launch_bounds__(256) void pack_bwd_theta(const uint16_t* __restrict__ th,
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(256) void pack_bwd_theta(const uint16_t* __restrict
   for (int i = 0; i < 4; ++i)
     v[i] = static_cast<uint32_t>(src[(2 * i) * static_cast<int64_t>(m)]) |
            (static_cast<uint32_t>(src[(2 * i + 1) * static_cast<int64_t>(m)]) << 16);
-  st16(pk + (f * 64 + packed_chunk(lane)) * 8, u32x4{v[0], v[1], v[2], v[3]});
+  st16(pk + (f * 64 + packed_chunk(lane, ks & 1)) * 8, u32x4{v[0], v[1], v[2], v[3]});
 }
 
 // LDS address of a shared-memory pointer, for the direct buffer-to-LDS copy
@@ -270,15 +273,15 @@ void featmap_bwd_dx(BwdArgs a) {
                                                static_cast<uint32_t>(fb * NFR + f) * 1024u, 0, 0);
     }
   };
-  // pass 1: this lane's chunk of a fragment
-  const int a_off = packed_chunk(lane) * 8;
+  // pass 1: this lane's chunk of a fragment of even (a_off) or odd ks
+  const int a_off = packed_chunk(lane, 0) * 8, a_odd = packed_chunk(lane, 1) * 8;
   // pass 2: in the 16-lane group g4 = lane/16 of a transposing read, lane s
   // supplies d = 32dt + 16(g4 & 1) + 4(s & 3) .. +3 (fragment ks = 2dt + (g4 & 1),
   // lane half (s & 3) / 2, chunk half (s & 1)) of feature row
   // 16hf + 4(g4 / 2) + s / 4, and 8 rows further for the second read
   const int g4 = lane >> 4, s4 = lane & 15;
   auto b_off = [&](int c) {
-    return (g4 & 1) * 512 + packed_chunk(32 * ((s4 & 3) >> 1) + c) * 8 + (s4 & 1) * 4;
+    return (g4 & 1) * 512 + packed_chunk(32 * ((s4 & 3) >> 1) + c, g4 & 1) * 8 + (s4 & 1) * 4;
   };
   const int crow = 4 * (g4 >> 1) + (s4 >> 2);
   const int b_lo0 = b_off(crow), b_hi0 = b_off(crow + 8);
@@ -334,8 +337,8 @@ void featmap_bwd_dx(BwdArgs a) {
     // lane offsets made opaque per block, so the fragment addresses of the
     // two buffers are formed here (base + immediate) instead of being
     // hoisted out of the loop into registers of their own
-    int ao = a_off, bl0 = b_lo0, bh0 = b_hi0, bl1 = b_lo1, bh1 = b_hi1;
-    asm volatile("" : "+v"(ao), "+v"(bl0), "+v"(bh0), "+v"(bl1), "+v"(bh1));
+    int ao = a_off, ao1 = a_odd, bl0 = b_lo0, bh0 = b_hi0, bl1 = b_lo1, bh1 = b_hi1;
+    asm volatile("" : "+v"(ao), "+v"(ao1), "+v"(bl0), "+v"(bh0), "+v"(bl1), "+v"(bh1));
     store_ds(fb > 0 ? fb - 1 : 0);
     // the gradient next, so that waiting for it leaves the copies below in
     // flight
@@ -353,7 +356,8 @@ void featmap_bwd_dx(BwdArgs a) {
     auto read_a = [&](int idx) __attribute__((always_inline)) {
       // idx = (r*KS + ks)*P + j
       const int j = idx % P, ks = (idx / P) % KS, r = idx / (P * KS);
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(blk + ((r * P + j) * KS + ks) * 512 + ao));
+      return as_bf16x8(
+          *reinterpret_cast<const u32x4*>(blk + ((r * P + j) * KS + ks) * 512 + (ks & 1 ? ao1 : ao)));
     };
     uint32_t yb[PT][8];
     f32x16 s = zero16();
@@ -524,20 +528,24 @@ void featmap_bwd_dth(BwdArgs a) {
   // with two transposing reads instead of 16 two-byte loads of its own.
   constexpr bool GT = GB && RM == 2;
   constexpr int GL = GT ? RB / 32 : 1;  // 8-byte gradient pieces per thread and step
-  // ds tile pieces (GT, DS): wave w moves rows 8w .. 8w + 7 whole (the 8
-  // pieces of a row are elements 4i .. 4i+3, i < 4, of dX lanes row and
-  // 32 + row), so its 64 shared-memory stores fill 512 contiguous bytes
-  const int ds_row = 8 * w + ((lane >> 2) & 7);
+  // ds tile pieces (GT, DS): wave w moves rows 8w .. 8w + 7, lane l the 8
+  // bytes at 8l of them (row 8w + l/8, features 4 (l % 8) .. + 3: elements
+  // 4 ((l/2) % 4) .. + 3 of dX lane 32 (l % 2) + row), so its 64 shared-memory
+  // stores fill 512 contiguous bytes in lane order
+  const int ds_row = 8 * w + (lane >> 3);
 
   stage_theta<D, PT>(Ts, TW, a.theta + h * a.th_hstride, a.m, fb, tid);
   __syncthreads();
   // B operands of Y_{j,rk} = X Theta_{j,rk}: Theta rows 16ks.. (P16), lane
   // column c32 = feature fb*32 + c32; held for the whole chunk
+  // (t = 4: natural k order, to pair with X rows read as 16-byte pieces)
   bf16x8 tf[P][KS];
 #pragma unroll
   for (int j = 0; j < P; ++j)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) tf[j][ks] = frag_tr(Ts, TW, ks * 16, (j * T + rk) * 32, lane);
+    for (int ks = 0; ks < KS; ++ks)
+      tf[j][ks] = T == 4 ? frag_tr_nat(Ts, TW, ks * 16, (j * T + rk) * 32, lane)
+                         : frag_tr(Ts, TW, ks * 16, (j * T + rk) * 32, lane);
 
   f32x16 acc[P][DT];
 #pragma unroll
@@ -565,7 +573,7 @@ void featmap_bwd_dth(BwdArgs a) {
       if constexpr (GT && DS) {  // the step is one 2 KiB tile of ds
         static_assert(GL == 1, "ds exists for t = 4 only: one piece per thread");
         const auto rg = make_rsrc(a.ds + ds_at(t, 0), 2048u);
-        gv[0] = buf_ld8(rg, ((32 * hh + ds_row) * 16 + 4 * (lane & 3)) * 2u);
+        gv[0] = buf_ld8(rg, ((32 * (lane & 1) + ds_row) * 16 + 4 * ((lane >> 1) & 3)) * 2u);
       } else if constexpr (GT) {  // piece idx: row idx / 8, features fb*32 + 4 (idx % 8) .. + 3
         const auto rg = make_rsrc(static_cast<const uint16_t*>(gsrc) + row0 * a.m,
                                   step_rows(t) * static_cast<uint32_t>(a.m) * 2u);
@@ -633,13 +641,10 @@ void featmap_bwd_dth(BwdArgs a) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
       const u32x4 v = t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
       st16(xbuf(k) + rr * XW + q * 8, v);
-      if constexpr (T == 4) {  // rows of the second copy are 8-byte aligned
-        *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8) = u32x2{v[0], v[1]};
-        *reinterpret_cast<u32x2*>(pbuf(k) + rr * XP + q * 8 + 4) = u32x2{v[2], v[3]};
-      }
+      if constexpr (T == 4) st16(pbuf(k) + rr * XP + q * 8, v);
     }
-    if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 8 (lane % 4) + 4 hh ..
-      *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 8 * (lane & 3) + 4 * hh) =
+    if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 4 (lane % 8) ..
+      *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 4 * (lane & 7)) =
           t + ds_row < r1 ? gv[0] : u32x2{0u, 0u};
     } else if constexpr (GT) {
 #pragma unroll
@@ -698,12 +703,16 @@ void featmap_bwd_dth(BwdArgs a) {
   advance();
   load_x(cx, tx);  // step 2
   __syncthreads();
-  // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..
-  // in P16 order) and B operands of the dTheta product (k = rows wr + 16hf..,
-  // column dt*32 + c32)
+  // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..;
+  // t = 4: natural order from the second copy, one 16-byte read; t = 1: P16
+  // order, two 8-byte reads) and B operands of the dTheta product (k = rows
+  // wr + 16hf.., column dt*32 + c32)
+  auto x_rows = [&](const uint16_t* buf, int ks) __attribute__((always_inline)) {
+    return T == 4 ? frag_nat(buf, XP, wr, ks * 16, lane) : frag_p16(buf, XP, wr, ks * 16, lane);
+  };
   bf16x8 xa[KS], xb[2][DT];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(pbuf(0), XP, wr, ks * 16, lane);
+  for (int ks = 0; ks < KS; ++ks) xa[ks] = x_rows(pbuf(0), ks);
   int cur = 0, nxt = 1, fut = 2;
   for (int64_t t0 = r0; t0 < r1; t0 += RB) {
 #pragma unroll
@@ -729,7 +738,7 @@ void featmap_bwd_dth(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     // the next step's Y operands, in flight during this step's products
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) xa[ks] = frag_p16(pbuf(nxt), XP, wr, ks * 16, lane);
+    for (int ks = 0; ks < KS; ++ks) xa[ks] = x_rows(pbuf(nxt), ks);
     f32x16 ds;
     if constexpr (GT)
       ds = tile_g(gtl, gth);
