@@ -598,12 +598,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
       bf16x8 qf[QD];
 #pragma unroll
-      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
+      for (int i = 0; i < QD; ++i) qf[i] = frag_p16_sep(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const int j = idx >> 1, h = idx & 1;
         const bf16x8 qa = qf[idx % QD];
-        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
+        if (idx + QD < NQ) qf[idx % QD] = frag_p16_sep(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], h), O);
         if (a.normalize && has_z && j == zj) D = mfma32x32x16(qa, acc_frag(Z, h), D);
         __builtin_amdgcn_sched_barrier(0);
@@ -1189,12 +1189,12 @@ void attn_out32_fq(Seg32Args a, const uint16_t* __restrict__ xq,
       constexpr int NQ = 2 * FH, QD = NQ < 2 ? NQ : 2;
       bf16x8 qf[QD];
 #pragma unroll
-      for (int i = 0; i < QD; ++i) qf[i] = frag_p16(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
+      for (int i = 0; i < QD; ++i) qf[i] = frag_p16_sep(Qs, QPAD, 0, f0 * 32 + i * 16, lane);
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const int j = idx >> 1, hf = idx & 1;
         const bf16x8 qa = qf[idx % QD];
-        if (idx + QD < NQ) qf[idx % QD] = frag_p16(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
+        if (idx + QD < NQ) qf[idx % QD] = frag_p16_sep(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], hf), O);
         if (a.normalize && has_z && j == zj) D2 = mfma32x32x16(qa, acc_frag(Z, hf), D2);
         __builtin_amdgcn_sched_barrier(0);

@@ -154,6 +154,22 @@ __device__ __forceinline__ bf16x8 frag_p16(const uint16_t* base, int stride, int
   return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
+// frag_p16 as two separate ds_read_b64. Two 8-byte reads from one base
+// register are otherwise merged into one ds_read2_b64, which on gfx950 takes
+// twice the LDS cycles of the two single reads (8 against 4 per wave, and 16
+// against 8 when rows sit 16 or 48 bytes apart modulo 256). The empty asm
+// statements emit nothing; their memory clobber keeps each read a separate
+// instruction, since no access may be moved across them to pair with another.
+__device__ __forceinline__ bf16x8 frag_p16_sep(const uint16_t* base, int stride, int rbase,
+                                               int kbase, int lane) {
+  const uint16_t* p = base + (rbase + (lane & 31)) * stride + kbase + 4 * (lane >> 5);
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  asm volatile("" ::: "memory");
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  asm volatile("" ::: "memory");
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+}
+
 // Natural-order fragment (k = kbase + 8hh .. +7) of row-major M[row][k].
 __device__ __forceinline__ bf16x8 frag_nat(const uint16_t* base, int stride, int rbase, int kbase,
                                            int lane) {
