@@ -369,14 +369,15 @@ def featmap_variants(steps, torch, lib):
     return res
 
 
-def featmap_backward(steps, torch, lib):
+def featmap_backward(steps, torch, lib, t=4):
     """The feature map's backward (dX and dTheta from a bf16 dphi) at the long
     workload's geometry: 1 x 32 heads x 65536 rows, d = 128, m = 256, p = 2,
-    t = 4, squared, per-head Theta. Algorithmic work is three products of
-    2 d m p t flops per row (Y = X Theta, dY Theta^T, X^T dY); the kernels
-    recompute Y (twice in the dX kernel when squared) instead of storing it."""
+    t = 4 (or t = 1, the BASED-shaped map), squared, per-head Theta.
+    Algorithmic work is three products of 2 d m p t flops per row (Y = X Theta,
+    dY Theta^T, X^T dY); each of the two kernels recomputes Y once instead of
+    reading it back."""
     g = torch.Generator(device="cpu").manual_seed(7)
-    B, H, n, d, m, p, t = 1, 32, 65536, 128, 256, 2, 4
+    B, H, n, d, m, p = 1, 32, 65536, 128, 256, 2
     X = (torch.randn(B, H, n, d, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda")
     th = (torch.randn(H, p, t, d, m, generator=g) / d ** 0.5).to(torch.bfloat16).to("cuda")
     G = torch.randn(B, H, n, m, generator=g).to(torch.bfloat16).to("cuda")
@@ -412,7 +413,7 @@ def featmap_backward(steps, torch, lib):
            "algorithmic_tflop": round(fl / 1e12, 4), "achieved_tflops": round(tf, 1),
            "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern.items()}}
-    # per kernel: dX does Y (x2 when squared) and dY Theta^T; dTheta does Y and X^T dY
+    # per kernel: dX does Y and dY Theta^T; dTheta does Y and X^T dY
     for k, mult in (("featmap_bwd_dx", 2), ("featmap_bwd_dth", 2)):
         if k in kern:
             a = mult * unit / (kern[k] * 1e-3) / 1e12
@@ -1070,6 +1071,7 @@ def main():
         line["variants"] = featmap_variants(10, torch, lib)
         log("feature-map backward")
         line["featmap_backward"] = featmap_backward(10, torch, lib)
+        line["featmap_backward_t1"] = featmap_backward(10, torch, lib, t=1)
         log("causal attention backward")
         line["causal_backward"] = causal_backward(3, torch, lib)
         log("gated causal attention backward")

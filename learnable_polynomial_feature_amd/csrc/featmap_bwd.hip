@@ -76,7 +76,7 @@ struct BwdGeom {
   // cycles); 16-byte row reads (frag_nat, 16 lanes a cycle) when rows sit 16
   // bytes apart modulo 256.
   static constexpr int TW = PT * 32 + 32;  // staged Theta, read transposed
-  static constexpr int XW = D + 32;        // staged X, read transposed
+  static constexpr int XW = T == 1 ? D : D + 32;  // staged X (t = 1: unpadded, swizzled)
   static constexpr int RB = T == 4 ? 32 : 128;  // rows per step of the dTheta kernel
   static constexpr size_t theta_lds() { return 1ull * D * TW * 2; }
   static constexpr int XP = D + 8;          // second copy of staged X (t = 4), read as rows
@@ -111,6 +111,38 @@ __device__ __forceinline__ void stage_theta(uint16_t* Ts, int TW, const uint16_t
     const int idx = tid + NT * i, k = idx / (4 * PT), pc = idx % (4 * PT);
     st16(Ts + k * TW + pc * 8, tv[i]);
   }
+}
+
+// With t = 1 the dTheta kernel keeps one copy of each step's 128 rows of X
+// (no room for a second) and reads it both ways: 16-byte row pieces (16 rows
+// a cycle) and transposing reads (4 rows x 64 bytes a cycle, 4 rows aligned
+// to 4). Rows are unpadded, and 16-byte chunk c of row r sits at chunk
+// c ^ xswz(r): any 16 consecutive rows put one chunk in 16 different groups
+// of 4 banks, and the 4 rows of a transposing read put their 4 chunks of a
+// 32-column block in 4 different ones.
+template <int D>
+__device__ __forceinline__ int xswz(int r) {
+  static_assert(D == 64 || D == 128, "rows of 8 or 16 chunks");
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int xswz_at(int r, int col) {  // element offset of (r, col)
+  return r * D + (((col >> 3) ^ xswz<D>(r)) << 3) + (col & 7);
+}
+// frag_nat and frag_tr_nat's counterparts on a swizzled block
+template <int D>
+__device__ __forceinline__ bf16x8 frag_nat_swz(const uint16_t* base, int rbase, int kbase,
+                                               int lane) {
+  return as_bf16x8(ld16(base + xswz_at<D>(rbase + (lane & 31), kbase + 8 * (lane >> 5))));
+}
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tr_swz(const uint16_t* base, int kbase, int cbase, int lane) {
+  const int s = lane & 15, G = lane >> 4;
+  const int row = kbase + 4 * (G >> 1) + (s >> 2);
+  const int col = cbase + (G & 1) * 16 + 4 * (s & 3);
+  const uint2 lo = lds_tr64(base + xswz_at<D>(row, col));
+  const uint2 hi = lds_tr64(base + xswz_at<D>(row + 8, col));
+  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
 // Row t of a head's B*n rows is token i of sequence b, stored at sequence row
@@ -536,16 +568,14 @@ void featmap_bwd_dth(BwdArgs a) {
 
   stage_theta<D, PT>(Ts, TW, a.theta + h * a.th_hstride, a.m, fb, tid);
   __syncthreads();
-  // B operands of Y_{j,rk} = X Theta_{j,rk}: Theta rows 16ks.. (P16), lane
-  // column c32 = feature fb*32 + c32; held for the whole chunk
-  // (t = 4: natural k order, to pair with X rows read as 16-byte pieces)
+  // B operands of Y_{j,rk} = X Theta_{j,rk}: Theta rows 16ks.. in natural k
+  // order (to pair with X rows read as 16-byte pieces), lane column c32 =
+  // feature fb*32 + c32; held for the whole chunk
   bf16x8 tf[P][KS];
 #pragma unroll
   for (int j = 0; j < P; ++j)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      tf[j][ks] = T == 4 ? frag_tr_nat(Ts, TW, ks * 16, (j * T + rk) * 32, lane)
-                         : frag_tr(Ts, TW, ks * 16, (j * T + rk) * 32, lane);
+    for (int ks = 0; ks < KS; ++ks) tf[j][ks] = frag_tr_nat(Ts, TW, ks * 16, (j * T + rk) * 32, lane);
 
   f32x16 acc[P][DT];
 #pragma unroll
@@ -624,7 +654,7 @@ void featmap_bwd_dth(BwdArgs a) {
   // LDS per row buffer: the rows with stride XW (read transposed, B operands
   // of the dTheta product) and, for t = 4, again with stride XP (read as A
   // operands of Y); each stride keeps its own read pattern free of bank
-  // conflicts. With t = 1 one copy serves both.
+  // conflicts. With t = 1 one swizzled copy (xswz) serves both.
   constexpr int XP = T == 4 ? G::XP : XW;
   constexpr int XBW = T == 4 ? RB * (XW + XP) : RB * XW;  // X rows of one buffer
   constexpr int BUFW = XBW + RB * 32;                      // then the gradient tile (GT)
@@ -640,8 +670,12 @@ void featmap_bwd_dth(BwdArgs a) {
     for (int it = 0; it < XL; ++it) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
       const u32x4 v = t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
-      st16(xbuf(k) + rr * XW + q * 8, v);
-      if constexpr (T == 4) st16(pbuf(k) + rr * XP + q * 8, v);
+      if constexpr (T == 1) {
+        st16(xbuf(k) + xswz_at<D>(rr, q * 8), v);
+      } else {
+        st16(xbuf(k) + rr * XW + q * 8, v);
+        st16(pbuf(k) + rr * XP + q * 8, v);
+      }
     }
     if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 4 (lane % 8) ..
       *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 4 * (lane & 7)) =
@@ -703,12 +737,14 @@ void featmap_bwd_dth(BwdArgs a) {
   advance();
   load_x(cx, tx);  // step 2
   __syncthreads();
-  // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..;
-  // t = 4: natural order from the second copy, one 16-byte read; t = 1: P16
-  // order, two 8-byte reads) and B operands of the dTheta product (k = rows
-  // wr + 16hf.., column dt*32 + c32)
+  // this wave's X fragments: A operands of Y (row wr + lane%32, k = 16ks..
+  // in natural order, one 16-byte read: t = 4 from the second copy) and B
+  // operands of the dTheta product (k = rows wr + 16hf.., column dt*32 + c32)
   auto x_rows = [&](const uint16_t* buf, int ks) __attribute__((always_inline)) {
-    return T == 4 ? frag_nat(buf, XP, wr, ks * 16, lane) : frag_p16(buf, XP, wr, ks * 16, lane);
+    if constexpr (T == 1)
+      return frag_nat_swz<D>(buf, wr, ks * 16, lane);
+    else
+      return frag_nat(buf, XP, wr, ks * 16, lane);
   };
   bf16x8 xa[KS], xb[2][DT];
 #pragma unroll
@@ -719,7 +755,8 @@ void featmap_bwd_dth(BwdArgs a) {
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        xb[hf][dt] = frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
+        xb[hf][dt] = T == 1 ? frag_tr_swz<D>(xbuf(cur), wr + hf * 16, dt * 32, lane)
+                            : frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
     u32x4 gtl, gth;
     if constexpr (GT) {
       gtl = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr, 0, lane));
