@@ -586,27 +586,32 @@ void featmap_bwd_dth(BwdArgs a) {
   // A step's X (row-major), requested two steps ahead, and its gradient
   // (element 4i+e: row wr + 8i + 4hh + e of the step, feature fb*32 + c32),
   // requested one step ahead and kept as raw bits until the step widens it.
-  // Rows past the chunk read as zeros (RM 2) or as its last row.
+  // Requests never pass the chunk's last step (RM 2: whole steps); with
+  // other RM a partial step's rows past the chunk read as its last row.
   u32x4 xv[XL];
   u32x2 gv[GL];  // GT: this thread's pieces of a step's gradient tile
   uint32_t gn[GT ? 1 : 16];
   constexpr uint32_t ES = GB ? 2 : 4;
-  auto step_rows = [&](int64_t t) __attribute__((always_inline)) {
-    return static_cast<uint32_t>(r1 - t < RB ? r1 - t : RB);
-  };
+  // RM 2: the first row (in [B][H][n] order) of the step whose X was
+  // requested last, and the offset of its ds tile, kept incrementally by
+  // advance() below: a step never straddles two sequences, so stepping is an
+  // add (and a hop to the next sequence), not a division and 64-bit products
+  int64_t xrow = 0, dsoff = 0;
   auto load_x = [&](const RowCursor& c, int64_t t) __attribute__((always_inline)) {
     if constexpr (RM == 2) {  // the step's rows are consecutive in memory
-      const int64_t row0 = (c.b * a.H + h) * a.n + c.i;
-      const auto rx = make_rsrc(a.X + row0 * D, step_rows(t) * D * 2u);
+      (void)c;
+      (void)t;
+      const int64_t row0 = xrow;  // whole steps: RB rows each
+      const auto rx = make_rsrc(a.X + row0 * D, static_cast<uint32_t>(RB) * D * 2u);
 #pragma unroll
       for (int it = 0; it < XL; ++it) xv[it] = buf_ld16(rx, (tid + 256u * it) * 16u, 0u);
       if constexpr (GT && DS) {  // the step is one 2 KiB tile of ds
         static_assert(GL == 1, "ds exists for t = 4 only: one piece per thread");
-        const auto rg = make_rsrc(a.ds + ds_at(t, 0), 2048u);
+        const auto rg = make_rsrc(a.ds + dsoff, 2048u);
         gv[0] = buf_ld8(rg, ((32 * (lane & 1) + ds_row) * 16 + 4 * ((lane >> 1) & 3)) * 2u);
       } else if constexpr (GT) {  // piece idx: row idx / 8, features fb*32 + 4 (idx % 8) .. + 3
         const auto rg = make_rsrc(static_cast<const uint16_t*>(gsrc) + row0 * a.m,
-                                  step_rows(t) * static_cast<uint32_t>(a.m) * 2u);
+                                  static_cast<uint32_t>(RB) * static_cast<uint32_t>(a.m) * 2u);
 #pragma unroll
         for (int it = 0; it < GL; ++it) {
           const uint32_t idx = tid + 256u * it;
@@ -627,8 +632,10 @@ void featmap_bwd_dth(BwdArgs a) {
       (void)c;
       (void)t;
     } else if constexpr (RM == 2) {
-      const auto rg = make_rsrc(static_cast<const char*>(gsrc) + ((c.b * a.H + h) * a.n + c.i) * a.m * ES,
-                                step_rows(t) * static_cast<uint32_t>(a.m) * ES);
+      (void)c;
+      (void)t;
+      const auto rg = make_rsrc(static_cast<const char*>(gsrc) + xrow * a.m * ES,
+                                static_cast<uint32_t>(RB) * static_cast<uint32_t>(a.m) * ES);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -669,7 +676,9 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
     for (int it = 0; it < XL; ++it) {
       const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
-      const u32x4 v = t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
+      // rows past the chunk read as zeros; with whole steps (RM 2) a step
+      // past the chunk is never read, so its rows need no masking
+      const u32x4 v = RM == 2 || t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
       if constexpr (T == 1) {
         st16(xbuf(k) + xswz_at<D>(rr, q * 8), v);
       } else {
@@ -678,14 +687,12 @@ void featmap_bwd_dth(BwdArgs a) {
       }
     }
     if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 4 (lane % 8) ..
-      *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 4 * (lane & 7)) =
-          t + ds_row < r1 ? gv[0] : u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 4 * (lane & 7)) = gv[0];  // RM 2
     } else if constexpr (GT) {
 #pragma unroll
       for (int it = 0; it < GL; ++it) {
         const int idx = tid + 256 * it, rr = idx >> 3;
-        *reinterpret_cast<u32x2*>(gbuf(k) + rr * 32 + (idx & 7) * 4) =
-            t + rr < r1 ? gv[it] : u32x2{0u, 0u};
+        *reinterpret_cast<u32x2*>(gbuf(k) + rr * 32 + (idx & 7) * 4) = gv[it];  // RM 2
       }
     }
   };
@@ -714,10 +721,23 @@ void featmap_bwd_dth(BwdArgs a) {
   // chunk's last step once there)
   RowCursor cx = cursor_at(r0, a);
   int64_t tx = r0;
+  const int64_t hop = RB + (a.H - 1) * a.n;  // RM 2: last step of a sequence -> next one's first
+  if constexpr (RM == 2) {
+    xrow = (cx.b * a.H + h) * a.n + cx.i;
+    if constexpr (GT && DS) dsoff = ds_at(r0, 0);
+  }
   auto advance = [&]() __attribute__((always_inline)) {
     if (tx + RB < r1) {
-      cx = cursor_advance(cx, RB, a);
       tx += RB;
+      if constexpr (RM == 2) {  // n is a multiple of RB: i lands on n exactly
+        cx.i += RB;
+        const bool wrap = cx.i >= a.n;
+        cx.i = wrap ? 0 : cx.i;
+        xrow += wrap ? hop : RB;
+        if constexpr (GT && DS) dsoff += FB * 1024;  // one 32-row ds tile per step
+      } else {
+        cx = cursor_advance(cx, RB, a);
+      }
     }
   };
 
