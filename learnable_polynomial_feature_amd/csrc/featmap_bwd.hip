@@ -672,20 +672,21 @@ void featmap_bwd_dth(BwdArgs a) {
   // gradient tile: RB rows of 32 features, rows 64 bytes apart (conflict free
   // for the transposing reads)
   auto gbuf = [&](int k) __attribute__((always_inline)) { return smem + k * BUFW + XBW; };
-  auto store_x = [&](int k, int64_t t) __attribute__((always_inline)) {
-#pragma unroll
-    for (int it = 0; it < XL; ++it) {
-      const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
-      // rows past the chunk read as zeros; with whole steps (RM 2) a step
-      // past the chunk is never read, so its rows need no masking
-      const u32x4 v = RM == 2 || t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
-      if constexpr (T == 1) {
-        st16(xbuf(k) + xswz_at<D>(rr, q * 8), v);
-      } else {
-        st16(xbuf(k) + rr * XW + q * 8, v);
-        st16(pbuf(k) + rr * XP + q * 8, v);
-      }
+  // piece `it` of the step's rows into buffer k
+  auto store_piece = [&](int k, int64_t t, int it) __attribute__((always_inline)) {
+    const int idx = tid + 256 * it, rr = idx / (D / 8), q = idx % (D / 8);
+    // rows past the chunk read as zeros; with whole steps (RM 2) a step past
+    // the chunk is never read, so its rows need no masking
+    const u32x4 v = RM == 2 || t + rr < r1 ? xv[it] : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (T == 1) {
+      st16(xbuf(k) + xswz_at<D>(rr, q * 8), v);
+    } else {
+      st16(xbuf(k) + rr * XW + q * 8, v);
+      st16(pbuf(k) + rr * XP + q * 8, v);
     }
+  };
+  // the step's gradient tile (GT) into buffer k
+  auto store_gtile = [&](int k) __attribute__((always_inline)) {
     if constexpr (GT && DS) {  // this thread's piece: row ds_row, features 4 (lane % 8) ..
       *reinterpret_cast<u32x2*>(gbuf(k) + ds_row * 32 + 4 * (lane & 7)) = gv[0];  // RM 2
     } else if constexpr (GT) {
@@ -695,6 +696,11 @@ void featmap_bwd_dth(BwdArgs a) {
         *reinterpret_cast<u32x2*>(gbuf(k) + rr * 32 + (idx & 7) * 4) = gv[it];  // RM 2
       }
     }
+  };
+  auto store_x = [&](int k, int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < XL; ++it) store_piece(k, t, it);
+    store_gtile(k);
   };
   auto widen = [&]() __attribute__((always_inline)) {
     f32x16 v = zero16();
@@ -727,17 +733,18 @@ void featmap_bwd_dth(BwdArgs a) {
     if constexpr (GT && DS) dsoff = ds_at(r0, 0);
   }
   auto advance = [&]() __attribute__((always_inline)) {
-    if (tx + RB < r1) {
+    if constexpr (RM == 2) {  // branch-free (selects), so the step stays one basic block
+      const bool more = tx + RB < r1;
+      tx += more ? RB : 0;
+      const int64_t i = cx.i + (more ? RB : 0);  // n is a multiple of RB: i lands on n exactly
+      const bool wrap = i >= a.n;
+      cx.i = wrap ? 0 : i;
+      cx.b += wrap ? 1 : 0;
+      xrow += more ? (wrap ? hop : RB) : 0;
+      if constexpr (GT && DS) dsoff += more ? FB * 1024 : 0;  // one 32-row ds tile per step
+    } else if (tx + RB < r1) {
       tx += RB;
-      if constexpr (RM == 2) {  // n is a multiple of RB: i lands on n exactly
-        cx.i += RB;
-        const bool wrap = cx.i >= a.n;
-        cx.i = wrap ? 0 : cx.i;
-        xrow += wrap ? hop : RB;
-        if constexpr (GT && DS) dsoff += FB * 1024;  // one 32-row ds tile per step
-      } else {
-        cx = cursor_advance(cx, RB, a);
-      }
+      cx = cursor_advance(cx, RB, a);
     }
   };
 
@@ -770,29 +777,54 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) xa[ks] = x_rows(pbuf(0), ks);
   int cur = 0, nxt = 1, fut = 2;
+  // One step. With one wave per SIMD nothing else hides a wave's non-MFMA
+  // work. With t = 1 (IL) the work that does not depend on this step's
+  // products runs between them: the rows two steps ahead go into the free
+  // buffer (last read before the previous barrier) one piece per Y k-step,
+  // the next requests are issued between the rank's dTheta products, and the
+  // dTheta product's X operands are read in two halves, so that at most 15
+  // LDS reads are in flight (the range of the wait counter). With t = 4 the
+  // stores and requests stay at the end of the step: its 32-row steps are
+  // short, and rows requested half a step before they are stored arrive
+  // late (measured: 2.29 against 2.10 ms; t = 1, 0.78 against 0.83 ms).
+  constexpr bool IL = T == 1;
+  auto read_xb = [&](int hf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      xb[hf][dt] = T == 1 ? frag_tr_swz<D>(xbuf(cur), wr + hf * 16, dt * 32, lane)
+                          : frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
+  };
   for (int64_t t0 = r0; t0 < r1; t0 += RB) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        xb[hf][dt] = T == 1 ? frag_tr_swz<D>(xbuf(cur), wr + hf * 16, dt * 32, lane)
-                            : frag_tr(xbuf(cur), XW, wr + hf * 16, dt * 32, lane);
-    u32x4 gtl, gth;
-    if constexpr (GT) {
-      gtl = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr, 0, lane));
-      gth = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr + 16, 0, lane));
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of their MFMAs
     // Y_{j,rk} in the natural orientation: element 4i+e is row wr + 8i + 4hh + e
-    // of the step, lane column c32 is feature fb*32 + c32
+    // of the step, lane column c32 is feature fb*32 + c32. The first products
+    // go ahead of the step's first reads: their accumulators are then live,
+    // so no read's address is formed in them (a product writing a register a
+    // read in flight still takes its address from waits for that read).
     f32x16 y[P];
 #pragma unroll
     for (int j = 0; j < P; ++j) y[j] = zero16();
+    u32x4 gtl, gth;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int j = 0; j < P; ++j) y[j] = mfma32x32x16(xa[ks], tf[j][ks], y[j]);
-    __builtin_amdgcn_sched_barrier(0);
+      auto read_rest = [&]() __attribute__((always_inline)) {
+        read_xb(1);
+        if constexpr (GT) {
+          gtl = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr, 0, lane));
+          gth = __builtin_bit_cast(u32x4, frag_tr(gbuf(cur), 32, wr + 16, 0, lane));
+        }
+      };
+      if (ks == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_xb(0);
+        if constexpr (IL) store_gtile(fut);
+        else read_rest();
+      }
+      if (IL && ks < XL) store_piece(fut, t0 + 2 * RB, ks);
+      if (IL && ks == KS / 2) read_rest();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // the next step's Y operands, in flight during this step's products
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) xa[ks] = x_rows(pbuf(nxt), ks);
@@ -828,15 +860,28 @@ void featmap_bwd_dth(BwdArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[j][dt] = mfma32x32x16(af, xb[hf][dt], acc[j][dt]);
       }
+      if (IL && j == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        // the next step's gradient is widened and the one after it
+        // requested; rows three steps ahead requested
+        g = widen();
+        load_g(cx, tx);
+        advance();
+        load_x(cx, tx);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // rows two steps ahead into the free buffer; the next step's gradient is
-    // widened and the one after it requested; rows three steps ahead requested
-    store_x(fut, t0 + 2 * RB);
-    g = widen();
-    load_g(cx, tx);
-    advance();
-    load_x(cx, tx);
+    if constexpr (!IL) {
+      // rows two steps ahead into the free buffer; the next step's gradient
+      // is widened and the one after it requested; rows three steps ahead
+      // requested
+      store_x(fut, t0 + 2 * RB);
+      g = widen();
+      load_g(cx, tx);
+      advance();
+      load_x(cx, tx);
+    }
     const int k = cur;
     cur = nxt;
     nxt = fut;
