@@ -426,6 +426,45 @@ hipError_t attn_on_features(const llops_shape_t* s, bool causal, int M, int DV,
               : llops::launch_attn_out_bf16(a, fq, fk, v, state, st_seg, st_bh, out, st);
 }
 
+// The backward's chain-rule passes on narrow operands (m = 256, dv = 128
+// kernels): phi_Q rows are stored as qald bf16 and read as [row | one? | 0]
+// (likewise phi_K), without padded copies; values are the phi slice v (rows
+// vld apart), rows go to outb (bf16, ldo apart). LLOPS_BWD_PADDED=1 in the
+// environment selects the padded copies instead.
+bool bwd_padded() {
+  const char* env = getenv("LLOPS_BWD_PADDED");
+  return env && env[0] == '1';
+}
+
+hipError_t attn_on_aug(const llops_shape_t* s, bool causal, bool anti, int M, int DV,
+                       const uint16_t* fq, int qald, int qone, const uint16_t* fk, int kald,
+                       int kone, const uint16_t* v, int vld, uint16_t* outb, int ldo, float* seg,
+                       float* tot, hipStream_t st) {
+  const llops_shape_t t = feat_attn_shape(s, M, DV);
+  llops::AttnShape a = attn_shape(&t, causal);
+  const int64_t per = static_cast<int64_t>(M) * DV + M;
+  if (anti) {  // suffix sums: the scan from the last segment, chunks from the last
+    if (!causal) return hipErrorInvalidValue;
+    a.anti = 1;
+  }
+  hipError_t e = llops::launch_seg_state32_aug(a, fk, kald, kone, v, vld, seg, st);
+  if (e != hipSuccess) return e;
+  const float* state = seg;
+  int64_t st_seg = per, st_bh = per * a.nseg;
+  if (causal) {
+    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, nullptr, nullptr, 1, st);
+  } else {
+    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, tot, tot + static_cast<int64_t>(M) * DV,
+                               0, st);
+    state = tot;
+    st_seg = 0;
+    st_bh = per;
+  }
+  if (e != hipSuccess) return e;
+  return llops::launch_attn_out32_aug(a, fq, qald, qone, fk, kald, kone, v, vld, state, st_seg,
+                                      st_bh, outb, ldo, st);
+}
+
 // num = M V and den = M 1 in one pass on the 32x32x16 shapes: the output pass
 // forms each row's denominator phi_Q,i . z_i for the normalised form anyway,
 // so it stores it beside the unnormalised row. (S0init, z0init): the initial
@@ -970,10 +1009,24 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   const bool rev = causal && !anti;
   uint16_t *a = u16(L.a), *b = u16(L.b), *dn = u16(L.rdnum);
   uint16_t *ra = rev ? u16(L.ra) : nullptr, *rb = rev ? u16(L.rb) : nullptr;
-  LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
-                                  s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
-                                  rev ? 1 : 0, den_ld, st),
-            "make_ab");
+  const bool inplace = on32(s, causal, MA, W);
+  const bool sliced = inplace && n * m * 2 < (int64_t{1} << 31);
+  const bool init = causal && (S0 || z0);
+  // the chain-rule passes read [dnum | dden | 0] from a narrow copy (held
+  // where a would be) and [V | 1 | 0] from V itself instead of the padded
+  // copies, where their kernels apply
+  const llops_shape_t ta = feat_attn_shape(s, MA, W);
+  const bool aug = !rev && sliced && !init && !dS0 && !dz0 && !bwd_padded() && dv % 8 == 0 &&
+                   dv + 8 <= MA && llops::aug32_supported(attn_shape(&ta, causal));
+  if (aug)
+    LLOPS_HIP(llops::launch_make_ab_aug(num, den1, dO, dv, R, s->normalize,
+                                        s->normalize ? s->delta : 0.f, a, dn, den_ld, st),
+              "make_ab");
+  else
+    LLOPS_HIP(llops::launch_make_ab(num, den1, dO, static_cast<const uint16_t*>(V), dv, MA, n, R,
+                                    s->normalize, s->normalize ? s->delta : 0.f, a, ra, b, rb, dn,
+                                    rev ? 1 : 0, den_ld, st),
+              "make_ab");
   uint16_t* vp = u16(L.vp);
   float* tmp = f32(L.tmp);
   uint16_t *dphq = u16(L.dphq), *dphk = u16(L.dphk);  // bf16, as the forward stores phi
@@ -1001,10 +1054,18 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // sequence); otherwise through tmp and a row copy. They also read their phi
   // slice in place (rows m apart; on the reversed path the reversed sequence's
   // from the reversed copy of phi_Q) instead of from a sliced copy.
-  const bool inplace = on32(s, causal, MA, W);
-  const bool sliced = inplace && n * m * 2 < (int64_t{1} << 31);
-  const bool init = causal && (S0 || z0);
-  for (int p0 = 0; p0 < m; p0 += W) {
+  const uint16_t* vv = static_cast<const uint16_t*>(V);
+  for (int p0 = 0; aug && p0 < m; p0 += W) {
+    // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j, a = [dnum | dden], b = [V | 1]
+    LLOPS_HIP(attn_on_aug(s, causal, false, MA, W, a, dv + 8, 0, vv, dv, 1, phk + p0, m, dphq + p0,
+                          m, seg, tot, st),
+              "attn dphi_q");
+    // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: suffix sums (anti-causal)
+    LLOPS_HIP(attn_on_aug(s, causal, anti, MA, W, vv, dv, 1, a, dv + 8, 0, phq + p0, m, dphk + p0,
+                          m, seg, tot, st),
+              "attn dphi_k");
+  }
+  for (int p0 = 0; !aug && p0 < m; p0 += W) {
     if (!sliced)
       LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     if (init)
@@ -1019,11 +1080,11 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: anti-causal, or causal over
   // the reversed sequence
   const int rv = rev ? 1 : 0;
-  for (int p0 = 0; anti && p0 < m; p0 += W)
+  for (int p0 = 0; !aug && anti && p0 < m; p0 += W)
     LLOPS_HIP(attn_on_features(s, true, MA, W, b, a, phq + p0, tmp, seg, tot, st, nullptr,
                                dphk + p0, m, 0, m, true),
               "attn dphi_k");
-  for (int p0 = 0; !anti && p0 < m; p0 += W) {
+  for (int p0 = 0; !aug && !anti && p0 < m; p0 += W) {
     if (!sliced)
       LLOPS_HIP(llops::launch_rows_copy_bf16(phq, m, p0, vp, W, 0, W, n, R, rv, st), "rows");
     const uint16_t* qv = sliced ? (causal ? rphq : phq) + p0 : vp;

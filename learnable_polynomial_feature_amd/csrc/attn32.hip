@@ -57,7 +57,39 @@ struct Seg32Args {
   float delta;
   const float* gl;   // gated: chunk-local inclusive sums of log gates [BH][n]
   float* gseg;       // gated pass 1: per-segment sum of log gates [BH][nseg]
+  // AUG passes (the backward's chain-rule operands): phi_Q (phi_K) rows are
+  // qald (kald) bf16 per row, then zeros, with a bf16 one at column qald
+  // (kald) when qone (kone) is set; see AugRows
+  int qald, kald;
+  int qone, kone;
 };
+
+// A narrow feature row read as M bf16: the ald values of a stored row (row
+// stride ald, a multiple of 8), then zeros, with a bf16 one at column ald if
+// `one`. This is the backward's [dnum | dden | 0] (stored [dnum | dden],
+// padded to a multiple of 8) and [v | 1 | 0] (v itself) without their
+// padded copies. Piece q (16 bytes) of a row is stored piece q (q < ald/8),
+// else zeros: the others are requested past the view, where the hardware
+// range check reads zeros, so the one load a piece takes is unconditional.
+struct AugRows {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t row;   // stored row bytes
+  int ald8;       // stored pieces per row
+  uint32_t one;   // bf16 one (0x3F80) or 0, ORed into element 0 of piece ald8
+};
+__device__ __forceinline__ AugRows aug_rows(const uint16_t* rows0, int ald, int one, int64_t row0,
+                                            uint32_t rows) {
+  return AugRows{make_rsrc(rows0 + row0 * ald, rows * static_cast<uint32_t>(ald) * 2u),
+                 static_cast<uint32_t>(ald) * 2u, ald / 8, one ? 0x3F80u : 0u};
+}
+// piece q of row `row` of chunk c (kC rows a chunk)
+__device__ __forceinline__ u32x4 aug_ld(const AugRows& v, int row, int q, int c) {
+  constexpr uint32_t kPast = 0x80000000u;  // past any view (views stay below 2^31 bytes)
+  const uint32_t off = q < v.ald8 ? static_cast<uint32_t>(row) * v.row + q * 16u : kPast;
+  u32x4 r = buf_ld16_nt(v.rs, off, static_cast<uint32_t>(c) * (kC * v.row));
+  r[0] |= q == v.ald8 ? v.one : 0u;
+  return r;
+}
 
 constexpr int kGL = 2 * kC;  // LDS slots (uint16) of one chunk's 32 fp32 gate sums
 
@@ -222,7 +254,8 @@ struct Seg32Geom {
 // the accumulator (every exponent still <= 0 for g <= 0).
 // VSTR: the value rows are vld elements apart (a column slice of a wider
 // row; v points at the slice's first column).
-template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false>
+// AUG: phi_K rows are narrow (AugRows: a.kald, a.kone).
+template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false, bool AUG = false>
 __global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
                                                      const uint16_t* __restrict__ v,
@@ -249,7 +282,10 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
   // return zeros (hardware range check), so every load is unconditional, the
   // number in flight is static and a wait for one chunk never drains the next.
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
-  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(AUG ? phik : Kg + t0 * M, AUG ? 0u : seg_rows * M * 2u);
+  AugRows ka{};
+  if constexpr (AUG) ka = aug_rows(phik, a.kald, a.kone, bh * a.n + t0, seg_rows);
+  static_assert(!AUG || G::NT % (M / 8) == 0, "a thread's pieces share one column");
   // strided: the view ends at the slice's last element
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(
       Vg + t0 * VL, VSTR ? (seg_rows ? ((seg_rows - 1u) * VL + DV) * 2u : 0u) : seg_rows * DV * 2u);
@@ -264,8 +300,12 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
     // are streamed once, so the loads are non-temporal (0.316 -> 0.291 ms at
     // 1 x 32 x 65536)
 #pragma unroll
-    for (int i = 0; i < LK; ++i)
-      rk[i] = buf_ld16_nt(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+    for (int i = 0; i < LK; ++i) {
+      if constexpr (AUG)
+        rk[i] = aug_ld(ka, (tid + i * NT) / (M / 8), tid % (M / 8), c);
+      else
+        rk[i] = buf_ld16_nt(rsk, (tid + i * NT) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
+    }
 #pragma unroll
     for (int i = 0; i < LV; ++i)
       rv[i] = buf_ld16_nt(rsv,
@@ -444,8 +484,10 @@ struct Out32Geom {
 // the pass goes to row n - 1 - t (a pass over the reversed sequence writes
 // in the original order); bit 1 set, bf16 (RNE) into outb, rows ldo elements
 // apart (a column slice of a wider row).
+// AUG: phi_Q and phi_K rows are narrow (AugRows: a.qald, a.qone, a.kald,
+// a.kone).
 template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
-          bool VSTR = false, bool ANTI = false>
+          bool VSTR = false, bool ANTI = false, bool AUG = false>
 __global__ __launch_bounds__(DV * 4) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* __restrict__ phik,
                 const uint16_t* __restrict__ v, const float* __restrict__ state, int64_t st_seg,
@@ -511,8 +553,14 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   // return zeros (hardware range check), so every load is unconditional and
   // the waits for one chunk never drain the loads of the next.
   const uint32_t seg_rows = static_cast<uint32_t>(t1 - t0);
-  const __amdgpu_buffer_rsrc_t rsq = make_rsrc(Qg + t0 * M, seg_rows * M * 2u);
-  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(Kg + t0 * M, seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsq = make_rsrc(AUG ? phiq : Qg + t0 * M, AUG ? 0u : seg_rows * M * 2u);
+  const __amdgpu_buffer_rsrc_t rsk = make_rsrc(AUG ? phik : Kg + t0 * M, AUG ? 0u : seg_rows * M * 2u);
+  AugRows qa{}, ka{};
+  if constexpr (AUG) {
+    qa = aug_rows(phiq, a.qald, a.qone, bh * a.n + t0, seg_rows);
+    ka = aug_rows(phik, a.kald, a.kone, bh * a.n + t0, seg_rows);
+  }
+  static_assert(!AUG || NT % (M / 8) == 0, "a thread's pieces share one column");
   const __amdgpu_buffer_rsrc_t rsv = make_rsrc(
       Vg + t0 * VL, VSTR ? (seg_rows ? ((seg_rows - 1u) * VL + DV) * 2u : 0u) : seg_rows * DV * 2u);
   // piece p of a chunk: phi_Q rows, then phi_K rows, then V rows, 16
@@ -530,7 +578,11 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int p = t + i * NT;
-      if (i * NT < QP)
+      if (AUG && i * NT < QP)
+        r[i] = aug_ld(qa, p / (M / 8), p % (M / 8), c);
+      else if (AUG && i * NT < 2 * QP)
+        r[i] = aug_ld(ka, (p - QP) / (M / 8), (p - QP) % (M / 8), c);
+      else if (i * NT < QP)
         r[i] = buf_ld16_nt(rsq, p * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
       else if (i * NT < 2 * QP)
         r[i] = buf_ld16_nt(rsk, (p - QP) * 16u, static_cast<uint32_t>(c) * (kC * M * 2u));
@@ -1327,13 +1379,14 @@ __global__ __launch_bounds__(256) void gate_cumsum32(int64_t n, int64_t nch, int
   if (live) L[bh * nch * kC + tok] = x;
 }
 
-template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false>
+template <int M, int DV, bool GATED, bool ANCHOR = false, bool VSTR = false, bool AUG = false>
 hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t* v, const float* gl,
-                          float* gseg, float* seg, hipStream_t st, int vld = 0) {
+                          float* gseg, float* seg, hipStream_t st, int vld = 0, int kald = 0,
+                          int kone = 0) {
   using G = Seg32Geom<M, DV>;
-  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, gseg};
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, gseg, 0, kald, 0, kone};
   const size_t lds = 2ull * (kC * G::MP + kC * G::VP + (GATED ? kGL : 0)) * sizeof(uint16_t);
-  auto* kern = seg_state32<M, DV, GATED, ANCHOR, VSTR>;
+  auto* kern = seg_state32<M, DV, GATED, ANCHOR, VSTR, AUG>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
@@ -1343,16 +1396,17 @@ hipError_t launch_state_t(const AttnShape& s, const uint16_t* k, const uint16_t*
 }
 
 template <int M, int DV, bool CAUSAL, bool GATED, bool DENOUT = false, int OM = 0,
-          bool VSTR = false, bool ANTI = false>
+          bool VSTR = false, bool ANTI = false, bool AUG = false>
 hipError_t launch_out_t(const AttnShape& s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const float* gl, const float* state, int64_t ss,
                         int64_t sb, float* out, hipStream_t st, float* den = nullptr,
-                        uint16_t* outb = nullptr, int ldo = 0, int vld = 0) {
+                        uint16_t* outb = nullptr, int ldo = 0, int vld = 0, int qald = 0,
+                        int qone = 0, int kald = 0, int kone = 0) {
   using G = Out32Geom<M, DV, GATED>;
-  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr};
+  Seg32Args a{s.n, s.seg_len, s.nseg, s.normalize, s.delta, gl, nullptr, qald, kald, qone, kone};
   const size_t lds = G::lds_bytes();
   if ((s.anti != 0) != ANTI) return hipErrorInvalidValue;
-  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM, VSTR, ANTI>;
+  auto* kern = attn_out32<M, DV, CAUSAL, GATED, DENOUT, OM, VSTR, ANTI, AUG>;
   const hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(s.nseg), static_cast<unsigned>(s.BH));
@@ -1529,6 +1583,46 @@ hipError_t launch_seg_state32_v(const AttnShape& s, const uint16_t* phik, const 
     case 64064: return launch_state_t<64, 64, false, false, true>(s, phik, v, nullptr, nullptr, seg, st, vld);
     default: return hipErrorInvalidValue;
   }
+}
+
+// a narrow row of ald bf16 (and a one at column ald) within the m = 256 rows
+bool aug_ok(const AttnShape& s, int ald, int one) {
+  return ald > 0 && ald % 8 == 0 && ald + (one ? 1 : 0) <= 256 &&
+         s.seg_len * ald * 2 < (int64_t{1} << 31) && s.n * ald * 2 < (int64_t{1} << 31);
+}
+
+bool aug32_supported(const AttnShape& s) { return key32(s) == 256128; }
+
+hipError_t launch_seg_state32_aug(const AttnShape& s, const uint16_t* phik, int kald, int kone,
+                                  const uint16_t* v, int vld, float* seg, hipStream_t st) {
+  if (!aug32_supported(s) || !aug_ok(s, kald, kone) || vld < s.dv ||
+      s.n * vld * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  return launch_state_t<256, 128, false, false, true, true>(s, phik, v, nullptr, nullptr, seg, st,
+                                                            vld, kald, kone);
+}
+
+hipError_t launch_attn_out32_aug(const AttnShape& s, const uint16_t* phiq, int qald, int qone,
+                                 const uint16_t* phik, int kald, int kone, const uint16_t* v,
+                                 int vld, const float* state, int64_t st_seg, int64_t st_bh,
+                                 uint16_t* outb, int ldo, hipStream_t st) {
+  if (!aug32_supported(s) || !aug_ok(s, qald, qone) || !aug_ok(s, kald, kone) || !outb ||
+      vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  const float* g = nullptr;
+  if (s.anti) {
+    if (!s.causal) return hipErrorInvalidValue;
+    return launch_out_t<256, 128, true, false, false, 2, true, true, true>(
+        s, phiq, phik, v, g, state, st_seg, st_bh, nullptr, st, nullptr, outb, ldo, vld, qald,
+        qone, kald, kone);
+  }
+  if (s.causal)
+    return launch_out_t<256, 128, true, false, false, 2, true, false, true>(
+        s, phiq, phik, v, g, state, st_seg, st_bh, nullptr, st, nullptr, outb, ldo, vld, qald,
+        qone, kald, kone);
+  return launch_out_t<256, 128, false, false, false, 2, true, false, true>(
+      s, phiq, phik, v, g, state, st_seg, st_bh, nullptr, st, nullptr, outb, ldo, vld, qald, qone,
+      kald, kone);
 }
 
 hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L, hipStream_t st) {

@@ -118,6 +118,51 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
   }
 }
 
+// make_ab for the passes on narrow operands: the same dnum and dden (same
+// arithmetic, so the passes see the same bf16 values), written as dnum
+// [rows][dv] and an = [dnum | dden | 0 x 7] [rows][dv + 8] instead of the
+// padded a and b (the passes read b as v with a one at column dv); rows in
+// order.
+__global__ __launch_bounds__(256) void make_ab_aug(const float* __restrict__ num,
+                                                  const float* __restrict__ den1,
+                                                  const float* __restrict__ G, int dv,
+                                                  int64_t rows, int normalize, float delta,
+                                                  uint16_t* __restrict__ an,
+                                                  uint16_t* __restrict__ rdnum, int den_ld) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int l = threadIdx.x & 31;
+  const bool live = r < rows;  // every lane joins the shuffles below
+  const int64_t rc = live ? r : rows - 1;
+  const float den = normalize ? den1[rc * den_ld] + delta : 1.f;
+  const float inv = 1.f / den;
+  const int c0 = 8 * l;  // this lane's columns c0 .. c0+7
+  float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float dot = 0.f;
+  if (c0 < dv) {
+    const u32x4 g0 = ld16(G + rc * dv + c0), g1 = ld16(G + rc * dv + c0 + 4);
+    const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      g[e] = __uint_as_float(g0[e]);
+      g[4 + e] = __uint_as_float(g1[e]);
+      dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
+    }
+  }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) dot += __shfl_xor(dot, o, 32);
+  const float dden = normalize ? -dot * inv : 0.f;
+  if (!live || c0 > dv) return;
+  const int64_t aw = dv + 8;  // an's row length
+  if (c0 < dv) {
+    const u32x4 av{pack_bf16x2(g[0] * inv, g[1] * inv), pack_bf16x2(g[2] * inv, g[3] * inv),
+                   pack_bf16x2(g[4] * inv, g[5] * inv), pack_bf16x2(g[6] * inv, g[7] * inv)};
+    st16(rdnum + rc * dv + c0, av);
+    st16(an + rc * aw + c0, av);
+  } else {  // c0 == dv: dden, then zeros
+    st16(an + rc * aw + c0, u32x4{static_cast<uint32_t>(f32_to_bf16(dden)), 0u, 0u, 0u});
+  }
+}
+
 unsigned blocks_for(int64_t work, int per) {
   return static_cast<unsigned>((work + per - 1) / per);
 }
@@ -169,6 +214,17 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
   LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab, dim3(static_cast<unsigned>((rows + 7) / 8)),
                dim3(256), 0, st, num, den1, G, V, dv, MA, n, rows, normalize, delta, a, ra, b, rb,
                rdnum, rev, den_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_make_ab_aug(const float* num, const float* den1, const float* G, int dv,
+                              int64_t rows, int normalize, float delta, uint16_t* an,
+                              uint16_t* rdnum, int den_ld, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  if ((rows + 7) / 8 > 0x7fffffffLL || dv % 8 || dv + 8 > 256 || den_ld < 1 || !an || !rdnum)
+    return hipErrorInvalidValue;
+  LLOPS_LAUNCH("attn_bwd_make_ab", st, make_ab_aug, dim3(static_cast<unsigned>((rows + 7) / 8)),
+               dim3(256), 0, st, num, den1, G, dv, rows, normalize, delta, an, rdnum, den_ld);
   return hipGetLastError();
 }
 

@@ -85,6 +85,12 @@ hipError_t launch_make_ab(const float* num, const float* den1, const float* G, c
                           int dv, int MA, int64_t n, int64_t rows, int normalize, float delta,
                           uint16_t* a, uint16_t* ra, uint16_t* b, uint16_t* rb, uint16_t* rdnum,
                           int rev, int den_ld, hipStream_t st);
+// The same for the narrow operands of launch_attn_out32_aug: dnum to rdnum
+// [rows][dv] and an = [dnum | dden | 0 x 7] [rows][dv + 8] (bf16, rows in
+// order) in place of the padded a and b (b is v with a one at column dv).
+hipError_t launch_make_ab_aug(const float* num, const float* den1, const float* G, int dv,
+                              int64_t rows, int normalize, float delta, uint16_t* an,
+                              uint16_t* rdnum, int den_ld, hipStream_t st);
 // Backward from an initial state (S0 [BH][m][dv], z0 [BH][m]): z0 broadcast
 // over `width` columns, the transposed [S0^T; z0^T] slice that starts a dphi_Q
 // pass, and one column of per-(b, h) totals.
@@ -185,6 +191,21 @@ hipError_t launch_attn_out32_to(const AttnShape& a, const uint16_t* phiq, const 
 // the slice's first column; launch_seg_state32_v is the matching state pass.
 hipError_t launch_seg_state32_v(const AttnShape& a, const uint16_t* phik, const uint16_t* v,
                                 int vld, float* seg, hipStream_t st);
+// The backward's chain-rule passes on narrow operands (m = 256, dv = 128
+// kernels only): each feature row of phi_Q (phi_K) is stored as qald (kald)
+// bf16 (row stride the same, a multiple of 8) and read as 256: those values,
+// a bf16 one at column qald (kald) if qone (kone), then zeros. So the passes
+// read [dnum | dden | 0] (stored [dnum | dden | 0 x 7]) and [v | 1 | 0] (v
+// itself) without padded copies. Values are a column slice (vld, as
+// launch_seg_state32_v); rows go to outb (bf16, ldo apart). a.anti selects
+// the suffix form.
+bool aug32_supported(const AttnShape& a);
+hipError_t launch_seg_state32_aug(const AttnShape& a, const uint16_t* phik, int kald, int kone,
+                                  const uint16_t* v, int vld, float* seg, hipStream_t st);
+hipError_t launch_attn_out32_aug(const AttnShape& a, const uint16_t* phiq, int qald, int qone,
+                                 const uint16_t* phik, int kald, int kone, const uint16_t* v,
+                                 int vld, const float* state, int64_t state_seg_stride,
+                                 int64_t state_bh_stride, uint16_t* outb, int ldo, hipStream_t st);
 // The same pass with a.normalize set, writing the unnormalised rows to out
 // and each row's denominator phi_Q,i . z_i (no delta) to den [BH][n].
 hipError_t launch_attn_out32_den(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,

@@ -72,6 +72,36 @@ def test_causal_bwd_reversed_form(lib, case, monkeypatch):
     monkeypatch.setenv("LLOPS_BWD_REVERSED", "1")
     test_causal_bwd(lib, case)
 
+# shapes on the m = 256, dv = 128 kernels, where the chain-rule passes read
+# narrow operands: ragged, one token, several segments, t = 1 unnormalised
+NARROW = [CASES[1], CASES[4], CASES[5], (2, 2, 1500, 128, 128, 256, 1, False, False, False)]
+
+
+@pytest.mark.parametrize("case", NARROW, ids=[str(c) for c in NARROW])
+def test_causal_bwd_narrow_equals_padded(lib, case, monkeypatch):
+    """The chain-rule passes read [dnum | dden | 0] from a narrow copy and
+    [V | 1 | 0] from V itself; LLOPS_BWD_PADDED=1 selects the padded copies.
+    Both put the same bf16 values in the same places of the same products,
+    so every gradient agrees bit for bit."""
+    B, H, n, d, dv, m, t, square, normalize, shared = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize, seed=3)
+    x = generate(w)
+    G = dev(dout(w), torch.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce(f"causal_bwd narrow vs padded {case}")
+
+    def run():
+        out = lib.llops_linattn_causal_bwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], G,
+                                           square=square, normalize=normalize, delta=w.delta)
+        torch.cuda.synchronize()
+        return out
+    narrow = run()
+    monkeypatch.setenv("LLOPS_BWD_PADDED", "1")
+    padded = run()
+    for name, a, b in zip(("dQ", "dK", "dV", "dtheta_q", "dtheta_k"), narrow, padded):
+        assert torch.equal(a, b), name
+
+
 def test_causal_bwd_no_rows(lib):
     w = _w(1, 2, 0, 64, 64, 64, 4, True, True)
     th = dev(generate(w.replace(n=1))["theta_q"], torch.bfloat16)

@@ -61,6 +61,32 @@ def test_linattn_bwd(lib, case):
         assert err <= TOL_BF16, (name, err)
 
 
+NARROW = [CASES[1], CASES[4], CASES[5]]
+
+
+@pytest.mark.parametrize("case", NARROW, ids=[str(c) for c in NARROW])
+def test_linattn_bwd_narrow_equals_padded(lib, case, monkeypatch):
+    """As for the causal backward: the non-causal chain-rule passes on narrow
+    operands agree bit for bit with the padded copies (LLOPS_BWD_PADDED=1)."""
+    B, H, n, d, dv, m, t, square, normalize, shared = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize)
+    x = generate(w)
+    G = dev(dout(w), torch.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce(f"linattn_bwd narrow vs padded {case}")
+
+    def run():
+        out = lib.llops_linattn_bwd(g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], G,
+                                    square=square, normalize=normalize, delta=w.delta)
+        torch.cuda.synchronize()
+        return out
+    narrow = run()
+    monkeypatch.setenv("LLOPS_BWD_PADDED", "1")
+    padded = run()
+    for name, a, b in zip(("dQ", "dK", "dV", "dtheta_q", "dtheta_k"), narrow, padded):
+        assert torch.equal(a, b), name
+
+
 def test_linattn_bwd_no_rows(lib):
     w = _w(1, 2, 0, 64, 64, 64, 4, True, True)
     th = dev(generate(w.replace(n=1))["theta_q"], torch.bfloat16)
