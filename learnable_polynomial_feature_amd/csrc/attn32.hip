@@ -82,6 +82,10 @@ __device__ __forceinline__ AugRows aug_rows(const uint16_t* rows0, int ald, int 
   return AugRows{make_rsrc(rows0 + row0 * ald, rows * static_cast<uint32_t>(ald) * 2u),
                  static_cast<uint32_t>(ald) * 2u, ald / 8, one ? 0x3F80u : 0u};
 }
+// Narrow rows fill at most kAugTiles 32-feature tiles (ald + one <= 160);
+// the tiles after them hold zeros in every operand and state, so the AUG
+// passes skip their products (adding exact zeros changes no sum).
+constexpr int kAugTiles = 5;
 // piece q of row `row` of chunk c (kC rows a chunk)
 __device__ __forceinline__ u32x4 aug_ld(const AugRows& v, int row, int q, int c) {
   constexpr uint32_t kPast = 0x80000000u;  // past any view (views stay below 2^31 bytes)
@@ -384,13 +388,15 @@ void seg_state32(Seg32Args a, const uint16_t* __restrict__ phik,
       }
       gsum += T;
     }
+    // AUG: the live feature tiles only (kAugTiles)
+    constexpr int FL = AUG ? kAugTiles : FT, NL = (kC / 16) * FL;
 #pragma unroll
-    for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FT) * 16, (i % FT) * 32, lane);
+    for (int i = 0; i < KD; ++i) kf[i] = frag_tr(Ks, MP, (i / FL) * 16, (i % FL) * 32, lane);
 #pragma unroll
-    for (int idx = 0; idx < NK; ++idx) {
-      const int ks = idx / FT, f = idx % FT;
+    for (int idx = 0; idx < NL; ++idx) {
+      const int ks = idx / FL, f = idx % FL;
       const bf16x8 ka = kf[idx % KD];
-      if (idx + KD < NK) kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FT) * 16, ((idx + KD) % FT) * 32, lane);
+      if (idx + KD < NL) kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FL) * 16, ((idx + KD) % FL) * 32, lane);
       S[f] = mfma32x32x16(ka, vb[ks], S[f]);
       if ((f % G::NW) == (w % G::NW) && f / G::NW < G::ZT)
         Z[f / G::NW] = mfma32x32x16(ka, zb[ks], Z[f / G::NW]);
@@ -508,6 +514,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
   const int f0 = half * FH;                    // first feature tile of this wave
   const bool has_z = dvt < FH;
   const int zj = dvt;                          // z tile = feature tile f0 + zj
+  // AUG: this half's live feature tiles (the first kAugTiles of all). The
+  // masked chunk product stays with half 0 (on half 1, whose tiles are
+  // mostly dead, it measured no faster, and it changes the order in which
+  // the two halves' partial rows are summed)
+  static_assert(!AUG || (kAugTiles > FH && kAugTiles <= 2 * FH), "live tiles reach the second half");
+  const int nlive = AUG ? (half == 0 ? FH : kAugTiles - FH) : FH;
   const int c32 = lane & 31, hh = lane >> 5;
   const int64_t bh = blockIdx.y;
   const int gseg = blockIdx.x;
@@ -654,6 +666,7 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
 #pragma unroll
       for (int idx = 0; idx < NQ; ++idx) {
         const int j = idx >> 1, h = idx & 1;
+        if (AUG && j >= nlive) break;  // wave-uniform: the rest of the half is dead tiles
         const bf16x8 qa = qf[idx % QD];
         if (idx + QD < NQ) qf[idx % QD] = frag_p16_sep(Qs, QPAD, 0, f0 * 32 + (idx + QD) * 16, lane);
         O = mfma32x32x16(qa, acc_frag(S[j], h), O);
@@ -666,8 +679,8 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       // masked A^T = phi_K phi_Q^T (keys x queries)
       // fragment reads run AD k-steps ahead of the MFMA chain (pinned: the
       // scheduler would otherwise sink each read next to its MFMA and expose
-      // the LDS latency on every step)
-      constexpr int KS = M / 16, AD = KS < 3 ? KS : 3;
+      // the LDS latency on every step); AUG: over the live features only
+      constexpr int KS = (AUG ? kAugTiles * 32 : M) / 16, AD = KS < 3 ? KS : 3;
       f32x16 At = zero16();
       bf16x8 fk[AD], fq[AD];
 #pragma unroll
@@ -811,10 +824,12 @@ void attn_out32(Seg32Args a, const uint16_t* __restrict__ phiq, const uint16_t* 
       for (int idx = 0; idx < NK; ++idx) {
         const int ks = idx / FH, j = idx % FH;
         const bf16x8 ka = kf[idx % KD];
-        if (idx + KD < NK)
+        if (idx + KD < NK && (!AUG || (idx + KD) % FH < nlive))
           kf[idx % KD] = frag_tr(Ks, MP, ((idx + KD) / FH) * 16, (f0 + (idx + KD) % FH) * 32, lane);
-        S[j] = mfma32x32x16(ka, vb[ks], S[j]);
-        if (has_z && j == zj) Z = mfma32x32x16(ka, zb[ks], Z);
+        if (!AUG || j < nlive) {  // wave-uniform
+          S[j] = mfma32x32x16(ka, vb[ks], S[j]);
+          if (has_z && j == zj) Z = mfma32x32x16(ka, zb[ks], Z);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -1585,9 +1600,9 @@ hipError_t launch_seg_state32_v(const AttnShape& s, const uint16_t* phik, const 
   }
 }
 
-// a narrow row of ald bf16 (and a one at column ald) within the m = 256 rows
+// a narrow row of ald bf16 (and a one at column ald) within the live tiles
 bool aug_ok(const AttnShape& s, int ald, int one) {
-  return ald > 0 && ald % 8 == 0 && ald + (one ? 1 : 0) <= 256 &&
+  return ald > 0 && ald % 8 == 0 && ald + (one ? 1 : 0) <= kAugTiles * 32 &&
          s.seg_len * ald * 2 < (int64_t{1} << 31) && s.n * ald * 2 < (int64_t{1} << 31);
 }
 

@@ -193,8 +193,9 @@ hipError_t launch_seg_state32_v(const AttnShape& a, const uint16_t* phik, const 
                                 int vld, float* seg, hipStream_t st);
 // The backward's chain-rule passes on narrow operands (m = 256, dv = 128
 // kernels only): each feature row of phi_Q (phi_K) is stored as qald (kald)
-// bf16 (row stride the same, a multiple of 8) and read as 256: those values,
-// a bf16 one at column qald (kald) if qone (kone), then zeros. So the passes
+// bf16 (row stride the same, a multiple of 8; qald + qone <= 160) and read
+// as 256: those values, a bf16 one at column qald (kald) if qone (kone), then
+// zeros (features past 160 take no products). So the passes
 // read [dnum | dden | 0] (stored [dnum | dden | 0 x 7]) and [v | 1 | 0] (v
 // itself) without padded copies. Values are a column slice (vld, as
 // launch_seg_state32_v); rows go to outb (bf16, ldo apart). a.anti selects
