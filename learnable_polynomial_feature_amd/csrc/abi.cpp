@@ -439,20 +439,20 @@ bool bwd_padded() {
 hipError_t attn_on_aug(const llops_shape_t* s, bool causal, bool anti, int M, int DV,
                        const uint16_t* fq, int qald, int qone, const uint16_t* fk, int kald,
                        int kone, const uint16_t* v, int vld, uint16_t* outb, int ldo, float* seg,
-                       float* tot, hipStream_t st) {
+                       float* tot, hipStream_t st, const float* S0init = nullptr) {
   const llops_shape_t t = feat_attn_shape(s, M, DV);
   llops::AttnShape a = attn_shape(&t, causal);
   const int64_t per = static_cast<int64_t>(M) * DV + M;
   if (anti) {  // suffix sums: the scan from the last segment, chunks from the last
-    if (!causal) return hipErrorInvalidValue;
+    if (!causal || S0init) return hipErrorInvalidValue;
     a.anti = 1;
   }
   hipError_t e = llops::launch_seg_state32_aug(a, fk, kald, kone, v, vld, seg, st);
   if (e != hipSuccess) return e;
   const float* state = seg;
   int64_t st_seg = per, st_bh = per * a.nseg;
-  if (causal) {
-    e = llops::launch_seg_scan(a, seg, nullptr, nullptr, nullptr, nullptr, 1, st);
+  if (causal) {  // S0init: [BH][M*DV] initial state (null = zeros)
+    e = llops::launch_seg_scan(a, seg, S0init, nullptr, nullptr, nullptr, 1, st);
   } else {
     e = llops::launch_seg_scan(a, seg, nullptr, nullptr, tot, tot + static_cast<int64_t>(M) * DV,
                                0, st);
@@ -1016,8 +1016,8 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   // where a would be) and [V | 1 | 0] from V itself instead of the padded
   // copies, where their kernels apply
   const llops_shape_t ta = feat_attn_shape(s, MA, W);
-  const bool aug = !rev && sliced && !init && !dS0 && !dz0 && !bwd_padded() && dv % 8 == 0 &&
-                   dv + 8 <= MA && llops::aug32_supported(attn_shape(&ta, causal));
+  const bool aug = !rev && sliced && !bwd_padded() && dv % 8 == 0 && dv + 8 <= MA &&
+                   llops::aug32_supported(attn_shape(&ta, causal));
   if (aug)
     LLOPS_HIP(llops::launch_make_ab_aug(num, den1, dO, dv, R, s->normalize,
                                         s->normalize ? s->delta : 0.f, a, dn, den_ld, st),
@@ -1041,7 +1041,15 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     LLOPS_HIP(state_total(s, m, dv, rev ? rphq : phq, dn, seg, dS0, nullptr, st), "dS0");
   if (causal && dz0) {
     float* stot = f32(L.stot);
-    LLOPS_HIP(llops::launch_rows_copy_bf16(a, MA, dv, vp, 16, 0, 16, n, R, 0, st), "rows");
+    // the dden column (with zeros after it) as a 16-wide value block; only
+    // column 0 of the total below is kept. The narrow a holds 8 columns from
+    // dv on: they go into both halves of the block, so every column is defined
+    if (aug) {
+      LLOPS_HIP(llops::launch_rows_copy_bf16(a, dv + 8, dv, vp, 16, 0, 8, n, R, 0, st), "rows");
+      LLOPS_HIP(llops::launch_rows_copy_bf16(a, dv + 8, dv, vp, 16, 8, 8, n, R, 0, st), "rows");
+    } else {
+      LLOPS_HIP(llops::launch_rows_copy_bf16(a, MA, dv, vp, 16, 0, 16, n, R, 0, st), "rows");
+    }
     LLOPS_HIP(state_total(s, m, 16, phq, vp, seg, stot, stot + static_cast<int64_t>(m) * 16, st),
               "dz0");
     LLOPS_HIP(llops::launch_col_extract(stot, BH, m, static_cast<int64_t>(m) * 16 + m, 16, dz0, st),
@@ -1057,8 +1065,12 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   const uint16_t* vv = static_cast<const uint16_t*>(V);
   for (int p0 = 0; aug && p0 < m; p0 += W) {
     // dphi_Q_i = sum_{j(<=i)} (a_i . b_j) phi_K_j, a = [dnum | dden], b = [V | 1]
+    // (+ dnum_i . S0 + dden_i z0 from an initial state: its rows past dv are
+    // zero, so the skipped feature tiles stay zero)
+    if (init)
+      LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
     LLOPS_HIP(attn_on_aug(s, causal, false, MA, W, a, dv + 8, 0, vv, dv, 1, phk + p0, m, dphq + p0,
-                          m, seg, tot, st),
+                          m, seg, tot, st, init ? f32(L.p0) : nullptr),
               "attn dphi_q");
     // dphi_K_j = sum_{i(>=j)} (a_i . b_j) phi_Q_i: suffix sums (anti-causal)
     LLOPS_HIP(attn_on_aug(s, causal, anti, MA, W, vv, dv, 1, a, dv + 8, 0, phq + p0, m, dphk + p0,

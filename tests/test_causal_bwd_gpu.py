@@ -177,6 +177,36 @@ def test_causal_bwd_from_initial_state(lib, case):
         assert err <= TOL_BF16, (name, err)
 
 
+@pytest.mark.parametrize("case", [STATE_CASES[1], (1, 2, 2048, 128, 128, 256, 1, True, True)],
+                         ids=[str(STATE_CASES[1]), "(1, 2, 2048, 128, 128, 256, 1, True, True)"])
+def test_causal_bwd_state_narrow_equals_padded(lib, case, monkeypatch):
+    """From an initial state the dphi_Q pass starts from the [S0^T; z0^T]
+    slice, and dz0 sums the dden column; on narrow operands all seven
+    gradients equal the padded form's bit for bit (LLOPS_BWD_PADDED=1)."""
+    B, H, n, d, dv, m, t, square, normalize = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize, seed=5)
+    x = generate(w)
+    rng = np.random.default_rng(37)
+    S0 = dev((0.01 * rng.standard_normal((B, H, m, dv))).astype(np.float32), torch.float32)
+    z0 = dev(np.abs(0.01 * rng.standard_normal((B, H, m))).astype(np.float32), torch.float32)
+    G = dev(dout(w), torch.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    announce(f"causal_bwd_state narrow vs padded {case}")
+
+    def run():
+        out = lib.llops_linattn_causal_bwd_state(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                 g["theta_k"], G, S0=S0, z0=z0, square=square,
+                                                 normalize=normalize, delta=w.delta)
+        torch.cuda.synchronize()
+        return out
+    narrow = run()
+    monkeypatch.setenv("LLOPS_BWD_PADDED", "1")
+    padded = run()
+    names = ("dQ", "dK", "dV", "dtheta_q", "dtheta_k", "dS0", "dz0")
+    for name, a, b in zip(names, narrow, padded):
+        assert torch.equal(a, b), name
+
+
 def test_causal_bwd_state_without_state_is_causal_bwd(lib):
     """No initial state: the same numbers as llops_linattn_causal_bwd bit for
     bit, plus dS0, dz0 of a zero state against the oracle."""
