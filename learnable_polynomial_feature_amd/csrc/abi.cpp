@@ -567,6 +567,24 @@ hipError_t gated_attn_on_features(const llops_shape_t* s, int M, int DV, const u
   return e;
 }
 
+// gated_attn_on_features on narrow operands (attn_on_aug): phi_Q rows stored
+// as qald bf16 (a one at column qald if qone), phi_K likewise; fp32 rows to out.
+hipError_t gated_attn_on_aug(const llops_shape_t* s, int M, int DV, const uint16_t* fq, int qald,
+                             int qone, const uint16_t* fk, int kald, int kone, const uint16_t* v,
+                             int vld, const float* gl, float* out, float* seg, float* gseg,
+                             hipStream_t st, const float* S0init) {
+  const llops_shape_t t = feat_attn_shape(s, M, DV);
+  const llops::AttnShape a = attn_shape(&t, true, kGatedBwdWG);
+  hipError_t e =
+      llops::launch_seg_state32_gated_aug(a, fk, kald, kone, v, vld, gl, gseg, seg, false, st);
+  if (e == hipSuccess)
+    e = llops::launch_seg_scan_gated(a, seg, gseg, S0init, nullptr, nullptr, nullptr, st);
+  if (e == hipSuccess)
+    e = llops::launch_attn_out32_gated_aug(a, fq, qald, qone, fk, kald, kone, v, vld, gl, seg, out,
+                                           st);
+  return e;
+}
+
 // Gated num = M V and den = M 1 per row in one pass (see attn_num_den).
 hipError_t gated_attn_num_den(const llops_shape_t* s, const uint16_t* fq, const uint16_t* fk,
                               const uint16_t* v, const float* gl, float* num, float* den,
@@ -1237,10 +1255,21 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
   }
   uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
   uint16_t *ra = anti ? nullptr : u16(L.b.ra), *rb = anti ? nullptr : u16(L.b.rb);
-  LLOPS_HIP(llops::launch_make_ab(num, den, dO, vv, dv, MA, n, R, s->normalize,
-                                  s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, anti ? 0 : 1, 1,
-                                  st),
-            "make_ab");
+  // narrow chain-rule operands (as in the ungated backward) on the anti-causal
+  // path of the m = 256, dv = 128 kernels, with phi read in place
+  const llops_shape_t tMW0 = feat_attn_shape(s, MA, W);
+  const bool aug = anti && n * m * 2 < (int64_t{1} << 31) && !bwd_padded() && dv % 8 == 0 &&
+                   dv + 8 <= MA &&
+                   llops::aug32_supported(attn_shape(&tMW0, true, kGatedBwdWG));
+  if (aug)
+    LLOPS_HIP(llops::launch_make_ab_aug(num, den, dO, dv, R, s->normalize,
+                                        s->normalize ? s->delta : 0.f, a, dn, 1, st),
+              "make_ab");
+  else
+    LLOPS_HIP(llops::launch_make_ab(num, den, dO, vv, dv, MA, n, R, s->normalize,
+                                    s->normalize ? s->delta : 0.f, a, ra, b, rb, dn, anti ? 0 : 1,
+                                    1, st),
+              "make_ab");
   uint16_t* vp = u16(L.b.vp);
   float* tmp = f32(L.b.tmp);
   float* dc = f32(L.dc);
@@ -1269,14 +1298,23 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
       LLOPS_HIP(llops::launch_rows_copy_bf16(phk, m, p0, vp, W, 0, W, n, R, 0, st), "rows");
     if (init)
       LLOPS_HIP(llops::launch_build_p0(S0, z0, BH, m, dv, MA, W, p0, f32(L.p0), st), "state");
-    LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, sliced ? phk + p0 : vp, glf, tmp, seg, gseg,
-                                     st, init ? f32(L.p0) : nullptr, sliced ? m : 0),
-              "attn dphi_q");
+    if (aug)
+      LLOPS_HIP(gated_attn_on_aug(s, MA, W, a, dv + 8, 0, vv, dv, 1, phk + p0, m, glf, tmp, seg,
+                                  gseg, st, init ? f32(L.p0) : nullptr),
+                "attn dphi_q");
+    else
+      LLOPS_HIP(gated_attn_on_features(s, MA, W, a, b, sliced ? phk + p0 : vp, glf, tmp, seg, gseg,
+                                       st, init ? f32(L.p0) : nullptr, sliced ? m : 0),
+                "attn dphi_q");
     // dc_i += phi_Q,i . dphi_Q,i, and the slice of dphi_Q stored as bf16
     LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phq, m, p0, W, n, R, 0, 1.f, p0 == 0 ? 1 : 0, dc,
                                        st, dphq),
               "rowdot");
-    if (sliced) {
+    if (aug) {
+      LLOPS_HIP(llops::launch_seg_state32_gated_aug(aMW, a, dv + 8, 0, phq + p0, m, glf, gseg, seg2,
+                                                    true, st),
+                "anchored");
+    } else if (sliced) {
       LLOPS_HIP(llops::launch_seg_state32_gated_v(aMW, a, phq + p0, m, glf, gseg, seg2, true, st),
                 "anchored");
     } else {
@@ -1298,8 +1336,13 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
       // of the next one, which seg2 now holds; dc_j -= phi_K,j . dphi_K,j
       llops::AttnShape ga = aMW;
       ga.anti = 1;
-      LLOPS_HIP(llops::launch_attn_out32_gated_to(ga, b, a, phq + p0, glf, seg2, tmp, 0, m, st),
-                "attn dphi_k");
+      if (aug)
+        LLOPS_HIP(llops::launch_attn_out32_gated_aug(ga, vv, dv, 1, a, dv + 8, 0, phq + p0, m, glf,
+                                                     seg2, tmp, st),
+                  "attn dphi_k");
+      else
+        LLOPS_HIP(llops::launch_attn_out32_gated_to(ga, b, a, phq + p0, glf, seg2, tmp, 0, m, st),
+                  "attn dphi_k");
       LLOPS_HIP(llops::launch_rowdot_acc(tmp, W, phk, m, p0, W, n, R, 0, -1.f, 0, dc, st, dphk),
                 "rowdot");
     }

@@ -1640,6 +1640,36 @@ hipError_t launch_attn_out32_aug(const AttnShape& s, const uint16_t* phiq, int q
       kald, kone);
 }
 
+hipError_t launch_seg_state32_gated_aug(const AttnShape& s, const uint16_t* phik, int kald, int kone,
+                                        const uint16_t* v, int vld, const float* gl, float* gseg,
+                                        float* seg, bool anchored, hipStream_t st) {
+  if (s.anti || !aug32_supported(s) || !aug_ok(s, kald, kone) || vld < s.dv ||
+      s.n * vld * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  if (anchored)
+    return launch_state_t<256, 128, true, true, true, true>(s, phik, v, gl, gseg, seg, st, vld,
+                                                            kald, kone);
+  return launch_state_t<256, 128, true, false, true, true>(s, phik, v, gl, gseg, seg, st, vld,
+                                                           kald, kone);
+}
+
+hipError_t launch_attn_out32_gated_aug(const AttnShape& s, const uint16_t* phiq, int qald, int qone,
+                                       const uint16_t* phik, int kald, int kone,
+                                       const uint16_t* v, int vld, const float* gl,
+                                       const float* state, float* out, hipStream_t st) {
+  if (!s.causal || !aug32_supported(s) || !aug_ok(s, qald, qone) || !aug_ok(s, kald, kone) ||
+      vld < s.dv || s.n * vld * 2 >= (int64_t{1} << 31))
+    return hipErrorInvalidValue;
+  const int64_t per = 256 * 128 + 256;
+  if (s.anti)  // suffix sums over start-anchored segment states (slot g + 1)
+    return launch_out_t<256, 128, true, true, false, 0, true, true, true>(
+        s, phiq, phik, v, gl, state, per, per * s.nseg, out, st, nullptr, nullptr, 0, vld, qald,
+        qone, kald, kone);
+  return launch_out_t<256, 128, true, true, false, 0, true, false, true>(
+      s, phiq, phik, v, gl, state, per, per * s.nseg, out, st, nullptr, nullptr, 0, vld, qald, qone,
+      kald, kone);
+}
+
 hipError_t launch_gate_cumsum32(int64_t BH, int64_t n, const float* g, float* L, hipStream_t st) {
   const int64_t nch = (n + kC - 1) / kC, total = BH * nch;
   if (total == 0) return hipSuccess;

@@ -207,6 +207,16 @@ hipError_t launch_attn_out32_aug(const AttnShape& a, const uint16_t* phiq, int q
                                  const uint16_t* phik, int kald, int kone, const uint16_t* v,
                                  int vld, const float* state, int64_t state_seg_stride,
                                  int64_t state_bh_stride, uint16_t* outb, int ldo, hipStream_t st);
+// The gated backward's passes on narrow operands: the decayed (or, anchored,
+// start-anchored) state pass, and the causal or (a.anti) suffix output pass
+// writing fp32 rows to out [rows][128].
+hipError_t launch_seg_state32_gated_aug(const AttnShape& a, const uint16_t* phik, int kald, int kone,
+                                        const uint16_t* v, int vld, const float* gl, float* gseg,
+                                        float* seg, bool anchored, hipStream_t st);
+hipError_t launch_attn_out32_gated_aug(const AttnShape& a, const uint16_t* phiq, int qald, int qone,
+                                       const uint16_t* phik, int kald, int kone,
+                                       const uint16_t* v, int vld, const float* gl,
+                                       const float* state, float* out, hipStream_t st);
 // The same pass with a.normalize set, writing the unnormalised rows to out
 // and each row's denominator phi_Q,i . z_i (no delta) to den [BH][n].
 hipError_t launch_attn_out32_den(const AttnShape& a, const uint16_t* phiq, const uint16_t* phik,

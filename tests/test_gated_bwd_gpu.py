@@ -70,6 +70,45 @@ def test_gated_bwd_reversed_form(lib, case, monkeypatch):
     monkeypatch.setenv("LLOPS_BWD_REVERSED", "1")
     test_gated_bwd(lib, case)
 
+@pytest.mark.parametrize("case", [CASES[1], CASES[4], CASES[5]],
+                         ids=[str(CASES[1]), str(CASES[4]), str(CASES[5])])
+@pytest.mark.parametrize("state", [False, True], ids=["no_state", "state"])
+def test_gated_bwd_narrow_equals_padded(lib, case, state, monkeypatch):
+    """On the m = 256, dv = 128 kernels the gated chain-rule passes read
+    [dnum | dden | 0] from a narrow copy and [V | 1 | 0] from V itself;
+    LLOPS_BWD_PADDED=1 selects the padded copies. Every gradient, the
+    log-gate one and (from an initial state) dS0, dz0 included, agrees bit
+    for bit."""
+    B, H, n, d, dv, m, t, square, normalize, shared, mu = case
+    w = _w(B, H, n, d, dv, m, t, square, normalize, seed=7)
+    x = generate(w)
+    G = dev(dout(w), torch.float32)
+    lg = dev(log_gates(w, mu=mu), torch.float32)
+    g = {k: dev(v, torch.bfloat16) for k, v in x.items()}
+    rng = np.random.default_rng(41)
+    S0 = dev((0.01 * rng.standard_normal((B, H, m, dv))).astype(np.float32), torch.float32)
+    z0 = dev(np.abs(0.01 * rng.standard_normal((B, H, m))).astype(np.float32), torch.float32)
+    announce(f"gated_bwd narrow vs padded {case} state={state}")
+
+    def run():
+        if state:
+            out = lib.llops_linattn_gated_causal_bwd_state(
+                g["Q"], g["K"], g["V"], g["theta_q"], g["theta_k"], lg, G, S0=S0, z0=z0,
+                square=square, normalize=normalize, delta=w.delta)
+        else:
+            out = lib.llops_linattn_gated_causal_bwd(g["Q"], g["K"], g["V"], g["theta_q"],
+                                                     g["theta_k"], lg, G, square=square,
+                                                     normalize=normalize, delta=w.delta)
+        torch.cuda.synchronize()
+        return out
+    narrow = run()
+    monkeypatch.setenv("LLOPS_BWD_PADDED", "1")
+    padded = run()
+    assert len(narrow) == len(padded)
+    for i, (a, b) in enumerate(zip(narrow, padded)):
+        assert torch.equal(a, b), i
+
+
 def test_gated_bwd_zero_gate_matches_ungated(lib):
     """log_gate = 0: the same gradients as llops_linattn_causal_bwd (different
     kernels and rounding order), and the gate gradient against the oracle."""
