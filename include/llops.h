@@ -235,7 +235,11 @@ llops_status_t llops_linattn_gated_causal_fwd(const llops_shape_t* shape, const 
  * is too long for a 32-bit view, or with LLOPS_BWD_REVERSED=1 in the
  * environment (read at each call and by the workspace query), the suffix sums
  * run as causal passes over reversed copies instead (a larger workspace; the
- * same gradients up to summation order).
+ * same gradients up to summation order). At m = 256, dv = 128 the dphi passes
+ * read [dnum | dden | 0] from a dv + 8 wide copy and [V | 1 | 0] from V
+ * itself (this entry point, the _state one and both gated ones);
+ * LLOPS_BWD_PADDED=1 in the environment (read at each call) selects 256-wide
+ * padded copies instead, with bit for bit the same gradients.
  * in_dtype BF16 only; kernels exist for p = 2, t in {1, 4}, d in {64, 128},
  * m in {64, 128, 256}, dv % 16 == 0 and dv <= 128 (else LLOPS_ERR_UNSUPPORTED).
  * theta_q and theta_k may alias; their gradients are still returned apart.
