@@ -29,10 +29,10 @@
 // (rows x features), so dY^T is an A operand from registers and X (read
 // transposed from LDS) the B operand. With t = 4 the four waves take one rank
 // each over the same 32 rows and read ds from the dX kernel; with t = 1 each
-// wave takes its own 32 of a 128-row step and forms s itself. A bf16
-// gradient of whole steps travels with the X rows: each step's tile is
-// staged once per workgroup and read back transposed by every wave. The
-// workgroup
+// wave takes its own 32 of a 128-row step and forms s itself (one swizzled
+// copy of the step's rows serves both its read patterns, xswz). A bf16
+// gradient of whole steps travels with the X rows: each step's tile is staged
+// once per workgroup and read back transposed by every wave. The workgroup
 // writes its chunk's partial dTheta (one per wave for t = 1);
 // featmap_bwd_reduce sums the partials (and the heads, for a shared Theta) in
 // a fixed order and transposes.
