@@ -995,8 +995,9 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
   llops::FeatJob jobs[2] = {{Q, theta_q, phq, w + L.pkq}, {K, theta_k, phk, w + L.pkk}};
   LLOPS_HIP(llops::launch_featmap_bf16(feat_shape(s, n, 1), jobs, 2, st), "featmap");
   // num = M V and, with the normaliser, M 1: one pass on the 32x32x16
-  // shapes, else a second pass over all-ones values
-  float* num = f32(L.num);
+  // shapes, else a second pass over all-ones values. Unnormalised, dnum = dO
+  // and dden = 0, so neither is formed.
+  float* num = s->normalize ? f32(L.num) : nullptr;
   float* den1 = nullptr;
   int den_ld = 16;
   if (s->normalize && num_den_one_pass(s, causal)) {
@@ -1005,7 +1006,7 @@ static llops_status_t attn_backward(const llops_shape_t* s, bool causal, const v
     LLOPS_HIP(attn_num_den(s, causal, phq, phk, static_cast<const uint16_t*>(V), num, den1, seg,
                            tot, st, S0, z0),
               "attn num den");
-  } else {
+  } else if (s->normalize) {
     LLOPS_HIP(attn_on_features(s, causal, m, dv, phq, phk, static_cast<const uint16_t*>(V), num,
                                seg, tot, st, S0),
               "attn num");
@@ -1242,16 +1243,14 @@ static llops_status_t gated_bwd_body(const llops_shape_t* s, const void* Q, cons
     LLOPS_HIP(llops::launch_gate_cumsum32(BH, n, grev, glr, st), "gate_cumsum");
   }
   // num = M V and, normalised, M 1 per row from the same pass
-  float* num = f32(L.b.num);
+  // unnormalised, dnum = dO and dden = 0: num is not formed
+  float* num = s->normalize ? f32(L.b.num) : nullptr;
   const uint16_t* vv = static_cast<const uint16_t*>(V);
   float* den = nullptr;
   if (s->normalize) {
     den = f32(L.gden);
     LLOPS_HIP(gated_attn_num_den(s, phq, phk, vv, glf, num, den, seg, gseg, st, S0, z0),
               "attn num den");
-  } else {
-    LLOPS_HIP(gated_attn_on_features(s, m, dv, phq, phk, vv, glf, num, seg, gseg, st, S0),
-              "attn num");
   }
   uint16_t *a = u16(L.b.a), *b = u16(L.b.b), *dn = u16(L.b.rdnum);
   uint16_t *ra = anti ? nullptr : u16(L.b.ra), *rb = anti ? nullptr : u16(L.b.rb);

@@ -86,12 +86,16 @@ __global__ __launch_bounds__(256) void make_ab(const float* __restrict__ num,
   float dot = 0.f;
   if (c0 < dv) {
     const u32x4 g0 = ld16(G + rc * dv + c0), g1 = ld16(G + rc * dv + c0 + 4);
-    const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       g[e] = __uint_as_float(g0[e]);
       g[4 + e] = __uint_as_float(g1[e]);
-      dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
+    }
+    if (normalize) {  // unnormalised: dden = 0 and num is not read (nor formed)
+      const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
     }
   }
   // dden = -(G . out) / den with out = num / den (sum over the row's 32 lanes)
@@ -140,12 +144,16 @@ __global__ __launch_bounds__(256) void make_ab_aug(const float* __restrict__ num
   float dot = 0.f;
   if (c0 < dv) {
     const u32x4 g0 = ld16(G + rc * dv + c0), g1 = ld16(G + rc * dv + c0 + 4);
-    const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       g[e] = __uint_as_float(g0[e]);
       g[4 + e] = __uint_as_float(g1[e]);
-      dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
+    }
+    if (normalize) {  // unnormalised: dden = 0 and num is not read (nor formed)
+      const u32x4 n0 = ld16(num + rc * dv + c0), n1 = ld16(num + rc * dv + c0 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dot += g[e] * (__uint_as_float(n0[e]) * inv) + g[4 + e] * (__uint_as_float(n1[e]) * inv);
     }
   }
 #pragma unroll
